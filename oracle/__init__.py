@@ -1,0 +1,156 @@
+"""fp64 CPU oracle for one exact Lloyd k-means iteration (ctypes over oracle.c).
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module.  The product path
+(the HIP library and its Python binding) never imports, loads or calls it, and
+the two share no code.
+
+The oracle computes the plain definition of a Lloyd iteration (Flash-KMeans
+article, lumevalley.com article 3696, section "Why being fast took so long":
+assign every point to its nearest centroid, then reduce-sum each cluster and
+divide by its size; section "Two kernels rewrite the GPU pipeline": the maths
+is unchanged and exact).  Cosine is L2 on L2-normalised rows with a zero norm
+replaced by 1 (LEANN FlashLib backend guide, mhpn.cn, paragraph "distance
+metric").  Every function below names the step it follows; the arithmetic is
+all in ``oracle.c``.
+
+Pins: every function here is checked in ``tests/test_oracle_pins.py`` against
+brute force, exact rational arithmetic, closed forms and library routines that
+do not share its code.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+METRICS = {"l2": 0, "cosine": 1}
+
+_CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared"]
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc into liboracle.so next to it."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", *_CFLAGS, "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        lib.fko_assign.argtypes = [P, I64, I64, P, I64, ctypes.c_int, P, P, P]
+        lib.fko_assign.restype = ctypes.c_int
+        lib.fko_update.argtypes = [P, I64, I64, P, I64, ctypes.c_int, P, P, P]
+        lib.fko_update.restype = ctypes.c_int
+        lib.fko_lloyd_iter.argtypes = [P, I64, I64, P, I64, ctypes.c_int, P, P, P, P, P, P]
+        lib.fko_lloyd_iter.restype = ctypes.c_int
+        lib.fko_num_threads.argtypes = []
+        lib.fko_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _f32(a):
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    if a.ndim != 2:
+        raise ValueError("expected a 2-D array")
+    return a
+
+
+def _ptr(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def num_threads() -> int:
+    """OpenMP threads the assignment step uses (OMP_NUM_THREADS or all cores)."""
+    return int(_load().fko_num_threads())
+
+
+def assign(X, C, metric: str = "l2"):
+    """Assignment step: for each row x_i of X, D_ik = ||x_i - c_k||^2 (fp64,
+    direct difference), a_i = lowest index attaining the minimum, D1 = that
+    minimum, D2 = the minimum over the other centroids (inf when K == 1).
+
+    Returns (a int32[N], D1 float64[N], D2 float64[N]).
+    """
+    X = _f32(X)
+    C = _f32(C)
+    N, d = X.shape
+    K, dc = C.shape
+    if dc != d:
+        raise ValueError("X and C differ in d")
+    a = np.empty(N, np.int32)
+    D1 = np.empty(N, np.float64)
+    D2 = np.empty(N, np.float64)
+    rc = _load().fko_assign(_ptr(X), N, d, _ptr(C), K, METRICS[metric], _ptr(a), _ptr(D1), _ptr(D2))
+    if rc != 0:
+        raise ValueError("oracle assign rejected its arguments")
+    return a, D1, D2
+
+
+def update(X, a, C_in, metric: str = "l2"):
+    """Update step: counts n_k, and C_new[k] = mean of the (normalised, for
+    cosine) rows assigned to k, summed in fp64 in increasing i; a cluster with
+    no rows keeps C_in[k].  Returns (C_new float64[K,d], counts int64[K])."""
+    X = _f32(X)
+    C_in = _f32(C_in)
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    N, d = X.shape
+    K = C_in.shape[0]
+    if a.shape != (N,) or C_in.shape[1] != d:
+        raise ValueError("shape mismatch")
+    C_out = np.empty((K, d), np.float64)
+    counts = np.empty(K, np.int64)
+    rc = _load().fko_update(_ptr(X), N, d, _ptr(a), K, METRICS[metric], _ptr(C_in), _ptr(C_out), _ptr(counts))
+    if rc != 0:
+        raise ValueError("oracle update rejected its arguments (label outside [0, K)?)")
+    return C_out, counts
+
+
+def lloyd_iter(X, C_in, metric: str = "l2"):
+    """One iteration from C_in: assignment, update, and the objective
+    J = sum_i D1_i under C_in.  Returns a dict with a, D1, D2, C (float64),
+    counts (int64), J."""
+    X = _f32(X)
+    C_in = _f32(C_in)
+    N, d = X.shape
+    K = C_in.shape[0]
+    a = np.empty(N, np.int32)
+    D1 = np.empty(N, np.float64)
+    D2 = np.empty(N, np.float64)
+    C_out = np.empty((K, d), np.float64)
+    counts = np.empty(K, np.int64)
+    J = ctypes.c_double(0.0)
+    rc = _load().fko_lloyd_iter(_ptr(X), N, d, _ptr(C_in), K, METRICS[metric], _ptr(a), _ptr(D1),
+                                _ptr(D2), _ptr(C_out), _ptr(counts), ctypes.byref(J))
+    if rc != 0:
+        raise ValueError("oracle iteration rejected its arguments")
+    return {"a": a, "D1": D1, "D2": D2, "C": C_out, "counts": counts, "J": J.value}
+
+
+def relative_gap(D1, D2):
+    """g_i = (D2_i - D1_i) / D1_i: the top-2 gap relative to the best distance
+    (inf when D1 == 0 < D2, 0 when D1 == D2).  Points with g above a threshold
+    have an assignment that any exact method must reproduce."""
+    D1 = np.asarray(D1, np.float64)
+    D2 = np.asarray(D2, np.float64)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        g = (D2 - D1) / D1
+    g = np.where(D1 == 0, np.where(D2 > 0, np.inf, 0.0), g)
+    return g

@@ -1,0 +1,239 @@
+/*
+ * fp64 CPU oracle for one exact Lloyd k-means iteration.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
+ * calls this file; only the tests, the smoke check and the CPU-baseline leg
+ * of the benchmark do.  It shares no code, header or constant with the HIP
+ * library.
+ *
+ * What it computes is the plain definition of a Lloyd iteration, which the
+ * Flash-KMeans article (lumevalley.com, article 3696) says its two kernels
+ * reach exactly, with no approximation:
+ *   - section "Why being fast took so long" (为什么"快"这件事被拖了这么久):
+ *     an iteration assigns each of N points to one of K clusters using the
+ *     N x K distances, then reduce-sums the points of each cluster and
+ *     divides by the cluster size;
+ *   - section "Two kernels rewrite the GPU pipeline" (两个 Kernel，重写了 GPU
+ *     流水线): the maths of k-means is left as it is and nothing is
+ *     approximated; only the data flow on the GPU changes.
+ * The metric is squared Euclidean distance; cosine is handled by
+ * L2-normalising every vector first, a zero norm being replaced by 1 before
+ * the divide (LEANN FlashLib backend guide, mhpn.cn, paragraph
+ * "距离度量" (distance metric)).
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *   - ties in the minimum distance go to the lowest centroid index;
+ *   - a cluster that receives no point keeps the centroid it was given;
+ *   - distances are taken by direct difference, sum_j (x_j - c_j)^2, in
+ *     fp64, accumulated in increasing j; inputs are fp32 and are promoted to
+ *     fp64 exactly;
+ *   - cluster sums are accumulated in fp64 in increasing point index.
+ *
+ * Build: gcc -O2 -fno-fast-math -ffp-contract=off -fopenmp -fPIC -shared.
+ * Points are independent in the assignment, so the OpenMP split over points
+ * does not change any result.
+ */
+#include <math.h>
+#include <omp.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define FKO_METRIC_L2 0
+#define FKO_METRIC_COSINE 1
+
+/* Promote one fp32 row to fp64; for cosine divide it by its L2 norm, the
+ * norm being taken as 1 when it is 0 (FlashLib guide, "距离度量"). */
+static void promote_row(const float *src, int64_t d, int metric, double *dst)
+{
+    for (int64_t j = 0; j < d; ++j)
+        dst[j] = (double)src[j];
+    if (metric == FKO_METRIC_COSINE) {
+        double s = 0.0;
+        for (int64_t j = 0; j < d; ++j)
+            s = s + dst[j] * dst[j];
+        double n = sqrt(s);
+        if (n == 0.0)
+            n = 1.0;
+        for (int64_t j = 0; j < d; ++j)
+            dst[j] = dst[j] / n;
+    }
+}
+
+/* Squared Euclidean distance by direct difference, in increasing j. */
+static double sqdist(const double *x, const double *c, int64_t d)
+{
+    double acc = 0.0;
+    for (int64_t j = 0; j < d; ++j) {
+        double t = x[j] - c[j];
+        acc = acc + t * t;
+    }
+    return acc;
+}
+
+/* Rows of C promoted (and, for cosine, normalised) once.  Returns NULL on
+ * allocation failure. */
+static double *promote_matrix(const float *M, int64_t rows, int64_t d, int metric)
+{
+    double *out = (double *)malloc((size_t)(rows > 0 ? rows : 1) * (size_t)(d > 0 ? d : 1) * sizeof(double));
+    if (!out)
+        return NULL;
+    for (int64_t r = 0; r < rows; ++r)
+        promote_row(M + r * d, d, metric, out + r * d);
+    return out;
+}
+
+/*
+ * Assignment step.  For every point i:
+ *   D_ik = ||x_i - c_k||^2 for all k,
+ *   a_i  = smallest k attaining min_k D_ik,
+ *   D1_i = D_{i,a_i},
+ *   D2_i = min over k != a_i of D_ik (+inf when K == 1).
+ * Any of a, D1, D2 may be NULL.  Returns 0, or -1 on bad arguments or
+ * allocation failure.
+ */
+int fko_assign(const float *X, int64_t N, int64_t d, const float *C, int64_t K,
+               int metric, int32_t *a, double *D1, double *D2)
+{
+    if (N < 0 || d <= 0 || K <= 0 || (N > 0 && !X) || !C)
+        return -1;
+    if (metric != FKO_METRIC_L2 && metric != FKO_METRIC_COSINE)
+        return -1;
+    double *Cd = promote_matrix(C, K, d, metric);
+    if (!Cd)
+        return -1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *xi = (double *)malloc((size_t)d * sizeof(double));
+        if (!xi) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < N; ++i) {
+            if (!xi)
+                continue;
+            promote_row(X + i * d, d, metric, xi);
+            int64_t best_k = 0;
+            double best = sqdist(xi, Cd, d);
+            double second = INFINITY;
+            for (int64_t k = 1; k < K; ++k) {
+                double D = sqdist(xi, Cd + k * d, d);
+                if (D < best) {
+                    second = best;
+                    best = D;
+                    best_k = k;
+                } else if (D < second) {
+                    second = D;
+                }
+            }
+            if (a)
+                a[i] = (int32_t)best_k;
+            if (D1)
+                D1[i] = best;
+            if (D2)
+                D2[i] = second;
+        }
+        free(xi);
+    }
+    free(Cd);
+    return failed ? -1 : 0;
+}
+
+/*
+ * Update step.  n_k = #{i : a_i = k}; s_k = sum of x_i over those i, in
+ * increasing i, in fp64; C_out[k] = s_k / n_k, or C_in[k] (as passed, not
+ * normalised) when n_k == 0.  Returns 0, or -1 on bad arguments (including a
+ * label outside [0, K)) or allocation failure.
+ */
+int fko_update(const float *X, int64_t N, int64_t d, const int32_t *a, int64_t K,
+               int metric, const float *C_in, double *C_out, int64_t *counts)
+{
+    if (N < 0 || d <= 0 || K <= 0 || (N > 0 && (!X || !a)) || !C_in || !C_out || !counts)
+        return -1;
+    if (metric != FKO_METRIC_L2 && metric != FKO_METRIC_COSINE)
+        return -1;
+    for (int64_t i = 0; i < N; ++i)
+        if (a[i] < 0 || (int64_t)a[i] >= K)
+            return -1;
+    double *xi = (double *)malloc((size_t)d * sizeof(double));
+    if (!xi)
+        return -1;
+    memset(C_out, 0, (size_t)K * (size_t)d * sizeof(double));
+    memset(counts, 0, (size_t)K * sizeof(int64_t));
+    for (int64_t i = 0; i < N; ++i) {
+        int64_t k = a[i];
+        promote_row(X + i * d, d, metric, xi);
+        counts[k] += 1;
+        double *s = C_out + k * d;
+        for (int64_t j = 0; j < d; ++j)
+            s[j] = s[j] + xi[j];
+    }
+    for (int64_t k = 0; k < K; ++k) {
+        double *s = C_out + k * d;
+        if (counts[k] > 0) {
+            double n = (double)counts[k];
+            for (int64_t j = 0; j < d; ++j)
+                s[j] = s[j] / n;
+        } else {
+            for (int64_t j = 0; j < d; ++j)
+                s[j] = (double)C_in[k * d + j];
+        }
+    }
+    free(xi);
+    return 0;
+}
+
+/*
+ * One full iteration from C_in: assignment, then update, then the objective
+ * J = sum_i D1_i under C_in (summed in increasing i).  a, D1, D2 are
+ * optional outputs; C_out and counts are required.
+ */
+int fko_lloyd_iter(const float *X, int64_t N, int64_t d, const float *C_in, int64_t K,
+                   int metric, int32_t *a, double *D1, double *D2, double *C_out,
+                   int64_t *counts, double *J)
+{
+    if (N < 0)
+        return -1;
+    int32_t *a_use = a;
+    double *d1_use = D1;
+    int32_t *a_own = NULL;
+    double *d1_own = NULL;
+    if (!a_use) {
+        a_own = (int32_t *)malloc((size_t)(N > 0 ? N : 1) * sizeof(int32_t));
+        a_use = a_own;
+    }
+    if (!d1_use) {
+        d1_own = (double *)malloc((size_t)(N > 0 ? N : 1) * sizeof(double));
+        d1_use = d1_own;
+    }
+    int rc = -1;
+    if (a_use && d1_use) {
+        rc = fko_assign(X, N, d, C_in, K, metric, a_use, d1_use, D2);
+        if (rc == 0)
+            rc = fko_update(X, N, d, a_use, K, metric, C_in, C_out, counts);
+        if (rc == 0 && J) {
+            double s = 0.0;
+            for (int64_t i = 0; i < N; ++i)
+                s = s + d1_use[i];
+            *J = s;
+        }
+    }
+    free(a_own);
+    free(d1_own);
+    return rc;
+}
+
+/* Number of OpenMP threads the assignment step will use. */
+int fko_num_threads(void)
+{
+    int n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}

@@ -1,0 +1,301 @@
+"""Pins for the fp64 oracle: each test checks it against something that does
+not share its code -- a hand-worked example, exact rational arithmetic, a
+closed form, a library routine, or an invariant of the mathematics -- chosen
+so that a dropped term, a wrong sign or index, or a transposed operand in the
+oracle fails at least one of them.  All run on the CPU."""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import scipy.cluster.vq
+import scipy.spatial.distance
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- worked examples
+
+def test_hand_worked_l2_example():
+    g = _golden("hand_2d_l2.json")
+    X = np.array(g["X"], np.float32)
+    C = np.array(g["C"], np.float32)
+    r = oracle.lloyd_iter(X, C, "l2")
+    assert r["a"].tolist() == g["a"]
+    assert r["D1"].tolist() == g["D1"]
+    assert r["D2"].tolist() == g["D2"]
+    assert r["counts"].tolist() == g["counts"]
+    assert r["C"].tolist() == g["C_new"]
+    assert r["J"] == g["J"]
+
+
+def test_hand_worked_cosine_example():
+    g = _golden("hand_2d_cosine.json")
+    X = np.array(g["X"], np.float32)
+    C = np.array(g["C"], np.float32)
+    r = oracle.lloyd_iter(X, C, "cosine")
+    assert r["a"].tolist() == g["a"]
+    np.testing.assert_allclose(r["D1"], g["D1"], rtol=0, atol=1e-15)
+    assert r["counts"].tolist() == g["counts"]
+    np.testing.assert_allclose(r["C"], np.array(g["C_new"]), rtol=0, atol=1e-15)
+
+
+# ---------------------------------------------------------------- assignment
+
+def _second_smallest(D):
+    if D.shape[1] == 1:
+        return np.full(D.shape[0], np.inf)
+    return np.partition(D, 1, axis=1)[:, 1]
+
+
+@pytest.mark.parametrize("N,d,K,seed", [(200, 5, 7, 0), (300, 16, 64, 1), (50, 1, 3, 2), (97, 33, 1, 3), (64, 128, 40, 4)])
+def test_assign_matches_cdist_bruteforce(N, d, K, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((N, d)).astype(np.float32)
+    C = rng.standard_normal((K, d)).astype(np.float32)
+    a, D1, D2 = oracle.assign(X, C)
+    D = scipy.spatial.distance.cdist(X.astype(np.float64), C.astype(np.float64), "sqeuclidean")
+    np.testing.assert_array_equal(a, np.argmin(D, axis=1))
+    np.testing.assert_allclose(D1, D.min(axis=1), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(D2, _second_smallest(D), rtol=1e-12, atol=1e-12)
+    # scipy's vector quantiser is a second, independent argmin
+    code, dist = scipy.cluster.vq.vq(X.astype(np.float64), C.astype(np.float64), check_finite=True)
+    np.testing.assert_array_equal(a, code)
+    np.testing.assert_allclose(np.sqrt(D1), dist, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_assign_exact_integers_with_planted_ties(seed):
+    """Small-integer data: every fp64 operation of the oracle is exact, so its
+    distances must equal exact integer arithmetic, and ties must go to the
+    lowest index."""
+    rng = np.random.default_rng([seed, 11])
+    N, d, K = 60, 4, 9
+    X = rng.integers(-3, 4, size=(N, d))
+    C = rng.integers(-3, 4, size=(K, d))
+    C[5] = C[2]            # duplicated centroid: exact ties everywhere it is nearest
+    C[8] = C[0]
+    a, D1, D2 = oracle.assign(X.astype(np.float32), C.astype(np.float32))
+    nties = 0
+    for i in range(N):
+        D = [sum(Fraction(int(X[i, j] - C[k, j])) ** 2 for j in range(d)) for k in range(K)]
+        m = min(D)
+        k_best = D.index(m)          # lowest index attaining the minimum
+        rest = D[:k_best] + D[k_best + 1:]
+        assert a[i] == k_best
+        assert D1[i] == float(m)
+        assert D2[i] == float(min(rest))
+        nties += D.count(m) > 1
+    assert nties > 0
+
+
+def test_assign_one_dimensional_voronoi_closed_form():
+    """In 1-D with sorted centroids, the cell boundaries are the midpoints;
+    points exactly on a midpoint go to the lower index."""
+    c = np.array([-8.0, -2.0, 0.0, 4.0, 10.0, 16.0], np.float32)   # midpoints -5,-1,2,7,13
+    mids = (c[:-1] + c[1:]) / 2
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.uniform(-20, 25, 400), mids, mids + 0.5, mids - 0.5]).astype(np.float32)
+    a, _, _ = oracle.assign(x[:, None], c[:, None])
+    expect = np.searchsorted(mids, x, side="left")
+    np.testing.assert_array_equal(a, expect)
+
+
+def test_assign_self_assignment():
+    rng = np.random.default_rng(6)
+    X = rng.standard_normal((500, 12)).astype(np.float32)
+    S = rng.choice(500, 37, replace=False)
+    a, D1, _ = oracle.assign(X, X[S])
+    np.testing.assert_array_equal(a[S], np.arange(37))
+    assert np.all(D1[S] == 0.0)
+    assert np.all(D1 >= 0.0)
+
+
+def test_assign_order_of_operands_matters_not():
+    """D is symmetric in the difference: swapping the roles of a single point
+    and a single centroid gives the same distance (guards a transposed
+    operand in the row/column indexing)."""
+    rng = np.random.default_rng(7)
+    X = rng.standard_normal((30, 7)).astype(np.float32)
+    C = rng.standard_normal((11, 7)).astype(np.float32)
+    _, D1, _ = oracle.assign(X, C)
+    a, _, _ = oracle.assign(X, C)
+    for i in range(30):
+        _, d_back, _ = oracle.assign(C[a[i]:a[i] + 1], X[i:i + 1])
+        assert d_back[0] == D1[i]
+
+
+# ---------------------------------------------------------------- update
+
+@pytest.mark.parametrize("seed", range(3))
+def test_update_exact_rational_means(seed):
+    rng = np.random.default_rng([seed, 12])
+    N, d, K = 80, 3, 6
+    X = rng.integers(-50, 51, size=(N, d))
+    a = rng.integers(0, K - 1, size=N).astype(np.int32)     # cluster K-1 stays empty
+    C_in = rng.standard_normal((K, d)).astype(np.float32)
+    C, counts = oracle.update(X.astype(np.float32), a, C_in)
+    for k in range(K):
+        members = X[a == k]
+        assert counts[k] == len(members)
+        for j in range(d):
+            if len(members):
+                assert C[k, j] == float(Fraction(int(members[:, j].sum()), len(members)))
+            else:
+                assert C[k, j] == float(C_in[k, j])
+    assert counts.sum() == N
+
+
+def test_update_k1_is_global_mean():
+    rng = np.random.default_rng(13)
+    X = rng.standard_normal((1000, 9)).astype(np.float32)
+    C, counts = oracle.update(X, np.zeros(1000, np.int32), np.zeros((1, 9), np.float32))
+    assert counts.tolist() == [1000]
+    exact = [float(sum(Fraction(float(v)) for v in X[:, j]) / 1000) for j in range(9)]
+    np.testing.assert_allclose(C[0], exact, rtol=1e-13, atol=1e-15)
+
+
+@pytest.mark.parametrize("metric", ["l2", "cosine"])
+def test_update_matches_add_at(metric):
+    rng = np.random.default_rng(14)
+    N, d, K = 2000, 17, 50
+    X = rng.standard_normal((N, d)).astype(np.float32)
+    X[::97] = 0.0
+    a = rng.integers(0, K, size=N).astype(np.int32)
+    a[a == 7] = 8            # cluster 7 empty
+    C_in = rng.standard_normal((K, d)).astype(np.float32)
+    C, counts = oracle.update(X, a, C_in, metric)
+    Xd = X.astype(np.float64)
+    if metric == "cosine":
+        n = np.linalg.norm(Xd, axis=1, keepdims=True)
+        n[n == 0] = 1.0
+        Xd = Xd / n
+    sums = np.zeros((K, d))
+    np.add.at(sums, a, Xd)
+    cnt = np.bincount(a, minlength=K)
+    np.testing.assert_array_equal(counts, cnt)
+    expect = np.where(cnt[:, None] > 0, sums / np.maximum(cnt, 1)[:, None], C_in.astype(np.float64))
+    np.testing.assert_allclose(C, expect, rtol=1e-12, atol=1e-14)
+    assert C[7].tolist() == C_in[7].astype(np.float64).tolist()
+
+
+def test_update_rejects_out_of_range_labels():
+    X = np.zeros((4, 2), np.float32)
+    with pytest.raises(ValueError):
+        oracle.update(X, np.array([0, 1, 2, 3], np.int32), np.zeros((3, 2), np.float32))
+    with pytest.raises(ValueError):
+        oracle.update(X, np.array([0, -1, 0, 0], np.int32), np.zeros((3, 2), np.float32))
+
+
+def test_one_iteration_matches_sklearn_lloyd():
+    """scikit-learn's Lloyd k-means, run for exactly one iteration from the
+    same centroids, is an independent implementation of the same step."""
+    from sklearn.cluster import KMeans
+    w = synth.WORKLOADS["gmm_1m_d128_k1024"]
+    X = synth.rows(w.scaled(20000), threads=1)[:, :16].copy()
+    rng = np.random.default_rng(15)
+    C0 = X[rng.choice(len(X), 24, replace=False)]
+    r = oracle.lloyd_iter(X, C0)
+    assert r["counts"].min() > 0          # sklearn would relocate an empty cluster
+    km = KMeans(n_clusters=24, init=C0.astype(np.float64), n_init=1, max_iter=1, algorithm="lloyd", tol=0.0)
+    km.fit(X.astype(np.float64))
+    np.testing.assert_allclose(r["C"], km.cluster_centers_, rtol=1e-9, atol=1e-11)
+
+
+# ---------------------------------------------------------------- iteration
+
+def test_objective_non_increasing_and_counts_sum_to_n():
+    w = synth.WORKLOADS["zipf_16m_d128_k32768"]
+    X = synth.rows(w.scaled(6000), threads=1)[:, :8].copy()
+    rng = np.random.default_rng(16)
+    C = X[rng.choice(len(X), 40, replace=False)]
+    Js = []
+    for _ in range(15):
+        r = oracle.lloyd_iter(X, C)
+        assert r["counts"].sum() == len(X)
+        Js.append(r["J"])
+        C = r["C"].astype(np.float32)
+    for j0, j1 in zip(Js, Js[1:]):
+        assert j1 <= j0 * (1 + 1e-6)
+    assert Js[-1] < Js[0]
+
+
+def test_fixed_point_on_planted_separated_clusters():
+    rng = np.random.default_rng(17)
+    K, d = 6, 5
+    centers = rng.standard_normal((K, d)) * 50
+    labels = rng.integers(0, K, size=600)
+    X = (centers[labels] + rng.standard_normal((600, d)) * 0.1).astype(np.float32)
+    C = X[[np.nonzero(labels == k)[0][0] for k in range(K)]]
+    for _ in range(3):
+        r = oracle.lloyd_iter(X, C)
+        C = r["C"].astype(np.float32)
+    np.testing.assert_array_equal(r["a"], labels)
+    r2 = oracle.lloyd_iter(X, C)
+    np.testing.assert_array_equal(r2["a"], labels)
+    np.testing.assert_allclose(r2["C"], r["C"], rtol=1e-7, atol=1e-6)
+
+
+def test_row_permutation_invariance():
+    rng = np.random.default_rng(18)
+    X = rng.standard_normal((700, 6)).astype(np.float32)
+    C = X[:20].copy()
+    perm = rng.permutation(700)
+    r = oracle.lloyd_iter(X, C)
+    rp = oracle.lloyd_iter(X[perm], C)
+    np.testing.assert_array_equal(rp["a"], r["a"][perm])
+    np.testing.assert_array_equal(rp["counts"], r["counts"])
+    np.testing.assert_allclose(rp["C"], r["C"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(rp["J"], r["J"], rtol=1e-12)
+
+
+# ---------------------------------------------------------------- cosine
+
+def test_cosine_equals_inner_product_on_unit_centroids():
+    """On unit vectors, squared L2 order equals inner-product order."""
+    rng = np.random.default_rng(19)
+    X = rng.standard_normal((400, 10)).astype(np.float32) * 3
+    C = rng.standard_normal((15, 10))
+    C = (C / np.linalg.norm(C, axis=1, keepdims=True)).astype(np.float32)
+    a, D1, D2 = oracle.assign(X, C, "cosine")
+    S = X.astype(np.float64) @ C.astype(np.float64).T
+    ok = oracle.relative_gap(D1, D2) > 1e-9
+    np.testing.assert_array_equal(a[ok], np.argmax(S, axis=1)[ok])
+    # and squared distances of unit vectors are 2 - 2 cos
+    cos = S / np.linalg.norm(X.astype(np.float64), axis=1, keepdims=True)
+    Cn = C.astype(np.float64) / np.linalg.norm(C.astype(np.float64), axis=1, keepdims=True)
+    cos = (X.astype(np.float64) / np.linalg.norm(X.astype(np.float64), axis=1, keepdims=True)) @ Cn.T
+    np.testing.assert_allclose(D1, 2 - 2 * cos.max(axis=1), rtol=0, atol=1e-12)
+
+
+def test_cosine_scale_invariance_and_zero_rows():
+    rng = np.random.default_rng(20)
+    X = rng.standard_normal((300, 8)).astype(np.float32)
+    X[::10] = 0.0
+    C = rng.standard_normal((12, 8)).astype(np.float32)
+    a1, D1, _ = oracle.assign(X, C, "cosine")
+    a2, _, _ = oracle.assign(X * np.float32(4.0), C * np.float32(0.5), "cosine")
+    np.testing.assert_array_equal(a1, a2)
+    # a zero row stays zero, so it is at distance ||c^||^2 = 1 (to rounding)
+    # from every normalised centroid
+    np.testing.assert_allclose(D1[::10], 1.0, rtol=0, atol=1e-15)
+    # with centroids that normalise exactly (scaled axis vectors) that is an
+    # exact tie, which goes to centroid 0
+    Cax = (np.eye(8, dtype=np.float32) * np.arange(1, 9, dtype=np.float32)[:, None])[::-1].copy()
+    a3, D13, D23 = oracle.assign(X, Cax, "cosine")
+    assert np.all(a3[::10] == 0)
+    assert np.all(D13[::10] == 1.0) and np.all(D23[::10] == 1.0)
+
+
+def test_relative_gap_definition():
+    g = oracle.relative_gap(np.array([1.0, 0.0, 0.0, 2.0]), np.array([1.5, 0.0, 3.0, 2.0]))
+    assert g[0] == 0.5 and g[1] == 0.0 and np.isinf(g[2]) and g[3] == 0.0
