@@ -1,0 +1,568 @@
+// Host side of libfk: argument validation, workspace carving, phase
+// sequencing on the caller's stream, the out-of-core chunk pipeline, and
+// phase timing.  Declared in include/fk.h.
+#include <mutex>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+#include <vector>
+
+#include "fk.h"
+#include "fk_internal.h"
+
+using namespace fk;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+fk_status fail(fk_status s, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+fk_status hip_fail(hipError_t e, const char *what) {
+    (void)hipGetLastError();
+    return fail(FK_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define FK_TRY(expr, what)                                  \
+    do {                                                    \
+        hipError_t e_ = (expr);                             \
+        if (e_ != hipSuccess) return hip_fail(e_, (what));  \
+    } while (0)
+
+// ---- workspace layout -----------------------------------------------------
+struct Layout {
+    size_t total = 0;
+    size_t ncn, cmax_part, scal, counter, flags;
+    size_t c64, c32, cnrm64, xnorm64;  // cosine only (else ~0)
+    size_t keys_sorted, perm, tmp_keys, tmp_vals, sort_scratch, offsets;
+    size_t sums, cnt, pfirst, plast;
+    size_t xchunk[2], achunk[2];      // out-of-core only
+};
+
+constexpr size_t kNone = ~(size_t)0;
+
+Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc) {
+    Layout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes > 0 ? bytes : 1, 256);
+        return o;
+    };
+    const int64_t r = rows > 0 ? rows : 1;
+    const int64_t Kpad = cdiv(K, kCentroidPad) * kCentroidPad;
+    const int64_t nseg = cdiv(r, kSegRows);
+    const bool cos = metric == FK_METRIC_COSINE;
+    L.ncn = take((size_t)Kpad * 4);
+    L.cmax_part = take((size_t)cdiv(Kpad, 4) * 4);
+    L.scal = take(64);
+    L.counter = take(64);
+    L.flags = take((size_t)r * 4);
+    L.c64 = cos ? take((size_t)K * d * 8) : kNone;
+    L.c32 = cos ? take((size_t)K * d * 4) : kNone;
+    L.cnrm64 = cos ? take((size_t)K * 8) : kNone;
+    L.xnorm64 = cos ? take((size_t)r * 8) : kNone;
+    L.keys_sorted = take((size_t)r * 4);
+    L.perm = take((size_t)r * 4);
+    L.tmp_keys = take((size_t)r * 4);
+    L.tmp_vals = take((size_t)r * 4);
+    L.sort_scratch = take(sort_scratch_bytes(r));
+    L.offsets = take((size_t)(K + 1) * 4);
+    L.sums = take((size_t)K * d * 8);
+    L.cnt = take((size_t)K * 4);
+    L.pfirst = take((size_t)nseg * d * 8);
+    L.plast = take((size_t)nseg * d * 8);
+    for (int i = 0; i < 2; ++i) {
+        L.xchunk[i] = ooc ? take((size_t)r * d * 4) : kNone;
+        L.achunk[i] = ooc ? take((size_t)r * 4) : kNone;
+    }
+    L.total = off;
+    return L;
+}
+
+template <typename T>
+T *at(void *ws, size_t off) {
+    return off == kNone ? nullptr : reinterpret_cast<T *>(static_cast<char *>(ws) + off);
+}
+
+// ---- validation -----------------------------------------------------------
+fk_status check_sizes(int64_t N, int64_t d, int64_t K) {
+    if (N < 0 || N > INT32_MAX) return fail(FK_ERR_INVALID_ARG, "N=%lld outside [0, 2^31-1]", (long long)N);
+    if (d < 1 || d > FK_MAX_D) return fail(FK_ERR_INVALID_ARG, "d=%lld outside [1, %d]", (long long)d, FK_MAX_D);
+    if (K < 1 || K > FK_MAX_K) return fail(FK_ERR_INVALID_ARG, "K=%lld outside [1, %d]", (long long)K, FK_MAX_K);
+    return FK_OK;
+}
+
+fk_status check_metric(int32_t metric) {
+    if (metric == FK_METRIC_INNER_PRODUCT)
+        return fail(FK_ERR_UNSUPPORTED, "the inner-product metric is not supported (L2 and cosine are)");
+    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE)
+        return fail(FK_ERR_INVALID_ARG, "unknown metric %d", (int)metric);
+    return FK_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlap(const void *a, size_t an, const void *b, size_t bn) {
+    const char *pa = (const char *)a, *pb = (const char *)b;
+    return pa < pb + bn && pb < pa + an;
+}
+
+fk_status check_workspace(void *ws, size_t ws_bytes, size_t need) {
+    if (ws == nullptr) return fail(FK_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(ws, 256)) return fail(FK_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < need) return fail(FK_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", ws_bytes, need);
+    return FK_OK;
+}
+
+fk_status check_device() {
+    int n = 0;
+    const hipError_t e = hipGetDeviceCount(&n);
+    if (e != hipSuccess || n <= 0) {
+        (void)hipGetLastError();
+        return fail(FK_ERR_NO_DEVICE, "no HIP device is visible");
+    }
+    return FK_OK;
+}
+
+// ---- phase timing -----------------------------------------------------------
+struct Pending {
+    int phase;
+    hipEvent_t a, b;
+};
+
+struct Prof {
+    std::mutex mu;
+    bool on = false;
+    std::vector<hipEvent_t> pool;
+    std::vector<Pending> pending;
+    std::vector<int32_t *> count_slots;  // pinned host slots receiving near-tie counts
+    size_t slots_used = 0;
+    fk_profile acc{};
+};
+Prof g_prof;
+
+hipEvent_t prof_event() {
+    if (!g_prof.pool.empty()) {
+        hipEvent_t e = g_prof.pool.back();
+        g_prof.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+struct PhaseScope {
+    int phase;
+    hipStream_t s;
+    hipEvent_t a = nullptr, b = nullptr;
+    PhaseScope(int ph, hipStream_t st) : phase(ph), s(st) {
+        std::lock_guard<std::mutex> g(g_prof.mu);
+        if (!g_prof.on) return;
+        a = prof_event();
+        b = prof_event();
+        if (a && b) (void)hipEventRecord(a, s);
+    }
+    ~PhaseScope() {
+        if (!a || !b) return;
+        std::lock_guard<std::mutex> g(g_prof.mu);
+        (void)hipEventRecord(b, s);
+        g_prof.pending.push_back({phase, a, b});
+    }
+};
+
+void prof_count_rechecks(const int32_t *dev_counter, int64_t n_assigned, hipStream_t s) {
+    std::lock_guard<std::mutex> g(g_prof.mu);
+    if (!g_prof.on) return;
+    if (g_prof.slots_used == g_prof.count_slots.size()) {
+        int32_t *h = nullptr;
+        if (hipHostMalloc((void **)&h, sizeof(int32_t)) != hipSuccess) return;
+        g_prof.count_slots.push_back(h);
+    }
+    int32_t *slot = g_prof.count_slots[g_prof.slots_used++];
+    *slot = 0;
+    (void)hipMemcpyAsync(slot, dev_counter, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    g_prof.acc.assigned += n_assigned;
+}
+
+// ---- the steps --------------------------------------------------------------
+struct Ctx {
+    const Layout &L;
+    void *ws;
+    hipStream_t s;
+    int d, K, metric;
+};
+
+// Centroid norms (and, for cosine, the normalised centroids).  Returns the
+// centroid array the MFMA kernel reads.
+fk_status step_prep(const Ctx &c, const float *C, const float **C_use) {
+    PhaseScope ph(FK_PH_PREP, c.s);
+    const float *Cu = C;
+    if (c.metric == FK_METRIC_COSINE) {
+        FK_TRY(launch_row_norm64(C, c.K, c.d, at<double>(c.ws, c.L.cnrm64), c.s), "centroid norms");
+        FK_TRY(launch_normalize_rows(C, c.K, c.d, at<double>(c.ws, c.L.cnrm64), at<double>(c.ws, c.L.c64),
+                                     at<float>(c.ws, c.L.c32), c.s),
+               "centroid normalisation");
+        Cu = at<float>(c.ws, c.L.c32);
+    }
+    int nparts = 0;
+    FK_TRY(launch_centroid_prep(Cu, c.K, c.d, at<float>(c.ws, c.L.ncn), at<float>(c.ws, c.L.cmax_part), &nparts,
+                                c.s),
+           "centroid prep");
+    FK_TRY(launch_prep_finish(at<float>(c.ws, c.L.cmax_part), nparts, at<float>(c.ws, c.L.scal),
+                              at<int32_t>(c.ws, c.L.counter), c.s),
+           "centroid prep finish");
+    *C_use = Cu;
+    return FK_OK;
+}
+
+fk_status step_xnorm(const Ctx &c, const float *X, int64_t rows) {
+    if (c.metric != FK_METRIC_COSINE) return FK_OK;
+    PhaseScope ph(FK_PH_PREP, c.s);
+    FK_TRY(launch_row_norm64(X, rows, c.d, at<double>(c.ws, c.L.xnorm64), c.s), "point norms");
+    return FK_OK;
+}
+
+// FlashAssign + fp64 recheck of the listed near-tie points.  Needs step_prep
+// (and step_xnorm for cosine) first; resets nothing itself except that
+// step_prep zeroed the near-tie counter.
+fk_status step_assign(const Ctx &c, const float *X, int64_t rows, const float *C, const float *C_use,
+                      int32_t *a_out, float *d1_out) {
+    const double *xn = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.xnorm64) : nullptr;
+    {
+        PhaseScope ph(FK_PH_ASSIGN, c.s);
+        FK_TRY(launch_flash_assign(X, rows, c.d, C_use, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal),
+                                   xn, a_out, d1_out, at<int32_t>(c.ws, c.L.flags), at<int32_t>(c.ws, c.L.counter),
+                                   c.s),
+               "flash assign");
+    }
+    {
+        PhaseScope ph(FK_PH_RECHECK, c.s);
+        const double *c64 = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.c64) : nullptr;
+        FK_TRY(launch_recheck(X, rows, c.d, C, c64, c.K, xn, at<int32_t>(c.ws, c.L.flags),
+                              at<int32_t>(c.ws, c.L.counter), a_out, d1_out, c.s),
+               "fp64 recheck");
+    }
+    prof_count_rechecks(at<int32_t>(c.ws, c.L.counter), rows, c.s);
+    return FK_OK;
+}
+
+// Inverse index of `a` into the workspace (keys_sorted, perm, offsets), or
+// into caller arrays when given.
+fk_status step_sort(const Ctx &c, const int32_t *a, int64_t rows, int32_t *perm_out, int32_t *offsets_out) {
+    PhaseScope ph(FK_PH_SORT, c.s);
+    int32_t *perm = perm_out ? perm_out : at<int32_t>(c.ws, c.L.perm);
+    int32_t *offs = offsets_out ? offsets_out : at<int32_t>(c.ws, c.L.offsets);
+    FK_TRY(launch_sort_by_key(a, rows, c.K, at<int32_t>(c.ws, c.L.keys_sorted), perm,
+                              at<int32_t>(c.ws, c.L.tmp_keys), at<int32_t>(c.ws, c.L.tmp_vals),
+                              at<void>(c.ws, c.L.sort_scratch), c.s),
+           "radix sort");
+    FK_TRY(launch_offsets(at<int32_t>(c.ws, c.L.keys_sorted), rows, c.K, offs, c.s), "cluster offsets");
+    return FK_OK;
+}
+
+fk_status step_zero_accumulators(const Ctx &c) {
+    PhaseScope ph(FK_PH_REDUCE, c.s);
+    FK_TRY(launch_fill_zero(at<void>(c.ws, c.L.sums), (size_t)c.K * c.d * 8, c.s), "zero sums");
+    FK_TRY(launch_fill_zero(at<void>(c.ws, c.L.cnt), (size_t)c.K * 4, c.s), "zero counts");
+    return FK_OK;
+}
+
+// Sort-Inverse accumulation of `rows` rows into the fp64 sums and counts.
+fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int32_t *a) {
+    if (rows <= 0) return FK_OK;
+    fk_status st = step_sort(c, a, rows, nullptr, nullptr);
+    if (st != FK_OK) return st;
+    PhaseScope ph(FK_PH_REDUCE, c.s);
+    const double *xn = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.xnorm64) : nullptr;
+    FK_TRY(launch_seg_reduce(X, rows, c.d, at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.perm), xn,
+                             at<double>(c.ws, c.L.sums), at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast),
+                             c.s),
+           "segmented reduction");
+    FK_TRY(launch_seg_fixup(at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.offsets), rows, c.d,
+                            at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast), at<double>(c.ws, c.L.sums),
+                            c.s),
+           "segment fix-up");
+    FK_TRY(launch_count_accumulate(at<int32_t>(c.ws, c.L.offsets), c.K, at<int32_t>(c.ws, c.L.cnt), c.s),
+           "count accumulate");
+    return FK_OK;
+}
+
+fk_status step_finalize(const Ctx &c, const float *C_prev, float *C_out, int32_t *counts) {
+    PhaseScope ph(FK_PH_FINALIZE, c.s);
+    FK_TRY(launch_finalize(at<double>(c.ws, c.L.sums), at<int32_t>(c.ws, c.L.cnt), C_prev, c.K, c.d, C_out, counts,
+                           c.s),
+           "finalize");
+    return FK_OK;
+}
+
+fk_status check_common(const float *X, int64_t N, int32_t d, const void *C, int32_t K, int32_t metric) {
+    fk_status st = check_sizes(N, d, K);
+    if (st != FK_OK) return st;
+    if ((st = check_metric(metric)) != FK_OK) return st;
+    if (N > 0 && X == nullptr) return fail(FK_ERR_INVALID_ARG, "X is NULL");
+    if (C == nullptr) return fail(FK_ERR_INVALID_ARG, "centroid array is NULL");
+    if (X != nullptr && !aligned(X, 16)) return fail(FK_ERR_INVALID_ARG, "X must be 16-byte aligned");
+    if (!aligned(C, 16)) return fail(FK_ERR_INVALID_ARG, "centroids must be 16-byte aligned");
+    return FK_OK;
+}
+
+}  // namespace
+
+// ============================================================================
+extern "C" {
+
+size_t fk_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric, int64_t chunk_rows) {
+    if (N < 0 || N > INT32_MAX || d < 1 || d > FK_MAX_D || K < 1 || K > FK_MAX_K) return 0;
+    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE) return 0;
+    if (chunk_rows < 0 || chunk_rows > INT32_MAX) return 0;
+    const bool ooc = chunk_rows > 0;
+    return make_layout(ooc ? chunk_rows : N, d, K, metric, ooc).total;
+}
+
+const char *fk_status_str(int32_t s) {
+    switch (s) {
+    case FK_OK: return "FK_OK";
+    case FK_ERR_INVALID_ARG: return "FK_ERR_INVALID_ARG";
+    case FK_ERR_UNSUPPORTED: return "FK_ERR_UNSUPPORTED";
+    case FK_ERR_WORKSPACE: return "FK_ERR_WORKSPACE";
+    case FK_ERR_NO_DEVICE: return "FK_ERR_NO_DEVICE";
+    case FK_ERR_HIP: return "FK_ERR_HIP";
+    default: return "FK_ERR_UNKNOWN";
+    }
+}
+
+const char *fk_last_error(void) { return g_err; }
+
+fk_status fk_assign(const float *X, int64_t N, int32_t d, const float *C, int32_t K, int32_t metric, int32_t *assign,
+                    float *min_dist, void *workspace, size_t workspace_bytes, void *stream) {
+    g_err[0] = 0;
+    fk_status st = check_common(X, N, d, C, K, metric);
+    if (st != FK_OK) return st;
+    if (N > 0 && assign == nullptr) return fail(FK_ERR_INVALID_ARG, "assign is NULL");
+    const Layout L = make_layout(N, d, K, metric, false);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
+    if ((st = check_device()) != FK_OK) return st;
+    if (N == 0) return FK_OK;
+    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric};
+    const float *Cu = nullptr;
+    if ((st = step_prep(c, C, &Cu)) != FK_OK) return st;
+    if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
+    return step_assign(c, X, N, C, Cu, assign, min_dist);
+}
+
+fk_status fk_sort_inverse(const int32_t *assign, int64_t N, int32_t K, int32_t *perm, int32_t *offsets,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    g_err[0] = 0;
+    fk_status st = check_sizes(N, 1, K);
+    if (st != FK_OK) return st;
+    if (N > 0 && (assign == nullptr || perm == nullptr))
+        return fail(FK_ERR_INVALID_ARG, "assign and perm must not be NULL");
+    if (offsets == nullptr) return fail(FK_ERR_INVALID_ARG, "offsets is NULL");
+    const Layout L = make_layout(N, 1, K, FK_METRIC_L2, false);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
+    if ((st = check_device()) != FK_OK) return st;
+    const Ctx c{L, workspace, (hipStream_t)stream, 1, K, FK_METRIC_L2};
+    if (N == 0) {
+        FK_TRY(launch_offsets(nullptr, 0, K, offsets, c.s), "cluster offsets");
+        return FK_OK;
+    }
+    return step_sort(c, assign, N, perm, offsets);
+}
+
+fk_status fk_update(const float *X, int64_t N, int32_t d, const int32_t *assign, int32_t K, int32_t metric,
+                    const float *C_prev, float *C_out, int32_t *counts, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    g_err[0] = 0;
+    fk_status st = check_common(X, N, d, C_prev, K, metric);
+    if (st != FK_OK) return st;
+    if (N > 0 && assign == nullptr) return fail(FK_ERR_INVALID_ARG, "assign is NULL");
+    if (C_out == nullptr || counts == nullptr) return fail(FK_ERR_INVALID_ARG, "C_out and counts must not be NULL");
+    const size_t cb = (size_t)K * d * 4;
+    if (overlap(C_out, cb, C_prev, cb)) return fail(FK_ERR_INVALID_ARG, "C_out overlaps C_prev");
+    const Layout L = make_layout(N, d, K, metric, false);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
+    if ((st = check_device()) != FK_OK) return st;
+    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric};
+    if ((st = step_zero_accumulators(c)) != FK_OK) return st;
+    if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
+    if ((st = step_accumulate(c, X, N, assign)) != FK_OK) return st;
+    return step_finalize(c, C_prev, C_out, counts);
+}
+
+fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in, int32_t K, int32_t metric,
+                        int32_t *assign, float *min_dist, float *C_out, int32_t *counts, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+    g_err[0] = 0;
+    fk_status st = check_common(X, N, d, C_in, K, metric);
+    if (st != FK_OK) return st;
+    if (N > 0 && assign == nullptr) return fail(FK_ERR_INVALID_ARG, "assign is NULL");
+    if (C_out == nullptr || counts == nullptr) return fail(FK_ERR_INVALID_ARG, "C_out and counts must not be NULL");
+    const size_t cb = (size_t)K * d * 4;
+    if (overlap(C_out, cb, C_in, cb)) return fail(FK_ERR_INVALID_ARG, "C_out overlaps C_in");
+    const Layout L = make_layout(N, d, K, metric, false);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
+    if ((st = check_device()) != FK_OK) return st;
+    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric};
+    if ((st = step_zero_accumulators(c)) != FK_OK) return st;
+    if (N > 0) {
+        const float *Cu = nullptr;
+        if ((st = step_prep(c, C_in, &Cu)) != FK_OK) return st;
+        if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
+        if ((st = step_assign(c, X, N, C_in, Cu, assign, min_dist)) != FK_OK) return st;
+        if ((st = step_accumulate(c, X, N, assign)) != FK_OK) return st;
+    }
+    return step_finalize(c, C_in, C_out, counts);
+}
+
+// Library-owned copy stream and events for the out-of-core pipeline (one set
+// per device, created on first use, default priority).
+namespace {
+struct OocRes {
+    int device = -1;
+    hipStream_t copy = nullptr;
+    hipEvent_t copied[2] = {nullptr, nullptr};
+    hipEvent_t freed[2] = {nullptr, nullptr};
+    hipEvent_t entry = nullptr;
+};
+std::mutex g_ooc_mu;
+std::vector<OocRes> g_ooc;
+
+fk_status ooc_resources(OocRes **out) {
+    int dev = 0;
+    FK_TRY(hipGetDevice(&dev), "hipGetDevice");
+    std::lock_guard<std::mutex> g(g_ooc_mu);
+    for (auto &r : g_ooc)
+        if (r.device == dev) {
+            *out = &r;
+            return FK_OK;
+        }
+    OocRes r;
+    r.device = dev;
+    FK_TRY(hipStreamCreateWithFlags(&r.copy, hipStreamNonBlocking), "copy stream");
+    for (int i = 0; i < 2; ++i) {
+        FK_TRY(hipEventCreateWithFlags(&r.copied[i], hipEventDisableTiming), "event");
+        FK_TRY(hipEventCreateWithFlags(&r.freed[i], hipEventDisableTiming), "event");
+    }
+    FK_TRY(hipEventCreateWithFlags(&r.entry, hipEventDisableTiming), "event");
+    g_ooc.reserve(16);
+    g_ooc.push_back(r);
+    *out = &g_ooc.back();
+    return FK_OK;
+}
+
+bool is_pinned_host(const void *p) {
+    hipPointerAttribute_t attr;
+    memset(&attr, 0, sizeof attr);
+    const hipError_t e = hipPointerGetAttributes(&attr, p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return attr.type == hipMemoryTypeHost;
+}
+}  // namespace
+
+fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const float *C_in, int32_t K,
+                               int32_t metric, int64_t chunk_rows, int32_t *assign_host, float *C_out,
+                               int32_t *counts, void *workspace, size_t workspace_bytes, void *stream) {
+    g_err[0] = 0;
+    fk_status st = check_common(X_host, N, d, C_in, K, metric);
+    if (st != FK_OK) return st;
+    if (chunk_rows < 1 || chunk_rows > INT32_MAX)
+        return fail(FK_ERR_INVALID_ARG, "chunk_rows=%lld must be in [1, 2^31-1]", (long long)chunk_rows);
+    if (C_out == nullptr || counts == nullptr) return fail(FK_ERR_INVALID_ARG, "C_out and counts must not be NULL");
+    const size_t cb = (size_t)K * d * 4;
+    if (overlap(C_out, cb, C_in, cb)) return fail(FK_ERR_INVALID_ARG, "C_out overlaps C_in");
+    const Layout L = make_layout(chunk_rows, d, K, metric, true);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
+    if ((st = check_device()) != FK_OK) return st;
+    if (N > 0 && !is_pinned_host(X_host)) return fail(FK_ERR_INVALID_ARG, "X_host is not pinned host memory");
+    if (N > 0 && assign_host != nullptr && !is_pinned_host(assign_host))
+        return fail(FK_ERR_INVALID_ARG, "assign_host is not pinned host memory");
+    OocRes *R = nullptr;
+    if ((st = ooc_resources(&R)) != FK_OK) return st;
+
+    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric};
+    if ((st = step_zero_accumulators(c)) != FK_OK) return st;
+    const float *Cu = nullptr;
+    if (N > 0 && (st = step_prep(c, C_in, &Cu)) != FK_OK) return st;
+    // the copy stream may not touch the chunk buffers before the work already
+    // queued on the caller's stream is done with the workspace
+    FK_TRY(hipEventRecord(R->entry, c.s), "event record");
+    FK_TRY(hipStreamWaitEvent(R->copy, R->entry, 0), "stream wait");
+
+    const int64_t nchunks = cdiv(N, chunk_rows);
+    for (int64_t ci = 0; ci < nchunks; ++ci) {
+        const int b = (int)(ci & 1);
+        const int64_t r0 = ci * chunk_rows;
+        const int64_t rows = (N - r0) < chunk_rows ? (N - r0) : chunk_rows;
+        float *Xd = at<float>(workspace, L.xchunk[b]);
+        int32_t *ad = at<int32_t>(workspace, L.achunk[b]);
+        if (ci >= 2) FK_TRY(hipStreamWaitEvent(R->copy, R->freed[b], 0), "stream wait");
+        {
+            PhaseScope ph(FK_PH_H2D, R->copy);
+            FK_TRY(hipMemcpyAsync(Xd, X_host + (size_t)r0 * d, (size_t)rows * d * 4, hipMemcpyHostToDevice, R->copy),
+                   "chunk copy");
+        }
+        FK_TRY(hipEventRecord(R->copied[b], R->copy), "event record");
+        FK_TRY(hipStreamWaitEvent(c.s, R->copied[b], 0), "stream wait");
+        if ((st = step_xnorm(c, Xd, rows)) != FK_OK) return st;
+        // the near-tie list is per chunk: reset its counter
+        FK_TRY(launch_fill_zero(at<void>(workspace, L.counter), 4, c.s), "reset counter");
+        if ((st = step_assign(c, Xd, rows, C_in, Cu, ad, nullptr)) != FK_OK) return st;
+        if ((st = step_accumulate(c, Xd, rows, ad)) != FK_OK) return st;
+        FK_TRY(hipEventRecord(R->freed[b], c.s), "event record");
+        if (assign_host != nullptr)
+            FK_TRY(hipMemcpyAsync(assign_host + r0, ad, (size_t)rows * 4, hipMemcpyDeviceToHost, c.s),
+                   "assignment copy");
+    }
+    return step_finalize(c, C_in, C_out, counts);
+}
+
+fk_status fk_profile_enable(int32_t on) {
+    g_err[0] = 0;
+    std::lock_guard<std::mutex> g(g_prof.mu);
+    g_prof.on = on != 0;
+    if (g_prof.on) {
+        g_prof.acc = fk_profile{};
+        for (auto &p : g_prof.pending) {
+            g_prof.pool.push_back(p.a);
+            g_prof.pool.push_back(p.b);
+        }
+        g_prof.pending.clear();
+        g_prof.slots_used = 0;
+    }
+    return FK_OK;
+}
+
+fk_status fk_profile_read(fk_profile *out) {
+    g_err[0] = 0;
+    if (out == nullptr) return fail(FK_ERR_INVALID_ARG, "out is NULL");
+    std::lock_guard<std::mutex> g(g_prof.mu);
+    for (auto &p : g_prof.pending) {
+        FK_TRY(hipEventSynchronize(p.b), "event sync");
+        float ms = 0.f;
+        FK_TRY(hipEventElapsedTime(&ms, p.a, p.b), "event time");
+        g_prof.acc.ms[p.phase] += ms;
+        g_prof.acc.calls[p.phase] += 1;
+        g_prof.pool.push_back(p.a);
+        g_prof.pool.push_back(p.b);
+    }
+    g_prof.pending.clear();
+    if (g_prof.slots_used > 0) FK_TRY(hipDeviceSynchronize(), "device sync");
+    for (size_t i = 0; i < g_prof.slots_used; ++i) g_prof.acc.rechecked += *g_prof.count_slots[i];
+    g_prof.slots_used = 0;
+    *out = g_prof.acc;
+    g_prof.acc = fk_profile{};
+    return FK_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,556 @@
+// FlashAssign for gfx950: the assignment step of an exact Lloyd iteration.
+//
+// The Flash-KMeans article (lumevalley.com, article 3696, section
+// "FlashAssign: cutting the distance matrix into a pipeline") computes the
+// distances of a block of points to every centroid on the spot and reduces
+// them to an argmin at once, so the N x K distance matrix is never written and
+// the IO is O(Nd + Kd).  This file does that on CDNA4:
+//   * the score s_ik = ||c_k||^2 - 2 x_i.c_k is a dense contraction, so it runs
+//     on v_mfma_f32_32x32x2_f32; the accumulator starts at -||c_k||^2 / 2, so
+//     the MFMA result is  x.c - ||c||^2/2 = (||x||^2 - D_ik) / 2  and the
+//     nearest centroid is the largest accumulator;
+//   * each wave keeps its points in VGPRs; centroid tiles are staged through
+//     LDS (double-buffered) and shared by the 4 waves of a workgroup;
+//   * the MFMA output puts one point per lane and 16 centroids per lane, so
+//     the running top-2 is kept per lane with no cross-lane traffic; lanes l
+//     and l^32 are merged once, after the last tile;
+//   * exactness: the fp32 accumulator has a proven error bound e_i; a point
+//     whose top-2 gap is within 2 e_i is listed, and k_recheck rescores it in
+//     fp64 with the direct-difference distance, which is the definition.
+#include "fk_internal.h"
+
+namespace fk {
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ uint64_t lanemask_lt() {
+    const unsigned lane = __lane_id();
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// ---------------------------------------------------------------------------
+// Row norms in fp64, summed in increasing j with no fused multiply-add:
+// nrm[r] = sqrt(sum_j M[r,j]^2), replaced by 1 when it is 0 (the zero-norm
+// guard of the cosine metric, LEANN FlashLib guide, paragraph "distance
+// metric").  One thread per row.
+__global__ __launch_bounds__(256) void k_row_norm64(const float *__restrict__ M, int64_t rows, int d,
+                                                    double *__restrict__ nrm) {
+#pragma clang fp contract(off)
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r >= rows) return;
+    const float *row = M + (size_t)r * d;
+    double s = 0.0;
+    for (int j = 0; j < d; ++j) {
+        const double v = (double)row[j];
+        s = s + v * v;
+    }
+    double n = sqrt(s);
+    if (n == 0.0) n = 1.0;
+    nrm[r] = n;
+}
+
+// out64[r,j] = M[r,j] / nrm[r] in fp64 (the normalised row), out32 its fp32
+// rounding.
+__global__ __launch_bounds__(256) void k_normalize_rows(const float *__restrict__ M, int64_t total, int d,
+                                                        const double *__restrict__ nrm, double *__restrict__ out64,
+                                                        float *__restrict__ out32) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= total) return;
+    const int64_t r = q / d;
+    const double v = (double)M[q] / nrm[r];
+    out64[q] = v;
+    out32[q] = (float)v;
+}
+
+// ncn[k] = -||c_k||^2 / 2 in fp32 for k < K, -inf for K <= k < Kpad (padded
+// centroids then never win), and the largest ||c_k||^2 of the block.  One wave
+// per centroid row.
+__global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__ C, int K, int Kpad, int d,
+                                                       float *__restrict__ ncn, float *__restrict__ cmax_part) {
+    __shared__ float wmax[4];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int k = blockIdx.x * 4 + w;
+    float cn = 0.f;
+    if (k < K) {
+        const float *row = C + (size_t)k * d;
+        float s = 0.f;
+        for (int j = lane; j < d; j += 64) {
+            const float v = row[j];
+            s = fmaf(v, v, s);
+        }
+        for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+        cn = s;
+    }
+    if (lane == 0) {
+        if (k < K)
+            ncn[k] = -0.5f * cn;
+        else if (k < Kpad)
+            ncn[k] = -INFINITY;
+        wmax[w] = cn;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) cmax_part[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+}
+
+// scal[0] = max_k ||c_k||^2 (fp32); resets the near-tie counter.
+__global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ cmax_part, int nparts,
+                                                     float *__restrict__ scal, int32_t *__restrict__ counter) {
+    __shared__ float sm[256];
+    float m = 0.f;
+    for (int i = threadIdx.x; i < nparts; i += 256) m = fmaxf(m, cmax_part[i]);
+    sm[threadIdx.x] = m;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) sm[threadIdx.x] = fmaxf(sm[threadIdx.x], sm[threadIdx.x + o]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+        scal[0] = sm[0];
+        *counter = 0;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// The FlashAssign kernel.
+//
+// DP: dims per chunk in VGPRs (multiple of 8); PB: 32-point blocks per wave;
+// CB: 32-centroid blocks per tile.  nch d-chunks of DP dims cover d (padding
+// is zero, which changes neither dots nor norms).  With nch == 1 a wave loads
+// its points once; otherwise it reloads its chunk for every stage.
+//
+// MFMA operands (v_mfma_f32_32x32x2_f32, checked on gfx950): lane l gives
+// A[l%32][l/32] and B[l/32][l%32]; D[i][j] sits in lane j + 32*((i/4)%2),
+// register (i%4) + 4*(i/8).  A = centroid rows, B = points, so a lane holds
+// one point and 16 centroids.  The two k-slots of each MFMA step take dims
+// h*DP/2 + s (h = l/32), so a lane reads 4 consecutive floats of its row per
+// ds_read_b128 and its points' coordinates are contiguous in memory.
+//
+// Error bound (why unflagged points are exact).  Let a_ik be the exact real
+// value x_i.c_k - ||c_k||^2/2 from the fp32 inputs.  The fp32 ||c||^2 has
+// relative error <= gamma_d, and the accumulator is a sum of d+1 terms
+// (-||c||^2/2 and the d products) in which every term passes through at most
+// d+2 roundings, so |acc - a| <= gamma_{d+3} (||c||^2 + ||x|| ||c||) with
+// gamma_n = n u / (1 - n u), u = 2^-24.  With g = (d+4) u >= gamma_{d+3},
+// M >= max ||c||^2 and the norms rounded up,
+//     e_i = 1.0625 g (M + ||x_i|| sqrt(M))
+// bounds the error of every accumulator of point i.  If best - second > 2 e_i
+// the fp32 winner is the strict exact winner, with a margin far above the fp64
+// rounding of a direct-difference distance.  Otherwise the point is listed for
+// k_recheck.  For cosine, the fp32 normalised rows differ from the fp64
+// normalised ones by at most 3.1u relative, which moves a by at most
+// 3.1u (||x|| ||c|| + ||c||^2); 8u is added to g for it.
+template <int DP, int PB, int CB>
+__global__ __launch_bounds__(kAssignThreads, 2) void k_flash_assign(
+    const float *__restrict__ X, int64_t N, int d, int nch, const float *__restrict__ C,
+    const float *__restrict__ ncn, int K, int ntiles, const float *__restrict__ scal,
+    const double *__restrict__ xnorm64, int32_t *__restrict__ a_out, float *__restrict__ d1_out,
+    int32_t *__restrict__ flag_list, int32_t *__restrict__ flag_count) {
+    constexpr int HALF = DP / 2;
+    constexpr int ROWS = CB * 32;
+    constexpr int LDR = DP + 4;  // padded LDS row: 8 consecutive lanes hit distinct 16-B bank groups
+    constexpr int Q4 = DP / 4;
+    constexpr int NQ4 = ROWS * Q4;
+    constexpr int PFN = (NQ4 + kAssignThreads - 1) / kAssignThreads;
+    static_assert(HALF % 4 == 0, "DP must be a multiple of 8");
+
+    __shared__ __attribute__((aligned(16))) float sC[2][ROWS * LDR];
+    __shared__ __attribute__((aligned(16))) float sN[2][ROWS];
+
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6;
+    const int lane = tid & 63;
+    const int h = lane >> 5;
+    const int jl = lane & 31;
+    const int64_t pbase = ((int64_t)blockIdx.x * kAssignWaves + wv) * (PB * 32);
+    const bool vec4 = (d & 3) == 0;
+
+    float4 pf[PFN];
+    float pn = 0.f;
+    auto load_stage = [&](int t, int ch) {
+#pragma unroll
+        for (int i = 0; i < PFN; ++i) {
+            const int q = tid + i * kAssignThreads;
+            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (q < NQ4) {
+                const int row = q / Q4;
+                const int col = ch * DP + (q % Q4) * 4;
+                const int k = t * ROWS + row;
+                if (k < K) {
+                    const float *src = C + (size_t)k * d + col;
+                    if (vec4) {
+                        if (col < d) v = *reinterpret_cast<const float4 *>(src);
+                    } else {
+                        if (col < d) v.x = src[0];
+                        if (col + 1 < d) v.y = src[1];
+                        if (col + 2 < d) v.z = src[2];
+                        if (col + 3 < d) v.w = src[3];
+                    }
+                }
+            }
+            pf[i] = v;
+        }
+        if (ch == 0 && tid < ROWS) pn = ncn[t * ROWS + tid];
+    };
+    auto store_stage = [&](int buf, int ch) {
+#pragma unroll
+        for (int i = 0; i < PFN; ++i) {
+            const int q = tid + i * kAssignThreads;
+            if (q < NQ4) *reinterpret_cast<float4 *>(&sC[buf][(q / Q4) * LDR + (q % Q4) * 4]) = pf[i];
+        }
+        if (ch == 0 && tid < ROWS) sN[buf][tid] = pn;
+    };
+
+    float xr[PB][HALF];
+    float xn[PB], xsc[PB], best[PB], sec[PB];
+    int idx[PB];
+#pragma unroll
+    for (int b = 0; b < PB; ++b) {
+        const int64_t p = pbase + b * 32 + jl;
+        xn[b] = 0.f;
+        xsc[b] = (xnorm64 != nullptr && p < N) ? (float)(1.0 / xnorm64[p]) : 1.f;
+        best[b] = -INFINITY;
+        sec[b] = -INFINITY;
+        idx[b] = 0;
+    }
+    auto load_x = [&](int ch, bool add_norm) {
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+            const int64_t p = pbase + b * 32 + jl;
+            const int col0 = ch * DP + h * HALF;
+            const float *src = X + (size_t)p * d + col0;
+            if (p < N) {
+                if (vec4) {
+#pragma unroll
+                    for (int s = 0; s < HALF; s += 4) {
+                        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                        if (col0 + s < d) v = *reinterpret_cast<const float4 *>(src + s);
+                        xr[b][s] = v.x;
+                        xr[b][s + 1] = v.y;
+                        xr[b][s + 2] = v.z;
+                        xr[b][s + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int s = 0; s < HALF; ++s) xr[b][s] = (col0 + s < d) ? src[s] : 0.f;
+                }
+            } else {
+#pragma unroll
+                for (int s = 0; s < HALF; ++s) xr[b][s] = 0.f;
+            }
+            if (xnorm64 != nullptr) {
+#pragma unroll
+                for (int s = 0; s < HALF; ++s) xr[b][s] *= xsc[b];
+            }
+            if (add_norm) {
+                float acc = xn[b];
+#pragma unroll
+                for (int s = 0; s < HALF; ++s) acc = fmaf(xr[b][s], xr[b][s], acc);
+                xn[b] = acc;
+            }
+        }
+    };
+
+    v16f acc[PB][CB];
+    const int nst = ntiles * nch;
+    load_stage(0, 0);
+    store_stage(0, 0);
+    if (nch == 1) load_x(0, true);
+    __syncthreads();
+
+    int t = 0, ch = 0;
+    for (int st = 0; st < nst; ++st) {
+        const int buf = st & 1;
+        int nt = t, nc = ch + 1;
+        if (nc == nch) {
+            nc = 0;
+            nt = t + 1;
+        }
+        const bool more = st + 1 < nst;
+        if (more) load_stage(nt, nc);
+        if (nch > 1) load_x(ch, t == 0);
+
+        if (ch == 0) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float4 nv = *reinterpret_cast<const float4 *>(&sN[buf][cb * 32 + 8 * q + 4 * h]);
+#pragma unroll
+                    for (int b = 0; b < PB; ++b) {
+                        acc[b][cb][4 * q + 0] = nv.x;
+                        acc[b][cb][4 * q + 1] = nv.y;
+                        acc[b][cb][4 * q + 2] = nv.z;
+                        acc[b][cb][4 * q + 3] = nv.w;
+                    }
+                }
+            }
+        }
+
+        const float *sc = &sC[buf][jl * LDR + h * HALF];
+#pragma unroll
+        for (int s = 0; s < HALF; s += 4) {
+            float4 av[CB];
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) av[cb] = *reinterpret_cast<const float4 *>(sc + cb * 32 * LDR + s);
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+                for (int b = 0; b < PB; ++b) {
+                    acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].x, xr[b][s + 0], acc[b][cb], 0, 0, 0);
+                    acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].y, xr[b][s + 1], acc[b][cb], 0, 0, 0);
+                    acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].z, xr[b][s + 2], acc[b][cb], 0, 0, 0);
+                    acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].w, xr[b][s + 3], acc[b][cb], 0, 0, 0);
+                }
+            }
+        }
+
+        if (ch == nch - 1) {
+            const int kt = t * ROWS + 4 * h;
+#pragma unroll
+            for (int b = 0; b < PB; ++b) {
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const float v = acc[b][cb][r];
+                        const int k = kt + cb * 32 + 8 * (r >> 2) + (r & 3);
+                        sec[b] = fmaxf(sec[b], fminf(v, best[b]));
+                        if (v > best[b]) {
+                            best[b] = v;
+                            idx[b] = k;
+                        }
+                    }
+                }
+            }
+        }
+        if (more) store_stage(buf ^ 1, nc);
+        __syncthreads();
+        t = nt;
+        ch = nc;
+    }
+
+    // merge the two half-waves (same point, the other 16 centroids of each
+    // 32-block): larger score wins, lower index on equal scores
+    const float u = 5.9604645e-8f;
+    const float g = (float)(d + 4) * u + (xnorm64 != nullptr ? 8.f * u : 0.f);
+    const float M = scal[0] * (1.f + g);
+    const float sqM = sqrtf(M) * (1.f + 2.f * u);
+#pragma unroll
+    for (int b = 0; b < PB; ++b) {
+        const float ob = __shfl_xor(best[b], 32);
+        const float os = __shfl_xor(sec[b], 32);
+        const int oi = __shfl_xor(idx[b], 32);
+        const float ns = fmaxf(fminf(best[b], ob), fmaxf(sec[b], os));
+        const bool take = (ob > best[b]) || (ob == best[b] && oi < idx[b]);
+        const float bb = take ? ob : best[b];
+        const int bi = take ? oi : idx[b];
+        const float xnt = xn[b] + __shfl_xor(xn[b], 32);
+        const int64_t p = pbase + b * 32 + jl;
+        const bool valid = (h == 0) && (p < N);
+        const float xnorm = sqrtf(xnt * (1.f + g)) * (1.f + 2.f * u);
+        const float e = 1.0625f * g * (M + xnorm * sqM) + 1e-30f;
+        const bool flagged = !((bb - ns) > 2.f * e);
+        if (valid) {
+            a_out[p] = bi;
+            if (d1_out != nullptr) d1_out[p] = fmaxf(xnt - 2.f * bb, 0.f);
+        }
+        const uint64_t m = __ballot(valid && flagged);
+        if (m != 0ull) {
+            const int leader = __ffsll((unsigned long long)m) - 1;
+            int base = 0;
+            if (lane == leader) base = atomicAdd(flag_count, __popcll(m));
+            base = __shfl(base, leader);
+            if (valid && flagged) flag_list[base + __popcll(m & lanemask_lt())] = (int32_t)p;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp64 rescoring of listed near-tie points: D_ik = sum_j (x_ij - c_kj)^2 in
+// fp64 in increasing j, no fused multiply-add, for every k; the lowest index
+// attaining the minimum wins.  That is the distance definition itself, so the
+// result is the exact assignment.  For cosine the rows are normalised in fp64
+// exactly as the definition says (C64 holds the normalised centroids).
+// A workgroup takes RP listed points at a time; thread t scores centroids
+// t, t+256, ...
+template <typename CT, int RP>
+__global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, int d, const CT *__restrict__ C,
+                                                 int K, const double *__restrict__ xnorm64,
+                                                 const int32_t *__restrict__ flag_list,
+                                                 const int32_t *__restrict__ flag_count, int P,
+                                                 int32_t *__restrict__ a_out, float *__restrict__ d1_out) {
+#pragma clang fp contract(off)
+    extern __shared__ double sx[];  // P * d
+    __shared__ double rb[4][RP];
+    __shared__ int ri[4][RP];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int cnt = *flag_count;
+    for (int base = blockIdx.x * P; base < cnt; base += gridDim.x * P) {
+        const int np = min(P, cnt - base);
+        for (int q = tid; q < np * d; q += 256) {
+            const int pi = q / d, jj = q - pi * d;
+            const int64_t p = flag_list[base + pi];
+            double v = (double)X[(size_t)p * d + jj];
+            if (xnorm64 != nullptr) v = v / xnorm64[p];
+            sx[pi * d + jj] = v;
+        }
+        __syncthreads();
+        double best[RP];
+        int bidx[RP];
+#pragma unroll
+        for (int pi = 0; pi < RP; ++pi) {
+            best[pi] = INFINITY;
+            bidx[pi] = 0x7fffffff;
+        }
+        for (int k = tid; k < K; k += 256) {
+            double acc[RP];
+#pragma unroll
+            for (int pi = 0; pi < RP; ++pi) acc[pi] = 0.0;
+            const CT *crow = C + (size_t)k * d;
+            for (int jj = 0; jj < d; ++jj) {
+                const double c = (double)crow[jj];
+#pragma unroll
+                for (int pi = 0; pi < RP; ++pi) {
+                    if (pi < np) {
+                        const double tt = sx[pi * d + jj] - c;
+                        acc[pi] = acc[pi] + tt * tt;
+                    }
+                }
+            }
+#pragma unroll
+            for (int pi = 0; pi < RP; ++pi) {
+                if (acc[pi] < best[pi]) {
+                    best[pi] = acc[pi];
+                    bidx[pi] = k;
+                }
+            }
+        }
+#pragma unroll
+        for (int pi = 0; pi < RP; ++pi) {
+            double b = best[pi];
+            int i = bidx[pi];
+            for (int off = 32; off > 0; off >>= 1) {
+                const double ob = __shfl_xor(b, off);
+                const int oi = __shfl_xor(i, off);
+                if (ob < b || (ob == b && oi < i)) {
+                    b = ob;
+                    i = oi;
+                }
+            }
+            if (lane == 0) {
+                rb[w][pi] = b;
+                ri[w][pi] = i;
+            }
+        }
+        __syncthreads();
+        if (tid < np) {
+            double b = rb[0][tid];
+            int i = ri[0][tid];
+            for (int ww = 1; ww < 4; ++ww) {
+                const double ob = rb[ww][tid];
+                const int oi = ri[ww][tid];
+                if (ob < b || (ob == b && oi < i)) {
+                    b = ob;
+                    i = oi;
+                }
+            }
+            const int64_t p = flag_list[base + tid];
+            a_out[p] = i;
+            if (d1_out != nullptr) d1_out[p] = (float)b;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+AssignShape assign_shape(int d) {
+    if (d <= 16) return {16, 2, 1, 1};
+    if (d <= 32) return {32, 2, 1, 1};
+    if (d <= 64) return {64, 2, 1, 1};
+    if (d <= 128) return {128, 2, 1, 1};
+    return {64, 1, 4, (int)cdiv(d, 64)};
+}
+
+hipError_t launch_row_norm64(const float *M, int64_t rows, int d, double *nrm, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_row_norm64, dim3((unsigned)cdiv(rows, 256)), dim3(256), 0, s, M, rows, d, nrm);
+    return hipGetLastError();
+}
+
+hipError_t launch_normalize_rows(const float *M, int64_t rows, int d, const double *nrm, double *out64,
+                                 float *out32, hipStream_t s) {
+    const int64_t total = rows * (int64_t)d;
+    if (total <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_normalize_rows, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, M, total, d, nrm,
+                       out64, out32);
+    return hipGetLastError();
+}
+
+hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float *cmax_part, int *nparts,
+                                hipStream_t s) {
+    const int Kpad = (int)(cdiv(K, kCentroidPad) * kCentroidPad);
+    const int nb = (int)cdiv(Kpad, 4);
+    *nparts = nb;
+    hipLaunchKernelGGL(k_centroid_prep, dim3(nb), dim3(256), 0, s, C, K, Kpad, d, ncn, cmax_part);
+    return hipGetLastError();
+}
+
+hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, int32_t *counter, hipStream_t s) {
+    hipLaunchKernelGGL(k_prep_finish, dim3(1), dim3(256), 0, s, cmax_part, nparts, scal, counter);
+    return hipGetLastError();
+}
+
+template <int DP, int PB, int CB>
+static hipError_t launch_fa(const float *X, int64_t N, int d, int nch, const float *C, const float *ncn, int K,
+                            const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
+                            int32_t *flag_list, int32_t *flag_count, hipStream_t s) {
+    const int ntiles = (int)cdiv(K, CB * 32);
+    const int64_t nb = cdiv(N, (int64_t)kAssignWaves * PB * 32);
+    hipLaunchKernelGGL((k_flash_assign<DP, PB, CB>), dim3((unsigned)nb), dim3(kAssignThreads), 0, s, X, N, d,
+                       nch, C, ncn, K, ntiles, scal, xnorm64, a_out, d1_out, flag_list, flag_count);
+    return hipGetLastError();
+}
+
+hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
+                               const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
+                               int32_t *flag_list, int32_t *flag_count, hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    const AssignShape sh = assign_shape(d);
+    switch (sh.DP) {
+    case 16:
+        return launch_fa<16, 2, 1>(X, N, d, 1, C, ncn, K, scal, xnorm64, a_out, d1_out, flag_list, flag_count, s);
+    case 32:
+        return launch_fa<32, 2, 1>(X, N, d, 1, C, ncn, K, scal, xnorm64, a_out, d1_out, flag_list, flag_count, s);
+    case 128:
+        return launch_fa<128, 2, 1>(X, N, d, 1, C, ncn, K, scal, xnorm64, a_out, d1_out, flag_list, flag_count,
+                                    s);
+    default:
+        if (sh.CB == 1)
+            return launch_fa<64, 2, 1>(X, N, d, 1, C, ncn, K, scal, xnorm64, a_out, d1_out, flag_list, flag_count,
+                                       s);
+        return launch_fa<64, 1, 4>(X, N, d, sh.nch, C, ncn, K, scal, xnorm64, a_out, d1_out, flag_list,
+                                   flag_count, s);
+    }
+}
+
+hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C32, const double *C64, int K,
+                          const double *xnorm64, const int32_t *flag_list, const int32_t *flag_count,
+                          int32_t *a_out, float *d1_out, hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    constexpr int RP = 8;
+    int P = (int)(49152 / (8 * (int64_t)d));
+    if (P > RP) P = RP;
+    if (P < 1) P = 1;
+    const size_t lds = (size_t)P * d * sizeof(double);
+    int64_t nb = cdiv(N, P);
+    if (nb > 2048) nb = 2048;
+    if (C64 != nullptr)
+        hipLaunchKernelGGL((k_recheck<double, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C64, K, xnorm64,
+                           flag_list, flag_count, P, a_out, d1_out);
+    else
+        hipLaunchKernelGGL((k_recheck<float, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C32, K, xnorm64,
+                           flag_list, flag_count, P, a_out, d1_out);
+    return hipGetLastError();
+}
+
+}  // namespace fk

@@ -1,0 +1,77 @@
+// Internal declarations shared by the HIP translation units of libfk.
+// Kernels are written for gfx950 (CDNA4): wave64, fp32 MFMA, 160 KB LDS.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fk {
+
+constexpr int kWave = 64;
+
+// ---- FlashAssign geometry -------------------------------------------------
+// A workgroup is 4 waves.  Each wave owns PB blocks of 32 points and keeps
+// their coordinates for one d-chunk of DP dims in VGPRs; all 4 waves share
+// centroid tiles of CB*32 rows x DP dims staged through LDS.
+constexpr int kAssignWaves = 4;
+constexpr int kAssignThreads = kAssignWaves * kWave;
+// Centroid counts are padded to a multiple of this (largest tile height).
+constexpr int kCentroidPad = 128;
+
+// ---- radix sort geometry --------------------------------------------------
+constexpr int kSortWaves = 4;
+constexpr int kSortThreads = kSortWaves * kWave;
+constexpr int kSortRows = 16;                                  // 64-key rows per wave
+constexpr int kSortTile = kSortWaves * kSortRows * kWave;       // 4096 keys per tile
+constexpr int kScanChunk = 4096;                                // scan elements per block
+
+// ---- segmented reduction geometry -----------------------------------------
+constexpr int kSegRows = 2048;    // sorted rows per wave segment
+constexpr int kSegWaves = 4;
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Which FlashAssign variant handles dimension d, and its geometry.
+struct AssignShape {
+    int DP;       // dims per chunk held in registers
+    int PB;       // 32-point blocks per wave
+    int CB;       // 32-centroid blocks per tile
+    int nch;      // number of d-chunks
+};
+AssignShape assign_shape(int d);
+
+// ---- launchers (each returns the launch status) ---------------------------
+hipError_t launch_row_norm64(const float *M, int64_t rows, int d, double *nrm, hipStream_t s);
+hipError_t launch_normalize_rows(const float *M, int64_t rows, int d, const double *nrm, double *out64,
+                                 float *out32, hipStream_t s);
+hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float *cmax_part, int *nparts,
+                                hipStream_t s);
+hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, int32_t *counter,
+                              hipStream_t s);
+hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
+                               const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
+                               int32_t *flag_list, int32_t *flag_count, hipStream_t s);
+hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C32, const double *C64, int K,
+                          const double *xnorm64, const int32_t *flag_list, const int32_t *flag_count,
+                          int32_t *a_out, float *d1_out, hipStream_t s);
+
+// Radix sort of (key = assign[i], value = i), stable, atomic-free.  Writes the
+// sorted keys and the permutation.  tmp* are N-sized scratch arrays.
+size_t sort_scratch_bytes(int64_t N);
+hipError_t launch_sort_by_key(const int32_t *keys, int64_t N, int K, int32_t *keys_sorted, int32_t *perm,
+                              int32_t *tmp_keys, int32_t *tmp_vals, void *scratch, hipStream_t s);
+hipError_t launch_offsets(const int32_t *keys_sorted, int64_t N, int K, int32_t *offsets, hipStream_t s);
+
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+hipError_t launch_seg_reduce(const float *X, int64_t N, int d, const int32_t *keys_sorted, const int32_t *perm,
+                             const double *xnorm64, double *sums, double *pfirst, double *plast,
+                             hipStream_t s);
+hipError_t launch_seg_fixup(const int32_t *keys_sorted, const int32_t *offsets, int64_t N, int d,
+                            const double *pfirst, const double *plast, double *sums, hipStream_t s);
+hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, hipStream_t s);
+hipError_t launch_finalize(const double *sums, const int32_t *cnt, const float *C_prev, int K, int d,
+                           float *C_out, int32_t *counts_out, hipStream_t s);
+
+}  // namespace fk

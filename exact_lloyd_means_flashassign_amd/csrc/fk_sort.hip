@@ -1,0 +1,291 @@
+// The inverse index of the Sort-Inverse Update: a stable, atomic-free LSD
+// radix sort of (key = cluster id, value = point id).
+//
+// The Flash-KMeans article (lumevalley.com, article 3696, section
+// "Sort-Inverse Update: another answer to atomics") sorts the assignment by
+// cluster id to obtain an inverse index, so that clusters can be reduced by
+// contiguous reads without any atomic operation.  Keys are below K <= 65536,
+// so at most two passes of <= 8 bits are needed.
+//
+// Each pass is hist -> scan -> scatter over tiles of 4096 keys.  Inside a tile
+// a wave ranks 64 keys at a time with ballots: for a digit of B bits, B ballots
+// give every lane the mask of lanes holding the same digit; its rank is the
+// number of such lanes below it, and the lowest such lane (the leader) alone
+// updates that digit's running count in LDS.  No atomic operation is used
+// anywhere: every LDS count has exactly one writer at a time.
+#include "fk_internal.h"
+
+namespace fk {
+
+__device__ __forceinline__ uint64_t lanemask_lt_s() {
+    const unsigned lane = __lane_id();
+    return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+// Mask of the lanes (among `active`) whose digit equals this lane's.
+template <int BITS>
+__device__ __forceinline__ uint64_t match_digit(unsigned dig, uint64_t active) {
+    uint64_t m = active;
+#pragma unroll
+    for (int b = 0; b < BITS; ++b) {
+        const bool bit = (dig >> b) & 1u;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+    }
+    return m;
+}
+
+// Per-wave digit counts of the tile into wcnt[wave][digit] (LDS).
+template <int BITS>
+__device__ __forceinline__ void tile_counts(const unsigned (&dig)[kSortRows], const int64_t row0, int64_t N,
+                                            int *wcnt_w) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int r = 0; r < kSortRows; ++r) {
+        const bool valid = row0 + r * 64 + lane < N;
+        const uint64_t act = __ballot(valid);
+        if (act == 0ull) break;
+        const uint64_t m = match_digit<BITS>(dig[r], act);
+        if (valid && (m & lanemask_lt_s()) == 0ull) wcnt_w[dig[r]] += __popcll(m);
+    }
+}
+
+// hist[digit * ntiles + tile] = number of keys of the tile with that digit.
+template <int BITS>
+__global__ __launch_bounds__(kSortThreads) void k_radix_hist(const int32_t *__restrict__ keys, int64_t N, int shift,
+                                                             int32_t *__restrict__ hist, int ntiles) {
+    constexpr int NB = 1 << BITS;
+    __shared__ int wcnt[kSortWaves][NB];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    for (int i = tid; i < kSortWaves * NB; i += kSortThreads) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const int64_t row0 = (int64_t)blockIdx.x * kSortTile + (int64_t)w * (kSortRows * 64);
+    unsigned dig[kSortRows];
+#pragma unroll
+    for (int r = 0; r < kSortRows; ++r) {
+        const int64_t i = row0 + r * 64 + lane;
+        dig[r] = i < N ? (((unsigned)keys[i] >> shift) & (NB - 1)) : 0u;
+    }
+    tile_counts<BITS>(dig, row0, N, wcnt[w]);
+    __syncthreads();
+    for (int v = tid; v < NB; v += kSortThreads) {
+        int s = 0;
+#pragma unroll
+        for (int ww = 0; ww < kSortWaves; ++ww) s += wcnt[ww][v];
+        hist[(int64_t)v * ntiles + blockIdx.x] = s;
+    }
+}
+
+// Stable scatter of one pass.  vals_in == nullptr means value = index.
+template <int BITS>
+__global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *__restrict__ keys_in,
+                                                                const int32_t *__restrict__ vals_in, int64_t N,
+                                                                int shift, const int32_t *__restrict__ hist_scan,
+                                                                int ntiles, int32_t *__restrict__ keys_out,
+                                                                int32_t *__restrict__ vals_out) {
+    constexpr int NB = 1 << BITS;
+    __shared__ int wcnt[kSortWaves][NB];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    for (int i = tid; i < kSortWaves * NB; i += kSortThreads) (&wcnt[0][0])[i] = 0;
+    __syncthreads();
+    const int64_t row0 = (int64_t)blockIdx.x * kSortTile + (int64_t)w * (kSortRows * 64);
+    int32_t key[kSortRows], val[kSortRows];
+    unsigned dig[kSortRows];
+#pragma unroll
+    for (int r = 0; r < kSortRows; ++r) {
+        const int64_t i = row0 + r * 64 + lane;
+        const bool valid = i < N;
+        key[r] = valid ? keys_in[i] : 0;
+        val[r] = valid ? (vals_in != nullptr ? vals_in[i] : (int32_t)i) : 0;
+        dig[r] = ((unsigned)key[r] >> shift) & (NB - 1);
+    }
+    tile_counts<BITS>(dig, row0, N, wcnt[w]);
+    __syncthreads();
+    // running start of every (wave, digit): global base of the digit in this
+    // tile plus the counts of the earlier waves
+    for (int v = tid; v < NB; v += kSortThreads) {
+        int s = hist_scan[(int64_t)v * ntiles + blockIdx.x];
+#pragma unroll
+        for (int ww = 0; ww < kSortWaves; ++ww) {
+            const int c = wcnt[ww][v];
+            wcnt[ww][v] = s;
+            s += c;
+        }
+    }
+    __syncthreads();
+    int *run = wcnt[w];
+#pragma unroll
+    for (int r = 0; r < kSortRows; ++r) {
+        const bool valid = row0 + r * 64 + lane < N;
+        const uint64_t act = __ballot(valid);
+        if (act == 0ull) break;
+        const uint64_t m = match_digit<BITS>(dig[r], act);
+        const uint64_t below = m & lanemask_lt_s();
+        int pos = 0;
+        if (valid) pos = run[dig[r]] + __popcll(below);
+        // every lane has read its run start before a leader moves it on
+        __builtin_amdgcn_wave_barrier();
+        if (valid && below == 0ull) run[dig[r]] += __popcll(m);
+        __builtin_amdgcn_wave_barrier();
+        if (valid) {
+            if (keys_out != nullptr) keys_out[pos] = key[r];
+            vals_out[pos] = val[r];
+        }
+    }
+}
+
+// ---- exclusive scan of an int32 array, reduce-then-scan, three kernels ----
+__global__ __launch_bounds__(256) void k_scan_reduce(const int32_t *__restrict__ in, int64_t n,
+                                                     int32_t *__restrict__ part) {
+    __shared__ int sm[256];
+    const int64_t b0 = (int64_t)blockIdx.x * kScanChunk;
+    int s = 0;
+    for (int i = threadIdx.x; i < kScanChunk; i += 256) {
+        const int64_t q = b0 + i;
+        if (q < n) s += in[q];
+    }
+    sm[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) sm[threadIdx.x] += sm[threadIdx.x + o];
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) part[blockIdx.x] = sm[0];
+}
+
+// In-place exclusive scan of part[0..np) by one workgroup.
+__global__ __launch_bounds__(256) void k_scan_top(int32_t *__restrict__ part, int np) {
+    __shared__ int sm[256];
+    __shared__ int carry;
+    if (threadIdx.x == 0) carry = 0;
+    __syncthreads();
+    for (int b = 0; b < np; b += 256) {
+        const int i = b + threadIdx.x;
+        const int v = i < np ? part[i] : 0;
+        sm[threadIdx.x] = v;
+        __syncthreads();
+        for (int o = 1; o < 256; o <<= 1) {
+            const int t = (int)threadIdx.x >= o ? sm[threadIdx.x - o] : 0;
+            __syncthreads();
+            sm[threadIdx.x] += t;
+            __syncthreads();
+        }
+        if (i < np) part[i] = carry + sm[threadIdx.x] - v;
+        __syncthreads();
+        if (threadIdx.x == 255) carry += sm[255];
+        __syncthreads();
+    }
+}
+
+// out = exclusive scan of in, each chunk offset by its scanned partial.
+__global__ __launch_bounds__(256) void k_scan_down(const int32_t *__restrict__ in, int64_t n,
+                                                   const int32_t *__restrict__ part, int32_t *__restrict__ out) {
+    constexpr int PER = kScanChunk / 256;
+    __shared__ int sm[256];
+    const int64_t b0 = (int64_t)blockIdx.x * kScanChunk + (int64_t)threadIdx.x * PER;
+    int v[PER];
+    int s = 0;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        v[i] = (b0 + i < n) ? in[b0 + i] : 0;
+        s += v[i];
+    }
+    sm[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 1; o < 256; o <<= 1) {
+        const int t = (int)threadIdx.x >= o ? sm[threadIdx.x - o] : 0;
+        __syncthreads();
+        sm[threadIdx.x] += t;
+        __syncthreads();
+    }
+    int run = part[blockIdx.x] + sm[threadIdx.x] - s;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (b0 + i < n) out[b0 + i] = run;
+        run += v[i];
+    }
+}
+
+// offsets[k] = first position of key k in the sorted keys (= position of the
+// first key >= k); offsets[K] = N.  Each offsets[k] is written by exactly one
+// thread: the one at the boundary where the key first reaches k.
+__global__ __launch_bounds__(256) void k_offsets(const int32_t *__restrict__ ks, int64_t N, int K,
+                                                 int32_t *__restrict__ offsets) {
+    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (r > N) return;
+    const int lo = (r == 0) ? 0 : ks[r - 1] + 1;
+    const int hi = (r == N) ? K : ks[r];
+    for (int k = lo; k <= hi; ++k) offsets[k] = (int32_t)r;
+}
+
+// ---------------------------------------------------------------------------
+static int key_bits(int K) {
+    int b = 0;
+    while ((1 << b) < K) ++b;
+    return b < 1 ? 1 : b;
+}
+
+static int64_t ntiles_of(int64_t N) { return cdiv(N, kSortTile); }
+
+size_t sort_scratch_bytes(int64_t N) {
+    const int64_t nt = ntiles_of(N > 0 ? N : 1);
+    const int64_t hn = 256 * nt;
+    const int64_t np = cdiv(hn, kScanChunk);
+    return align_up((size_t)hn * 4, 256) * 2 + align_up((size_t)np * 4, 256);
+}
+
+template <int BITS>
+static hipError_t radix_pass(const int32_t *kin, const int32_t *vin, int64_t N, int shift, int32_t *kout,
+                             int32_t *vout, int32_t *hist, int32_t *hscan, int32_t *part, hipStream_t s) {
+    const int nt = (int)ntiles_of(N);
+    const int64_t hn = (int64_t)(1 << BITS) * nt;
+    const int np = (int)cdiv(hn, kScanChunk);
+    hipLaunchKernelGGL(k_radix_hist<BITS>, dim3(nt), dim3(kSortThreads), 0, s, kin, N, shift, hist, nt);
+    hipLaunchKernelGGL(k_scan_reduce, dim3(np), dim3(256), 0, s, hist, hn, part);
+    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(256), 0, s, part, np);
+    hipLaunchKernelGGL(k_scan_down, dim3(np), dim3(256), 0, s, hist, hn, part, hscan);
+    hipLaunchKernelGGL(k_radix_scatter<BITS>, dim3(nt), dim3(kSortThreads), 0, s, kin, vin, N, shift, hscan, nt,
+                       kout, vout);
+    return hipGetLastError();
+}
+
+static hipError_t radix_pass_bits(int bits, const int32_t *kin, const int32_t *vin, int64_t N, int shift,
+                                  int32_t *kout, int32_t *vout, int32_t *hist, int32_t *hscan, int32_t *part,
+                                  hipStream_t s) {
+    switch (bits) {
+    case 1: return radix_pass<1>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
+    case 2: return radix_pass<2>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
+    case 3: return radix_pass<3>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
+    case 4: return radix_pass<4>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
+    case 5: return radix_pass<5>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
+    case 6: return radix_pass<6>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
+    case 7: return radix_pass<7>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
+    default: return radix_pass<8>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
+    }
+}
+
+hipError_t launch_sort_by_key(const int32_t *keys, int64_t N, int K, int32_t *keys_sorted, int32_t *perm,
+                              int32_t *tmp_keys, int32_t *tmp_vals, void *scratch, hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    const int64_t nt = ntiles_of(N);
+    const int64_t hn = 256 * nt;
+    char *p = (char *)scratch;
+    int32_t *hist = (int32_t *)p;
+    p += align_up((size_t)hn * 4, 256);
+    int32_t *hscan = (int32_t *)p;
+    p += align_up((size_t)hn * 4, 256);
+    int32_t *part = (int32_t *)p;
+    const int bits = key_bits(K);
+    if (bits <= 8)
+        return radix_pass_bits(bits, keys, nullptr, N, 0, keys_sorted, perm, hist, hscan, part, s);
+    hipError_t e = radix_pass_bits(8, keys, nullptr, N, 0, tmp_keys, tmp_vals, hist, hscan, part, s);
+    if (e != hipSuccess) return e;
+    return radix_pass_bits(bits - 8, tmp_keys, tmp_vals, N, 8, keys_sorted, perm, hist, hscan, part, s);
+}
+
+hipError_t launch_offsets(const int32_t *keys_sorted, int64_t N, int K, int32_t *offsets, hipStream_t s) {
+    hipLaunchKernelGGL(k_offsets, dim3((unsigned)cdiv(N + 1, 256)), dim3(256), 0, s, keys_sorted, N, K, offsets);
+    return hipGetLastError();
+}
+
+}  // namespace fk

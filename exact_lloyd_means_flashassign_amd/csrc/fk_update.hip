@@ -1,0 +1,270 @@
+// Sort-Inverse Update for gfx950: per-cluster sums over the inverse index,
+// without atomics.
+//
+// The Flash-KMeans article (lumevalley.com, article 3696, section
+// "Sort-Inverse Update: another answer to atomics") reduces each cluster by
+// reading the sorted inverse index contiguously, one thread block per few
+// clusters.  Under a skewed (Zipf) size distribution one cluster can hold a
+// fifth of all points, so a block per cluster would leave one block reading
+// millions of rows.  Here the sorted rows are cut into equal segments of
+// kSegRows rows, one wave each:
+//   * a cluster that lies inside one segment is summed and written by that
+//     wave alone;
+//   * a cluster that crosses segment boundaries leaves one partial row per
+//     segment it touches (pfirst: the segment's first cluster when it started
+//     earlier; plast: the segment's last cluster when it continues later), and
+//     k_seg_fixup adds those partials in a fixed order.
+// Every output element has exactly one writer and a fixed summation order, so
+// the result is bitwise reproducible.  Sums are fp64.  The gathered rows
+// X[perm[r]] are read as whole coalesced rows.
+#include "fk_internal.h"
+
+namespace fk {
+
+__global__ __launch_bounds__(256) void k_fill_zero(uint32_t *__restrict__ p, int64_t n) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0u;
+}
+
+// NV loads of E consecutive floats per lane cover 64*E*NV columns starting at
+// blockIdx.y * 64*E*NV.  U rows are loaded before they are accumulated so that
+// U row reads per lane are in flight at once.
+template <int NV, int E, int U>
+__global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X, int64_t N, int d,
+                                                    const int32_t *__restrict__ ks, const int32_t *__restrict__ perm,
+                                                    const double *__restrict__ xnorm64, double *__restrict__ sums,
+                                                    double *__restrict__ pfirst, double *__restrict__ plast) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t seg = (int64_t)blockIdx.x * kSegWaves + w;
+    const int64_t r0 = seg * kSegRows;
+    if (r0 >= N) return;
+    const int64_t r1 = (r0 + kSegRows < N) ? r0 + kSegRows : N;
+    const int cbase = blockIdx.y * (64 * E * NV);
+
+    const int first_k = ks[r0];
+    const bool started_before = r0 > 0 && ks[r0 - 1] == first_k;
+    const int last_k = ks[r1 - 1];
+    const bool cont_after = r1 < N && ks[r1] == last_k;
+
+    int col[NV];
+    bool cok[NV];
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+        col[v] = cbase + (v * 64 + lane) * E;
+        cok[v] = col[v] < d;  // d is a multiple of E, so the whole E-group is in or out
+    }
+
+    double acc[NV][E];
+#pragma unroll
+    for (int v = 0; v < NV; ++v)
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc[v][e] = 0.0;
+    int cur = first_k;
+
+    auto flush = [&](int k) {
+        double *dst;
+        bool add;
+        if (k == first_k && started_before) {
+            dst = pfirst + seg * (int64_t)d;
+            add = false;
+        } else if (k == last_k && cont_after) {
+            dst = plast + seg * (int64_t)d;
+            add = false;
+        } else {
+            dst = sums + (int64_t)k * d;
+            add = true;
+        }
+#pragma unroll
+        for (int v = 0; v < NV; ++v) {
+            if (!cok[v]) continue;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const double val = add ? dst[col[v] + e] + acc[v][e] : acc[v][e];
+                dst[col[v] + e] = val;
+                acc[v][e] = 0.0;
+            }
+        }
+    };
+
+    for (int64_t r = r0; r < r1; r += 64) {
+        const int nb = (int)((r1 - r) < 64 ? (r1 - r) : 64);
+        const int kk = lane < nb ? ks[r + lane] : -1;
+        const int pp = lane < nb ? perm[r + lane] : 0;
+        for (int i = 0; i < nb; i += U) {
+            float vals[U][NV][E];
+            int keys[U];
+            double scl[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                keys[u] = __builtin_amdgcn_readlane(kk, (i + u) & 63);
+                scl[u] = 1.0;
+                if (i + u < nb) {
+                    const int p = __builtin_amdgcn_readlane(pp, (i + u) & 63);
+                    const float *row = X + (size_t)p * d;
+                    if (xnorm64 != nullptr) scl[u] = 1.0 / xnorm64[p];
+#pragma unroll
+                    for (int v = 0; v < NV; ++v) {
+                        if (E == 2) {
+                            float2 t = make_float2(0.f, 0.f);
+                            if (cok[v]) t = *reinterpret_cast<const float2 *>(row + col[v]);
+                            vals[u][v][0] = t.x;
+                            vals[u][v][E - 1] = t.y;
+                        } else {
+                            vals[u][v][0] = cok[v] ? row[col[v]] : 0.f;
+                        }
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (i + u < nb) {
+                    if (keys[u] != cur) {
+                        flush(cur);
+                        cur = keys[u];
+                    }
+#pragma unroll
+                    for (int v = 0; v < NV; ++v)
+#pragma unroll
+                        for (int e = 0; e < E; ++e) {
+                            const double x = (double)vals[u][v][e];
+                            acc[v][e] += (xnorm64 != nullptr) ? x * scl[u] : x;
+                        }
+                }
+            }
+        }
+    }
+    flush(cur);
+}
+
+// One workgroup per segment boundary b (between segments b and b+1).  If a
+// cluster k crosses it and b is the first boundary k crosses, the workgroup
+// adds k's partials: plast of k's first segment, then pfirst of every later
+// segment k touches, into sums[k].  Wave w takes the segments sa+1+w,
+// sa+1+w+8, ... in order; the 8 wave sums are added in wave order.
+constexpr int kFixWaves = 8;
+__global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__restrict__ ks,
+                                                             const int32_t *__restrict__ offsets, int64_t N, int d,
+                                                             const double *__restrict__ pfirst,
+                                                             const double *__restrict__ plast,
+                                                             double *__restrict__ sums) {
+    __shared__ double red[kFixWaves][64];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t b = blockIdx.x;
+    const int64_t rb = (b + 1) * kSegRows;
+    if (rb >= N) return;
+    const int k = ks[rb];
+    if (ks[rb - 1] != k) return;
+    const int64_t o0 = offsets[k], o1 = offsets[k + 1];
+    const int64_t sa = o0 / kSegRows;
+    if (sa != b) return;
+    const int64_t sb = (o1 - 1) / kSegRows;
+    for (int c0 = 0; c0 < d; c0 += 64) {
+        const int c = c0 + lane;
+        double s = 0.0;
+        if (c < d) {
+            if (w == 0) s = plast[sa * d + c];
+            int64_t sg = sa + 1 + w;
+            for (; sg + 3 * kFixWaves <= sb; sg += 4 * kFixWaves) {
+                const double a0 = pfirst[sg * d + c];
+                const double a1 = pfirst[(sg + kFixWaves) * d + c];
+                const double a2 = pfirst[(sg + 2 * kFixWaves) * d + c];
+                const double a3 = pfirst[(sg + 3 * kFixWaves) * d + c];
+                s += a0;
+                s += a1;
+                s += a2;
+                s += a3;
+            }
+            for (; sg <= sb; sg += kFixWaves) s += pfirst[sg * d + c];
+        }
+        red[w][lane] = s;
+        __syncthreads();
+        if (w == 0 && c < d) {
+            double t = red[0][lane];
+#pragma unroll
+            for (int ww = 1; ww < kFixWaves; ++ww) t += red[ww][lane];
+            sums[(int64_t)k * d + c] += t;
+        }
+        __syncthreads();
+    }
+}
+
+// cnt[k] += size of cluster k in this batch of rows.
+__global__ __launch_bounds__(256) void k_count_acc(const int32_t *__restrict__ offsets, int K,
+                                                   int32_t *__restrict__ cnt) {
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k < K) cnt[k] += offsets[k + 1] - offsets[k];
+}
+
+// C_out = sums / cnt, or C_prev for an empty cluster; counts_out = cnt.
+__global__ __launch_bounds__(256) void k_finalize(const double *__restrict__ sums, const int32_t *__restrict__ cnt,
+                                                  const float *__restrict__ C_prev, int64_t total, int d,
+                                                  float *__restrict__ C_out, int32_t *__restrict__ counts_out) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= total) return;
+    const int64_t k = q / d;
+    const int c = cnt[k];
+    C_out[q] = c > 0 ? (float)(sums[q] / (double)c) : C_prev[q];
+    if (q == k * d) counts_out[k] = c;
+}
+
+// ---------------------------------------------------------------------------
+hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
+    const int64_t n = (int64_t)(bytes / 4);
+    if (n <= 0) return hipSuccess;
+    int64_t nb = cdiv(n, 256);
+    if (nb > 4096) nb = 4096;
+    hipLaunchKernelGGL(k_fill_zero, dim3((unsigned)nb), dim3(256), 0, s, (uint32_t *)p, n);
+    return hipGetLastError();
+}
+
+template <int NV, int E>
+static hipError_t seg_launch(const float *X, int64_t N, int d, const int32_t *ks, const int32_t *perm,
+                             const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
+    constexpr int U = NV <= 2 ? 8 : 4;
+    const int64_t nseg = cdiv(N, kSegRows);
+    const unsigned gy = (unsigned)cdiv(d, 64 * E * NV);
+    hipLaunchKernelGGL((k_seg_reduce<NV, E, U>), dim3((unsigned)cdiv(nseg, kSegWaves), gy), dim3(kSegWaves * 64), 0,
+                       s, X, N, d, ks, perm, xnorm64, sums, pfirst, plast);
+    return hipGetLastError();
+}
+
+hipError_t launch_seg_reduce(const float *X, int64_t N, int d, const int32_t *ks, const int32_t *perm,
+                             const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    const int E = (d % 2 == 0) ? 2 : 1;
+    const int need = (int)cdiv(d, 64 * E);
+    if (E == 2) {
+        if (need <= 1) return seg_launch<1, 2>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+        if (need <= 2) return seg_launch<2, 2>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+        if (need <= 4) return seg_launch<4, 2>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+        return seg_launch<8, 2>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    }
+    if (need <= 1) return seg_launch<1, 1>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (need <= 2) return seg_launch<2, 1>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (need <= 4) return seg_launch<4, 1>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    return seg_launch<8, 1>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+}
+
+hipError_t launch_seg_fixup(const int32_t *ks, const int32_t *offsets, int64_t N, int d, const double *pfirst,
+                            const double *plast, double *sums, hipStream_t s) {
+    const int64_t nseg = cdiv(N, kSegRows);
+    if (nseg <= 1) return hipSuccess;
+    hipLaunchKernelGGL(k_seg_fixup, dim3((unsigned)(nseg - 1)), dim3(kFixWaves * 64), 0, s, ks, offsets, N, d,
+                       pfirst, plast, sums);
+    return hipGetLastError();
+}
+
+hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, hipStream_t s) {
+    hipLaunchKernelGGL(k_count_acc, dim3((unsigned)cdiv(K, 256)), dim3(256), 0, s, offsets, K, cnt);
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(const double *sums, const int32_t *cnt, const float *C_prev, int K, int d, float *C_out,
+                           int32_t *counts_out, hipStream_t s) {
+    const int64_t total = (int64_t)K * d;
+    hipLaunchKernelGGL(k_finalize, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, sums, cnt, C_prev, total, d,
+                       C_out, counts_out);
+    return hipGetLastError();
+}
+
+}  // namespace fk

@@ -1,0 +1,129 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol include/fk.h
+declares, names its status codes, sizes workspaces, and rejects bad arguments
+before touching any device (so no GPU is needed here)."""
+import ctypes
+import os
+
+import pytest
+
+import exact_lloyd_means_flashassign_amd as fk
+
+OK, INVALID, UNSUPPORTED, WORKSPACE, NO_DEVICE, HIPERR = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fk.LIB_PATH):
+        from exact_lloyd_means_flashassign_amd import build
+        build.build()
+    return fk.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = fk.declared_symbols()
+    expected = {"fk_workspace_size", "fk_assign", "fk_sort_inverse", "fk_update", "fk_lloyd_iter",
+                "fk_lloyd_iter_stream", "fk_status_str", "fk_last_error", "fk_profile_enable", "fk_profile_read"}
+    assert expected <= set(names)
+    raw = ctypes.CDLL(fk.LIB_PATH)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+def test_status_names(lib):
+    names = [fk.fk_status_str(i) for i in range(6)]
+    assert names == ["FK_OK", "FK_ERR_INVALID_ARG", "FK_ERR_UNSUPPORTED", "FK_ERR_WORKSPACE",
+                     "FK_ERR_NO_DEVICE", "FK_ERR_HIP"]
+    assert fk.fk_status_str(99) == "FK_ERR_UNKNOWN"
+
+
+def test_workspace_sizes(lib):
+    a = fk.fk_workspace_size(1000, 128, 1024)
+    b = fk.fk_workspace_size(100000, 128, 1024)
+    assert 0 < a < b
+    assert fk.fk_workspace_size(0, 16, 64) > 0
+    assert fk.fk_workspace_size(1000, 128, 1024, "cosine") > a
+    s = fk.fk_workspace_size(10 ** 9, 128, 32768, "l2", chunk_rows=1 << 20)
+    assert s > 2 * (1 << 20) * 128 * 4          # two chunk buffers
+    # the zipf 16M x 128, K=32768 shape fits comfortably in 288 GB
+    assert fk.fk_workspace_size(1 << 24, 128, 32768) < 2 * 10 ** 9
+    for bad in [(-1, 16, 4), (10, 0, 4), (10, 16, 0), (10, 16, 65537), (10, 4097, 4), (2 ** 31, 4, 4)]:
+        assert lib.fk_workspace_size(*bad, 0, 0) == 0
+    assert lib.fk_workspace_size(10, 4, 4, 2, 0) == 0            # inner product
+
+
+P = ctypes.c_void_p
+
+
+def _fake(addr):
+    return P(addr)
+
+
+def _call_assign(lib, N=100, d=8, K=4, metric=0, X=0x10000, C=0x20000, a=0x30000, ws=0x100000, wsn=1 << 30):
+    return lib.fk_assign(_fake(X) if X else None, N, d, _fake(C) if C else None, K, metric,
+                         _fake(a) if a else None, None, _fake(ws) if ws else None, wsn, None)
+
+
+def test_validation_happens_before_any_device_call(lib):
+    assert _call_assign(lib, N=-1) == INVALID
+    assert _call_assign(lib, d=0) == INVALID
+    assert _call_assign(lib, d=5000) == INVALID
+    assert _call_assign(lib, K=0) == INVALID
+    assert _call_assign(lib, K=70000) == INVALID
+    assert _call_assign(lib, metric=2) == UNSUPPORTED
+    assert b"inner-product" in lib.fk_last_error()
+    assert _call_assign(lib, metric=7) == INVALID
+    assert _call_assign(lib, X=0) == INVALID
+    assert _call_assign(lib, C=0) == INVALID
+    assert _call_assign(lib, a=0) == INVALID
+    assert _call_assign(lib, X=0x10004) == INVALID                # X not 16-byte aligned
+    assert _call_assign(lib, ws=0) == WORKSPACE
+    assert _call_assign(lib, ws=0x100010) == WORKSPACE            # not 256-byte aligned
+    assert _call_assign(lib, wsn=100) == WORKSPACE
+    assert b"needed" in lib.fk_last_error()
+
+
+def test_update_and_iter_reject_aliasing(lib):
+    K, d = 16, 8
+    C = 0x200000
+    st = lib.fk_update(_fake(0x10000), 10, d, _fake(0x30000), K, 0, _fake(C), _fake(C + 64), _fake(0x40000),
+                       _fake(0x1000000), 1 << 30, None)
+    assert st == INVALID and b"overlaps" in lib.fk_last_error()
+    st = lib.fk_lloyd_iter(_fake(0x10000), 10, d, _fake(C), K, 0, _fake(0x30000), None, _fake(C), _fake(0x40000),
+                           _fake(0x1000000), 1 << 30, None)
+    assert st == INVALID
+    st = lib.fk_lloyd_iter(_fake(0x10000), 10, d, _fake(C), K, 0, _fake(0x30000), None, None, _fake(0x40000),
+                           _fake(0x1000000), 1 << 30, None)
+    assert st == INVALID
+
+
+def test_stream_rejects_bad_chunks(lib):
+    st = lib.fk_lloyd_iter_stream(_fake(0x10000), 100, 8, _fake(0x20000), 4, 0, 0, None, _fake(0x30000),
+                                  _fake(0x40000), _fake(0x1000000), 1 << 30, None)
+    assert st == INVALID and b"chunk_rows" in lib.fk_last_error()
+
+
+def test_sort_inverse_validation(lib):
+    assert lib.fk_sort_inverse(None, 10, 4, _fake(0x10000), _fake(0x20000), _fake(0x100000), 1 << 30, None) == INVALID
+    assert lib.fk_sort_inverse(_fake(0x10000), 10, 4, _fake(0x20000), None, _fake(0x100000), 1 << 30, None) == INVALID
+    assert lib.fk_sort_inverse(_fake(0x10000), 10, 0, _fake(0x20000), _fake(0x30000), _fake(0x100000), 1 << 30,
+                               None) == INVALID
+
+
+@pytest.mark.skipif(__import__("torch").cuda.device_count() > 0, reason="a device is visible")
+def test_no_device_is_reported(lib):
+    assert _call_assign(lib) == NO_DEVICE
+    assert b"no HIP device" in lib.fk_last_error()
+
+
+def test_binding_rejects_host_tensors(lib):
+    import torch
+    X = torch.zeros(10, 4)
+    with pytest.raises(ValueError):
+        fk.fk_assign(X, X[:2].clone())
+
+
+def test_profile_api_without_device(lib):
+    fk.fk_profile_enable(True)
+    r = fk.fk_profile_read()
+    assert r["rechecked"] == 0 and all(v == 0 for v in r["calls"].values())
+    fk.fk_profile_enable(False)

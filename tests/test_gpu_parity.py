@@ -1,0 +1,178 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle on the
+same seeded inputs.  Shapes span several tiles and ragged tails in N, d and
+K, plus the degenerate cases (K=1, K>N, N=1, duplicated centroids, exact ties
+on integer grids, zero rows, a large common offset)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import centroid_rel_err, check_min_dist, check_update, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+SHAPES = [
+    (1, 1, 1), (5, 3, 7), (64, 4, 1), (1000, 16, 64), (4097, 128, 33), (3000, 100, 1000), (2049, 129, 65),
+    (777, 768, 300), (500, 20, 4097), (300, 2048, 17), (2000, 31, 129), (130, 64, 3), (1025, 2, 2),
+]
+
+
+@pytest.mark.parametrize("N,d,K", SHAPES)
+@pytest.mark.parametrize("kind", ["gauss", "dup", "grid", "far", "zero"])
+def test_assign_matches_oracle(gpu_lib, N, d, K, kind):
+    fk = gpu_lib
+    log(f"assign N={N} d={d} K={K} kind={kind}")
+    X, C = synth.adversarial(3, N, d, K, kind)
+    a_ref, D1, D2 = oracle.assign(X, C)
+    a, md = fk.fk_assign(dev(X), dev(C), with_min_dist=True)
+    a = host(a)
+    np.testing.assert_array_equal(a, a_ref)
+    check_min_dist(host(md), D1, X, C)
+
+
+@pytest.mark.parametrize("N,d,K", [(1000, 16, 64), (3001, 128, 257), (400, 768, 100), (999, 7, 5)])
+@pytest.mark.parametrize("kind", ["gauss", "zero", "dup"])
+def test_assign_cosine_matches_oracle(gpu_lib, N, d, K, kind):
+    fk = gpu_lib
+    log(f"cosine assign N={N} d={d} K={K} kind={kind}")
+    X, C = synth.adversarial(4, N, d, K, kind)
+    X[::3] *= np.float32(7.0)
+    a_ref, D1, _ = oracle.assign(X, C, "cosine")
+    a, md = fk.fk_assign(dev(X), dev(C), metric="cosine", with_min_dist=True)
+    np.testing.assert_array_equal(host(a), a_ref)
+    check_min_dist(host(md), D1, X, C, "cosine")
+
+
+@pytest.mark.parametrize("N,d,K", [(1, 4, 1), (1000, 16, 64), (5000, 128, 1024), (4096 * 3 + 5, 8, 300),
+                                   (2048 * 5 + 7, 65, 40), (300, 768, 4096), (20000, 3, 2), (9000, 1030, 7)])
+@pytest.mark.parametrize("metric", ["l2", "cosine"])
+def test_update_matches_oracle(gpu_lib, N, d, K, metric):
+    fk = gpu_lib
+    log(f"update N={N} d={d} K={K} {metric}")
+    rng = np.random.default_rng([N, d, K])
+    X = rng.standard_normal((N, d)).astype(np.float32)
+    # skewed labels, with some clusters left empty
+    w = (np.arange(1, K + 1) ** -1.2)
+    w /= w.sum()
+    a = rng.choice(K, size=N, p=w).astype(np.int32)
+    C_prev = rng.standard_normal((K, d)).astype(np.float32)
+    C_out, counts = fk.fk_update(dev(X), dev(a), dev(C_prev), metric=metric)
+    check_update(X, a, C_prev, host(C_out), host(counts), metric)
+
+
+def test_update_single_giant_cluster(gpu_lib):
+    """Every point in one cluster: the cluster crosses every segment boundary."""
+    fk = gpu_lib
+    N, d, K = 200000, 64, 5
+    rng = np.random.default_rng(9)
+    X = rng.standard_normal((N, d)).astype(np.float32)
+    a = np.full(N, 3, np.int32)
+    C_prev = rng.standard_normal((K, d)).astype(np.float32)
+    C_out, counts = fk.fk_update(dev(X), dev(a), dev(C_prev))
+    check_update(X, a, C_prev, host(C_out), host(counts))
+
+
+def test_update_empty_input(gpu_lib):
+    fk = gpu_lib
+    C_prev = np.random.default_rng(1).standard_normal((9, 5)).astype(np.float32)
+    X = torch.empty((0, 5), dtype=torch.float32, device="cuda:0")
+    a = torch.empty(0, dtype=torch.int32, device="cuda:0")
+    C_out, counts = fk.fk_update(X, a, dev(C_prev))
+    assert host(counts).tolist() == [0] * 9
+    assert np.array_equal(host(C_out), C_prev)
+
+
+@pytest.mark.parametrize("N,K", [(0, 5), (1, 1), (100, 1), (4096, 256), (4097, 257), (10000, 2), (70000, 1024),
+                                 (300000, 32768), (50000, 65536), (8191, 255)])
+def test_sort_inverse_matches_stable_argsort(gpu_lib, N, K):
+    fk = gpu_lib
+    log(f"sort N={N} K={K}")
+    rng = np.random.default_rng([N, K])
+    a = rng.integers(0, K, size=N).astype(np.int32)
+    if N > 100:
+        a[: N // 3] = K - 1      # a long run of one key, and skew
+    perm, offsets = fk.fk_sort_inverse(dev(a), K) if N > 0 else fk.fk_sort_inverse(
+        torch.empty(0, dtype=torch.int32, device="cuda:0"), K)
+    perm = host(perm)
+    offsets = host(offsets)
+    np.testing.assert_array_equal(perm, np.argsort(a, kind="stable"))
+    expect = np.concatenate([[0], np.cumsum(np.bincount(a, minlength=K))])
+    np.testing.assert_array_equal(offsets, expect)
+
+
+@pytest.mark.parametrize("name,N,iters", [("tiny_d16_k64", 65536, 3), ("gmm_1m_d128_k1024", 60000, 3),
+                                          ("ivf_1m_d768_k4096", 12000, 2), ("zipf_16m_d128_k32768", 33000, 2)])
+def test_lloyd_iterations_step_level(gpu_lib, name, N, iters):
+    """Step-level protocol: at every iteration the oracle is given the GPU's
+    own centroids; assignments and counts must match exactly and centroids to
+    1e-6 relative, and the objective must not increase."""
+    fk = gpu_lib
+    w = synth.WORKLOADS[name].scaled(N)
+    log(f"iterations {name} N={N}")
+    X = synth.rows(w)
+    C = synth.initial_centroids(w, X)
+    Xd = dev(X)
+    Cd = dev(C)
+    Js = []
+    for t in range(iters):
+        a, C1, counts, md = fk.fk_lloyd_iter(Xd, Cd, with_min_dist=True)
+        ref = oracle.lloyd_iter(X, C)
+        a_h = host(a)
+        np.testing.assert_array_equal(a_h, ref["a"])
+        np.testing.assert_array_equal(host(counts), ref["counts"])
+        err = centroid_rel_err(host(C1), ref["C"], ref["counts"])
+        assert err <= 1e-6, err
+        assert host(counts).sum() == N
+        Js.append(ref["J"])
+        C = host(C1).copy()
+        Cd = C1
+    for j0, j1 in zip(Js, Js[1:]):
+        assert j1 <= j0 * (1 + 1e-6)
+
+
+def test_determinism_bitwise(gpu_lib):
+    fk = gpu_lib
+    w = synth.WORKLOADS["zipf_16m_d128_k32768"].scaled(300000)
+    X = synth.rows(w)
+    C = synth.initial_centroids(w, X)
+    Xd, Cd = dev(X), dev(C)
+    r1 = [host(t) for t in fk.fk_lloyd_iter(Xd, Cd, with_min_dist=True)]
+    r2 = [host(t) for t in fk.fk_lloyd_iter(Xd, Cd, with_min_dist=True)]
+    for u, v in zip(r1, r2):
+        assert u.tobytes() == v.tobytes()
+
+
+def test_k_larger_than_n(gpu_lib):
+    fk = gpu_lib
+    X, C = synth.adversarial(5, 50, 12, 200)
+    a, C1, counts, _ = fk.fk_lloyd_iter(dev(X), dev(C))
+    ref = oracle.lloyd_iter(X, C)
+    np.testing.assert_array_equal(host(a), ref["a"])
+    np.testing.assert_array_equal(host(counts), ref["counts"])
+    assert (host(counts) == 0).sum() >= 150
+    check_update(X, ref["a"], C, host(C1), host(counts))
+
+
+def test_error_paths_on_device(gpu_lib):
+    fk = gpu_lib
+    X = torch.zeros((100, 8), device="cuda:0")
+    C = torch.zeros((4, 8), device="cuda:0")
+    with pytest.raises(fk.FkError) as e:
+        fk.fk_assign(X, C, metric="inner_product")
+    assert e.value.status == 2
+    small = torch.empty(1024, dtype=torch.uint8, device="cuda:0")
+    with pytest.raises(fk.FkError) as e:
+        fk.fk_assign(X, C, workspace=small)
+    assert e.value.status == 3
+    host_x = torch.zeros((100, 8))          # pageable
+    import ctypes
+    lib = fk.load()
+    ws = torch.empty(fk.fk_workspace_size(100, 8, 4, "l2", 50) + 256, dtype=torch.uint8, device="cuda:0")
+    base = ws.data_ptr() + (-ws.data_ptr()) % 256
+    out = torch.empty((4, 8), device="cuda:0")
+    cnt = torch.empty(4, dtype=torch.int32, device="cuda:0")
+    st = lib.fk_lloyd_iter_stream(ctypes.c_void_p(host_x.data_ptr()), 100, 8, ctypes.c_void_p(C.data_ptr()), 4, 0, 50,
+                                  None, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(cnt.data_ptr()),
+                                  ctypes.c_void_p(base), ws.numel() - 256, None)
+    assert st == 1 and b"pinned" in lib.fk_last_error()

@@ -1,0 +1,52 @@
+"""Out-of-core iteration (pinned host X streamed in chunks) against the
+in-core iteration and the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import centroid_rel_err, dev, host, log
+
+pytestmark = pytest.mark.gpu
+
+
+def _pinned(a):
+    t = torch.empty(a.shape, dtype=torch.from_numpy(a[:0]).dtype, pin_memory=True)
+    t.numpy()[...] = a
+    return t
+
+
+@pytest.mark.parametrize("metric", ["l2", "cosine"])
+@pytest.mark.parametrize("chunk", [100000, 65537, 300000, 300005, 4096])
+def test_stream_equals_in_core(gpu_lib, chunk, metric):
+    fk = gpu_lib
+    w = synth.WORKLOADS["ooc_1b_d128_k32768"].scaled(300000)
+    K = 2048
+    log(f"stream chunk={chunk} {metric}")
+    X = synth.rows(w)
+    C = X[synth.init_indices(w)[:K]].copy()
+    a_ic, C_ic, n_ic, _ = fk.fk_lloyd_iter(dev(X), dev(C), metric=metric)
+    Xh = _pinned(X)
+    ah = torch.empty(w.N, dtype=torch.int32, pin_memory=True)
+    C_s, n_s = fk.fk_lloyd_iter_stream(Xh, dev(C), chunk, metric=metric, assign_host=ah)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ah.numpy(), host(a_ic))
+    np.testing.assert_array_equal(host(n_s), host(n_ic))
+    err = centroid_rel_err(host(C_s), host(C_ic).astype(np.float64), host(n_ic))
+    assert err <= 1e-6, err
+    # and against the oracle on a sample of points
+    idx = np.random.default_rng(0).choice(w.N, 500, replace=False)
+    a_ref, _, _ = oracle.assign(X[idx], C, metric)
+    np.testing.assert_array_equal(ah.numpy()[idx], a_ref)
+
+
+def test_stream_without_assignment_output(gpu_lib):
+    fk = gpu_lib
+    w = synth.WORKLOADS["tiny_d16_k64"]
+    X = synth.rows(w)
+    C = synth.initial_centroids(w, X)
+    C_s, n_s = fk.fk_lloyd_iter_stream(_pinned(X), dev(C), 10000)
+    ref = oracle.lloyd_iter(X, C)
+    np.testing.assert_array_equal(host(n_s), ref["counts"])
+    assert centroid_rel_err(host(C_s), ref["C"], ref["counts"]) <= 1e-6
