@@ -1,0 +1,170 @@
+"""Benchmark: seconds per exact Lloyd iteration on one MI355X, with assign
+TFLOP/s and update GB/s, on the skewed large-K workload (16,777,216 x 128,
+K = 32,768, Zipf(1.2) mixture).
+
+One step = one full Lloyd iteration (FlashAssign + fp64 near-tie recheck +
+Sort-Inverse Update) through the C ABI, with X and C resident in HBM.  Prints
+one JSON line.  Phase times come from HIP events the library records on the
+stream it launches on; the FlashAssign kernel's average duration gives the
+roofline line.  The CPU baseline times the fp64 oracle on a bounded sample of
+the same workload on this host's cores and scales it to the full N.
+
+usage: python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--workload NAME]
+                       [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, TFLOP/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_assign_zipf_16m_d128_k32768_traffic.json")
+ASSIGN_SRC = os.path.join(ROOT, "exact_lloyd_means_flashassign_amd", "csrc", "fk_assign.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def source_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_per_launch():
+    """HBM bytes per FlashAssign launch from the committed rocprofv3 counter
+    summary, or None when the kernel source changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha") != source_sha(ASSIGN_SRC):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, X, C, budget_s=15.0):
+    """Time the fp64 oracle on a bounded sample (the first n rows, all K
+    centroids) and scale seconds per iteration linearly to the full N."""
+    import oracle
+    probe = 512
+    t0 = time.perf_counter()
+    oracle.lloyd_iter(X[:probe], C)
+    dt = time.perf_counter() - t0
+    n = int(min(w.N, max(probe, budget_s / max(dt, 1e-9) * probe)))
+    t0 = time.perf_counter()
+    oracle.lloyd_iter(X[:n], C)
+    dt = time.perf_counter() - t0
+    return {"value": dt * w.N / n, "unit": "s/iter", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {n} of {w.N} points against all K={w.K} centroids, one iteration in {dt:.1f} s; "
+                      f"seconds per iteration scaled linearly by N/{n}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="zipf_16m_d128_k32768")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
+              "the per-GPU shard is what one GPU shows.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import exact_lloyd_means_flashassign_amd as fk
+    import synth
+
+    fk.load()
+    w = synth.WORKLOADS[args.workload]
+    if w.chunk_rows:
+        raise SystemExit("the out-of-core workload is not a bench line; use the in-core workloads")
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    X = synth.rows(w)
+    C0 = synth.initial_centroids(w, X)
+    log(f"generated {w.name}: N={w.N} d={w.d} K={w.K} in {time.perf_counter() - t0:.1f} s")
+    Xd = torch.from_numpy(X).to(dev)
+    Cs = [torch.from_numpy(C0).to(dev), torch.empty((w.K, w.d), dtype=torch.float32, device=dev)]
+    a = torch.empty(w.N, dtype=torch.int32, device=dev)
+    counts = torch.empty(w.K, dtype=torch.int32, device=dev)
+    ws = torch.empty(fk.fk_workspace_size(w.N, w.d, w.K, w.metric) + 256, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    def step(i):
+        fk.fk_lloyd_iter(Xd, Cs[i % 2], metric=w.metric, assign=a, C_out=Cs[(i + 1) % 2], counts=counts,
+                         workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+        log(f"warmup step {i} done")
+    torch.cuda.synchronize()
+    fk.fk_profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = fk.fk_profile_read()
+    fk.fk_profile_enable(False)
+    log(f"timed {args.steps} steps in {elapsed:.3f} s")
+    assert int(counts.sum().item()) == w.N
+
+    N, d, K = w.N, w.d, w.K
+    ms, calls = prof["ms"], prof["calls"]
+    per = {k: ms[k] / max(args.steps, 1) for k in ms}
+    t_assign = (per["prep"] + per["assign"] + per["recheck"]) / 1e3
+    t_update = (per["sort"] + per["reduce"] + per["finalize"]) / 1e3
+    flops = 2.0 * N * K * d
+    upd_bytes = 4.0 * (N * d + N + K * d + K)
+    fa_ms = ms["assign"] / max(calls["assign"], 1)
+    fa_tflops = flops / (fa_ms / 1e3) / 1e12
+    traffic = traffic_per_launch()
+    out = {
+        "metric": "s per Lloyd iter; assign TFLOP/s & update GB/s at N=16M,d=128,K=32768",
+        "value": elapsed / args.steps,
+        "unit": "s/iter",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": 1e3 * elapsed / args.steps,
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "N": N, "d": d, "K": K, "metric": w.metric, "sigma": w.sigma,
+                   "weights": w.weights if w.weights == "equal" else f"zipf({w.zipf_s})", "seed": w.seed},
+        "assign_tflops": flops / t_assign / 1e12,
+        "update_gbps": upd_bytes / t_update / 1e9,
+        "assign_frac_fp32_mfma": flops / t_assign / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+        "update_frac_hbm": upd_bytes / t_update / 1e9 / HBM_PEAK_GBS,
+        "phase_ms_per_step": {k: round(v, 4) for k, v in per.items()},
+        "near_tie_fraction": {"pair": prof["paired"] / max(prof["assigned"], 1),
+                              "full": prof["rechecked"] / max(prof["assigned"], 1)},
+        "roofline": {"kernel": "k_flash_assign", "bound": "mfma", "achieved": fa_tflops,
+                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": fa_tflops / FP32_MFMA_PEAK_TFLOPS,
+                     "avg_ms": fa_ms, "traffic": traffic},
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        out["cpu_baseline"] = cpu_baseline(w, X, C0)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

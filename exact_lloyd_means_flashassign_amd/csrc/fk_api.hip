@@ -38,7 +38,7 @@ fk_status hip_fail(hipError_t e, const char *what) {
 // ---- workspace layout -----------------------------------------------------
 struct Layout {
     size_t total = 0;
-    size_t ncn, cmax_part, scal, counter, flags;
+    size_t ncn, cmax_part, scal, counter, flags, pairs;
     size_t c64, c32, cnrm64, xnorm64;  // cosine only (else ~0)
     size_t keys_sorted, perm, tmp_keys, tmp_vals, sort_scratch, offsets;
     size_t sums, cnt, pfirst, plast;
@@ -64,6 +64,7 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc) {
     L.scal = take(64);
     L.counter = take(64);
     L.flags = take((size_t)r * 4);
+    L.pairs = take((size_t)r * 12);
     L.c64 = cos ? take((size_t)K * d * 8) : kNone;
     L.c32 = cos ? take((size_t)K * d * 4) : kNone;
     L.cnrm64 = cos ? take((size_t)K * 8) : kNone;
@@ -178,17 +179,17 @@ struct PhaseScope {
     }
 };
 
-void prof_count_rechecks(const int32_t *dev_counter, int64_t n_assigned, hipStream_t s) {
+void prof_count_rechecks(const int32_t *dev_counters, int64_t n_assigned, hipStream_t s) {
     std::lock_guard<std::mutex> g(g_prof.mu);
     if (!g_prof.on) return;
     if (g_prof.slots_used == g_prof.count_slots.size()) {
         int32_t *h = nullptr;
-        if (hipHostMalloc((void **)&h, sizeof(int32_t)) != hipSuccess) return;
+        if (hipHostMalloc((void **)&h, 2 * sizeof(int32_t)) != hipSuccess) return;
         g_prof.count_slots.push_back(h);
     }
     int32_t *slot = g_prof.count_slots[g_prof.slots_used++];
-    *slot = 0;
-    (void)hipMemcpyAsync(slot, dev_counter, sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    slot[0] = slot[1] = 0;
+    (void)hipMemcpyAsync(slot, dev_counters, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, s);
     g_prof.acc.assigned += n_assigned;
 }
 
@@ -239,15 +240,15 @@ fk_status step_assign(const Ctx &c, const float *X, int64_t rows, const float *C
     {
         PhaseScope ph(FK_PH_ASSIGN, c.s);
         FK_TRY(launch_flash_assign(X, rows, c.d, C_use, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal),
-                                   xn, a_out, d1_out, at<int32_t>(c.ws, c.L.flags), at<int32_t>(c.ws, c.L.counter),
-                                   c.s),
+                                   xn, a_out, d1_out, at<int32_t>(c.ws, c.L.flags), at<int32_t>(c.ws, c.L.pairs),
+                                   at<int32_t>(c.ws, c.L.counter), c.s),
                "flash assign");
     }
     {
         PhaseScope ph(FK_PH_RECHECK, c.s);
         const double *c64 = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.c64) : nullptr;
         FK_TRY(launch_recheck(X, rows, c.d, C, c64, c.K, xn, at<int32_t>(c.ws, c.L.flags),
-                              at<int32_t>(c.ws, c.L.counter), a_out, d1_out, c.s),
+                              at<int32_t>(c.ws, c.L.pairs), at<int32_t>(c.ws, c.L.counter), a_out, d1_out, c.s),
                "fp64 recheck");
     }
     prof_count_rechecks(at<int32_t>(c.ws, c.L.counter), rows, c.s);
@@ -516,7 +517,7 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
         FK_TRY(hipStreamWaitEvent(c.s, R->copied[b], 0), "stream wait");
         if ((st = step_xnorm(c, Xd, rows)) != FK_OK) return st;
         // the near-tie list is per chunk: reset its counter
-        FK_TRY(launch_fill_zero(at<void>(workspace, L.counter), 4, c.s), "reset counter");
+        FK_TRY(launch_fill_zero(at<void>(workspace, L.counter), 8, c.s), "reset counters");
         if ((st = step_assign(c, Xd, rows, C_in, Cu, ad, nullptr)) != FK_OK) return st;
         if ((st = step_accumulate(c, Xd, rows, ad)) != FK_OK) return st;
         FK_TRY(hipEventRecord(R->freed[b], c.s), "event record");
@@ -558,7 +559,10 @@ fk_status fk_profile_read(fk_profile *out) {
     }
     g_prof.pending.clear();
     if (g_prof.slots_used > 0) FK_TRY(hipDeviceSynchronize(), "device sync");
-    for (size_t i = 0; i < g_prof.slots_used; ++i) g_prof.acc.rechecked += *g_prof.count_slots[i];
+    for (size_t i = 0; i < g_prof.slots_used; ++i) {
+        g_prof.acc.rechecked += g_prof.count_slots[i][0];
+        g_prof.acc.paired += g_prof.count_slots[i][1];
+    }
     g_prof.slots_used = 0;
     *out = g_prof.acc;
     g_prof.acc = fk_profile{};

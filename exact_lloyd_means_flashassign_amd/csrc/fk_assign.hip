@@ -12,11 +12,13 @@
 //   * each wave keeps its points in VGPRs; centroid tiles are staged through
 //     LDS (double-buffered) and shared by the 4 waves of a workgroup;
 //   * the MFMA output puts one point per lane and 16 centroids per lane, so
-//     the running top-2 is kept per lane with no cross-lane traffic; lanes l
+//     the running top-3 is kept per lane with no cross-lane traffic; lanes l
 //     and l^32 are merged once, after the last tile;
-//   * exactness: the fp32 accumulator has a proven error bound e_i; a point
-//     whose top-2 gap is within 2 e_i is listed, and k_recheck rescores it in
-//     fp64 with the direct-difference distance, which is the definition.
+//   * exactness: the fp32 accumulator has a proven error bound e_i.  A point
+//     whose top-2 gap is within 2 e_i is a near tie.  If its third score is
+//     more than 2 e_i below the best, only the top two can win and
+//     k_recheck_pair compares those two in fp64 by direct difference (the
+//     distance definition); otherwise k_recheck rescores it against all K.
 #include "fk_internal.h"
 
 namespace fk {
@@ -92,7 +94,7 @@ __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__
     if (threadIdx.x == 0) cmax_part[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
-// scal[0] = max_k ||c_k||^2 (fp32); resets the near-tie counter.
+// scal[0] = max_k ||c_k||^2 (fp32); resets the two near-tie list counters.
 __global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ cmax_part, int nparts,
                                                      float *__restrict__ scal, int32_t *__restrict__ counter) {
     __shared__ float sm[256];
@@ -106,7 +108,8 @@ __global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ c
     }
     if (threadIdx.x == 0) {
         scal[0] = sm[0];
-        *counter = 0;
+        counter[0] = 0;
+        counter[1] = 0;
     }
 }
 
@@ -134,23 +137,26 @@ __global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ c
 // M >= max ||c||^2 and the norms rounded up,
 //     e_i = 1.0625 g (M + ||x_i|| sqrt(M))
 // bounds the error of every accumulator of point i.  If best - second > 2 e_i
-// the fp32 winner is the strict exact winner, with a margin far above the fp64
-// rounding of a direct-difference distance.  Otherwise the point is listed for
-// k_recheck.  For cosine, the fp32 normalised rows differ from the fp64
+// the fp32 winner is the strict exact winner, with a margin (at least
+// 0.125 e_i) far above the fp64 rounding of a direct-difference distance.
+// Otherwise, if best - third > 2 e_i, every centroid but the top two is
+// excluded with the same margin and the point goes on the pair list; else on
+// the full list.  For cosine, the fp32 normalised rows differ from the fp64
 // normalised ones by at most 3.1u relative, which moves a by at most
 // 3.1u (||x|| ||c|| + ||c||^2); 8u is added to g for it.
-template <int DP, int PB, int CB>
-__global__ __launch_bounds__(kAssignThreads, 2) void k_flash_assign(
+template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool VEC>
+__global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(
     const float *__restrict__ X, int64_t N, int d, int nch, const float *__restrict__ C,
     const float *__restrict__ ncn, int K, int ntiles, const float *__restrict__ scal,
     const double *__restrict__ xnorm64, int32_t *__restrict__ a_out, float *__restrict__ d1_out,
-    int32_t *__restrict__ flag_list, int32_t *__restrict__ flag_count) {
+    int32_t *__restrict__ full_list, int32_t *__restrict__ pair_list, int32_t *__restrict__ counters) {
+    constexpr int NT = WAVES * 64;
     constexpr int HALF = DP / 2;
     constexpr int ROWS = CB * 32;
     constexpr int LDR = DP + 4;  // padded LDS row: 8 consecutive lanes hit distinct 16-B bank groups
     constexpr int Q4 = DP / 4;
     constexpr int NQ4 = ROWS * Q4;
-    constexpr int PFN = (NQ4 + kAssignThreads - 1) / kAssignThreads;
+    constexpr int PFN = (NQ4 + NT - 1) / NT;
     static_assert(HALF % 4 == 0, "DP must be a multiple of 8");
 
     __shared__ __attribute__((aligned(16))) float sC[2][ROWS * LDR];
@@ -161,15 +167,15 @@ __global__ __launch_bounds__(kAssignThreads, 2) void k_flash_assign(
     const int lane = tid & 63;
     const int h = lane >> 5;
     const int jl = lane & 31;
-    const int64_t pbase = ((int64_t)blockIdx.x * kAssignWaves + wv) * (PB * 32);
-    const bool vec4 = (d & 3) == 0;
+    const int64_t pbase = ((int64_t)blockIdx.x * WAVES + wv) * (PB * 32);
 
+    // global -> registers for one centroid stage (tile t, d-chunk ch)
     float4 pf[PFN];
     float pn = 0.f;
     auto load_stage = [&](int t, int ch) {
 #pragma unroll
         for (int i = 0; i < PFN; ++i) {
-            const int q = tid + i * kAssignThreads;
+            const int q = tid + i * NT;
             float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
             if (q < NQ4) {
                 const int row = q / Q4;
@@ -177,7 +183,7 @@ __global__ __launch_bounds__(kAssignThreads, 2) void k_flash_assign(
                 const int k = t * ROWS + row;
                 if (k < K) {
                     const float *src = C + (size_t)k * d + col;
-                    if (vec4) {
+                    if (VEC) {
                         if (col < d) v = *reinterpret_cast<const float4 *>(src);
                     } else {
                         if (col < d) v.x = src[0];
@@ -191,51 +197,53 @@ __global__ __launch_bounds__(kAssignThreads, 2) void k_flash_assign(
         }
         if (ch == 0 && tid < ROWS) pn = ncn[t * ROWS + tid];
     };
+    // registers -> LDS buffer
     auto store_stage = [&](int buf, int ch) {
 #pragma unroll
         for (int i = 0; i < PFN; ++i) {
-            const int q = tid + i * kAssignThreads;
+            const int q = tid + i * NT;
             if (q < NQ4) *reinterpret_cast<float4 *>(&sC[buf][(q / Q4) * LDR + (q % Q4) * 4]) = pf[i];
         }
         if (ch == 0 && tid < ROWS) sN[buf][tid] = pn;
     };
 
     float xr[PB][HALF];
-    float xn[PB], xsc[PB], best[PB], sec[PB];
-    int idx[PB];
+    // running top-3 scores per point (b1 >= b2 >= b3) and the indices of the
+    // first two
+    float xn[PB], xsc[PB], b1[PB], b2[PB], b3[PB];
+    int i1[PB], i2[PB];
 #pragma unroll
     for (int b = 0; b < PB; ++b) {
         const int64_t p = pbase + b * 32 + jl;
         xn[b] = 0.f;
         xsc[b] = (xnorm64 != nullptr && p < N) ? (float)(1.0 / xnorm64[p]) : 1.f;
-        best[b] = -INFINITY;
-        sec[b] = -INFINITY;
-        idx[b] = 0;
+        b1[b] = -INFINITY;
+        b2[b] = -INFINITY;
+        b3[b] = -INFINITY;
+        i1[b] = 0;
+        i2[b] = 0;
     }
+    // this wave's points, dims ch*DP + h*HALF + [0, HALF), into registers
     auto load_x = [&](int ch, bool add_norm) {
 #pragma unroll
         for (int b = 0; b < PB; ++b) {
             const int64_t p = pbase + b * 32 + jl;
             const int col0 = ch * DP + h * HALF;
             const float *src = X + (size_t)p * d + col0;
-            if (p < N) {
-                if (vec4) {
+            const bool pin = p < N;
+            if (VEC) {
 #pragma unroll
-                    for (int s = 0; s < HALF; s += 4) {
-                        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                        if (col0 + s < d) v = *reinterpret_cast<const float4 *>(src + s);
-                        xr[b][s] = v.x;
-                        xr[b][s + 1] = v.y;
-                        xr[b][s + 2] = v.z;
-                        xr[b][s + 3] = v.w;
-                    }
-                } else {
-#pragma unroll
-                    for (int s = 0; s < HALF; ++s) xr[b][s] = (col0 + s < d) ? src[s] : 0.f;
+                for (int s = 0; s < HALF; s += 4) {
+                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (pin && col0 + s < d) v = *reinterpret_cast<const float4 *>(src + s);
+                    xr[b][s] = v.x;
+                    xr[b][s + 1] = v.y;
+                    xr[b][s + 2] = v.z;
+                    xr[b][s + 3] = v.w;
                 }
             } else {
 #pragma unroll
-                for (int s = 0; s < HALF; ++s) xr[b][s] = 0.f;
+                for (int s = 0; s < HALF; ++s) xr[b][s] = (pin && col0 + s < d) ? src[s] : 0.f;
             }
             if (xnorm64 != nullptr) {
 #pragma unroll
@@ -251,23 +259,26 @@ __global__ __launch_bounds__(kAssignThreads, 2) void k_flash_assign(
     };
 
     v16f acc[PB][CB];
-    const int nst = ntiles * nch;
+    const int cnch = RES ? 1 : nch;
+    const int nst = ntiles * cnch;
+    if (RES) load_x(0, true);
     load_stage(0, 0);
     store_stage(0, 0);
-    if (nch == 1) load_x(0, true);
     __syncthreads();
 
     int t = 0, ch = 0;
     for (int st = 0; st < nst; ++st) {
         const int buf = st & 1;
         int nt = t, nc = ch + 1;
-        if (nc == nch) {
+        if (nc == cnch) {
             nc = 0;
             nt = t + 1;
         }
         const bool more = st + 1 < nst;
+        // the chunk's own points first, so that waiting for them does not
+        // also wait for the next stage's prefetch
+        if (!RES) load_x(ch, t == 0);
         if (more) load_stage(nt, nc);
-        if (nch > 1) load_x(ch, t == 0);
 
         if (ch == 0) {
 #pragma unroll
@@ -304,7 +315,7 @@ __global__ __launch_bounds__(kAssignThreads, 2) void k_flash_assign(
             }
         }
 
-        if (ch == nch - 1) {
+        if (ch == cnch - 1) {
             const int kt = t * ROWS + 4 * h;
 #pragma unroll
             for (int b = 0; b < PB; ++b) {
@@ -314,11 +325,17 @@ __global__ __launch_bounds__(kAssignThreads, 2) void k_flash_assign(
                     for (int r = 0; r < 16; ++r) {
                         const float v = acc[b][cb][r];
                         const int k = kt + cb * 32 + 8 * (r >> 2) + (r & 3);
-                        sec[b] = fmaxf(sec[b], fminf(v, best[b]));
-                        if (v > best[b]) {
-                            best[b] = v;
-                            idx[b] = k;
-                        }
+                        // insert v into the sorted top-3 with medians of three
+                        // (v_med3_f32); a strict '>' keeps the lower index first
+                        // on equal scores (k increases per lane)
+                        const bool c1 = v > b1[b];
+                        const bool c2 = v > b2[b];
+                        const int t2 = c2 ? k : i2[b];
+                        i2[b] = c1 ? i1[b] : t2;
+                        i1[b] = c1 ? k : i1[b];
+                        b3[b] = __builtin_amdgcn_fmed3f(b2[b], b3[b], v);
+                        b2[b] = __builtin_amdgcn_fmed3f(b1[b], b2[b], v);
+                        b1[b] = c1 ? v : b1[b];
                     }
                 }
             }
@@ -330,38 +347,98 @@ __global__ __launch_bounds__(kAssignThreads, 2) void k_flash_assign(
     }
 
     // merge the two half-waves (same point, the other 16 centroids of each
-    // 32-block): larger score wins, lower index on equal scores
+    // 32-block): larger score first, lower index first on equal scores
     const float u = 5.9604645e-8f;
     const float g = (float)(d + 4) * u + (xnorm64 != nullptr ? 8.f * u : 0.f);
     const float M = scal[0] * (1.f + g);
     const float sqM = sqrtf(M) * (1.f + 2.f * u);
 #pragma unroll
     for (int b = 0; b < PB; ++b) {
-        const float ob = __shfl_xor(best[b], 32);
-        const float os = __shfl_xor(sec[b], 32);
-        const int oi = __shfl_xor(idx[b], 32);
-        const float ns = fmaxf(fminf(best[b], ob), fmaxf(sec[b], os));
-        const bool take = (ob > best[b]) || (ob == best[b] && oi < idx[b]);
-        const float bb = take ? ob : best[b];
-        const int bi = take ? oi : idx[b];
+        const float o1 = __shfl_xor(b1[b], 32);
+        const float o2 = __shfl_xor(b2[b], 32);
+        const float o3 = __shfl_xor(b3[b], 32);
+        const int oi1 = __shfl_xor(i1[b], 32);
+        const int oi2 = __shfl_xor(i2[b], 32);
+        // W = the list whose head wins, L = the other
+        const bool take = (o1 > b1[b]) || (o1 == b1[b] && oi1 < i1[b]);
+        const float w1 = take ? o1 : b1[b], w2 = take ? o2 : b2[b], w3 = take ? o3 : b3[b];
+        const int wi1 = take ? oi1 : i1[b], wi2 = take ? oi2 : i2[b];
+        const float l1 = take ? b1[b] : o1, l2 = take ? b2[b] : o2;
+        const int li1 = take ? i1[b] : oi1;
+        const bool wsec = (w2 > l1) || (w2 == l1 && wi2 < li1);
+        const float s2 = wsec ? w2 : l1;
+        const int si2 = wsec ? wi2 : li1;
+        const float s3 = wsec ? fmaxf(w3, l1) : fmaxf(w2, l2);
+
         const float xnt = xn[b] + __shfl_xor(xn[b], 32);
         const int64_t p = pbase + b * 32 + jl;
         const bool valid = (h == 0) && (p < N);
         const float xnorm = sqrtf(xnt * (1.f + g)) * (1.f + 2.f * u);
-        const float e = 1.0625f * g * (M + xnorm * sqM) + 1e-30f;
-        const bool flagged = !((bb - ns) > 2.f * e);
+        const float e2 = 2.f * (1.0625f * g * (M + xnorm * sqM) + 1e-30f);
+        // near tie: the exact winner is not certain
+        const bool flagged = !((w1 - s2) > e2);
+        // only the top two can win: every other score is more than 2e below
+        const bool pair = flagged && ((w1 - s3) > e2);
         if (valid) {
-            a_out[p] = bi;
-            if (d1_out != nullptr) d1_out[p] = fmaxf(xnt - 2.f * bb, 0.f);
+            a_out[p] = wi1;
+            if (d1_out != nullptr) d1_out[p] = fmaxf(xnt - 2.f * w1, 0.f);
         }
-        const uint64_t m = __ballot(valid && flagged);
-        if (m != 0ull) {
-            const int leader = __ffsll((unsigned long long)m) - 1;
+        const uint64_t lt = lanemask_lt();
+        const uint64_t mp = __ballot(valid && pair);
+        if (mp != 0ull) {
+            const int leader = __ffsll((unsigned long long)mp) - 1;
             int base = 0;
-            if (lane == leader) base = atomicAdd(flag_count, __popcll(m));
+            if (lane == leader) base = atomicAdd(&counters[1], __popcll(mp));
             base = __shfl(base, leader);
-            if (valid && flagged) flag_list[base + __popcll(m & lanemask_lt())] = (int32_t)p;
+            if (valid && pair) {
+                int32_t *e = pair_list + 3 * (int64_t)(base + __popcll(mp & lt));
+                e[0] = (int32_t)p;
+                e[1] = wi1;
+                e[2] = si2;
+            }
         }
+        const uint64_t mf = __ballot(valid && flagged && !pair);
+        if (mf != 0ull) {
+            const int leader = __ffsll((unsigned long long)mf) - 1;
+            int base = 0;
+            if (lane == leader) base = atomicAdd(&counters[0], __popcll(mf));
+            base = __shfl(base, leader);
+            if (valid && flagged && !pair) full_list[base + __popcll(mf & lt)] = (int32_t)p;
+        }
+    }
+}
+
+// fp64 check of a near-tie point whose winner is one of two known centroids:
+// D = sum_j (x_j - c_j)^2 in fp64 in increasing j, no fused multiply-add, for
+// both; the smaller wins, the lower index on a tie.  One thread per point.
+template <typename CT>
+__global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ X, int d, const CT *__restrict__ C,
+                                                      const double *__restrict__ xnorm64,
+                                                      const int32_t *__restrict__ pair_list,
+                                                      const int32_t *__restrict__ counters,
+                                                      int32_t *__restrict__ a_out, float *__restrict__ d1_out) {
+#pragma clang fp contract(off)
+    const int cnt = counters[1];
+    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
+        const int64_t p = pair_list[3 * (int64_t)q];
+        const int k1 = pair_list[3 * (int64_t)q + 1];
+        const int k2 = pair_list[3 * (int64_t)q + 2];
+        const float *x = X + (size_t)p * d;
+        const CT *c1 = C + (size_t)k1 * d;
+        const CT *c2 = C + (size_t)k2 * d;
+        const double nx = xnorm64 != nullptr ? xnorm64[p] : 1.0;
+        double D1 = 0.0, D2 = 0.0;
+        for (int j = 0; j < d; ++j) {
+            double xv = (double)x[j];
+            if (xnorm64 != nullptr) xv = xv / nx;
+            const double t1 = xv - (double)c1[j];
+            const double t2 = xv - (double)c2[j];
+            D1 = D1 + t1 * t1;
+            D2 = D2 + t2 * t2;
+        }
+        const bool second = (D2 < D1) || (D2 == D1 && k2 < k1);
+        a_out[p] = second ? k2 : k1;
+        if (d1_out != nullptr) d1_out[p] = (float)(second ? D2 : D1);
     }
 }
 
@@ -377,14 +454,14 @@ template <typename CT, int RP>
 __global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, int d, const CT *__restrict__ C,
                                                  int K, const double *__restrict__ xnorm64,
                                                  const int32_t *__restrict__ flag_list,
-                                                 const int32_t *__restrict__ flag_count, int P,
+                                                 const int32_t *__restrict__ counters, int P,
                                                  int32_t *__restrict__ a_out, float *__restrict__ d1_out) {
 #pragma clang fp contract(off)
     extern __shared__ double sx[];  // P * d
     __shared__ double rb[4][RP];
     __shared__ int ri[4][RP];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int cnt = *flag_count;
+    const int cnt = counters[0];
     for (int base = blockIdx.x * P; base < cnt; base += gridDim.x * P) {
         const int np = min(P, cnt - base);
         for (int q = tid; q < np * d; q += 256) {
@@ -464,11 +541,11 @@ __global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, in
 
 // ---------------------------------------------------------------------------
 AssignShape assign_shape(int d) {
-    if (d <= 16) return {16, 2, 1, 1};
-    if (d <= 32) return {32, 2, 1, 1};
-    if (d <= 64) return {64, 2, 1, 1};
+    if (d <= 16) return {16, 1, 1, 1};
+    if (d <= 32) return {32, 1, 1, 1};
+    if (d <= 64) return {64, 1, 1, 1};
     if (d <= 128) return {128, 2, 1, 1};
-    return {64, 1, 4, (int)cdiv(d, 64)};
+    return {64, 1, 2, (int)cdiv(d, 64)};
 }
 
 hipError_t launch_row_norm64(const float *M, int64_t rows, int d, double *nrm, hipStream_t s) {
@@ -500,43 +577,57 @@ hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, i
     return hipGetLastError();
 }
 
-template <int DP, int PB, int CB>
+template <int DP, int PB, int CB, int WAVES, int MINB, bool RES>
 static hipError_t launch_fa(const float *X, int64_t N, int d, int nch, const float *C, const float *ncn, int K,
                             const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                            int32_t *flag_list, int32_t *flag_count, hipStream_t s) {
+                            int32_t *full_list, int32_t *pair_list, int32_t *counters, hipStream_t s) {
     const int ntiles = (int)cdiv(K, CB * 32);
-    const int64_t nb = cdiv(N, (int64_t)kAssignWaves * PB * 32);
-    hipLaunchKernelGGL((k_flash_assign<DP, PB, CB>), dim3((unsigned)nb), dim3(kAssignThreads), 0, s, X, N, d,
-                       nch, C, ncn, K, ntiles, scal, xnorm64, a_out, d1_out, flag_list, flag_count);
+    const int64_t nb = cdiv(N, (int64_t)WAVES * PB * 32);
+    if (d % 4 == 0)
+        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, true>), dim3((unsigned)nb), dim3(WAVES * 64),
+                           0, s, X, N, d, nch, C, ncn, K, ntiles, scal, xnorm64, a_out, d1_out, full_list, pair_list,
+                           counters);
+    else
+        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, false>), dim3((unsigned)nb),
+                           dim3(WAVES * 64), 0, s, X, N, d, nch, C, ncn, K, ntiles, scal, xnorm64, a_out, d1_out,
+                           full_list, pair_list, counters);
     return hipGetLastError();
 }
 
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                                const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                               int32_t *flag_list, int32_t *flag_count, hipStream_t s) {
+                               int32_t *full_list, int32_t *pair_list, int32_t *counters, hipStream_t s) {
     if (N <= 0) return hipSuccess;
     const AssignShape sh = assign_shape(d);
+#define FK_FA(DP_, PB_, CB_, W_, MB_, RES_)                                                                     \
+    launch_fa<DP_, PB_, CB_, W_, MB_, RES_>(X, N, d, sh.nch, C, ncn, K, scal, xnorm64, a_out, d1_out, full_list, \
+                                            pair_list, counters, s)
+    if (sh.nch > 1) return FK_FA(64, 1, 2, 8, 2, false);
     switch (sh.DP) {
-    case 16:
-        return launch_fa<16, 2, 1>(X, N, d, 1, C, ncn, K, scal, xnorm64, a_out, d1_out, flag_list, flag_count, s);
-    case 32:
-        return launch_fa<32, 2, 1>(X, N, d, 1, C, ncn, K, scal, xnorm64, a_out, d1_out, flag_list, flag_count, s);
-    case 128:
-        return launch_fa<128, 2, 1>(X, N, d, 1, C, ncn, K, scal, xnorm64, a_out, d1_out, flag_list, flag_count,
-                                    s);
-    default:
-        if (sh.CB == 1)
-            return launch_fa<64, 2, 1>(X, N, d, 1, C, ncn, K, scal, xnorm64, a_out, d1_out, flag_list, flag_count,
-                                       s);
-        return launch_fa<64, 1, 4>(X, N, d, sh.nch, C, ncn, K, scal, xnorm64, a_out, d1_out, flag_list,
-                                   flag_count, s);
+    case 16: return FK_FA(16, 1, 1, 8, 4, true);
+    case 32: return FK_FA(32, 1, 1, 8, 4, true);
+    case 64: return FK_FA(64, 1, 1, 8, 4, true);
+    default: return FK_FA(128, 2, 1, 4, 2, true);
     }
+#undef FK_FA
 }
 
 hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C32, const double *C64, int K,
-                          const double *xnorm64, const int32_t *flag_list, const int32_t *flag_count,
-                          int32_t *a_out, float *d1_out, hipStream_t s) {
+                          const double *xnorm64, const int32_t *full_list, const int32_t *pair_list,
+                          const int32_t *counters, int32_t *a_out, float *d1_out, hipStream_t s) {
     if (N <= 0) return hipSuccess;
+    {
+        int64_t nb = cdiv(N, 256);
+        if (nb > 4096) nb = 4096;
+        if (C64 != nullptr)
+            hipLaunchKernelGGL(k_recheck_pair<double>, dim3((unsigned)nb), dim3(256), 0, s, X, d, C64, xnorm64,
+                               pair_list, counters, a_out, d1_out);
+        else
+            hipLaunchKernelGGL(k_recheck_pair<float>, dim3((unsigned)nb), dim3(256), 0, s, X, d, C32, xnorm64,
+                               pair_list, counters, a_out, d1_out);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     constexpr int RP = 8;
     int P = (int)(49152 / (8 * (int64_t)d));
     if (P > RP) P = RP;
@@ -546,10 +637,10 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C32, co
     if (nb > 2048) nb = 2048;
     if (C64 != nullptr)
         hipLaunchKernelGGL((k_recheck<double, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C64, K, xnorm64,
-                           flag_list, flag_count, P, a_out, d1_out);
+                           full_list, counters, P, a_out, d1_out);
     else
         hipLaunchKernelGGL((k_recheck<float, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C32, K, xnorm64,
-                           flag_list, flag_count, P, a_out, d1_out);
+                           full_list, counters, P, a_out, d1_out);
     return hipGetLastError();
 }
 

@@ -11,11 +11,9 @@ namespace fk {
 constexpr int kWave = 64;
 
 // ---- FlashAssign geometry -------------------------------------------------
-// A workgroup is 4 waves.  Each wave owns PB blocks of 32 points and keeps
-// their coordinates for one d-chunk of DP dims in VGPRs; all 4 waves share
+// A workgroup is WAVES waves.  Each wave owns PB blocks of 32 points and keeps
+// their coordinates for one d-chunk of DP dims in VGPRs; all waves share
 // centroid tiles of CB*32 rows x DP dims staged through LDS.
-constexpr int kAssignWaves = 4;
-constexpr int kAssignThreads = kAssignWaves * kWave;
 // Centroid counts are padded to a multiple of this (largest tile height).
 constexpr int kCentroidPad = 128;
 
@@ -40,6 +38,7 @@ struct AssignShape {
     int CB;       // 32-centroid blocks per tile
     int nch;      // number of d-chunks
 };
+// The point-block geometry of the kernel variant used for d.
 AssignShape assign_shape(int d);
 
 // ---- launchers (each returns the launch status) ---------------------------
@@ -50,12 +49,15 @@ hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float 
                                 hipStream_t s);
 hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, int32_t *counter,
                               hipStream_t s);
+// counters[0] = length of full_list (near ties to rescore against all K),
+// counters[1] = length of pair_list (near ties between two known centroids,
+// 3 ints per entry: point, k1, k2).
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                                const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                               int32_t *flag_list, int32_t *flag_count, hipStream_t s);
+                               int32_t *full_list, int32_t *pair_list, int32_t *counters, hipStream_t s);
 hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C32, const double *C64, int K,
-                          const double *xnorm64, const int32_t *flag_list, const int32_t *flag_count,
-                          int32_t *a_out, float *d1_out, hipStream_t s);
+                          const double *xnorm64, const int32_t *full_list, const int32_t *pair_list,
+                          const int32_t *counters, int32_t *a_out, float *d1_out, hipStream_t s);
 
 // Radix sort of (key = assign[i], value = i), stable, atomic-free.  Writes the
 // sorted keys and the permutation.  tmp* are N-sized scratch arrays.

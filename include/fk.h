@@ -175,7 +175,8 @@ enum {
 typedef struct {
     int64_t calls[FK_NPHASE];
     double ms[FK_NPHASE];
-    int64_t rechecked;      /* points rescored in fp64, summed over the calls read */
+    int64_t rechecked;      /* near-tie points rescored in fp64 against all K      */
+    int64_t paired;         /* near-tie points settled by an fp64 two-way compare  */
     int64_t assigned;       /* points assigned, summed over the calls read         */
 } fk_profile;
 
