@@ -153,7 +153,8 @@ def main():
         "update_frac_hbm": upd_bytes / t_update / 1e9 / HBM_PEAK_GBS,
         "phase_ms_per_step": {k: round(v, 4) for k, v in per.items()},
         "near_tie_fraction": {"pair": prof["paired"] / max(prof["assigned"], 1),
-                              "full": prof["rechecked"] / max(prof["assigned"], 1)},
+                              "window": prof["windowed"] / max(prof["assigned"], 1),
+                              "all_k": prof["rechecked"] / max(prof["assigned"], 1)},
         "roofline": {"kernel": "k_flash_assign", "bound": "mfma", "achieved": fa_tflops,
                      "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": fa_tflops / FP32_MFMA_PEAK_TFLOPS,
                      "avg_ms": fa_ms, "traffic": traffic},

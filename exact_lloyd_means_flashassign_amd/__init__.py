@@ -39,7 +39,8 @@ class FkError(RuntimeError):
 
 class _Profile(ctypes.Structure):
     _fields_ = [("calls", ctypes.c_int64 * len(PHASES)), ("ms", ctypes.c_double * len(PHASES)),
-                ("rechecked", ctypes.c_int64), ("paired", ctypes.c_int64), ("assigned", ctypes.c_int64)]
+                ("rechecked", ctypes.c_int64), ("paired", ctypes.c_int64), ("windowed", ctypes.c_int64),
+                ("assigned", ctypes.c_int64)]
 
 
 _lib = None
@@ -287,11 +288,12 @@ def fk_profile_enable(on: bool = True):
 
 def fk_profile_read() -> dict:
     """Waits for the pending phase events; returns per-phase calls and
-    milliseconds, the near-tie points settled by a two-way fp64 compare
-    ("paired") or rescored in fp64 against all K ("rechecked"), and the
-    points assigned."""
+    milliseconds, the near-tie points settled by an fp64 compare of two
+    centroids ("paired"), of the centroids within their error window
+    ("windowed"), or against all K ("rechecked"), and the points assigned."""
     p = _Profile()
     _check(load().fk_profile_read(ctypes.byref(p)))
     return {"calls": {ph: int(p.calls[i]) for i, ph in enumerate(PHASES)},
             "ms": {ph: float(p.ms[i]) for i, ph in enumerate(PHASES)},
-            "rechecked": int(p.rechecked), "paired": int(p.paired), "assigned": int(p.assigned)}
+            "rechecked": int(p.rechecked), "paired": int(p.paired), "windowed": int(p.windowed),
+            "assigned": int(p.assigned)}

@@ -38,7 +38,7 @@ fk_status hip_fail(hipError_t e, const char *what) {
 // ---- workspace layout -----------------------------------------------------
 struct Layout {
     size_t total = 0;
-    size_t ncn, cmax_part, scal, counter, flags, pairs;
+    size_t ncn, cmax_part, scal, counter, flags, thr, pairs, cand, ccount, ovf;
     size_t c64, c32, cnrm64, xnorm64;  // cosine only (else ~0)
     size_t keys_sorted, perm, tmp_keys, tmp_vals, sort_scratch, offsets;
     size_t sums, cnt, pfirst, plast;
@@ -64,7 +64,11 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc) {
     L.scal = take(64);
     L.counter = take(64);
     L.flags = take((size_t)r * 4);
+    L.thr = take((size_t)r * 4);
     L.pairs = take((size_t)r * 12);
+    L.cand = take((size_t)near_tie_cap(r) * kCandPerSlot * 4);
+    L.ccount = take((size_t)near_tie_cap(r) * 2 * 4);
+    L.ovf = take((size_t)r * 4);
     L.c64 = cos ? take((size_t)K * d * 8) : kNone;
     L.c32 = cos ? take((size_t)K * d * 4) : kNone;
     L.cnrm64 = cos ? take((size_t)K * 8) : kNone;
@@ -184,12 +188,12 @@ void prof_count_rechecks(const int32_t *dev_counters, int64_t n_assigned, hipStr
     if (!g_prof.on) return;
     if (g_prof.slots_used == g_prof.count_slots.size()) {
         int32_t *h = nullptr;
-        if (hipHostMalloc((void **)&h, 2 * sizeof(int32_t)) != hipSuccess) return;
+        if (hipHostMalloc((void **)&h, 3 * sizeof(int32_t)) != hipSuccess) return;
         g_prof.count_slots.push_back(h);
     }
     int32_t *slot = g_prof.count_slots[g_prof.slots_used++];
-    slot[0] = slot[1] = 0;
-    (void)hipMemcpyAsync(slot, dev_counters, 2 * sizeof(int32_t), hipMemcpyDeviceToHost, s);
+    slot[0] = slot[1] = slot[2] = 0;
+    (void)hipMemcpyAsync(slot, dev_counters, 3 * sizeof(int32_t), hipMemcpyDeviceToHost, s);
     g_prof.acc.assigned += n_assigned;
 }
 
@@ -237,19 +241,26 @@ fk_status step_xnorm(const Ctx &c, const float *X, int64_t rows) {
 fk_status step_assign(const Ctx &c, const float *X, int64_t rows, const float *C, const float *C_use,
                       int32_t *a_out, float *d1_out) {
     const double *xn = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.xnorm64) : nullptr;
+    NearTies nt;
+    nt.full_list = at<int32_t>(c.ws, c.L.flags);
+    nt.full_thr = at<float>(c.ws, c.L.thr);
+    nt.pair_list = at<int32_t>(c.ws, c.L.pairs);
+    nt.counters = at<int32_t>(c.ws, c.L.counter);
+    nt.cand = at<int32_t>(c.ws, c.L.cand);
+    nt.ccount = at<int32_t>(c.ws, c.L.ccount);
+    nt.ovf_list = at<int32_t>(c.ws, c.L.ovf);
     {
         PhaseScope ph(FK_PH_ASSIGN, c.s);
-        FK_TRY(launch_flash_assign(X, rows, c.d, C_use, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal),
-                                   xn, a_out, d1_out, at<int32_t>(c.ws, c.L.flags), at<int32_t>(c.ws, c.L.pairs),
-                                   at<int32_t>(c.ws, c.L.counter), c.s),
+        FK_TRY(launch_flash_assign(X, rows, c.d, C_use, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal), xn,
+                                   a_out, d1_out, nt, c.s),
                "flash assign");
     }
     {
         PhaseScope ph(FK_PH_RECHECK, c.s);
         const double *c64 = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.c64) : nullptr;
-        FK_TRY(launch_recheck(X, rows, c.d, C, c64, c.K, xn, at<int32_t>(c.ws, c.L.flags),
-                              at<int32_t>(c.ws, c.L.pairs), at<int32_t>(c.ws, c.L.counter), a_out, d1_out, c.s),
-               "fp64 recheck");
+        FK_TRY(launch_recheck(X, rows, c.d, C_use, C, c64, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal),
+                              xn, nt, a_out, d1_out, c.s),
+               "near-tie recheck");
     }
     prof_count_rechecks(at<int32_t>(c.ws, c.L.counter), rows, c.s);
     return FK_OK;
@@ -517,7 +528,7 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
         FK_TRY(hipStreamWaitEvent(c.s, R->copied[b], 0), "stream wait");
         if ((st = step_xnorm(c, Xd, rows)) != FK_OK) return st;
         // the near-tie list is per chunk: reset its counter
-        FK_TRY(launch_fill_zero(at<void>(workspace, L.counter), 8, c.s), "reset counters");
+        FK_TRY(launch_fill_zero(at<void>(workspace, L.counter), 16, c.s), "reset counters");
         if ((st = step_assign(c, Xd, rows, C_in, Cu, ad, nullptr)) != FK_OK) return st;
         if ((st = step_accumulate(c, Xd, rows, ad)) != FK_OK) return st;
         FK_TRY(hipEventRecord(R->freed[b], c.s), "event record");
@@ -560,8 +571,9 @@ fk_status fk_profile_read(fk_profile *out) {
     g_prof.pending.clear();
     if (g_prof.slots_used > 0) FK_TRY(hipDeviceSynchronize(), "device sync");
     for (size_t i = 0; i < g_prof.slots_used; ++i) {
-        g_prof.acc.rechecked += g_prof.count_slots[i][0];
+        g_prof.acc.windowed += g_prof.count_slots[i][0];
         g_prof.acc.paired += g_prof.count_slots[i][1];
+        g_prof.acc.rechecked += g_prof.count_slots[i][2];
     }
     g_prof.slots_used = 0;
     *out = g_prof.acc;

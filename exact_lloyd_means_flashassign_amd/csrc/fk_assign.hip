@@ -25,6 +25,29 @@ namespace fk {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
 
+// candidates kept per point half-lane when the full near-tie list is collected
+constexpr int kMaxCand = 8;
+
+struct FlashArgs {
+    const float *X;
+    int64_t N;
+    int d, nch;
+    const float *C;
+    const float *ncn;  // -||c||^2/2, padded with -inf
+    int K, ntiles;
+    const float *scal;
+    const double *xnorm64;  // cosine: fp64 row norms of X, else null
+    int32_t *a_out;
+    float *d1_out;
+    int32_t *full_list;  // near ties with a third score within the window
+    float *full_thr;     // their score threshold
+    int32_t *pair_list;  // near ties settled by the top two: (point, k1, k2)
+    int32_t *counters;   // [0] full, [1] pair, [2] overflow list lengths
+    int32_t *cand;       // collect mode: candidates per (slot, half)
+    int32_t *ccount;     // collect mode: candidate counts per (slot, half)
+    int64_t cap_slots;   // collect mode: slots with candidate storage
+};
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     const unsigned lane = __lane_id();
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
@@ -94,7 +117,7 @@ __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__
     if (threadIdx.x == 0) cmax_part[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
 }
 
-// scal[0] = max_k ||c_k||^2 (fp32); resets the two near-tie list counters.
+// scal[0] = max_k ||c_k||^2 (fp32); resets the three near-tie list counters.
 __global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ cmax_part, int nparts,
                                                      float *__restrict__ scal, int32_t *__restrict__ counter) {
     __shared__ float sm[256];
@@ -110,6 +133,7 @@ __global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ c
         scal[0] = sm[0];
         counter[0] = 0;
         counter[1] = 0;
+        counter[2] = 0;
     }
 }
 
@@ -144,12 +168,8 @@ __global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ c
 // the full list.  For cosine, the fp32 normalised rows differ from the fp64
 // normalised ones by at most 3.1u relative, which moves a by at most
 // 3.1u (||x|| ||c|| + ||c||^2); 8u is added to g for it.
-template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool VEC>
-__global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(
-    const float *__restrict__ X, int64_t N, int d, int nch, const float *__restrict__ C,
-    const float *__restrict__ ncn, int K, int ntiles, const float *__restrict__ scal,
-    const double *__restrict__ xnorm64, int32_t *__restrict__ a_out, float *__restrict__ d1_out,
-    int32_t *__restrict__ full_list, int32_t *__restrict__ pair_list, int32_t *__restrict__ counters) {
+template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool VEC, bool COLLECT>
+__global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashArgs A) {
     constexpr int NT = WAVES * 64;
     constexpr int HALF = DP / 2;
     constexpr int ROWS = CB * 32;
@@ -157,254 +177,343 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(
     constexpr int Q4 = DP / 4;
     constexpr int NQ4 = ROWS * Q4;
     constexpr int PFN = (NQ4 + NT - 1) / NT;
+    constexpr int BM = WAVES * PB * 32;  // points per workgroup pass
     static_assert(HALF % 4 == 0, "DP must be a multiple of 8");
 
     __shared__ __attribute__((aligned(16))) float sC[2][ROWS * LDR];
     __shared__ __attribute__((aligned(16))) float sN[2][ROWS];
 
+    const float *__restrict__ X = A.X;
+    const float *__restrict__ C = A.C;
+    const int d = A.d, K = A.K;
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
     const int lane = tid & 63;
     const int h = lane >> 5;
     const int jl = lane & 31;
-    const int64_t pbase = ((int64_t)blockIdx.x * WAVES + wv) * (PB * 32);
 
-    // global -> registers for one centroid stage (tile t, d-chunk ch)
-    float4 pf[PFN];
-    float pn = 0.f;
-    auto load_stage = [&](int t, int ch) {
+    // Assign mode: workgroup g takes points [g*BM, (g+1)*BM).  Collect mode:
+    // the workgroups stride over slots of the full near-tie list.
+    const int64_t nslots = COLLECT ? (int64_t)min((int64_t)A.counters[0], A.cap_slots) : A.N;
+    const int64_t ngroups = COLLECT ? (nslots + BM - 1) / BM : 1;
+    for (int64_t grp = COLLECT ? (int64_t)blockIdx.x : 0; grp < ngroups; grp += COLLECT ? gridDim.x : 1) {
+        const int64_t sbase = ((COLLECT ? grp : (int64_t)blockIdx.x) * WAVES + wv) * (PB * 32);
+
+        // global -> registers for one centroid stage (tile t, d-chunk ch)
+        float4 pf[PFN];
+        float pn = 0.f;
+        auto load_stage = [&](int t, int ch) {
 #pragma unroll
-        for (int i = 0; i < PFN; ++i) {
-            const int q = tid + i * NT;
-            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-            if (q < NQ4) {
-                const int row = q / Q4;
-                const int col = ch * DP + (q % Q4) * 4;
-                const int k = t * ROWS + row;
-                if (k < K) {
-                    const float *src = C + (size_t)k * d + col;
-                    if (VEC) {
-                        if (col < d) v = *reinterpret_cast<const float4 *>(src);
-                    } else {
-                        if (col < d) v.x = src[0];
-                        if (col + 1 < d) v.y = src[1];
-                        if (col + 2 < d) v.z = src[2];
-                        if (col + 3 < d) v.w = src[3];
+            for (int i = 0; i < PFN; ++i) {
+                const int q = tid + i * NT;
+                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (q < NQ4) {
+                    const int row = q / Q4;
+                    const int col = ch * DP + (q % Q4) * 4;
+                    const int k = t * ROWS + row;
+                    if (k < K) {
+                        const float *src = C + (size_t)k * d + col;
+                        if (VEC) {
+                            if (col < d) v = *reinterpret_cast<const float4 *>(src);
+                        } else {
+                            if (col < d) v.x = src[0];
+                            if (col + 1 < d) v.y = src[1];
+                            if (col + 2 < d) v.z = src[2];
+                            if (col + 3 < d) v.w = src[3];
+                        }
                     }
                 }
+                pf[i] = v;
             }
-            pf[i] = v;
-        }
-        if (ch == 0 && tid < ROWS) pn = ncn[t * ROWS + tid];
-    };
-    // registers -> LDS buffer
-    auto store_stage = [&](int buf, int ch) {
+            if (ch == 0 && tid < ROWS) pn = A.ncn[t * ROWS + tid];
+        };
+        // registers -> LDS buffer
+        auto store_stage = [&](int buf, int ch) {
 #pragma unroll
-        for (int i = 0; i < PFN; ++i) {
-            const int q = tid + i * NT;
-            if (q < NQ4) *reinterpret_cast<float4 *>(&sC[buf][(q / Q4) * LDR + (q % Q4) * 4]) = pf[i];
-        }
-        if (ch == 0 && tid < ROWS) sN[buf][tid] = pn;
-    };
+            for (int i = 0; i < PFN; ++i) {
+                const int q = tid + i * NT;
+                if (q < NQ4) *reinterpret_cast<float4 *>(&sC[buf][(q / Q4) * LDR + (q % Q4) * 4]) = pf[i];
+            }
+            if (ch == 0 && tid < ROWS) sN[buf][tid] = pn;
+        };
 
-    float xr[PB][HALF];
-    // running top-3 scores per point (b1 >= b2 >= b3) and the indices of the
-    // first two
-    float xn[PB], xsc[PB], b1[PB], b2[PB], b3[PB];
-    int i1[PB], i2[PB];
-#pragma unroll
-    for (int b = 0; b < PB; ++b) {
-        const int64_t p = pbase + b * 32 + jl;
-        xn[b] = 0.f;
-        xsc[b] = (xnorm64 != nullptr && p < N) ? (float)(1.0 / xnorm64[p]) : 1.f;
-        b1[b] = -INFINITY;
-        b2[b] = -INFINITY;
-        b3[b] = -INFINITY;
-        i1[b] = 0;
-        i2[b] = 0;
-    }
-    // this wave's points, dims ch*DP + h*HALF + [0, HALF), into registers
-    auto load_x = [&](int ch, bool add_norm) {
+        float xr[PB][HALF];
+        // assign mode: running top-3 scores per point (b1 >= b2 >= b3) and the
+        // indices of the first two.  collect mode: the listed point's
+        // threshold and this half-lane's candidate count.
+        float xn[PB], xsc[PB], b1[PB], b2[PB], b3[PB];
+        int i1[PB], i2[PB];
+        int64_t pt[PB];
+        bool pv[PB];
 #pragma unroll
         for (int b = 0; b < PB; ++b) {
-            const int64_t p = pbase + b * 32 + jl;
-            const int col0 = ch * DP + h * HALF;
-            const float *src = X + (size_t)p * d + col0;
-            const bool pin = p < N;
-            if (VEC) {
-#pragma unroll
-                for (int s = 0; s < HALF; s += 4) {
-                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                    if (pin && col0 + s < d) v = *reinterpret_cast<const float4 *>(src + s);
-                    xr[b][s] = v.x;
-                    xr[b][s + 1] = v.y;
-                    xr[b][s + 2] = v.z;
-                    xr[b][s + 3] = v.w;
-                }
+            const int64_t slot = sbase + b * 32 + jl;
+            if (COLLECT) {
+                pv[b] = slot < nslots;
+                pt[b] = pv[b] ? A.full_list[slot] : 0;
+                b1[b] = pv[b] ? A.full_thr[slot] : INFINITY;
             } else {
-#pragma unroll
-                for (int s = 0; s < HALF; ++s) xr[b][s] = (pin && col0 + s < d) ? src[s] : 0.f;
+                pv[b] = slot < A.N;
+                pt[b] = slot;
+                b1[b] = -INFINITY;
             }
-            if (xnorm64 != nullptr) {
-#pragma unroll
-                for (int s = 0; s < HALF; ++s) xr[b][s] *= xsc[b];
-            }
-            if (add_norm) {
-                float acc = xn[b];
-#pragma unroll
-                for (int s = 0; s < HALF; ++s) acc = fmaf(xr[b][s], xr[b][s], acc);
-                xn[b] = acc;
-            }
+            xn[b] = 0.f;
+            xsc[b] = (A.xnorm64 != nullptr && pv[b]) ? (float)(1.0 / A.xnorm64[pt[b]]) : 1.f;
+            b2[b] = -INFINITY;
+            b3[b] = -INFINITY;
+            i1[b] = 0;
+            i2[b] = 0;
         }
-    };
-
-    v16f acc[PB][CB];
-    const int cnch = RES ? 1 : nch;
-    const int nst = ntiles * cnch;
-    if (RES) load_x(0, true);
-    load_stage(0, 0);
-    store_stage(0, 0);
-    __syncthreads();
-
-    int t = 0, ch = 0;
-    for (int st = 0; st < nst; ++st) {
-        const int buf = st & 1;
-        int nt = t, nc = ch + 1;
-        if (nc == cnch) {
-            nc = 0;
-            nt = t + 1;
-        }
-        const bool more = st + 1 < nst;
-        // the chunk's own points first, so that waiting for them does not
-        // also wait for the next stage's prefetch
-        if (!RES) load_x(ch, t == 0);
-        if (more) load_stage(nt, nc);
-
-        if (ch == 0) {
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const float4 nv = *reinterpret_cast<const float4 *>(&sN[buf][cb * 32 + 8 * q + 4 * h]);
-#pragma unroll
-                    for (int b = 0; b < PB; ++b) {
-                        acc[b][cb][4 * q + 0] = nv.x;
-                        acc[b][cb][4 * q + 1] = nv.y;
-                        acc[b][cb][4 * q + 2] = nv.z;
-                        acc[b][cb][4 * q + 3] = nv.w;
-                    }
-                }
-            }
-        }
-
-        const float *sc = &sC[buf][jl * LDR + h * HALF];
-#pragma unroll
-        for (int s = 0; s < HALF; s += 4) {
-            float4 av[CB];
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) av[cb] = *reinterpret_cast<const float4 *>(sc + cb * 32 * LDR + s);
-#pragma unroll
-            for (int cb = 0; cb < CB; ++cb) {
-#pragma unroll
-                for (int b = 0; b < PB; ++b) {
-                    acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].x, xr[b][s + 0], acc[b][cb], 0, 0, 0);
-                    acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].y, xr[b][s + 1], acc[b][cb], 0, 0, 0);
-                    acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].z, xr[b][s + 2], acc[b][cb], 0, 0, 0);
-                    acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].w, xr[b][s + 3], acc[b][cb], 0, 0, 0);
-                }
-            }
-        }
-
-        if (ch == cnch - 1) {
-            const int kt = t * ROWS + 4 * h;
+        // this wave's points, dims ch*DP + h*HALF + [0, HALF), into registers
+        auto load_x = [&](int ch, bool add_norm) {
 #pragma unroll
             for (int b = 0; b < PB; ++b) {
+                const int col0 = ch * DP + h * HALF;
+                const float *src = X + (size_t)pt[b] * d + col0;
+                if (VEC) {
+#pragma unroll
+                    for (int s = 0; s < HALF; s += 4) {
+                        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                        if (pv[b] && col0 + s < d) v = *reinterpret_cast<const float4 *>(src + s);
+                        xr[b][s] = v.x;
+                        xr[b][s + 1] = v.y;
+                        xr[b][s + 2] = v.z;
+                        xr[b][s + 3] = v.w;
+                    }
+                } else {
+#pragma unroll
+                    for (int s = 0; s < HALF; ++s) xr[b][s] = (pv[b] && col0 + s < d) ? src[s] : 0.f;
+                }
+                if (A.xnorm64 != nullptr) {
+#pragma unroll
+                    for (int s = 0; s < HALF; ++s) xr[b][s] *= xsc[b];
+                }
+                if (add_norm) {
+                    float acc = xn[b];
+#pragma unroll
+                    for (int s = 0; s < HALF; ++s) acc = fmaf(xr[b][s], xr[b][s], acc);
+                    xn[b] = acc;
+                }
+            }
+        };
+
+        v16f acc[PB][CB];
+        const int cnch = RES ? 1 : A.nch;
+        const int nst = A.ntiles * cnch;
+        if (RES) load_x(0, true);
+        load_stage(0, 0);
+        store_stage(0, 0);
+        __syncthreads();
+
+        int t = 0, ch = 0;
+        for (int st = 0; st < nst; ++st) {
+            const int buf = st & 1;
+            int nt = t, nc = ch + 1;
+            if (nc == cnch) {
+                nc = 0;
+                nt = t + 1;
+            }
+            const bool more = st + 1 < nst;
+            // the chunk's own points first, so that waiting for them does not
+            // also wait for the next stage's prefetch
+            if (!RES) load_x(ch, t == 0);
+            if (more) load_stage(nt, nc);
+
+            if (ch == 0) {
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const float v = acc[b][cb][r];
-                        const int k = kt + cb * 32 + 8 * (r >> 2) + (r & 3);
-                        // insert v into the sorted top-3 with medians of three
-                        // (v_med3_f32); a strict '>' keeps the lower index first
-                        // on equal scores (k increases per lane)
-                        const bool c1 = v > b1[b];
-                        const bool c2 = v > b2[b];
-                        const int t2 = c2 ? k : i2[b];
-                        i2[b] = c1 ? i1[b] : t2;
-                        i1[b] = c1 ? k : i1[b];
-                        b3[b] = __builtin_amdgcn_fmed3f(b2[b], b3[b], v);
-                        b2[b] = __builtin_amdgcn_fmed3f(b1[b], b2[b], v);
-                        b1[b] = c1 ? v : b1[b];
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 nv = *reinterpret_cast<const float4 *>(&sN[buf][cb * 32 + 8 * q + 4 * h]);
+#pragma unroll
+                        for (int b = 0; b < PB; ++b) {
+                            acc[b][cb][4 * q + 0] = nv.x;
+                            acc[b][cb][4 * q + 1] = nv.y;
+                            acc[b][cb][4 * q + 2] = nv.z;
+                            acc[b][cb][4 * q + 3] = nv.w;
+                        }
                     }
                 }
             }
-        }
-        if (more) store_stage(buf ^ 1, nc);
-        __syncthreads();
-        t = nt;
-        ch = nc;
-    }
 
-    // merge the two half-waves (same point, the other 16 centroids of each
-    // 32-block): larger score first, lower index first on equal scores
-    const float u = 5.9604645e-8f;
-    const float g = (float)(d + 4) * u + (xnorm64 != nullptr ? 8.f * u : 0.f);
-    const float M = scal[0] * (1.f + g);
-    const float sqM = sqrtf(M) * (1.f + 2.f * u);
+            const float *sc = &sC[buf][jl * LDR + h * HALF];
 #pragma unroll
-    for (int b = 0; b < PB; ++b) {
-        const float o1 = __shfl_xor(b1[b], 32);
-        const float o2 = __shfl_xor(b2[b], 32);
-        const float o3 = __shfl_xor(b3[b], 32);
-        const int oi1 = __shfl_xor(i1[b], 32);
-        const int oi2 = __shfl_xor(i2[b], 32);
-        // W = the list whose head wins, L = the other
-        const bool take = (o1 > b1[b]) || (o1 == b1[b] && oi1 < i1[b]);
-        const float w1 = take ? o1 : b1[b], w2 = take ? o2 : b2[b], w3 = take ? o3 : b3[b];
-        const int wi1 = take ? oi1 : i1[b], wi2 = take ? oi2 : i2[b];
-        const float l1 = take ? b1[b] : o1, l2 = take ? b2[b] : o2;
-        const int li1 = take ? i1[b] : oi1;
-        const bool wsec = (w2 > l1) || (w2 == l1 && wi2 < li1);
-        const float s2 = wsec ? w2 : l1;
-        const int si2 = wsec ? wi2 : li1;
-        const float s3 = wsec ? fmaxf(w3, l1) : fmaxf(w2, l2);
+            for (int s = 0; s < HALF; s += 4) {
+                float4 av[CB];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) av[cb] = *reinterpret_cast<const float4 *>(sc + cb * 32 * LDR + s);
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+                    for (int b = 0; b < PB; ++b) {
+                        acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].x, xr[b][s + 0], acc[b][cb], 0, 0, 0);
+                        acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].y, xr[b][s + 1], acc[b][cb], 0, 0, 0);
+                        acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].z, xr[b][s + 2], acc[b][cb], 0, 0, 0);
+                        acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].w, xr[b][s + 3], acc[b][cb], 0, 0, 0);
+                    }
+                }
+            }
 
-        const float xnt = xn[b] + __shfl_xor(xn[b], 32);
-        const int64_t p = pbase + b * 32 + jl;
-        const bool valid = (h == 0) && (p < N);
-        const float xnorm = sqrtf(xnt * (1.f + g)) * (1.f + 2.f * u);
-        const float e2 = 2.f * (1.0625f * g * (M + xnorm * sqM) + 1e-30f);
-        // near tie: the exact winner is not certain
-        const bool flagged = !((w1 - s2) > e2);
-        // only the top two can win: every other score is more than 2e below
-        const bool pair = flagged && ((w1 - s3) > e2);
-        if (valid) {
-            a_out[p] = wi1;
-            if (d1_out != nullptr) d1_out[p] = fmaxf(xnt - 2.f * w1, 0.f);
+            if (ch == cnch - 1) {
+                const int kt = t * ROWS + 4 * h;
+#pragma unroll
+                for (int b = 0; b < PB; ++b) {
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const float v = acc[b][cb][r];
+                            const int k = kt + cb * 32 + 8 * (r >> 2) + (r & 3);
+                            if (COLLECT) {
+                                // every centroid within the window may win
+                                if (v >= b1[b]) {
+                                    if (i1[b] < kMaxCand)
+                                        A.cand[((sbase + b * 32 + jl) * 2 + h) * kMaxCand + i1[b]] = k;
+                                    ++i1[b];
+                                }
+                            } else {
+                                // insert v into the sorted top-3 with medians of
+                                // three (v_med3_f32); a strict '>' keeps the lower
+                                // index first on equal scores (k increases per lane)
+                                const bool c1 = v > b1[b];
+                                const bool c2 = v > b2[b];
+                                const int t2 = c2 ? k : i2[b];
+                                i2[b] = c1 ? i1[b] : t2;
+                                i1[b] = c1 ? k : i1[b];
+                                b3[b] = __builtin_amdgcn_fmed3f(b2[b], b3[b], v);
+                                b2[b] = __builtin_amdgcn_fmed3f(b1[b], b2[b], v);
+                                b1[b] = c1 ? v : b1[b];
+                            }
+                        }
+                    }
+                }
+            }
+            if (more) store_stage(buf ^ 1, nc);
+            __syncthreads();
+            t = nt;
+            ch = nc;
         }
-        const uint64_t lt = lanemask_lt();
-        const uint64_t mp = __ballot(valid && pair);
-        if (mp != 0ull) {
-            const int leader = __ffsll((unsigned long long)mp) - 1;
-            int base = 0;
-            if (lane == leader) base = atomicAdd(&counters[1], __popcll(mp));
-            base = __shfl(base, leader);
-            if (valid && pair) {
-                int32_t *e = pair_list + 3 * (int64_t)(base + __popcll(mp & lt));
-                e[0] = (int32_t)p;
-                e[1] = wi1;
-                e[2] = si2;
+
+        if (COLLECT) {
+#pragma unroll
+            for (int b = 0; b < PB; ++b)
+                if (pv[b]) A.ccount[(sbase + b * 32 + jl) * 2 + h] = i1[b];
+            continue;
+        }
+
+        // merge the two half-waves (same point, the other 16 centroids of each
+        // 32-block): larger score first, lower index first on equal scores
+        const float u = 5.9604645e-8f;
+        const float g = (float)(d + 4) * u + (A.xnorm64 != nullptr ? 8.f * u : 0.f);
+        const float M = A.scal[0] * (1.f + g);
+        const float sqM = sqrtf(M) * (1.f + 2.f * u);
+#pragma unroll
+        for (int b = 0; b < PB; ++b) {
+            const float o1 = __shfl_xor(b1[b], 32);
+            const float o2 = __shfl_xor(b2[b], 32);
+            const float o3 = __shfl_xor(b3[b], 32);
+            const int oi1 = __shfl_xor(i1[b], 32);
+            const int oi2 = __shfl_xor(i2[b], 32);
+            // W = the list whose head wins, L = the other
+            const bool take = (o1 > b1[b]) || (o1 == b1[b] && oi1 < i1[b]);
+            const float w1 = take ? o1 : b1[b], w2 = take ? o2 : b2[b], w3 = take ? o3 : b3[b];
+            const int wi1 = take ? oi1 : i1[b], wi2 = take ? oi2 : i2[b];
+            const float l1 = take ? b1[b] : o1, l2 = take ? b2[b] : o2;
+            const int li1 = take ? i1[b] : oi1;
+            const bool wsec = (w2 > l1) || (w2 == l1 && wi2 < li1);
+            const float s2 = wsec ? w2 : l1;
+            const int si2 = wsec ? wi2 : li1;
+            const float s3 = wsec ? fmaxf(w3, l1) : fmaxf(w2, l2);
+
+            const float xnt = xn[b] + __shfl_xor(xn[b], 32);
+            const int64_t p = pt[b];
+            const bool valid = (h == 0) && pv[b];
+            const float xnorm = sqrtf(xnt * (1.f + g)) * (1.f + 2.f * u);
+            const float e2 = 2.f * (1.0625f * g * (M + xnorm * sqM) + 1e-30f);
+            // near tie: the exact winner is not certain
+            const bool flagged = !((w1 - s2) > e2);
+            // only the top two can win: every other score is more than 2e below
+            const bool pair = flagged && ((w1 - s3) > e2);
+            const bool full = flagged && !pair;
+            if (valid) {
+                A.a_out[p] = wi1;
+                if (A.d1_out != nullptr) A.d1_out[p] = fmaxf(xnt - 2.f * w1, 0.f);
+            }
+            const uint64_t lt = lanemask_lt();
+            const uint64_t mp = __ballot(valid && pair);
+            if (mp != 0ull) {
+                const int leader = __ffsll((unsigned long long)mp) - 1;
+                int base = 0;
+                if (lane == leader) base = atomicAdd(&A.counters[1], __popcll(mp));
+                base = __shfl(base, leader);
+                if (valid && pair) {
+                    int32_t *e = A.pair_list + 3 * (int64_t)(base + __popcll(mp & lt));
+                    e[0] = (int32_t)p;
+                    e[1] = wi1;
+                    e[2] = si2;
+                }
+            }
+            const uint64_t mf = __ballot(valid && full);
+            if (mf != 0ull) {
+                const int leader = __ffsll((unsigned long long)mf) - 1;
+                int base = 0;
+                if (lane == leader) base = atomicAdd(&A.counters[0], __popcll(mf));
+                base = __shfl(base, leader);
+                if (valid && full) {
+                    const int slot = base + __popcll(mf & lt);
+                    A.full_list[slot] = (int32_t)p;
+                    // any centroid that can still win scores at least this
+                    A.full_thr[slot] = w1 - e2;
+                }
             }
         }
-        const uint64_t mf = __ballot(valid && flagged && !pair);
-        if (mf != 0ull) {
-            const int leader = __ffsll((unsigned long long)mf) - 1;
-            int base = 0;
-            if (lane == leader) base = atomicAdd(&counters[0], __popcll(mf));
-            base = __shfl(base, leader);
-            if (valid && flagged && !pair) full_list[base + __popcll(mf & lt)] = (int32_t)p;
+    }
+}
+
+// fp64 check of a near-tie point from the full list whose candidates were
+// collected: the lowest-index minimum of the direct-difference fp64 distance
+// over its candidates (both half-lane lists).  A point whose lists overflowed,
+// or that lies beyond the collected slots, goes to the overflow list for a
+// rescoring against all K.  One thread per listed point.
+template <typename CT>
+__global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ X, int d, const CT *__restrict__ C,
+                                                      const double *__restrict__ xnorm64,
+                                                      const int32_t *__restrict__ full_list,
+                                                      const int32_t *__restrict__ cand,
+                                                      const int32_t *__restrict__ ccount, int64_t cap_slots,
+                                                      int32_t *__restrict__ ovf_list, int32_t *__restrict__ counters,
+                                                      int32_t *__restrict__ a_out, float *__restrict__ d1_out) {
+#pragma clang fp contract(off)
+    const int cnt = counters[0];
+    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
+        const int64_t p = full_list[q];
+        const int c0 = q < cap_slots ? ccount[2 * (int64_t)q] : kMaxCand + 1;
+        const int c1 = q < cap_slots ? ccount[2 * (int64_t)q + 1] : kMaxCand + 1;
+        if (c0 > kMaxCand || c1 > kMaxCand) {
+            ovf_list[atomicAdd(&counters[2], 1)] = (int32_t)p;
+            continue;
         }
+        const float *x = X + (size_t)p * d;
+        const double nx = xnorm64 != nullptr ? xnorm64[p] : 1.0;
+        double best = INFINITY;
+        int bk = 0x7fffffff;
+        for (int m = 0; m < c0 + c1; ++m) {
+            const int k = m < c0 ? cand[2 * (int64_t)q * kMaxCand + m] : cand[(2 * (int64_t)q + 1) * kMaxCand + m - c0];
+            const CT *c = C + (size_t)k * d;
+            double D = 0.0;
+            for (int j = 0; j < d; ++j) {
+                double xv = (double)x[j];
+                if (xnorm64 != nullptr) xv = xv / nx;
+                const double tt = xv - (double)c[j];
+                D = D + tt * tt;
+            }
+            if (D < best || (D == best && k < bk)) {
+                best = D;
+                bk = k;
+            }
+        }
+        a_out[p] = bk;
+        if (d1_out != nullptr) d1_out[p] = (float)best;
     }
 }
 
@@ -577,57 +686,108 @@ hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, i
     return hipGetLastError();
 }
 
-template <int DP, int PB, int CB, int WAVES, int MINB, bool RES>
-static hipError_t launch_fa(const float *X, int64_t N, int d, int nch, const float *C, const float *ncn, int K,
-                            const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                            int32_t *full_list, int32_t *pair_list, int32_t *counters, hipStream_t s) {
-    const int ntiles = (int)cdiv(K, CB * 32);
-    const int64_t nb = cdiv(N, (int64_t)WAVES * PB * 32);
-    if (d % 4 == 0)
-        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, true>), dim3((unsigned)nb), dim3(WAVES * 64),
-                           0, s, X, N, d, nch, C, ncn, K, ntiles, scal, xnorm64, a_out, d1_out, full_list, pair_list,
-                           counters);
+template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool COLLECT>
+static hipError_t launch_fa(const FlashArgs &A, hipStream_t s) {
+    constexpr int BM = WAVES * PB * 32;
+    int64_t nb = COLLECT ? cdiv(A.cap_slots, BM) : cdiv(A.N, BM);
+    if (COLLECT && nb > 512) nb = 512;  // persistent: the workgroups stride over the listed slots
+    if (A.d % 4 == 0)
+        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, true, COLLECT>), dim3((unsigned)nb),
+                           dim3(WAVES * 64), 0, s, A);
     else
-        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, false>), dim3((unsigned)nb),
-                           dim3(WAVES * 64), 0, s, X, N, d, nch, C, ncn, K, ntiles, scal, xnorm64, a_out, d1_out,
-                           full_list, pair_list, counters);
+        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, false, COLLECT>), dim3((unsigned)nb),
+                           dim3(WAVES * 64), 0, s, A);
     return hipGetLastError();
+}
+
+template <bool COLLECT>
+static hipError_t launch_fa_shape(const FlashArgs &A, hipStream_t s) {
+    const AssignShape sh = assign_shape(A.d);
+    if (sh.nch > 1) return launch_fa<64, 1, 2, 8, 2, false, COLLECT>(A, s);
+    switch (sh.DP) {
+    case 16: return launch_fa<16, 1, 1, 8, 4, true, COLLECT>(A, s);
+    case 32: return launch_fa<32, 1, 1, 8, 4, true, COLLECT>(A, s);
+    case 64: return launch_fa<64, 1, 1, 8, 4, true, COLLECT>(A, s);
+    default: return launch_fa<128, 2, 1, 4, 2, true, COLLECT>(A, s);
+    }
+}
+
+static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
+                            const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
+                            const NearTies &nt) {
+    const AssignShape sh = assign_shape(d);
+    FlashArgs A;
+    A.X = X;
+    A.N = N;
+    A.d = d;
+    A.nch = sh.nch;
+    A.C = C;
+    A.ncn = ncn;
+    A.K = K;
+    A.ntiles = (int)cdiv(K, sh.CB * 32);
+    A.scal = scal;
+    A.xnorm64 = xnorm64;
+    A.a_out = a_out;
+    A.d1_out = d1_out;
+    A.full_list = nt.full_list;
+    A.full_thr = nt.full_thr;
+    A.pair_list = nt.pair_list;
+    A.counters = nt.counters;
+    A.cand = nt.cand;
+    A.ccount = nt.ccount;
+    A.cap_slots = near_tie_cap(N);
+    return A;
+}
+
+int64_t near_tie_cap(int64_t N) {
+    int64_t cap = N / 8;
+    if (cap < 65536) cap = 65536;
+    if (cap > N) cap = N;
+    return cap < 1 ? 1 : cap;
 }
 
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                                const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                               int32_t *full_list, int32_t *pair_list, int32_t *counters, hipStream_t s) {
+                               const NearTies &nt, hipStream_t s) {
     if (N <= 0) return hipSuccess;
-    const AssignShape sh = assign_shape(d);
-#define FK_FA(DP_, PB_, CB_, W_, MB_, RES_)                                                                     \
-    launch_fa<DP_, PB_, CB_, W_, MB_, RES_>(X, N, d, sh.nch, C, ncn, K, scal, xnorm64, a_out, d1_out, full_list, \
-                                            pair_list, counters, s)
-    if (sh.nch > 1) return FK_FA(64, 1, 2, 8, 2, false);
-    switch (sh.DP) {
-    case 16: return FK_FA(16, 1, 1, 8, 4, true);
-    case 32: return FK_FA(32, 1, 1, 8, 4, true);
-    case 64: return FK_FA(64, 1, 1, 8, 4, true);
-    default: return FK_FA(128, 2, 1, 4, 2, true);
-    }
-#undef FK_FA
+    return launch_fa_shape<false>(flash_args(X, N, d, C, ncn, K, scal, xnorm64, a_out, d1_out, nt), s);
 }
 
-hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C32, const double *C64, int K,
-                          const double *xnorm64, const int32_t *full_list, const int32_t *pair_list,
-                          const int32_t *counters, int32_t *a_out, float *d1_out, hipStream_t s) {
+hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma, const float *C32,
+                          const double *C64, const float *ncn, int K, const float *scal, const double *xnorm64,
+                          const NearTies &nt, int32_t *a_out, float *d1_out, hipStream_t s) {
     if (N <= 0) return hipSuccess;
+    hipError_t e;
+    // 1. near ties between two known centroids
     {
         int64_t nb = cdiv(N, 256);
         if (nb > 4096) nb = 4096;
         if (C64 != nullptr)
             hipLaunchKernelGGL(k_recheck_pair<double>, dim3((unsigned)nb), dim3(256), 0, s, X, d, C64, xnorm64,
-                               pair_list, counters, a_out, d1_out);
+                               nt.pair_list, nt.counters, a_out, d1_out);
         else
             hipLaunchKernelGGL(k_recheck_pair<float>, dim3((unsigned)nb), dim3(256), 0, s, X, d, C32, xnorm64,
-                               pair_list, counters, a_out, d1_out);
-        const hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
+                               nt.pair_list, nt.counters, a_out, d1_out);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
     }
+    // 2. the full list: collect every centroid within each point's window
+    if ((e = launch_fa_shape<true>(flash_args(X, N, d, C_mfma, ncn, K, scal, xnorm64, a_out, d1_out, nt), s)) !=
+        hipSuccess)
+        return e;
+    // 3. fp64 over the collected candidates; overflows go to the last list
+    {
+        const int64_t cap = near_tie_cap(N);
+        int64_t nb = cdiv(N, 256);
+        if (nb > 4096) nb = 4096;
+        if (C64 != nullptr)
+            hipLaunchKernelGGL(k_recheck_cand<double>, dim3((unsigned)nb), dim3(256), 0, s, X, d, C64, xnorm64,
+                               nt.full_list, nt.cand, nt.ccount, cap, nt.ovf_list, nt.counters, a_out, d1_out);
+        else
+            hipLaunchKernelGGL(k_recheck_cand<float>, dim3((unsigned)nb), dim3(256), 0, s, X, d, C32, xnorm64,
+                               nt.full_list, nt.cand, nt.ccount, cap, nt.ovf_list, nt.counters, a_out, d1_out);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // 4. overflow: rescore against all K
     constexpr int RP = 8;
     int P = (int)(49152 / (8 * (int64_t)d));
     if (P > RP) P = RP;
@@ -637,10 +797,10 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C32, co
     if (nb > 2048) nb = 2048;
     if (C64 != nullptr)
         hipLaunchKernelGGL((k_recheck<double, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C64, K, xnorm64,
-                           full_list, counters, P, a_out, d1_out);
+                           nt.ovf_list, nt.counters + 2, P, a_out, d1_out);
     else
         hipLaunchKernelGGL((k_recheck<float, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C32, K, xnorm64,
-                           full_list, counters, P, a_out, d1_out);
+                           nt.ovf_list, nt.counters + 2, P, a_out, d1_out);
     return hipGetLastError();
 }
 

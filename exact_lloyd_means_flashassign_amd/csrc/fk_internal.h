@@ -49,15 +49,31 @@ hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float 
                                 hipStream_t s);
 hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, int32_t *counter,
                               hipStream_t s);
-// counters[0] = length of full_list (near ties to rescore against all K),
-// counters[1] = length of pair_list (near ties between two known centroids,
-// 3 ints per entry: point, k1, k2).
+// Near-tie bookkeeping of FlashAssign (all in the workspace):
+//   counters[0] = length of full_list (near ties whose third score is also in
+//   the window), counters[1] = length of pair_list (near ties between two known
+//   centroids, 3 ints per entry: point, k1, k2), counters[2] = length of
+//   ovf_list (points rescored against all K).
+struct NearTies {
+    int32_t *full_list;
+    float *full_thr;
+    int32_t *pair_list;
+    int32_t *counters;
+    int32_t *cand;    // near_tie_cap(N) slots x 2 halves x 8 candidates
+    int32_t *ccount;  // near_tie_cap(N) slots x 2 halves
+    int32_t *ovf_list;
+};
+constexpr int kCandPerSlot = 16;
+int64_t near_tie_cap(int64_t N);
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                                const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                               int32_t *full_list, int32_t *pair_list, int32_t *counters, hipStream_t s);
-hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C32, const double *C64, int K,
-                          const double *xnorm64, const int32_t *full_list, const int32_t *pair_list,
-                          const int32_t *counters, int32_t *a_out, float *d1_out, hipStream_t s);
+                               const NearTies &nt, hipStream_t s);
+// Settles every listed near tie exactly (fp64 direct-difference distances).
+// C_mfma is the centroid array the MFMA pass used (normalised for cosine); C32
+// (L2) or C64 (cosine, normalised in fp64) is the one the distances use.
+hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma, const float *C32,
+                          const double *C64, const float *ncn, int K, const float *scal, const double *xnorm64,
+                          const NearTies &nt, int32_t *a_out, float *d1_out, hipStream_t s);
 
 // Radix sort of (key = assign[i], value = i), stable, atomic-free.  Writes the
 // sorted keys and the permutation.  tmp* are N-sized scratch arrays.

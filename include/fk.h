@@ -43,8 +43,9 @@
  *     K > N is accepted (some clusters are then empty).
  *   - Exactness: assignments equal the lowest-index argmin of the fp64
  *     direct-difference distance sum_j (x_j - c_j)^2 taken in increasing j:
- *     the fp32 MFMA scores carry a proven error bound, and every point whose
- *     top-2 score gap is within twice that bound is rescored in fp64.
+ *     the fp32 MFMA scores carry a proven error bound, and for every point
+ *     whose top-2 score gap is within twice that bound, every centroid that
+ *     can still win is compared in fp64 by that definition.
  *     Cluster sums are accumulated in fp64.  An empty cluster keeps the
  *     centroid it was given.  Results are bitwise reproducible run to run.
  */
@@ -91,8 +92,9 @@ size_t fk_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric, int64_
  * (fp32; the fp64 value rounded for rescored points).  X, C, assign and
  * min_dist are device pointers.  The N x K distance matrix is never stored:
  * each workgroup keeps a block of points in registers, streams centroid
- * tiles through LDS into fp32 MFMA and keeps a running top-2 per point in
- * registers (FlashAssign section of the Flash-KMeans article).
+ * tiles through LDS into fp32 MFMA and keeps a running top-3 per point in
+ * registers (FlashAssign section of the Flash-KMeans article).  Near ties
+ * are settled in fp64 (see Exactness above).
  */
 fk_status fk_assign(const float *X, int64_t N, int32_t d, const float *C, int32_t K, int32_t metric,
                     int32_t *assign, float *min_dist, void *workspace, size_t workspace_bytes, void *stream);
@@ -177,6 +179,8 @@ typedef struct {
     double ms[FK_NPHASE];
     int64_t rechecked;      /* near-tie points rescored in fp64 against all K      */
     int64_t paired;         /* near-tie points settled by an fp64 two-way compare  */
+    int64_t windowed;       /* near-tie points settled by an fp64 compare of the
+                               centroids collected within their error window     */
     int64_t assigned;       /* points assigned, summed over the calls read         */
 } fk_profile;
 

@@ -192,6 +192,8 @@ def adversarial(seed: int, N: int, d: int, K: int, kind: str = "gauss"):
     """Small seeded inputs for edge cases: returns (X, C) float32.
 
     kinds: "gauss" (random), "dup" (C has duplicated rows, so exact ties),
+    "dup3" (every centroid has two copies, so three-way ties), "dup40" (40
+    copies of one row, so ties wider than any fixed candidate list),
     "grid" (small integers: many exact ties), "far" (large offset, so the
     expanded distance form cancels badly), "zero" (some zero rows in X and C).
     """
@@ -206,6 +208,12 @@ def adversarial(seed: int, N: int, d: int, K: int, kind: str = "gauss"):
         src = rng.integers(0, K, size=K // 2)
         dst = rng.integers(0, K, size=K // 2)
         C[dst] = C[src]
+    if kind == "dup3" and K >= 3:
+        C[1::3] = C[0::3][: len(C[1::3])]
+        C[2::3] = C[0::3][: len(C[2::3])]
+    if kind == "dup40" and K >= 2:
+        C[: min(K, 40)] = C[0]
+        X[: N // 2] = C[0] + np.float32(0.01) * X[: N // 2]
     if kind == "far":
         X += np.float32(100.0)
         C += np.float32(100.0)

@@ -19,7 +19,7 @@ SHAPES = [
 
 
 @pytest.mark.parametrize("N,d,K", SHAPES)
-@pytest.mark.parametrize("kind", ["gauss", "dup", "grid", "far", "zero"])
+@pytest.mark.parametrize("kind", ["gauss", "dup", "dup3", "dup40", "grid", "far", "zero"])
 def test_assign_matches_oracle(gpu_lib, N, d, K, kind):
     fk = gpu_lib
     log(f"assign N={N} d={d} K={K} kind={kind}")
@@ -59,6 +59,22 @@ def test_update_matches_oracle(gpu_lib, N, d, K, metric):
     C_prev = rng.standard_normal((K, d)).astype(np.float32)
     C_out, counts = fk.fk_update(dev(X), dev(a), dev(C_prev), metric=metric)
     check_update(X, a, C_prev, host(C_out), host(counts), metric)
+
+
+@pytest.mark.parametrize("kind,path", [("dup", "paired"), ("dup3", "windowed"), ("dup40", "rechecked")])
+def test_each_near_tie_path_is_taken(gpu_lib, kind, path):
+    """Exact ties between 2, 3 and 40 copies of a centroid send points down
+    each of the three fp64 paths (two-way compare, window compare, all K);
+    the result must match the oracle on every one."""
+    fk = gpu_lib
+    X, C = synth.adversarial(6, 3000, 24, 200, kind)
+    a_ref, _, _ = oracle.assign(X, C)
+    fk.fk_profile_enable(True)
+    a, _ = fk.fk_assign(dev(X), dev(C))
+    prof = fk.fk_profile_read()
+    fk.fk_profile_enable(False)
+    np.testing.assert_array_equal(host(a), a_ref)
+    assert prof[path] > 0, prof
 
 
 def test_update_single_giant_cluster(gpu_lib):
