@@ -74,6 +74,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="zipf_16m_d128_k32768")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy three times (the reference kernel that scales the "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
@@ -85,6 +88,16 @@ def main():
 
     import exact_lloyd_means_flashassign_amd as fk
     import synth
+
+    if args.copy_calibration:
+        n = 1 << 28  # 2^28 floats = 1 GiB read + 1 GiB written per copy
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "copies": 3}))
+        return
 
     fk.load()
     w = synth.WORKLOADS[args.workload]

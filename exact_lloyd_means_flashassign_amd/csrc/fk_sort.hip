@@ -77,6 +77,9 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_hist(const int32_t *__re
 }
 
 // Stable scatter of one pass.  vals_in == nullptr means value = index.
+// The tile is first ordered by digit in LDS (stable), then written out so
+// that consecutive threads write consecutive positions of a digit's run: the
+// global writes are coalesced instead of one scattered 4-byte write per key.
 template <int BITS>
 __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *__restrict__ keys_in,
                                                                 const int32_t *__restrict__ vals_in, int64_t N,
@@ -85,10 +88,16 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *_
                                                                 int32_t *__restrict__ vals_out) {
     constexpr int NB = 1 << BITS;
     __shared__ int wcnt[kSortWaves][NB];
+    __shared__ int dstart[NB];   // first tile-local position of each digit
+    __shared__ int gbase[NB];    // global position of each digit's first key of this tile
+    __shared__ int skey[kSortTile];
+    __shared__ int sval[kSortTile];
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     for (int i = tid; i < kSortWaves * NB; i += kSortThreads) (&wcnt[0][0])[i] = 0;
     __syncthreads();
-    const int64_t row0 = (int64_t)blockIdx.x * kSortTile + (int64_t)w * (kSortRows * 64);
+    const int64_t tile0 = (int64_t)blockIdx.x * kSortTile;
+    const int64_t row0 = tile0 + (int64_t)w * (kSortRows * 64);
+    const int tcount = (int)((N - tile0) < kSortTile ? (N - tile0) : kSortTile);
     int32_t key[kSortRows], val[kSortRows];
     unsigned dig[kSortRows];
 #pragma unroll
@@ -101,15 +110,34 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *_
     }
     tile_counts<BITS>(dig, row0, N, wcnt[w]);
     __syncthreads();
-    // running start of every (wave, digit): global base of the digit in this
-    // tile plus the counts of the earlier waves
-    for (int v = tid; v < NB; v += kSortThreads) {
-        int s = hist_scan[(int64_t)v * ntiles + blockIdx.x];
+    // exclusive scan of the digit totals over the tile (one digit per thread;
+    // NB <= kSortThreads), then each (wave, digit) run start
+    {
+        __shared__ int tot[kSortThreads];
+        const int v = tid;
+        int t = 0;
+        if (v < NB) {
 #pragma unroll
-        for (int ww = 0; ww < kSortWaves; ++ww) {
-            const int c = wcnt[ww][v];
-            wcnt[ww][v] = s;
-            s += c;
+            for (int ww = 0; ww < kSortWaves; ++ww) t += wcnt[ww][v];
+        }
+        tot[tid] = t;
+        __syncthreads();
+        for (int o = 1; o < kSortThreads; o <<= 1) {
+            const int a = tid >= o ? tot[tid - o] : 0;
+            __syncthreads();
+            tot[tid] += a;
+            __syncthreads();
+        }
+        if (v < NB) {
+            int s = tot[v] - t;  // exclusive
+            dstart[v] = s;
+            gbase[v] = hist_scan[(int64_t)v * ntiles + blockIdx.x];
+#pragma unroll
+            for (int ww = 0; ww < kSortWaves; ++ww) {
+                const int c = wcnt[ww][v];
+                wcnt[ww][v] = s;
+                s += c;
+            }
         }
     }
     __syncthreads();
@@ -128,9 +156,17 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *_
         if (valid && below == 0ull) run[dig[r]] += __popcll(m);
         __builtin_amdgcn_wave_barrier();
         if (valid) {
-            if (keys_out != nullptr) keys_out[pos] = key[r];
-            vals_out[pos] = val[r];
+            skey[pos] = key[r];
+            sval[pos] = val[r];
         }
+    }
+    __syncthreads();
+    for (int i = tid; i < tcount; i += kSortThreads) {
+        const int k = skey[i];
+        const unsigned dg = ((unsigned)k >> shift) & (NB - 1);
+        const int pos = gbase[dg] + (i - dstart[dg]);
+        if (keys_out != nullptr) keys_out[pos] = k;
+        vals_out[pos] = sval[i];
     }
 }
 

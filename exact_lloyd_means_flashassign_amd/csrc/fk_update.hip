@@ -220,7 +220,7 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
 template <int NV, int E>
 static hipError_t seg_launch(const float *X, int64_t N, int d, const int32_t *ks, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
-    constexpr int U = NV <= 2 ? 8 : 4;
+    constexpr int U = NV <= 1 ? 16 : (NV <= 2 ? 8 : 4);
     const int64_t nseg = cdiv(N, kSegRows);
     const unsigned gy = (unsigned)cdiv(d, 64 * E * NV);
     hipLaunchKernelGGL((k_seg_reduce<NV, E, U>), dim3((unsigned)cdiv(nseg, kSegWaves), gy), dim3(kSegWaves * 64), 0,
