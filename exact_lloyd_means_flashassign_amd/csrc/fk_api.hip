@@ -57,7 +57,7 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc) {
     };
     const int64_t r = rows > 0 ? rows : 1;
     const int64_t Kpad = cdiv(K, kCentroidPad) * kCentroidPad;
-    const int64_t nseg = cdiv(r, kSegRows);
+    const int64_t nseg = seg_count_bound(r);
     const bool cos = metric == FK_METRIC_COSINE;
     L.ncn = take((size_t)Kpad * 4);
     L.cmax_part = take((size_t)cdiv(Kpad, 4) * 4);

@@ -25,8 +25,23 @@ constexpr int kSortTile = kSortWaves * kSortRows * kWave;       // 4096 keys per
 constexpr int kScanChunk = 4096;                                // scan elements per block
 
 // ---- segmented reduction geometry -----------------------------------------
-constexpr int kSegRows = 2048;    // sorted rows per wave segment
 constexpr int kSegWaves = 4;
+// Sorted rows per wave segment: enough segments to fill the chip (about 8192
+// waves) while keeping each segment long enough to stream, 64..2048 rows.
+inline int seg_rows(int64_t N) {
+    int r = 2048;
+    while (r > 64 && N / r < 8192) r >>= 1;
+    return r;
+}
+// An upper bound of cdiv(n, seg_rows(n)) over all n <= rows (the count is not
+// monotone in n): either the rows were shortened, and then n / (2r) < 8192,
+// or they were not (2048-row segments), or they stopped at 64.
+inline int64_t seg_count_bound(int64_t rows) {
+    const int64_t a = (rows + 63) / 64;
+    int64_t b = (rows + 2047) / 2048;
+    if (b < 16385) b = 16385;
+    return a < b ? a : b;
+}
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }

@@ -7,7 +7,7 @@
 // clusters.  Under a skewed (Zipf) size distribution one cluster can hold a
 // fifth of all points, so a block per cluster would leave one block reading
 // millions of rows.  Here the sorted rows are cut into equal segments of
-// kSegRows rows, one wave each:
+// seg_rows(N) rows, one wave each:
 //   * a cluster that lies inside one segment is summed and written by that
 //     wave alone;
 //   * a cluster that crosses segment boundaries leaves one partial row per
@@ -30,15 +30,15 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t *__restrict__ p, int
 // blockIdx.y * 64*E*NV.  U rows are loaded before they are accumulated so that
 // U row reads per lane are in flight at once.
 template <int NV, int E, int U>
-__global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X, int64_t N, int d,
+__global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X, int64_t N, int d, int srows,
                                                     const int32_t *__restrict__ ks, const int32_t *__restrict__ perm,
                                                     const double *__restrict__ xnorm64, double *__restrict__ sums,
                                                     double *__restrict__ pfirst, double *__restrict__ plast) {
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t seg = (int64_t)blockIdx.x * kSegWaves + w;
-    const int64_t r0 = seg * kSegRows;
+    const int64_t r0 = seg * srows;
     if (r0 >= N) return;
-    const int64_t r1 = (r0 + kSegRows < N) ? r0 + kSegRows : N;
+    const int64_t r1 = (r0 + srows < N) ? r0 + srows : N;
     const int cbase = blockIdx.y * (64 * E * NV);
 
     const int first_k = ks[r0];
@@ -104,11 +104,18 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
                     if (xnorm64 != nullptr) scl[u] = 1.0 / xnorm64[p];
 #pragma unroll
                     for (int v = 0; v < NV; ++v) {
-                        if (E == 2) {
+                        if constexpr (E == 4) {
+                            float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
+                            if (cok[v]) t = *reinterpret_cast<const float4 *>(row + col[v]);
+                            vals[u][v][0] = t.x;
+                            vals[u][v][1] = t.y;
+                            vals[u][v][2] = t.z;
+                            vals[u][v][3] = t.w;
+                        } else if constexpr (E == 2) {
                             float2 t = make_float2(0.f, 0.f);
                             if (cok[v]) t = *reinterpret_cast<const float2 *>(row + col[v]);
                             vals[u][v][0] = t.x;
-                            vals[u][v][E - 1] = t.y;
+                            vals[u][v][1] = t.y;
                         } else {
                             vals[u][v][0] = cok[v] ? row[col[v]] : 0.f;
                         }
@@ -144,20 +151,21 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
 constexpr int kFixWaves = 8;
 __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__restrict__ ks,
                                                              const int32_t *__restrict__ offsets, int64_t N, int d,
+                                                             int srows,
                                                              const double *__restrict__ pfirst,
                                                              const double *__restrict__ plast,
                                                              double *__restrict__ sums) {
     __shared__ double red[kFixWaves][64];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t b = blockIdx.x;
-    const int64_t rb = (b + 1) * kSegRows;
+    const int64_t rb = (b + 1) * srows;
     if (rb >= N) return;
     const int k = ks[rb];
     if (ks[rb - 1] != k) return;
     const int64_t o0 = offsets[k], o1 = offsets[k + 1];
-    const int64_t sa = o0 / kSegRows;
+    const int64_t sa = o0 / srows;
     if (sa != b) return;
-    const int64_t sb = (o1 - 1) / kSegRows;
+    const int64_t sb = (o1 - 1) / srows;
     for (int c0 = 0; c0 < d; c0 += 64) {
         const int c = c0 + lane;
         double s = 0.0;
@@ -220,36 +228,42 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
 template <int NV, int E>
 static hipError_t seg_launch(const float *X, int64_t N, int d, const int32_t *ks, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
-    constexpr int U = NV <= 1 ? 16 : (NV <= 2 ? 8 : 4);
-    const int64_t nseg = cdiv(N, kSegRows);
+    constexpr int U = NV * E <= 2 ? 16 : (NV * E <= 8 ? 8 : 4);
+    const int srows = seg_rows(N);
+    const int64_t nseg = cdiv(N, srows);
     const unsigned gy = (unsigned)cdiv(d, 64 * E * NV);
     hipLaunchKernelGGL((k_seg_reduce<NV, E, U>), dim3((unsigned)cdiv(nseg, kSegWaves), gy), dim3(kSegWaves * 64), 0,
-                       s, X, N, d, ks, perm, xnorm64, sums, pfirst, plast);
+                       s, X, N, d, srows, ks, perm, xnorm64, sums, pfirst, plast);
     return hipGetLastError();
 }
 
+template <int E>
+static hipError_t seg_launch_e(const float *X, int64_t N, int d, const int32_t *ks, const int32_t *perm,
+                               const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
+    const int need = (int)cdiv(d, 64 * E);
+    if (need <= 1) return seg_launch<1, E>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (need <= 2) return seg_launch<2, E>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (need <= 3) return seg_launch<3, E>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    return seg_launch<4, E>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+}
+
+// Row loads of E floats per lane: float4 when a row spans at least 256
+// floats, float2 from 128, scalar otherwise (or when d is not a multiple);
+// column blocks of up to 4 loads per lane, more blocks on blockIdx.y.
 hipError_t launch_seg_reduce(const float *X, int64_t N, int d, const int32_t *ks, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
     if (N <= 0) return hipSuccess;
-    const int E = (d % 2 == 0) ? 2 : 1;
-    const int need = (int)cdiv(d, 64 * E);
-    if (E == 2) {
-        if (need <= 1) return seg_launch<1, 2>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-        if (need <= 2) return seg_launch<2, 2>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-        if (need <= 4) return seg_launch<4, 2>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-        return seg_launch<8, 2>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-    }
-    if (need <= 1) return seg_launch<1, 1>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-    if (need <= 2) return seg_launch<2, 1>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-    if (need <= 4) return seg_launch<4, 1>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-    return seg_launch<8, 1>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (d % 4 == 0 && d >= 256) return seg_launch_e<4>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (d % 2 == 0 && d >= 128) return seg_launch_e<2>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    return seg_launch_e<1>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
 }
 
 hipError_t launch_seg_fixup(const int32_t *ks, const int32_t *offsets, int64_t N, int d, const double *pfirst,
                             const double *plast, double *sums, hipStream_t s) {
-    const int64_t nseg = cdiv(N, kSegRows);
+    const int srows = seg_rows(N);
+    const int64_t nseg = cdiv(N, srows);
     if (nseg <= 1) return hipSuccess;
-    hipLaunchKernelGGL(k_seg_fixup, dim3((unsigned)(nseg - 1)), dim3(kFixWaves * 64), 0, s, ks, offsets, N, d,
+    hipLaunchKernelGGL(k_seg_fixup, dim3((unsigned)(nseg - 1)), dim3(kFixWaves * 64), 0, s, ks, offsets, N, d, srows,
                        pfirst, plast, sums);
     return hipGetLastError();
 }
