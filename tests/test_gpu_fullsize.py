@@ -1,0 +1,92 @@
+"""Parity at the workloads' full sizes, in the launch configuration bench.py
+times (fk_lloyd_iter through the C ABI, X and C resident in HBM).
+
+The oracle cannot score every point against every centroid at these sizes, so
+the assignment is checked exactly on a seeded sample of points (the oracle
+scores each sampled point against all K); the update is checked in full by
+running the oracle's update on the GPU's own assignment (O(Nd)); counts are
+checked in full against bincount of the GPU assignment and against the
+oracle's update.  The out-of-core shape runs at a scaled N (its 10^9 rows need
+512 GB of pinned host memory, more than a GPU-box command may hold) with the
+configured 2^26-row chunks and a ragged last chunk."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_helpers import centroid_rel_err, check_min_dist, dev, host, log
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+
+
+def _sample(N, n, seed):
+    rng = np.random.default_rng([seed, 99])
+    return np.sort(rng.choice(N, size=min(n, N), replace=False))
+
+
+@pytest.mark.parametrize("name,nsample", [("gmm_1m_d128_k1024", 4096), ("ivf_1m_d768_k4096", 1024),
+                                          ("zipf_16m_d128_k32768", 2048)])
+def test_full_size_iteration(gpu_lib, name, nsample):
+    fk = gpu_lib
+    w = synth.WORKLOADS[name]
+    log(f"full size {name}: generating N={w.N}")
+    X = synth.rows(w)
+    C = synth.initial_centroids(w, X)
+    Xd, Cd = dev(X), dev(C)
+    # one warm-up iteration moves the centroids off the sampled points, as in
+    # the timed steps of the benchmark
+    _, C1d, _, _ = fk.fk_lloyd_iter(Xd, Cd)
+    C1 = host(C1d).copy()
+    log(f"full size {name}: second iteration")
+    a, C2d, counts, md = fk.fk_lloyd_iter(Xd, C1d, with_min_dist=True)
+    a = host(a)
+    counts = host(counts)
+    C2 = host(C2d)
+    md = host(md)
+    assert counts.sum() == w.N
+    np.testing.assert_array_equal(counts, np.bincount(a, minlength=w.K))
+    idx = _sample(w.N, nsample, w.seed)
+    log(f"full size {name}: oracle on {len(idx)} sampled points")
+    a_ref, D1, D2 = oracle.assign(X[idx], C1)
+    np.testing.assert_array_equal(a[idx], a_ref)
+    check_min_dist(md[idx], D1, X[idx], C1)
+    log(f"full size {name}: oracle update on the GPU assignment")
+    C_ref, n_ref = oracle.update(X, a, C1)
+    np.testing.assert_array_equal(counts, n_ref)
+    err = centroid_rel_err(C2, C_ref, n_ref)
+    assert err <= 1e-6, err
+    empty = n_ref == 0
+    assert np.array_equal(C2[empty].view(np.uint32), C1[empty].view(np.uint32))
+
+
+def test_out_of_core_scaled(gpu_lib):
+    fk = gpu_lib
+    w0 = synth.WORKLOADS["ooc_1b_d128_k32768"]
+    N = (1 << 26) + (1 << 25) + 777          # two chunks of 2^26 rows, the second ragged
+    w = w0.scaled(N)
+    log(f"out of core: N={N}, chunk {w.chunk_rows}")
+    Xh = torch.empty((N, w.d), dtype=torch.float32, pin_memory=True)
+    X = Xh.numpy()
+    synth.rows(w, out=X)
+    C = X[synth.init_indices(w)].copy()
+    ah = torch.empty(N, dtype=torch.int32, pin_memory=True)
+    Cd = dev(C)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    C1d, cnt = fk.fk_lloyd_iter_stream(Xh, Cd, w.chunk_rows, assign_host=ah)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    log(f"out of core: one iteration in {dt:.2f} s including PCIe ({N * w.d * 4 / dt / 1e9:.1f} GB/s of X)")
+    a = ah.numpy()
+    counts = host(cnt)
+    assert counts.sum() == N
+    np.testing.assert_array_equal(counts, np.bincount(a, minlength=w.K))
+    idx = _sample(N, 1024, 3)
+    a_ref, _, _ = oracle.assign(X[idx], C)
+    np.testing.assert_array_equal(a[idx], a_ref)
+    C_ref, n_ref = oracle.update(X, a, C)
+    np.testing.assert_array_equal(counts, n_ref)
+    assert centroid_rel_err(host(C1d), C_ref, n_ref) <= 1e-6
