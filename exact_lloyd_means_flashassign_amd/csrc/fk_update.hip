@@ -21,6 +21,9 @@
 
 namespace fk {
 
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef float f4v __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void k_fill_zero(uint32_t *__restrict__ p, int64_t n) {
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
         p[i] = 0u;
@@ -104,20 +107,22 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
                     if (xnorm64 != nullptr) scl[u] = 1.0 / xnorm64[p];
 #pragma unroll
                     for (int v = 0; v < NV; ++v) {
+                        // each row is read once: non-temporal loads keep the
+                        // stream from evicting the sorted keys and the sums
                         if constexpr (E == 4) {
-                            float4 t = make_float4(0.f, 0.f, 0.f, 0.f);
-                            if (cok[v]) t = *reinterpret_cast<const float4 *>(row + col[v]);
+                            f4v t = {0.f, 0.f, 0.f, 0.f};
+                            if (cok[v]) t = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(row + col[v]));
                             vals[u][v][0] = t.x;
                             vals[u][v][1] = t.y;
                             vals[u][v][2] = t.z;
                             vals[u][v][3] = t.w;
                         } else if constexpr (E == 2) {
-                            float2 t = make_float2(0.f, 0.f);
-                            if (cok[v]) t = *reinterpret_cast<const float2 *>(row + col[v]);
+                            f2v t = {0.f, 0.f};
+                            if (cok[v]) t = __builtin_nontemporal_load(reinterpret_cast<const f2v *>(row + col[v]));
                             vals[u][v][0] = t.x;
                             vals[u][v][1] = t.y;
                         } else {
-                            vals[u][v][0] = cok[v] ? row[col[v]] : 0.f;
+                            vals[u][v][0] = cok[v] ? __builtin_nontemporal_load(row + col[v]) : 0.f;
                         }
                     }
                 }
