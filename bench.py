@@ -73,6 +73,8 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="zipf_16m_d128_k32768")
+    ap.add_argument("--score", default="fp32", choices=["fp32", "split_bf16"],
+                    help="FlashAssign scoring: fp32 MFMA, or bf16 MFMA on split operands (same exact result)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference kernel that scales the "
@@ -117,7 +119,7 @@ def main():
 
     def step(i):
         fk.fk_lloyd_iter(Xd, Cs[i % 2], metric=w.metric, assign=a, C_out=Cs[(i + 1) % 2], counts=counts,
-                         workspace=ws)
+                         workspace=ws, score=args.score)
 
     for i in range(args.warmup):
         step(i)

@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(_HERE, "libfk.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fk.h")
 
 METRICS = {"l2": 0, "cosine": 1, "inner_product": 2}
+SCORES = {"fp32": 0, "split_bf16": 1}
 PHASES = ("prep", "assign", "recheck", "sort", "reduce", "finalize", "h2d")
 MAX_K = 65536
 MAX_D = 4096
@@ -57,11 +58,11 @@ def load():
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.fk_workspace_size.argtypes = [I64, I32, I32, I32, I64]
     lib.fk_workspace_size.restype = SZ
-    lib.fk_assign.argtypes = [P, I64, I32, P, I32, I32, P, P, P, SZ, P]
+    lib.fk_assign.argtypes = [P, I64, I32, P, I32, I32, I32, P, P, P, SZ, P]
     lib.fk_sort_inverse.argtypes = [P, I64, I32, P, P, P, SZ, P]
     lib.fk_update.argtypes = [P, I64, I32, P, I32, I32, P, P, P, P, SZ, P]
-    lib.fk_lloyd_iter.argtypes = [P, I64, I32, P, I32, I32, P, P, P, P, P, SZ, P]
-    lib.fk_lloyd_iter_stream.argtypes = [P, I64, I32, P, I32, I32, I64, P, P, P, P, SZ, P]
+    lib.fk_lloyd_iter.argtypes = [P, I64, I32, P, I32, I32, I32, P, P, P, P, P, SZ, P]
+    lib.fk_lloyd_iter_stream.argtypes = [P, I64, I32, P, I32, I32, I32, I64, P, P, P, P, SZ, P]
     for f in ("fk_assign", "fk_sort_inverse", "fk_update", "fk_lloyd_iter", "fk_lloyd_iter_stream",
               "fk_profile_enable", "fk_profile_read"):
         getattr(lib, f).restype = ctypes.c_int
@@ -105,6 +106,15 @@ def _metric(m) -> int:
         return METRICS[m]
     except KeyError:
         raise ValueError(f"unknown metric {m!r}") from None
+
+
+def _score(s) -> int:
+    if isinstance(s, int):
+        return s
+    try:
+        return SCORES[s]
+    except KeyError:
+        raise ValueError(f"unknown score mode {s!r}") from None
 
 
 def _dev(t, name, dtype, shape=None):
@@ -175,8 +185,9 @@ def _ws_args(N, d, K, metric, device, workspace, chunk_rows=0):
     return ctypes.c_void_p(p), ctypes.c_size_t(n)
 
 
-def fk_assign(X, C, metric="l2", assign=None, min_dist=None, with_min_dist=False, workspace=None):
-    """FlashAssign: returns (assign int32[N], min_dist float32[N] or None)."""
+def fk_assign(X, C, metric="l2", assign=None, min_dist=None, with_min_dist=False, workspace=None, score="fp32"):
+    """FlashAssign: returns (assign int32[N], min_dist float32[N] or None).
+    score: "fp32" or "split_bf16" (same exact result, different speed)."""
     _dev(X, "X", torch.float32)
     _dev(C, "C", torch.float32)
     if X.dim() != 2 or C.dim() != 2 or X.shape[1] != C.shape[1]:
@@ -191,8 +202,8 @@ def fk_assign(X, C, metric="l2", assign=None, min_dist=None, with_min_dist=False
     if min_dist is not None:
         _dev(min_dist, "min_dist", torch.float32, (N,))
     ws, wsn = _ws_args(N, d, K, metric, X.device, workspace)
-    _check(load().fk_assign(_ptr(X), N, d, _ptr(C), K, _metric(metric), _ptr(assign), _ptr(min_dist), ws, wsn,
-                            _stream(X.device)))
+    _check(load().fk_assign(_ptr(X), N, d, _ptr(C), K, _metric(metric), _score(score), _ptr(assign),
+                            _ptr(min_dist), ws, wsn, _stream(X.device)))
     return assign, min_dist
 
 
@@ -232,7 +243,7 @@ def fk_update(X, assign, C_prev, metric="l2", C_out=None, counts=None, workspace
 
 
 def fk_lloyd_iter(X, C_in, metric="l2", assign=None, C_out=None, counts=None, min_dist=None, with_min_dist=False,
-                  workspace=None):
+                  workspace=None, score="fp32"):
     """One Lloyd iteration: returns (assign, C_out, counts, min_dist or None)."""
     _dev(X, "X", torch.float32)
     _dev(C_in, "C_in", torch.float32)
@@ -254,13 +265,13 @@ def fk_lloyd_iter(X, C_in, metric="l2", assign=None, C_out=None, counts=None, mi
     if min_dist is not None:
         _dev(min_dist, "min_dist", torch.float32, (N,))
     ws, wsn = _ws_args(N, d, K, metric, X.device, workspace)
-    _check(load().fk_lloyd_iter(_ptr(X), N, d, _ptr(C_in), K, _metric(metric), _ptr(assign), _ptr(min_dist),
-                                _ptr(C_out), _ptr(counts), ws, wsn, _stream(X.device)))
+    _check(load().fk_lloyd_iter(_ptr(X), N, d, _ptr(C_in), K, _metric(metric), _score(score), _ptr(assign),
+                                _ptr(min_dist), _ptr(C_out), _ptr(counts), ws, wsn, _stream(X.device)))
     return assign, C_out, counts, min_dist
 
 
 def fk_lloyd_iter_stream(X_host, C_in, chunk_rows: int, metric="l2", assign_host=None, C_out=None, counts=None,
-                         workspace=None):
+                         workspace=None, score="fp32"):
     """Out-of-core iteration from pinned host X: returns (C_out, counts).
     assign_host, if given, must be a pinned int32[N] host tensor."""
     _host_pinned(X_host, "X_host", torch.float32)
@@ -276,8 +287,8 @@ def fk_lloyd_iter_stream(X_host, C_in, chunk_rows: int, metric="l2", assign_host
     _dev(C_out, "C_out", torch.float32, (K, d))
     _dev(counts, "counts", torch.int32, (K,))
     ws, wsn = _ws_args(N, d, K, metric, C_in.device, workspace, chunk_rows=chunk_rows)
-    _check(load().fk_lloyd_iter_stream(_ptr(X_host), N, d, _ptr(C_in), K, _metric(metric), int(chunk_rows),
-                                       _ptr(assign_host), _ptr(C_out), _ptr(counts), ws, wsn,
+    _check(load().fk_lloyd_iter_stream(_ptr(X_host), N, d, _ptr(C_in), K, _metric(metric), _score(score),
+                                       int(chunk_rows), _ptr(assign_host), _ptr(C_out), _ptr(counts), ws, wsn,
                                        _stream(C_in.device)))
     return C_out, counts
 

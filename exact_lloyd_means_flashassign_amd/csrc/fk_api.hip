@@ -41,7 +41,7 @@ struct Layout {
     size_t ncn, cmax_part, scal, counter, flags, thr, pairs, cand, ccount, ovf;
     size_t c64, c32, cnrm64, xnorm64;  // cosine only (else ~0)
     size_t keys_sorted, perm, tmp_keys, tmp_vals, sort_scratch, offsets;
-    size_t sums, cnt, pfirst, plast;
+    size_t sums, cnt, pfirst, plast, chi, clo;
     size_t xchunk[2], achunk[2];      // out-of-core only
 };
 
@@ -79,6 +79,8 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc) {
     L.tmp_vals = take((size_t)r * 4);
     L.sort_scratch = take(sort_scratch_bytes(r));
     L.offsets = take((size_t)(K + 1) * 4);
+    L.chi = take((size_t)K * cdiv(d, 8) * 8 * 2);
+    L.clo = take((size_t)K * cdiv(d, 8) * 8 * 2);
     L.sums = take((size_t)K * d * 8);
     L.cnt = take((size_t)K * 4);
     L.pfirst = take((size_t)nseg * d * 8);
@@ -101,6 +103,12 @@ fk_status check_sizes(int64_t N, int64_t d, int64_t K) {
     if (N < 0 || N > INT32_MAX) return fail(FK_ERR_INVALID_ARG, "N=%lld outside [0, 2^31-1]", (long long)N);
     if (d < 1 || d > FK_MAX_D) return fail(FK_ERR_INVALID_ARG, "d=%lld outside [1, %d]", (long long)d, FK_MAX_D);
     if (K < 1 || K > FK_MAX_K) return fail(FK_ERR_INVALID_ARG, "K=%lld outside [1, %d]", (long long)K, FK_MAX_K);
+    return FK_OK;
+}
+
+fk_status check_score(int32_t score) {
+    if (score != FK_SCORE_FP32 && score != FK_SCORE_SPLIT_BF16)
+        return fail(FK_ERR_INVALID_ARG, "unknown score mode %d", (int)score);
     return FK_OK;
 }
 
@@ -203,6 +211,11 @@ struct Ctx {
     void *ws;
     hipStream_t s;
     int d, K, metric;
+    int score;
+    SplitC split() const {
+        if (score != FK_SCORE_SPLIT_BF16) return SplitC{nullptr, nullptr};
+        return SplitC{at<__bf16>(ws, L.chi), at<__bf16>(ws, L.clo)};
+    }
 };
 
 // Centroid norms (and, for cosine, the normalised centroids).  Returns the
@@ -224,6 +237,7 @@ fk_status step_prep(const Ctx &c, const float *C, const float **C_use) {
     FK_TRY(launch_prep_finish(at<float>(c.ws, c.L.cmax_part), nparts, at<float>(c.ws, c.L.scal),
                               at<int32_t>(c.ws, c.L.counter), c.s),
            "centroid prep finish");
+    if (c.score == FK_SCORE_SPLIT_BF16) FK_TRY(launch_split_bf16(Cu, c.K, c.d, c.split(), c.s), "centroid split");
     *C_use = Cu;
     return FK_OK;
 }
@@ -252,14 +266,14 @@ fk_status step_assign(const Ctx &c, const float *X, int64_t rows, const float *C
     {
         PhaseScope ph(FK_PH_ASSIGN, c.s);
         FK_TRY(launch_flash_assign(X, rows, c.d, C_use, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal), xn,
-                                   a_out, d1_out, nt, c.s),
+                                   a_out, d1_out, nt, c.split(), c.s),
                "flash assign");
     }
     {
         PhaseScope ph(FK_PH_RECHECK, c.s);
         const double *c64 = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.c64) : nullptr;
         FK_TRY(launch_recheck(X, rows, c.d, C_use, C, c64, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal),
-                              xn, nt, a_out, d1_out, c.s),
+                              xn, nt, c.split(), a_out, d1_out, c.s),
                "near-tie recheck");
     }
     prof_count_rechecks(at<int32_t>(c.ws, c.L.counter), rows, c.s);
@@ -353,17 +367,18 @@ const char *fk_status_str(int32_t s) {
 
 const char *fk_last_error(void) { return g_err; }
 
-fk_status fk_assign(const float *X, int64_t N, int32_t d, const float *C, int32_t K, int32_t metric, int32_t *assign,
-                    float *min_dist, void *workspace, size_t workspace_bytes, void *stream) {
+fk_status fk_assign(const float *X, int64_t N, int32_t d, const float *C, int32_t K, int32_t metric, int32_t score,
+                    int32_t *assign, float *min_dist, void *workspace, size_t workspace_bytes, void *stream) {
     g_err[0] = 0;
     fk_status st = check_common(X, N, d, C, K, metric);
     if (st != FK_OK) return st;
+    if ((st = check_score(score)) != FK_OK) return st;
     if (N > 0 && assign == nullptr) return fail(FK_ERR_INVALID_ARG, "assign is NULL");
     const Layout L = make_layout(N, d, K, metric, false);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
     if (N == 0) return FK_OK;
-    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric};
+    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
     const float *Cu = nullptr;
     if ((st = step_prep(c, C, &Cu)) != FK_OK) return st;
     if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
@@ -381,7 +396,7 @@ fk_status fk_sort_inverse(const int32_t *assign, int64_t N, int32_t K, int32_t *
     const Layout L = make_layout(N, 1, K, FK_METRIC_L2, false);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
-    const Ctx c{L, workspace, (hipStream_t)stream, 1, K, FK_METRIC_L2};
+    const Ctx c{L, workspace, (hipStream_t)stream, 1, K, FK_METRIC_L2, FK_SCORE_FP32};
     if (N == 0) {
         FK_TRY(launch_offsets(nullptr, 0, K, offsets, c.s), "cluster offsets");
         return FK_OK;
@@ -402,7 +417,7 @@ fk_status fk_update(const float *X, int64_t N, int32_t d, const int32_t *assign,
     const Layout L = make_layout(N, d, K, metric, false);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
-    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric};
+    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, FK_SCORE_FP32};
     if ((st = step_zero_accumulators(c)) != FK_OK) return st;
     if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
     if ((st = step_accumulate(c, X, N, assign)) != FK_OK) return st;
@@ -410,11 +425,12 @@ fk_status fk_update(const float *X, int64_t N, int32_t d, const int32_t *assign,
 }
 
 fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in, int32_t K, int32_t metric,
-                        int32_t *assign, float *min_dist, float *C_out, int32_t *counts, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+                        int32_t score, int32_t *assign, float *min_dist, float *C_out, int32_t *counts,
+                        void *workspace, size_t workspace_bytes, void *stream) {
     g_err[0] = 0;
     fk_status st = check_common(X, N, d, C_in, K, metric);
     if (st != FK_OK) return st;
+    if ((st = check_score(score)) != FK_OK) return st;
     if (N > 0 && assign == nullptr) return fail(FK_ERR_INVALID_ARG, "assign is NULL");
     if (C_out == nullptr || counts == nullptr) return fail(FK_ERR_INVALID_ARG, "C_out and counts must not be NULL");
     const size_t cb = (size_t)K * d * 4;
@@ -422,7 +438,7 @@ fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in,
     const Layout L = make_layout(N, d, K, metric, false);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
-    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric};
+    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
     if ((st = step_zero_accumulators(c)) != FK_OK) return st;
     if (N > 0) {
         const float *Cu = nullptr;
@@ -483,11 +499,13 @@ bool is_pinned_host(const void *p) {
 }  // namespace
 
 fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const float *C_in, int32_t K,
-                               int32_t metric, int64_t chunk_rows, int32_t *assign_host, float *C_out,
-                               int32_t *counts, void *workspace, size_t workspace_bytes, void *stream) {
+                               int32_t metric, int32_t score, int64_t chunk_rows, int32_t *assign_host,
+                               float *C_out, int32_t *counts, void *workspace, size_t workspace_bytes,
+                               void *stream) {
     g_err[0] = 0;
     fk_status st = check_common(X_host, N, d, C_in, K, metric);
     if (st != FK_OK) return st;
+    if ((st = check_score(score)) != FK_OK) return st;
     if (chunk_rows < 1 || chunk_rows > INT32_MAX)
         return fail(FK_ERR_INVALID_ARG, "chunk_rows=%lld must be in [1, 2^31-1]", (long long)chunk_rows);
     if (C_out == nullptr || counts == nullptr) return fail(FK_ERR_INVALID_ARG, "C_out and counts must not be NULL");
@@ -502,7 +520,7 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
     OocRes *R = nullptr;
     if ((st = ooc_resources(&R)) != FK_OK) return st;
 
-    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric};
+    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
     if ((st = step_zero_accumulators(c)) != FK_OK) return st;
     const float *Cu = nullptr;
     if (N > 0 && (st = step_prep(c, C_in, &Cu)) != FK_OK) return st;

@@ -24,6 +24,7 @@
 namespace fk {
 
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 // candidates kept per point half-lane when the full near-tie list is collected
 constexpr int kMaxCand = 8;
@@ -46,6 +47,9 @@ struct FlashArgs {
     int32_t *cand;       // collect mode: candidates per (slot, half)
     int32_t *ccount;     // collect mode: candidate counts per (slot, half)
     int64_t cap_slots;   // collect mode: slots with candidate storage
+    const __bf16 *Ch;    // split scoring: bf16 high parts of C, rows of dpad
+    const __bf16 *Cl;    // split scoring: bf16 low parts (C - Ch, rounded)
+    int dpad;            // d rounded up to a multiple of 8
 };
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -168,19 +172,27 @@ __global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ c
 // the full list.  For cosine, the fp32 normalised rows differ from the fp64
 // normalised ones by at most 3.1u relative, which moves a by at most
 // 3.1u (||x|| ||c|| + ||c||^2); 8u is added to g for it.
-template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool VEC, bool COLLECT>
+template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool VEC, bool COLLECT, bool SPLIT>
 __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashArgs A) {
     constexpr int NT = WAVES * 64;
     constexpr int HALF = DP / 2;
     constexpr int ROWS = CB * 32;
-    constexpr int LDR = DP + 4;  // padded LDS row: 8 consecutive lanes hit distinct 16-B bank groups
+    constexpr int LDR = DP + 4;  // padded fp32 LDS row: 8 consecutive lanes hit distinct 16-B bank groups
+    constexpr int LDB = DP + 8;  // padded bf16 LDS row (split scoring), same property
     constexpr int Q4 = DP / 4;
     constexpr int NQ4 = ROWS * Q4;
-    constexpr int PFN = (NQ4 + NT - 1) / NT;
+    constexpr int PFN = SPLIT ? 1 : (NQ4 + NT - 1) / NT;
+    constexpr int Q8 = DP / 8;
+    constexpr int NQ8 = ROWS * Q8;
+    constexpr int PFS = SPLIT ? (NQ8 + NT - 1) / NT : 1;
+    constexpr int NS = DP / 16;           // split scoring: 16-dim MFMA steps per chunk
     constexpr int BM = WAVES * PB * 32;  // points per workgroup pass
     static_assert(HALF % 4 == 0, "DP must be a multiple of 8");
+    static_assert(!SPLIT || DP % 16 == 0, "split scoring needs DP a multiple of 16");
 
-    __shared__ __attribute__((aligned(16))) float sC[2][ROWS * LDR];
+    __shared__ __attribute__((aligned(16))) float sC[2][SPLIT ? 4 : ROWS * LDR];
+    __shared__ __attribute__((aligned(16))) __bf16 sCh[2][SPLIT ? ROWS * LDB : 8];
+    __shared__ __attribute__((aligned(16))) __bf16 sCl[2][SPLIT ? ROWS * LDB : 8];
     __shared__ __attribute__((aligned(16))) float sN[2][ROWS];
 
     const float *__restrict__ X = A.X;
@@ -201,43 +213,76 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
 
         // global -> registers for one centroid stage (tile t, d-chunk ch)
         float4 pf[PFN];
+        float4 pfh[PFS], pfl[PFS];
         float pn = 0.f;
         auto load_stage = [&](int t, int ch) {
+            if constexpr (SPLIT) {
 #pragma unroll
-            for (int i = 0; i < PFN; ++i) {
-                const int q = tid + i * NT;
-                float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                if (q < NQ4) {
-                    const int row = q / Q4;
-                    const int col = ch * DP + (q % Q4) * 4;
-                    const int k = t * ROWS + row;
-                    if (k < K) {
-                        const float *src = C + (size_t)k * d + col;
-                        if (VEC) {
-                            if (col < d) v = *reinterpret_cast<const float4 *>(src);
-                        } else {
-                            if (col < d) v.x = src[0];
-                            if (col + 1 < d) v.y = src[1];
-                            if (col + 2 < d) v.z = src[2];
-                            if (col + 3 < d) v.w = src[3];
+                for (int i = 0; i < PFS; ++i) {
+                    const int q = tid + i * NT;
+                    float4 vh = make_float4(0.f, 0.f, 0.f, 0.f), vl = vh;
+                    if (q < NQ8) {
+                        const int row = q / Q8;
+                        const int col = ch * DP + (q % Q8) * 8;
+                        const int k = t * ROWS + row;
+                        if (k < K && col < A.dpad) {
+                            vh = *reinterpret_cast<const float4 *>(A.Ch + (size_t)k * A.dpad + col);
+                            vl = *reinterpret_cast<const float4 *>(A.Cl + (size_t)k * A.dpad + col);
                         }
                     }
+                    pfh[i] = vh;
+                    pfl[i] = vl;
                 }
-                pf[i] = v;
+            } else {
+#pragma unroll
+                for (int i = 0; i < PFN; ++i) {
+                    const int q = tid + i * NT;
+                    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                    if (q < NQ4) {
+                        const int row = q / Q4;
+                        const int col = ch * DP + (q % Q4) * 4;
+                        const int k = t * ROWS + row;
+                        if (k < K) {
+                            const float *src = C + (size_t)k * d + col;
+                            if (VEC) {
+                                if (col < d) v = *reinterpret_cast<const float4 *>(src);
+                            } else {
+                                if (col < d) v.x = src[0];
+                                if (col + 1 < d) v.y = src[1];
+                                if (col + 2 < d) v.z = src[2];
+                                if (col + 3 < d) v.w = src[3];
+                            }
+                        }
+                    }
+                    pf[i] = v;
+                }
             }
             if (ch == 0 && tid < ROWS) pn = A.ncn[t * ROWS + tid];
         };
         // registers -> LDS buffer
         auto store_stage = [&](int buf, int ch) {
+            if constexpr (SPLIT) {
 #pragma unroll
-            for (int i = 0; i < PFN; ++i) {
-                const int q = tid + i * NT;
-                if (q < NQ4) *reinterpret_cast<float4 *>(&sC[buf][(q / Q4) * LDR + (q % Q4) * 4]) = pf[i];
+                for (int i = 0; i < PFS; ++i) {
+                    const int q = tid + i * NT;
+                    if (q < NQ8) {
+                        const int o = (q / Q8) * LDB + (q % Q8) * 8;
+                        *reinterpret_cast<float4 *>(&sCh[buf][o]) = pfh[i];
+                        *reinterpret_cast<float4 *>(&sCl[buf][o]) = pfl[i];
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < PFN; ++i) {
+                    const int q = tid + i * NT;
+                    if (q < NQ4) *reinterpret_cast<float4 *>(&sC[buf][(q / Q4) * LDR + (q % Q4) * 4]) = pf[i];
+                }
             }
             if (ch == 0 && tid < ROWS) sN[buf][tid] = pn;
         };
 
-        float xr[PB][HALF];
+        float xr[PB][SPLIT ? 1 : HALF];
+        v8bf xh[PB][SPLIT ? NS : 1], xl[PB][SPLIT ? NS : 1];
         // assign mode: running top-3 scores per point (b1 >= b2 >= b3) and the
         // indices of the first two.  collect mode: the listed point's
         // threshold and this half-lane's candidate count.
@@ -264,35 +309,71 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             i1[b] = 0;
             i2[b] = 0;
         }
-        // this wave's points, dims ch*DP + h*HALF + [0, HALF), into registers
+        // this wave's points into registers.  fp32 scoring: dims
+        // ch*DP + h*HALF + [0, HALF).  split scoring: for MFMA step s, dims
+        // ch*DP + 16s + 8h + [0, 8), each split into a bf16 high part (the
+        // round-to-nearest value) and a bf16 low part (the rounded remainder).
         auto load_x = [&](int ch, bool add_norm) {
 #pragma unroll
             for (int b = 0; b < PB; ++b) {
-                const int col0 = ch * DP + h * HALF;
-                const float *src = X + (size_t)pt[b] * d + col0;
-                if (VEC) {
+                if constexpr (SPLIT) {
+                    float nacc = xn[b];
 #pragma unroll
-                    for (int s = 0; s < HALF; s += 4) {
-                        float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                        if (pv[b] && col0 + s < d) v = *reinterpret_cast<const float4 *>(src + s);
-                        xr[b][s] = v.x;
-                        xr[b][s + 1] = v.y;
-                        xr[b][s + 2] = v.z;
-                        xr[b][s + 3] = v.w;
+                    for (int st = 0; st < NS; ++st) {
+                        const int col0 = ch * DP + 16 * st + 8 * h;
+                        const float *src = X + (size_t)pt[b] * d + col0;
+                        float v[8];
+                        if (VEC) {
+                            float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
+                            if (pv[b] && col0 < d) u0 = *reinterpret_cast<const float4 *>(src);
+                            if (pv[b] && col0 + 4 < d) u1 = *reinterpret_cast<const float4 *>(src + 4);
+                            v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
+                            v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
+                        } else {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) v[e] = (pv[b] && col0 + e < d) ? src[e] : 0.f;
+                        }
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const float xv = (A.xnorm64 != nullptr) ? v[e] * xsc[b] : v[e];
+                            if (add_norm) nacc = fmaf(xv, xv, nacc);
+                            const __bf16 hi = (__bf16)xv;
+                            xh[b][st][e] = hi;
+                            xl[b][st][e] = (__bf16)(xv - (float)hi);
+                        }
+                        // keep the scheduler from hoisting every load of the
+                        // row ahead of the splits (it would hold all the fp32
+                        // values and the bf16 halves live at once)
+                        __builtin_amdgcn_sched_barrier(0);
                     }
+                    xn[b] = nacc;
                 } else {
+                    const int col0 = ch * DP + h * HALF;
+                    const float *src = X + (size_t)pt[b] * d + col0;
+                    if (VEC) {
 #pragma unroll
-                    for (int s = 0; s < HALF; ++s) xr[b][s] = (pv[b] && col0 + s < d) ? src[s] : 0.f;
-                }
-                if (A.xnorm64 != nullptr) {
+                        for (int s = 0; s < HALF; s += 4) {
+                            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+                            if (pv[b] && col0 + s < d) v = *reinterpret_cast<const float4 *>(src + s);
+                            xr[b][s] = v.x;
+                            xr[b][s + 1] = v.y;
+                            xr[b][s + 2] = v.z;
+                            xr[b][s + 3] = v.w;
+                        }
+                    } else {
 #pragma unroll
-                    for (int s = 0; s < HALF; ++s) xr[b][s] *= xsc[b];
-                }
-                if (add_norm) {
-                    float acc = xn[b];
+                        for (int s = 0; s < HALF; ++s) xr[b][s] = (pv[b] && col0 + s < d) ? src[s] : 0.f;
+                    }
+                    if (A.xnorm64 != nullptr) {
 #pragma unroll
-                    for (int s = 0; s < HALF; ++s) acc = fmaf(xr[b][s], xr[b][s], acc);
-                    xn[b] = acc;
+                        for (int s = 0; s < HALF; ++s) xr[b][s] *= xsc[b];
+                    }
+                    if (add_norm) {
+                        float acc = xn[b];
+#pragma unroll
+                        for (int s = 0; s < HALF; ++s) acc = fmaf(xr[b][s], xr[b][s], acc);
+                        xn[b] = acc;
+                    }
                 }
             }
         };
@@ -336,20 +417,44 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 }
             }
 
-            const float *sc = &sC[buf][jl * LDR + h * HALF];
+            if constexpr (SPLIT) {
+                // x.c ~ hi.hi + hi.lo + lo.hi, small terms first
+                const __bf16 *sh = &sCh[buf][jl * LDB + 8 * h];
+                const __bf16 *sl = &sCl[buf][jl * LDB + 8 * h];
 #pragma unroll
-            for (int s = 0; s < HALF; s += 4) {
-                float4 av[CB];
+                for (int st = 0; st < NS; ++st) {
+                    v8bf ah[CB], al[CB];
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) av[cb] = *reinterpret_cast<const float4 *>(sc + cb * 32 * LDR + s);
+                    for (int cb = 0; cb < CB; ++cb) {
+                        ah[cb] = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB + 16 * st);
+                        al[cb] = *reinterpret_cast<const v8bf *>(sl + cb * 32 * LDB + 16 * st);
+                    }
 #pragma unroll
-                for (int cb = 0; cb < CB; ++cb) {
+                    for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
-                    for (int b = 0; b < PB; ++b) {
-                        acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].x, xr[b][s + 0], acc[b][cb], 0, 0, 0);
-                        acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].y, xr[b][s + 1], acc[b][cb], 0, 0, 0);
-                        acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].z, xr[b][s + 2], acc[b][cb], 0, 0, 0);
-                        acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].w, xr[b][s + 3], acc[b][cb], 0, 0, 0);
+                        for (int b = 0; b < PB; ++b) {
+                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[cb], xh[b][st], acc[b][cb], 0, 0, 0);
+                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[cb], xl[b][st], acc[b][cb], 0, 0, 0);
+                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[cb], xh[b][st], acc[b][cb], 0, 0, 0);
+                        }
+                    }
+                }
+            } else {
+                const float *sc = &sC[buf][jl * LDR + h * HALF];
+#pragma unroll
+                for (int s = 0; s < HALF; s += 4) {
+                    float4 av[CB];
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) av[cb] = *reinterpret_cast<const float4 *>(sc + cb * 32 * LDR + s);
+#pragma unroll
+                    for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+                        for (int b = 0; b < PB; ++b) {
+                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].x, xr[b][s + 0], acc[b][cb], 0, 0, 0);
+                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].y, xr[b][s + 1], acc[b][cb], 0, 0, 0);
+                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].z, xr[b][s + 2], acc[b][cb], 0, 0, 0);
+                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x2f32(av[cb].w, xr[b][s + 3], acc[b][cb], 0, 0, 0);
+                        }
                     }
                 }
             }
@@ -360,6 +465,15 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 for (int b = 0; b < PB; ++b) {
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
+                        // A value changes this lane's state only if it beats the
+                        // third best (top-3) or reaches the threshold (collect).
+                        // Late in the sweep most 16-value groups change no lane
+                        // of the wave; they are skipped with one wave vote.
+                        bool any = false;
+#pragma unroll
+                        for (int r = 0; r < 16; ++r)
+                            any |= COLLECT ? (acc[b][cb][r] >= b1[b]) : (acc[b][cb][r] > b3[b]);
+                        if (__ballot(any) == 0ull) continue;
 #pragma unroll
                         for (int r = 0; r < 16; ++r) {
                             const float v = acc[b][cb][r];
@@ -404,7 +518,9 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         // merge the two half-waves (same point, the other 16 centroids of each
         // 32-block): larger score first, lower index first on equal scores
         const float u = 5.9604645e-8f;
-        const float g = (float)(d + 4) * u + (A.xnorm64 != nullptr ? 8.f * u : 0.f);
+        // roundings per accumulator path: d + 3 (fp32 scoring) or 3d + 3
+        // (split: three products per dim)
+        const float g = (float)((SPLIT ? 3 : 1) * d + 4) * u + (A.xnorm64 != nullptr ? 8.f * u : 0.f);
         const float M = A.scal[0] * (1.f + g);
         const float sqM = sqrtf(M) * (1.f + 2.f * u);
 #pragma unroll
@@ -429,7 +545,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             const int64_t p = pt[b];
             const bool valid = (h == 0) && pv[b];
             const float xnorm = sqrtf(xnt * (1.f + g)) * (1.f + 2.f * u);
-            const float e2 = 2.f * (1.0625f * g * (M + xnorm * sqM) + 1e-30f);
+            // split scoring also drops lo.lo and the bf16 remainders:
+            // at most 3.01 * 2^-18 sum_j |x_j c_j| <= 1.15e-5 ||x|| ||c||;
+            // the last term covers flushed denormal operands
+            const float e2 = 2.f * (1.0625f * (g * (M + xnorm * sqM) + (SPLIT ? 1.15e-5f * xnorm * sqM : 0.f)) +
+                                    7.6e-37f * (float)d * (sqM + xnorm) + 1e-30f);
             // near tie: the exact winner is not certain
             const bool flagged = !((w1 - s2) > e2);
             // only the top two can win: every other score is more than 2e below
@@ -648,6 +768,27 @@ __global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, in
     }
 }
 
+// Split scoring operands: hi = bf16(c) (round to nearest even), lo =
+// bf16(c - hi); rows padded with zeros to dpad (a multiple of 8 elements).
+__global__ __launch_bounds__(256) void k_split_bf16(const float *__restrict__ C, int K, int d, int dpad,
+                                                    __bf16 *__restrict__ hi, __bf16 *__restrict__ lo) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= (int64_t)K * dpad) return;
+    const int64_t k = q / dpad;
+    const int j = (int)(q - k * dpad);
+    const float c = j < d ? C[k * d + j] : 0.f;
+    const __bf16 h = (__bf16)c;
+    hi[q] = h;
+    lo[q] = (__bf16)(c - (float)h);
+}
+
+hipError_t launch_split_bf16(const float *C, int K, int d, const SplitC &sc, hipStream_t s) {
+    const int dpad = (int)cdiv(d, 8) * 8;
+    const int64_t total = (int64_t)K * dpad;
+    hipLaunchKernelGGL(k_split_bf16, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, C, K, d, dpad, sc.hi, sc.lo);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 AssignShape assign_shape(int d) {
     if (d <= 16) return {16, 1, 1, 1};
@@ -686,35 +827,45 @@ hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, i
     return hipGetLastError();
 }
 
-template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool COLLECT>
+template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool COLLECT, bool SPLIT>
 static hipError_t launch_fa(const FlashArgs &A, hipStream_t s) {
     constexpr int BM = WAVES * PB * 32;
     int64_t nb = COLLECT ? cdiv(A.cap_slots, BM) : cdiv(A.N, BM);
     if (COLLECT && nb > 512) nb = 512;  // persistent: the workgroups stride over the listed slots
     if (A.d % 4 == 0)
-        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, true, COLLECT>), dim3((unsigned)nb),
+        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, true, COLLECT, SPLIT>), dim3((unsigned)nb),
                            dim3(WAVES * 64), 0, s, A);
     else
-        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, false, COLLECT>), dim3((unsigned)nb),
+        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, false, COLLECT, SPLIT>), dim3((unsigned)nb),
                            dim3(WAVES * 64), 0, s, A);
     return hipGetLastError();
 }
 
-template <bool COLLECT>
+template <bool COLLECT, bool SPLIT>
 static hipError_t launch_fa_shape(const FlashArgs &A, hipStream_t s) {
     const AssignShape sh = assign_shape(A.d);
-    if (sh.nch > 1) return launch_fa<64, 1, 2, 8, 2, false, COLLECT>(A, s);
+    if (sh.nch > 1) return launch_fa<64, 1, 2, 8, 2, false, COLLECT, SPLIT>(A, s);
     switch (sh.DP) {
-    case 16: return launch_fa<16, 1, 1, 8, 4, true, COLLECT>(A, s);
-    case 32: return launch_fa<32, 1, 1, 8, 4, true, COLLECT>(A, s);
-    case 64: return launch_fa<64, 1, 1, 8, 4, true, COLLECT>(A, s);
-    default: return launch_fa<128, 2, 1, 4, 2, true, COLLECT>(A, s);
+    case 16: return launch_fa<16, 1, 1, 8, 4, true, COLLECT, SPLIT>(A, s);
+    case 32: return launch_fa<32, 1, 1, 8, 4, true, COLLECT, SPLIT>(A, s);
+    case 64: return launch_fa<64, 1, 1, 8, 4, true, COLLECT, SPLIT>(A, s);
+    default:
+        // split scoring holds hi and lo halves: one 32-point block per wave
+        if constexpr (SPLIT)
+            return launch_fa<128, 1, 1, 8, 2, true, COLLECT, SPLIT>(A, s);
+        else
+            return launch_fa<128, 2, 1, 4, 2, true, COLLECT, SPLIT>(A, s);
     }
+}
+
+template <bool COLLECT>
+static hipError_t launch_fa_score(const FlashArgs &A, bool split, hipStream_t s) {
+    return split ? launch_fa_shape<COLLECT, true>(A, s) : launch_fa_shape<COLLECT, false>(A, s);
 }
 
 static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                             const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                            const NearTies &nt) {
+                            const NearTies &nt, const SplitC &sc) {
     const AssignShape sh = assign_shape(d);
     FlashArgs A;
     A.X = X;
@@ -736,6 +887,9 @@ static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, co
     A.cand = nt.cand;
     A.ccount = nt.ccount;
     A.cap_slots = near_tie_cap(N);
+    A.Ch = sc.hi;
+    A.Cl = sc.lo;
+    A.dpad = (int)cdiv(d, 8) * 8;
     return A;
 }
 
@@ -748,14 +902,15 @@ int64_t near_tie_cap(int64_t N) {
 
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                                const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                               const NearTies &nt, hipStream_t s) {
+                               const NearTies &nt, const SplitC &sc, hipStream_t s) {
     if (N <= 0) return hipSuccess;
-    return launch_fa_shape<false>(flash_args(X, N, d, C, ncn, K, scal, xnorm64, a_out, d1_out, nt), s);
+    return launch_fa_score<false>(flash_args(X, N, d, C, ncn, K, scal, xnorm64, a_out, d1_out, nt, sc),
+                                  sc.hi != nullptr, s);
 }
 
 hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma, const float *C32,
                           const double *C64, const float *ncn, int K, const float *scal, const double *xnorm64,
-                          const NearTies &nt, int32_t *a_out, float *d1_out, hipStream_t s) {
+                          const NearTies &nt, const SplitC &sc, int32_t *a_out, float *d1_out, hipStream_t s) {
     if (N <= 0) return hipSuccess;
     hipError_t e;
     // 1. near ties between two known centroids
@@ -771,8 +926,8 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 2. the full list: collect every centroid within each point's window
-    if ((e = launch_fa_shape<true>(flash_args(X, N, d, C_mfma, ncn, K, scal, xnorm64, a_out, d1_out, nt), s)) !=
-        hipSuccess)
+    if ((e = launch_fa_score<true>(flash_args(X, N, d, C_mfma, ncn, K, scal, xnorm64, a_out, d1_out, nt, sc),
+                                   sc.hi != nullptr, s)) != hipSuccess)
         return e;
     // 3. fp64 over the collected candidates; overflows go to the last list
     {

@@ -80,15 +80,22 @@ struct NearTies {
 };
 constexpr int kCandPerSlot = 16;
 int64_t near_tie_cap(int64_t N);
+// Split-bf16 scoring operands (hi, lo: K rows of d rounded up to 8 bf16);
+// both null selects fp32 scoring.
+struct SplitC {
+    __bf16 *hi;
+    __bf16 *lo;
+};
+hipError_t launch_split_bf16(const float *C, int K, int d, const SplitC &sc, hipStream_t s);
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                                const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                               const NearTies &nt, hipStream_t s);
+                               const NearTies &nt, const SplitC &sc, hipStream_t s);
 // Settles every listed near tie exactly (fp64 direct-difference distances).
 // C_mfma is the centroid array the MFMA pass used (normalised for cosine); C32
 // (L2) or C64 (cosine, normalised in fp64) is the one the distances use.
 hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma, const float *C32,
                           const double *C64, const float *ncn, int K, const float *scal, const double *xnorm64,
-                          const NearTies &nt, int32_t *a_out, float *d1_out, hipStream_t s);
+                          const NearTies &nt, const SplitC &sc, int32_t *a_out, float *d1_out, hipStream_t s);
 
 // Radix sort of (key = assign[i], value = i), stable, atomic-free.  Writes the
 // sorted keys and the permutation.  tmp* are N-sized scratch arrays.

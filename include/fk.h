@@ -78,6 +78,22 @@ typedef enum {
 } fk_metric;
 
 /*
+ * How FlashAssign scores x.c before near ties are settled in fp64.  Both give
+ * the same (exact) assignment; they differ in speed and in how many points
+ * fall inside the error window and go to the fp64 paths.
+ *   FK_SCORE_FP32: fp32 MFMA (v_mfma_f32_32x32x2_f32) on the fp32 inputs.
+ *   FK_SCORE_SPLIT_BF16: each fp32 value v is split into bf16 parts
+ *     hi = bf16(v), lo = bf16(v - hi); x.c is taken as hi.hi + hi.lo + lo.hi
+ *     on bf16 MFMA (v_mfma_f32_32x32x16_bf16) with fp32 accumulation; its
+ *     error bound is about 3.6 times the fp32 one (three products per
+ *     dimension, plus the dropped lo.lo and remainders).
+ */
+typedef enum {
+    FK_SCORE_FP32 = 0,
+    FK_SCORE_SPLIT_BF16 = 1
+} fk_score;
+
+/*
  * Bytes of workspace needed by a call with these sizes.  chunk_rows = 0 sizes
  * the in-core calls (fk_assign, fk_sort_inverse, fk_update, fk_lloyd_iter)
  * for N rows; chunk_rows > 0 sizes fk_lloyd_iter_stream with that chunk
@@ -89,15 +105,16 @@ size_t fk_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric, int64_
 /*
  * FlashAssign: assign[i] = the nearest centroid of point i (lowest index on
  * ties), and, when min_dist is not NULL, min_dist[i] = its squared distance
- * (fp32; the fp64 value rounded for rescored points).  X, C, assign and
- * min_dist are device pointers.  The N x K distance matrix is never stored:
+ * (fp32; the fp64 value rounded for rescored points).  score is an
+ * fk_score.  X, C, assign and min_dist are device pointers.  The N x K distance matrix is never stored:
  * each workgroup keeps a block of points in registers, streams centroid
  * tiles through LDS into fp32 MFMA and keeps a running top-3 per point in
  * registers (FlashAssign section of the Flash-KMeans article).  Near ties
  * are settled in fp64 (see Exactness above).
  */
 fk_status fk_assign(const float *X, int64_t N, int32_t d, const float *C, int32_t K, int32_t metric,
-                    int32_t *assign, float *min_dist, void *workspace, size_t workspace_bytes, void *stream);
+                    int32_t score, int32_t *assign, float *min_dist, void *workspace, size_t workspace_bytes,
+                    void *stream);
 
 /*
  * The inverse index of the Sort-Inverse Update: perm[0..N) lists the point
@@ -125,13 +142,14 @@ fk_status fk_update(const float *X, int64_t N, int32_t d, const int32_t *assign,
                     size_t workspace_bytes, void *stream);
 
 /*
- * One full Lloyd iteration: fk_assign then fk_update, from C_in to C_out.
+ * One full Lloyd iteration: fk_assign (with `score`) then fk_update, from C_in
+ * to C_out.
  * assign and counts receive the assignment under C_in and the cluster sizes;
  * min_dist may be NULL.  C_out must not overlap C_in.  Device pointers.
  */
 fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in, int32_t K, int32_t metric,
-                        int32_t *assign, float *min_dist, float *C_out, int32_t *counts, void *workspace,
-                        size_t workspace_bytes, void *stream);
+                        int32_t score, int32_t *assign, float *min_dist, float *C_out, int32_t *counts,
+                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Out-of-core Lloyd iteration: X_host is PINNED host memory (hipHostMalloc
@@ -147,8 +165,9 @@ fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in,
  * pinned.
  */
 fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const float *C_in, int32_t K,
-                               int32_t metric, int64_t chunk_rows, int32_t *assign_host, float *C_out,
-                               int32_t *counts, void *workspace, size_t workspace_bytes, void *stream);
+                               int32_t metric, int32_t score, int64_t chunk_rows, int32_t *assign_host,
+                               float *C_out, int32_t *counts, void *workspace, size_t workspace_bytes,
+                               void *stream);
 
 /* Static name of a status code. */
 const char *fk_status_str(int32_t status);

@@ -10,7 +10,8 @@ Tolerances
   * empty centroids: bitwise equal to the centroid that was passed in;
   * min_dist (fp32 output): |d_gpu - D1| <= 3 (d+4) 2^-24 (||x||^2 + M +
     2 ||x|| sqrt(M)), M = max ||c||^2: the fp32 rounding bound of the expanded
-    distance, three times over.
+    distance, three times over; with split-bf16 scoring (3d+4) replaces
+    (d+4) and the dropped bf16 remainders add 3 * 2.3e-5 ||x|| sqrt(M).
 """
 import sys
 
@@ -46,7 +47,7 @@ def centroid_rel_err(C_gpu, C_ref, counts):
     return float(err.max())
 
 
-def check_min_dist(d1_gpu, D1, X, C, metric="l2"):
+def check_min_dist(d1_gpu, D1, X, C, metric="l2", score="fp32"):
     X = np.asarray(X, np.float64)
     C = np.asarray(C, np.float64)
     if metric == "cosine":
@@ -59,7 +60,10 @@ def check_min_dist(d1_gpu, D1, X, C, metric="l2"):
     d = X.shape[1]
     xn = (X * X).sum(1)
     M = (C * C).sum(1).max()
-    tol = 3 * (d + 4) * 2.0 ** -24 * (xn + M + 2 * np.sqrt(xn * M)) + 1e-30
+    n = 3 * d + 4 if score == "split_bf16" else d + 4
+    tol = 3 * n * 2.0 ** -24 * (xn + M + 2 * np.sqrt(xn * M)) + 1e-30
+    if score == "split_bf16":
+        tol += 3 * 2.3e-5 * np.sqrt(xn * M)
     err = np.abs(np.asarray(d1_gpu, np.float64) - D1)
     bad = err > tol
     assert not bad.any(), f"min_dist off at {np.nonzero(bad)[0][:5]}: err {err[bad][:5]} tol {tol[bad][:5]}"

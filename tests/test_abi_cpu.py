@@ -58,8 +58,8 @@ def _fake(addr):
     return P(addr)
 
 
-def _call_assign(lib, N=100, d=8, K=4, metric=0, X=0x10000, C=0x20000, a=0x30000, ws=0x100000, wsn=1 << 30):
-    return lib.fk_assign(_fake(X) if X else None, N, d, _fake(C) if C else None, K, metric,
+def _call_assign(lib, N=100, d=8, K=4, metric=0, X=0x10000, C=0x20000, a=0x30000, ws=0x100000, wsn=1 << 30, score=0):
+    return lib.fk_assign(_fake(X) if X else None, N, d, _fake(C) if C else None, K, metric, score,
                          _fake(a) if a else None, None, _fake(ws) if ws else None, wsn, None)
 
 
@@ -72,6 +72,8 @@ def test_validation_happens_before_any_device_call(lib):
     assert _call_assign(lib, metric=2) == UNSUPPORTED
     assert b"inner-product" in lib.fk_last_error()
     assert _call_assign(lib, metric=7) == INVALID
+    assert _call_assign(lib, score=2) == INVALID
+    assert b"score" in lib.fk_last_error()
     assert _call_assign(lib, X=0) == INVALID
     assert _call_assign(lib, C=0) == INVALID
     assert _call_assign(lib, a=0) == INVALID
@@ -88,16 +90,16 @@ def test_update_and_iter_reject_aliasing(lib):
     st = lib.fk_update(_fake(0x10000), 10, d, _fake(0x30000), K, 0, _fake(C), _fake(C + 64), _fake(0x40000),
                        _fake(0x1000000), 1 << 30, None)
     assert st == INVALID and b"overlaps" in lib.fk_last_error()
-    st = lib.fk_lloyd_iter(_fake(0x10000), 10, d, _fake(C), K, 0, _fake(0x30000), None, _fake(C), _fake(0x40000),
+    st = lib.fk_lloyd_iter(_fake(0x10000), 10, d, _fake(C), K, 0, 0, _fake(0x30000), None, _fake(C), _fake(0x40000),
                            _fake(0x1000000), 1 << 30, None)
     assert st == INVALID
-    st = lib.fk_lloyd_iter(_fake(0x10000), 10, d, _fake(C), K, 0, _fake(0x30000), None, None, _fake(0x40000),
+    st = lib.fk_lloyd_iter(_fake(0x10000), 10, d, _fake(C), K, 0, 0, _fake(0x30000), None, None, _fake(0x40000),
                            _fake(0x1000000), 1 << 30, None)
     assert st == INVALID
 
 
 def test_stream_rejects_bad_chunks(lib):
-    st = lib.fk_lloyd_iter_stream(_fake(0x10000), 100, 8, _fake(0x20000), 4, 0, 0, None, _fake(0x30000),
+    st = lib.fk_lloyd_iter_stream(_fake(0x10000), 100, 8, _fake(0x20000), 4, 0, 0, 0, None, _fake(0x30000),
                                   _fake(0x40000), _fake(0x1000000), 1 << 30, None)
     assert st == INVALID and b"chunk_rows" in lib.fk_last_error()
 

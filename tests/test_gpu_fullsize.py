@@ -27,9 +27,10 @@ def _sample(N, n, seed):
     return np.sort(rng.choice(N, size=min(n, N), replace=False))
 
 
+@pytest.mark.parametrize("score", ["fp32", "split_bf16"])
 @pytest.mark.parametrize("name,nsample", [("gmm_1m_d128_k1024", 4096), ("ivf_1m_d768_k4096", 1024),
                                           ("zipf_16m_d128_k32768", 2048)])
-def test_full_size_iteration(gpu_lib, name, nsample):
+def test_full_size_iteration(gpu_lib, name, nsample, score):
     fk = gpu_lib
     w = synth.WORKLOADS[name]
     log(f"full size {name}: generating N={w.N}")
@@ -38,10 +39,10 @@ def test_full_size_iteration(gpu_lib, name, nsample):
     Xd, Cd = dev(X), dev(C)
     # one warm-up iteration moves the centroids off the sampled points, as in
     # the timed steps of the benchmark
-    _, C1d, _, _ = fk.fk_lloyd_iter(Xd, Cd)
+    _, C1d, _, _ = fk.fk_lloyd_iter(Xd, Cd, score=score)
     C1 = host(C1d).copy()
     log(f"full size {name}: second iteration")
-    a, C2d, counts, md = fk.fk_lloyd_iter(Xd, C1d, with_min_dist=True)
+    a, C2d, counts, md = fk.fk_lloyd_iter(Xd, C1d, with_min_dist=True, score=score)
     a = host(a)
     counts = host(counts)
     C2 = host(C2d)
@@ -52,7 +53,7 @@ def test_full_size_iteration(gpu_lib, name, nsample):
     log(f"full size {name}: oracle on {len(idx)} sampled points")
     a_ref, D1, D2 = oracle.assign(X[idx], C1)
     np.testing.assert_array_equal(a[idx], a_ref)
-    check_min_dist(md[idx], D1, X[idx], C1)
+    check_min_dist(md[idx], D1, X[idx], C1, score=score)
     log(f"full size {name}: oracle update on the GPU assignment")
     C_ref, n_ref = oracle.update(X, a, C1)
     np.testing.assert_array_equal(counts, n_ref)
@@ -62,7 +63,8 @@ def test_full_size_iteration(gpu_lib, name, nsample):
     assert np.array_equal(C2[empty].view(np.uint32), C1[empty].view(np.uint32))
 
 
-def test_out_of_core_scaled(gpu_lib):
+@pytest.mark.parametrize("score", ["fp32", "split_bf16"])
+def test_out_of_core_scaled(gpu_lib, score):
     fk = gpu_lib
     w0 = synth.WORKLOADS["ooc_1b_d128_k32768"]
     N = (1 << 26) + (1 << 25) + 777          # two chunks of 2^26 rows, the second ragged
@@ -76,10 +78,10 @@ def test_out_of_core_scaled(gpu_lib):
     Cd = dev(C)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    C1d, cnt = fk.fk_lloyd_iter_stream(Xh, Cd, w.chunk_rows, assign_host=ah)
+    C1d, cnt = fk.fk_lloyd_iter_stream(Xh, Cd, w.chunk_rows, assign_host=ah, score=score)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
-    log(f"out of core: one iteration in {dt:.2f} s including PCIe ({N * w.d * 4 / dt / 1e9:.1f} GB/s of X)")
+    log(f"out of core ({score}): one iteration in {dt:.2f} s including PCIe ({N * w.d * 4 / dt / 1e9:.1f} GB/s of X)")
     a = ah.numpy()
     counts = host(cnt)
     assert counts.sum() == N

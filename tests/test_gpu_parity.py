@@ -18,30 +18,35 @@ SHAPES = [
 ]
 
 
+SCORES = ["fp32", "split_bf16"]
+
+
+@pytest.mark.parametrize("score", SCORES)
 @pytest.mark.parametrize("N,d,K", SHAPES)
 @pytest.mark.parametrize("kind", ["gauss", "dup", "dup3", "dup40", "grid", "far", "zero"])
-def test_assign_matches_oracle(gpu_lib, N, d, K, kind):
+def test_assign_matches_oracle(gpu_lib, N, d, K, kind, score):
     fk = gpu_lib
-    log(f"assign N={N} d={d} K={K} kind={kind}")
+    log(f"assign N={N} d={d} K={K} kind={kind} score={score}")
     X, C = synth.adversarial(3, N, d, K, kind)
     a_ref, D1, D2 = oracle.assign(X, C)
-    a, md = fk.fk_assign(dev(X), dev(C), with_min_dist=True)
+    a, md = fk.fk_assign(dev(X), dev(C), with_min_dist=True, score=score)
     a = host(a)
     np.testing.assert_array_equal(a, a_ref)
-    check_min_dist(host(md), D1, X, C)
+    check_min_dist(host(md), D1, X, C, score=score)
 
 
+@pytest.mark.parametrize("score", SCORES)
 @pytest.mark.parametrize("N,d,K", [(1000, 16, 64), (3001, 128, 257), (400, 768, 100), (999, 7, 5)])
 @pytest.mark.parametrize("kind", ["gauss", "zero", "dup"])
-def test_assign_cosine_matches_oracle(gpu_lib, N, d, K, kind):
+def test_assign_cosine_matches_oracle(gpu_lib, N, d, K, kind, score):
     fk = gpu_lib
-    log(f"cosine assign N={N} d={d} K={K} kind={kind}")
+    log(f"cosine assign N={N} d={d} K={K} kind={kind} score={score}")
     X, C = synth.adversarial(4, N, d, K, kind)
     X[::3] *= np.float32(7.0)
     a_ref, D1, _ = oracle.assign(X, C, "cosine")
-    a, md = fk.fk_assign(dev(X), dev(C), metric="cosine", with_min_dist=True)
+    a, md = fk.fk_assign(dev(X), dev(C), metric="cosine", with_min_dist=True, score=score)
     np.testing.assert_array_equal(host(a), a_ref)
-    check_min_dist(host(md), D1, X, C, "cosine")
+    check_min_dist(host(md), D1, X, C, "cosine", score=score)
 
 
 @pytest.mark.parametrize("N,d,K", [(1, 4, 1), (1000, 16, 64), (5000, 128, 1024), (4096 * 3 + 5, 8, 300),
@@ -61,8 +66,9 @@ def test_update_matches_oracle(gpu_lib, N, d, K, metric):
     check_update(X, a, C_prev, host(C_out), host(counts), metric)
 
 
+@pytest.mark.parametrize("score", SCORES)
 @pytest.mark.parametrize("kind,path", [("dup", "paired"), ("dup3", "windowed"), ("dup40", "rechecked")])
-def test_each_near_tie_path_is_taken(gpu_lib, kind, path):
+def test_each_near_tie_path_is_taken(gpu_lib, kind, path, score):
     """Exact ties between 2, 3 and 40 copies of a centroid send points down
     each of the three fp64 paths (two-way compare, window compare, all K);
     the result must match the oracle on every one."""
@@ -70,7 +76,7 @@ def test_each_near_tie_path_is_taken(gpu_lib, kind, path):
     X, C = synth.adversarial(6, 3000, 24, 200, kind)
     a_ref, _, _ = oracle.assign(X, C)
     fk.fk_profile_enable(True)
-    a, _ = fk.fk_assign(dev(X), dev(C))
+    a, _ = fk.fk_assign(dev(X), dev(C), score=score)
     prof = fk.fk_profile_read()
     fk.fk_profile_enable(False)
     np.testing.assert_array_equal(host(a), a_ref)
@@ -117,9 +123,10 @@ def test_sort_inverse_matches_stable_argsort(gpu_lib, N, K):
     np.testing.assert_array_equal(offsets, expect)
 
 
+@pytest.mark.parametrize("score", SCORES)
 @pytest.mark.parametrize("name,N,iters", [("tiny_d16_k64", 65536, 3), ("gmm_1m_d128_k1024", 60000, 3),
                                           ("ivf_1m_d768_k4096", 12000, 2), ("zipf_16m_d128_k32768", 33000, 2)])
-def test_lloyd_iterations_step_level(gpu_lib, name, N, iters):
+def test_lloyd_iterations_step_level(gpu_lib, name, N, iters, score):
     """Step-level protocol: at every iteration the oracle is given the GPU's
     own centroids; assignments and counts must match exactly and centroids to
     1e-6 relative, and the objective must not increase."""
@@ -132,7 +139,7 @@ def test_lloyd_iterations_step_level(gpu_lib, name, N, iters):
     Cd = dev(C)
     Js = []
     for t in range(iters):
-        a, C1, counts, md = fk.fk_lloyd_iter(Xd, Cd, with_min_dist=True)
+        a, C1, counts, md = fk.fk_lloyd_iter(Xd, Cd, with_min_dist=True, score=score)
         ref = oracle.lloyd_iter(X, C)
         a_h = host(a)
         np.testing.assert_array_equal(a_h, ref["a"])
@@ -147,14 +154,28 @@ def test_lloyd_iterations_step_level(gpu_lib, name, N, iters):
         assert j1 <= j0 * (1 + 1e-6)
 
 
-def test_determinism_bitwise(gpu_lib):
+@pytest.mark.parametrize("score", SCORES)
+def test_determinism_bitwise(gpu_lib, score):
     fk = gpu_lib
     w = synth.WORKLOADS["zipf_16m_d128_k32768"].scaled(300000)
     X = synth.rows(w)
     C = synth.initial_centroids(w, X)
     Xd, Cd = dev(X), dev(C)
-    r1 = [host(t) for t in fk.fk_lloyd_iter(Xd, Cd, with_min_dist=True)]
-    r2 = [host(t) for t in fk.fk_lloyd_iter(Xd, Cd, with_min_dist=True)]
+    r1 = [host(t) for t in fk.fk_lloyd_iter(Xd, Cd, with_min_dist=True, score=score)]
+    r2 = [host(t) for t in fk.fk_lloyd_iter(Xd, Cd, with_min_dist=True, score=score)]
+    for u, v in zip(r1, r2):
+        assert u.tobytes() == v.tobytes()
+
+
+def test_scores_agree(gpu_lib):
+    """Both scoring modes give the same exact assignment, counts and centroids."""
+    fk = gpu_lib
+    w = synth.WORKLOADS["gmm_1m_d128_k1024"].scaled(200000)
+    X = synth.rows(w)
+    C = synth.initial_centroids(w, X)
+    Xd, Cd = dev(X), dev(C)
+    r1 = [host(t) for t in fk.fk_lloyd_iter(Xd, Cd, score="fp32")[:3]]
+    r2 = [host(t) for t in fk.fk_lloyd_iter(Xd, Cd, score="split_bf16")[:3]]
     for u, v in zip(r1, r2):
         assert u.tobytes() == v.tobytes()
 
@@ -177,6 +198,9 @@ def test_error_paths_on_device(gpu_lib):
     with pytest.raises(fk.FkError) as e:
         fk.fk_assign(X, C, metric="inner_product")
     assert e.value.status == 2
+    with pytest.raises(fk.FkError) as e:
+        fk.fk_assign(X, C, score=5)
+    assert e.value.status == 1
     small = torch.empty(1024, dtype=torch.uint8, device="cuda:0")
     with pytest.raises(fk.FkError) as e:
         fk.fk_assign(X, C, workspace=small)
@@ -188,7 +212,7 @@ def test_error_paths_on_device(gpu_lib):
     base = ws.data_ptr() + (-ws.data_ptr()) % 256
     out = torch.empty((4, 8), device="cuda:0")
     cnt = torch.empty(4, dtype=torch.int32, device="cuda:0")
-    st = lib.fk_lloyd_iter_stream(ctypes.c_void_p(host_x.data_ptr()), 100, 8, ctypes.c_void_p(C.data_ptr()), 4, 0, 50,
+    st = lib.fk_lloyd_iter_stream(ctypes.c_void_p(host_x.data_ptr()), 100, 8, ctypes.c_void_p(C.data_ptr()), 4, 0, 0, 50,
                                   None, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(cnt.data_ptr()),
                                   ctypes.c_void_p(base), ws.numel() - 256, None)
     assert st == 1 and b"pinned" in lib.fk_last_error()

@@ -17,19 +17,20 @@ def _pinned(a):
     return t
 
 
+@pytest.mark.parametrize("score", ["fp32", "split_bf16"])
 @pytest.mark.parametrize("metric", ["l2", "cosine"])
 @pytest.mark.parametrize("chunk", [100000, 65537, 300000, 300005, 4096])
-def test_stream_equals_in_core(gpu_lib, chunk, metric):
+def test_stream_equals_in_core(gpu_lib, chunk, metric, score):
     fk = gpu_lib
     w = synth.WORKLOADS["ooc_1b_d128_k32768"].scaled(300000)
     K = 2048
     log(f"stream chunk={chunk} {metric}")
     X = synth.rows(w)
     C = X[synth.init_indices(w)[:K]].copy()
-    a_ic, C_ic, n_ic, _ = fk.fk_lloyd_iter(dev(X), dev(C), metric=metric)
+    a_ic, C_ic, n_ic, _ = fk.fk_lloyd_iter(dev(X), dev(C), metric=metric, score=score)
     Xh = _pinned(X)
     ah = torch.empty(w.N, dtype=torch.int32, pin_memory=True)
-    C_s, n_s = fk.fk_lloyd_iter_stream(Xh, dev(C), chunk, metric=metric, assign_host=ah)
+    C_s, n_s = fk.fk_lloyd_iter_stream(Xh, dev(C), chunk, metric=metric, assign_host=ah, score=score)
     torch.cuda.synchronize()
     np.testing.assert_array_equal(ah.numpy(), host(a_ic))
     np.testing.assert_array_equal(host(n_s), host(n_ic))
