@@ -308,11 +308,11 @@ fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int3
     if (st != FK_OK) return st;
     PhaseScope ph(FK_PH_REDUCE, c.s);
     const double *xn = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.xnorm64) : nullptr;
-    FK_TRY(launch_seg_reduce(X, rows, c.d, at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.perm), xn,
+    FK_TRY(launch_seg_reduce(X, rows, c.d, c.K, at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.perm), xn,
                              at<double>(c.ws, c.L.sums), at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast),
                              c.s),
            "segmented reduction");
-    FK_TRY(launch_seg_fixup(at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.offsets), rows, c.d,
+    FK_TRY(launch_seg_fixup(at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.offsets), rows, c.d, c.K,
                             at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast), at<double>(c.ws, c.L.sums),
                             c.s),
            "segment fix-up");

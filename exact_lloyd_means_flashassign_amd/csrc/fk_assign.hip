@@ -828,7 +828,15 @@ hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, i
 }
 
 template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool COLLECT, bool SPLIT>
-static hipError_t launch_fa(const FlashArgs &A, hipStream_t s) {
+static hipError_t launch_fa(const FlashArgs &A0, hipStream_t s) {
+    // the tile count and chunk count follow this instantiation's geometry:
+    // the -||c||^2/2 array is padded to kCentroidPad, a multiple of every
+    // tile height, so the tiles never read past it
+    static_assert(kCentroidPad % (CB * 32) == 0, "tile height must divide the centroid padding");
+    FlashArgs A = A0;
+    A.ntiles = (int)cdiv(A.K, CB * 32);
+    A.nch = RES ? 1 : (int)cdiv(A.d, DP);
+    if (RES && A.d > DP) return hipErrorInvalidValue;
     constexpr int BM = WAVES * PB * 32;
     int64_t nb = COLLECT ? cdiv(A.cap_slots, BM) : cdiv(A.N, BM);
     if (COLLECT && nb > 512) nb = 512;  // persistent: the workgroups stride over the listed slots

@@ -249,8 +249,10 @@ __global__ __launch_bounds__(256) void k_offsets(const int32_t *__restrict__ ks,
                                                  int32_t *__restrict__ offsets) {
     const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (r > N) return;
-    const int lo = (r == 0) ? 0 : ks[r - 1] + 1;
-    const int hi = (r == N) ? K : ks[r];
+    // keys are documented to lie in [0, K); the clamps only keep a bad key
+    // from writing outside offsets[0..K]
+    const int lo = max((r == 0) ? 0 : ks[r - 1] + 1, 0);
+    const int hi = min((r == N) ? K : ks[r], K);
     for (int k = lo; k <= hi; ++k) offsets[k] = (int32_t)r;
 }
 

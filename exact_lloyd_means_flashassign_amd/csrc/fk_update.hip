@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t *__restrict__ p, int
 // blockIdx.y * 64*E*NV.  U rows are loaded before they are accumulated so that
 // U row reads per lane are in flight at once.
 template <int NV, int E, int U>
-__global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X, int64_t N, int d, int srows,
+__global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X, int64_t N, int d, int K, int srows,
                                                     const int32_t *__restrict__ ks, const int32_t *__restrict__ perm,
                                                     const double *__restrict__ xnorm64, double *__restrict__ sums,
                                                     double *__restrict__ pfirst, double *__restrict__ plast) {
@@ -65,6 +65,15 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
     int cur = first_k;
 
     auto flush = [&](int k) {
+        // keys are documented to lie in [0, K); a bad key is dropped rather
+        // than written outside the sums
+        if ((unsigned)k >= (unsigned)K) {
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[v][e] = 0.0;
+            return;
+        }
         double *dst;
         bool add;
         if (k == first_k && started_before) {
@@ -156,7 +165,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
 constexpr int kFixWaves = 8;
 __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__restrict__ ks,
                                                              const int32_t *__restrict__ offsets, int64_t N, int d,
-                                                             int srows,
+                                                             int K, int srows,
                                                              const double *__restrict__ pfirst,
                                                              const double *__restrict__ plast,
                                                              double *__restrict__ sums) {
@@ -166,7 +175,7 @@ __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__r
     const int64_t rb = (b + 1) * srows;
     if (rb >= N) return;
     const int k = ks[rb];
-    if (ks[rb - 1] != k) return;
+    if (ks[rb - 1] != k || (unsigned)k >= (unsigned)K) return;
     const int64_t o0 = offsets[k], o1 = offsets[k + 1];
     const int64_t sa = o0 / srows;
     if (sa != b) return;
@@ -231,45 +240,45 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
 }
 
 template <int NV, int E>
-static hipError_t seg_launch(const float *X, int64_t N, int d, const int32_t *ks, const int32_t *perm,
+static hipError_t seg_launch(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
     constexpr int U = NV * E <= 2 ? 16 : (NV * E <= 8 ? 8 : 4);
     const int srows = seg_rows(N);
     const int64_t nseg = cdiv(N, srows);
     const unsigned gy = (unsigned)cdiv(d, 64 * E * NV);
     hipLaunchKernelGGL((k_seg_reduce<NV, E, U>), dim3((unsigned)cdiv(nseg, kSegWaves), gy), dim3(kSegWaves * 64), 0,
-                       s, X, N, d, srows, ks, perm, xnorm64, sums, pfirst, plast);
+                       s, X, N, d, K, srows, ks, perm, xnorm64, sums, pfirst, plast);
     return hipGetLastError();
 }
 
 template <int E>
-static hipError_t seg_launch_e(const float *X, int64_t N, int d, const int32_t *ks, const int32_t *perm,
+static hipError_t seg_launch_e(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
                                const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
     const int need = (int)cdiv(d, 64 * E);
-    if (need <= 1) return seg_launch<1, E>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-    if (need <= 2) return seg_launch<2, E>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-    if (need <= 3) return seg_launch<3, E>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-    return seg_launch<4, E>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (need <= 1) return seg_launch<1, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (need <= 2) return seg_launch<2, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (need <= 3) return seg_launch<3, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
+    return seg_launch<4, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
 }
 
 // Row loads of E floats per lane: float4 when a row spans at least 256
 // floats, float2 from 128, scalar otherwise (or when d is not a multiple);
 // column blocks of up to 4 loads per lane, more blocks on blockIdx.y.
-hipError_t launch_seg_reduce(const float *X, int64_t N, int d, const int32_t *ks, const int32_t *perm,
+hipError_t launch_seg_reduce(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
     if (N <= 0) return hipSuccess;
-    if (d % 4 == 0 && d >= 256) return seg_launch_e<4>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-    if (d % 2 == 0 && d >= 128) return seg_launch_e<2>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
-    return seg_launch_e<1>(X, N, d, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (d % 4 == 0 && d >= 256) return seg_launch_e<4>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (d % 2 == 0 && d >= 128) return seg_launch_e<2>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
+    return seg_launch_e<1>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
 }
 
-hipError_t launch_seg_fixup(const int32_t *ks, const int32_t *offsets, int64_t N, int d, const double *pfirst,
+hipError_t launch_seg_fixup(const int32_t *ks, const int32_t *offsets, int64_t N, int d, int K, const double *pfirst,
                             const double *plast, double *sums, hipStream_t s) {
     const int srows = seg_rows(N);
     const int64_t nseg = cdiv(N, srows);
     if (nseg <= 1) return hipSuccess;
-    hipLaunchKernelGGL(k_seg_fixup, dim3((unsigned)(nseg - 1)), dim3(kFixWaves * 64), 0, s, ks, offsets, N, d, srows,
-                       pfirst, plast, sums);
+    hipLaunchKernelGGL(k_seg_fixup, dim3((unsigned)(nseg - 1)), dim3(kFixWaves * 64), 0, s, ks, offsets, N, d, K,
+                       srows, pfirst, plast, sums);
     return hipGetLastError();
 }
 
