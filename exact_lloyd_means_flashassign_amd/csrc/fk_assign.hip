@@ -590,6 +590,66 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     }
 }
 
+// Four consecutive elements of a centroid row as fp64.
+__device__ __forceinline__ void load4_64(const float *c, double (&o)[4]) {
+    const float4 v = *reinterpret_cast<const float4 *>(c);
+    o[0] = (double)v.x;
+    o[1] = (double)v.y;
+    o[2] = (double)v.z;
+    o[3] = (double)v.w;
+}
+__device__ __forceinline__ void load4_64(const double *c, double (&o)[4]) {
+    const double2 a = *reinterpret_cast<const double2 *>(c);
+    const double2 b = *reinterpret_cast<const double2 *>(c + 2);
+    o[0] = a.x;
+    o[1] = a.y;
+    o[2] = b.x;
+    o[3] = b.y;
+}
+
+// The fp64 direct-difference distances of one point to NC centroids:
+// D[m] = sum_j (x_j - c_mj)^2 in increasing j, with no fused multiply-add;
+// for cosine x_j is first divided by the row norm nx (as the definition
+// does).  Rows are read four elements at a time when d is a multiple of 4
+// (X, C and the fp64 normalised centroids are then 16-byte aligned).
+template <typename CT, int NC>
+__device__ __forceinline__ void sqdist64(const float *__restrict__ x, const CT *const (&c)[NC], int d, double nx,
+                                         bool cosine, double (&D)[NC]) {
+#pragma clang fp contract(off)
+#pragma unroll
+    for (int m = 0; m < NC; ++m) D[m] = 0.0;
+    int j = 0;
+    if ((d & 3) == 0) {
+        for (; j < d; j += 4) {
+            const float4 xv4 = *reinterpret_cast<const float4 *>(x + j);
+            double xv[4] = {(double)xv4.x, (double)xv4.y, (double)xv4.z, (double)xv4.w};
+            if (cosine) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xv[e] = xv[e] / nx;
+            }
+#pragma unroll
+            for (int m = 0; m < NC; ++m) {
+                double cv[4];
+                load4_64(c[m] + j, cv);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const double t = xv[e] - cv[e];
+                    D[m] = D[m] + t * t;
+                }
+            }
+        }
+    }
+    for (; j < d; ++j) {
+        double xv = (double)x[j];
+        if (cosine) xv = xv / nx;
+#pragma unroll
+        for (int m = 0; m < NC; ++m) {
+            const double t = xv - (double)c[m][j];
+            D[m] = D[m] + t * t;
+        }
+    }
+}
+
 // fp64 check of a near-tie point from the full list whose candidates were
 // collected: the lowest-index minimum of the direct-difference fp64 distance
 // over its candidates (both half-lane lists).  A point whose lists overflowed,
@@ -613,22 +673,16 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
             ovf_list[atomicAdd(&counters[2], 1)] = (int32_t)p;
             continue;
         }
-        const float *x = X + (size_t)p * d;
         const double nx = xnorm64 != nullptr ? xnorm64[p] : 1.0;
         double best = INFINITY;
         int bk = 0x7fffffff;
         for (int m = 0; m < c0 + c1; ++m) {
             const int k = m < c0 ? cand[2 * (int64_t)q * kMaxCand + m] : cand[(2 * (int64_t)q + 1) * kMaxCand + m - c0];
-            const CT *c = C + (size_t)k * d;
-            double D = 0.0;
-            for (int j = 0; j < d; ++j) {
-                double xv = (double)x[j];
-                if (xnorm64 != nullptr) xv = xv / nx;
-                const double tt = xv - (double)c[j];
-                D = D + tt * tt;
-            }
-            if (D < best || (D == best && k < bk)) {
-                best = D;
+            const CT *const row[1] = {C + (size_t)k * d};
+            double D[1];
+            sqdist64<CT, 1>(X + (size_t)p * d, row, d, nx, xnorm64 != nullptr, D);
+            if (D[0] < best || (D[0] == best && k < bk)) {
+                best = D[0];
                 bk = k;
             }
         }
@@ -638,36 +692,25 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
 }
 
 // fp64 check of a near-tie point whose winner is one of two known centroids:
-// D = sum_j (x_j - c_j)^2 in fp64 in increasing j, no fused multiply-add, for
-// both; the smaller wins, the lower index on a tie.  One thread per point.
+// the smaller direct-difference distance wins, the lower index on a tie.  One
+// thread per listed point.
 template <typename CT>
 __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ X, int d, const CT *__restrict__ C,
                                                       const double *__restrict__ xnorm64,
                                                       const int32_t *__restrict__ pair_list,
                                                       const int32_t *__restrict__ counters,
                                                       int32_t *__restrict__ a_out, float *__restrict__ d1_out) {
-#pragma clang fp contract(off)
     const int cnt = counters[1];
     for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
         const int64_t p = pair_list[3 * (int64_t)q];
         const int k1 = pair_list[3 * (int64_t)q + 1];
         const int k2 = pair_list[3 * (int64_t)q + 2];
-        const float *x = X + (size_t)p * d;
-        const CT *c1 = C + (size_t)k1 * d;
-        const CT *c2 = C + (size_t)k2 * d;
-        const double nx = xnorm64 != nullptr ? xnorm64[p] : 1.0;
-        double D1 = 0.0, D2 = 0.0;
-        for (int j = 0; j < d; ++j) {
-            double xv = (double)x[j];
-            if (xnorm64 != nullptr) xv = xv / nx;
-            const double t1 = xv - (double)c1[j];
-            const double t2 = xv - (double)c2[j];
-            D1 = D1 + t1 * t1;
-            D2 = D2 + t2 * t2;
-        }
-        const bool second = (D2 < D1) || (D2 == D1 && k2 < k1);
+        const CT *const rows[2] = {C + (size_t)k1 * d, C + (size_t)k2 * d};
+        double D[2];
+        sqdist64<CT, 2>(X + (size_t)p * d, rows, d, xnorm64 != nullptr ? xnorm64[p] : 1.0, xnorm64 != nullptr, D);
+        const bool second = (D[1] < D[0]) || (D[1] == D[0] && k2 < k1);
         a_out[p] = second ? k2 : k1;
-        if (d1_out != nullptr) d1_out[p] = (float)(second ? D2 : D1);
+        if (d1_out != nullptr) d1_out[p] = (float)(second ? D[1] : D[0]);
     }
 }
 
@@ -858,9 +901,10 @@ static hipError_t launch_fa_shape(const FlashArgs &A, hipStream_t s) {
     case 32: return launch_fa<32, 1, 1, 8, 4, true, COLLECT, SPLIT>(A, s);
     case 64: return launch_fa<64, 1, 1, 8, 4, true, COLLECT, SPLIT>(A, s);
     default:
-        // split scoring holds hi and lo halves: one 32-point block per wave
+        // split scoring: 8 waves of 2 point blocks (a few values of the
+        // prologue spill; the tile loop does not)
         if constexpr (SPLIT)
-            return launch_fa<128, 1, 1, 8, 2, true, COLLECT, SPLIT>(A, s);
+            return launch_fa<128, 2, 1, 8, 2, true, COLLECT, SPLIT>(A, s);
         else
             return launch_fa<128, 2, 1, 4, 2, true, COLLECT, SPLIT>(A, s);
     }
