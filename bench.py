@@ -9,8 +9,15 @@ stream it launches on; the FlashAssign kernel's average duration gives the
 roofline line.  The CPU baseline times the fp64 oracle on a bounded sample of
 the same workload on this host's cores and scales it to the full N.
 
+The headline line uses split-bf16 scoring (three bf16 MFMAs per product on
+hi/lo halves of the fp32 operands; the near-tie recheck makes the result the
+same exact assignment as fp32 scoring).  Its roofline is priced against the
+bf16 dense MFMA peak with the algorithmic 2NKd FLOPs; the FLOPs the matrix
+cores actually execute (3 x 2NKd) are reported beside it.  The fp32-scoring
+path is timed after it on the same inputs and reported under "other_scores".
+
 usage: python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--workload NAME]
-                       [--no-cpu-baseline]
+                       [--score split_bf16|fp32] [--no-compare] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -24,7 +31,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense fp32 matrix, TFLOP/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "flash_assign_zipf_16m_d128_k32768_traffic.json")
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix, TFLOP/s
+# per scoring mode: MFMA input type, its dense peak, matrix products issued per
+# algorithmic product, and the main FlashAssign kernel's template arguments
+SCORES = {
+    "fp32": {"mfma_dtype": "fp32", "peak": FP32_MFMA_PEAK_TFLOPS, "products": 1, "dtype": "f32"},
+    "split_bf16": {"mfma_dtype": "bf16", "peak": BF16_MFMA_PEAK_TFLOPS, "products": 3, "dtype": "bf16"},
+}
 ASSIGN_SRC = os.path.join(ROOT, "exact_lloyd_means_flashassign_amd", "csrc", "fk_assign.hip")
 
 
@@ -37,11 +50,15 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def traffic_per_launch():
+def traffic_file(workload, score):
+    return os.path.join(ROOT, "profiles", f"flash_assign_{score}_{workload}_traffic.json")
+
+
+def traffic_per_launch(workload, score):
     """HBM bytes per FlashAssign launch from the committed rocprofv3 counter
     summary, or None when the kernel source changed since it was taken."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file(workload, score)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
@@ -73,8 +90,9 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--workload", default="zipf_16m_d128_k32768")
-    ap.add_argument("--score", default="fp32", choices=["fp32", "split_bf16"],
-                    help="FlashAssign scoring: fp32 MFMA, or bf16 MFMA on split operands (same exact result)")
+    ap.add_argument("--score", default="split_bf16", choices=["split_bf16", "fp32"],
+                    help="FlashAssign scoring: bf16 MFMA on split operands, or fp32 MFMA (same exact result)")
+    ap.add_argument("--no-compare", action="store_true", help="do not also time the other scoring mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference kernel that scales the "
@@ -117,63 +135,85 @@ def main():
     ws = torch.empty(fk.fk_workspace_size(w.N, w.d, w.K, w.metric) + 256, dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
 
-    def step(i):
-        fk.fk_lloyd_iter(Xd, Cs[i % 2], metric=w.metric, assign=a, C_out=Cs[(i + 1) % 2], counts=counts,
-                         workspace=ws, score=args.score)
+    def run(score, steps, warmup):
+        def step(i):
+            fk.fk_lloyd_iter(Xd, Cs[i % 2], metric=w.metric, assign=a, C_out=Cs[(i + 1) % 2], counts=counts,
+                             workspace=ws, score=score)
 
-    for i in range(args.warmup):
-        step(i)
-        log(f"warmup step {i} done")
-    torch.cuda.synchronize()
-    fk.fk_profile_enable(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(args.warmup + i)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    prof = fk.fk_profile_read()
-    fk.fk_profile_enable(False)
-    log(f"timed {args.steps} steps in {elapsed:.3f} s")
-    assert int(counts.sum().item()) == w.N
+        # every run starts from the same initial centroids
+        Cs[0].copy_(C0d)
+        for i in range(warmup):
+            step(i)
+            log(f"{score}: warmup step {i} done")
+        torch.cuda.synchronize()
+        fk.fk_profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(warmup + i)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        prof = fk.fk_profile_read()
+        fk.fk_profile_enable(False)
+        log(f"{score}: timed {steps} steps in {elapsed:.3f} s")
+        assert int(counts.sum().item()) == w.N
+        return summarize(score, steps, elapsed, prof)
 
-    N, d, K = w.N, w.d, w.K
-    ms, calls = prof["ms"], prof["calls"]
-    per = {k: ms[k] / max(args.steps, 1) for k in ms}
-    t_assign = (per["prep"] + per["assign"] + per["recheck"]) / 1e3
-    t_update = (per["sort"] + per["reduce"] + per["finalize"]) / 1e3
-    flops = 2.0 * N * K * d
-    upd_bytes = 4.0 * (N * d + N + K * d + K)
-    fa_ms = ms["assign"] / max(calls["assign"], 1)
-    fa_tflops = flops / (fa_ms / 1e3) / 1e12
-    traffic = traffic_per_launch()
+    def summarize(score, steps, elapsed, prof):
+        N, d, K = w.N, w.d, w.K
+        sc = SCORES[score]
+        ms, calls = prof["ms"], prof["calls"]
+        per = {k: ms[k] / max(steps, 1) for k in ms}
+        t_assign = (per["prep"] + per["assign"] + per["recheck"]) / 1e3
+        t_update = (per["sort"] + per["reduce"] + per["finalize"]) / 1e3
+        flops = 2.0 * N * K * d
+        upd_bytes = 4.0 * (N * d + N + K * d + K)
+        fa_ms = ms["assign"] / max(calls["assign"], 1)
+        fa_tflops = flops / (fa_ms / 1e3) / 1e12
+        return {
+            "s_per_iter": elapsed / steps,
+            "assign_tflops": flops / t_assign / 1e12,
+            "update_gbps": upd_bytes / t_update / 1e9,
+            "assign_frac_fp32_mfma": flops / t_assign / 1e12 / FP32_MFMA_PEAK_TFLOPS,
+            "assign_frac_own_mfma": flops / t_assign / 1e12 / sc["peak"],
+            "update_frac_hbm": upd_bytes / t_update / 1e9 / HBM_PEAK_GBS,
+            "phase_ms_per_step": {k: round(v, 4) for k, v in per.items()},
+            "near_tie_fraction": {"pair": prof["paired"] / max(prof["assigned"], 1),
+                                  "window": prof["windowed"] / max(prof["assigned"], 1),
+                                  "all_k": prof["rechecked"] / max(prof["assigned"], 1)},
+            "roofline": {"kernel": "k_flash_assign", "bound": "mfma", "mfma_dtype": sc["mfma_dtype"],
+                         "achieved": fa_tflops, "peak": sc["peak"], "unit": "TFLOP/s",
+                         "frac": fa_tflops / sc["peak"], "avg_ms": fa_ms,
+                         "executed": fa_tflops * sc["products"],
+                         "executed_frac": fa_tflops * sc["products"] / sc["peak"],
+                         "traffic": traffic_per_launch(w.name, score)},
+        }
+
+    C0d = torch.from_numpy(C0).to(dev)
+    r = run(args.score, args.steps, args.warmup)
     out = {
         "metric": "s per Lloyd iter; assign TFLOP/s & update GB/s at N=16M,d=128,K=32768",
-        "value": elapsed / args.steps,
+        "value": r["s_per_iter"],
         "unit": "s/iter",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": 1e3 * elapsed / args.steps,
+        "ms_per_step": 1e3 * r["s_per_iter"],
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": SCORES[args.score]["dtype"],
         "data": "synthetic",
-        "config": {"workload": w.name, "N": N, "d": d, "K": K, "metric": w.metric, "sigma": w.sigma,
-                   "weights": w.weights if w.weights == "equal" else f"zipf({w.zipf_s})", "seed": w.seed},
-        "assign_tflops": flops / t_assign / 1e12,
-        "update_gbps": upd_bytes / t_update / 1e9,
-        "assign_frac_fp32_mfma": flops / t_assign / 1e12 / FP32_MFMA_PEAK_TFLOPS,
-        "update_frac_hbm": upd_bytes / t_update / 1e9 / HBM_PEAK_GBS,
-        "phase_ms_per_step": {k: round(v, 4) for k, v in per.items()},
-        "near_tie_fraction": {"pair": prof["paired"] / max(prof["assigned"], 1),
-                              "window": prof["windowed"] / max(prof["assigned"], 1),
-                              "all_k": prof["rechecked"] / max(prof["assigned"], 1)},
-        "roofline": {"kernel": "k_flash_assign", "bound": "mfma", "achieved": fa_tflops,
-                     "peak": FP32_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": fa_tflops / FP32_MFMA_PEAK_TFLOPS,
-                     "avg_ms": fa_ms, "traffic": traffic},
+        "config": {"workload": w.name, "N": w.N, "d": w.d, "K": w.K, "metric": w.metric, "sigma": w.sigma,
+                   "weights": w.weights if w.weights == "equal" else f"zipf({w.zipf_s})", "seed": w.seed,
+                   "score": args.score},
     }
+    out.update({k: v for k, v in r.items() if k != "s_per_iter"})
+    if not args.no_compare:
+        out["other_scores"] = {}
+        for other in SCORES:
+            if other != args.score:
+                out["other_scores"][other] = run(other, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         out["cpu_baseline"] = cpu_baseline(w, X, C0)

@@ -41,7 +41,7 @@ struct Layout {
     size_t ncn, cmax_part, scal, counter, flags, thr, pairs, cand, ccount, ovf;
     size_t c64, c32, cnrm64, xnorm64;  // cosine only (else ~0)
     size_t keys_sorted, perm, tmp_keys, tmp_vals, sort_scratch, offsets;
-    size_t sums, cnt, pfirst, plast, chi, clo;
+    size_t sums, cnt, pfirst, plast, csplit;
     size_t xchunk[2], achunk[2];      // out-of-core only
 };
 
@@ -60,7 +60,7 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc) {
     const int64_t nseg = seg_count_bound(r);
     const bool cos = metric == FK_METRIC_COSINE;
     L.ncn = take((size_t)Kpad * 4);
-    L.cmax_part = take((size_t)cdiv(Kpad, 4) * 4);
+    L.cmax_part = take((size_t)cdiv(Kpad, 4) * 3 * 4);
     L.scal = take(64);
     L.counter = take(64);
     L.flags = take((size_t)r * 4);
@@ -79,8 +79,7 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc) {
     L.tmp_vals = take((size_t)r * 4);
     L.sort_scratch = take(sort_scratch_bytes(r));
     L.offsets = take((size_t)(K + 1) * 4);
-    L.chi = take((size_t)K * cdiv(d, 8) * 8 * 2);
-    L.clo = take((size_t)K * cdiv(d, 8) * 8 * 2);
+    L.csplit = take((size_t)Kpad * 2 * split_width(d) * 2);
     L.sums = take((size_t)K * d * 8);
     L.cnt = take((size_t)K * 4);
     L.pfirst = take((size_t)nseg * d * 8);
@@ -213,8 +212,8 @@ struct Ctx {
     int d, K, metric;
     int score;
     SplitC split() const {
-        if (score != FK_SCORE_SPLIT_BF16) return SplitC{nullptr, nullptr};
-        return SplitC{at<__bf16>(ws, L.chi), at<__bf16>(ws, L.clo)};
+        if (score != FK_SCORE_SPLIT_BF16) return SplitC{nullptr, 0};
+        return SplitC{at<__bf16>(ws, L.csplit), split_width(d)};
     }
 };
 
@@ -232,12 +231,11 @@ fk_status step_prep(const Ctx &c, const float *C, const float **C_use) {
     }
     int nparts = 0;
     FK_TRY(launch_centroid_prep(Cu, c.K, c.d, at<float>(c.ws, c.L.ncn), at<float>(c.ws, c.L.cmax_part), &nparts,
-                                c.s),
+                                c.split(), c.s),
            "centroid prep");
     FK_TRY(launch_prep_finish(at<float>(c.ws, c.L.cmax_part), nparts, at<float>(c.ws, c.L.scal),
                               at<int32_t>(c.ws, c.L.counter), c.s),
            "centroid prep finish");
-    if (c.score == FK_SCORE_SPLIT_BF16) FK_TRY(launch_split_bf16(Cu, c.K, c.d, c.split(), c.s), "centroid split");
     *C_use = Cu;
     return FK_OK;
 }

@@ -47,9 +47,8 @@ struct FlashArgs {
     int32_t *cand;       // collect mode: candidates per (slot, half)
     int32_t *ccount;     // collect mode: candidate counts per (slot, half)
     int64_t cap_slots;   // collect mode: slots with candidate storage
-    const __bf16 *Ch;    // split scoring: bf16 high parts of C, rows of dpad
-    const __bf16 *Cl;    // split scoring: bf16 low parts (C - Ch, rounded)
-    int dpad;            // d rounded up to a multiple of 8
+    const __bf16 *Cs;    // split scoring: per centroid row, w bf16 high parts then
+    int sw;              // w bf16 low parts (C - high, rounded); Kpad rows
 };
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -95,11 +94,12 @@ __global__ __launch_bounds__(256) void k_normalize_rows(const float *__restrict_
 // centroids then never win), and the largest ||c_k||^2 of the block.  One wave
 // per centroid row.
 __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__ C, int K, int Kpad, int d,
-                                                       float *__restrict__ ncn, float *__restrict__ cmax_part) {
-    __shared__ float wmax[4];
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int k = blockIdx.x * 4 + w;
-    float cn = 0.f;
+                                                       float *__restrict__ ncn, float *__restrict__ cmax_part,
+                                                       __bf16 *__restrict__ cs, int w) {
+    __shared__ float wmax[3][4];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int k = blockIdx.x * 4 + wv;
+    float cn = 0.f, dn = 0.f, rn = 0.f;
     if (k < K) {
         const float *row = C + (size_t)k * d;
         float s = 0.f;
@@ -110,31 +110,64 @@ __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__
         for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
         cn = s;
     }
+    if (cs != nullptr && k < Kpad) {
+        // split scoring operands: hi = bf16(c) (round to nearest even), lo =
+        // bf16(c - hi); the row holds hi of dims [0, w) then lo of dims
+        // [0, w), zero past d and for k >= K.  dn and rn are the squared
+        // norms of the remainders c - hi (exact in fp32) and c - hi - lo.
+        __bf16 *out = cs + (size_t)k * 2 * w;
+        for (int j = lane; j < w; j += 64) {
+            const float v = (k < K && j < d) ? C[(size_t)k * d + j] : 0.f;
+            const __bf16 hi = (__bf16)v;
+            const float dl = v - (float)hi;
+            const __bf16 lo = (__bf16)dl;
+            const float r = dl - (float)lo;
+            out[j] = hi;
+            out[w + j] = lo;
+            dn = fmaf(dl, dl, dn);
+            rn = fmaf(r, r, rn);
+        }
+        for (int off = 32; off > 0; off >>= 1) {
+            dn += __shfl_xor(dn, off);
+            rn += __shfl_xor(rn, off);
+        }
+    }
     if (lane == 0) {
         if (k < K)
             ncn[k] = -0.5f * cn;
         else if (k < Kpad)
             ncn[k] = -INFINITY;
-        wmax[w] = cn;
+        wmax[0][wv] = cn;
+        wmax[1][wv] = dn;
+        wmax[2][wv] = rn;
     }
     __syncthreads();
-    if (threadIdx.x == 0) cmax_part[blockIdx.x] = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+    if (threadIdx.x < 3) {
+        const float *m = wmax[threadIdx.x];
+        cmax_part[(size_t)blockIdx.x * 3 + threadIdx.x] = fmaxf(fmaxf(m[0], m[1]), fmaxf(m[2], m[3]));
+    }
 }
 
-// scal[0] = max_k ||c_k||^2 (fp32); resets the three near-tie list counters.
+// scal[0] = max_k ||c_k||^2, scal[1] = max_k ||c_k - hi_k||^2, scal[2] =
+// max_k ||c_k - hi_k - lo_k||^2 (fp32; the last two are zero without split
+// scoring); resets the three near-tie list counters.
 __global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ cmax_part, int nparts,
                                                      float *__restrict__ scal, int32_t *__restrict__ counter) {
-    __shared__ float sm[256];
-    float m = 0.f;
-    for (int i = threadIdx.x; i < nparts; i += 256) m = fmaxf(m, cmax_part[i]);
-    sm[threadIdx.x] = m;
+    __shared__ float sm[3][256];
+    float m[3] = {0.f, 0.f, 0.f};
+    for (int i = threadIdx.x; i < nparts; i += 256)
+        for (int c = 0; c < 3; ++c) m[c] = fmaxf(m[c], cmax_part[(size_t)i * 3 + c]);
+    for (int c = 0; c < 3; ++c) sm[c][threadIdx.x] = m[c];
     __syncthreads();
     for (int o = 128; o > 0; o >>= 1) {
-        if ((int)threadIdx.x < o) sm[threadIdx.x] = fmaxf(sm[threadIdx.x], sm[threadIdx.x + o]);
+        if ((int)threadIdx.x < o)
+            for (int c = 0; c < 3; ++c) sm[c][threadIdx.x] = fmaxf(sm[c][threadIdx.x], sm[c][threadIdx.x + o]);
         __syncthreads();
     }
     if (threadIdx.x == 0) {
-        scal[0] = sm[0];
+        scal[0] = sm[0][0];
+        scal[1] = sm[1][0];
+        scal[2] = sm[2][0];
         counter[0] = 0;
         counter[1] = 0;
         counter[2] = 0;
@@ -217,18 +250,18 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         float pn = 0.f;
         auto load_stage = [&](int t, int ch) {
             if constexpr (SPLIT) {
+                // the split copy has Kpad zero-padded rows of sw >= DP * nch
+                // dims, so a whole stage is in bounds; one uniform tile base
+                // serves both halves
+                const __bf16 *tb = A.Cs + (size_t)t * ROWS * (2 * A.sw) + ch * DP;
 #pragma unroll
                 for (int i = 0; i < PFS; ++i) {
                     const int q = tid + i * NT;
                     float4 vh = make_float4(0.f, 0.f, 0.f, 0.f), vl = vh;
-                    if (q < NQ8) {
-                        const int row = q / Q8;
-                        const int col = ch * DP + (q % Q8) * 8;
-                        const int k = t * ROWS + row;
-                        if (k < K && col < A.dpad) {
-                            vh = *reinterpret_cast<const float4 *>(A.Ch + (size_t)k * A.dpad + col);
-                            vl = *reinterpret_cast<const float4 *>(A.Cl + (size_t)k * A.dpad + col);
-                        }
+                    if (NQ8 % NT == 0 || q < NQ8) {
+                        const unsigned o = (unsigned)((q / Q8) * (2 * A.sw) + (q % Q8) * 8);
+                        vh = *reinterpret_cast<const float4 *>(tb + o);
+                        vl = *reinterpret_cast<const float4 *>(tb + o + A.sw);
                     }
                     pfh[i] = vh;
                     pfl[i] = vl;
@@ -287,6 +320,9 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         // indices of the first two.  collect mode: the listed point's
         // threshold and this half-lane's candidate count.
         float xn[PB], xsc[PB], b1[PB], b2[PB], b3[PB];
+        // split scoring: squared norms of this half-lane's low parts and of
+        // the remainders x - hi - lo (for the bound on the dropped terms)
+        float xl2[PB], xr2[PB];
         int i1[PB], i2[PB];
         int64_t pt[PB];
         bool pv[PB];
@@ -303,6 +339,8 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 b1[b] = -INFINITY;
             }
             xn[b] = 0.f;
+            xl2[b] = 0.f;
+            xr2[b] = 0.f;
             xsc[b] = (A.xnorm64 != nullptr && pv[b]) ? (float)(1.0 / A.xnorm64[pt[b]]) : 1.f;
             b2[b] = -INFINITY;
             b3[b] = -INFINITY;
@@ -317,7 +355,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
 #pragma unroll
             for (int b = 0; b < PB; ++b) {
                 if constexpr (SPLIT) {
-                    float nacc = xn[b];
+                    float nacc = xn[b], lacc = xl2[b], racc = xr2[b];
 #pragma unroll
                     for (int st = 0; st < NS; ++st) {
                         const int col0 = ch * DP + 16 * st + 8 * h;
@@ -336,10 +374,17 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
 #pragma unroll
                         for (int e = 0; e < 8; ++e) {
                             const float xv = (A.xnorm64 != nullptr) ? v[e] * xsc[b] : v[e];
-                            if (add_norm) nacc = fmaf(xv, xv, nacc);
                             const __bf16 hi = (__bf16)xv;
+                            const float dl = xv - (float)hi;  // exact
+                            const __bf16 lo = (__bf16)dl;
                             xh[b][st][e] = hi;
-                            xl[b][st][e] = (__bf16)(xv - (float)hi);
+                            xl[b][st][e] = lo;
+                            if (add_norm) {
+                                const float lf = (float)lo, r = dl - lf;  // exact
+                                nacc = fmaf(xv, xv, nacc);
+                                lacc = fmaf(lf, lf, lacc);
+                                racc = fmaf(r, r, racc);
+                            }
                         }
                         // keep the scheduler from hoisting every load of the
                         // row ahead of the splits (it would hold all the fp32
@@ -347,6 +392,8 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                         __builtin_amdgcn_sched_barrier(0);
                     }
                     xn[b] = nacc;
+                    xl2[b] = lacc;
+                    xr2[b] = racc;
                 } else {
                     const int col0 = ch * DP + h * HALF;
                     const float *src = X + (size_t)pt[b] * d + col0;
@@ -378,10 +425,50 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             }
         };
 
+        // Per-point bound of the accumulator error (see the derivation above
+        // the kernel): on return xn[b] holds ||x||^2 (both half-lanes) and
+        // xl2[b] holds 2 e_i, the near-tie window.
+        const float u = 5.9604645e-8f;
+        // roundings per accumulator path: d + 3 (fp32 scoring) or 3d + 3
+        // (split: three products per dim)
+        const float g = (float)((SPLIT ? 3 : 1) * d + 4) * u + (A.xnorm64 != nullptr ? 8.f * u : 0.f);
+        auto point_bounds = [&]() {
+            const float M = A.scal[0] * (1.f + g);
+            const float sqM = sqrtf(M) * (1.f + 2.f * u);
+#pragma unroll
+            for (int b = 0; b < PB; ++b) {
+                const float xnt = xn[b] + __shfl_xor(xn[b], 32);
+                const float xnorm = sqrtf(xnt * (1.f + g)) * (1.f + 2.f * u);
+                // split scoring computes hx.hc + hx.lc + lx.hc; with the
+                // remainders dx = x - hx, rx = x - hx - lx (and likewise for c)
+                // the dropped part of x.c is exactly lx.dc + rx.c + hx.rc, at
+                // most ||lx|| max||dc|| + ||rx|| max||c|| + ||hx|| max||rc|| by
+                // Cauchy-Schwarz (||hx|| <= (1 + 2^-8) ||x||).  The norms are
+                // fp32 sums of squares: relative error far below the 1% added,
+                // and a square under 2^-126 that is flushed to zero loses at
+                // most sqrt(d) * 1.1e-19 of a norm, which is added back.
+                float drop = 0.f;
+                if constexpr (SPLIT) {
+                    const float uf = 1.1e-19f * sqrtf((float)d);
+                    const float l2 = xl2[b] + __shfl_xor(xl2[b], 32);
+                    const float r2 = xr2[b] + __shfl_xor(xr2[b], 32);
+                    drop = 1.01f * ((sqrtf(l2) + uf) * (sqrtf(A.scal[1]) + uf) + (sqrtf(r2) + uf) * sqM +
+                                    1.004f * xnorm * (sqrtf(A.scal[2]) + uf));
+                }
+                // the last term covers flushed denormal operands
+                xl2[b] = 2.f * (1.0625f * (g * (M + xnorm * sqM) + drop) + 7.6e-37f * (float)d * (sqM + xnorm) +
+                                1e-30f);
+                xn[b] = xnt;
+            }
+        };
+
         v16f acc[PB][CB];
         const int cnch = RES ? 1 : A.nch;
         const int nst = A.ntiles * cnch;
-        if (RES) load_x(0, true);
+        if (RES) {
+            load_x(0, true);
+            if (!COLLECT) point_bounds();
+        }
         load_stage(0, 0);
         store_stage(0, 0);
         __syncthreads();
@@ -515,14 +602,9 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             continue;
         }
 
+        if (!RES) point_bounds();
         // merge the two half-waves (same point, the other 16 centroids of each
         // 32-block): larger score first, lower index first on equal scores
-        const float u = 5.9604645e-8f;
-        // roundings per accumulator path: d + 3 (fp32 scoring) or 3d + 3
-        // (split: three products per dim)
-        const float g = (float)((SPLIT ? 3 : 1) * d + 4) * u + (A.xnorm64 != nullptr ? 8.f * u : 0.f);
-        const float M = A.scal[0] * (1.f + g);
-        const float sqM = sqrtf(M) * (1.f + 2.f * u);
 #pragma unroll
         for (int b = 0; b < PB; ++b) {
             const float o1 = __shfl_xor(b1[b], 32);
@@ -541,15 +623,9 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             const int si2 = wsec ? wi2 : li1;
             const float s3 = wsec ? fmaxf(w3, l1) : fmaxf(w2, l2);
 
-            const float xnt = xn[b] + __shfl_xor(xn[b], 32);
-            const int64_t p = pt[b];
-            const bool valid = (h == 0) && pv[b];
-            const float xnorm = sqrtf(xnt * (1.f + g)) * (1.f + 2.f * u);
-            // split scoring also drops lo.lo and the bf16 remainders:
-            // at most 3.01 * 2^-18 sum_j |x_j c_j| <= 1.15e-5 ||x|| ||c||;
-            // the last term covers flushed denormal operands
-            const float e2 = 2.f * (1.0625f * (g * (M + xnorm * sqM) + (SPLIT ? 1.15e-5f * xnorm * sqM : 0.f)) +
-                                    7.6e-37f * (float)d * (sqM + xnorm) + 1e-30f);
+            const float xnt = xn[b], e2 = xl2[b];
+            const int64_t p = sbase + b * 32 + jl;
+            const bool valid = (h == 0) && p < A.N;
             // near tie: the exact winner is not certain
             const bool flagged = !((w1 - s2) > e2);
             // only the top two can win: every other score is more than 2e below
@@ -811,25 +887,9 @@ __global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, in
     }
 }
 
-// Split scoring operands: hi = bf16(c) (round to nearest even), lo =
-// bf16(c - hi); rows padded with zeros to dpad (a multiple of 8 elements).
-__global__ __launch_bounds__(256) void k_split_bf16(const float *__restrict__ C, int K, int d, int dpad,
-                                                    __bf16 *__restrict__ hi, __bf16 *__restrict__ lo) {
-    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (q >= (int64_t)K * dpad) return;
-    const int64_t k = q / dpad;
-    const int j = (int)(q - k * dpad);
-    const float c = j < d ? C[k * d + j] : 0.f;
-    const __bf16 h = (__bf16)c;
-    hi[q] = h;
-    lo[q] = (__bf16)(c - (float)h);
-}
-
-hipError_t launch_split_bf16(const float *C, int K, int d, const SplitC &sc, hipStream_t s) {
-    const int dpad = (int)cdiv(d, 8) * 8;
-    const int64_t total = (int64_t)K * dpad;
-    hipLaunchKernelGGL(k_split_bf16, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, C, K, d, dpad, sc.hi, sc.lo);
-    return hipGetLastError();
+int split_width(int d) {
+    const AssignShape sh = assign_shape(d);
+    return sh.DP * sh.nch;
 }
 
 // ---------------------------------------------------------------------------
@@ -857,11 +917,11 @@ hipError_t launch_normalize_rows(const float *M, int64_t rows, int d, const doub
 }
 
 hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float *cmax_part, int *nparts,
-                                hipStream_t s) {
+                                const SplitC &sc, hipStream_t s) {
     const int Kpad = (int)(cdiv(K, kCentroidPad) * kCentroidPad);
     const int nb = (int)cdiv(Kpad, 4);
     *nparts = nb;
-    hipLaunchKernelGGL(k_centroid_prep, dim3(nb), dim3(256), 0, s, C, K, Kpad, d, ncn, cmax_part);
+    hipLaunchKernelGGL(k_centroid_prep, dim3(nb), dim3(256), 0, s, C, K, Kpad, d, ncn, cmax_part, sc.cs, sc.w);
     return hipGetLastError();
 }
 
@@ -939,9 +999,8 @@ static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, co
     A.cand = nt.cand;
     A.ccount = nt.ccount;
     A.cap_slots = near_tie_cap(N);
-    A.Ch = sc.hi;
-    A.Cl = sc.lo;
-    A.dpad = (int)cdiv(d, 8) * 8;
+    A.Cs = sc.cs;
+    A.sw = sc.w;
     return A;
 }
 
@@ -957,7 +1016,7 @@ hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C,
                                const NearTies &nt, const SplitC &sc, hipStream_t s) {
     if (N <= 0) return hipSuccess;
     return launch_fa_score<false>(flash_args(X, N, d, C, ncn, K, scal, xnorm64, a_out, d1_out, nt, sc),
-                                  sc.hi != nullptr, s);
+                                  sc.cs != nullptr, s);
 }
 
 hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma, const float *C32,
@@ -979,7 +1038,7 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
     }
     // 2. the full list: collect every centroid within each point's window
     if ((e = launch_fa_score<true>(flash_args(X, N, d, C_mfma, ncn, K, scal, xnorm64, a_out, d1_out, nt, sc),
-                                   sc.hi != nullptr, s)) != hipSuccess)
+                                   sc.cs != nullptr, s)) != hipSuccess)
         return e;
     // 3. fp64 over the collected candidates; overflows go to the last list
     {

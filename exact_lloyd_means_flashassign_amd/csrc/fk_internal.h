@@ -55,13 +55,24 @@ struct AssignShape {
 };
 // The point-block geometry of the kernel variant used for d.
 AssignShape assign_shape(int d);
+// Split-bf16 scoring operands: Kpad rows (Kpad = K rounded up to
+// kCentroidPad, rows past K are zero), each holding the bf16 high parts of
+// dims [0, w) and then the bf16 low parts, w = split_width(d) (d rounded up to
+// the FlashAssign chunk width).  cs == nullptr selects fp32 scoring.
+struct SplitC {
+    __bf16 *cs;
+    int w;
+};
+int split_width(int d);
 
 // ---- launchers (each returns the launch status) ---------------------------
 hipError_t launch_row_norm64(const float *M, int64_t rows, int d, double *nrm, hipStream_t s);
 hipError_t launch_normalize_rows(const float *M, int64_t rows, int d, const double *nrm, double *out64,
                                  float *out32, hipStream_t s);
+// -||c||^2/2 (padded with -inf to kCentroidPad) and per-block maxima of the
+// centroid norms; with split scoring also writes the split operands.
 hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float *cmax_part, int *nparts,
-                                hipStream_t s);
+                                const SplitC &sc, hipStream_t s);
 hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, int32_t *counter,
                               hipStream_t s);
 // Near-tie bookkeeping of FlashAssign (all in the workspace):
@@ -80,13 +91,6 @@ struct NearTies {
 };
 constexpr int kCandPerSlot = 16;
 int64_t near_tie_cap(int64_t N);
-// Split-bf16 scoring operands (hi, lo: K rows of d rounded up to 8 bf16);
-// both null selects fp32 scoring.
-struct SplitC {
-    __bf16 *hi;
-    __bf16 *lo;
-};
-hipError_t launch_split_bf16(const float *C, int K, int d, const SplitC &sc, hipStream_t s);
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                                const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
                                const NearTies &nt, const SplitC &sc, hipStream_t s);
