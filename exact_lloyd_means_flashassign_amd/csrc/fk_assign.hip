@@ -429,9 +429,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         // the kernel): on return xn[b] holds ||x||^2 (both half-lanes) and
         // xl2[b] holds 2 e_i, the near-tie window.
         const float u = 5.9604645e-8f;
-        // roundings per accumulator path: d + 3 (fp32 scoring) or 3d + 3
-        // (split: three products per dim)
-        const float g = (float)((SPLIT ? 3 : 1) * d + 4) * u + (A.xnorm64 != nullptr ? 8.f * u : 0.f);
+        // roundings per accumulator path: at most d + 3 for -||c||^2/2 and
+        // the fp32 (or hi.hi) products; the split cross terms, below 2^-7 of
+        // the products in size, pass through at most 2d + 1 and add less than
+        // 0.016 (2d + 1) u ||x|| ||c||, which the 1.0625 factor covers
+        const float g = (float)(d + 4) * u + (A.xnorm64 != nullptr ? 8.f * u : 0.f);
         auto point_bounds = [&]() {
             const float M = A.scal[0] * (1.f + g);
             const float sqM = sqrtf(M) * (1.f + 2.f * u);
@@ -462,7 +464,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             }
         };
 
+        // acc: -||c||^2/2 + the fp32 (or hi.hi) products; split scoring keeps
+        // the two small cross terms in a second accumulator (acl) that is
+        // added once per tile, so that they pass through few roundings
         v16f acc[PB][CB];
+        v16f acl[PB][SPLIT ? CB : 1];
         const int cnch = RES ? 1 : A.nch;
         const int nst = A.ntiles * cnch;
         if (RES) {
@@ -499,13 +505,15 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                             acc[b][cb][4 * q + 1] = nv.y;
                             acc[b][cb][4 * q + 2] = nv.z;
                             acc[b][cb][4 * q + 3] = nv.w;
+                            if constexpr (SPLIT)
+                                for (int e = 0; e < 4; ++e) acl[b][cb][4 * q + e] = 0.f;
                         }
                     }
                 }
             }
 
             if constexpr (SPLIT) {
-                // x.c ~ hi.hi + hi.lo + lo.hi, small terms first
+                // x.c ~ hi.hi + (hi.lo + lo.hi)
                 const __bf16 *sh = &sCh[buf][jl * LDB + 8 * h];
                 const __bf16 *sl = &sCl[buf][jl * LDB + 8 * h];
 #pragma unroll
@@ -520,8 +528,8 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
                         for (int b = 0; b < PB; ++b) {
-                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[cb], xh[b][st], acc[b][cb], 0, 0, 0);
-                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[cb], xl[b][st], acc[b][cb], 0, 0, 0);
+                            acl[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[cb], xh[b][st], acl[b][cb], 0, 0, 0);
+                            acl[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[cb], xl[b][st], acl[b][cb], 0, 0, 0);
                             acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah[cb], xh[b][st], acc[b][cb], 0, 0, 0);
                         }
                     }
@@ -552,6 +560,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 for (int b = 0; b < PB; ++b) {
 #pragma unroll
                     for (int cb = 0; cb < CB; ++cb) {
+                        if constexpr (SPLIT) acc[b][cb] += acl[b][cb];
                         // A value changes this lane's state only if it beats the
                         // third best (top-3) or reaches the threshold (collect).
                         // Late in the sweep most 16-value groups change no lane
