@@ -22,7 +22,6 @@ constexpr int kSortWaves = 4;
 constexpr int kSortThreads = kSortWaves * kWave;
 constexpr int kSortRows = 16;                                  // 64-key rows per wave
 constexpr int kSortTile = kSortWaves * kSortRows * kWave;       // 4096 keys per tile
-constexpr int kScanChunk = 4096;                                // scan elements per block
 
 // ---- segmented reduction geometry -----------------------------------------
 constexpr int kSegWaves = 4;

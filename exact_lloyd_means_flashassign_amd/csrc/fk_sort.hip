@@ -8,11 +8,13 @@
 // so at most two passes of <= 8 bits are needed.
 //
 // Each pass is hist -> scan -> scatter over tiles of 4096 keys.  Inside a tile
-// a wave ranks 64 keys at a time with ballots: for a digit of B bits, B ballots
-// give every lane the mask of lanes holding the same digit; its rank is the
-// number of such lanes below it, and the lowest such lane (the leader) alone
-// updates that digit's running count in LDS.  No atomic operation is used
-// anywhere: every LDS count has exactly one writer at a time.
+// the scatter ranks 64 keys at a time with ballots: for a digit of B bits, B
+// ballots give every lane the mask of lanes holding the same digit; its rank
+// is the number of such lanes below it, and the lowest such lane (the leader)
+// alone updates that digit's running count in LDS, so the order of equal
+// digits is kept without any atomic operation.  Only the per-tile digit
+// counts, where order does not matter, use LDS atomic adds; nothing touches
+// global memory atomically.
 #include "fk_internal.h"
 
 namespace fk {
@@ -35,22 +37,19 @@ __device__ __forceinline__ uint64_t match_digit(unsigned dig, uint64_t active) {
     return m;
 }
 
-// Per-wave digit counts of the tile into wcnt[wave][digit] (LDS).
+// Per-wave digit counts of the tile into wcnt[wave][digit] (LDS); counting
+// needs no order, so lanes add with LDS atomic adds.
 template <int BITS>
 __device__ __forceinline__ void tile_counts(const unsigned (&dig)[kSortRows], const int64_t row0, int64_t N,
                                             int *wcnt_w) {
     const int lane = threadIdx.x & 63;
 #pragma unroll
-    for (int r = 0; r < kSortRows; ++r) {
-        const bool valid = row0 + r * 64 + lane < N;
-        const uint64_t act = __ballot(valid);
-        if (act == 0ull) break;
-        const uint64_t m = match_digit<BITS>(dig[r], act);
-        if (valid && (m & lanemask_lt_s()) == 0ull) wcnt_w[dig[r]] += __popcll(m);
-    }
+    for (int r = 0; r < kSortRows; ++r)
+        if (row0 + r * 64 + lane < N) atomicAdd(&wcnt_w[dig[r]], 1);
 }
 
-// hist[digit * ntiles + tile] = number of keys of the tile with that digit.
+// hist[tile * NB + digit] = number of keys of the tile with that digit (one
+// contiguous row per tile), summed over the waves' LDS sub-histograms.
 template <int BITS>
 __global__ __launch_bounds__(kSortThreads) void k_radix_hist(const int32_t *__restrict__ keys, int64_t N, int shift,
                                                              int32_t *__restrict__ hist, int ntiles) {
@@ -72,7 +71,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_hist(const int32_t *__re
         int s = 0;
 #pragma unroll
         for (int ww = 0; ww < kSortWaves; ++ww) s += wcnt[ww][v];
-        hist[(int64_t)v * ntiles + blockIdx.x] = s;
+        hist[(int64_t)blockIdx.x * NB + v] = s;
     }
 }
 
@@ -131,7 +130,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *_
         if (v < NB) {
             int s = tot[v] - t;  // exclusive
             dstart[v] = s;
-            gbase[v] = hist_scan[(int64_t)v * ntiles + blockIdx.x];
+            gbase[v] = hist_scan[(int64_t)blockIdx.x * NB + v];
 #pragma unroll
             for (int ww = 0; ww < kSortWaves; ++ww) {
                 const int c = wcnt[ww][v];
@@ -170,90 +169,106 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *_
     }
 }
 
-// ---- exclusive scan of an int32 array, reduce-then-scan, three kernels ----
-__global__ __launch_bounds__(256) void k_scan_reduce(const int32_t *__restrict__ in, int64_t n,
-                                                     int32_t *__restrict__ part) {
-    __shared__ int sm[256];
-    const int64_t b0 = (int64_t)blockIdx.x * kScanChunk;
-    int s = 0;
-    for (int i = threadIdx.x; i < kScanChunk; i += 256) {
-        const int64_t q = b0 + i;
-        if (q < n) s += in[q];
-    }
-    sm[threadIdx.x] = s;
-    __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
-        if ((int)threadIdx.x < o) sm[threadIdx.x] += sm[threadIdx.x + o];
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) part[blockIdx.x] = sm[0];
-}
+// ---- global digit offsets: hscan[t][v] = (keys with a digit below v) + (keys
+// with digit v in tiles before t).  Column scan of the [tile][digit] counts
+// in three kernels over chunks of kColChunk tiles; one thread per digit, so
+// every access reads or writes whole contiguous rows.
+constexpr int kColChunk = 32;
 
-// In-place exclusive scan of part[0..np) by one workgroup.
-__global__ __launch_bounds__(256) void k_scan_top(int32_t *__restrict__ part, int np) {
-    __shared__ int sm[256];
-    __shared__ int carry;
-    if (threadIdx.x == 0) carry = 0;
-    __syncthreads();
-    for (int b = 0; b < np; b += 256) {
-        const int i = b + threadIdx.x;
-        const int v = i < np ? part[i] : 0;
-        sm[threadIdx.x] = v;
-        __syncthreads();
-        for (int o = 1; o < 256; o <<= 1) {
-            const int t = (int)threadIdx.x >= o ? sm[threadIdx.x - o] : 0;
-            __syncthreads();
-            sm[threadIdx.x] += t;
-            __syncthreads();
-        }
-        if (i < np) part[i] = carry + sm[threadIdx.x] - v;
-        __syncthreads();
-        if (threadIdx.x == 255) carry += sm[255];
-        __syncthreads();
-    }
-}
-
-// out = exclusive scan of in, each chunk offset by its scanned partial.
-__global__ __launch_bounds__(256) void k_scan_down(const int32_t *__restrict__ in, int64_t n,
-                                                   const int32_t *__restrict__ part, int32_t *__restrict__ out) {
-    constexpr int PER = kScanChunk / 256;
-    __shared__ int sm[256];
-    const int64_t b0 = (int64_t)blockIdx.x * kScanChunk + (int64_t)threadIdx.x * PER;
-    int v[PER];
+// part[c][v] = digit-v keys in the tiles of chunk c
+__global__ __launch_bounds__(256) void k_col_reduce(const int32_t *__restrict__ hist, int ntiles, int NB,
+                                                    int32_t *__restrict__ part) {
+    const int v = threadIdx.x;
+    if (v >= NB) return;
+    const int t0 = blockIdx.x * kColChunk;
+    int x[kColChunk];
+#pragma unroll
+    for (int i = 0; i < kColChunk; ++i) x[i] = t0 + i < ntiles ? hist[(int64_t)(t0 + i) * NB + v] : 0;
     int s = 0;
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        v[i] = (b0 + i < n) ? in[b0 + i] : 0;
-        s += v[i];
+    for (int i = 0; i < kColChunk; ++i) s += x[i];
+    part[(int64_t)blockIdx.x * NB + v] = s;
+}
+
+// part[c][v] <- digit-v keys in chunks before c; part[nchunks][v] <- keys with
+// a digit below v
+__global__ __launch_bounds__(256) void k_col_top(int32_t *__restrict__ part, int nchunks, int NB) {
+    constexpr int B = 16;
+    __shared__ int sm[256];
+    const int v = threadIdx.x;
+    int run = 0;
+    if (v < NB) {
+        for (int c0 = 0; c0 < nchunks; c0 += B) {
+            int x[B];
+#pragma unroll
+            for (int i = 0; i < B; ++i) x[i] = c0 + i < nchunks ? part[(int64_t)(c0 + i) * NB + v] : 0;
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                if (c0 + i < nchunks) part[(int64_t)(c0 + i) * NB + v] = run;
+                run += x[i];
+            }
+        }
     }
-    sm[threadIdx.x] = s;
+    // exclusive scan of the digit totals
+    sm[v] = run;
     __syncthreads();
     for (int o = 1; o < 256; o <<= 1) {
-        const int t = (int)threadIdx.x >= o ? sm[threadIdx.x - o] : 0;
+        const int a = v >= o ? sm[v - o] : 0;
         __syncthreads();
-        sm[threadIdx.x] += t;
+        sm[v] += a;
         __syncthreads();
     }
-    int run = part[blockIdx.x] + sm[threadIdx.x] - s;
+    if (v < NB) part[(int64_t)nchunks * NB + v] = sm[v] - run;
+}
+
+__global__ __launch_bounds__(256) void k_col_down(const int32_t *__restrict__ hist, int ntiles, int NB,
+                                                  const int32_t *__restrict__ part, int nchunks,
+                                                  int32_t *__restrict__ hscan) {
+    const int v = threadIdx.x;
+    if (v >= NB) return;
+    const int t0 = blockIdx.x * kColChunk;
+    int x[kColChunk];
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-        if (b0 + i < n) out[b0 + i] = run;
-        run += v[i];
+    for (int i = 0; i < kColChunk; ++i) x[i] = t0 + i < ntiles ? hist[(int64_t)(t0 + i) * NB + v] : 0;
+    int run = part[(int64_t)blockIdx.x * NB + v] + part[(int64_t)nchunks * NB + v];
+#pragma unroll
+    for (int i = 0; i < kColChunk; ++i) {
+        if (t0 + i < ntiles) hscan[(int64_t)(t0 + i) * NB + v] = run;
+        run += x[i];
     }
 }
 
 // offsets[k] = first position of key k in the sorted keys (= position of the
 // first key >= k); offsets[K] = N.  Each offsets[k] is written by exactly one
-// thread: the one at the boundary where the key first reaches k.
+// thread: the one at the boundary where the key first reaches k.  A thread
+// covers four consecutive positions (one 16-byte load).
 __global__ __launch_bounds__(256) void k_offsets(const int32_t *__restrict__ ks, int64_t N, int K,
                                                  int32_t *__restrict__ offsets) {
-    const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (r > N) return;
-    // keys are documented to lie in [0, K); the clamps only keep a bad key
-    // from writing outside offsets[0..K]
-    const int lo = max((r == 0) ? 0 : ks[r - 1] + 1, 0);
-    const int hi = min((r == N) ? K : ks[r], K);
-    for (int k = lo; k <= hi; ++k) offsets[k] = (int32_t)r;
+    const int64_t r0 = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    if (r0 > N) return;
+    int cur[4];
+    if (r0 + 4 <= N) {
+        const int4 v = *reinterpret_cast<const int4 *>(ks + r0);
+        cur[0] = v.x;
+        cur[1] = v.y;
+        cur[2] = v.z;
+        cur[3] = v.w;
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) cur[i] = r0 + i < N ? ks[r0 + i] : K;
+    }
+    int prev = r0 == 0 ? -1 : ks[r0 - 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = r0 + i;
+        if (r > N) break;
+        // keys are documented to lie in [0, K); the clamps only keep a bad key
+        // from writing outside offsets[0..K]
+        const int lo = max(prev + 1, 0);
+        const int hi = min(cur[i], K);
+        for (int k = lo; k <= hi; ++k) offsets[k] = (int32_t)r;
+        prev = cur[i];
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -268,20 +283,20 @@ static int64_t ntiles_of(int64_t N) { return cdiv(N, kSortTile); }
 size_t sort_scratch_bytes(int64_t N) {
     const int64_t nt = ntiles_of(N > 0 ? N : 1);
     const int64_t hn = 256 * nt;
-    const int64_t np = cdiv(hn, kScanChunk);
+    const int64_t np = 256 * (cdiv(nt, kColChunk) + 1);
     return align_up((size_t)hn * 4, 256) * 2 + align_up((size_t)np * 4, 256);
 }
 
 template <int BITS>
 static hipError_t radix_pass(const int32_t *kin, const int32_t *vin, int64_t N, int shift, int32_t *kout,
                              int32_t *vout, int32_t *hist, int32_t *hscan, int32_t *part, hipStream_t s) {
+    constexpr int NB = 1 << BITS;
     const int nt = (int)ntiles_of(N);
-    const int64_t hn = (int64_t)(1 << BITS) * nt;
-    const int np = (int)cdiv(hn, kScanChunk);
+    const int nc = (int)cdiv(nt, kColChunk);
     hipLaunchKernelGGL(k_radix_hist<BITS>, dim3(nt), dim3(kSortThreads), 0, s, kin, N, shift, hist, nt);
-    hipLaunchKernelGGL(k_scan_reduce, dim3(np), dim3(256), 0, s, hist, hn, part);
-    hipLaunchKernelGGL(k_scan_top, dim3(1), dim3(256), 0, s, part, np);
-    hipLaunchKernelGGL(k_scan_down, dim3(np), dim3(256), 0, s, hist, hn, part, hscan);
+    hipLaunchKernelGGL(k_col_reduce, dim3(nc), dim3(256), 0, s, hist, nt, NB, part);
+    hipLaunchKernelGGL(k_col_top, dim3(1), dim3(256), 0, s, part, nc, NB);
+    hipLaunchKernelGGL(k_col_down, dim3(nc), dim3(256), 0, s, hist, nt, NB, part, nc, hscan);
     hipLaunchKernelGGL(k_radix_scatter<BITS>, dim3(nt), dim3(kSortThreads), 0, s, kin, vin, N, shift, hscan, nt,
                        kout, vout);
     return hipGetLastError();
@@ -322,7 +337,7 @@ hipError_t launch_sort_by_key(const int32_t *keys, int64_t N, int K, int32_t *ke
 }
 
 hipError_t launch_offsets(const int32_t *keys_sorted, int64_t N, int K, int32_t *offsets, hipStream_t s) {
-    hipLaunchKernelGGL(k_offsets, dim3((unsigned)cdiv(N + 1, 256)), dim3(256), 0, s, keys_sorted, N, K, offsets);
+    hipLaunchKernelGGL(k_offsets, dim3((unsigned)cdiv(N / 4 + 1, 256)), dim3(256), 0, s, keys_sorted, N, K, offsets);
     return hipGetLastError();
 }
 
