@@ -292,15 +292,18 @@ fk_status step_sort(const Ctx &c, const int32_t *a, int64_t rows, int32_t *perm_
     return FK_OK;
 }
 
-fk_status step_zero_accumulators(const Ctx &c) {
+// Counts start at zero (so that no rows give empty clusters); the fp64 sums
+// only need it when several batches of rows are added into them.
+fk_status step_zero_accumulators(const Ctx &c, bool batches) {
     PhaseScope ph(FK_PH_REDUCE, c.s);
-    FK_TRY(launch_fill_zero(at<void>(c.ws, c.L.sums), (size_t)c.K * c.d * 8, c.s), "zero sums");
+    if (batches) FK_TRY(launch_fill_zero(at<void>(c.ws, c.L.sums), (size_t)c.K * c.d * 8, c.s), "zero sums");
     FK_TRY(launch_fill_zero(at<void>(c.ws, c.L.cnt), (size_t)c.K * 4, c.s), "zero counts");
     return FK_OK;
 }
 
-// Sort-Inverse accumulation of `rows` rows into the fp64 sums and counts.
-fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int32_t *a) {
+// Sort-Inverse accumulation of `rows` rows into the fp64 sums and counts
+// (added to them when `batches`, else written).
+fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int32_t *a, bool batches) {
     if (rows <= 0) return FK_OK;
     fk_status st = step_sort(c, a, rows, nullptr, nullptr);
     if (st != FK_OK) return st;
@@ -308,13 +311,13 @@ fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int3
     const double *xn = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.xnorm64) : nullptr;
     FK_TRY(launch_seg_reduce(X, rows, c.d, c.K, at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.perm), xn,
                              at<double>(c.ws, c.L.sums), at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast),
-                             c.s),
+                             batches, c.s),
            "segmented reduction");
     FK_TRY(launch_seg_fixup(at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.offsets), rows, c.d, c.K,
                             at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast), at<double>(c.ws, c.L.sums),
-                            c.s),
+                            batches, c.s),
            "segment fix-up");
-    FK_TRY(launch_count_accumulate(at<int32_t>(c.ws, c.L.offsets), c.K, at<int32_t>(c.ws, c.L.cnt), c.s),
+    FK_TRY(launch_count_accumulate(at<int32_t>(c.ws, c.L.offsets), c.K, at<int32_t>(c.ws, c.L.cnt), batches, c.s),
            "count accumulate");
     return FK_OK;
 }
@@ -416,9 +419,9 @@ fk_status fk_update(const float *X, int64_t N, int32_t d, const int32_t *assign,
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
     const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, FK_SCORE_FP32};
-    if ((st = step_zero_accumulators(c)) != FK_OK) return st;
+    if ((st = step_zero_accumulators(c, false)) != FK_OK) return st;
     if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
-    if ((st = step_accumulate(c, X, N, assign)) != FK_OK) return st;
+    if ((st = step_accumulate(c, X, N, assign, false)) != FK_OK) return st;
     return step_finalize(c, C_prev, C_out, counts);
 }
 
@@ -437,13 +440,13 @@ fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in,
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
     const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
-    if ((st = step_zero_accumulators(c)) != FK_OK) return st;
+    if ((st = step_zero_accumulators(c, false)) != FK_OK) return st;
     if (N > 0) {
         const float *Cu = nullptr;
         if ((st = step_prep(c, C_in, &Cu)) != FK_OK) return st;
         if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
         if ((st = step_assign(c, X, N, C_in, Cu, assign, min_dist)) != FK_OK) return st;
-        if ((st = step_accumulate(c, X, N, assign)) != FK_OK) return st;
+        if ((st = step_accumulate(c, X, N, assign, false)) != FK_OK) return st;
     }
     return step_finalize(c, C_in, C_out, counts);
 }
@@ -519,7 +522,7 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
     if ((st = ooc_resources(&R)) != FK_OK) return st;
 
     const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
-    if ((st = step_zero_accumulators(c)) != FK_OK) return st;
+    if ((st = step_zero_accumulators(c, true)) != FK_OK) return st;
     const float *Cu = nullptr;
     if (N > 0 && (st = step_prep(c, C_in, &Cu)) != FK_OK) return st;
     // the copy stream may not touch the chunk buffers before the work already
@@ -546,7 +549,7 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
         // the near-tie list is per chunk: reset its counter
         FK_TRY(launch_fill_zero(at<void>(workspace, L.counter), 16, c.s), "reset counters");
         if ((st = step_assign(c, Xd, rows, C_in, Cu, ad, nullptr)) != FK_OK) return st;
-        if ((st = step_accumulate(c, Xd, rows, ad)) != FK_OK) return st;
+        if ((st = step_accumulate(c, Xd, rows, ad, true)) != FK_OK) return st;
         FK_TRY(hipEventRecord(R->freed[b], c.s), "event record");
         if (assign_host != nullptr)
             FK_TRY(hipMemcpyAsync(assign_host + r0, ad, (size_t)rows * 4, hipMemcpyDeviceToHost, c.s),

@@ -232,7 +232,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     const float *__restrict__ C = A.C;
     const int d = A.d, K = A.K;
     const int tid = threadIdx.x;
-    const int wv = tid >> 6;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: a scalar
     const int lane = tid & 63;
     const int h = lane >> 5;
     const int jl = lane & 31;

@@ -108,12 +108,13 @@ hipError_t launch_sort_by_key(const int32_t *keys, int64_t N, int K, int32_t *ke
 hipError_t launch_offsets(const int32_t *keys_sorted, int64_t N, int K, int32_t *offsets, hipStream_t s);
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+// acc: add to sums / cnt (rows fed in several batches) instead of writing them
 hipError_t launch_seg_reduce(const float *X, int64_t N, int d, int K, const int32_t *keys_sorted, const int32_t *perm,
-                             const double *xnorm64, double *sums, double *pfirst, double *plast,
+                             const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
                              hipStream_t s);
 hipError_t launch_seg_fixup(const int32_t *keys_sorted, const int32_t *offsets, int64_t N, int d, int K,
-                            const double *pfirst, const double *plast, double *sums, hipStream_t s);
-hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, hipStream_t s);
+                            const double *pfirst, const double *plast, double *sums, bool acc, hipStream_t s);
+hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, bool acc, hipStream_t s);
 hipError_t launch_finalize(const double *sums, const int32_t *cnt, const float *C_prev, int K, int d,
                            float *C_out, int32_t *counts_out, hipStream_t s);
 

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_hist(const int32_t *__re
                                                              int32_t *__restrict__ hist, int ntiles) {
     constexpr int NB = 1 << BITS;
     __shared__ int wcnt[kSortWaves][NB];
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     for (int i = tid; i < kSortWaves * NB; i += kSortThreads) (&wcnt[0][0])[i] = 0;
     __syncthreads();
     const int64_t row0 = (int64_t)blockIdx.x * kSortTile + (int64_t)w * (kSortRows * 64);
@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *_
     __shared__ int gbase[NB];    // global position of each digit's first key of this tile
     __shared__ int skey[kSortTile];
     __shared__ int sval[kSortTile];
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, w = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     for (int i = tid; i < kSortWaves * NB; i += kSortThreads) (&wcnt[0][0])[i] = 0;
     __syncthreads();
     const int64_t tile0 = (int64_t)blockIdx.x * kSortTile;

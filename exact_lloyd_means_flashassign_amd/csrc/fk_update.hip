@@ -31,13 +31,18 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t *__restrict__ p, int
 
 // NV loads of E consecutive floats per lane cover 64*E*NV columns starting at
 // blockIdx.y * 64*E*NV.  U rows are loaded before they are accumulated so that
-// U row reads per lane are in flight at once.
-template <int NV, int E, int U>
+// U row reads per lane are in flight at once.  COS: rows are scaled by
+// 1/xnorm64 (cosine).  ACC: cluster sums are added to what sums holds (rows
+// fed in several batches); otherwise they are written, and the clusters that
+// no row reaches are left untouched (the finalize step does not read them).
+template <int NV, int E, int U, bool COS, bool ACC>
 __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X, int64_t N, int d, int K, int srows,
                                                     const int32_t *__restrict__ ks, const int32_t *__restrict__ perm,
                                                     const double *__restrict__ xnorm64, double *__restrict__ sums,
                                                     double *__restrict__ pfirst, double *__restrict__ plast) {
-    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    // the wave index is uniform across the wave: taking it as a scalar makes
+    // the segment bounds, the keys and every branch on them scalar
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int64_t seg = (int64_t)blockIdx.x * kSegWaves + w;
     const int64_t r0 = seg * srows;
     if (r0 >= N) return;
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
             add = false;
         } else {
             dst = sums + (int64_t)k * d;
-            add = true;
+            add = ACC;
         }
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
@@ -98,61 +103,89 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
         }
     };
 
-    for (int64_t r = r0; r < r1; r += 64) {
-        const int nb = (int)((r1 - r) < 64 ? (r1 - r) : 64);
-        const int kk = lane < nb ? ks[r + lane] : -1;
-        const int pp = lane < nb ? perm[r + lane] : 0;
-        for (int i = 0; i < nb; i += U) {
-            float vals[U][NV][E];
-            int keys[U];
-            double scl[U];
+    // Rows go in windows of 64 (one key and one row index per lane) and
+    // batches of U rows.  The loads of the next batch are issued before the
+    // current one is added, and every load is unconditional (row indices past
+    // the segment repeat its last row, columns past d repeat the last valid
+    // group), so that the wait for a batch never waits on later loads or on
+    // the stores of a flush.
+    static_assert(64 % (2 * U) == 0, "batches must pair up inside a window");
+    constexpr int NBW = 64 / U;  // batches per window
+    auto load_window = [&](int64_t r, int &kk, int &pp) {
+        const int64_t q = (r + lane < r1) ? r + lane : r1 - 1;
+        kk = ks[q];
+        pp = perm[q];
+    };
+    int ccol[NV];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                keys[u] = __builtin_amdgcn_readlane(kk, (i + u) & 63);
-                scl[u] = 1.0;
-                if (i + u < nb) {
-                    const int p = __builtin_amdgcn_readlane(pp, (i + u) & 63);
-                    const float *row = X + (size_t)p * d;
-                    if (xnorm64 != nullptr) scl[u] = 1.0 / xnorm64[p];
+    for (int v = 0; v < NV; ++v) ccol[v] = cok[v] ? col[v] : d - E;
+    auto load_batch = [&](float (&vb)[U][NV][E], double (&sb)[U], int pp, int off) {
 #pragma unroll
-                    for (int v = 0; v < NV; ++v) {
-                        // each row is read once: non-temporal loads keep the
-                        // stream from evicting the sorted keys and the sums
-                        if constexpr (E == 4) {
-                            f4v t = {0.f, 0.f, 0.f, 0.f};
-                            if (cok[v]) t = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(row + col[v]));
-                            vals[u][v][0] = t.x;
-                            vals[u][v][1] = t.y;
-                            vals[u][v][2] = t.z;
-                            vals[u][v][3] = t.w;
-                        } else if constexpr (E == 2) {
-                            f2v t = {0.f, 0.f};
-                            if (cok[v]) t = __builtin_nontemporal_load(reinterpret_cast<const f2v *>(row + col[v]));
-                            vals[u][v][0] = t.x;
-                            vals[u][v][1] = t.y;
-                        } else {
-                            vals[u][v][0] = cok[v] ? __builtin_nontemporal_load(row + col[v]) : 0.f;
-                        }
-                    }
-                }
-            }
+        for (int u = 0; u < U; ++u) {
+            const int p = __builtin_amdgcn_readlane(pp, off + u);
+            const float *row = X + (size_t)p * d;
+            if (COS) sb[u] = 1.0 / xnorm64[p];
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                if (i + u < nb) {
-                    if (keys[u] != cur) {
-                        flush(cur);
-                        cur = keys[u];
-                    }
-#pragma unroll
-                    for (int v = 0; v < NV; ++v)
-#pragma unroll
-                        for (int e = 0; e < E; ++e) {
-                            const double x = (double)vals[u][v][e];
-                            acc[v][e] += (xnorm64 != nullptr) ? x * scl[u] : x;
-                        }
+            for (int v = 0; v < NV; ++v) {
+                // each row is read once: non-temporal loads keep the stream
+                // from evicting the sorted keys and the sums
+                if constexpr (E == 4) {
+                    const f4v t = __builtin_nontemporal_load(reinterpret_cast<const f4v *>(row + ccol[v]));
+                    vb[u][v][0] = t.x;
+                    vb[u][v][1] = t.y;
+                    vb[u][v][2] = t.z;
+                    vb[u][v][3] = t.w;
+                } else if constexpr (E == 2) {
+                    const f2v t = __builtin_nontemporal_load(reinterpret_cast<const f2v *>(row + ccol[v]));
+                    vb[u][v][0] = t.x;
+                    vb[u][v][1] = t.y;
+                } else {
+                    vb[u][v][0] = __builtin_nontemporal_load(row + ccol[v]);
                 }
             }
         }
+    };
+    auto consume = [&](const float (&vb)[U][NV][E], const double (&sb)[U], int kk, int64_t r, int off) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if (r + off + u >= r1) break;
+            const int key = __builtin_amdgcn_readlane(kk, off + u);
+            if (key != cur) {
+                flush(cur);
+                cur = key;
+            }
+            // columns past d add into accumulators that are never written
+#pragma unroll
+            for (int v = 0; v < NV; ++v)
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    const double x = (double)vb[u][v][e];
+                    acc[v][e] += COS ? x * sb[u] : x;
+                }
+        }
+    };
+
+    int kkc, ppc, kkn, ppn;
+    load_window(r0, kkc, ppc);
+    load_window(r0 + 64, kkn, ppn);
+    float va[U][NV][E], vb[U][NV][E];
+    double sa[U], sb[U];
+    load_batch(va, sa, ppc, 0);
+    for (int64_t r = r0; r < r1; r += 64) {
+#pragma unroll
+        for (int j = 0; j < NBW; j += 2) {
+            // even batches sit in va, odd ones in vb
+            load_batch(vb, sb, ppc, (j + 1) * U);
+            consume(va, sa, kkc, r, j * U);
+            if (j + 2 < NBW)
+                load_batch(va, sa, ppc, (j + 2) * U);
+            else
+                load_batch(va, sa, ppn, 0);
+            consume(vb, sb, kkc, r, (j + 1) * U);
+        }
+        kkc = kkn;
+        ppc = ppn;
+        load_window(r + 128, kkn, ppn);
     }
     flush(cur);
 }
@@ -160,15 +193,16 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
 // One workgroup per segment boundary b (between segments b and b+1).  If a
 // cluster k crosses it and b is the first boundary k crosses, the workgroup
 // adds k's partials: plast of k's first segment, then pfirst of every later
-// segment k touches, into sums[k].  Wave w takes the segments sa+1+w,
-// sa+1+w+8, ... in order; the 8 wave sums are added in wave order.
+// segment k touches, into sums[k] (acc) or as sums[k].  Wave w takes the
+// segments sa+1+w, sa+1+w+8, ... in order; the 8 wave sums are added in wave
+// order.
 constexpr int kFixWaves = 8;
 __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__restrict__ ks,
                                                              const int32_t *__restrict__ offsets, int64_t N, int d,
                                                              int K, int srows,
                                                              const double *__restrict__ pfirst,
                                                              const double *__restrict__ plast,
-                                                             double *__restrict__ sums) {
+                                                             double *__restrict__ sums, bool acc) {
     __shared__ double red[kFixWaves][64];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t b = blockIdx.x;
@@ -204,17 +238,18 @@ __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__r
             double t = red[0][lane];
 #pragma unroll
             for (int ww = 1; ww < kFixWaves; ++ww) t += red[ww][lane];
-            sums[(int64_t)k * d + c] += t;
+            double *dst = sums + (int64_t)k * d + c;
+            *dst = acc ? *dst + t : t;
         }
         __syncthreads();
     }
 }
 
-// cnt[k] += size of cluster k in this batch of rows.
+// cnt[k] (+)= size of cluster k in this batch of rows.
 __global__ __launch_bounds__(256) void k_count_acc(const int32_t *__restrict__ offsets, int K,
-                                                   int32_t *__restrict__ cnt) {
+                                                   int32_t *__restrict__ cnt, bool acc) {
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
-    if (k < K) cnt[k] += offsets[k + 1] - offsets[k];
+    if (k < K) cnt[k] = (acc ? cnt[k] : 0) + offsets[k + 1] - offsets[k];
 }
 
 // C_out = sums / cnt, or C_prev for an empty cluster; counts_out = cnt.
@@ -241,49 +276,66 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
 
 template <int NV, int E>
 static hipError_t seg_launch(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
-                             const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
+                             const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
+                             hipStream_t s) {
     constexpr int U = NV * E <= 2 ? 16 : (NV * E <= 8 ? 8 : 4);
     const int srows = seg_rows(N);
     const int64_t nseg = cdiv(N, srows);
-    const unsigned gy = (unsigned)cdiv(d, 64 * E * NV);
-    hipLaunchKernelGGL((k_seg_reduce<NV, E, U>), dim3((unsigned)cdiv(nseg, kSegWaves), gy), dim3(kSegWaves * 64), 0,
-                       s, X, N, d, K, srows, ks, perm, xnorm64, sums, pfirst, plast);
+    const dim3 grid((unsigned)cdiv(nseg, kSegWaves), (unsigned)cdiv(d, 64 * E * NV));
+    const dim3 block(kSegWaves * 64);
+    if (xnorm64 != nullptr) {
+        if (acc)
+            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, true, true>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
+                               xnorm64, sums, pfirst, plast);
+        else
+            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, true, false>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
+                               xnorm64, sums, pfirst, plast);
+    } else {
+        if (acc)
+            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, false, true>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
+                               xnorm64, sums, pfirst, plast);
+        else
+            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, false, false>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
+                               xnorm64, sums, pfirst, plast);
+    }
     return hipGetLastError();
 }
 
 template <int E>
 static hipError_t seg_launch_e(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
-                               const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
+                               const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
+                               hipStream_t s) {
     const int need = (int)cdiv(d, 64 * E);
-    if (need <= 1) return seg_launch<1, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
-    if (need <= 2) return seg_launch<2, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
-    if (need <= 3) return seg_launch<3, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
-    return seg_launch<4, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (need <= 1) return seg_launch<1, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
+    if (need <= 2) return seg_launch<2, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
+    if (need <= 3) return seg_launch<3, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
+    return seg_launch<4, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
 }
 
 // Row loads of E floats per lane: float4 when a row spans at least 256
 // floats, float2 from 128, scalar otherwise (or when d is not a multiple);
 // column blocks of up to 4 loads per lane, more blocks on blockIdx.y.
 hipError_t launch_seg_reduce(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
-                             const double *xnorm64, double *sums, double *pfirst, double *plast, hipStream_t s) {
+                             const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
+                             hipStream_t s) {
     if (N <= 0) return hipSuccess;
-    if (d % 4 == 0 && d >= 256) return seg_launch_e<4>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
-    if (d % 2 == 0 && d >= 128) return seg_launch_e<2>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
-    return seg_launch_e<1>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, s);
+    if (d % 4 == 0 && d >= 256) return seg_launch_e<4>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
+    if (d % 2 == 0 && d >= 128) return seg_launch_e<2>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
+    return seg_launch_e<1>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
 }
 
 hipError_t launch_seg_fixup(const int32_t *ks, const int32_t *offsets, int64_t N, int d, int K, const double *pfirst,
-                            const double *plast, double *sums, hipStream_t s) {
+                            const double *plast, double *sums, bool acc, hipStream_t s) {
     const int srows = seg_rows(N);
     const int64_t nseg = cdiv(N, srows);
     if (nseg <= 1) return hipSuccess;
     hipLaunchKernelGGL(k_seg_fixup, dim3((unsigned)(nseg - 1)), dim3(kFixWaves * 64), 0, s, ks, offsets, N, d, K,
-                       srows, pfirst, plast, sums);
+                       srows, pfirst, plast, sums, acc);
     return hipGetLastError();
 }
 
-hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, hipStream_t s) {
-    hipLaunchKernelGGL(k_count_acc, dim3((unsigned)cdiv(K, 256)), dim3(256), 0, s, offsets, K, cnt);
+hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, bool acc, hipStream_t s) {
+    hipLaunchKernelGGL(k_count_acc, dim3((unsigned)cdiv(K, 256)), dim3(256), 0, s, offsets, K, cnt, acc);
     return hipGetLastError();
 }
 
