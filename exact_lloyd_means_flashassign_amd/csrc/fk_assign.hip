@@ -49,6 +49,8 @@ struct FlashArgs {
     int64_t cap_slots;   // collect mode: slots with candidate storage
     const __bf16 *Cs;    // split scoring: per centroid row, w bf16 high parts then
     int sw;              // w bf16 low parts (C - high, rounded); Kpad rows
+    const __bf16 *ncs;   // split scoring: -||c||^2/2 as three bf16 parts + 5 zeros
+    unsigned cs_bytes;   // size of the split copy
 };
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -95,7 +97,7 @@ __global__ __launch_bounds__(256) void k_normalize_rows(const float *__restrict_
 // per centroid row.
 __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__ C, int K, int Kpad, int d,
                                                        float *__restrict__ ncn, float *__restrict__ cmax_part,
-                                                       __bf16 *__restrict__ cs, int w) {
+                                                       __bf16 *__restrict__ cs, int w, __bf16 *__restrict__ ncs) {
     __shared__ float wmax[3][4];
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int k = blockIdx.x * 4 + wv;
@@ -137,6 +139,22 @@ __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__
             ncn[k] = -0.5f * cn;
         else if (k < Kpad)
             ncn[k] = -INFINITY;
+        if (ncs != nullptr && k < Kpad) {
+            // -||c||^2/2 = p0 + p1 + p2 exactly: each part takes the next 8
+            // significant bits of what is left (24 in all).  Rows past K get
+            // -2^127, finite so that the MFMA against the zero k-slots stays
+            // finite, and below any real score.
+            const float v = k < K ? -0.5f * cn : -1.7014118e38f;
+            const __bf16 p0 = (__bf16)v;
+            const float r1 = v - (float)p0;
+            const __bf16 p1 = (__bf16)r1;
+            const __bf16 p2 = (__bf16)(r1 - (float)p1);
+            __bf16 *o = ncs + (size_t)k * 8;
+            o[0] = p0;
+            o[1] = p1;
+            o[2] = p2;
+            for (int e = 3; e < 8; ++e) o[e] = (__bf16)0.0f;
+        }
         wmax[0][wv] = cn;
         wmax[1][wv] = dn;
         wmax[2][wv] = rn;
@@ -222,11 +240,18 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     constexpr int BM = WAVES * PB * 32;  // points per workgroup pass
     static_assert(HALF % 4 == 0, "DP must be a multiple of 8");
     static_assert(!SPLIT || DP % 16 == 0, "split scoring needs DP a multiple of 16");
+    // Split scoring with resident points runs each tile in phases on one
+    // accumulator: the two cross terms from zero, then -||c||^2/2 (as an
+    // exact sum of three bf16 parts, through one MFMA against ones), then
+    // the hi.hi products.  Chunked points keep the cross terms in a second
+    // accumulator instead (the phases would span chunks).
+    constexpr bool PHASED = SPLIT && RES;
 
     __shared__ __attribute__((aligned(16))) float sC[2][SPLIT ? 4 : ROWS * LDR];
     __shared__ __attribute__((aligned(16))) __bf16 sCh[2][SPLIT ? ROWS * LDB : 8];
     __shared__ __attribute__((aligned(16))) __bf16 sCl[2][SPLIT ? ROWS * LDB : 8];
-    __shared__ __attribute__((aligned(16))) float sN[2][ROWS];
+    __shared__ __attribute__((aligned(16))) float sN[2][PHASED ? 4 : ROWS];
+    __shared__ __attribute__((aligned(16))) float4 sNs[2][PHASED ? ROWS : 1];
 
     const float *__restrict__ X = A.X;
     const float *__restrict__ C = A.C;
@@ -236,6 +261,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     const int lane = tid & 63;
     const int h = lane >> 5;
     const int jl = lane & 31;
+
+    // buffer resource of the split centroid copy (raw, byte-addressed,
+    // loads past its end read zero)
+    const __amdgpu_buffer_rsrc_t cs_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)A.Cs, (short)0, SPLIT ? (int)A.cs_bytes : 0, 0x00020000);
 
     // Assign mode: workgroup g takes points [g*BM, (g+1)*BM).  Collect mode:
     // the workgroups stride over slots of the full near-tie list.
@@ -248,20 +278,23 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         float4 pf[PFN];
         float4 pfh[PFS], pfl[PFS];
         float pn = 0.f;
+        float4 pns = make_float4(0.f, 0.f, 0.f, 0.f);
         auto load_stage = [&](int t, int ch) {
             if constexpr (SPLIT) {
                 // the split copy has Kpad zero-padded rows of sw >= DP * nch
-                // dims, so a whole stage is in bounds; one uniform tile base
-                // serves both halves
-                const __bf16 *tb = A.Cs + (size_t)t * ROWS * (2 * A.sw) + ch * DP;
+                // dims, so a whole stage is in bounds.  Buffer loads: the
+                // lane's byte offset in the tile stays in one VGPR per load
+                // slot, the tile (and the low half) offsets are scalars.
+                const unsigned tile_b = (unsigned)t * ROWS * (4u * A.sw) + ch * DP * 2u;
 #pragma unroll
                 for (int i = 0; i < PFS; ++i) {
                     const int q = tid + i * NT;
                     float4 vh = make_float4(0.f, 0.f, 0.f, 0.f), vl = vh;
                     if (NQ8 % NT == 0 || q < NQ8) {
-                        const unsigned o = (unsigned)((q / Q8) * (2 * A.sw) + (q % Q8) * 8);
-                        vh = *reinterpret_cast<const float4 *>(tb + o);
-                        vl = *reinterpret_cast<const float4 *>(tb + o + A.sw);
+                        const unsigned o = (unsigned)((q / Q8) * (4 * A.sw) + (q % Q8) * 16);
+                        vh = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(cs_rsrc, o, tile_b, 0));
+                        vl = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(cs_rsrc, o,
+                                                                                              tile_b + 2u * A.sw, 0));
                     }
                     pfh[i] = vh;
                     pfl[i] = vl;
@@ -290,7 +323,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     pf[i] = v;
                 }
             }
-            if (ch == 0 && tid < ROWS) pn = A.ncn[t * ROWS + tid];
+            if (PHASED) {
+                if (tid < ROWS) pns = *reinterpret_cast<const float4 *>(A.ncs + (size_t)(t * ROWS + tid) * 8);
+            } else if (ch == 0 && tid < ROWS) {
+                pn = A.ncn[t * ROWS + tid];
+            }
         };
         // registers -> LDS buffer
         auto store_stage = [&](int buf, int ch) {
@@ -311,7 +348,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     if (q < NQ4) *reinterpret_cast<float4 *>(&sC[buf][(q / Q4) * LDR + (q % Q4) * 4]) = pf[i];
                 }
             }
-            if (ch == 0 && tid < ROWS) sN[buf][tid] = pn;
+            if (PHASED) {
+                if (tid < ROWS) sNs[buf][tid] = pns;
+            } else if (ch == 0 && tid < ROWS) {
+                sN[buf][tid] = pn;
+            }
         };
 
         float xr[PB][SPLIT ? 1 : HALF];
@@ -467,8 +508,47 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         // acc: -||c||^2/2 + the fp32 (or hi.hi) products; split scoring keeps
         // the two small cross terms in a second accumulator (acl) that is
         // added once per tile, so that they pass through few roundings
-        v16f acc[PB][CB];
-        v16f acl[PB][SPLIT ? CB : 1];
+        // phased split scoring computes its centroid blocks one after another
+        // (each with its epilogue), so one accumulator per point block serves
+        v16f acc[PB][PHASED ? 1 : CB];
+        v16f acl[PB][SPLIT && !PHASED ? CB : 1];
+
+        // Fold one 32-centroid block of scores (a) of point block b, centroid
+        // indices kb + 8(r/4) + r%4, into this lane's state.
+        auto epilogue = [&](const v16f &a, int b, int kb) {
+            // A value changes this lane's state only if it beats the third
+            // best (top-3) or reaches the threshold (collect).  Late in the
+            // sweep most 16-value groups change no lane of the wave; they are
+            // skipped with one wave vote.
+            bool any = false;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) any |= COLLECT ? (a[r] >= b1[b]) : (a[r] > b3[b]);
+            if (__ballot(any) == 0ull) return;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float v = a[r];
+                const int k = kb + 8 * (r >> 2) + (r & 3);
+                if (COLLECT) {
+                    // every centroid within the window may win
+                    if (v >= b1[b]) {
+                        if (i1[b] < kMaxCand) A.cand[((sbase + b * 32 + jl) * 2 + h) * kMaxCand + i1[b]] = k;
+                        ++i1[b];
+                    }
+                } else {
+                    // insert v into the sorted top-3 with medians of three
+                    // (v_med3_f32); a strict '>' keeps the lower index first on
+                    // equal scores (k increases per lane)
+                    const bool c1 = v > b1[b];
+                    const bool c2 = v > b2[b];
+                    const int t2 = c2 ? k : i2[b];
+                    i2[b] = c1 ? i1[b] : t2;
+                    i1[b] = c1 ? k : i1[b];
+                    b3[b] = __builtin_amdgcn_fmed3f(b2[b], b3[b], v);
+                    b2[b] = __builtin_amdgcn_fmed3f(b1[b], b2[b], v);
+                    b1[b] = c1 ? v : b1[b];
+                }
+            }
+        };
         const int cnch = RES ? 1 : A.nch;
         const int nst = A.ntiles * cnch;
         if (RES) {
@@ -493,7 +573,8 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             if (!RES) load_x(ch, t == 0);
             if (more) load_stage(nt, nc);
 
-            if (ch == 0) {
+            if constexpr (!PHASED) {
+              if (ch == 0) {
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
 #pragma unroll
@@ -510,9 +591,69 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                         }
                     }
                 }
+              }
             }
 
-            if constexpr (SPLIT) {
+            if constexpr (PHASED) {
+                const __bf16 *sh = &sCh[buf][jl * LDB + 8 * h];
+                const __bf16 *sl = &sCl[buf][jl * LDB + 8 * h];
+                // B operand of the -||c||^2/2 step: ones in k-slots 0..2
+                v8bf ones;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ones[e] = (h == 0 && e < 3) ? (__bf16)1.0f : (__bf16)0.0f;
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+                    // phase 1: lo.hi + hi.lo, from zero; each step's LDS
+                    // operands are read one step ahead
+                    v8bf ah = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB);
+                    v8bf al = *reinterpret_cast<const v8bf *>(sl + cb * 32 * LDB);
+#pragma unroll
+                    for (int st = 0; st < NS; ++st) {
+                        v8bf ahn = ah, aln = al;
+                        if (st + 1 < NS) {
+                            ahn = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB + 16 * (st + 1));
+                            aln = *reinterpret_cast<const v8bf *>(sl + cb * 32 * LDB + 16 * (st + 1));
+                        }
+#pragma unroll
+                        for (int b = 0; b < PB; ++b) {
+                            const v16f c0 = {};
+                            acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh[b][st], st == 0 ? c0 : acc[b][0],
+                                                                                0, 0, 0);
+                            acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[b][st], acc[b][0], 0, 0, 0);
+                        }
+                        ah = ahn;
+                        al = aln;
+                    }
+                    // phase 2: + (p0 + p1 + p2) of -||c||^2/2, its exact fp32 value
+                    {
+                        const float4 nr = sNs[buf][cb * 32 + jl];
+                        const v8bf an = *reinterpret_cast<const v8bf *>(&nr);
+#pragma unroll
+                        for (int b = 0; b < PB; ++b)
+                            acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(an, ones, acc[b][0], 0, 0, 0);
+                    }
+                    // phase 3: hi.hi (the high parts are read from LDS again:
+                    // the empty asm keeps the compiler from holding the phase-1
+                    // reads in registers)
+                    asm volatile("" ::: "memory");
+                    v8bf ah3 = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB);
+#pragma unroll
+                    for (int st = 0; st < NS; ++st) {
+                        v8bf ahn = ah3;
+                        if (st + 1 < NS) ahn = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB + 16 * (st + 1));
+#pragma unroll
+                        for (int b = 0; b < PB; ++b)
+                            acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah3, xh[b][st], acc[b][0], 0, 0, 0);
+                        ah3 = ahn;
+                    }
+#pragma unroll
+                    for (int b = 0; b < PB; ++b) epilogue(acc[b][0], b, t * ROWS + cb * 32 + 4 * h);
+                    // the next stage goes to the other LDS buffer (which no
+                    // wave reads during this tile) once the first block is
+                    // done, so the prefetch registers are free for the rest
+                    if (CB > 1 && cb == 0 && more) store_stage(buf ^ 1, nc);
+                }
+            } else if constexpr (SPLIT) {
                 // x.c ~ hi.hi + (hi.lo + lo.hi)
                 const __bf16 *sh = &sCh[buf][jl * LDB + 8 * h];
                 const __bf16 *sl = &sCl[buf][jl * LDB + 8 * h];
@@ -554,51 +695,19 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 }
             }
 
-            if (ch == cnch - 1) {
-                const int kt = t * ROWS + 4 * h;
+            if constexpr (!PHASED) {
+                if (ch == cnch - 1) {
 #pragma unroll
-                for (int b = 0; b < PB; ++b) {
+                    for (int b = 0; b < PB; ++b) {
 #pragma unroll
-                    for (int cb = 0; cb < CB; ++cb) {
-                        if constexpr (SPLIT) acc[b][cb] += acl[b][cb];
-                        // A value changes this lane's state only if it beats the
-                        // third best (top-3) or reaches the threshold (collect).
-                        // Late in the sweep most 16-value groups change no lane
-                        // of the wave; they are skipped with one wave vote.
-                        bool any = false;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r)
-                            any |= COLLECT ? (acc[b][cb][r] >= b1[b]) : (acc[b][cb][r] > b3[b]);
-                        if (__ballot(any) == 0ull) continue;
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const float v = acc[b][cb][r];
-                            const int k = kt + cb * 32 + 8 * (r >> 2) + (r & 3);
-                            if (COLLECT) {
-                                // every centroid within the window may win
-                                if (v >= b1[b]) {
-                                    if (i1[b] < kMaxCand)
-                                        A.cand[((sbase + b * 32 + jl) * 2 + h) * kMaxCand + i1[b]] = k;
-                                    ++i1[b];
-                                }
-                            } else {
-                                // insert v into the sorted top-3 with medians of
-                                // three (v_med3_f32); a strict '>' keeps the lower
-                                // index first on equal scores (k increases per lane)
-                                const bool c1 = v > b1[b];
-                                const bool c2 = v > b2[b];
-                                const int t2 = c2 ? k : i2[b];
-                                i2[b] = c1 ? i1[b] : t2;
-                                i1[b] = c1 ? k : i1[b];
-                                b3[b] = __builtin_amdgcn_fmed3f(b2[b], b3[b], v);
-                                b2[b] = __builtin_amdgcn_fmed3f(b1[b], b2[b], v);
-                                b1[b] = c1 ? v : b1[b];
-                            }
+                        for (int cb = 0; cb < CB; ++cb) {
+                            if constexpr (SPLIT) acc[b][cb] += acl[b][cb];
+                            epilogue(acc[b][cb], b, t * ROWS + cb * 32 + 4 * h);
                         }
                     }
                 }
             }
-            if (more) store_stage(buf ^ 1, nc);
+            if (!(PHASED && CB > 1) && more) store_stage(buf ^ 1, nc);
             __syncthreads();
             t = nt;
             ch = nc;
@@ -930,7 +1039,8 @@ hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float 
     const int Kpad = (int)(cdiv(K, kCentroidPad) * kCentroidPad);
     const int nb = (int)cdiv(Kpad, 4);
     *nparts = nb;
-    hipLaunchKernelGGL(k_centroid_prep, dim3(nb), dim3(256), 0, s, C, K, Kpad, d, ncn, cmax_part, sc.cs, sc.w);
+    hipLaunchKernelGGL(k_centroid_prep, dim3(nb), dim3(256), 0, s, C, K, Kpad, d, ncn, cmax_part, sc.cs, sc.w,
+                       sc.ncs);
     return hipGetLastError();
 }
 
@@ -973,7 +1083,7 @@ static hipError_t launch_fa_shape(const FlashArgs &A, hipStream_t s) {
         // split scoring: 8 waves of 2 point blocks (a few values of the
         // prologue spill; the tile loop does not)
         if constexpr (SPLIT)
-            return launch_fa<128, 2, 1, 8, 2, true, COLLECT, SPLIT>(A, s);
+            return launch_fa<128, 2, 2, 8, 2, true, COLLECT, SPLIT>(A, s);
         else
             return launch_fa<128, 2, 1, 4, 2, true, COLLECT, SPLIT>(A, s);
     }
@@ -1010,6 +1120,8 @@ static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, co
     A.cap_slots = near_tie_cap(N);
     A.Cs = sc.cs;
     A.sw = sc.w;
+    A.ncs = sc.ncs;
+    A.cs_bytes = (unsigned)(cdiv(K, kCentroidPad) * kCentroidPad * 4 * (int64_t)sc.w);
     return A;
 }
 
