@@ -293,12 +293,13 @@ fk_status step_sort(const Ctx &c, const int32_t *a, int64_t rows, int32_t *perm_
     return FK_OK;
 }
 
-// Counts start at zero (so that no rows give empty clusters); the fp64 sums
-// only need it when several batches of rows are added into them.
-fk_status step_zero_accumulators(const Ctx &c, bool batches) {
+// Accumulators for rows fed in several batches start at zero.  A single batch
+// writes the sums and takes the counts from the offsets, so only an empty
+// batch needs zero counts.
+fk_status step_zero_accumulators(const Ctx &c, bool batches, int64_t rows) {
     PhaseScope ph(FK_PH_REDUCE, c.s);
     if (batches) FK_TRY(launch_fill_zero(at<void>(c.ws, c.L.sums), (size_t)c.K * c.d * 8, c.s), "zero sums");
-    FK_TRY(launch_fill_zero(at<void>(c.ws, c.L.cnt), (size_t)c.K * 4, c.s), "zero counts");
+    if (batches || rows <= 0) FK_TRY(launch_fill_zero(at<void>(c.ws, c.L.cnt), (size_t)c.K * 4, c.s), "zero counts");
     return FK_OK;
 }
 
@@ -318,14 +319,17 @@ fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int3
                             at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast), at<double>(c.ws, c.L.sums),
                             batches, c.s),
            "segment fix-up");
-    FK_TRY(launch_count_accumulate(at<int32_t>(c.ws, c.L.offsets), c.K, at<int32_t>(c.ws, c.L.cnt), batches, c.s),
-           "count accumulate");
+    if (batches)
+        FK_TRY(launch_count_accumulate(at<int32_t>(c.ws, c.L.offsets), c.K, at<int32_t>(c.ws, c.L.cnt), true, c.s),
+               "count accumulate");
     return FK_OK;
 }
 
-fk_status step_finalize(const Ctx &c, const float *C_prev, float *C_out, int32_t *counts) {
+// one_batch: the rows came in a single non-empty batch (counts from offsets)
+fk_status step_finalize(const Ctx &c, const float *C_prev, float *C_out, int32_t *counts, bool one_batch) {
     PhaseScope ph(FK_PH_FINALIZE, c.s);
-    FK_TRY(launch_finalize(at<double>(c.ws, c.L.sums), at<int32_t>(c.ws, c.L.cnt), C_prev, c.K, c.d, C_out, counts,
+    FK_TRY(launch_finalize(at<double>(c.ws, c.L.sums), at<int32_t>(c.ws, c.L.cnt),
+                           one_batch ? at<int32_t>(c.ws, c.L.offsets) : nullptr, C_prev, c.K, c.d, C_out, counts,
                            c.s),
            "finalize");
     return FK_OK;
@@ -420,10 +424,10 @@ fk_status fk_update(const float *X, int64_t N, int32_t d, const int32_t *assign,
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
     const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, FK_SCORE_FP32};
-    if ((st = step_zero_accumulators(c, false)) != FK_OK) return st;
+    if ((st = step_zero_accumulators(c, false, N)) != FK_OK) return st;
     if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
     if ((st = step_accumulate(c, X, N, assign, false)) != FK_OK) return st;
-    return step_finalize(c, C_prev, C_out, counts);
+    return step_finalize(c, C_prev, C_out, counts, N > 0);
 }
 
 fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in, int32_t K, int32_t metric,
@@ -441,7 +445,7 @@ fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in,
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
     const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
-    if ((st = step_zero_accumulators(c, false)) != FK_OK) return st;
+    if ((st = step_zero_accumulators(c, false, N)) != FK_OK) return st;
     if (N > 0) {
         const float *Cu = nullptr;
         if ((st = step_prep(c, C_in, &Cu)) != FK_OK) return st;
@@ -449,7 +453,7 @@ fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in,
         if ((st = step_assign(c, X, N, C_in, Cu, assign, min_dist)) != FK_OK) return st;
         if ((st = step_accumulate(c, X, N, assign, false)) != FK_OK) return st;
     }
-    return step_finalize(c, C_in, C_out, counts);
+    return step_finalize(c, C_in, C_out, counts, N > 0);
 }
 
 // Library-owned copy stream and events for the out-of-core pipeline (one set
@@ -523,7 +527,7 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
     if ((st = ooc_resources(&R)) != FK_OK) return st;
 
     const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
-    if ((st = step_zero_accumulators(c, true)) != FK_OK) return st;
+    if ((st = step_zero_accumulators(c, true, N)) != FK_OK) return st;
     const float *Cu = nullptr;
     if (N > 0 && (st = step_prep(c, C_in, &Cu)) != FK_OK) return st;
     // the copy stream may not touch the chunk buffers before the work already
@@ -556,7 +560,7 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
             FK_TRY(hipMemcpyAsync(assign_host + r0, ad, (size_t)rows * 4, hipMemcpyDeviceToHost, c.s),
                    "assignment copy");
     }
-    return step_finalize(c, C_in, C_out, counts);
+    return step_finalize(c, C_in, C_out, counts, false);
 }
 
 fk_status fk_profile_enable(int32_t on) {

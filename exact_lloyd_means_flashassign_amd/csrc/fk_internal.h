@@ -116,7 +116,8 @@ hipError_t launch_seg_reduce(const float *X, int64_t N, int d, int K, const int3
 hipError_t launch_seg_fixup(const int32_t *keys_sorted, const int32_t *offsets, int64_t N, int d, int K,
                             const double *pfirst, const double *plast, double *sums, bool acc, hipStream_t s);
 hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, bool acc, hipStream_t s);
-hipError_t launch_finalize(const double *sums, const int32_t *cnt, const float *C_prev, int K, int d,
-                           float *C_out, int32_t *counts_out, hipStream_t s);
+// counts from cnt, or (offsets != nullptr, rows in one batch) from the offsets
+hipError_t launch_finalize(const double *sums, const int32_t *cnt, const int32_t *offsets, const float *C_prev, int K,
+                           int d, float *C_out, int32_t *counts_out, hipStream_t s);
 
 }  // namespace fk

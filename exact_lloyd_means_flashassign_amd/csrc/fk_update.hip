@@ -252,14 +252,16 @@ __global__ __launch_bounds__(256) void k_count_acc(const int32_t *__restrict__ o
     if (k < K) cnt[k] = (acc ? cnt[k] : 0) + offsets[k + 1] - offsets[k];
 }
 
-// C_out = sums / cnt, or C_prev for an empty cluster; counts_out = cnt.
+// C_out = sums / n_k, or C_prev for an empty cluster; counts_out = n_k, with
+// n_k = cnt[k], or offsets[k+1] - offsets[k] when the rows came in one batch.
 __global__ __launch_bounds__(256) void k_finalize(const double *__restrict__ sums, const int32_t *__restrict__ cnt,
+                                                  const int32_t *__restrict__ offsets,
                                                   const float *__restrict__ C_prev, int64_t total, int d,
                                                   float *__restrict__ C_out, int32_t *__restrict__ counts_out) {
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= total) return;
     const int64_t k = q / d;
-    const int c = cnt[k];
+    const int c = offsets != nullptr ? offsets[k + 1] - offsets[k] : cnt[k];
     C_out[q] = c > 0 ? (float)(sums[q] / (double)c) : C_prev[q];
     if (q == k * d) counts_out[k] = c;
 }
@@ -339,11 +341,11 @@ hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, 
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const double *sums, const int32_t *cnt, const float *C_prev, int K, int d, float *C_out,
-                           int32_t *counts_out, hipStream_t s) {
+hipError_t launch_finalize(const double *sums, const int32_t *cnt, const int32_t *offsets, const float *C_prev, int K,
+                           int d, float *C_out, int32_t *counts_out, hipStream_t s) {
     const int64_t total = (int64_t)K * d;
-    hipLaunchKernelGGL(k_finalize, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, sums, cnt, C_prev, total, d,
-                       C_out, counts_out);
+    hipLaunchKernelGGL(k_finalize, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, sums, cnt, offsets, C_prev, total,
+                       d, C_out, counts_out);
     return hipGetLastError();
 }
 
