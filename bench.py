@@ -84,6 +84,75 @@ def cpu_baseline(w, X, C, budget_s=15.0):
                       f"seconds per iteration scaled linearly by N/{n}"}
 
 
+IVF_BUILD_H200_S = 10.6  # the LEANN FlashLib guide's build time at this shape (NVIDIA H200), context only
+
+
+def ivf_build_bench(args, fk, synth, np, torch):
+    """Seconds per IVF-Flat build (quantizer: niter = 20 Lloyd iterations from
+    seeded initial rows, then the cell-contiguous lists) at the shape of the
+    FlashLib guide's build measurement: 1M x 768 unit rows, nlist = 4096."""
+    w = synth.WORKLOADS["ivf_1m_d768_k4096"]
+    n_iter = 20
+    dev = torch.device("cuda:0")
+    t0 = time.perf_counter()
+    X = synth.rows(w)
+    init = synth.init_indices(w).astype(np.int32)
+    log(f"generated {w.name}: N={w.N} d={w.d} nlist={w.K} in {time.perf_counter() - t0:.1f} s")
+    Xd = torch.from_numpy(X).to(dev)
+    ws = torch.empty(fk.fk_ivf_workspace_size(w.N, w.d, w.K, w.metric) + 256, dtype=torch.uint8, device=dev)
+
+    def run(score):
+        for i in range(args.warmup):
+            fk.fk_ivf_build(Xd, w.K, init, n_iter=n_iter, metric=w.metric, workspace=ws, score=score)
+        torch.cuda.synchronize()
+        fk.fk_profile_enable(True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            out = fk.fk_ivf_build(Xd, w.K, init, n_iter=n_iter, metric=w.metric, workspace=ws, score=score)
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) / args.steps
+        prof = fk.fk_profile_read()
+        fk.fk_profile_enable(False)
+        assert int(out["offsets"][-1].item()) == w.N
+        log(f"{score}: {el:.3f} s per build")
+        return {"s_per_build": el,
+                "phase_ms_per_build": {k: round(v / args.steps, 3) for k, v in prof["ms"].items()},
+                "s_per_iteration": el / (n_iter + 1)}
+
+    r = run(args.score)
+    out = {"metric": "s per IVF-Flat build (1M x 768, nlist 4096, niter 20)", "value": r["s_per_build"], "unit": "s",
+           "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": 1e3 * r["s_per_build"],
+           "higher_is_better": False, "scaling": "weak", "vs_baseline": r["s_per_build"] / IVF_BUILD_H200_S,
+           "dtype": SCORES[args.score]["dtype"], "data": "synthetic",
+           "config": {"workload": w.name, "N": w.N, "d": w.d, "nlist": w.K, "niter": n_iter, "metric": w.metric,
+                      "seed": w.seed, "score": args.score},
+           "phase_ms_per_build": r["phase_ms_per_build"],
+           "baseline_context": f"{IVF_BUILD_H200_S} s on an NVIDIA H200 (FlashLib), 140.7 s FAISS CPU, as the "
+                               "LEANN FlashLib guide reports; other hardware"}
+    if not args.no_compare:
+        out["other_scores"] = {o: run(o) for o in SCORES if o != args.score}
+    if not args.no_cpu_baseline:
+        import oracle
+        C0 = X[init]
+        probe = 256
+        t0 = time.perf_counter()
+        oracle.lloyd_iter(X[:probe], C0)
+        dt = time.perf_counter() - t0
+        n = int(min(w.N, max(probe, 15.0 / max(dt, 1e-9) * probe)))
+        t0 = time.perf_counter()
+        oracle.lloyd_iter(X[:n], C0)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": dt * w.N / n * (n_iter + 1), "unit": "s", "cores": oracle.num_threads(),
+                               "kind": "oracle",
+                               "sample": f"one oracle iteration on the first {n} of {w.N} rows against the {w.K} "
+                                         f"initial centroids in {dt:.1f} s, scaled by N/{n} and by {n_iter + 1} "
+                                         "(the iterations plus the final assignment)"}
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -94,6 +163,8 @@ def main():
                     help="FlashAssign scoring: bf16 MFMA on split operands, or fp32 MFMA (same exact result)")
     ap.add_argument("--no-compare", action="store_true", help="do not also time the other scoring mode")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ivf-build", action="store_true",
+                    help="instead: time the IVF-Flat build (1,000,000 x 768, nlist 4096, niter 20, seed 0)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference kernel that scales the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -120,6 +191,8 @@ def main():
         return
 
     fk.load()
+    if args.ivf_build:
+        return ivf_build_bench(args, fk, synth, np, torch)
     w = synth.WORKLOADS[args.workload]
     if w.chunk_rows:
         raise SystemExit("the out-of-core workload is not a bench line; use the in-core workloads")

@@ -63,8 +63,14 @@ def load():
     lib.fk_update.argtypes = [P, I64, I32, P, I32, I32, P, P, P, P, SZ, P]
     lib.fk_lloyd_iter.argtypes = [P, I64, I32, P, I32, I32, I32, P, P, P, P, P, SZ, P]
     lib.fk_lloyd_iter_stream.argtypes = [P, I64, I32, P, I32, I32, I32, I64, P, P, P, P, SZ, P]
+    lib.fk_fit_workspace_size.argtypes = [I64, I32, I32, I32]
+    lib.fk_fit_workspace_size.restype = SZ
+    lib.fk_fit.argtypes = [P, I64, I32, P, I32, I32, I32, I32, P, P, P, P, SZ, P]
+    lib.fk_ivf_workspace_size.argtypes = [I64, I32, I32, I32]
+    lib.fk_ivf_workspace_size.restype = SZ
+    lib.fk_ivf_build.argtypes = [P, I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]
     for f in ("fk_assign", "fk_sort_inverse", "fk_update", "fk_lloyd_iter", "fk_lloyd_iter_stream",
-              "fk_profile_enable", "fk_profile_read"):
+              "fk_fit", "fk_ivf_build", "fk_profile_enable", "fk_profile_read"):
         getattr(lib, f).restype = ctypes.c_int
     lib.fk_status_str.argtypes = [I32]
     lib.fk_status_str.restype = ctypes.c_char_p
@@ -291,6 +297,74 @@ def fk_lloyd_iter_stream(X_host, C_in, chunk_rows: int, metric="l2", assign_host
                                        int(chunk_rows), _ptr(assign_host), _ptr(C_out), _ptr(counts), ws, wsn,
                                        _stream(C_in.device)))
     return C_out, counts
+
+
+def fk_fit_workspace_size(N: int, d: int, K: int, metric="l2") -> int:
+    n = load().fk_fit_workspace_size(int(N), int(d), int(K), _metric(metric))
+    if n == 0:
+        raise FkError(1, f"sizes outside the limits: N={N} d={d} K={K}")
+    return int(n)
+
+
+def fk_fit(X, C_init, n_iter: int, metric="l2", assign=None, C_out=None, counts=None, workspace=None,
+           score="fp32"):
+    """Lloyd k-means, n_iter iterations from C_init: returns (C_out, assign, counts)
+    (assign and counts are those of the last iteration)."""
+    _dev(X, "X", torch.float32)
+    _dev(C_init, "C_init", torch.float32)
+    if X.dim() != 2 or C_init.dim() != 2 or X.shape[1] != C_init.shape[1]:
+        raise ValueError("X[N,d] and C[K,d] must be 2-D with the same d")
+    N, d = X.shape
+    K = C_init.shape[0]
+    if assign is None:
+        assign = torch.empty(N, dtype=torch.int32, device=X.device)
+    if C_out is None:
+        C_out = torch.empty_like(C_init)
+    if counts is None:
+        counts = torch.empty(K, dtype=torch.int32, device=X.device)
+    _dev(assign, "assign", torch.int32, (N,))
+    _dev(C_out, "C_out", torch.float32, (K, d))
+    _dev(counts, "counts", torch.int32, (K,))
+    need = load().fk_fit_workspace_size(int(N), int(d), int(K), _metric(metric)) or 256
+    p, n = _workspace(need, X.device, workspace)
+    _check(load().fk_fit(_ptr(X), N, d, _ptr(C_init), K, _metric(metric), _score(score), int(n_iter), _ptr(C_out),
+                         _ptr(assign), _ptr(counts), ctypes.c_void_p(p), ctypes.c_size_t(n), _stream(X.device)))
+    return C_out, assign, counts
+
+
+def fk_ivf_workspace_size(N: int, d: int, nlist: int, metric="l2") -> int:
+    n = load().fk_ivf_workspace_size(int(N), int(d), int(nlist), _metric(metric))
+    if n == 0:
+        raise FkError(1, f"sizes outside the limits: N={N} d={d} nlist={nlist}")
+    return int(n)
+
+
+def fk_ivf_build(X, nlist: int, init_idx, n_iter: int = 20, metric="l2", workspace=None, score="fp32"):
+    """IVF-Flat build: returns a dict with centroids [nlist', d], offsets
+    [nlist'+1], ids [N] and data [N, d] (rows grouped by cell), where nlist' =
+    min(nlist, N) as the FlashLib guide clamps it; init_idx holds the
+    quantizer's initial rows (at least nlist' of them, host ints)."""
+    import numpy as np
+    _dev(X, "X", torch.float32)
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
+    N, d = X.shape
+    nl = min(int(nlist), int(N))
+    idx = np.ascontiguousarray(np.asarray(init_idx, dtype=np.int32)[:nl])
+    if idx.shape[0] != nl:
+        raise ValueError(f"init_idx has {idx.shape[0]} entries, {nl} needed")
+    dev = X.device
+    out = {"centroids": torch.empty((nl, d), dtype=torch.float32, device=dev),
+           "offsets": torch.empty(nl + 1, dtype=torch.int32, device=dev),
+           "ids": torch.empty(N, dtype=torch.int32, device=dev),
+           "data": torch.empty((N, d), dtype=torch.float32, device=dev), "nlist": nl}
+    need = load().fk_ivf_workspace_size(int(N), int(d), nl, _metric(metric)) or 256
+    p, n = _workspace(need, dev, workspace)
+    _check(load().fk_ivf_build(_ptr(X), N, d, nl, _metric(metric), _score(score), int(n_iter),
+                               ctypes.c_void_p(idx.ctypes.data), _ptr(out["centroids"]), _ptr(out["offsets"]),
+                               _ptr(out["ids"]), _ptr(out["data"]), ctypes.c_void_p(p), ctypes.c_size_t(n),
+                               _stream(dev)))
+    return out
 
 
 def fk_profile_enable(on: bool = True):

@@ -43,11 +43,17 @@ struct Layout {
     size_t keys_sorted, perm, tmp_keys, tmp_vals, sort_scratch, offsets;
     size_t sums, cnt, pfirst, plast, csplit, ncsplit;
     size_t xchunk[2], achunk[2];      // out-of-core only
+    size_t ctmp, cinit, labels, xcopy;  // fit / IVF build only
 };
 
 constexpr size_t kNone = ~(size_t)0;
 
-Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc) {
+// extras: kFitExtras adds a second centroid buffer (the fit's ping-pong);
+// kIvfExtras adds the initial centroids, the list labels and, for cosine, a
+// normalised copy of X.
+constexpr int kFitExtras = 1, kIvfExtras = 2;
+
+Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc, int extras = 0) {
     Layout L;
     size_t off = 0;
     auto take = [&](size_t bytes) {
@@ -89,6 +95,11 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc) {
         L.xchunk[i] = ooc ? take((size_t)r * d * 4) : kNone;
         L.achunk[i] = ooc ? take((size_t)r * 4) : kNone;
     }
+    const bool fit = (extras & (kFitExtras | kIvfExtras)) != 0, ivf = (extras & kIvfExtras) != 0;
+    L.ctmp = fit ? take((size_t)K * d * 4) : kNone;
+    L.cinit = ivf ? take((size_t)K * d * 4) : kNone;
+    L.labels = ivf ? take((size_t)r * 4) : kNone;
+    L.xcopy = (ivf && cos) ? take((size_t)r * d * 4) : kNone;
     L.total = off;
     return L;
 }
@@ -346,9 +357,38 @@ fk_status check_common(const float *X, int64_t N, int32_t d, const void *C, int3
     return FK_OK;
 }
 
+// One Lloyd iteration on validated arguments (the body of fk_lloyd_iter).
+fk_status lloyd_step(const Ctx &c, const float *X, int64_t N, const float *C_in, int32_t *assign, float *min_dist,
+                     float *C_out, int32_t *counts) {
+    fk_status st;
+    if ((st = step_zero_accumulators(c, false, N)) != FK_OK) return st;
+    if (N > 0) {
+        const float *Cu = nullptr;
+        if ((st = step_prep(c, C_in, &Cu)) != FK_OK) return st;
+        if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
+        if ((st = step_assign(c, X, N, C_in, Cu, assign, min_dist)) != FK_OK) return st;
+        if ((st = step_accumulate(c, X, N, assign, false)) != FK_OK) return st;
+    }
+    return step_finalize(c, C_in, C_out, counts, N > 0);
+}
+
+// n_iter Lloyd iterations from C_init; the centroid buffers alternate between
+// C_out and the workspace so that the last iteration writes C_out.
+fk_status fit_steps(const Ctx &c, const float *X, int64_t N, const float *C_init, int n_iter, float *C_out,
+                    int32_t *assign, int32_t *counts) {
+    float *ctmp = at<float>(c.ws, c.L.ctmp);
+    const float *cur = C_init;
+    for (int i = 0; i < n_iter; ++i) {
+        float *next = ((n_iter - 1 - i) % 2 == 0) ? C_out : ctmp;
+        const fk_status st = lloyd_step(c, X, N, cur, assign, nullptr, next, counts);
+        if (st != FK_OK) return st;
+        cur = next;
+    }
+    return FK_OK;
+}
+
 }  // namespace
 
-// ============================================================================
 extern "C" {
 
 size_t fk_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric, int64_t chunk_rows) {
@@ -445,15 +485,7 @@ fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in,
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
     const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
-    if ((st = step_zero_accumulators(c, false, N)) != FK_OK) return st;
-    if (N > 0) {
-        const float *Cu = nullptr;
-        if ((st = step_prep(c, C_in, &Cu)) != FK_OK) return st;
-        if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
-        if ((st = step_assign(c, X, N, C_in, Cu, assign, min_dist)) != FK_OK) return st;
-        if ((st = step_accumulate(c, X, N, assign, false)) != FK_OK) return st;
-    }
-    return step_finalize(c, C_in, C_out, counts, N > 0);
+    return lloyd_step(c, X, N, C_in, assign, min_dist, C_out, counts);
 }
 
 // Library-owned copy stream and events for the out-of-core pipeline (one set
@@ -561,6 +593,93 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
                    "assignment copy");
     }
     return step_finalize(c, C_in, C_out, counts, false);
+}
+
+size_t fk_fit_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric) {
+    if (N < 0 || N > INT32_MAX || d < 1 || d > FK_MAX_D || K < 1 || K > FK_MAX_K) return 0;
+    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE) return 0;
+    return make_layout(N, d, K, metric, false, kFitExtras).total;
+}
+
+fk_status fk_fit(const float *X, int64_t N, int32_t d, const float *C_init, int32_t K, int32_t metric, int32_t score,
+                 int32_t n_iter, float *C_out, int32_t *assign, int32_t *counts, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+    g_err[0] = 0;
+    fk_status st = check_common(X, N, d, C_init, K, metric);
+    if (st != FK_OK) return st;
+    if ((st = check_score(score)) != FK_OK) return st;
+    if (n_iter < 1) return fail(FK_ERR_INVALID_ARG, "n_iter=%d must be at least 1", (int)n_iter);
+    if (N > 0 && assign == nullptr) return fail(FK_ERR_INVALID_ARG, "assign is NULL");
+    if (C_out == nullptr || counts == nullptr) return fail(FK_ERR_INVALID_ARG, "C_out and counts must not be NULL");
+    if (!aligned(C_out, 16)) return fail(FK_ERR_INVALID_ARG, "C_out must be 16-byte aligned");
+    const size_t cb = (size_t)K * d * 4;
+    if (overlap(C_out, cb, C_init, cb)) return fail(FK_ERR_INVALID_ARG, "C_out overlaps C_init");
+    const Layout L = make_layout(N, d, K, metric, false, kFitExtras);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
+    if ((st = check_device()) != FK_OK) return st;
+    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
+    return fit_steps(c, X, N, C_init, n_iter, C_out, assign, counts);
+}
+
+size_t fk_ivf_workspace_size(int64_t N, int32_t d, int32_t nlist, int32_t metric) {
+    if (N < 1 || N > INT32_MAX || d < 1 || d > FK_MAX_D || nlist < 1 || nlist > FK_MAX_K || nlist > N) return 0;
+    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE) return 0;
+    return make_layout(N, d, nlist, metric, false, kIvfExtras).total;
+}
+
+fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int32_t metric, int32_t score,
+                       int32_t n_iter, const int32_t *init_idx_host, float *centroids, int32_t *list_offsets,
+                       int32_t *list_ids, float *list_data, void *workspace, size_t workspace_bytes, void *stream) {
+    g_err[0] = 0;
+    fk_status st = check_sizes(N, d, nlist);
+    if (st != FK_OK) return st;
+    if ((st = check_metric(metric)) != FK_OK) return st;
+    if ((st = check_score(score)) != FK_OK) return st;
+    if (N < 1 || nlist > N) return fail(FK_ERR_INVALID_ARG, "need 1 <= nlist=%d <= N=%lld", (int)nlist, (long long)N);
+    if (n_iter < 1) return fail(FK_ERR_INVALID_ARG, "n_iter=%d must be at least 1", (int)n_iter);
+    if (X == nullptr || init_idx_host == nullptr || centroids == nullptr || list_offsets == nullptr ||
+        list_ids == nullptr || list_data == nullptr)
+        return fail(FK_ERR_INVALID_ARG, "X, init_idx, centroids, list_offsets, list_ids and list_data are required");
+    if (!aligned(X, 16) || !aligned(centroids, 16) || !aligned(list_data, 16))
+        return fail(FK_ERR_INVALID_ARG, "X, centroids and list_data must be 16-byte aligned");
+    for (int32_t k = 0; k < nlist; ++k)
+        if (init_idx_host[k] < 0 || init_idx_host[k] >= N)
+            return fail(FK_ERR_INVALID_ARG, "init_idx[%d]=%d outside [0, N)", (int)k, (int)init_idx_host[k]);
+    const size_t xb = (size_t)N * d * 4;
+    if (overlap(list_data, xb, X, xb)) return fail(FK_ERR_INVALID_ARG, "list_data overlaps X");
+    const Layout L = make_layout(N, d, nlist, metric, false, kIvfExtras);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
+    if ((st = check_device()) != FK_OK) return st;
+    const hipStream_t s = (hipStream_t)stream;
+    // cosine: the lists hold the normalised rows and the quantizer is L2
+    // k-means on them (normalising X and C on entry of every iteration would
+    // train a different, spherical, quantizer)
+    const Ctx c{L, workspace, s, d, nlist, FK_METRIC_L2, score};
+    const float *Xu = X;
+    if (metric == FK_METRIC_COSINE) {
+        PhaseScope ph(FK_PH_PREP, s);
+        FK_TRY(launch_row_norm64(X, N, d, at<double>(workspace, L.xnorm64), s), "row norms");
+        FK_TRY(launch_normalize_rows(X, N, d, at<double>(workspace, L.xnorm64), nullptr, at<float>(workspace, L.xcopy),
+                                     s),
+               "row normalisation");
+        Xu = at<float>(workspace, L.xcopy);
+    }
+    int32_t *idx_dev = at<int32_t>(workspace, L.labels);  // the labels buffer holds the indices first
+    FK_TRY(hipMemcpyAsync(idx_dev, init_idx_host, (size_t)nlist * 4, hipMemcpyHostToDevice, s), "init indices");
+    FK_TRY(launch_gather_rows(Xu, idx_dev, nlist, d, at<float>(workspace, L.cinit), s), "initial centroids");
+    int32_t *labels = at<int32_t>(workspace, L.labels);
+    int32_t *cnt = at<int32_t>(workspace, L.cnt);
+    if ((st = fit_steps(c, Xu, N, at<float>(workspace, L.cinit), n_iter, centroids, labels, cnt)) != FK_OK) return st;
+    // the lists: every row under the final centroids, grouped by cell
+    const float *Cu = nullptr;
+    if ((st = step_prep(c, centroids, &Cu)) != FK_OK) return st;
+    if ((st = step_assign(c, Xu, N, centroids, Cu, labels, nullptr)) != FK_OK) return st;
+    if ((st = step_sort(c, labels, N, list_ids, list_offsets)) != FK_OK) return st;
+    {
+        PhaseScope ph(FK_PH_REDUCE, s);
+        FK_TRY(launch_gather_rows(Xu, list_ids, N, d, list_data, s), "list rows");
+    }
+    return FK_OK;
 }
 
 fk_status fk_profile_enable(int32_t on) {

@@ -88,8 +88,39 @@ __global__ __launch_bounds__(256) void k_normalize_rows(const float *__restrict_
     if (q >= total) return;
     const int64_t r = q / d;
     const double v = (double)M[q] / nrm[r];
-    out64[q] = v;
+    if (out64 != nullptr) out64[q] = v;
     out32[q] = (float)v;
+}
+
+// out[r, :] = M[idx[r], :] (rows of d floats; indices checked by the caller).
+__global__ __launch_bounds__(256) void k_gather_rows(const float *__restrict__ M, const int32_t *__restrict__ idx,
+                                                     int64_t total, int d, float *__restrict__ out) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= total) return;
+    const int64_t r = q / d;
+    out[q] = M[(int64_t)idx[r] * d + (q - r * d)];
+}
+
+// Four floats per thread when d is a multiple of 4 (rows 16-byte aligned).
+__global__ __launch_bounds__(256) void k_gather_rows4(const float4 *__restrict__ M, const int32_t *__restrict__ idx,
+                                                      int64_t total4, int d4, float4 *__restrict__ out) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= total4) return;
+    const int64_t r = q / d4;
+    out[q] = M[(int64_t)idx[r] * d4 + (q - r * d4)];
+}
+
+hipError_t launch_gather_rows(const float *M, const int32_t *idx, int64_t rows, int d, float *out, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    if (d % 4 == 0) {
+        const int64_t total4 = rows * (int64_t)(d / 4);
+        hipLaunchKernelGGL(k_gather_rows4, dim3((unsigned)cdiv(total4, 256)), dim3(256), 0, s,
+                           reinterpret_cast<const float4 *>(M), idx, total4, d / 4, reinterpret_cast<float4 *>(out));
+    } else {
+        const int64_t total = rows * (int64_t)d;
+        hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, M, idx, total, d, out);
+    }
+    return hipGetLastError();
 }
 
 // ncn[k] = -||c_k||^2 / 2 in fp32 for k < K, -inf for K <= k < Kpad (padded

@@ -67,8 +67,11 @@ int split_width(int d);
 
 // ---- launchers (each returns the launch status) ---------------------------
 hipError_t launch_row_norm64(const float *M, int64_t rows, int d, double *nrm, hipStream_t s);
+// out64 may be null (only the fp32 normalised rows are written then)
 hipError_t launch_normalize_rows(const float *M, int64_t rows, int d, const double *nrm, double *out64,
                                  float *out32, hipStream_t s);
+// out[r, :] = M[idx[r], :] for r < rows
+hipError_t launch_gather_rows(const float *M, const int32_t *idx, int64_t rows, int d, float *out, hipStream_t s);
 // -||c||^2/2 (padded with -inf to kCentroidPad) and per-block maxima of the
 // centroid norms; with split scoring also writes the split operands.
 hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float *cmax_part, int *nparts,

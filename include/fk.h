@@ -173,6 +173,46 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
                                float *C_out, int32_t *counts, void *workspace, size_t workspace_bytes,
                                void *stream);
 
+/*
+ * Lloyd k-means: n_iter >= 1 iterations of fk_lloyd_iter starting from
+ * C_init (the plain iteration of the Flash-KMeans article, repeated; the
+ * LEANN FlashLib guide, paragraph "parameters", trains its IVF quantizer with
+ * niter = 20 such iterations).  C_out receives the centroids after the last
+ * iteration, assign the last iteration's assignment (under the centroids
+ * before it) and counts its cluster sizes.  Workspace:
+ * fk_fit_workspace_size() bytes (it also holds the intermediate centroids).
+ * C_out must not overlap C_init.  Device pointers; errors as fk_lloyd_iter,
+ * plus FK_ERR_INVALID_ARG for n_iter < 1.
+ */
+size_t fk_fit_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric);
+fk_status fk_fit(const float *X, int64_t N, int32_t d, const float *C_init, int32_t K, int32_t metric, int32_t score,
+                 int32_t n_iter, float *C_out, int32_t *assign, int32_t *counts, void *workspace,
+                 size_t workspace_bytes, void *stream);
+
+/*
+ * IVF-Flat index build (LEANN FlashLib guide, paragraphs "how it works",
+ * "parameters"): a coarse quantizer of nlist centroids trained by n_iter
+ * Lloyd iterations from the rows init_idx_host[0..nlist) of X, then every row
+ * assigned to its nearest final centroid and the rows grouped by cell:
+ *   centroids[nlist, d]      the quantizer (fp32),
+ *   list_offsets[nlist + 1]  CSR offsets: cell k holds list positions
+ *                            [list_offsets[k], list_offsets[k+1]),
+ *   list_ids[N]              the row of X at each list position (increasing
+ *                            within a cell),
+ *   list_data[N, d]          those rows, cell-contiguous.
+ * metric COSINE L2-normalises the rows first (zero norm taken as 1), trains
+ * plain L2 k-means on them and stores the normalised rows; L2 uses X as is.
+ * Requires 1 <= nlist <= N (the guide clamps nlist to N; the Python binding
+ * does that).  init_idx_host is HOST memory (nlist int32 row indices, each
+ * checked to lie in [0, N)); every other pointer is device memory.  Workspace:
+ * fk_ivf_workspace_size() bytes.  list_data must not overlap X.  The
+ * assignments are exact in the sense of fk_assign.
+ */
+size_t fk_ivf_workspace_size(int64_t N, int32_t d, int32_t nlist, int32_t metric);
+fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int32_t metric, int32_t score,
+                       int32_t n_iter, const int32_t *init_idx_host, float *centroids, int32_t *list_offsets,
+                       int32_t *list_ids, float *list_data, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Static name of a status code. */
 const char *fk_status_str(int32_t status);
 

@@ -60,6 +60,8 @@ def _load():
         lib.fko_update.restype = ctypes.c_int
         lib.fko_lloyd_iter.argtypes = [P, I64, I64, P, I64, ctypes.c_int, P, P, P, P, P, P]
         lib.fko_lloyd_iter.restype = ctypes.c_int
+        lib.fko_normalize_rows.argtypes = [P, I64, I64, P]
+        lib.fko_normalize_rows.restype = ctypes.c_int
         lib.fko_num_threads.argtypes = []
         lib.fko_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -142,6 +144,53 @@ def lloyd_iter(X, C_in, metric: str = "l2"):
     if rc != 0:
         raise ValueError("oracle iteration rejected its arguments")
     return {"a": a, "D1": D1, "D2": D2, "C": C_out, "counts": counts, "J": J.value}
+
+
+def normalize_rows(X):
+    """The rows as the cosine metric sees them: promoted to fp64, divided by
+    their L2 norm (zero norm taken as 1), rounded once to fp32."""
+    X = _f32(X)
+    N, d = X.shape
+    out = np.empty_like(X)
+    if _load().fko_normalize_rows(_ptr(X), N, d, _ptr(out)) != 0:
+        raise ValueError("oracle normalisation rejected its arguments")
+    return out
+
+
+def fit(X, C_init, n_iter: int, metric: str = "l2"):
+    """Lloyd k-means: the iteration above repeated n_iter times from C_init.
+    Between iterations the centroids are held in fp32, the precision of C in
+    the problem statement (Flash-KMeans article, "Why being fast took so
+    long": X and C are the inputs of every iteration).  Returns (C float32,
+    a of the last iteration, counts of the last iteration, [J per
+    iteration])."""
+    if n_iter < 1:
+        raise ValueError("n_iter must be at least 1")
+    C = _f32(C_init)
+    Js = []
+    for _ in range(int(n_iter)):
+        r = lloyd_iter(X, C, metric)
+        Js.append(r["J"])
+        C = r["C"].astype(np.float32)
+    return C, r["a"], r["counts"], Js
+
+
+def ivf_build(X, init_idx, n_iter: int, metric: str = "l2"):
+    """IVF-Flat build as the LEANN FlashLib guide describes it (paragraphs
+    "工作原理" and "参数速查"): for cosine the rows are normalised first; a
+    coarse quantizer is trained by n_iter Lloyd iterations (L2) from the rows
+    init_idx; every row is then assigned to its nearest final centroid, and
+    the rows are grouped by cell (CSR offsets, the row ids of each cell in
+    increasing order, and the rows themselves).  Returns a dict with
+    centroids, labels, offsets, ids, data."""
+    Xu = normalize_rows(X) if metric == "cosine" else _f32(X)
+    init_idx = np.asarray(init_idx, np.int64)
+    C, _, _, _ = fit(Xu, Xu[init_idx], n_iter, "l2")
+    a, _, _ = assign(Xu, C, "l2")
+    ids = np.argsort(a, kind="stable").astype(np.int32)
+    counts = np.bincount(a, minlength=C.shape[0])
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    return {"centroids": C, "labels": a, "offsets": offsets, "ids": ids, "data": Xu[ids]}
 
 
 def relative_gap(D1, D2):

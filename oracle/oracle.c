@@ -237,3 +237,23 @@ int fko_num_threads(void)
     }
     return n;
 }
+
+/* The rows of X as the cosine metric sees them, rounded once to fp32: each
+ * row promoted to fp64 and divided by its L2 norm, a zero norm taken as 1
+ * (FlashLib guide, "距离度量"; the IVF lists of the same guide, paragraph
+ * "工作原理", hold these normalised rows).  Returns 0, or -1 on bad sizes. */
+int fko_normalize_rows(const float *X, int64_t N, int64_t d, float *out)
+{
+    if (N < 0 || d < 1 || (N > 0 && (X == NULL || out == NULL)))
+        return -1;
+    double *row = (double *)malloc((size_t)d * sizeof(double));
+    if (row == NULL)
+        return -1;
+    for (int64_t i = 0; i < N; ++i) {
+        promote_row(X + i * d, d, FKO_METRIC_COSINE, row);
+        for (int64_t j = 0; j < d; ++j)
+            out[i * d + j] = (float)row[j];
+    }
+    free(row);
+    return 0;
+}

@@ -22,7 +22,8 @@ def lib():
 def test_every_declared_symbol_is_exported(lib):
     names = fk.declared_symbols()
     expected = {"fk_workspace_size", "fk_assign", "fk_sort_inverse", "fk_update", "fk_lloyd_iter",
-                "fk_lloyd_iter_stream", "fk_status_str", "fk_last_error", "fk_profile_enable", "fk_profile_read"}
+                "fk_lloyd_iter_stream", "fk_status_str", "fk_last_error", "fk_profile_enable", "fk_profile_read",
+                "fk_fit_workspace_size", "fk_fit", "fk_ivf_workspace_size", "fk_ivf_build"}
     assert expected <= set(names)
     raw = ctypes.CDLL(fk.LIB_PATH)
     for n in names:
@@ -129,3 +130,28 @@ def test_profile_api_without_device(lib):
     r = fk.fk_profile_read()
     assert r["rechecked"] == 0 and all(v == 0 for v in r["calls"].values())
     fk.fk_profile_enable(False)
+
+
+def test_fit_and_ivf_validation(lib):
+    ws = _fake(0x1000000)
+    # fk_fit: n_iter < 1, aliasing of C_out and C_init
+    st = lib.fk_fit(_fake(0x10000), 100, 8, _fake(0x20000), 4, 0, 0, 0, _fake(0x30000), _fake(0x40000),
+                    _fake(0x50000), ws, 1 << 30, None)
+    assert st == INVALID and b"n_iter" in lib.fk_last_error()
+    st = lib.fk_fit(_fake(0x10000), 100, 8, _fake(0x20000), 4, 0, 0, 3, _fake(0x20000 + 16), _fake(0x40000),
+                    _fake(0x50000), ws, 1 << 30, None)
+    assert st == INVALID and b"overlaps" in lib.fk_last_error()
+    assert fk.fk_fit_workspace_size(1000, 16, 10) > fk.fk_workspace_size(1000, 16, 10)
+    # fk_ivf_build: nlist > N, an initial index out of range, n_iter < 1
+    idx = (ctypes.c_int32 * 4)(0, 1, 2, 99)
+    args = dict(X=_fake(0x10000), cent=_fake(0x20000), offs=_fake(0x30000), ids=_fake(0x40000), data=_fake(0x800000))
+
+    def ivf(N, nlist, n_iter, init):
+        return lib.fk_ivf_build(args["X"], N, 8, nlist, 0, 0, n_iter, init, args["cent"], args["offs"], args["ids"],
+                                args["data"], ws, 1 << 30, None)
+    assert ivf(3, 4, 2, idx) == INVALID
+    assert ivf(50, 4, 2, idx) == INVALID and b"init_idx[3]" in lib.fk_last_error()
+    assert ivf(500, 4, 0, idx) == INVALID and b"n_iter" in lib.fk_last_error()
+    assert ivf(500, 4, 2, None) == INVALID
+    assert lib.fk_ivf_workspace_size(10, 8, 11, 0) == 0
+    assert fk.fk_ivf_workspace_size(1000, 16, 10, "cosine") > fk.fk_ivf_workspace_size(1000, 16, 10)

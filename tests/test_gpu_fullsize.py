@@ -92,3 +92,36 @@ def test_out_of_core_scaled(gpu_lib, score):
     C_ref, n_ref = oracle.update(X, a, C)
     np.testing.assert_array_equal(counts, n_ref)
     assert centroid_rel_err(host(C1d), C_ref, n_ref) <= 1e-6
+
+
+@pytest.mark.parametrize("score", ["fp32", "split_bf16"])
+def test_ivf_build_full_size(gpu_lib, score):
+    """The IVF-Flat build at the 1M x 768, nlist = 4096, niter = 20 shape
+    (rows pre-normalised, L2), in the configuration bench.py --ivf-build
+    times: sampled list positions must hold a row whose exact nearest final
+    centroid (oracle, fp64) is the position's cell, the row copied bit for
+    bit; ids must be a permutation, increasing within each cell."""
+    fk = gpu_lib
+    w = synth.WORKLOADS["ivf_1m_d768_k4096"]
+    X = synth.rows(w)
+    init = synth.init_indices(w).astype(np.int32)
+    Xd = dev(X)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    out = fk.fk_ivf_build(Xd, w.K, init, n_iter=20, score=score)
+    torch.cuda.synchronize()
+    log(f"ivf build ({score}): {time.perf_counter() - t0:.2f} s")
+    C = host(out["centroids"])
+    ids_t = out["ids"].long()
+    assert torch.equal(torch.sort(ids_t).values, torch.arange(w.N, device=ids_t.device))
+    offs = host(out["offsets"]).astype(np.int64)
+    assert offs[0] == 0 and offs[-1] == w.N and (np.diff(offs) >= 0).all()
+    ids = host(out["ids"])
+    cell = np.searchsorted(offs, np.arange(w.N), side="right") - 1
+    same_cell = cell[1:] == cell[:-1]
+    assert (np.diff(ids.astype(np.int64))[same_cell] > 0).all()
+    pos = _sample(w.N, 1024, 5)
+    a_ref, _, _ = oracle.assign(X[ids[pos]], C)
+    np.testing.assert_array_equal(a_ref, cell[pos])
+    data = host(out["data"][torch.from_numpy(pos).to(Xd.device)])
+    np.testing.assert_array_equal(data.view(np.uint32), X[ids[pos]].view(np.uint32))

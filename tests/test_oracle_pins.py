@@ -299,3 +299,89 @@ def test_cosine_scale_invariance_and_zero_rows():
 def test_relative_gap_definition():
     g = oracle.relative_gap(np.array([1.0, 0.0, 0.0, 2.0]), np.array([1.5, 0.0, 3.0, 2.0]))
     assert g[0] == 0.5 and g[1] == 0.0 and np.isinf(g[2]) and g[3] == 0.0
+
+
+# ---------------------------------------------------------- fit and IVF build
+
+def test_fit_reaches_exact_cluster_means_on_planted_integer_clusters():
+    """Integer points in far-apart clusters, one initial centroid per cluster:
+    from the second iteration on every point is in its own cluster, so the
+    fit's centroids are the exact cluster means rounded to fp32 (the sums of
+    small integers are exact in fp64; each mean is the correctly rounded fp64
+    quotient, as float(Fraction) gives it, then fp32)."""
+    rng = np.random.default_rng(31)
+    K, d, n = 7, 4, 350
+    centers = rng.integers(-1000, 1000, size=(K, d)) * 10
+    labels = rng.integers(0, K, size=n)
+    X = (centers[labels] + rng.integers(-3, 4, size=(n, d))).astype(np.float32)
+    init = [int(np.nonzero(labels == k)[0][0]) for k in range(K)]
+    C, a, counts, Js = oracle.fit(X, X[init], 4)
+    np.testing.assert_array_equal(a, labels)
+    np.testing.assert_array_equal(counts, np.bincount(labels, minlength=K))
+    for k in range(K):
+        rows = X[labels == k].astype(np.int64)
+        for j in range(d):
+            exact = Fraction(int(rows[:, j].sum()), len(rows))
+            assert C[k, j] == np.float32(float(exact)), (k, j)
+    assert all(j1 <= j0 for j0, j1 in zip(Js, Js[1:]))
+
+
+def test_fit_one_iteration_is_the_iteration_rounded_to_fp32():
+    rng = np.random.default_rng(32)
+    X = rng.standard_normal((500, 6)).astype(np.float32)
+    C0 = X[:9].copy()
+    C, a, counts, Js = oracle.fit(X, C0, 1)
+    r = oracle.lloyd_iter(X, C0)
+    np.testing.assert_array_equal(a, r["a"])
+    np.testing.assert_array_equal(C, r["C"].astype(np.float32))
+    assert Js == [r["J"]]
+
+
+def test_normalize_rows_unit_norm_direction_and_zero_rows():
+    rng = np.random.default_rng(33)
+    X = (rng.standard_normal((300, 11)) * rng.uniform(0.01, 100, size=(300, 1))).astype(np.float32)
+    X[7] = 0.0
+    Y = oracle.normalize_rows(X)
+    n = np.linalg.norm(Y.astype(np.float64), axis=1)
+    n[7] = 1.0
+    np.testing.assert_allclose(n, 1.0, rtol=0, atol=4e-7)
+    assert not Y[7].any()
+    # the same direction: each row is a positive multiple of the input row
+    ratio = Y.astype(np.float64) / np.where(X == 0, 1, X)
+    ok = np.delete(np.arange(300), 7)
+    np.testing.assert_allclose(ratio[ok], (1.0 / np.linalg.norm(X[ok].astype(np.float64), axis=1))[:, None]
+                               * np.ones((1, 11)), rtol=2e-7)
+    # and the assignment under cosine is the L2 assignment of the normalised
+    # rows, up to the fp32 rounding of those rows (it can only flip points
+    # whose two best distances are within a few fp32 ulps)
+    C = X[rng.choice(300, 12, replace=False)]
+    Cn = oracle.normalize_rows(C)
+    a_cos, D1, D2 = oracle.assign(X, C, "cosine")
+    a_l2, _, _ = oracle.assign(Y, Cn, "l2")
+    flips = a_cos != a_l2
+    assert (oracle.relative_gap(D1, D2)[flips] < 1e-5).all()
+    assert flips.mean() < 0.05
+
+
+@pytest.mark.parametrize("metric", ["l2", "cosine"])
+def test_ivf_build_layout_by_brute_force(metric):
+    """Every cell's list is the rows assigned to it, in increasing row order
+    (checked with plain loops), the offsets delimit them, and the data rows
+    are those rows."""
+    rng = np.random.default_rng(34)
+    X = rng.standard_normal((420, 5)).astype(np.float32)
+    init = rng.choice(420, 13, replace=False)
+    r = oracle.ivf_build(X, init, 3, metric)
+    Xu = oracle.normalize_rows(X) if metric == "cosine" else X
+    C, _, _, _ = oracle.fit(Xu, Xu[init], 3)
+    np.testing.assert_array_equal(r["centroids"], C)
+    a, _, _ = oracle.assign(Xu, C)
+    np.testing.assert_array_equal(r["labels"], a)
+    pos = 0
+    for k in range(13):
+        members = [i for i in range(420) if a[i] == k]
+        assert r["offsets"][k] == pos
+        assert list(r["ids"][pos:pos + len(members)]) == members
+        pos += len(members)
+    assert r["offsets"][13] == 420 == pos
+    np.testing.assert_array_equal(r["data"], Xu[r["ids"]])
