@@ -124,9 +124,7 @@ fk_status check_score(int32_t score) {
 }
 
 fk_status check_metric(int32_t metric) {
-    if (metric == FK_METRIC_INNER_PRODUCT)
-        return fail(FK_ERR_UNSUPPORTED, "the inner-product metric is not supported (L2 and cosine are)");
-    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE)
+    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE && metric != FK_METRIC_INNER_PRODUCT)
         return fail(FK_ERR_INVALID_ARG, "unknown metric %d", (int)metric);
     return FK_OK;
 }
@@ -243,7 +241,7 @@ fk_status step_prep(const Ctx &c, const float *C, const float **C_use) {
     }
     int nparts = 0;
     FK_TRY(launch_centroid_prep(Cu, c.K, c.d, at<float>(c.ws, c.L.ncn), at<float>(c.ws, c.L.cmax_part), &nparts,
-                                c.split(), c.s),
+                                c.split(), c.metric == FK_METRIC_INNER_PRODUCT, c.s),
            "centroid prep");
     FK_TRY(launch_prep_finish(at<float>(c.ws, c.L.cmax_part), nparts, at<float>(c.ws, c.L.scal),
                               at<int32_t>(c.ws, c.L.counter), c.s),
@@ -276,14 +274,14 @@ fk_status step_assign(const Ctx &c, const float *X, int64_t rows, const float *C
     {
         PhaseScope ph(FK_PH_ASSIGN, c.s);
         FK_TRY(launch_flash_assign(X, rows, c.d, C_use, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal), xn,
-                                   a_out, d1_out, nt, c.split(), c.s),
+                                   a_out, d1_out, nt, c.split(), c.metric == FK_METRIC_INNER_PRODUCT, c.s),
                "flash assign");
     }
     {
         PhaseScope ph(FK_PH_RECHECK, c.s);
         const double *c64 = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.c64) : nullptr;
         FK_TRY(launch_recheck(X, rows, c.d, C_use, C, c64, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal),
-                              xn, nt, c.split(), a_out, d1_out, c.s),
+                              xn, nt, c.split(), c.metric == FK_METRIC_INNER_PRODUCT, a_out, d1_out, c.s),
                "near-tie recheck");
     }
     prof_count_rechecks(at<int32_t>(c.ws, c.L.counter), rows, c.s);
@@ -393,7 +391,7 @@ extern "C" {
 
 size_t fk_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric, int64_t chunk_rows) {
     if (N < 0 || N > INT32_MAX || d < 1 || d > FK_MAX_D || K < 1 || K > FK_MAX_K) return 0;
-    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE) return 0;
+    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE && metric != FK_METRIC_INNER_PRODUCT) return 0;
     if (chunk_rows < 0 || chunk_rows > INT32_MAX) return 0;
     const bool ooc = chunk_rows > 0;
     return make_layout(ooc ? chunk_rows : N, d, K, metric, ooc).total;
@@ -597,7 +595,7 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
 
 size_t fk_fit_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric) {
     if (N < 0 || N > INT32_MAX || d < 1 || d > FK_MAX_D || K < 1 || K > FK_MAX_K) return 0;
-    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE) return 0;
+    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE && metric != FK_METRIC_INNER_PRODUCT) return 0;
     return make_layout(N, d, K, metric, false, kFitExtras).total;
 }
 
@@ -634,6 +632,8 @@ fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int3
     fk_status st = check_sizes(N, d, nlist);
     if (st != FK_OK) return st;
     if ((st = check_metric(metric)) != FK_OK) return st;
+    if (metric == FK_METRIC_INNER_PRODUCT)
+        return fail(FK_ERR_UNSUPPORTED, "the IVF build takes L2 or cosine (inner product: normalise, i.e. cosine)");
     if ((st = check_score(score)) != FK_OK) return st;
     if (N < 1 || nlist > N) return fail(FK_ERR_INVALID_ARG, "need 1 <= nlist=%d <= N=%lld", (int)nlist, (long long)N);
     if (n_iter < 1) return fail(FK_ERR_INVALID_ARG, "n_iter=%d must be at least 1", (int)n_iter);

@@ -51,6 +51,7 @@ struct FlashArgs {
     int sw;              // w bf16 low parts (C - high, rounded); Kpad rows
     const __bf16 *ncs;   // split scoring: -||c||^2/2 as three bf16 parts + 5 zeros
     unsigned cs_bytes;   // size of the split copy
+    int ip;              // inner product: scores are x.c (no -||c||^2/2 term)
 };
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -128,7 +129,8 @@ hipError_t launch_gather_rows(const float *M, const int32_t *idx, int64_t rows, 
 // per centroid row.
 __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__ C, int K, int Kpad, int d,
                                                        float *__restrict__ ncn, float *__restrict__ cmax_part,
-                                                       __bf16 *__restrict__ cs, int w, __bf16 *__restrict__ ncs) {
+                                                       __bf16 *__restrict__ cs, int w, __bf16 *__restrict__ ncs,
+                                                       int ip) {
     __shared__ float wmax[3][4];
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int k = blockIdx.x * 4 + wv;
@@ -167,7 +169,7 @@ __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__
     }
     if (lane == 0) {
         if (k < K)
-            ncn[k] = -0.5f * cn;
+            ncn[k] = ip ? 0.f : -0.5f * cn;
         else if (k < Kpad)
             ncn[k] = -INFINITY;
         if (ncs != nullptr && k < Kpad) {
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__
             // significant bits of what is left (24 in all).  Rows past K get
             // -2^127, finite so that the MFMA against the zero k-slots stays
             // finite, and below any real score.
-            const float v = k < K ? -0.5f * cn : -1.7014118e38f;
+            const float v = k < K ? (ip ? 0.f : -0.5f * cn) : -1.7014118e38f;
             const __bf16 p0 = (__bf16)v;
             const float r1 = v - (float)p0;
             const __bf16 p1 = (__bf16)r1;
@@ -530,8 +532,9 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                                     1.004f * xnorm * (sqrtf(A.scal[2]) + uf));
                 }
                 // the last term covers flushed denormal operands
-                xl2[b] = 2.f * (1.0625f * (g * (M + xnorm * sqM) + drop) + 7.6e-37f * (float)d * (sqM + xnorm) +
-                                1e-30f);
+                // inner product: no -||c||^2/2 term, so no M term
+                xl2[b] = 2.f * (1.0625f * (g * ((A.ip ? 0.f : M) + xnorm * sqM) + drop) +
+                                7.6e-37f * (float)d * (sqM + xnorm) + 1e-30f);
                 xn[b] = xnt;
             }
         };
@@ -782,7 +785,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             const bool full = flagged && !pair;
             if (valid) {
                 A.a_out[p] = wi1;
-                if (A.d1_out != nullptr) A.d1_out[p] = fmaxf(xnt - 2.f * w1, 0.f);
+                if (A.d1_out != nullptr) A.d1_out[p] = A.ip ? -w1 : fmaxf(xnt - 2.f * w1, 0.f);
             }
             const uint64_t lt = lanemask_lt();
             const uint64_t mp = __ballot(valid && pair);
@@ -833,13 +836,15 @@ __device__ __forceinline__ void load4_64(const double *c, double (&o)[4]) {
 }
 
 // The fp64 direct-difference distances of one point to NC centroids:
-// D[m] = sum_j (x_j - c_mj)^2 in increasing j, with no fused multiply-add;
+// D[m] = sum_j (x_j - c_mj)^2 in increasing j, with no fused multiply-add
+// (inner product: D[m] = -sum_j x_j c_mj, the same order, whose negation is
+// exact so that the smallest D is the largest dot product);
 // for cosine x_j is first divided by the row norm nx (as the definition
 // does).  Rows are read four elements at a time when d is a multiple of 4
 // (X, C and the fp64 normalised centroids are then 16-byte aligned).
 template <typename CT, int NC>
 __device__ __forceinline__ void sqdist64(const float *__restrict__ x, const CT *const (&c)[NC], int d, double nx,
-                                         bool cosine, double (&D)[NC]) {
+                                         bool cosine, bool ip, double (&D)[NC]) {
 #pragma clang fp contract(off)
 #pragma unroll
     for (int m = 0; m < NC; ++m) D[m] = 0.0;
@@ -858,8 +863,12 @@ __device__ __forceinline__ void sqdist64(const float *__restrict__ x, const CT *
                 load4_64(c[m] + j, cv);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const double t = xv[e] - cv[e];
-                    D[m] = D[m] + t * t;
+                    if (ip) {
+                        D[m] = D[m] - xv[e] * cv[e];
+                    } else {
+                        const double t = xv[e] - cv[e];
+                        D[m] = D[m] + t * t;
+                    }
                 }
             }
         }
@@ -869,8 +878,12 @@ __device__ __forceinline__ void sqdist64(const float *__restrict__ x, const CT *
         if (cosine) xv = xv / nx;
 #pragma unroll
         for (int m = 0; m < NC; ++m) {
-            const double t = xv - (double)c[m][j];
-            D[m] = D[m] + t * t;
+            if (ip) {
+                D[m] = D[m] - xv * (double)c[m][j];
+            } else {
+                const double t = xv - (double)c[m][j];
+                D[m] = D[m] + t * t;
+            }
         }
     }
 }
@@ -887,7 +900,7 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
                                                       const int32_t *__restrict__ cand,
                                                       const int32_t *__restrict__ ccount, int64_t cap_slots,
                                                       int32_t *__restrict__ ovf_list, int32_t *__restrict__ counters,
-                                                      int32_t *__restrict__ a_out, float *__restrict__ d1_out) {
+                                                      int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
 #pragma clang fp contract(off)
     const int cnt = counters[0];
     for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
@@ -905,7 +918,7 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
             const int k = m < c0 ? cand[2 * (int64_t)q * kMaxCand + m] : cand[(2 * (int64_t)q + 1) * kMaxCand + m - c0];
             const CT *const row[1] = {C + (size_t)k * d};
             double D[1];
-            sqdist64<CT, 1>(X + (size_t)p * d, row, d, nx, xnorm64 != nullptr, D);
+            sqdist64<CT, 1>(X + (size_t)p * d, row, d, nx, xnorm64 != nullptr, ip != 0, D);
             if (D[0] < best || (D[0] == best && k < bk)) {
                 best = D[0];
                 bk = k;
@@ -924,7 +937,7 @@ __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ 
                                                       const double *__restrict__ xnorm64,
                                                       const int32_t *__restrict__ pair_list,
                                                       const int32_t *__restrict__ counters,
-                                                      int32_t *__restrict__ a_out, float *__restrict__ d1_out) {
+                                                      int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
     const int cnt = counters[1];
     for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
         const int64_t p = pair_list[3 * (int64_t)q];
@@ -932,7 +945,8 @@ __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ 
         const int k2 = pair_list[3 * (int64_t)q + 2];
         const CT *const rows[2] = {C + (size_t)k1 * d, C + (size_t)k2 * d};
         double D[2];
-        sqdist64<CT, 2>(X + (size_t)p * d, rows, d, xnorm64 != nullptr ? xnorm64[p] : 1.0, xnorm64 != nullptr, D);
+        sqdist64<CT, 2>(X + (size_t)p * d, rows, d, xnorm64 != nullptr ? xnorm64[p] : 1.0, xnorm64 != nullptr,
+                        ip != 0, D);
         const bool second = (D[1] < D[0]) || (D[1] == D[0] && k2 < k1);
         a_out[p] = second ? k2 : k1;
         if (d1_out != nullptr) d1_out[p] = (float)(second ? D[1] : D[0]);
@@ -952,7 +966,7 @@ __global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, in
                                                  int K, const double *__restrict__ xnorm64,
                                                  const int32_t *__restrict__ flag_list,
                                                  const int32_t *__restrict__ counters, int P,
-                                                 int32_t *__restrict__ a_out, float *__restrict__ d1_out) {
+                                                 int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
 #pragma clang fp contract(off)
     extern __shared__ double sx[];  // P * d
     __shared__ double rb[4][RP];
@@ -986,8 +1000,12 @@ __global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, in
 #pragma unroll
                 for (int pi = 0; pi < RP; ++pi) {
                     if (pi < np) {
-                        const double tt = sx[pi * d + jj] - c;
-                        acc[pi] = acc[pi] + tt * tt;
+                        if (ip) {
+                            acc[pi] = acc[pi] - sx[pi * d + jj] * c;
+                        } else {
+                            const double tt = sx[pi * d + jj] - c;
+                            acc[pi] = acc[pi] + tt * tt;
+                        }
                     }
                 }
             }
@@ -1066,12 +1084,12 @@ hipError_t launch_normalize_rows(const float *M, int64_t rows, int d, const doub
 }
 
 hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float *cmax_part, int *nparts,
-                                const SplitC &sc, hipStream_t s) {
+                                const SplitC &sc, bool ip, hipStream_t s) {
     const int Kpad = (int)(cdiv(K, kCentroidPad) * kCentroidPad);
     const int nb = (int)cdiv(Kpad, 4);
     *nparts = nb;
     hipLaunchKernelGGL(k_centroid_prep, dim3(nb), dim3(256), 0, s, C, K, Kpad, d, ncn, cmax_part, sc.cs, sc.w,
-                       sc.ncs);
+                       sc.ncs, ip ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1127,7 +1145,7 @@ static hipError_t launch_fa_score(const FlashArgs &A, bool split, hipStream_t s)
 
 static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                             const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                            const NearTies &nt, const SplitC &sc) {
+                            const NearTies &nt, const SplitC &sc, bool ip) {
     const AssignShape sh = assign_shape(d);
     FlashArgs A;
     A.X = X;
@@ -1152,6 +1170,7 @@ static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, co
     A.Cs = sc.cs;
     A.sw = sc.w;
     A.ncs = sc.ncs;
+    A.ip = ip ? 1 : 0;
     A.cs_bytes = (unsigned)(cdiv(K, kCentroidPad) * kCentroidPad * 4 * (int64_t)sc.w);
     return A;
 }
@@ -1165,15 +1184,16 @@ int64_t near_tie_cap(int64_t N) {
 
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                                const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                               const NearTies &nt, const SplitC &sc, hipStream_t s) {
+                               const NearTies &nt, const SplitC &sc, bool ip, hipStream_t s) {
     if (N <= 0) return hipSuccess;
-    return launch_fa_score<false>(flash_args(X, N, d, C, ncn, K, scal, xnorm64, a_out, d1_out, nt, sc),
+    return launch_fa_score<false>(flash_args(X, N, d, C, ncn, K, scal, xnorm64, a_out, d1_out, nt, sc, ip),
                                   sc.cs != nullptr, s);
 }
 
 hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma, const float *C32,
                           const double *C64, const float *ncn, int K, const float *scal, const double *xnorm64,
-                          const NearTies &nt, const SplitC &sc, int32_t *a_out, float *d1_out, hipStream_t s) {
+                          const NearTies &nt, const SplitC &sc, bool ip, int32_t *a_out, float *d1_out,
+                          hipStream_t s) {
     if (N <= 0) return hipSuccess;
     hipError_t e;
     // 1. near ties between two known centroids
@@ -1182,14 +1202,14 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
         if (nb > 4096) nb = 4096;
         if (C64 != nullptr)
             hipLaunchKernelGGL(k_recheck_pair<double>, dim3((unsigned)nb), dim3(256), 0, s, X, d, C64, xnorm64,
-                               nt.pair_list, nt.counters, a_out, d1_out);
+                               nt.pair_list, nt.counters, a_out, d1_out, ip ? 1 : 0);
         else
             hipLaunchKernelGGL(k_recheck_pair<float>, dim3((unsigned)nb), dim3(256), 0, s, X, d, C32, xnorm64,
-                               nt.pair_list, nt.counters, a_out, d1_out);
+                               nt.pair_list, nt.counters, a_out, d1_out, ip ? 1 : 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 2. the full list: collect every centroid within each point's window
-    if ((e = launch_fa_score<true>(flash_args(X, N, d, C_mfma, ncn, K, scal, xnorm64, a_out, d1_out, nt, sc),
+    if ((e = launch_fa_score<true>(flash_args(X, N, d, C_mfma, ncn, K, scal, xnorm64, a_out, d1_out, nt, sc, ip),
                                    sc.cs != nullptr, s)) != hipSuccess)
         return e;
     // 3. fp64 over the collected candidates; overflows go to the last list
@@ -1199,10 +1219,12 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
         if (nb > 4096) nb = 4096;
         if (C64 != nullptr)
             hipLaunchKernelGGL(k_recheck_cand<double>, dim3((unsigned)nb), dim3(256), 0, s, X, d, C64, xnorm64,
-                               nt.full_list, nt.cand, nt.ccount, cap, nt.ovf_list, nt.counters, a_out, d1_out);
+                               nt.full_list, nt.cand, nt.ccount, cap, nt.ovf_list, nt.counters, a_out, d1_out,
+                               ip ? 1 : 0);
         else
             hipLaunchKernelGGL(k_recheck_cand<float>, dim3((unsigned)nb), dim3(256), 0, s, X, d, C32, xnorm64,
-                               nt.full_list, nt.cand, nt.ccount, cap, nt.ovf_list, nt.counters, a_out, d1_out);
+                               nt.full_list, nt.cand, nt.ccount, cap, nt.ovf_list, nt.counters, a_out, d1_out,
+                               ip ? 1 : 0);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 4. overflow: rescore against all K
@@ -1215,10 +1237,10 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
     if (nb > 2048) nb = 2048;
     if (C64 != nullptr)
         hipLaunchKernelGGL((k_recheck<double, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C64, K, xnorm64,
-                           nt.ovf_list, nt.counters + 2, P, a_out, d1_out);
+                           nt.ovf_list, nt.counters + 2, P, a_out, d1_out, ip ? 1 : 0);
     else
         hipLaunchKernelGGL((k_recheck<float, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C32, K, xnorm64,
-                           nt.ovf_list, nt.counters + 2, P, a_out, d1_out);
+                           nt.ovf_list, nt.counters + 2, P, a_out, d1_out, ip ? 1 : 0);
     return hipGetLastError();
 }
 

@@ -74,8 +74,9 @@ hipError_t launch_normalize_rows(const float *M, int64_t rows, int d, const doub
 hipError_t launch_gather_rows(const float *M, const int32_t *idx, int64_t rows, int d, float *out, hipStream_t s);
 // -||c||^2/2 (padded with -inf to kCentroidPad) and per-block maxima of the
 // centroid norms; with split scoring also writes the split operands.
+// ip: inner product (the scores are x.c: no -||c||^2/2 term)
 hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float *cmax_part, int *nparts,
-                                const SplitC &sc, hipStream_t s);
+                                const SplitC &sc, bool ip, hipStream_t s);
 hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, int32_t *counter,
                               hipStream_t s);
 // Near-tie bookkeeping of FlashAssign (all in the workspace):
@@ -96,13 +97,14 @@ constexpr int kCandPerSlot = 16;
 int64_t near_tie_cap(int64_t N);
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
                                const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
-                               const NearTies &nt, const SplitC &sc, hipStream_t s);
+                               const NearTies &nt, const SplitC &sc, bool ip, hipStream_t s);
 // Settles every listed near tie exactly (fp64 direct-difference distances).
 // C_mfma is the centroid array the MFMA pass used (normalised for cosine); C32
 // (L2) or C64 (cosine, normalised in fp64) is the one the distances use.
 hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma, const float *C32,
                           const double *C64, const float *ncn, int K, const float *scal, const double *xnorm64,
-                          const NearTies &nt, const SplitC &sc, int32_t *a_out, float *d1_out, hipStream_t s);
+                          const NearTies &nt, const SplitC &sc, bool ip, int32_t *a_out, float *d1_out,
+                          hipStream_t s);
 
 // Radix sort of (key = assign[i], value = i), stable, atomic-free.  Writes the
 // sorted keys and the permutation.  tmp* are N-sized scratch arrays.

@@ -16,9 +16,12 @@
  *     index, and the per-cluster sums are reduced by reading that index
  *     contiguously, with no atomic operations.
  * The article lists squared L2 and cosine as the supported metrics and inner
- * product as not yet supported (section "Not a silver bullet").  Cosine is L2
- * on L2-normalised vectors, a zero norm being taken as 1 before the divide
- * (LEANN FlashLib backend guide, mhpn.cn, paragraph "distance metric").  The
+ * product as the next one (section "Not a silver bullet").  Cosine is L2 on
+ * L2-normalised vectors, a zero norm being taken as 1 before the divide
+ * (LEANN FlashLib backend guide, mhpn.cn, paragraph "distance metric").
+ * Inner product assigns each point to the centroid of largest x.c (lowest
+ * index on ties, the dot product taken in fp64 in increasing j where it is
+ * settled) and updates with plain means; its min_dist is -max_k x.c.  The
  * out-of-core entry point follows the article's out-of-core mode, which keeps
  * the data in host memory and computes on the GPU (section "Real-time MoE
  * routing").
@@ -75,7 +78,7 @@ typedef enum {
 typedef enum {
     FK_METRIC_L2 = 0,            /* squared Euclidean distance                 */
     FK_METRIC_COSINE = 1,        /* L2 on rows normalised to unit length       */
-    FK_METRIC_INNER_PRODUCT = 2  /* not supported: returns FK_ERR_UNSUPPORTED  */
+    FK_METRIC_INNER_PRODUCT = 2  /* largest x.c (no normalisation)             */
 } fk_metric;
 
 /*

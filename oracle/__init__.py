@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-METRICS = {"l2": 0, "cosine": 1}
+METRICS = {"l2": 0, "cosine": 1, "inner_product": 2}
 
 _CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared"]
 
@@ -86,7 +86,8 @@ def num_threads() -> int:
 
 def assign(X, C, metric: str = "l2"):
     """Assignment step: for each row x_i of X, D_ik = ||x_i - c_k||^2 (fp64,
-    direct difference), a_i = lowest index attaining the minimum, D1 = that
+    direct difference; inner product: D_ik = -x_i.c_k, the dot product summed
+    in increasing j), a_i = lowest index attaining the minimum, D1 = that
     minimum, D2 = the minimum over the other centroids (inf when K == 1).
 
     Returns (a int32[N], D1 float64[N], D2 float64[N]).

@@ -42,6 +42,7 @@
 
 #define FKO_METRIC_L2 0
 #define FKO_METRIC_COSINE 1
+#define FKO_METRIC_INNER_PRODUCT 2
 
 /* Promote one fp32 row to fp64; for cosine divide it by its L2 norm, the
  * norm being taken as 1 when it is 0 (FlashLib guide, "距离度量"). */
@@ -72,6 +73,22 @@ static double sqdist(const double *x, const double *c, int64_t d)
     return acc;
 }
 
+/* Negated inner product -x.c, the dot product summed in increasing j: the
+ * largest inner product is the smallest of these, so the same lowest-index
+ * argmin gives the inner-product assignment. */
+static double negdot(const double *x, const double *c, int64_t d)
+{
+    double acc = 0.0;
+    for (int64_t j = 0; j < d; ++j)
+        acc = acc + x[j] * c[j];
+    return -acc;
+}
+
+static double score(const double *x, const double *c, int64_t d, int metric)
+{
+    return metric == FKO_METRIC_INNER_PRODUCT ? negdot(x, c, d) : sqdist(x, c, d);
+}
+
 /* Rows of C promoted (and, for cosine, normalised) once.  Returns NULL on
  * allocation failure. */
 static double *promote_matrix(const float *M, int64_t rows, int64_t d, int metric)
@@ -86,7 +103,7 @@ static double *promote_matrix(const float *M, int64_t rows, int64_t d, int metri
 
 /*
  * Assignment step.  For every point i:
- *   D_ik = ||x_i - c_k||^2 for all k,
+ *   D_ik = ||x_i - c_k||^2 for all k (inner product: D_ik = -x_i.c_k),
  *   a_i  = smallest k attaining min_k D_ik,
  *   D1_i = D_{i,a_i},
  *   D2_i = min over k != a_i of D_ik (+inf when K == 1).
@@ -98,7 +115,7 @@ int fko_assign(const float *X, int64_t N, int64_t d, const float *C, int64_t K,
 {
     if (N < 0 || d <= 0 || K <= 0 || (N > 0 && !X) || !C)
         return -1;
-    if (metric != FKO_METRIC_L2 && metric != FKO_METRIC_COSINE)
+    if (metric != FKO_METRIC_L2 && metric != FKO_METRIC_COSINE && metric != FKO_METRIC_INNER_PRODUCT)
         return -1;
     double *Cd = promote_matrix(C, K, d, metric);
     if (!Cd)
@@ -117,10 +134,10 @@ int fko_assign(const float *X, int64_t N, int64_t d, const float *C, int64_t K,
                 continue;
             promote_row(X + i * d, d, metric, xi);
             int64_t best_k = 0;
-            double best = sqdist(xi, Cd, d);
+            double best = score(xi, Cd, d, metric);
             double second = INFINITY;
             for (int64_t k = 1; k < K; ++k) {
-                double D = sqdist(xi, Cd + k * d, d);
+                double D = score(xi, Cd + k * d, d, metric);
                 if (D < best) {
                     second = best;
                     best = D;
@@ -144,7 +161,8 @@ int fko_assign(const float *X, int64_t N, int64_t d, const float *C, int64_t K,
 
 /*
  * Update step.  n_k = #{i : a_i = k}; s_k = sum of x_i over those i, in
- * increasing i, in fp64; C_out[k] = s_k / n_k, or C_in[k] (as passed, not
+ * increasing i, in fp64 (rows normalised for cosine; taken as they are for L2
+ * and inner product); C_out[k] = s_k / n_k, or C_in[k] (as passed, not
  * normalised) when n_k == 0.  Returns 0, or -1 on bad arguments (including a
  * label outside [0, K)) or allocation failure.
  */
@@ -153,7 +171,7 @@ int fko_update(const float *X, int64_t N, int64_t d, const int32_t *a, int64_t K
 {
     if (N < 0 || d <= 0 || K <= 0 || (N > 0 && (!X || !a)) || !C_in || !C_out || !counts)
         return -1;
-    if (metric != FKO_METRIC_L2 && metric != FKO_METRIC_COSINE)
+    if (metric != FKO_METRIC_L2 && metric != FKO_METRIC_COSINE && metric != FKO_METRIC_INNER_PRODUCT)
         return -1;
     for (int64_t i = 0; i < N; ++i)
         if (a[i] < 0 || (int64_t)a[i] >= K)

@@ -50,6 +50,19 @@ def centroid_rel_err(C_gpu, C_ref, counts):
 def check_min_dist(d1_gpu, D1, X, C, metric="l2", score="fp32"):
     X = np.asarray(X, np.float64)
     C = np.asarray(C, np.float64)
+    if metric == "inner_product":
+        # min_dist = -max x.c: the score's own bound, three times over
+        d = X.shape[1]
+        xn = np.sqrt((X * X).sum(1))
+        sqM = np.sqrt((C * C).sum(1).max())
+        n = d + 4
+        tol = 3 * n * 2.0 ** -24 * xn * sqM + 1e-30
+        if score == "split_bf16":
+            tol += 3 * 4.7e-5 * xn * sqM
+        err = np.abs(np.asarray(d1_gpu, np.float64) - D1)
+        bad = err > tol
+        assert not bad.any(), f"min_dist off at {np.nonzero(bad)[0][:5]}: err {err[bad][:5]} tol {tol[bad][:5]}"
+        return
     if metric == "cosine":
         nx = np.linalg.norm(X, axis=1, keepdims=True)
         nx[nx == 0] = 1

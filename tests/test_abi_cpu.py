@@ -49,7 +49,8 @@ def test_workspace_sizes(lib):
     assert fk.fk_workspace_size(1 << 24, 128, 32768) < 2 * 10 ** 9
     for bad in [(-1, 16, 4), (10, 0, 4), (10, 16, 0), (10, 16, 65537), (10, 4097, 4), (2 ** 31, 4, 4)]:
         assert lib.fk_workspace_size(*bad, 0, 0) == 0
-    assert lib.fk_workspace_size(10, 4, 4, 2, 0) == 0            # inner product
+    assert lib.fk_workspace_size(10, 4, 4, 2, 0) > 0             # inner product
+    assert lib.fk_workspace_size(10, 4, 4, 3, 0) == 0            # no such metric
 
 
 P = ctypes.c_void_p
@@ -70,9 +71,8 @@ def test_validation_happens_before_any_device_call(lib):
     assert _call_assign(lib, d=5000) == INVALID
     assert _call_assign(lib, K=0) == INVALID
     assert _call_assign(lib, K=70000) == INVALID
-    assert _call_assign(lib, metric=2) == UNSUPPORTED
-    assert b"inner-product" in lib.fk_last_error()
     assert _call_assign(lib, metric=7) == INVALID
+    assert b"metric" in lib.fk_last_error()
     assert _call_assign(lib, score=2) == INVALID
     assert b"score" in lib.fk_last_error()
     assert _call_assign(lib, X=0) == INVALID
@@ -153,5 +153,8 @@ def test_fit_and_ivf_validation(lib):
     assert ivf(50, 4, 2, idx) == INVALID and b"init_idx[3]" in lib.fk_last_error()
     assert ivf(500, 4, 0, idx) == INVALID and b"n_iter" in lib.fk_last_error()
     assert ivf(500, 4, 2, None) == INVALID
+    st = lib.fk_ivf_build(args["X"], 500, 8, 4, 2, 0, 2, idx, args["cent"], args["offs"], args["ids"], args["data"],
+                          ws, 1 << 30, None)
+    assert st == UNSUPPORTED and b"inner product" in lib.fk_last_error()
     assert lib.fk_ivf_workspace_size(10, 8, 11, 0) == 0
     assert fk.fk_ivf_workspace_size(1000, 16, 10, "cosine") > fk.fk_ivf_workspace_size(1000, 16, 10)

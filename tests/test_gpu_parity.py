@@ -196,7 +196,10 @@ def test_error_paths_on_device(gpu_lib):
     X = torch.zeros((100, 8), device="cuda:0")
     C = torch.zeros((4, 8), device="cuda:0")
     with pytest.raises(fk.FkError) as e:
-        fk.fk_assign(X, C, metric="inner_product")
+        fk.fk_assign(X, C, metric=3)
+    assert e.value.status == 1
+    with pytest.raises(fk.FkError) as e:
+        fk.fk_ivf_build(X, 4, np.arange(4, dtype=np.int32), metric="inner_product")
     assert e.value.status == 2
     with pytest.raises(fk.FkError) as e:
         fk.fk_assign(X, C, score=5)
@@ -216,3 +219,35 @@ def test_error_paths_on_device(gpu_lib):
                                   None, ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(cnt.data_ptr()),
                                   ctypes.c_void_p(base), ws.numel() - 256, None)
     assert st == 1 and b"pinned" in lib.fk_last_error()
+
+
+# ------------------------------------------------------------ inner product
+
+@pytest.mark.parametrize("score", SCORES)
+@pytest.mark.parametrize("N,d,K", [(1000, 16, 64), (4097, 128, 33), (2049, 129, 65), (777, 768, 300), (5, 3, 7),
+                                   (3000, 100, 1000)])
+@pytest.mark.parametrize("kind", ["gauss", "dup", "dup3", "grid", "zero"])
+def test_inner_product_assign_matches_oracle(gpu_lib, N, d, K, kind, score):
+    fk = gpu_lib
+    log(f"ip assign N={N} d={d} K={K} kind={kind} score={score}")
+    X, C = synth.adversarial(5, N, d, K, kind)
+    a_ref, D1, _ = oracle.assign(X, C, "inner_product")
+    a, md = fk.fk_assign(dev(X), dev(C), metric="inner_product", with_min_dist=True, score=score)
+    np.testing.assert_array_equal(host(a), a_ref)
+    check_min_dist(host(md), D1, X, C, metric="inner_product", score=score)
+
+
+@pytest.mark.parametrize("score", SCORES)
+def test_inner_product_iteration(gpu_lib, score):
+    fk = gpu_lib
+    w = synth.WORKLOADS["gmm_1m_d128_k1024"].scaled(20011)
+    X = synth.rows(w)
+    C = X[synth.init_indices(w)[:300]].copy()
+    Xd, Cd = dev(X), dev(C)
+    for it in range(3):
+        a, Cn, n, _ = fk.fk_lloyd_iter(Xd, Cd, metric="inner_product", score=score)
+        a = host(a)
+        a_ref, _, _ = oracle.assign(X, host(Cd), "inner_product")
+        np.testing.assert_array_equal(a, a_ref)
+        check_update(X, a, host(Cd), host(Cn), host(n), "inner_product")
+        Cd = Cn

@@ -385,3 +385,52 @@ def test_ivf_build_layout_by_brute_force(metric):
         pos += len(members)
     assert r["offsets"][13] == 420 == pos
     np.testing.assert_array_equal(r["data"], Xu[r["ids"]])
+
+
+# ------------------------------------------------------------ inner product
+
+@pytest.mark.parametrize("N,d,K,seed", [(300, 5, 17, 51), (64, 33, 3, 52), (1000, 2, 40, 53)])
+def test_inner_product_assign_matches_bruteforce(N, d, K, seed):
+    rng = np.random.default_rng(seed)
+    X = rng.standard_normal((N, d)).astype(np.float32)
+    C = rng.standard_normal((K, d)).astype(np.float32)
+    a, D1, D2 = oracle.assign(X, C, "inner_product")
+    S = X.astype(np.float64) @ C.astype(np.float64).T
+    np.testing.assert_array_equal(a, S.argmax(1))
+    np.testing.assert_allclose(D1, -S.max(1), rtol=1e-12, atol=1e-12)
+    part = np.sort(S, axis=1)
+    np.testing.assert_allclose(D2, -part[:, -2], rtol=1e-12, atol=1e-12)
+
+
+def test_inner_product_exact_integer_ties_lowest_index():
+    rng = np.random.default_rng(54)
+    X = rng.integers(-4, 5, size=(200, 6)).astype(np.float32)
+    base = rng.integers(-3, 4, size=(5, 6))
+    C = np.concatenate([base, base[[2, 0]]]).astype(np.float32)     # rows 5, 6 copy rows 2, 0
+    a, _, _ = oracle.assign(X, C, "inner_product")
+    dots = [[sum(Fraction(int(x[j])) * int(c[j]) for j in range(6)) for c in C] for x in X]
+    expect = [max(range(7), key=lambda k: (row[k], -k)) for row in dots]
+    np.testing.assert_array_equal(a, expect)
+
+
+def test_inner_product_on_unit_centroids_is_l2_order():
+    """With unit-norm centroids, -2 x.c = ||x - c||^2 - ||x||^2 - 1, so the
+    largest inner product is the nearest centroid."""
+    rng = np.random.default_rng(55)
+    X = rng.standard_normal((400, 9)).astype(np.float32)
+    C = oracle.normalize_rows(rng.standard_normal((25, 9)).astype(np.float32))
+    a_ip, D1, D2 = oracle.assign(X, C, "inner_product")
+    a_l2, E1, E2 = oracle.assign(X, C, "l2")
+    close = oracle.relative_gap(E1, E2) < 1e-6
+    np.testing.assert_array_equal(a_ip[~close], a_l2[~close])
+
+
+def test_inner_product_update_is_plain_mean():
+    rng = np.random.default_rng(56)
+    X = rng.standard_normal((300, 4)).astype(np.float32)
+    a = rng.integers(0, 9, size=300).astype(np.int32)
+    C0 = rng.standard_normal((9, 4)).astype(np.float32)
+    C_ip, n_ip = oracle.update(X, a, C0, "inner_product")
+    C_l2, n_l2 = oracle.update(X, a, C0, "l2")
+    np.testing.assert_array_equal(C_ip, C_l2)
+    np.testing.assert_array_equal(n_ip, n_l2)
