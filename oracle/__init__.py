@@ -62,6 +62,8 @@ def _load():
         lib.fko_lloyd_iter.restype = ctypes.c_int
         lib.fko_normalize_rows.argtypes = [P, I64, I64, P]
         lib.fko_normalize_rows.restype = ctypes.c_int
+        lib.fko_knn.argtypes = [P, I64, I64, P, I64, I64, ctypes.c_int, P, P]
+        lib.fko_knn.restype = ctypes.c_int
         lib.fko_num_threads.argtypes = []
         lib.fko_num_threads.restype = ctypes.c_int
         _lib = lib
@@ -192,6 +194,26 @@ def ivf_build(X, init_idx, n_iter: int, metric: str = "l2"):
     counts = np.bincount(a, minlength=C.shape[0])
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     return {"centroids": C, "labels": a, "offsets": offsets, "ids": ids, "data": Xu[ids]}
+
+
+def knn(Q, DB, k: int, metric: str = "l2"):
+    """Exact k nearest neighbours by brute force (LEANN FlashLib guide,
+    paragraph "何时使用": the exact GPU k-NN backend): for each query, the k
+    database rows first in (fp64 distance, row index) order, the distance
+    being the assignment step's (cosine: both rows normalised; inner
+    product: -q.x).  Returns (idx int32[M, k], dist float64[M, k])."""
+    Q = _f32(Q)
+    DB = _f32(DB)
+    M, d = Q.shape
+    Ndb, dd = DB.shape
+    if dd != d:
+        raise ValueError("Q and DB differ in d")
+    idx = np.empty((M, k), np.int32)
+    dist = np.empty((M, k), np.float64)
+    rc = _load().fko_knn(_ptr(Q), M, d, _ptr(DB), Ndb, int(k), METRICS[metric], _ptr(idx), _ptr(dist))
+    if rc != 0:
+        raise ValueError("oracle knn rejected its arguments")
+    return idx, dist
 
 
 def relative_gap(D1, D2):

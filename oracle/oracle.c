@@ -275,3 +275,70 @@ int fko_normalize_rows(const float *X, int64_t N, int64_t d, float *out)
     free(row);
     return 0;
 }
+
+/*
+ * Exact k nearest neighbours by brute force (the exact GPU k-NN backend of
+ * the LEANN FlashLib guide, paragraph "何时使用" (when to use)).  For every
+ * query q: D_j = the distance of q to database row j by the metric above (for
+ * cosine both rows normalised; inner product: -q.x_j) for every j, and
+ * idx[q, 0..k) = the k rows that come first when all rows are ordered by
+ * (D_j, j), with dist[q, r] = D of idx[q, r].  The scan over j in increasing
+ * order keeps the k first rows seen so far in that order: a new row goes
+ * after every kept row of distance <= its own, so ties keep the lower index
+ * first.  Requires 1 <= k <= Ndb.  Returns 0, or -1 on bad arguments or
+ * allocation failure.
+ */
+int fko_knn(const float *Q, int64_t M, int64_t d, const float *DB, int64_t Ndb, int64_t k,
+            int metric, int32_t *idx, double *dist)
+{
+    if (M < 0 || d <= 0 || Ndb <= 0 || k < 1 || k > Ndb || (M > 0 && (!Q || !idx || !dist)) || !DB)
+        return -1;
+    if (metric != FKO_METRIC_L2 && metric != FKO_METRIC_COSINE && metric != FKO_METRIC_INNER_PRODUCT)
+        return -1;
+    double *Dd = promote_matrix(DB, Ndb, d, metric);
+    if (!Dd)
+        return -1;
+    int failed = 0;
+#pragma omp parallel
+    {
+        double *qi = (double *)malloc((size_t)d * sizeof(double));
+        double *bd = (double *)malloc((size_t)k * sizeof(double));
+        int64_t *bi = (int64_t *)malloc((size_t)k * sizeof(int64_t));
+        if (!qi || !bd || !bi) {
+#pragma omp atomic write
+            failed = 1;
+        }
+#pragma omp for schedule(dynamic, 4)
+        for (int64_t q = 0; q < M; ++q) {
+            if (!qi || !bd || !bi)
+                continue;
+            promote_row(Q + q * d, d, metric, qi);
+            int64_t kept = 0;
+            for (int64_t j = 0; j < Ndb; ++j) {
+                double D = score(qi, Dd + j * d, d, metric);
+                if (kept == k && !(D < bd[k - 1]))
+                    continue;
+                /* position: after every kept entry with distance <= D */
+                int64_t pos = kept < k ? kept : k - 1;
+                while (pos > 0 && bd[pos - 1] > D) {
+                    bd[pos] = bd[pos - 1];
+                    bi[pos] = bi[pos - 1];
+                    --pos;
+                }
+                bd[pos] = D;
+                bi[pos] = j;
+                if (kept < k)
+                    ++kept;
+            }
+            for (int64_t r = 0; r < k; ++r) {
+                idx[q * k + r] = (int32_t)bi[r];
+                dist[q * k + r] = bd[r];
+            }
+        }
+        free(qi);
+        free(bd);
+        free(bi);
+    }
+    free(Dd);
+    return failed ? -1 : 0;
+}

@@ -18,7 +18,10 @@ Recipe (all draws from numpy ``default_rng`` / PCG64):
     and stored as float32 (the IVF coarse-quantizer shape: cosine reduced to
     L2 on unit vectors);
   * initial centroids: the first K rows, or the rows
-    ``default_rng([seed, 1]).choice(N, K, replace=False)`` in drawn order.
+    ``default_rng([seed, 1]).choice(N, K, replace=False)`` in drawn order;
+  * k-NN queries: rows of the same mixture drawn as above, block b with
+    ``default_rng([seed, 3, b])``; means "zero" makes every row plain
+    standard normal noise (the FlashLib guide's ``randn`` example).
 
 Because every block has its own generator, any row range can be generated on
 its own, in parallel, and gives the same bytes as a full generation.
@@ -50,6 +53,8 @@ class Workload:
     normalize: bool
     metric: str = "l2"
     chunk_rows: int = 0  # rows per host->device chunk for the out-of-core shape
+    queries: int = 0     # k-NN shapes: query rows
+    k: int = 0           # k-NN shapes: neighbours per query
 
     def scaled(self, N: int) -> "Workload":
         """Same recipe with fewer rows (the first N rows of the full set are
@@ -72,13 +77,22 @@ WORKLOADS = {
     # Out-of-core headline shape: 1e9 x 128, K=32,768, equal weights, sigma 0.2,
     # seed 3, one iteration, 2^26-row host->device chunks.
     "ooc_1b_d128_k32768": Workload("ooc_1b_d128_k32768", 1000000000, 128, 32768, 0.2, "normal", "equal", 0.0, 3, "sample", 1, False, "l2", 1 << 26),
+    # Exact k-NN, the FlashLib guide's example: a 1,000,000 x 128 standard
+    # normal database, 10,000 standard normal queries, 10 neighbours, seed 4.
+    "knn_1m_d128_q10k": Workload("knn_1m_d128_q10k", 1000000, 128, 1, 1.0, "zero", "equal", 0.0, 4, "first", 1, False, "l2", 0, 10000, 10),
+    # Exact k-NN on the guide's benchmark corpus shape: 1,000,000 x 768, a
+    # mixture of 8,192 Gaussians (more components than the IVF's 4,096 cells),
+    # sigma 0.5, 10,000 queries from the same mixture, 10 neighbours, seed 5.
+    "knn_1m_d768_q10k": Workload("knn_1m_d768_q10k", 1000000, 768, 8192, 0.5, "normal", "equal", 0.0, 5, "first", 1, False, "l2", 0, 10000, 10),
 }
 
 
 def means(w: Workload) -> np.ndarray:
     """Component means, float32 [K, d]."""
     rng = np.random.default_rng([w.seed, 0])
-    if w.means == "uniform":
+    if w.means == "zero":
+        m = np.zeros((w.K, w.d))
+    elif w.means == "uniform":
         m = rng.uniform(-1.0, 1.0, size=(w.K, w.d))
     else:
         m = rng.standard_normal((w.K, w.d))
@@ -93,9 +107,10 @@ def weights(w: Workload):
     return r / r.sum()
 
 
-def _block(w: Workload, mu: np.ndarray, p, b: int, lo: int, hi: int, out: np.ndarray):
-    """Rows [lo, hi) of block b (lo, hi relative to the block start) into out."""
-    rng = np.random.default_rng([w.seed, 2, b])
+def _block(w: Workload, mu: np.ndarray, p, b: int, lo: int, hi: int, out: np.ndarray, stream: int = 2):
+    """Rows [lo, hi) of block b (lo, hi relative to the block start) into out
+    (stream 2: the rows of X, stream 3: the k-NN queries)."""
+    rng = np.random.default_rng([w.seed, stream, b])
     n = BLOCK  # always a whole block, so a scaled workload is a prefix of the full one
     if p is None:
         labels = rng.integers(0, w.K, size=n)
@@ -156,6 +171,20 @@ def rows(w: Workload, start: int = 0, stop: int | None = None, out: np.ndarray |
         with ThreadPoolExecutor(threads) as ex:
             list(ex.map(run, jobs))
     return (out, labels) if return_labels else out
+
+
+def queries(w: Workload, M: int | None = None) -> np.ndarray:
+    """The first M (default: w.queries) k-NN query rows, float32 [M, d]: the
+    same mixture as the rows of X, from their own generators."""
+    M = w.queries if M is None else int(M)
+    out = np.empty((M, w.d), np.float32)
+    mu = means(w)
+    p = weights(w)
+    for b in range((M + BLOCK - 1) // BLOCK):
+        lo = b * BLOCK
+        hi = min(M, lo + BLOCK)
+        _block(w, mu, p, b, 0, hi - lo, out[lo:hi], stream=3)
+    return out
 
 
 def init_indices(w: Workload) -> np.ndarray:

@@ -434,3 +434,96 @@ def test_inner_product_update_is_plain_mean():
     C_l2, n_l2 = oracle.update(X, a, C0, "l2")
     np.testing.assert_array_equal(C_ip, C_l2)
     np.testing.assert_array_equal(n_ip, n_l2)
+
+
+# ---- exact k nearest neighbours (LEANN FlashLib guide, paragraph "何时使用":
+# the exact GPU k-NN backend)
+
+def _lex_topk(D, k):
+    """k first columns of each row of D in (value, column) order."""
+    cols = np.arange(D.shape[1])
+    return np.stack([np.lexsort((cols, row))[:k] for row in D])
+
+
+@pytest.mark.parametrize("metric", ["l2", "inner_product"])
+@pytest.mark.parametrize("k", [1, 5, 17])
+def test_knn_exact_integers_with_ties(metric, k):
+    """Integer rows: every distance is an exact integer in fp64, so the order
+    is fixed exactly (int64 arithmetic here), with many ties that must go to
+    the lower row index."""
+    rng = np.random.default_rng(60 + k)
+    Q = rng.integers(-3, 4, size=(40, 5))
+    base = rng.integers(-3, 4, size=(30, 5))
+    DB = np.concatenate([base, base[::3], base[:7]])              # duplicated rows: exact ties
+    if metric == "l2":
+        D = ((Q[:, None, :] - DB[None, :, :]) ** 2).sum(-1)
+    else:
+        D = -(Q[:, None, :] * DB[None, :, :]).sum(-1)
+    idx, dist = oracle.knn(Q.astype(np.float32), DB.astype(np.float32), k, metric)
+    expect = _lex_topk(D, k)
+    np.testing.assert_array_equal(idx, expect)
+    np.testing.assert_array_equal(dist, np.take_along_axis(D, expect, 1).astype(np.float64))
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_knn_matches_cdist_where_ranks_are_clear(seed):
+    """Continuous data against scipy's direct-difference distances: the order
+    of the k first rows, and every row left out being at least as far."""
+    rng = np.random.default_rng(70 + seed)
+    Q = rng.standard_normal((60, 12)).astype(np.float32)
+    DB = rng.standard_normal((500, 12)).astype(np.float32)
+    k = 10
+    idx, dist = oracle.knn(Q, DB, k)
+    D = scipy.spatial.distance.cdist(Q.astype(np.float64), DB.astype(np.float64), "sqeuclidean")
+    order = np.argsort(D, axis=1, kind="stable")
+    srt = np.take_along_axis(D, order, 1)
+    clear = (np.diff(srt[:, :k + 1], axis=1) > 1e-9 * srt[:, 1:k + 1]).all(1)
+    assert clear.mean() > 0.9
+    np.testing.assert_array_equal(idx[clear], order[clear, :k])
+    np.testing.assert_allclose(dist, np.take_along_axis(D, idx.astype(np.int64), 1), rtol=1e-12)
+    assert (np.diff(dist, axis=1) >= 0).all()
+
+
+def test_knn_k1_is_the_assignment_and_k_eq_n_is_a_full_sort():
+    rng = np.random.default_rng(80)
+    Q = rng.standard_normal((50, 6)).astype(np.float32)
+    DB = rng.standard_normal((23, 6)).astype(np.float32)
+    a, D1, _ = oracle.assign(Q, DB)
+    idx, dist = oracle.knn(Q, DB, 1)
+    np.testing.assert_array_equal(idx[:, 0], a)
+    np.testing.assert_array_equal(dist[:, 0], D1)
+    idx, dist = oracle.knn(Q, DB, 23)
+    assert all(sorted(r) == list(range(23)) for r in idx.tolist())
+    assert (np.diff(dist, axis=1) >= 0).all()
+
+
+def test_knn_cosine_is_largest_cosine_similarity():
+    """For unit rows ||q - x||^2 = 2 - 2 cos(q, x): nearest is most similar,
+    whatever the rows' lengths (zero rows count as having norm 1)."""
+    rng = np.random.default_rng(81)
+    Q = (rng.standard_normal((40, 7)) * rng.uniform(0.1, 9, (40, 1))).astype(np.float32)
+    DB = (rng.standard_normal((200, 7)) * rng.uniform(0.1, 9, (200, 1))).astype(np.float32)
+    DB[5] = 0.0
+    k = 6
+    idx, dist = oracle.knn(Q, DB, k, "cosine")
+    q = Q.astype(np.float64)
+    x = DB.astype(np.float64)
+    nq = np.linalg.norm(q, axis=1, keepdims=True)
+    nx = np.linalg.norm(x, axis=1, keepdims=True)
+    nx[nx == 0] = 1.0
+    cs = (q / nq) @ (x / nx).T
+    order = np.argsort(-cs, axis=1, kind="stable")
+    srt = np.take_along_axis(-cs, order, 1)
+    clear = (np.diff(srt[:, :k + 1], axis=1) > 1e-9).all(1)
+    assert clear.mean() > 0.9
+    np.testing.assert_array_equal(idx[clear], order[clear, :k])
+    np.testing.assert_allclose(dist, 2.0 - 2.0 * np.take_along_axis(cs, idx.astype(np.int64), 1), atol=1e-12)
+
+
+def test_knn_rejects_k_above_database_size():
+    Q = np.zeros((2, 3), np.float32)
+    DB = np.zeros((4, 3), np.float32)
+    with pytest.raises(ValueError):
+        oracle.knn(Q, DB, 5)
+    with pytest.raises(ValueError):
+        oracle.knn(Q, DB, 0)

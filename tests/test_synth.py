@@ -84,3 +84,15 @@ def test_adversarial_inputs(kind):
     X2, C2 = synth.adversarial(1, 100, 7, 9, kind)
     assert X.dtype == np.float32 and X.shape == (100, 7) and C.shape == (9, 7)
     assert X.tobytes() == X2.tobytes() and C.tobytes() == C2.tobytes()
+
+
+def test_knn_queries_are_seeded_prefixes_and_differ_from_rows():
+    w = synth.WORKLOADS["knn_1m_d128_q10k"]
+    q = synth.queries(w, 3000)
+    np.testing.assert_array_equal(q[:1000], synth.queries(w, 1000))
+    np.testing.assert_array_equal(q, synth.queries(w, 3000))
+    x = synth.rows(w.scaled(70000), 0, 3000)
+    assert not np.array_equal(q, x)
+    # the "zero" means: plain standard normal draws
+    assert abs(float(q.mean())) < 0.01 and abs(float(q.std()) - 1.0) < 0.01
+    assert synth.queries(w).shape == (w.queries, w.d)
