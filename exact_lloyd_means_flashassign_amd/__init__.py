@@ -69,8 +69,11 @@ def load():
     lib.fk_ivf_workspace_size.argtypes = [I64, I32, I32, I32]
     lib.fk_ivf_workspace_size.restype = SZ
     lib.fk_ivf_build.argtypes = [P, I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]
+    lib.fk_knn_workspace_size.argtypes = [I64, I32, I64, I32, I32]
+    lib.fk_knn_workspace_size.restype = SZ
+    lib.fk_knn.argtypes = [P, I64, I32, P, I64, I32, I32, I32, P, P, P, SZ, P]
     for f in ("fk_assign", "fk_sort_inverse", "fk_update", "fk_lloyd_iter", "fk_lloyd_iter_stream",
-              "fk_fit", "fk_ivf_build", "fk_profile_enable", "fk_profile_read"):
+              "fk_fit", "fk_ivf_build", "fk_knn", "fk_profile_enable", "fk_profile_read"):
         getattr(lib, f).restype = ctypes.c_int
     lib.fk_status_str.argtypes = [I32]
     lib.fk_status_str.restype = ctypes.c_char_p
@@ -365,6 +368,38 @@ def fk_ivf_build(X, nlist: int, init_idx, n_iter: int = 20, metric="l2", workspa
                                _ptr(out["ids"]), _ptr(out["data"]), ctypes.c_void_p(p), ctypes.c_size_t(n),
                                _stream(dev)))
     return out
+
+
+def fk_knn_workspace_size(M: int, d: int, Ndb: int, k: int, metric="l2") -> int:
+    n = load().fk_knn_workspace_size(int(M), int(d), int(Ndb), int(k), _metric(metric))
+    if n == 0:
+        raise FkError(1, f"sizes outside the limits: M={M} d={d} Ndb={Ndb} k={k}")
+    return int(n)
+
+
+def fk_knn(Q, DB, k: int, metric="l2", idx=None, dist=None, workspace=None, score="fp32"):
+    """Exact k nearest database rows of every query: returns (idx [M, k'] int32,
+    dist [M, k'] fp32), nearest first (lower row index first on equal
+    distances), where k' = min(k, Ndb) as the FlashLib backend clamps top_k to
+    the corpus size."""
+    _dev(Q, "Q", torch.float32)
+    _dev(DB, "DB", torch.float32)
+    if Q.dim() != 2 or DB.dim() != 2 or Q.shape[1] != DB.shape[1]:
+        raise ValueError("Q[M,d] and DB[Ndb,d] must be 2-D with the same d")
+    M, d = Q.shape
+    Ndb = DB.shape[0]
+    kk = min(int(k), int(Ndb))
+    if idx is None:
+        idx = torch.empty((M, kk), dtype=torch.int32, device=Q.device)
+    if dist is None:
+        dist = torch.empty((M, kk), dtype=torch.float32, device=Q.device)
+    _dev(idx, "idx", torch.int32, (M, kk))
+    _dev(dist, "dist", torch.float32, (M, kk))
+    need = load().fk_knn_workspace_size(int(M), int(d), int(Ndb), kk, _metric(metric)) or 256
+    p, n = _workspace(need, Q.device, workspace)
+    _check(load().fk_knn(_ptr(Q), M, d, _ptr(DB), Ndb, kk, _metric(metric), _score(score), _ptr(idx), _ptr(dist),
+                         ctypes.c_void_p(p), ctypes.c_size_t(n), _stream(Q.device)))
+    return idx, dist
 
 
 def fk_profile_enable(on: bool = True):

@@ -44,6 +44,7 @@ struct Layout {
     size_t sums, cnt, pfirst, plast, csplit, ncsplit;
     size_t xchunk[2], achunk[2];      // out-of-core only
     size_t ctmp, cinit, labels, xcopy;  // fit / IVF build only
+    size_t knn_cand, knn_score, knn_win, knn_list;  // k nearest neighbours only
 };
 
 constexpr size_t kNone = ~(size_t)0;
@@ -100,6 +101,45 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc, int extras 
     L.cinit = ivf ? take((size_t)K * d * 4) : kNone;
     L.labels = ivf ? take((size_t)r * 4) : kNone;
     L.xcopy = (ivf && cos) ? take((size_t)r * d * 4) : kNone;
+    L.knn_cand = L.knn_score = L.knn_win = L.knn_list = kNone;
+    L.total = off;
+    return L;
+}
+
+// k nearest neighbours of M queries among Ndb database rows: the database
+// takes the centroids' buffers (norms, split copy, cosine copies), the queries
+// the points' (norms), plus L candidates and a list slot per query.
+Layout make_knn_layout(int64_t M, int d, int64_t Ndb, int k, int metric) {
+    Layout L;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off += align_up(bytes > 0 ? bytes : 1, 256);
+        return o;
+    };
+    const int64_t m = M > 0 ? M : 1;
+    const int64_t Kpad = cdiv(Ndb, kCentroidPad) * kCentroidPad;
+    const bool cos = metric == FK_METRIC_COSINE;
+    L.ncn = take((size_t)Kpad * 4);
+    L.cmax_part = take((size_t)cdiv(Kpad, 4) * 3 * 4);
+    L.scal = take(64);
+    L.counter = take(64);
+    L.c64 = cos ? take((size_t)Ndb * d * 8) : kNone;
+    L.c32 = cos ? take((size_t)Ndb * d * 4) : kNone;
+    L.cnrm64 = cos ? take((size_t)Ndb * 8) : kNone;
+    L.xnorm64 = cos ? take((size_t)m * 8) : kNone;
+    L.csplit = take((size_t)Kpad * 2 * split_width(d) * 2);
+    L.ncsplit = take((size_t)Kpad * 16);
+    const size_t ncand = (size_t)m * knn_slices(m, Ndb).slices * knn_list_len(k);
+    L.knn_cand = take(ncand * 4);
+    L.knn_score = take(ncand * 4);
+    L.knn_win = take((size_t)m * 4);
+    L.knn_list = take((size_t)m * 4);
+    L.flags = L.thr = L.pairs = L.cand = L.ccount = L.ovf = kNone;
+    L.keys_sorted = L.perm = L.tmp_keys = L.tmp_vals = L.sort_scratch = L.offsets = kNone;
+    L.sums = L.cnt = L.pfirst = L.plast = kNone;
+    L.xchunk[0] = L.xchunk[1] = L.achunk[0] = L.achunk[1] = kNone;
+    L.ctmp = L.cinit = L.labels = L.xcopy = kNone;
     L.total = off;
     return L;
 }
@@ -678,6 +718,63 @@ fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int3
     {
         PhaseScope ph(FK_PH_REDUCE, s);
         FK_TRY(launch_gather_rows(Xu, list_ids, N, d, list_data, s), "list rows");
+    }
+    return FK_OK;
+}
+
+size_t fk_knn_workspace_size(int64_t M, int32_t d, int64_t Ndb, int32_t k, int32_t metric) {
+    if (M < 0 || M > INT32_MAX || d < 1 || d > FK_MAX_D || Ndb < 1 || Ndb > FK_MAX_KNN_DB) return 0;
+    if (k < 1 || k > FK_MAX_KNN_K || k > Ndb) return 0;
+    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE && metric != FK_METRIC_INNER_PRODUCT) return 0;
+    return make_knn_layout(M, d, Ndb, k, metric).total;
+}
+
+fk_status fk_knn(const float *Q, int64_t M, int32_t d, const float *DB, int64_t Ndb, int32_t k, int32_t metric,
+                 int32_t score, int32_t *idx, float *dist, void *workspace, size_t workspace_bytes, void *stream) {
+    g_err[0] = 0;
+    if (M < 0 || M > INT32_MAX) return fail(FK_ERR_INVALID_ARG, "M=%lld outside [0, 2^31-1]", (long long)M);
+    if (d < 1 || d > FK_MAX_D) return fail(FK_ERR_INVALID_ARG, "d=%d outside [1, %d]", (int)d, FK_MAX_D);
+    if (Ndb < 1 || Ndb > FK_MAX_KNN_DB)
+        return fail(FK_ERR_INVALID_ARG, "Ndb=%lld outside [1, %d]", (long long)Ndb, FK_MAX_KNN_DB);
+    if (k < 1 || k > FK_MAX_KNN_K || k > Ndb)
+        return fail(FK_ERR_INVALID_ARG, "k=%d outside [1, min(%d, Ndb=%lld)]", (int)k, FK_MAX_KNN_K, (long long)Ndb);
+    fk_status st = check_metric(metric);
+    if (st != FK_OK) return st;
+    if ((st = check_score(score)) != FK_OK) return st;
+    if (DB == nullptr) return fail(FK_ERR_INVALID_ARG, "DB is NULL");
+    if (M > 0 && (Q == nullptr || idx == nullptr || dist == nullptr))
+        return fail(FK_ERR_INVALID_ARG, "Q, idx and dist are required");
+    if (!aligned(DB, 16) || (Q != nullptr && !aligned(Q, 16)))
+        return fail(FK_ERR_INVALID_ARG, "Q and DB must be 16-byte aligned");
+    if (score == FK_SCORE_SPLIT_BF16 &&
+        cdiv(Ndb, kCentroidPad) * kCentroidPad * 4 * (int64_t)split_width(d) > (int64_t)UINT32_MAX)
+        return fail(FK_ERR_UNSUPPORTED, "split scoring: the database's bf16 copy (Ndb=%lld, d=%d) exceeds 4 GiB",
+                    (long long)Ndb, (int)d);
+    const Layout L = make_knn_layout(M, d, Ndb, k, metric);
+    if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
+    if ((st = check_device()) != FK_OK) return st;
+    if (M == 0) return FK_OK;
+    const hipStream_t s = (hipStream_t)stream;
+    const Ctx c{L, workspace, s, d, (int)Ndb, metric, score};
+    const float *DBu = nullptr;
+    if ((st = step_prep(c, DB, &DBu)) != FK_OK) return st;
+    if ((st = step_xnorm(c, Q, M)) != FK_OK) return st;
+    const bool cos = metric == FK_METRIC_COSINE, ip = metric == FK_METRIC_INNER_PRODUCT;
+    const double *qn = cos ? at<double>(workspace, L.xnorm64) : nullptr;
+    int32_t *cand = at<int32_t>(workspace, L.knn_cand), *list = at<int32_t>(workspace, L.knn_list);
+    float *cscore = at<float>(workspace, L.knn_score), *win = at<float>(workspace, L.knn_win);
+    int32_t *counters = at<int32_t>(workspace, L.counter);
+    {
+        PhaseScope ph(FK_PH_ASSIGN, s);
+        FK_TRY(launch_knn_sweep(Q, M, d, DBu, at<float>(workspace, L.ncn), (int)Ndb, at<float>(workspace, L.scal), qn,
+                                c.split(), ip, k, cand, cscore, win, s),
+               "knn sweep");
+    }
+    {
+        PhaseScope ph(FK_PH_RECHECK, s);
+        FK_TRY(launch_knn_finish(Q, M, d, DB, cos ? at<double>(workspace, L.c64) : nullptr, qn, ip, cand, cscore, win,
+                                 k, (int)Ndb, list, counters, idx, dist, s),
+               "knn finish");
     }
     return FK_OK;
 }

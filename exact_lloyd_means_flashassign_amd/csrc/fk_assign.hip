@@ -52,6 +52,16 @@ struct FlashArgs {
     const __bf16 *ncs;   // split scoring: -||c||^2/2 as three bf16 parts + 5 zeros
     unsigned cs_bytes;   // size of the split copy
     int ip;              // inner product: scores are x.c (no -||c||^2/2 term)
+    // top-L mode: the centroid rows are cut into knn_slices slices of
+    // knn_rows rows (a multiple of the tile height); workgroup (x, y) sweeps
+    // point block x against slice y and writes, per point and slice, its L
+    // best scores and their indices, best first (lower index first on equal
+    // scores), at ((point * knn_slices + y) * L); slice 0 also writes each
+    // point's score error window
+    int knn_slices, knn_rows, knn_tps;
+    int32_t *knn_cand;
+    float *knn_score;
+    float *knn_win;
 };
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -256,8 +266,12 @@ __global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ c
 // the full list.  For cosine, the fp32 normalised rows differ from the fp64
 // normalised ones by at most 3.1u relative, which moves a by at most
 // 3.1u (||x|| ||c|| + ||c||^2); 8u is added to g for it.
-template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool VEC, bool COLLECT, bool SPLIT>
+template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool VEC, bool COLLECT, bool SPLIT, int TL = 0>
 __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashArgs A) {
+    // TL > 0: k-nearest-neighbour mode; every lane keeps its TL best scores
+    // (and their indices) sorted, the two half-lanes of a point are merged at
+    // the end and the point's TL best candidates are written out.
+    static_assert(TL == 0 || (!COLLECT && (TL & (TL - 1)) == 0), "top-L mode: a power of two, no collect pass");
     constexpr int NT = WAVES * 64;
     constexpr int HALF = DP / 2;
     constexpr int ROWS = CB * 32;
@@ -398,6 +412,17 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         // the remainders x - hi - lo (for the bound on the dropped terms)
         float xl2[PB], xr2[PB];
         int i1[PB], i2[PB];
+        // top-L mode: sorted best-first scores and indices (lower index first
+        // on equal scores)
+        float bl[PB][TL > 0 ? TL : 1];
+        int il[PB][TL > 0 ? TL : 1];
+#pragma unroll
+        for (int b = 0; b < PB; ++b)
+#pragma unroll
+            for (int j = 0; j < (TL > 0 ? TL : 1); ++j) {
+                bl[b][j] = -INFINITY;
+                il[b][j] = 0x7fffffff;
+            }
         int64_t pt[PB];
         bool pv[PB];
 #pragma unroll
@@ -550,6 +575,44 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         // Fold one 32-centroid block of scores (a) of point block b, centroid
         // indices kb + 8(r/4) + r%4, into this lane's state.
         auto epilogue = [&](const v16f &a, int b, int kb) {
+            if constexpr (TL > 0) {
+                // take the group's values in decreasing order (the lowest
+                // index first among equals) while any lane of the wave still
+                // has one above its L-th best, and insert each by bubbling
+                float v[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) v[r] = a[r];
+                auto vmax = [&]() {
+                    float m = v[0];
+#pragma unroll
+                    for (int r = 1; r < 16; ++r) m = fmaxf(m, v[r]);
+                    return m;
+                };
+                float m = vmax();
+                while (__ballot(m > bl[b][TL - 1]) != 0ull) {
+                    if (m > bl[b][TL - 1]) {
+                        int rs = 15;
+#pragma unroll
+                        for (int r = 15; r >= 0; --r) rs = (v[r] == m) ? r : rs;
+                        float sv = m;
+                        int sk = kb + 8 * (rs >> 2) + (rs & 3);
+#pragma unroll
+                        for (int j = 0; j < TL; ++j) {
+                            const bool c = sv > bl[b][j];
+                            const float tv = bl[b][j];
+                            const int tk = il[b][j];
+                            bl[b][j] = c ? sv : tv;
+                            il[b][j] = c ? sk : tk;
+                            sv = c ? tv : sv;
+                            sk = c ? tk : sk;
+                        }
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) v[r] = (r == rs) ? -INFINITY : v[r];
+                        m = vmax();
+                    }
+                }
+                return;
+            }
             // A value changes this lane's state only if it beats the third
             // best (top-3) or reaches the threshold (collect).  Late in the
             // sweep most 16-value groups change no lane of the wave; they are
@@ -584,16 +647,19 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             }
         };
         const int cnch = RES ? 1 : A.nch;
-        const int nst = A.ntiles * cnch;
+        // the tiles this workgroup sweeps: all, or its slice in top-L mode
+        const int tb = TL > 0 ? (int)blockIdx.y * A.knn_tps : 0;
+        const int te = TL > 0 ? min(A.ntiles, tb + A.knn_tps) : A.ntiles;
+        const int nst = (te - tb) * cnch;
         if (RES) {
             load_x(0, true);
             if (!COLLECT) point_bounds();
         }
-        load_stage(0, 0);
+        load_stage(tb, 0);
         store_stage(0, 0);
         __syncthreads();
 
-        int t = 0, ch = 0;
+        int t = tb, ch = 0;
         for (int st = 0; st < nst; ++st) {
             const int buf = st & 1;
             int nt = t, nc = ch + 1;
@@ -604,7 +670,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             const bool more = st + 1 < nst;
             // the chunk's own points first, so that waiting for them does not
             // also wait for the next stage's prefetch
-            if (!RES) load_x(ch, t == 0);
+            if (!RES) load_x(ch, t == tb);
             if (more) load_stage(nt, nc);
 
             if constexpr (!PHASED) {
@@ -755,6 +821,52 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         }
 
         if (!RES) point_bounds();
+        if constexpr (TL > 0) {
+#pragma unroll
+            for (int b = 0; b < PB; ++b) {
+                // bitonic merge with the other half-lane's list (reversed):
+                // the larger of each pair forms the top L, then TL/2, ...
+                // sorting steps; "larger" = higher score, lower index on ties
+                float mv[TL];
+                int mi[TL];
+#pragma unroll
+                for (int j = 0; j < TL; ++j) {
+                    const float ov = __shfl_xor(bl[b][TL - 1 - j], 32);
+                    const int oi = __shfl_xor(il[b][TL - 1 - j], 32);
+                    const bool own = (bl[b][j] > ov) || (bl[b][j] == ov && il[b][j] < oi);
+                    mv[j] = own ? bl[b][j] : ov;
+                    mi[j] = own ? il[b][j] : oi;
+                }
+#pragma unroll
+                for (int w = TL / 2; w > 0; w >>= 1) {
+#pragma unroll
+                    for (int j = 0; j < TL; ++j) {
+                        if ((j & w) == 0) {
+                            const int q = j + w;
+                            const bool keep = (mv[j] > mv[q]) || (mv[j] == mv[q] && mi[j] < mi[q]);
+                            const float hv = keep ? mv[j] : mv[q], lv = keep ? mv[q] : mv[j];
+                            const int hi_ = keep ? mi[j] : mi[q], li = keep ? mi[q] : mi[j];
+                            mv[j] = hv;
+                            mi[j] = hi_;
+                            mv[q] = lv;
+                            mi[q] = li;
+                        }
+                    }
+                }
+                const int64_t p = sbase + b * 32 + jl;
+                if (h == 0 && p < A.N) {
+                    const size_t o = ((size_t)p * A.knn_slices + blockIdx.y) * TL;
+#pragma unroll
+                    for (int j = 0; j < TL; j += 4) {
+                        *reinterpret_cast<int4 *>(A.knn_cand + o + j) = make_int4(mi[j], mi[j + 1], mi[j + 2], mi[j + 3]);
+                        *reinterpret_cast<float4 *>(A.knn_score + o + j) =
+                            make_float4(mv[j], mv[j + 1], mv[j + 2], mv[j + 3]);
+                    }
+                    if (blockIdx.y == 0) A.knn_win[p] = xl2[b];
+                }
+            }
+            continue;
+        }
         // merge the two half-waves (same point, the other 16 centroids of each
         // 32-block): larger score first, lower index first on equal scores
 #pragma unroll
@@ -1098,7 +1210,7 @@ hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, i
     return hipGetLastError();
 }
 
-template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool COLLECT, bool SPLIT>
+template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool COLLECT, bool SPLIT, int TL = 0>
 static hipError_t launch_fa(const FlashArgs &A0, hipStream_t s) {
     // the tile count and chunk count follow this instantiation's geometry:
     // the -||c||^2/2 array is padded to kCentroidPad, a multiple of every
@@ -1111,12 +1223,18 @@ static hipError_t launch_fa(const FlashArgs &A0, hipStream_t s) {
     constexpr int BM = WAVES * PB * 32;
     int64_t nb = COLLECT ? cdiv(A.cap_slots, BM) : cdiv(A.N, BM);
     if (COLLECT && nb > 512) nb = 512;  // persistent: the workgroups stride over the listed slots
+    unsigned gy = 1;
+    if (TL > 0) {
+        if (A.knn_rows % (CB * 32) != 0) return hipErrorInvalidValue;
+        A.knn_tps = A.knn_rows / (CB * 32);
+        gy = (unsigned)A.knn_slices;
+    }
     if (A.d % 4 == 0)
-        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, true, COLLECT, SPLIT>), dim3((unsigned)nb),
-                           dim3(WAVES * 64), 0, s, A);
+        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, true, COLLECT, SPLIT, TL>),
+                           dim3((unsigned)nb, gy), dim3(WAVES * 64), 0, s, A);
     else
-        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, false, COLLECT, SPLIT>), dim3((unsigned)nb),
-                           dim3(WAVES * 64), 0, s, A);
+        hipLaunchKernelGGL((k_flash_assign<DP, PB, CB, WAVES, MINB, RES, false, COLLECT, SPLIT, TL>),
+                           dim3((unsigned)nb, gy), dim3(WAVES * 64), 0, s, A);
     return hipGetLastError();
 }
 
@@ -1241,6 +1359,284 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
     else
         hipLaunchKernelGGL((k_recheck<float, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C32, K, xnorm64,
                            nt.ovf_list, nt.counters + 2, P, a_out, d1_out, ip ? 1 : 0);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// k nearest neighbours: the FlashAssign sweep with a per-lane top-L list
+// (queries are the points, database rows the centroids), then fp64.
+
+// The candidate lists take 2L registers per lane (two waves per SIMD, 256
+// VGPRs each).  With L = 32 and d > 64 the resident point block no longer
+// fits beside them: the points are streamed in 64-dim chunks instead, scored
+// in fp32 (the split variant of that shape spills inside its tile loop).
+template <bool SPLIT, int TL>
+static hipError_t launch_knn_shape(const FlashArgs &A, hipStream_t s) {
+    const AssignShape sh = assign_shape(A.d);
+    if constexpr (TL > 16) {
+        if (A.d > 64) return launch_fa<64, 1, 2, 8, 2, false, false, false, TL>(A, s);
+    } else {
+        if (sh.nch > 1) return launch_fa<64, 1, 2, 8, 2, false, false, SPLIT, TL>(A, s);
+        if (sh.DP == 128) return launch_fa<128, 1, 1, 8, 2, true, false, SPLIT, TL>(A, s);
+    }
+    switch (sh.DP) {
+    case 16: return launch_fa<16, 1, 1, 8, 2, true, false, SPLIT, TL>(A, s);
+    case 32: return launch_fa<32, 1, 1, 8, 2, true, false, SPLIT, TL>(A, s);
+    default: return launch_fa<64, 1, 1, 8, 2, true, false, SPLIT, TL>(A, s);
+    }
+}
+
+int knn_list_len(int k) { return k <= kKnnShort ? 16 : 32; }
+
+// Database slices: enough (point blocks x slices) workgroups to fill the chip
+// a few times over when there are few queries, each slice at least
+// kKnnMinSliceRows rows and a multiple of kCentroidPad rows (so of every tile
+// height), at most kKnnMaxSlices of them.
+KnnSlices knn_slices(int64_t M, int64_t Ndb) {
+    constexpr int64_t kTargetGroups = 2048, kMinRows = 4096;
+    const int64_t qb = cdiv(M > 0 ? M : 1, 256);
+    int64_t S = cdiv(kTargetGroups, qb);
+    if (S > kKnnMaxSlices) S = kKnnMaxSlices;
+    const int64_t smax = cdiv(Ndb, kMinRows);
+    if (S > smax) S = smax;
+    if (S < 1) S = 1;
+    const int64_t R = cdiv(cdiv(Ndb, S), kCentroidPad) * kCentroidPad;
+    return KnnSlices{(int)cdiv(Ndb, R), (int)R};
+}
+
+hipError_t launch_knn_sweep(const float *Q, int64_t M, int d, const float *DB, const float *ncn, int Ndb,
+                            const float *scal, const double *qnorm64, const SplitC &sc, bool ip, int k,
+                            int32_t *cand, float *score, float *win, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    NearTies nt{};
+    FlashArgs A = flash_args(Q, M, d, DB, ncn, Ndb, scal, qnorm64, nullptr, nullptr, nt, sc, ip);
+    const KnnSlices ks = knn_slices(M, Ndb);
+    A.knn_slices = ks.slices;
+    A.knn_rows = ks.rows;
+    A.knn_cand = cand;
+    A.knn_score = score;
+    A.knn_win = win;
+    const bool split = sc.cs != nullptr;
+    if (knn_list_len(k) == 16)
+        return split ? launch_knn_shape<true, 16>(A, s) : launch_knn_shape<false, 16>(A, s);
+    return split ? launch_knn_shape<true, 32>(A, s) : launch_knn_shape<false, 32>(A, s);
+}
+
+// One thread per query: merge the slices' candidate lists into the L best
+// MFMA scores (lower index first on equal scores).  Every row outside them
+// scores at most the L-th: when the k-th beats it by more than the window
+// the exact top k lies among the L, which are then ranked by their fp64
+// distances (the definition: direct differences, or the negated dot product,
+// in increasing j) by (distance, index).  Otherwise the query is listed for
+// k_knn_full.
+template <typename CT, int TL>
+__global__ __launch_bounds__(256) void k_knn_finish(const float *__restrict__ Q, int64_t M, int d,
+                                                    const CT *__restrict__ DB, const double *__restrict__ qnorm64,
+                                                    int ip, const int32_t *__restrict__ cand,
+                                                    const float *__restrict__ score, const float *__restrict__ win,
+                                                    int S, int k, int Ndb, int32_t *__restrict__ list,
+                                                    int32_t *__restrict__ counter, int32_t *__restrict__ idx,
+                                                    float *__restrict__ dist) {
+#pragma clang fp contract(off)
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= M) return;
+    float V[TL];
+    int I[TL];
+#pragma unroll
+    for (int j = 0; j < TL; ++j) {
+        V[j] = -INFINITY;
+        I[j] = 0x7fffffff;
+    }
+    const size_t base = (size_t)q * S * TL;
+    for (int e = 0; e < S * TL; ++e) {
+        float v = score[base + e];
+        int c = cand[base + e];
+        if (!(v > V[TL - 1] || (v == V[TL - 1] && c < I[TL - 1]))) continue;
+#pragma unroll
+        for (int j = 0; j < TL; ++j) {
+            const bool sw = v > V[j] || (v == V[j] && c < I[j]);
+            const float tv = V[j];
+            const int tc = I[j];
+            V[j] = sw ? v : tv;
+            I[j] = sw ? c : tc;
+            v = sw ? tv : v;
+            c = sw ? tc : c;
+        }
+    }
+    float sk = V[0];
+#pragma unroll
+    for (int j = 0; j < TL; ++j) sk = (j == k - 1) ? V[j] : sk;
+    if (!((sk - V[TL - 1]) > win[q])) {
+        // wave-aggregated append to the list of queries ranked against all rows
+        const uint64_t mk = __ballot(true);
+        const int leader = __ffsll((unsigned long long)mk) - 1;
+        int pos = 0;
+        if ((int)__lane_id() == leader) pos = atomicAdd(counter, __popcll(mk));
+        pos = __shfl(pos, leader);
+        list[pos + __popcll(mk & lanemask_lt())] = (int32_t)q;
+        return;
+    }
+    double D[TL];
+    const double nx = qnorm64 != nullptr ? qnorm64[q] : 1.0;
+#pragma unroll
+    for (int j = 0; j < TL; ++j) {
+        // fewer than L real rows: the sweep's padding rows (index >= Ndb)
+        if (I[j] < 0 || I[j] >= Ndb) {
+            I[j] = 0x7fffffff;
+            D[j] = INFINITY;
+            continue;
+        }
+        const CT *const row[1] = {DB + (size_t)I[j] * d};
+        double Dj[1];
+        sqdist64<CT, 1>(Q + (size_t)q * d, row, d, nx, qnorm64 != nullptr, ip != 0, Dj);
+        D[j] = Dj[0];
+    }
+    // k passes of a minimum by (distance, index), static indexing only
+    for (int r = 0; r < k; ++r) {
+        double b = INFINITY;
+        int bi = 0x7fffffff, bj = 0;
+#pragma unroll
+        for (int j = 0; j < TL; ++j) {
+            const bool t = D[j] < b || (D[j] == b && I[j] < bi);
+            b = t ? D[j] : b;
+            bi = t ? I[j] : bi;
+            bj = t ? j : bj;
+        }
+        idx[q * k + r] = bi;
+        dist[q * k + r] = (float)b;
+#pragma unroll
+        for (int j = 0; j < TL; ++j) D[j] = (j == bj) ? (double)INFINITY : D[j];
+#pragma unroll
+        for (int j = 0; j < TL; ++j) I[j] = (j == bj) ? 0x7fffffff : I[j];
+    }
+}
+
+// The exact k best database rows of each listed query against all Ndb rows
+// in fp64 (the definition itself).  One workgroup per query: each thread keeps
+// the k best of its rows (t, t + 256, ...), then k rounds of a workgroup-wide
+// minimum of (distance, index) take them out in order.
+template <typename CT>
+__global__ __launch_bounds__(256) void k_knn_full(const float *__restrict__ Q, int d, const CT *__restrict__ DB,
+                                                  int Ndb, const double *__restrict__ qnorm64, int ip,
+                                                  const int32_t *__restrict__ list,
+                                                  const int32_t *__restrict__ counters, int k,
+                                                  int32_t *__restrict__ idx, float *__restrict__ dist) {
+#pragma clang fp contract(off)
+    __shared__ double wd[4];
+    __shared__ int wi[4], wt[4];
+    __shared__ int win_t;
+    const int tid = threadIdx.x, w = tid >> 6;
+    const int cnt = counters[0];
+    for (int li = blockIdx.x; li < cnt; li += gridDim.x) {
+        const int64_t q = list[li];
+        const double nx = qnorm64 != nullptr ? qnorm64[q] : 1.0;
+        double D[kMaxKnn];
+        int I[kMaxKnn];
+#pragma unroll
+        for (int j = 0; j < kMaxKnn; ++j) {
+            D[j] = INFINITY;
+            I[j] = 0x7fffffff;
+        }
+        for (int c = tid; c < Ndb; c += 256) {
+            const CT *const row[1] = {DB + (size_t)c * d};
+            double Dc[1];
+            sqdist64<CT, 1>(Q + (size_t)q * d, row, d, nx, qnorm64 != nullptr, ip != 0, Dc);
+            // rows come in increasing index: a strict '<' keeps the lower
+            // index first among equal distances
+            double dv = Dc[0];
+            int iv = c;
+#pragma unroll
+            for (int j = 0; j < kMaxKnn; ++j) {
+                const bool sw = j < k && dv < D[j];
+                const double td = D[j];
+                const int ti = I[j];
+                D[j] = sw ? dv : td;
+                I[j] = sw ? iv : ti;
+                dv = sw ? td : dv;
+                iv = sw ? ti : iv;
+            }
+        }
+        for (int r = 0; r < k; ++r) {
+            double b = D[0];
+            int bi = I[0];
+            int bt = tid;
+            for (int off = 32; off > 0; off >>= 1) {
+                const double ob = __shfl_xor(b, off);
+                const int oi = __shfl_xor(bi, off);
+                const int ot = __shfl_xor(bt, off);
+                if (ob < b || (ob == b && oi < bi)) {
+                    b = ob;
+                    bi = oi;
+                    bt = ot;
+                }
+            }
+            if ((tid & 63) == 0) {
+                wd[w] = b;
+                wi[w] = bi;
+                wt[w] = bt;
+            }
+            __syncthreads();
+            if (tid == 0) {
+                double bb = wd[0];
+                int bbi = wi[0], btt = wt[0];
+                for (int ww = 1; ww < 4; ++ww)
+                    if (wd[ww] < bb || (wd[ww] == bb && wi[ww] < bbi)) {
+                        bb = wd[ww];
+                        bbi = wi[ww];
+                        btt = wt[ww];
+                    }
+                idx[q * k + r] = bbi;
+                dist[q * k + r] = (float)bb;
+                win_t = btt;
+            }
+            __syncthreads();
+            if (tid == win_t) {
+                // take this thread's best out
+#pragma unroll
+                for (int j = 0; j < kMaxKnn - 1; ++j) {
+                    D[j] = D[j + 1];
+                    I[j] = I[j + 1];
+                }
+                D[kMaxKnn - 1] = INFINITY;
+                I[kMaxKnn - 1] = 0x7fffffff;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+hipError_t launch_knn_finish(const float *Q, int64_t M, int d, const float *DB32, const double *DB64,
+                             const double *qnorm64, bool ip, const int32_t *cand, const float *score,
+                             const float *win, int k, int Ndb, int32_t *list, int32_t *counters, int32_t *idx,
+                             float *dist, hipStream_t s) {
+    if (M <= 0) return hipSuccess;
+    const unsigned nb = (unsigned)cdiv(M, 256);
+    const int ipi = ip ? 1 : 0;
+    const int S = knn_slices(M, Ndb).slices;
+#define FK_KNN_FINISH(CT, TLV, DBP)                                                                              \
+    hipLaunchKernelGGL((k_knn_finish<CT, TLV>), dim3(nb), dim3(256), 0, s, Q, M, d, DBP, qnorm64, ipi, cand, score, \
+                       win, S, k, Ndb, list, counters, idx, dist)
+    if (knn_list_len(k) == 16) {
+        if (DB64 != nullptr)
+            FK_KNN_FINISH(double, 16, DB64);
+        else
+            FK_KNN_FINISH(float, 16, DB32);
+    } else {
+        if (DB64 != nullptr)
+            FK_KNN_FINISH(double, 32, DB64);
+        else
+            FK_KNN_FINISH(float, 32, DB32);
+    }
+#undef FK_KNN_FINISH
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nf = M < 4096 ? M : 4096;
+    if (DB64 != nullptr)
+        hipLaunchKernelGGL(k_knn_full<double>, dim3((unsigned)nf), dim3(256), 0, s, Q, d, DB64, Ndb, qnorm64, ipi,
+                           list, counters, k, idx, dist);
+    else
+        hipLaunchKernelGGL(k_knn_full<float>, dim3((unsigned)nf), dim3(256), 0, s, Q, d, DB32, Ndb, qnorm64, ipi,
+                           list, counters, k, idx, dist);
     return hipGetLastError();
 }
 

@@ -125,4 +125,27 @@ hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, 
 hipError_t launch_finalize(const double *sums, const int32_t *cnt, const int32_t *offsets, const float *C_prev, int K,
                            int d, float *C_out, int32_t *counts_out, hipStream_t s);
 
+// k nearest neighbours (k <= kMaxKnn): the sweep cuts the database into
+// slices (a second grid dimension) and writes, per query and slice, the L
+// best MFMA scores and their rows (L = knn_list_len(k), a power of two above
+// k) and the query's score error window; the finish step merges the slices,
+// ranks the L best in fp64 when they must hold the exact top k, and lists the
+// other queries (counters[0] = list length, zeroed by launch_prep_finish),
+// which are then ranked against every row.
+constexpr int kMaxKnn = 24;
+constexpr int kKnnShort = 12;   // k <= 12: 16 candidates per query and slice, else 32
+constexpr int kKnnMaxSlices = 64;
+int knn_list_len(int k);
+struct KnnSlices {
+    int slices, rows;  // rows per slice: a multiple of kCentroidPad
+};
+KnnSlices knn_slices(int64_t M, int64_t Ndb);
+hipError_t launch_knn_sweep(const float *Q, int64_t M, int d, const float *DB, const float *ncn, int Ndb,
+                            const float *scal, const double *qnorm64, const SplitC &sc, bool ip, int k,
+                            int32_t *cand, float *score, float *win, hipStream_t s);
+hipError_t launch_knn_finish(const float *Q, int64_t M, int d, const float *DB32, const double *DB64,
+                             const double *qnorm64, bool ip, const int32_t *cand, const float *score,
+                             const float *win, int k, int Ndb, int32_t *list, int32_t *counters, int32_t *idx,
+                             float *dist, hipStream_t s);
+
 }  // namespace fk

@@ -65,6 +65,8 @@ extern "C" {
 
 #define FK_MAX_K 65536
 #define FK_MAX_D 4096
+#define FK_MAX_KNN_K 24          /* largest k of fk_knn          */
+#define FK_MAX_KNN_DB 1073741824 /* most database rows of fk_knn */
 
 typedef enum {
     FK_OK = 0,
@@ -215,6 +217,33 @@ size_t fk_ivf_workspace_size(int64_t N, int32_t d, int32_t nlist, int32_t metric
 fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int32_t metric, int32_t score,
                        int32_t n_iter, const int32_t *init_idx_host, float *centroids, int32_t *list_offsets,
                        int32_t *list_ids, float *list_data, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Exact k nearest neighbours by brute force (flash-knn, the exact GPU k-NN
+ * backend of the LEANN FlashLib guide, paragraph "when to use FlashLib"):
+ * for each query q of Q[M,d], idx[q, 0..k) are the k database rows of DB[Ndb,d]
+ * with the smallest fp64 distances, in increasing (distance, row index)
+ * order, and dist[q, j] is that distance rounded to fp32:
+ *   L2      sum_j (q_j - x_j)^2 (direct differences, increasing j),
+ *   COSINE  the same on both rows L2-normalised (zero norm taken as 1),
+ *   INNER_PRODUCT  -sum_j q_j x_j (largest inner product first).
+ * The FlashAssign sweep runs with the queries as points and the database
+ * rows as centroids, and keeps for every query its L best MFMA scores
+ * (L = 16 for k <= 12, else 32) instead of the top 3.  The exact top k lies
+ * among those L whenever the k-th score beats the L-th by more than twice the
+ * score error bound (as for fk_assign); the L candidates are then ranked in
+ * fp64.  The other queries are ranked against every database row in fp64.
+ * Limits: 0 <= M <= 2^31-1, 1 <= Ndb <= FK_MAX_KNN_DB,
+ * 1 <= k <= min(FK_MAX_KNN_K, Ndb); FK_SCORE_SPLIT_BF16 also needs the
+ * database's bf16 copy (about 4 Ndb d bytes: Ndb rounded up to 128, d up to
+ * 16, 32, 64, 128 or a multiple of 64) under 4 GiB, else FK_ERR_UNSUPPORTED;
+ * with k > 12 and d > 64 the sweep scores in fp32 whichever mode is asked.  Q, DB, idx[M,k]
+ * (int32) and dist[M,k] (fp32) are device pointers; workspace:
+ * fk_knn_workspace_size() bytes.
+ */
+size_t fk_knn_workspace_size(int64_t M, int32_t d, int64_t Ndb, int32_t k, int32_t metric);
+fk_status fk_knn(const float *Q, int64_t M, int32_t d, const float *DB, int64_t Ndb, int32_t k, int32_t metric,
+                 int32_t score, int32_t *idx, float *dist, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Static name of a status code. */
 const char *fk_status_str(int32_t status);

@@ -23,7 +23,8 @@ def test_every_declared_symbol_is_exported(lib):
     names = fk.declared_symbols()
     expected = {"fk_workspace_size", "fk_assign", "fk_sort_inverse", "fk_update", "fk_lloyd_iter",
                 "fk_lloyd_iter_stream", "fk_status_str", "fk_last_error", "fk_profile_enable", "fk_profile_read",
-                "fk_fit_workspace_size", "fk_fit", "fk_ivf_workspace_size", "fk_ivf_build"}
+                "fk_fit_workspace_size", "fk_fit", "fk_ivf_workspace_size", "fk_ivf_build",
+                "fk_knn_workspace_size", "fk_knn"}
     assert expected <= set(names)
     raw = ctypes.CDLL(fk.LIB_PATH)
     for n in names:
@@ -158,3 +159,30 @@ def test_fit_and_ivf_validation(lib):
     assert st == UNSUPPORTED and b"inner product" in lib.fk_last_error()
     assert lib.fk_ivf_workspace_size(10, 8, 11, 0) == 0
     assert fk.fk_ivf_workspace_size(1000, 16, 10, "cosine") > fk.fk_ivf_workspace_size(1000, 16, 10)
+
+
+def test_knn_validation(lib):
+    ws = _fake(0x1000000)
+    Q, DB, idx, dist = _fake(0x10000), _fake(0x20000), _fake(0x30000), _fake(0x40000)
+
+    def knn(M=10, d=8, Ndb=100, k=5, metric=0, score=0, q=Q, db=DB, wsb=1 << 30):
+        return lib.fk_knn(q, M, d, db, Ndb, k, metric, score, idx, dist, ws, wsb, None)
+    assert knn(k=0) == INVALID
+    assert knn(k=25) == INVALID and b"k=25" in lib.fk_last_error()
+    assert knn(Ndb=4, k=5) == INVALID
+    assert knn(Ndb=0) == INVALID
+    assert knn(d=0) == INVALID
+    assert knn(M=-1) == INVALID
+    assert knn(metric=3) == INVALID
+    assert knn(score=2) == INVALID
+    assert knn(q=None) == INVALID
+    assert knn(db=_fake(0x20004)) == INVALID and b"aligned" in lib.fk_last_error()
+    assert knn(wsb=16) == WORKSPACE
+    # the split copy of a 2^22 x 512 database is 8 GiB: beyond a buffer resource
+    assert knn(d=512, Ndb=1 << 22, score=1) == UNSUPPORTED and b"4 GiB" in lib.fk_last_error()
+    assert lib.fk_knn_workspace_size(10, 8, 4, 5, 0) == 0
+    assert lib.fk_knn_workspace_size(10, 8, 100, 25, 0) == 0
+    a = fk.fk_knn_workspace_size(10000, 128, 1 << 20, 10)
+    assert a > (1 << 20) * 128 * 4                # the database's bf16 copy
+    assert fk.fk_knn_workspace_size(10000, 128, 1 << 20, 10, "cosine") > a + (1 << 20) * 128 * 12
+    assert fk.fk_knn_workspace_size(10000, 128, 1 << 20, 20) > a  # 32 candidates per query

@@ -125,3 +125,32 @@ def test_ivf_build_full_size(gpu_lib, score):
     np.testing.assert_array_equal(a_ref, cell[pos])
     data = host(out["data"][torch.from_numpy(pos).to(Xd.device)])
     np.testing.assert_array_equal(data.view(np.uint32), X[ids[pos]].view(np.uint32))
+
+
+@pytest.mark.parametrize("score", ["fp32", "split_bf16"])
+@pytest.mark.parametrize("name,nsample", [("knn_1m_d128_q10k", 96), ("knn_1m_d768_q10k", 24)])
+def test_knn_full_size(gpu_lib, name, nsample, score):
+    """Exact k-NN at the full shapes, in the configuration bench.py --knn
+    times (all queries in one call): a seeded sample of queries checked
+    exactly against the oracle's brute force over the whole database; for
+    every query the distances must be non-decreasing and equal the fp64
+    distance of the reported row rounded to fp32 (checked on the GPU)."""
+    fk = gpu_lib
+    w = synth.WORKLOADS[name]
+    DB = synth.rows(w)
+    Q = synth.queries(w)
+    DBd, Qd = dev(DB), dev(Q)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    idx, dist = fk.fk_knn(Qd, DBd, w.k, metric=w.metric, score=score)
+    torch.cuda.synchronize()
+    log(f"knn {name} ({score}): {1e3 * (time.perf_counter() - t0):.1f} ms")
+    assert bool((dist[:, 1:] >= dist[:, :-1]).all())
+    rows = DBd[idx.long()].double()                          # [M, k, d]
+    D = ((Qd.double()[:, None, :] - rows) ** 2).sum(-1)
+    # a different summation order: equal to within a few fp64 ulps
+    assert bool(((D.float() - dist).abs() <= 1e-5 * dist.abs() + 1e-30).all())
+    qs = _sample(Q.shape[0], nsample, 17)
+    i_ref, d_ref = oracle.knn(Q[qs], DB, w.k, w.metric)
+    np.testing.assert_array_equal(host(idx)[qs], i_ref)
+    np.testing.assert_array_equal(host(dist)[qs], d_ref.astype(np.float32))
