@@ -106,3 +106,28 @@ def test_knn_repeatable_and_workspace_reuse(gpu_lib):
     np.testing.assert_array_equal(a[0], c[0])
     np.testing.assert_array_equal(a[1].view(np.uint32), c[1].view(np.uint32))
     np.testing.assert_array_equal(a[0][:500], b[0])
+
+
+@pytest.mark.parametrize("score", SCORES)
+@pytest.mark.parametrize("d,k", [(32, 10), (128, 10), (128, 20), (200, 5)])
+def test_knn_database_slices(gpu_lib, score, d, k):
+    """A database of 20,001 rows is cut into 5 slices (4,096 rows each, the
+    last ragged): the slices' candidate lists are merged per query."""
+    rng = np.random.default_rng(2000 + d + k)
+    Q = rng.standard_normal((700, d)).astype(np.float32)
+    DB = rng.standard_normal((20001, d)).astype(np.float32)
+    log(f"knn slices d={d} k={k} score={score}")
+    _check(gpu_lib, Q, DB, k, "l2", score)
+
+
+@pytest.mark.parametrize("score", SCORES)
+def test_knn_ties_across_slices(gpu_lib, score):
+    """Copies of the same rows in different slices: equal distances across
+    slices must still come out lower index first."""
+    rng = np.random.default_rng(12)
+    base = rng.standard_normal((4096, 24)).astype(np.float32)
+    DB = np.concatenate([base, base[::-1], base, base[:1000]])        # 13,288 rows, 4 slices
+    Q = np.concatenate([base[::37] + np.float32(0.01), rng.standard_normal((200, 24)).astype(np.float32)])
+    log(f"knn ties across slices score={score}")
+    _check(gpu_lib, Q, DB, 7, "l2", score)
+    _check(gpu_lib, Q, DB, 16, "inner_product", score)
