@@ -83,7 +83,8 @@ template <int BITS>
 __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *__restrict__ keys_in,
                                                                 const int32_t *__restrict__ vals_in, int64_t N,
                                                                 int shift, const int32_t *__restrict__ hist_scan,
-                                                                int ntiles, int32_t *__restrict__ keys_out,
+                                                                const int32_t *__restrict__ dtot, int ntiles,
+                                                                int32_t *__restrict__ keys_out,
                                                                 int32_t *__restrict__ vals_out) {
     constexpr int NB = 1 << BITS;
     __shared__ int wcnt[kSortWaves][NB];
@@ -109,28 +110,34 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *_
     }
     tile_counts<BITS>(dig, row0, N, wcnt[w]);
     __syncthreads();
-    // exclusive scan of the digit totals over the tile (one digit per thread;
-    // NB <= kSortThreads), then each (wave, digit) run start
+    // exclusive scans (one digit per thread; NB <= kSortThreads) of the
+    // tile's digit counts and of the whole pass's digit totals, then each
+    // (wave, digit) run start
     {
-        __shared__ int tot[kSortThreads];
+        __shared__ int tot[kSortThreads], all[kSortThreads];
         const int v = tid;
-        int t = 0;
+        int t = 0, g = 0;
         if (v < NB) {
 #pragma unroll
             for (int ww = 0; ww < kSortWaves; ++ww) t += wcnt[ww][v];
+            g = dtot[v];
         }
         tot[tid] = t;
+        all[tid] = g;
         __syncthreads();
         for (int o = 1; o < kSortThreads; o <<= 1) {
             const int a = tid >= o ? tot[tid - o] : 0;
+            const int b = tid >= o ? all[tid - o] : 0;
             __syncthreads();
             tot[tid] += a;
+            all[tid] += b;
             __syncthreads();
         }
         if (v < NB) {
             int s = tot[v] - t;  // exclusive
             dstart[v] = s;
-            gbase[v] = hist_scan[(int64_t)blockIdx.x * NB + v];
+            // keys of lower digits, plus keys of this digit in earlier tiles
+            gbase[v] = (all[v] - g) + hist_scan[(int64_t)v * ntiles + blockIdx.x];
 #pragma unroll
             for (int ww = 0; ww < kSortWaves; ++ww) {
                 const int c = wcnt[ww][v];
@@ -169,73 +176,54 @@ __global__ __launch_bounds__(kSortThreads) void k_radix_scatter(const int32_t *_
     }
 }
 
-// ---- global digit offsets: hscan[t][v] = (keys with a digit below v) + (keys
-// with digit v in tiles before t).  Column scan of the [tile][digit] counts
-// in three kernels over chunks of kColChunk tiles; one thread per digit, so
-// every access reads or writes whole contiguous rows.
-constexpr int kColChunk = 32;
+// ---- global digit offsets.  One workgroup per digit v scans that digit's
+// column of tile counts (stride NB in the tile-major histogram; the
+// workgroups of neighbouring digits read the same lines):
+// hscan[v][t] = digit-v keys in the tiles before t (digit-major, so the
+// writes are contiguous), dtot[v] = all digit-v keys.  The scatter adds the
+// keys of lower digits (a scan of dtot).  Each thread takes kColPer
+// consecutive tiles of a chunk; the chunk's thread sums are scanned across
+// the workgroup.
+constexpr int kColPer = 16;
 
-// part[c][v] = digit-v keys in the tiles of chunk c
-__global__ __launch_bounds__(256) void k_col_reduce(const int32_t *__restrict__ hist, int ntiles, int NB,
-                                                    int32_t *__restrict__ part) {
-    const int v = threadIdx.x;
-    if (v >= NB) return;
-    const int t0 = blockIdx.x * kColChunk;
-    int x[kColChunk];
+__global__ __launch_bounds__(256) void k_col_scan(const int32_t *__restrict__ hist, int ntiles, int NB,
+                                                  int32_t *__restrict__ hscan, int32_t *__restrict__ dtot) {
+    __shared__ int wsum[4];
+    const int v = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    int32_t *out = hscan + (int64_t)v * ntiles;
+    int carry = 0;
+    for (int c0 = 0; c0 < ntiles; c0 += 256 * kColPer) {
+        const int t0 = c0 + tid * kColPer;
+        int x[kColPer];
+        int sum = 0;
 #pragma unroll
-    for (int i = 0; i < kColChunk; ++i) x[i] = t0 + i < ntiles ? hist[(int64_t)(t0 + i) * NB + v] : 0;
-    int s = 0;
-#pragma unroll
-    for (int i = 0; i < kColChunk; ++i) s += x[i];
-    part[(int64_t)blockIdx.x * NB + v] = s;
-}
-
-// part[c][v] <- digit-v keys in chunks before c; part[nchunks][v] <- keys with
-// a digit below v
-__global__ __launch_bounds__(256) void k_col_top(int32_t *__restrict__ part, int nchunks, int NB) {
-    constexpr int B = 16;
-    __shared__ int sm[256];
-    const int v = threadIdx.x;
-    int run = 0;
-    if (v < NB) {
-        for (int c0 = 0; c0 < nchunks; c0 += B) {
-            int x[B];
-#pragma unroll
-            for (int i = 0; i < B; ++i) x[i] = c0 + i < nchunks ? part[(int64_t)(c0 + i) * NB + v] : 0;
-#pragma unroll
-            for (int i = 0; i < B; ++i) {
-                if (c0 + i < nchunks) part[(int64_t)(c0 + i) * NB + v] = run;
-                run += x[i];
-            }
+        for (int i = 0; i < kColPer; ++i) {
+            x[i] = t0 + i < ntiles ? hist[(int64_t)(t0 + i) * NB + v] : 0;
+            sum += x[i];
         }
-    }
-    // exclusive scan of the digit totals
-    sm[v] = run;
-    __syncthreads();
-    for (int o = 1; o < 256; o <<= 1) {
-        const int a = v >= o ? sm[v - o] : 0;
-        __syncthreads();
-        sm[v] += a;
-        __syncthreads();
-    }
-    if (v < NB) part[(int64_t)nchunks * NB + v] = sm[v] - run;
-}
-
-__global__ __launch_bounds__(256) void k_col_down(const int32_t *__restrict__ hist, int ntiles, int NB,
-                                                  const int32_t *__restrict__ part, int nchunks,
-                                                  int32_t *__restrict__ hscan) {
-    const int v = threadIdx.x;
-    if (v >= NB) return;
-    const int t0 = blockIdx.x * kColChunk;
-    int x[kColChunk];
+        // inclusive scan of the thread sums within the wave, then across waves
+        int inc = sum;
 #pragma unroll
-    for (int i = 0; i < kColChunk; ++i) x[i] = t0 + i < ntiles ? hist[(int64_t)(t0 + i) * NB + v] : 0;
-    int run = part[(int64_t)blockIdx.x * NB + v] + part[(int64_t)nchunks * NB + v];
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(inc, o);
+            if (lane >= o) inc += y;
+        }
+        if (lane == 63) wsum[w] = inc;
+        __syncthreads();
+        int before = carry;
 #pragma unroll
-    for (int i = 0; i < kColChunk; ++i) {
-        if (t0 + i < ntiles) hscan[(int64_t)(t0 + i) * NB + v] = run;
-        run += x[i];
+        for (int ww = 0; ww < 4; ++ww) before += ww < w ? wsum[ww] : 0;
+        const int total = wsum[0] + wsum[1] + wsum[2] + wsum[3];
+        int run = before + inc - sum;
+#pragma unroll
+        for (int i = 0; i < kColPer; ++i) {
+            if (t0 + i < ntiles) out[t0 + i] = run;
+            run += x[i];
+        }
+        carry += total;
+        __syncthreads();  // wsum is rewritten by the next chunk
     }
+    if (tid == 0) dtot[v] = carry;
 }
 
 // offsets[k] = first position of key k in the sorted keys (= position of the
@@ -283,37 +271,33 @@ static int64_t ntiles_of(int64_t N) { return cdiv(N, kSortTile); }
 size_t sort_scratch_bytes(int64_t N) {
     const int64_t nt = ntiles_of(N > 0 ? N : 1);
     const int64_t hn = 256 * nt;
-    const int64_t np = 256 * (cdiv(nt, kColChunk) + 1);
-    return align_up((size_t)hn * 4, 256) * 2 + align_up((size_t)np * 4, 256);
+    return align_up((size_t)hn * 4, 256) * 2 + align_up(256 * 4, 256);
 }
 
 template <int BITS>
 static hipError_t radix_pass(const int32_t *kin, const int32_t *vin, int64_t N, int shift, int32_t *kout,
-                             int32_t *vout, int32_t *hist, int32_t *hscan, int32_t *part, hipStream_t s) {
+                             int32_t *vout, int32_t *hist, int32_t *hscan, int32_t *dtot, hipStream_t s) {
     constexpr int NB = 1 << BITS;
     const int nt = (int)ntiles_of(N);
-    const int nc = (int)cdiv(nt, kColChunk);
     hipLaunchKernelGGL(k_radix_hist<BITS>, dim3(nt), dim3(kSortThreads), 0, s, kin, N, shift, hist, nt);
-    hipLaunchKernelGGL(k_col_reduce, dim3(nc), dim3(256), 0, s, hist, nt, NB, part);
-    hipLaunchKernelGGL(k_col_top, dim3(1), dim3(256), 0, s, part, nc, NB);
-    hipLaunchKernelGGL(k_col_down, dim3(nc), dim3(256), 0, s, hist, nt, NB, part, nc, hscan);
-    hipLaunchKernelGGL(k_radix_scatter<BITS>, dim3(nt), dim3(kSortThreads), 0, s, kin, vin, N, shift, hscan, nt,
-                       kout, vout);
+    hipLaunchKernelGGL(k_col_scan, dim3(NB), dim3(256), 0, s, hist, nt, NB, hscan, dtot);
+    hipLaunchKernelGGL(k_radix_scatter<BITS>, dim3(nt), dim3(kSortThreads), 0, s, kin, vin, N, shift, hscan, dtot,
+                       nt, kout, vout);
     return hipGetLastError();
 }
 
 static hipError_t radix_pass_bits(int bits, const int32_t *kin, const int32_t *vin, int64_t N, int shift,
-                                  int32_t *kout, int32_t *vout, int32_t *hist, int32_t *hscan, int32_t *part,
+                                  int32_t *kout, int32_t *vout, int32_t *hist, int32_t *hscan, int32_t *dtot,
                                   hipStream_t s) {
     switch (bits) {
-    case 1: return radix_pass<1>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
-    case 2: return radix_pass<2>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
-    case 3: return radix_pass<3>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
-    case 4: return radix_pass<4>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
-    case 5: return radix_pass<5>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
-    case 6: return radix_pass<6>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
-    case 7: return radix_pass<7>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
-    default: return radix_pass<8>(kin, vin, N, shift, kout, vout, hist, hscan, part, s);
+    case 1: return radix_pass<1>(kin, vin, N, shift, kout, vout, hist, hscan, dtot, s);
+    case 2: return radix_pass<2>(kin, vin, N, shift, kout, vout, hist, hscan, dtot, s);
+    case 3: return radix_pass<3>(kin, vin, N, shift, kout, vout, hist, hscan, dtot, s);
+    case 4: return radix_pass<4>(kin, vin, N, shift, kout, vout, hist, hscan, dtot, s);
+    case 5: return radix_pass<5>(kin, vin, N, shift, kout, vout, hist, hscan, dtot, s);
+    case 6: return radix_pass<6>(kin, vin, N, shift, kout, vout, hist, hscan, dtot, s);
+    case 7: return radix_pass<7>(kin, vin, N, shift, kout, vout, hist, hscan, dtot, s);
+    default: return radix_pass<8>(kin, vin, N, shift, kout, vout, hist, hscan, dtot, s);
     }
 }
 
@@ -327,13 +311,13 @@ hipError_t launch_sort_by_key(const int32_t *keys, int64_t N, int K, int32_t *ke
     p += align_up((size_t)hn * 4, 256);
     int32_t *hscan = (int32_t *)p;
     p += align_up((size_t)hn * 4, 256);
-    int32_t *part = (int32_t *)p;
+    int32_t *dtot = (int32_t *)p;
     const int bits = key_bits(K);
     if (bits <= 8)
-        return radix_pass_bits(bits, keys, nullptr, N, 0, keys_sorted, perm, hist, hscan, part, s);
-    hipError_t e = radix_pass_bits(8, keys, nullptr, N, 0, tmp_keys, tmp_vals, hist, hscan, part, s);
+        return radix_pass_bits(bits, keys, nullptr, N, 0, keys_sorted, perm, hist, hscan, dtot, s);
+    hipError_t e = radix_pass_bits(8, keys, nullptr, N, 0, tmp_keys, tmp_vals, hist, hscan, dtot, s);
     if (e != hipSuccess) return e;
-    return radix_pass_bits(bits - 8, tmp_keys, tmp_vals, N, 8, keys_sorted, perm, hist, hscan, part, s);
+    return radix_pass_bits(bits - 8, tmp_keys, tmp_vals, N, 8, keys_sorted, perm, hist, hscan, dtot, s);
 }
 
 hipError_t launch_offsets(const int32_t *keys_sorted, int64_t N, int K, int32_t *offsets, hipStream_t s) {

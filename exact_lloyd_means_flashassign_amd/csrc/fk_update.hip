@@ -280,7 +280,7 @@ template <int NV, int E>
 static hipError_t seg_launch(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
                              hipStream_t s) {
-    constexpr int U = NV * E <= 2 ? 16 : (NV * E <= 8 ? 8 : 4);
+    constexpr int U = NV * E <= 2 ? 8 : (NV * E <= 8 ? 8 : 4);
     const int srows = seg_rows(N);
     const int64_t nseg = cdiv(N, srows);
     const dim3 grid((unsigned)cdiv(nseg, kSegWaves), (unsigned)cdiv(d, 64 * E * NV));
