@@ -194,9 +194,10 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
 // cluster k crosses it and b is the first boundary k crosses, the workgroup
 // adds k's partials: plast of k's first segment, then pfirst of every later
 // segment k touches, into sums[k] (acc) or as sums[k].  Wave w takes the
-// segments sa+1+w, sa+1+w+8, ... in order; the 8 wave sums are added in wave
-// order.
-constexpr int kFixWaves = 8;
+// segments sa+1+w, sa+1+w+16, ... in order (eight loads in flight: the
+// largest cluster of a skewed mixture crosses thousands of boundaries); the
+// 16 wave sums are added in wave order.
+constexpr int kFixWaves = 16;
 __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__restrict__ ks,
                                                              const int32_t *__restrict__ offsets, int64_t N, int d,
                                                              int K, int srows,
@@ -220,15 +221,12 @@ __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__r
         if (c < d) {
             if (w == 0) s = plast[sa * d + c];
             int64_t sg = sa + 1 + w;
-            for (; sg + 3 * kFixWaves <= sb; sg += 4 * kFixWaves) {
-                const double a0 = pfirst[sg * d + c];
-                const double a1 = pfirst[(sg + kFixWaves) * d + c];
-                const double a2 = pfirst[(sg + 2 * kFixWaves) * d + c];
-                const double a3 = pfirst[(sg + 3 * kFixWaves) * d + c];
-                s += a0;
-                s += a1;
-                s += a2;
-                s += a3;
+            for (; sg + 7 * kFixWaves <= sb; sg += 8 * kFixWaves) {
+                double a[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) a[i] = pfirst[(sg + i * kFixWaves) * d + c];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s += a[i];
             }
             for (; sg <= sb; sg += kFixWaves) s += pfirst[sg * d + c];
         }
