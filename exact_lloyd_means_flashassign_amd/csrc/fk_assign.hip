@@ -1389,11 +1389,12 @@ static hipError_t launch_knn_shape(const FlashArgs &A, hipStream_t s) {
 int knn_list_len(int k) { return k <= kKnnShort ? 16 : 32; }
 
 // Database slices: enough (point blocks x slices) workgroups to fill the chip
-// a few times over when there are few queries, each slice at least
-// kKnnMinSliceRows rows and a multiple of kCentroidPad rows (so of every tile
-// height), at most kKnnMaxSlices of them.
+// (one workgroup per CU at a time) many times over when there are few
+// queries -- about 4096, which at 10,000 queries is 64 slices and exactly ten
+// rounds of 256 CUs -- each slice at least 4096 rows and a multiple of
+// kCentroidPad rows (so of every tile height), at most kKnnMaxSlices of them.
 KnnSlices knn_slices(int64_t M, int64_t Ndb) {
-    constexpr int64_t kTargetGroups = 2048, kMinRows = 4096;
+    constexpr int64_t kTargetGroups = 4096, kMinRows = 4096;
     const int64_t qb = cdiv(M > 0 ? M : 1, 256);
     int64_t S = cdiv(kTargetGroups, qb);
     if (S > kKnnMaxSlices) S = kKnnMaxSlices;
