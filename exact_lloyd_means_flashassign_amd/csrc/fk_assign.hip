@@ -1366,8 +1366,8 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
 // k nearest neighbours: the FlashAssign sweep with a per-lane top-L list
 // (queries are the points, database rows the centroids), then fp64.
 
-// The candidate lists take 2L registers per lane (two waves per SIMD, 256
-// VGPRs each).  With L = 32 and d > 64 the resident point block no longer
+// Two 32-row blocks per LDS stage.  The candidate lists take 2L registers
+// per lane (two waves per SIMD, 256 VGPRs each).  With L = 32 and d > 64 the resident point block no longer
 // fits beside them: the points are streamed in 64-dim chunks instead, scored
 // in fp32 (the split variant of that shape spills inside its tile loop).
 template <bool SPLIT, int TL>
@@ -1377,12 +1377,12 @@ static hipError_t launch_knn_shape(const FlashArgs &A, hipStream_t s) {
         if (A.d > 64) return launch_fa<64, 1, 2, 8, 2, false, false, false, TL>(A, s);
     } else {
         if (sh.nch > 1) return launch_fa<64, 1, 2, 8, 2, false, false, SPLIT, TL>(A, s);
-        if (sh.DP == 128) return launch_fa<128, 1, 1, 8, 2, true, false, SPLIT, TL>(A, s);
+        if (sh.DP == 128) return launch_fa<128, 1, 2, 8, 2, true, false, SPLIT, TL>(A, s);
     }
     switch (sh.DP) {
-    case 16: return launch_fa<16, 1, 1, 8, 2, true, false, SPLIT, TL>(A, s);
-    case 32: return launch_fa<32, 1, 1, 8, 2, true, false, SPLIT, TL>(A, s);
-    default: return launch_fa<64, 1, 1, 8, 2, true, false, SPLIT, TL>(A, s);
+    case 16: return launch_fa<16, 1, 2, 8, 2, true, false, SPLIT, TL>(A, s);
+    case 32: return launch_fa<32, 1, 2, 8, 2, true, false, SPLIT, TL>(A, s);
+    default: return launch_fa<64, 1, 2, 8, 2, true, false, SPLIT, TL>(A, s);
     }
 }
 
