@@ -194,10 +194,11 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
 // cluster k crosses it and b is the first boundary k crosses, the workgroup
 // adds k's partials: plast of k's first segment, then pfirst of every later
 // segment k touches, into sums[k] (acc) or as sums[k].  Wave w takes the
-// segments sa+1+w, sa+1+w+16, ... in order (eight loads in flight: the
+// segments sa+1+w, sa+1+w+8, ... in order (eight loads in flight: the
 // largest cluster of a skewed mixture crosses thousands of boundaries); the
-// 16 wave sums are added in wave order.
-constexpr int kFixWaves = 16;
+// 8 wave sums are added in wave order.  Most workgroups find no cluster to
+// finish and exit at once, so they stay small.
+constexpr int kFixWaves = 8;
 __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__restrict__ ks,
                                                              const int32_t *__restrict__ offsets, int64_t N, int d,
                                                              int K, int srows,
