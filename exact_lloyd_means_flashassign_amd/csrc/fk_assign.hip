@@ -161,16 +161,31 @@ __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__
         // [0, w), zero past d and for k >= K.  dn and rn are the squared
         // norms of the remainders c - hi (exact in fp32) and c - hi - lo.
         __bf16 *out = cs + (size_t)k * 2 * w;
-        for (int j = lane; j < w; j += 64) {
-            const float v = (k < K && j < d) ? C[(size_t)k * d + j] : 0.f;
-            const __bf16 hi = (__bf16)v;
+        auto split1 = [&](float v, __bf16 &hi, __bf16 &lo) {
+            hi = (__bf16)v;
             const float dl = v - (float)hi;
-            const __bf16 lo = (__bf16)dl;
+            lo = (__bf16)dl;
             const float r = dl - (float)lo;
-            out[j] = hi;
-            out[w + j] = lo;
             dn = fmaf(dl, dl, dn);
             rn = fmaf(r, r, rn);
+        };
+        if ((d & 1) == 0) {
+            // pairs of dims: one 8-byte load and two 4-byte stores per lane
+            // (w is even, and so is every pair start below d)
+            for (int j = 2 * lane; j < w; j += 128) {
+                float2 v = make_float2(0.f, 0.f);
+                if (k < K && j < d) v = *reinterpret_cast<const float2 *>(C + (size_t)k * d + j);
+                __bf16 h2[2], l2[2];
+                split1(v.x, h2[0], l2[0]);
+                split1(v.y, h2[1], l2[1]);
+                *reinterpret_cast<uint32_t *>(out + j) = __builtin_bit_cast(uint32_t, h2);
+                *reinterpret_cast<uint32_t *>(out + w + j) = __builtin_bit_cast(uint32_t, l2);
+            }
+        } else {
+            for (int j = lane; j < w; j += 64) {
+                const float v = (k < K && j < d) ? C[(size_t)k * d + j] : 0.f;
+                split1(v, out[j], out[w + j]);
+            }
         }
         for (int off = 32; off > 0; off >>= 1) {
             dn += __shfl_xor(dn, off);
@@ -211,16 +226,31 @@ __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__
 
 // scal[0] = max_k ||c_k||^2, scal[1] = max_k ||c_k - hi_k||^2, scal[2] =
 // max_k ||c_k - hi_k - lo_k||^2 (fp32; the last two are zero without split
-// scoring); resets the three near-tie list counters.
-__global__ __launch_bounds__(256) void k_prep_finish(const float *__restrict__ cmax_part, int nparts,
-                                                     float *__restrict__ scal, int32_t *__restrict__ counter) {
-    __shared__ float sm[3][256];
+// scoring); resets the three near-tie list counters.  One workgroup of 1024
+// threads, eight partial rows in flight per thread (a k-NN database of a
+// million rows leaves a quarter of a million partials).
+__global__ __launch_bounds__(1024) void k_prep_finish(const float *__restrict__ cmax_part, int nparts,
+                                                      float *__restrict__ scal, int32_t *__restrict__ counter) {
+    constexpr int NT = 1024, U = 8;
+    __shared__ float sm[3][NT];
     float m[3] = {0.f, 0.f, 0.f};
-    for (int i = threadIdx.x; i < nparts; i += 256)
+    int i = threadIdx.x;
+    for (; i + (U - 1) * NT < nparts; i += U * NT) {
+        float a[U][3];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) a[u][c] = cmax_part[(size_t)(i + u * NT) * 3 + c];
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int c = 0; c < 3; ++c) m[c] = fmaxf(m[c], a[u][c]);
+    }
+    for (; i < nparts; i += NT)
         for (int c = 0; c < 3; ++c) m[c] = fmaxf(m[c], cmax_part[(size_t)i * 3 + c]);
     for (int c = 0; c < 3; ++c) sm[c][threadIdx.x] = m[c];
     __syncthreads();
-    for (int o = 128; o > 0; o >>= 1) {
+    for (int o = NT / 2; o > 0; o >>= 1) {
         if ((int)threadIdx.x < o)
             for (int c = 0; c < 3; ++c) sm[c][threadIdx.x] = fmaxf(sm[c][threadIdx.x], sm[c][threadIdx.x + o]);
         __syncthreads();
@@ -1206,7 +1236,7 @@ hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float 
 }
 
 hipError_t launch_prep_finish(const float *cmax_part, int nparts, float *scal, int32_t *counter, hipStream_t s) {
-    hipLaunchKernelGGL(k_prep_finish, dim3(1), dim3(256), 0, s, cmax_part, nparts, scal, counter);
+    hipLaunchKernelGGL(k_prep_finish, dim3(1), dim3(1024), 0, s, cmax_part, nparts, scal, counter);
     return hipGetLastError();
 }
 
