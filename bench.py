@@ -246,8 +246,8 @@ def main():
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this build has no multi-GPU path; "
-              "the per-GPU shard is what one GPU shows.", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the library has no multi-GPU path; "
+              "a GPU's shard of the points is what one GPU measures.", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
