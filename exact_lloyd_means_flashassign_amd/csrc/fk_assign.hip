@@ -645,12 +645,15 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             }
             // A value changes this lane's state only if it beats the third
             // best (top-3) or reaches the threshold (collect).  Late in the
-            // sweep most 16-value groups change no lane of the wave; they are
-            // skipped with one wave vote.
+            // sweep most 16-value groups change no lane; a lane (and then a
+            // value) that changes nothing sits out with its execution bit
+            // off: the work is skipped when no lane of the wave needs it, and
+            // idle lanes draw less power when some do (the matrix cores run
+            // near the chip's power limit here).
             bool any = false;
 #pragma unroll
             for (int r = 0; r < 16; ++r) any |= COLLECT ? (a[r] >= b1[b]) : (a[r] > b3[b]);
-            if (__ballot(any) == 0ull) return;
+            if (!any) return;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const float v = a[r];
@@ -661,10 +664,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                         if (i1[b] < kMaxCand) A.cand[((sbase + b * 32 + jl) * 2 + h) * kMaxCand + i1[b]] = k;
                         ++i1[b];
                     }
-                } else {
+                } else if (v > b3[b]) {
                     // insert v into the sorted top-3 with medians of three
                     // (v_med3_f32); a strict '>' keeps the lower index first on
-                    // equal scores (k increases per lane)
+                    // equal scores (k increases per lane); a value at or below
+                    // the third best would leave the state as it is
                     const bool c1 = v > b1[b];
                     const bool c2 = v > b2[b];
                     const int t2 = c2 ? k : i2[b];
