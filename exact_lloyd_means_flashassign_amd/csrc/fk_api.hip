@@ -41,7 +41,7 @@ struct Layout {
     size_t ncn, cmax_part, scal, counter, flags, thr, pairs, cand, ccount, ovf;
     size_t c64, c32, cnrm64, xnorm64;  // cosine only (else ~0)
     size_t keys_sorted, perm, tmp_keys, tmp_vals, sort_scratch, offsets;
-    size_t sums, cnt, pfirst, plast, csplit, ncsplit;
+    size_t sums, cnt, pfirst, plast, csplit;
     size_t xchunk[2], achunk[2];      // out-of-core only
     size_t ctmp, cinit, labels, xcopy;  // fit / IVF build only
     size_t knn_cand, knn_score, knn_win, knn_list;  // k nearest neighbours only
@@ -87,7 +87,6 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc, int extras 
     L.sort_scratch = take(sort_scratch_bytes(r));
     L.offsets = take((size_t)(K + 1) * 4);
     L.csplit = take((size_t)Kpad * 2 * split_width(d) * 2);
-    L.ncsplit = take((size_t)Kpad * 16);
     L.sums = take((size_t)K * d * 8);
     L.cnt = take((size_t)K * 4);
     L.pfirst = take((size_t)nseg * d * 8);
@@ -129,7 +128,6 @@ Layout make_knn_layout(int64_t M, int d, int64_t Ndb, int k, int metric) {
     L.cnrm64 = cos ? take((size_t)Ndb * 8) : kNone;
     L.xnorm64 = cos ? take((size_t)m * 8) : kNone;
     L.csplit = take((size_t)Kpad * 2 * split_width(d) * 2);
-    L.ncsplit = take((size_t)Kpad * 16);
     const size_t ncand = (size_t)m * knn_slices(m, Ndb).slices * knn_list_len(k);
     L.knn_cand = take(ncand * 4);
     L.knn_score = take(ncand * 4);
@@ -262,8 +260,8 @@ struct Ctx {
     int d, K, metric;
     int score;
     SplitC split() const {
-        if (score != FK_SCORE_SPLIT_BF16) return SplitC{nullptr, 0, nullptr};
-        return SplitC{at<__bf16>(ws, L.csplit), split_width(d), at<__bf16>(ws, L.ncsplit)};
+        if (score != FK_SCORE_SPLIT_BF16) return SplitC{nullptr, 0};
+        return SplitC{at<__bf16>(ws, L.csplit), split_width(d)};
     }
 };
 

@@ -49,7 +49,6 @@ struct FlashArgs {
     int64_t cap_slots;   // collect mode: slots with candidate storage
     const __bf16 *Cs;    // split scoring: per centroid row, w bf16 high parts then
     int sw;              // w bf16 low parts (C - high, rounded); Kpad rows
-    const __bf16 *ncs;   // split scoring: -||c||^2/2 as three bf16 parts + 5 zeros
     unsigned cs_bytes;   // size of the split copy
     int ip;              // inner product: scores are x.c (no -||c||^2/2 term)
     // top-L mode: the centroid rows are cut into knn_slices slices of
@@ -139,7 +138,7 @@ hipError_t launch_gather_rows(const float *M, const int32_t *idx, int64_t rows, 
 // per centroid row.
 __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__ C, int K, int Kpad, int d,
                                                        float *__restrict__ ncn, float *__restrict__ cmax_part,
-                                                       __bf16 *__restrict__ cs, int w, __bf16 *__restrict__ ncs,
+                                                       __bf16 *__restrict__ cs, int w,
                                                        int ip) {
     __shared__ float wmax[3][4];
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -197,22 +196,6 @@ __global__ __launch_bounds__(256) void k_centroid_prep(const float *__restrict__
             ncn[k] = ip ? 0.f : -0.5f * cn;
         else if (k < Kpad)
             ncn[k] = -INFINITY;
-        if (ncs != nullptr && k < Kpad) {
-            // -||c||^2/2 = p0 + p1 + p2 exactly: each part takes the next 8
-            // significant bits of what is left (24 in all).  Rows past K get
-            // -2^127, finite so that the MFMA against the zero k-slots stays
-            // finite, and below any real score.
-            const float v = k < K ? (ip ? 0.f : -0.5f * cn) : -1.7014118e38f;
-            const __bf16 p0 = (__bf16)v;
-            const float r1 = v - (float)p0;
-            const __bf16 p1 = (__bf16)r1;
-            const __bf16 p2 = (__bf16)(r1 - (float)p1);
-            __bf16 *o = ncs + (size_t)k * 8;
-            o[0] = p0;
-            o[1] = p1;
-            o[2] = p2;
-            for (int e = 3; e < 8; ++e) o[e] = (__bf16)0.0f;
-        }
         wmax[0][wv] = cn;
         wmax[1][wv] = dn;
         wmax[2][wv] = rn;
@@ -318,17 +301,16 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     static_assert(HALF % 4 == 0, "DP must be a multiple of 8");
     static_assert(!SPLIT || DP % 16 == 0, "split scoring needs DP a multiple of 16");
     // Split scoring with resident points runs each tile in phases on one
-    // accumulator: the two cross terms from zero, then -||c||^2/2 (as an
-    // exact sum of three bf16 parts, through one MFMA against ones), then
-    // the hi.hi products.  Chunked points keep the cross terms in a second
-    // accumulator instead (the phases would span chunks).
+    // accumulator: the two cross terms from zero, then -||c||^2/2 (its fp32
+    // value, one add per score), then the hi.hi products.  Chunked points keep
+    // the cross terms in a second accumulator instead (the phases would span
+    // chunks).
     constexpr bool PHASED = SPLIT && RES;
 
     __shared__ __attribute__((aligned(16))) float sC[2][SPLIT ? 4 : ROWS * LDR];
     __shared__ __attribute__((aligned(16))) __bf16 sCh[2][SPLIT ? ROWS * LDB : 8];
     __shared__ __attribute__((aligned(16))) __bf16 sCl[2][SPLIT ? ROWS * LDB : 8];
-    __shared__ __attribute__((aligned(16))) float sN[2][PHASED ? 4 : ROWS];
-    __shared__ __attribute__((aligned(16))) float4 sNs[2][PHASED ? ROWS : 1];
+    __shared__ __attribute__((aligned(16))) float sN[2][ROWS];
 
     const float *__restrict__ X = A.X;
     const float *__restrict__ C = A.C;
@@ -355,7 +337,6 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         float4 pf[PFN];
         float4 pfh[PFS], pfl[PFS];
         float pn = 0.f;
-        float4 pns = make_float4(0.f, 0.f, 0.f, 0.f);
         auto load_stage = [&](int t, int ch) {
             if constexpr (SPLIT) {
                 // the split copy has Kpad zero-padded rows of sw >= DP * nch
@@ -400,11 +381,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     pf[i] = v;
                 }
             }
-            if (PHASED) {
-                if (tid < ROWS) pns = *reinterpret_cast<const float4 *>(A.ncs + (size_t)(t * ROWS + tid) * 8);
-            } else if (ch == 0 && tid < ROWS) {
-                pn = A.ncn[t * ROWS + tid];
-            }
+            if (ch == 0 && tid < ROWS) pn = A.ncn[t * ROWS + tid];
         };
         // registers -> LDS buffer
         auto store_stage = [&](int buf, int ch) {
@@ -425,11 +402,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     if (q < NQ4) *reinterpret_cast<float4 *>(&sC[buf][(q / Q4) * LDR + (q % Q4) * 4]) = pf[i];
                 }
             }
-            if (PHASED) {
-                if (tid < ROWS) sNs[buf][tid] = pns;
-            } else if (ch == 0 && tid < ROWS) {
-                sN[buf][tid] = pn;
-            }
+            if (ch == 0 && tid < ROWS) sN[buf][tid] = pn;
         };
 
         float xr[PB][SPLIT ? 1 : HALF];
@@ -688,6 +661,15 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         if (RES) {
             load_x(0, true);
             if (!COLLECT) point_bounds();
+            if constexpr (PHASED) {
+                // the split points are packed into their MFMA operand
+                // registers here (left to itself the compiler would pack them
+                // after the first stage's loads and spill the halves)
+#pragma unroll
+                for (int b = 0; b < PB; ++b)
+#pragma unroll
+                    for (int st = 0; st < NS; ++st) asm volatile("" : "+v"(xh[b][st]), "+v"(xl[b][st]));
+            }
         }
         load_stage(tb, 0);
         store_stage(0, 0);
@@ -731,10 +713,6 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             if constexpr (PHASED) {
                 const __bf16 *sh = &sCh[buf][jl * LDB + 8 * h];
                 const __bf16 *sl = &sCl[buf][jl * LDB + 8 * h];
-                // B operand of the -||c||^2/2 step: ones in k-slots 0..2
-                v8bf ones;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) ones[e] = (h == 0 && e < 3) ? (__bf16)1.0f : (__bf16)0.0f;
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
                     // phase 1: lo.hi + hi.lo, from zero; each step's LDS
@@ -758,13 +736,17 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                         ah = ahn;
                         al = aln;
                     }
-                    // phase 2: + (p0 + p1 + p2) of -||c||^2/2, its exact fp32 value
-                    {
-                        const float4 nr = sNs[buf][cb * 32 + jl];
-                        const v8bf an = *reinterpret_cast<const v8bf *>(&nr);
+                    // phase 2: + -||c||^2/2 (fp32) of this lane's 16 centroid rows
 #pragma unroll
-                        for (int b = 0; b < PB; ++b)
-                            acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(an, ones, acc[b][0], 0, 0, 0);
+                    for (int q = 0; q < 4; ++q) {
+                        const float4 nv = *reinterpret_cast<const float4 *>(&sN[buf][cb * 32 + 8 * q + 4 * h]);
+#pragma unroll
+                        for (int b = 0; b < PB; ++b) {
+                            acc[b][0][4 * q + 0] += nv.x;
+                            acc[b][0][4 * q + 1] += nv.y;
+                            acc[b][0][4 * q + 2] += nv.z;
+                            acc[b][0][4 * q + 3] += nv.w;
+                        }
                     }
                     // phase 3: hi.hi (the high parts are read from LDS again:
                     // the empty asm keeps the compiler from holding the phase-1
@@ -1235,7 +1217,7 @@ hipError_t launch_centroid_prep(const float *C, int K, int d, float *ncn, float 
     const int nb = (int)cdiv(Kpad, 4);
     *nparts = nb;
     hipLaunchKernelGGL(k_centroid_prep, dim3(nb), dim3(256), 0, s, C, K, Kpad, d, ncn, cmax_part, sc.cs, sc.w,
-                       sc.ncs, ip ? 1 : 0);
+                       ip ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -1321,7 +1303,6 @@ static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, co
     A.cap_slots = near_tie_cap(N);
     A.Cs = sc.cs;
     A.sw = sc.w;
-    A.ncs = sc.ncs;
     A.ip = ip ? 1 : 0;
     A.cs_bytes = (unsigned)(cdiv(K, kCentroidPad) * kCentroidPad * 4 * (int64_t)sc.w);
     return A;

@@ -61,7 +61,6 @@ AssignShape assign_shape(int d);
 struct SplitC {
     __bf16 *cs;
     int w;
-    __bf16 *ncs;  // Kpad rows of 8 bf16: -||c||^2/2 split into three parts, then zeros
 };
 int split_width(int d);
 
