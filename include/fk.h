@@ -115,11 +115,12 @@ size_t fk_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric, int64_
  * FlashAssign: assign[i] = the nearest centroid of point i (lowest index on
  * ties), and, when min_dist is not NULL, min_dist[i] = its squared distance
  * (fp32; the fp64 value rounded for rescored points).  score is an
- * fk_score.  X, C, assign and min_dist are device pointers.  The N x K distance matrix is never stored:
- * each workgroup keeps a block of points in registers, streams centroid
- * tiles through LDS into fp32 MFMA and keeps a running top-3 per point in
- * registers (FlashAssign section of the Flash-KMeans article).  Near ties
- * are settled in fp64 (see Exactness above).
+ * fk_score.  X, C, assign and min_dist are device pointers.  The N x K
+ * distance matrix is never stored: each workgroup keeps a block of points in
+ * registers, streams centroid tiles through LDS into MFMA (fp32, or
+ * split-bf16) and keeps a running top-3 per point in registers (FlashAssign
+ * section of the Flash-KMeans article).  Near ties are settled in fp64 (see
+ * Exactness above).
  */
 fk_status fk_assign(const float *X, int64_t N, int32_t d, const float *C, int32_t K, int32_t metric,
                     int32_t score, int32_t *assign, float *min_dist, void *workspace, size_t workspace_bytes,
