@@ -18,6 +18,7 @@ path is timed after it on the same inputs and reported under "other_scores".
 
 usage: python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--workload NAME]
                        [--score split_bf16|fp32] [--no-compare] [--no-cpu-baseline]
+                       [--ivf-build | --knn [WORKLOAD] | --ooc [--ooc-rows N]]
 """
 import argparse
 import hashlib
@@ -227,6 +228,63 @@ def knn_bench(args, fk, synth, np, torch):
     print(json.dumps(out), flush=True)
 
 
+OOC_H200_S = 41.4  # the Flash-KMeans article's time per iteration at 1e9 x 128, K = 32768 (H200), context only
+
+
+def ooc_bench(args, fk, synth, np, torch):
+    """Seconds per out-of-core Lloyd iteration (fk_lloyd_iter_stream: X in
+    pinned host memory, streamed in 2^26-row chunks, PCIe included) on the
+    article's headline mixture (1e9 x 128, K = 32768) cut to --ooc-rows rows,
+    the most a box's host memory comfortably holds; also given per 1e9 rows
+    (the time is linear in N)."""
+    w0 = synth.WORKLOADS["ooc_1b_d128_k32768"]
+    N = int(args.ooc_rows)
+    w = w0.scaled(N)
+    t0 = time.perf_counter()
+    Xh = torch.empty((N, w.d), dtype=torch.float32, pin_memory=True)
+    X = Xh.numpy()
+    synth.rows(w, out=X)
+    C = X[synth.init_indices(w)].copy()
+    ah = torch.empty(N, dtype=torch.int32, pin_memory=True)
+    Cd = torch.from_numpy(C).to("cuda:0")
+    log(f"generated {w.name} cut to N={N} (pinned) in {time.perf_counter() - t0:.1f} s")
+    ws = torch.empty(fk.fk_workspace_size(N, w.d, w.K, w.metric, chunk_rows=w.chunk_rows) + 256,
+                     dtype=torch.uint8, device="cuda:0")
+
+    def run(score):
+        for i in range(args.warmup):
+            fk.fk_lloyd_iter_stream(Xh, Cd, w.chunk_rows, assign_host=ah, workspace=ws, score=score)
+        torch.cuda.synchronize()
+        fk.fk_profile_enable(True)
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            C1, cnt = fk.fk_lloyd_iter_stream(Xh, Cd, w.chunk_rows, assign_host=ah, workspace=ws, score=score)
+        torch.cuda.synchronize()
+        el = (time.perf_counter() - t0) / args.steps
+        prof = fk.fk_profile_read()
+        fk.fk_profile_enable(False)
+        assert int(cnt.sum().item()) == N
+        log(f"{score}: {el:.3f} s per iteration")
+        return {"s_per_iter": el, "s_per_1e9_rows": el * 1e9 / N, "x_gbps_incl_pcie": N * w.d * 4 / el / 1e9,
+                "phase_ms_per_step": {k: round(v / args.steps, 3) for k, v in prof["ms"].items()}}
+
+    r = run(args.score)
+    out = {"metric": f"s per out-of-core Lloyd iteration (X pinned on the host, {N} x {w.d}, K={w.K}, "
+                     "PCIe included)", "value": r["s_per_iter"], "unit": "s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": 1e3 * r["s_per_iter"], "higher_is_better": False,
+           "scaling": "weak", "vs_baseline": None, "dtype": SCORES[args.score]["dtype"], "data": "synthetic",
+           "config": {"workload": w.name, "N": N, "d": w.d, "K": w.K, "chunk_rows": w.chunk_rows, "seed": w.seed,
+                      "score": args.score},
+           "s_per_1e9_rows": r["s_per_1e9_rows"], "x_gbps_incl_pcie": r["x_gbps_incl_pcie"],
+           "phase_ms_per_step": r["phase_ms_per_step"],
+           "baseline_context": f"{OOC_H200_S} s per iteration at 1e9 x 128, K = 32768 on an NVIDIA H200, as the "
+                               "Flash-KMeans article reports; other hardware"}
+    if not args.no_compare:
+        out["other_scores"] = {o: run(o) for o in SCORES if o != args.score}
+    out["cpu_baseline"] = None if args.no_cpu_baseline else cpu_baseline(w, X, C)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -241,6 +299,10 @@ def main():
                     help="instead: time the IVF-Flat build (1,000,000 x 768, nlist 4096, niter 20, seed 0)")
     ap.add_argument("--knn", nargs="?", const="knn_1m_d128_q10k", default=None,
                     help="time exact k-NN (fk_knn) on a k-NN workload instead of the Lloyd iteration")
+    ap.add_argument("--ooc", action="store_true",
+                    help="time the out-of-core iteration (pinned host X, PCIe included) on --ooc-rows rows of the "
+                         "1e9 x 128, K = 32768 mixture")
+    ap.add_argument("--ooc-rows", type=int, default=1 << 27)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy three times (the reference kernel that scales the "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -269,6 +331,8 @@ def main():
     fk.load()
     if args.knn:
         return knn_bench(args, fk, synth, np, torch)
+    if args.ooc:
+        return ooc_bench(args, fk, synth, np, torch)
     if args.ivf_build:
         return ivf_build_bench(args, fk, synth, np, torch)
     w = synth.WORKLOADS[args.workload]
