@@ -1257,7 +1257,16 @@ static hipError_t launch_fa(const FlashArgs &A0, hipStream_t s) {
 template <bool COLLECT, bool SPLIT>
 static hipError_t launch_fa_shape(const FlashArgs &A, hipStream_t s) {
     const AssignShape sh = assign_shape(A.d);
-    if (sh.nch > 1) return launch_fa<64, 1, 2, 8, 2, false, COLLECT, SPLIT>(A, s);
+    if (sh.nch > 1) {
+        // streamed points are re-read for every centroid tile: 128-row tiles
+        // halve that traffic (the d = 768 shape is bound by it at 64 rows).
+        // Split scoring at that height needs more than 256 registers: one
+        // wave per SIMD, accumulators in AGPRs, rather than spilling.
+        if constexpr (SPLIT)
+            return launch_fa<64, 1, 4, 4, 1, false, COLLECT, SPLIT>(A, s);
+        else
+            return launch_fa<64, 1, 4, 4, 2, false, COLLECT, SPLIT>(A, s);
+    }
     switch (sh.DP) {
     case 16: return launch_fa<16, 1, 1, 8, 4, true, COLLECT, SPLIT>(A, s);
     case 32: return launch_fa<32, 1, 1, 8, 4, true, COLLECT, SPLIT>(A, s);
