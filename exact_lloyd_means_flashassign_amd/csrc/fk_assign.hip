@@ -1390,17 +1390,17 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
 // k nearest neighbours: the FlashAssign sweep with a per-lane top-L list
 // (queries are the points, database rows the centroids), then fp64.
 
-// Two 32-row blocks per LDS stage.  The candidate lists take 2L registers
-// per lane (two waves per SIMD, 256 VGPRs each).  With L = 32 and d > 64 the resident point block no longer
-// fits beside them: the points are streamed in 64-dim chunks instead, scored
-// in fp32 (the split variant of that shape spills inside its tile loop).
+// Resident point blocks: two 32-row blocks per LDS stage, two waves per SIMD
+// (256 VGPRs each), of which the candidate lists take 2L per lane.  With
+// L = 32 and d > 64 the resident point block no longer fits beside them, and
+// for d > 128 it never does: the points are streamed in 64-dim chunks, four
+// 32-row blocks per stage (which halves the re-reads of the query chunks),
+// one wave per SIMD with the accumulators in AGPRs.
 template <bool SPLIT, int TL>
 static hipError_t launch_knn_shape(const FlashArgs &A, hipStream_t s) {
     const AssignShape sh = assign_shape(A.d);
-    if constexpr (TL > 16) {
-        if (A.d > 64) return launch_fa<64, 1, 2, 8, 2, false, false, false, TL>(A, s);
-    } else {
-        if (sh.nch > 1) return launch_fa<64, 1, 2, 8, 2, false, false, SPLIT, TL>(A, s);
+    if (sh.nch > 1 || (TL > 16 && A.d > 64)) return launch_fa<64, 1, 4, 4, 1, false, false, SPLIT, TL>(A, s);
+    if constexpr (TL <= 16) {
         if (sh.DP == 128) return launch_fa<128, 1, 2, 8, 2, true, false, SPLIT, TL>(A, s);
     }
     switch (sh.DP) {
@@ -1414,9 +1414,11 @@ int knn_list_len(int k) { return k <= kKnnShort ? 16 : 32; }
 
 // Database slices: enough (point blocks x slices) workgroups to fill the chip
 // (one workgroup per CU at a time) many times over when there are few
-// queries -- about 4096, which at 10,000 queries is 64 slices and exactly ten
-// rounds of 256 CUs -- each slice at least 4096 rows and a multiple of
-// kCentroidPad rows (so of every tile height), at most kKnnMaxSlices of them.
+// queries -- about 4096 blocks of 256 queries, which at 10,000 queries is 64
+// slices and exactly ten rounds of 256 CUs (the streamed-chunk kernels take
+// 128 queries per workgroup, so twice as many) -- each slice at least 4096
+// rows and a multiple of kCentroidPad rows (so of every tile height), at most
+// kKnnMaxSlices of them.
 KnnSlices knn_slices(int64_t M, int64_t Ndb) {
     constexpr int64_t kTargetGroups = 4096, kMinRows = 4096;
     const int64_t qb = cdiv(M > 0 ? M : 1, 256);

@@ -237,9 +237,8 @@ fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int3
  * Limits: 0 <= M <= 2^31-1, 1 <= Ndb <= FK_MAX_KNN_DB,
  * 1 <= k <= min(FK_MAX_KNN_K, Ndb); FK_SCORE_SPLIT_BF16 also needs the
  * database's bf16 copy (about 4 Ndb d bytes: Ndb rounded up to 128, d up to
- * 16, 32, 64, 128 or a multiple of 64) under 4 GiB, else FK_ERR_UNSUPPORTED;
- * with k > 12 and d > 64 the sweep scores in fp32 whichever mode is asked.  Q, DB, idx[M,k]
- * (int32) and dist[M,k] (fp32) are device pointers; workspace:
+ * 16, 32, 64, 128 or a multiple of 64) under 4 GiB, else FK_ERR_UNSUPPORTED.
+ * Q, DB, idx[M,k] (int32) and dist[M,k] (fp32) are device pointers; workspace:
  * fk_knn_workspace_size() bytes.
  */
 size_t fk_knn_workspace_size(int64_t M, int32_t d, int64_t Ndb, int32_t k, int32_t metric);
