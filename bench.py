@@ -285,6 +285,11 @@ def ooc_bench(args, fk, synth, np, torch):
     print(json.dumps(out), flush=True)
 
 
+def _rows_label(n):
+    """16777216 -> '16M' (a multiple of 2^20), else the plain count."""
+    return f"{n >> 20}M" if n % (1 << 20) == 0 else str(n)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -407,7 +412,7 @@ def main():
     C0d = torch.from_numpy(C0).to(dev)
     r = run(args.score, args.steps, args.warmup)
     out = {
-        "metric": "s per Lloyd iter; assign TFLOP/s & update GB/s at N=16M,d=128,K=32768",
+        "metric": f"s per Lloyd iter; assign TFLOP/s & update GB/s at N={_rows_label(w.N)},d={w.d},K={w.K}",
         "value": r["s_per_iter"],
         "unit": "s/iter",
         "n_gpus": 1,
