@@ -327,8 +327,10 @@ fk_status step_assign(const Ctx &c, const float *X, int64_t rows, const float *C
 }
 
 // Inverse index of `a` into the workspace (keys_sorted, perm, offsets), or
-// into caller arrays when given.
-fk_status step_sort(const Ctx &c, const int32_t *a, int64_t rows, int32_t *perm_out, int32_t *offsets_out) {
+// into caller arrays when given.  with_offsets = false leaves the offsets to
+// the segmented reduction, which meets every key change anyway.
+fk_status step_sort(const Ctx &c, const int32_t *a, int64_t rows, int32_t *perm_out, int32_t *offsets_out,
+                    bool with_offsets = true) {
     PhaseScope ph(FK_PH_SORT, c.s);
     int32_t *perm = perm_out ? perm_out : at<int32_t>(c.ws, c.L.perm);
     int32_t *offs = offsets_out ? offsets_out : at<int32_t>(c.ws, c.L.offsets);
@@ -336,13 +338,14 @@ fk_status step_sort(const Ctx &c, const int32_t *a, int64_t rows, int32_t *perm_
                               at<int32_t>(c.ws, c.L.tmp_keys), at<int32_t>(c.ws, c.L.tmp_vals),
                               at<void>(c.ws, c.L.sort_scratch), c.s),
            "radix sort");
-    FK_TRY(launch_offsets(at<int32_t>(c.ws, c.L.keys_sorted), rows, c.K, offs, c.s), "cluster offsets");
+    if (with_offsets)
+        FK_TRY(launch_offsets(at<int32_t>(c.ws, c.L.keys_sorted), rows, c.K, offs, c.s), "cluster offsets");
     return FK_OK;
 }
 
 // Accumulators for rows fed in several batches start at zero.  A single batch
-// writes the sums and takes the counts from the offsets, so only an empty
-// batch needs zero counts.
+// writes the centroids and counts directly, so only an empty one (finalized
+// from zero counts) needs them.
 fk_status step_zero_accumulators(const Ctx &c, bool batches, int64_t rows) {
     PhaseScope ph(FK_PH_REDUCE, c.s);
     if (batches) FK_TRY(launch_fill_zero(at<void>(c.ws, c.L.sums), (size_t)c.K * c.d * 8, c.s), "zero sums");
@@ -350,33 +353,41 @@ fk_status step_zero_accumulators(const Ctx &c, bool batches, int64_t rows) {
     return FK_OK;
 }
 
-// Sort-Inverse accumulation of `rows` rows into the fp64 sums and counts
-// (added to them when `batches`, else written).
-fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int32_t *a, bool batches) {
+// Sort-Inverse reduction of `rows` rows.  batches: added into the fp64 sums
+// and counts, which step_finalize divides once every batch is in.  Otherwise
+// the rows are all of them (rows > 0) and the new centroids and counts go
+// straight to C_out and counts (C_prev for an empty cluster).
+fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int32_t *a, bool batches,
+                          const float *C_prev = nullptr, float *C_out = nullptr, int32_t *counts = nullptr) {
     if (rows <= 0) return FK_OK;
-    fk_status st = step_sort(c, a, rows, nullptr, nullptr);
+    fk_status st = step_sort(c, a, rows, nullptr, nullptr, false);
     if (st != FK_OK) return st;
-    PhaseScope ph(FK_PH_REDUCE, c.s);
-    const double *xn = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.xnorm64) : nullptr;
-    FK_TRY(launch_seg_reduce(X, rows, c.d, c.K, at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.perm), xn,
-                             at<double>(c.ws, c.L.sums), at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast),
-                             batches, c.s),
-           "segmented reduction");
-    FK_TRY(launch_seg_fixup(at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.offsets), rows, c.d, c.K,
-                            at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast), at<double>(c.ws, c.L.sums),
-                            batches, c.s),
-           "segment fix-up");
-    if (batches)
-        FK_TRY(launch_count_accumulate(at<int32_t>(c.ws, c.L.offsets), c.K, at<int32_t>(c.ws, c.L.cnt), true, c.s),
-               "count accumulate");
+    int32_t *offs = at<int32_t>(c.ws, c.L.offsets);
+    {
+        PhaseScope ph(FK_PH_REDUCE, c.s);
+        const double *xn = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.xnorm64) : nullptr;
+        FK_TRY(launch_seg_reduce(X, rows, c.d, c.K, at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.perm),
+                                 xn, at<double>(c.ws, c.L.sums), at<double>(c.ws, c.L.pfirst),
+                                 at<double>(c.ws, c.L.plast), batches, offs, C_out, c.s),
+               "segmented reduction");
+        FK_TRY(launch_seg_fixup(at<int32_t>(c.ws, c.L.keys_sorted), offs, rows, c.d, c.K,
+                                at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast),
+                                at<double>(c.ws, c.L.sums), batches, C_out, c.s),
+               "segment fix-up");
+        if (batches)
+            FK_TRY(launch_count_accumulate(offs, c.K, at<int32_t>(c.ws, c.L.cnt), true, c.s), "count accumulate");
+    }
+    if (!batches) {
+        PhaseScope ph(FK_PH_FINALIZE, c.s);
+        FK_TRY(launch_counts_keep(offs, c.K, c.d, C_prev, C_out, counts, c.s), "counts");
+    }
     return FK_OK;
 }
 
-// one_batch: the rows came in a single non-empty batch (counts from offsets)
-fk_status step_finalize(const Ctx &c, const float *C_prev, float *C_out, int32_t *counts, bool one_batch) {
+// Centroids from the accumulated sums and counts (C_prev for an empty cluster)
+fk_status step_finalize(const Ctx &c, const float *C_prev, float *C_out, int32_t *counts) {
     PhaseScope ph(FK_PH_FINALIZE, c.s);
-    FK_TRY(launch_finalize(at<double>(c.ws, c.L.sums), at<int32_t>(c.ws, c.L.cnt),
-                           one_batch ? at<int32_t>(c.ws, c.L.offsets) : nullptr, C_prev, c.K, c.d, C_out, counts,
+    FK_TRY(launch_finalize(at<double>(c.ws, c.L.sums), at<int32_t>(c.ws, c.L.cnt), C_prev, c.K, c.d, C_out, counts,
                            c.s),
            "finalize");
     return FK_OK;
@@ -403,9 +414,9 @@ fk_status lloyd_step(const Ctx &c, const float *X, int64_t N, const float *C_in,
         if ((st = step_prep(c, C_in, &Cu)) != FK_OK) return st;
         if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
         if ((st = step_assign(c, X, N, C_in, Cu, assign, min_dist)) != FK_OK) return st;
-        if ((st = step_accumulate(c, X, N, assign, false)) != FK_OK) return st;
+        return step_accumulate(c, X, N, assign, false, C_in, C_out, counts);
     }
-    return step_finalize(c, C_in, C_out, counts, N > 0);
+    return step_finalize(c, C_in, C_out, counts);
 }
 
 // n_iter Lloyd iterations from C_init; the centroid buffers alternate between
@@ -502,8 +513,8 @@ fk_status fk_update(const float *X, int64_t N, int32_t d, const int32_t *assign,
     const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, FK_SCORE_FP32};
     if ((st = step_zero_accumulators(c, false, N)) != FK_OK) return st;
     if ((st = step_xnorm(c, X, N)) != FK_OK) return st;
-    if ((st = step_accumulate(c, X, N, assign, false)) != FK_OK) return st;
-    return step_finalize(c, C_prev, C_out, counts, N > 0);
+    if (N > 0) return step_accumulate(c, X, N, assign, false, C_prev, C_out, counts);
+    return step_finalize(c, C_prev, C_out, counts);
 }
 
 fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in, int32_t K, int32_t metric,
@@ -628,7 +639,7 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
             FK_TRY(hipMemcpyAsync(assign_host + r0, ad, (size_t)rows * 4, hipMemcpyDeviceToHost, c.s),
                    "assignment copy");
     }
-    return step_finalize(c, C_in, C_out, counts, false);
+    return step_finalize(c, C_in, C_out, counts);
 }
 
 size_t fk_fit_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric) {

@@ -18,10 +18,10 @@ constexpr int kWave = 64;
 constexpr int kCentroidPad = 128;
 
 // ---- radix sort geometry --------------------------------------------------
-constexpr int kSortWaves = 4;
+constexpr int kSortWaves = 8;
 constexpr int kSortThreads = kSortWaves * kWave;
 constexpr int kSortRows = 16;                                  // 64-key rows per wave
-constexpr int kSortTile = kSortWaves * kSortRows * kWave;       // 4096 keys per tile
+constexpr int kSortTile = kSortWaves * kSortRows * kWave;       // 8192 keys per tile
 
 // ---- segmented reduction geometry -----------------------------------------
 constexpr int kSegWaves = 4;
@@ -113,16 +113,24 @@ hipError_t launch_sort_by_key(const int32_t *keys, int64_t N, int K, int32_t *ke
 hipError_t launch_offsets(const int32_t *keys_sorted, int64_t N, int K, int32_t *offsets, hipStream_t s);
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
-// acc: add to sums / cnt (rows fed in several batches) instead of writing them
+// The segmented reduction also writes the cluster offsets (first sorted row of
+// each key, offsets[K] = N).  acc: rows fed in several batches, cluster sums
+// added to sums (divided by launch_finalize at the end); otherwise the rows
+// came in one batch and the reduction and its fix-up write the new centroids
+// of the non-empty clusters to C_out, launch_counts_keep the rest.
 hipError_t launch_seg_reduce(const float *X, int64_t N, int d, int K, const int32_t *keys_sorted, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
-                             hipStream_t s);
+                             int32_t *offsets, float *C_out, hipStream_t s);
 hipError_t launch_seg_fixup(const int32_t *keys_sorted, const int32_t *offsets, int64_t N, int d, int K,
-                            const double *pfirst, const double *plast, double *sums, bool acc, hipStream_t s);
+                            const double *pfirst, const double *plast, double *sums, bool acc, float *C_out,
+                            hipStream_t s);
 hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, bool acc, hipStream_t s);
-// counts from cnt, or (offsets != nullptr, rows in one batch) from the offsets
-hipError_t launch_finalize(const double *sums, const int32_t *cnt, const int32_t *offsets, const float *C_prev, int K,
-                           int d, float *C_out, int32_t *counts_out, hipStream_t s);
+// counts from the offsets, previous centroids for the empty clusters
+hipError_t launch_counts_keep(const int32_t *offsets, int K, int d, const float *C_prev, float *C_out,
+                              int32_t *counts_out, hipStream_t s);
+// counts from cnt, C_out = sums / count (C_prev for an empty cluster)
+hipError_t launch_finalize(const double *sums, const int32_t *cnt, const float *C_prev, int K, int d, float *C_out,
+                           int32_t *counts_out, hipStream_t s);
 
 // k nearest neighbours (k <= kMaxKnn): the sweep cuts the database into
 // slices (a second grid dimension) and writes, per query and slice, the L

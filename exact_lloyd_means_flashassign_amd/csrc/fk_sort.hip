@@ -7,7 +7,7 @@
 // contiguous reads without any atomic operation.  Keys are below K <= 65536,
 // so at most two passes of <= 8 bits are needed.
 //
-// Each pass is hist -> scan -> scatter over tiles of 4096 keys.  Inside a tile
+// Each pass is hist -> scan -> scatter over tiles of 8192 keys.  Inside a tile
 // the scatter ranks 64 keys at a time with ballots: for a digit of B bits, B
 // ballots give every lane the mask of lanes holding the same digit; its rank
 // is the number of such lanes below it, and the lowest such lane (the leader)

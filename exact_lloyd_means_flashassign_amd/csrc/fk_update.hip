@@ -16,7 +16,11 @@
 //     k_seg_fixup adds those partials in a fixed order.
 // Every output element has exactly one writer and a fixed summation order, so
 // the result is bitwise reproducible.  Sums are fp64.  The gathered rows
-// X[perm[r]] are read as whole coalesced rows.
+// X[perm[r]] are read as whole coalesced rows.  When all rows come in one
+// batch, the divide by the count is done where a cluster's sum is complete
+// (the wave of an inner cluster, k_seg_fixup for a crossing one), so the fp64
+// sums never go through memory; the cluster offsets are written by the
+// reduction as it meets each key change.
 #include "fk_internal.h"
 
 namespace fk {
@@ -33,13 +37,18 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t *__restrict__ p, int
 // blockIdx.y * 64*E*NV.  U rows are loaded before they are accumulated so that
 // U row reads per lane are in flight at once.  COS: rows are scaled by
 // 1/xnorm64 (cosine).  ACC: cluster sums are added to what sums holds (rows
-// fed in several batches); otherwise they are written, and the clusters that
-// no row reaches are left untouched (the finalize step does not read them).
+// fed in several batches; the finalize step divides).  Otherwise the rows
+// come in one batch and a cluster inside the segment is written to C_out as
+// its sum divided by its row count (clusters that no row reaches are left to
+// k_counts_keep).  The column block blockIdx.y == 0 also writes offsets[k] =
+// the first sorted row whose key is >= k (offsets[K] = N): the entries between
+// two consecutive keys are written by the wave that sees the change.
 template <int NV, int E, int U, bool COS, bool ACC>
 __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X, int64_t N, int d, int K, int srows,
                                                     const int32_t *__restrict__ ks, const int32_t *__restrict__ perm,
                                                     const double *__restrict__ xnorm64, double *__restrict__ sums,
-                                                    double *__restrict__ pfirst, double *__restrict__ plast) {
+                                                    double *__restrict__ pfirst, double *__restrict__ plast,
+                                                    int32_t *__restrict__ offsets, float *__restrict__ C_out) {
     // the wave index is uniform across the wave: taking it as a scalar makes
     // the segment bounds, the keys and every branch on them scalar
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
@@ -50,9 +59,18 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
     const int cbase = blockIdx.y * (64 * E * NV);
 
     const int first_k = ks[r0];
-    const bool started_before = r0 > 0 && ks[r0 - 1] == first_k;
+    const int prev_k = r0 > 0 ? ks[r0 - 1] : -1;
+    const bool started_before = r0 > 0 && prev_k == first_k;
     const int last_k = ks[r1 - 1];
     const bool cont_after = r1 < N && ks[r1] == last_k;
+    int32_t *const offs = blockIdx.y == 0 ? offsets : nullptr;
+    // offsets[from+1 .. to] = row, spread over the lanes (the clamps only keep
+    // a key outside [0, K) from writing outside offsets[0..K])
+    auto mark = [&](int from, int to, int64_t row) {
+        const int lo = max(from + 1, 0), hi = min(to, K);
+        for (int k = lo + lane; k <= hi; k += 64) offs[k] = (int32_t)row;
+    };
+    if (offs != nullptr) mark(prev_k, first_k, r0);
 
     int col[NV];
     bool cok[NV];
@@ -68,8 +86,10 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
 #pragma unroll
         for (int e = 0; e < E; ++e) acc[v][e] = 0.0;
     int cur = first_k;
+    int64_t cstart = r0;  // first row of cluster cur in this segment
 
-    auto flush = [&](int k) {
+    // the sum of cluster k, whose rows in this segment end before row rend
+    auto flush = [&](int k, int64_t rend) {
         // keys are documented to lie in [0, K); a bad key is dropped rather
         // than written outside the sums
         if ((unsigned)k >= (unsigned)K) {
@@ -79,18 +99,27 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
                 for (int e = 0; e < E; ++e) acc[v][e] = 0.0;
             return;
         }
-        double *dst;
-        bool add;
-        if (k == first_k && started_before) {
-            dst = pfirst + seg * (int64_t)d;
-            add = false;
-        } else if (k == last_k && cont_after) {
-            dst = plast + seg * (int64_t)d;
-            add = false;
-        } else {
-            dst = sums + (int64_t)k * d;
-            add = ACC;
+        const bool part_first = k == first_k && started_before;
+        const bool part_last = k == last_k && cont_after;
+        if (!ACC && !part_first && !part_last) {
+            // the whole cluster is in this segment: its centroid
+            const double n = (double)(rend - cstart);
+            float *o = C_out + (int64_t)k * d;
+#pragma unroll
+            for (int v = 0; v < NV; ++v) {
+                if (!cok[v]) continue;
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    o[col[v] + e] = (float)(acc[v][e] / n);
+                    acc[v][e] = 0.0;
+                }
+            }
+            return;
         }
+        double *dst = part_first  ? pfirst + seg * (int64_t)d
+                      : part_last ? plast + seg * (int64_t)d
+                                  : sums + (int64_t)k * d;
+        const bool add = !part_first && !part_last;  // ACC here
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
             if (!cok[v]) continue;
@@ -151,8 +180,11 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
             if (r + off + u >= r1) break;
             const int key = __builtin_amdgcn_readlane(kk, off + u);
             if (key != cur) {
-                flush(cur);
+                const int64_t rr = r + off + u;
+                if (offs != nullptr) mark(cur, key, rr);
+                flush(cur, rr);
                 cur = key;
+                cstart = rr;
             }
             // columns past d add into accumulators that are never written
 #pragma unroll
@@ -187,13 +219,15 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
         ppc = ppn;
         load_window(r + 128, kkn, ppn);
     }
-    flush(cur);
+    flush(cur, r1);
+    if (offs != nullptr && r1 == N) mark(cur, K, N);
 }
 
 // One workgroup per segment boundary b (between segments b and b+1).  If a
 // cluster k crosses it and b is the first boundary k crosses, the workgroup
 // adds k's partials: plast of k's first segment, then pfirst of every later
-// segment k touches, into sums[k] (acc) or as sums[k].  Wave w takes the
+// segment k touches, into sums[k] (acc), or (rows in one batch) divides the
+// total by the cluster's row count into C_out[k].  Wave w takes the
 // segments sa+1+w, sa+1+w+8, ... in order (eight loads in flight: the
 // largest cluster of a skewed mixture crosses thousands of boundaries); the
 // 8 wave sums are added in wave order.  Most workgroups find no cluster to
@@ -204,7 +238,8 @@ __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__r
                                                              int K, int srows,
                                                              const double *__restrict__ pfirst,
                                                              const double *__restrict__ plast,
-                                                             double *__restrict__ sums, bool acc) {
+                                                             double *__restrict__ sums, bool acc,
+                                                             float *__restrict__ C_out) {
     __shared__ double red[kFixWaves][64];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int64_t b = blockIdx.x;
@@ -237,8 +272,12 @@ __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__r
             double t = red[0][lane];
 #pragma unroll
             for (int ww = 1; ww < kFixWaves; ++ww) t += red[ww][lane];
-            double *dst = sums + (int64_t)k * d + c;
-            *dst = acc ? *dst + t : t;
+            if (acc) {
+                double *dst = sums + (int64_t)k * d + c;
+                *dst += t;
+            } else {
+                C_out[(int64_t)k * d + c] = (float)(t / (double)(o1 - o0));
+            }
         }
         __syncthreads();
     }
@@ -251,16 +290,29 @@ __global__ __launch_bounds__(256) void k_count_acc(const int32_t *__restrict__ o
     if (k < K) cnt[k] = (acc ? cnt[k] : 0) + offsets[k + 1] - offsets[k];
 }
 
-// C_out = sums / n_k, or C_prev for an empty cluster; counts_out = n_k, with
-// n_k = cnt[k], or offsets[k+1] - offsets[k] when the rows came in one batch.
+// Rows in one batch: counts_out[k] = offsets[k+1] - offsets[k], and a cluster
+// with no row keeps its previous centroid (the others were written by the
+// reduction).
+__global__ __launch_bounds__(256) void k_counts_keep(const int32_t *__restrict__ offsets, int K, int d,
+                                                     const float *__restrict__ C_prev, float *__restrict__ C_out,
+                                                     int32_t *__restrict__ counts_out) {
+    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    if (k >= K) return;
+    const int c = offsets[k + 1] - offsets[k];
+    counts_out[k] = c;
+    if (c == 0)
+        for (int j = 0; j < d; ++j) C_out[(int64_t)k * d + j] = C_prev[(int64_t)k * d + j];
+}
+
+// Rows in several batches: C_out = sums / n_k, or C_prev for an empty
+// cluster; counts_out = n_k = cnt[k].
 __global__ __launch_bounds__(256) void k_finalize(const double *__restrict__ sums, const int32_t *__restrict__ cnt,
-                                                  const int32_t *__restrict__ offsets,
                                                   const float *__restrict__ C_prev, int64_t total, int d,
                                                   float *__restrict__ C_out, int32_t *__restrict__ counts_out) {
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= total) return;
     const int64_t k = q / d;
-    const int c = offsets != nullptr ? offsets[k + 1] - offsets[k] : cnt[k];
+    const int c = cnt[k];
     C_out[q] = c > 0 ? (float)(sums[q] / (double)c) : C_prev[q];
     if (q == k * d) counts_out[k] = c;
 }
@@ -278,7 +330,7 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
 template <int NV, int E>
 static hipError_t seg_launch(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
-                             hipStream_t s) {
+                             int32_t *offsets, float *C_out, hipStream_t s) {
     constexpr int U = NV * E <= 2 ? 8 : (NV * E <= 8 ? 8 : 4);
     const int srows = seg_rows(N);
     const int64_t nseg = cdiv(N, srows);
@@ -287,17 +339,17 @@ static hipError_t seg_launch(const float *X, int64_t N, int d, int K, const int3
     if (xnorm64 != nullptr) {
         if (acc)
             hipLaunchKernelGGL((k_seg_reduce<NV, E, U, true, true>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
-                               xnorm64, sums, pfirst, plast);
+                               xnorm64, sums, pfirst, plast, offsets, C_out);
         else
             hipLaunchKernelGGL((k_seg_reduce<NV, E, U, true, false>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
-                               xnorm64, sums, pfirst, plast);
+                               xnorm64, sums, pfirst, plast, offsets, C_out);
     } else {
         if (acc)
             hipLaunchKernelGGL((k_seg_reduce<NV, E, U, false, true>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
-                               xnorm64, sums, pfirst, plast);
+                               xnorm64, sums, pfirst, plast, offsets, C_out);
         else
             hipLaunchKernelGGL((k_seg_reduce<NV, E, U, false, false>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
-                               xnorm64, sums, pfirst, plast);
+                               xnorm64, sums, pfirst, plast, offsets, C_out);
     }
     return hipGetLastError();
 }
@@ -305,12 +357,14 @@ static hipError_t seg_launch(const float *X, int64_t N, int d, int K, const int3
 template <int E>
 static hipError_t seg_launch_e(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
                                const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
-                               hipStream_t s) {
+                               int32_t *offsets, float *C_out, hipStream_t s) {
     const int need = (int)cdiv(d, 64 * E);
-    if (need <= 1) return seg_launch<1, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
-    if (need <= 2) return seg_launch<2, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
-    if (need <= 3) return seg_launch<3, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
-    return seg_launch<4, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
+#define FK_SEG(nv) seg_launch<nv, E>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, offsets, C_out, s)
+    if (need <= 1) return FK_SEG(1);
+    if (need <= 2) return FK_SEG(2);
+    if (need <= 3) return FK_SEG(3);
+    return FK_SEG(4);
+#undef FK_SEG
 }
 
 // Row loads of E floats per lane: float4 when a row spans at least 256
@@ -318,20 +372,22 @@ static hipError_t seg_launch_e(const float *X, int64_t N, int d, int K, const in
 // column blocks of up to 4 loads per lane, more blocks on blockIdx.y.
 hipError_t launch_seg_reduce(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
-                             hipStream_t s) {
+                             int32_t *offsets, float *C_out, hipStream_t s) {
     if (N <= 0) return hipSuccess;
-    if (d % 4 == 0 && d >= 256) return seg_launch_e<4>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
-    if (d % 2 == 0 && d >= 128) return seg_launch_e<2>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
-    return seg_launch_e<1>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, s);
+    if (d % 4 == 0 && d >= 256)
+        return seg_launch_e<4>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, offsets, C_out, s);
+    if (d % 2 == 0 && d >= 128)
+        return seg_launch_e<2>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, offsets, C_out, s);
+    return seg_launch_e<1>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, offsets, C_out, s);
 }
 
 hipError_t launch_seg_fixup(const int32_t *ks, const int32_t *offsets, int64_t N, int d, int K, const double *pfirst,
-                            const double *plast, double *sums, bool acc, hipStream_t s) {
+                            const double *plast, double *sums, bool acc, float *C_out, hipStream_t s) {
     const int srows = seg_rows(N);
     const int64_t nseg = cdiv(N, srows);
     if (nseg <= 1) return hipSuccess;
     hipLaunchKernelGGL(k_seg_fixup, dim3((unsigned)(nseg - 1)), dim3(kFixWaves * 64), 0, s, ks, offsets, N, d, K,
-                       srows, pfirst, plast, sums, acc);
+                       srows, pfirst, plast, sums, acc, C_out);
     return hipGetLastError();
 }
 
@@ -340,11 +396,18 @@ hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, 
     return hipGetLastError();
 }
 
-hipError_t launch_finalize(const double *sums, const int32_t *cnt, const int32_t *offsets, const float *C_prev, int K,
-                           int d, float *C_out, int32_t *counts_out, hipStream_t s) {
+hipError_t launch_counts_keep(const int32_t *offsets, int K, int d, const float *C_prev, float *C_out,
+                              int32_t *counts_out, hipStream_t s) {
+    hipLaunchKernelGGL(k_counts_keep, dim3((unsigned)cdiv(K, 256)), dim3(256), 0, s, offsets, K, d, C_prev, C_out,
+                       counts_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(const double *sums, const int32_t *cnt, const float *C_prev, int K, int d, float *C_out,
+                           int32_t *counts_out, hipStream_t s) {
     const int64_t total = (int64_t)K * d;
-    hipLaunchKernelGGL(k_finalize, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, sums, cnt, offsets, C_prev, total,
-                       d, C_out, counts_out);
+    hipLaunchKernelGGL(k_finalize, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, sums, cnt, C_prev, total, d,
+                       C_out, counts_out);
     return hipGetLastError();
 }
 
