@@ -292,16 +292,17 @@ __global__ __launch_bounds__(256) void k_count_acc(const int32_t *__restrict__ o
 
 // Rows in one batch: counts_out[k] = offsets[k+1] - offsets[k], and a cluster
 // with no row keeps its previous centroid (the others were written by the
-// reduction).
+// reduction).  One wave per cluster: an empty cluster's row is copied by the
+// whole wave, coalesced.
 __global__ __launch_bounds__(256) void k_counts_keep(const int32_t *__restrict__ offsets, int K, int d,
                                                      const float *__restrict__ C_prev, float *__restrict__ C_out,
                                                      int32_t *__restrict__ counts_out) {
-    const int k = blockIdx.x * blockDim.x + threadIdx.x;
+    const int k = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
     if (k >= K) return;
     const int c = offsets[k + 1] - offsets[k];
-    counts_out[k] = c;
+    if (lane == 0) counts_out[k] = c;
     if (c == 0)
-        for (int j = 0; j < d; ++j) C_out[(int64_t)k * d + j] = C_prev[(int64_t)k * d + j];
+        for (int j = lane; j < d; j += 64) C_out[(int64_t)k * d + j] = C_prev[(int64_t)k * d + j];
 }
 
 // Rows in several batches: C_out = sums / n_k, or C_prev for an empty
@@ -398,7 +399,7 @@ hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, 
 
 hipError_t launch_counts_keep(const int32_t *offsets, int K, int d, const float *C_prev, float *C_out,
                               int32_t *counts_out, hipStream_t s) {
-    hipLaunchKernelGGL(k_counts_keep, dim3((unsigned)cdiv(K, 256)), dim3(256), 0, s, offsets, K, d, C_prev, C_out,
+    hipLaunchKernelGGL(k_counts_keep, dim3((unsigned)cdiv(K, 4)), dim3(256), 0, s, offsets, K, d, C_prev, C_out,
                        counts_out);
     return hipGetLastError();
 }
