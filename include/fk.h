@@ -262,9 +262,12 @@ enum {
     FK_PH_PREP = 0,      /* centroid norms (and cosine normalisation)       */
     FK_PH_ASSIGN = 1,    /* the FlashAssign kernel                          */
     FK_PH_RECHECK = 2,   /* fp64 rescoring of near-tie points               */
-    FK_PH_SORT = 3,      /* radix sort + offsets (the inverse index)        */
-    FK_PH_REDUCE = 4,    /* segmented reduction + carry fix-up              */
-    FK_PH_FINALIZE = 5,  /* divide by count / keep empty centroids          */
+    FK_PH_SORT = 3,      /* radix sort (the inverse index)                  */
+    FK_PH_REDUCE = 4,    /* segmented reduction + carry fix-up (with the
+                            cluster offsets; rows in one batch: also the
+                            divide by count)                                */
+    FK_PH_FINALIZE = 5,  /* counts, empty centroids kept (and the divide
+                            when rows came in several batches)              */
     FK_PH_H2D = 6,       /* host-to-device chunk copies (out-of-core)       */
     FK_NPHASE = 7
 };
