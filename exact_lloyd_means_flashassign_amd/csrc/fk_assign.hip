@@ -306,6 +306,10 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     // the cross terms in a second accumulator instead (the phases would span
     // chunks).
     constexpr bool PHASED = SPLIT && RES;
+    // Streamed chunks fetch the next stage's points a stage ahead, except
+    // beside 32-long candidate lists (no registers left for them there: the
+    // points are loaded at the start of their own stage).
+    constexpr bool PRE = !RES && TL <= 16;
 
     __shared__ __attribute__((aligned(16))) float sC[2][SPLIT ? 4 : ROWS * LDR];
     __shared__ __attribute__((aligned(16))) __bf16 sCh[2][SPLIT ? ROWS * LDB : 8];
@@ -449,81 +453,87 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             i1[b] = 0;
             i2[b] = 0;
         }
-        // this wave's points into registers.  fp32 scoring: dims
-        // ch*DP + h*HALF + [0, HALF).  split scoring: for MFMA step s, dims
-        // ch*DP + 16s + 8h + [0, 8), each split into a bf16 high part (the
-        // round-to-nearest value) and a bf16 low part (the rounded remainder).
+        // This wave's points in registers.  Slot q (of HALF per point block
+        // and lane) holds, for fp32 scoring, dim ch*DP + h*HALF + q; for split
+        // scoring, dim ch*DP + 16(q/8) + 8h + q%8 of MFMA step q/8, as a bf16
+        // high part (the round-to-nearest value) and a bf16 low part (the
+        // rounded remainder).
+        // fetch_x4: the fp32 values of slots q..q+3 (zero outside the data)
+        auto fetch_x4 = [&](int ch, int b, int q, float *v) {
+            const int col0 = SPLIT ? ch * DP + 16 * (q / 8) + 8 * h + (q % 8) : ch * DP + h * HALF + q;
+            const float *src = X + (size_t)pt[b] * d + col0;
+            if (VEC) {
+                float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (pv[b] && col0 < d) u = *reinterpret_cast<const float4 *>(src);
+                v[0] = u.x;
+                v[1] = u.y;
+                v[2] = u.z;
+                v[3] = u.w;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = (pv[b] && col0 + e < d) ? src[e] : 0.f;
+            }
+        };
+        // put_x: slot q's value into the MFMA operand registers (scaled for
+        // cosine) and, with add_norm, into the point's squared norms
+        auto put_x = [&](int b, int q, float v, bool add_norm, float &nacc, float &lacc, float &racc) {
+            const float xv = (A.xnorm64 != nullptr) ? v * xsc[b] : v;
+            if constexpr (SPLIT) {
+                const __bf16 hi = (__bf16)xv;
+                const float dl = xv - (float)hi;  // exact
+                const __bf16 lo = (__bf16)dl;
+                xh[b][q / 8][q % 8] = hi;
+                xl[b][q / 8][q % 8] = lo;
+                if (add_norm) {
+                    const float lf = (float)lo, r = dl - lf;  // exact
+                    nacc = fmaf(xv, xv, nacc);
+                    lacc = fmaf(lf, lf, lacc);
+                    racc = fmaf(r, r, racc);
+                }
+            } else {
+                xr[b][q] = xv;
+                if (add_norm) nacc = fmaf(xv, xv, nacc);
+            }
+        };
         auto load_x = [&](int ch, bool add_norm) {
 #pragma unroll
             for (int b = 0; b < PB; ++b) {
-                if constexpr (SPLIT) {
-                    float nacc = xn[b], lacc = xl2[b], racc = xr2[b];
+                float nacc = xn[b], lacc = xl2[b], racc = xr2[b];
 #pragma unroll
-                    for (int st = 0; st < NS; ++st) {
-                        const int col0 = ch * DP + 16 * st + 8 * h;
-                        const float *src = X + (size_t)pt[b] * d + col0;
-                        float v[8];
-                        if (VEC) {
-                            float4 u0 = make_float4(0.f, 0.f, 0.f, 0.f), u1 = u0;
-                            if (pv[b] && col0 < d) u0 = *reinterpret_cast<const float4 *>(src);
-                            if (pv[b] && col0 + 4 < d) u1 = *reinterpret_cast<const float4 *>(src + 4);
-                            v[0] = u0.x; v[1] = u0.y; v[2] = u0.z; v[3] = u0.w;
-                            v[4] = u1.x; v[5] = u1.y; v[6] = u1.z; v[7] = u1.w;
-                        } else {
+                for (int q = 0; q < HALF; q += 8) {
+                    float v[8];
+                    fetch_x4(ch, b, q, v);
+                    fetch_x4(ch, b, q + 4, v + 4);
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) v[e] = (pv[b] && col0 + e < d) ? src[e] : 0.f;
-                        }
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const float xv = (A.xnorm64 != nullptr) ? v[e] * xsc[b] : v[e];
-                            const __bf16 hi = (__bf16)xv;
-                            const float dl = xv - (float)hi;  // exact
-                            const __bf16 lo = (__bf16)dl;
-                            xh[b][st][e] = hi;
-                            xl[b][st][e] = lo;
-                            if (add_norm) {
-                                const float lf = (float)lo, r = dl - lf;  // exact
-                                nacc = fmaf(xv, xv, nacc);
-                                lacc = fmaf(lf, lf, lacc);
-                                racc = fmaf(r, r, racc);
-                            }
-                        }
-                        // keep the scheduler from hoisting every load of the
-                        // row ahead of the splits (it would hold all the fp32
-                        // values and the bf16 halves live at once)
-                        __builtin_amdgcn_sched_barrier(0);
-                    }
-                    xn[b] = nacc;
-                    xl2[b] = lacc;
-                    xr2[b] = racc;
-                } else {
-                    const int col0 = ch * DP + h * HALF;
-                    const float *src = X + (size_t)pt[b] * d + col0;
-                    if (VEC) {
-#pragma unroll
-                        for (int s = 0; s < HALF; s += 4) {
-                            float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-                            if (pv[b] && col0 + s < d) v = *reinterpret_cast<const float4 *>(src + s);
-                            xr[b][s] = v.x;
-                            xr[b][s + 1] = v.y;
-                            xr[b][s + 2] = v.z;
-                            xr[b][s + 3] = v.w;
-                        }
-                    } else {
-#pragma unroll
-                        for (int s = 0; s < HALF; ++s) xr[b][s] = (pv[b] && col0 + s < d) ? src[s] : 0.f;
-                    }
-                    if (A.xnorm64 != nullptr) {
-#pragma unroll
-                        for (int s = 0; s < HALF; ++s) xr[b][s] *= xsc[b];
-                    }
-                    if (add_norm) {
-                        float acc = xn[b];
-#pragma unroll
-                        for (int s = 0; s < HALF; ++s) acc = fmaf(xr[b][s], xr[b][s], acc);
-                        xn[b] = acc;
-                    }
+                    for (int e = 0; e < 8; ++e) put_x(b, q + e, v[e], add_norm, nacc, lacc, racc);
+                    // split scoring: keep the scheduler from hoisting every
+                    // load of the row ahead of the splits (it would hold all
+                    // the fp32 values and the bf16 halves live at once)
+                    if constexpr (SPLIT) __builtin_amdgcn_sched_barrier(0);
                 }
+                xn[b] = nacc;
+                xl2[b] = lacc;
+                xr2[b] = racc;
+            }
+        };
+        // streamed chunks: the next stage's point values, fetched a whole
+        // stage ahead and put into the operand registers at its end
+        float xraw[PB][PRE ? HALF : 4];
+        auto fetch_next = [&](int ch) {
+#pragma unroll
+            for (int b = 0; b < PB; ++b)
+#pragma unroll
+                for (int q = 0; q < HALF; q += 4) fetch_x4(ch, b, q, &xraw[b][q]);
+        };
+        auto put_next = [&](bool add_norm) {
+#pragma unroll
+            for (int b = 0; b < PB; ++b) {
+                float nacc = xn[b], lacc = xl2[b], racc = xr2[b];
+#pragma unroll
+                for (int q = 0; q < HALF; ++q) put_x(b, q, xraw[b][q], add_norm, nacc, lacc, racc);
+                xn[b] = nacc;
+                xl2[b] = lacc;
+                xr2[b] = racc;
             }
         };
 
@@ -658,8 +668,8 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         const int tb = TL > 0 ? (int)blockIdx.y * A.knn_tps : 0;
         const int te = TL > 0 ? min(A.ntiles, tb + A.knn_tps) : A.ntiles;
         const int nst = (te - tb) * cnch;
+        if (RES || PRE) load_x(0, true);
         if (RES) {
-            load_x(0, true);
             if (!COLLECT) point_bounds();
             if constexpr (PHASED) {
                 // the split points are packed into their MFMA operand
@@ -684,9 +694,14 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 nt = t + 1;
             }
             const bool more = st + 1 < nst;
-            // the chunk's own points first, so that waiting for them does not
-            // also wait for the next stage's prefetch
-            if (!RES) load_x(ch, t == tb);
+            // streamed chunks: the next stage's points are fetched with the
+            // next centroid stage, a whole stage before they are used (beside
+            // 32-long lists: this stage's points, loaded now)
+            if constexpr (PRE) {
+                if (more) fetch_next(nc);
+            } else if constexpr (!RES) {
+                load_x(ch, t == tb);
+            }
             if (more) load_stage(nt, nc);
 
             if constexpr (!PHASED) {
@@ -824,6 +839,14 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 }
             }
             if (!(PHASED && CB > 1) && more) store_stage(buf ^ 1, nc);
+            if constexpr (PRE) {
+                if (more) {
+                    // after this stage's products: the wait for the fetched
+                    // values must not move ahead of them
+                    __builtin_amdgcn_sched_barrier(0);
+                    put_next(nt == tb);
+                }
+            }
             __syncthreads();
             t = nt;
             ch = nc;

@@ -95,6 +95,27 @@ def test_update_single_giant_cluster(gpu_lib):
     check_update(X, a, C_prev, host(C_out), host(counts))
 
 
+@pytest.mark.parametrize("d", [33, 128, 300])
+def test_update_sparse_labels(gpu_lib, d):
+    """Labels on a few scattered clusters: cluster 0, long runs of ids and the
+    last ids are empty, one cluster holds half the rows (it crosses many
+    segment boundaries) and a few hold one row each.  The reduction writes
+    the cluster offsets at each key change and the centroids of the clusters
+    it completes; the empty ones must keep C_prev and count 0."""
+    fk = gpu_lib
+    N, K = 150001, 5000
+    rng = np.random.default_rng(d)
+    ids = np.array([3, 4, 17, 2000, 4990] + list(range(500, 540)), np.int32)
+    a = rng.choice(ids, size=N).astype(np.int32)
+    a[rng.choice(N, N // 2, replace=False)] = 2000
+    a[rng.choice(N, 3, replace=False)] = np.array([1, 1234, 4998], np.int32)
+    X = rng.standard_normal((N, d)).astype(np.float32)
+    C_prev = rng.standard_normal((K, d)).astype(np.float32)
+    log(f"update sparse labels d={d}")
+    C_out, counts = fk.fk_update(dev(X), dev(a), dev(C_prev))
+    check_update(X, a, C_prev, host(C_out), host(counts))
+
+
 def test_update_empty_input(gpu_lib):
     fk = gpu_lib
     C_prev = np.random.default_rng(1).standard_normal((9, 5)).astype(np.float32)
