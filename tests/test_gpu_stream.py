@@ -51,3 +51,27 @@ def test_stream_without_assignment_output(gpu_lib):
     ref = oracle.lloyd_iter(X, C)
     np.testing.assert_array_equal(host(n_s), ref["counts"])
     assert centroid_rel_err(host(C_s), ref["C"], ref["counts"]) <= 1e-6
+
+
+@pytest.mark.parametrize("score", ["fp32", "split_bf16"])
+@pytest.mark.parametrize("d,chunk", [(200, 20000), (37, 7777)])
+def test_stream_other_widths(gpu_lib, d, chunk, score):
+    """Streamed chunks of rows with d > 128 (points streamed through the
+    assignment kernel in 64-dim chunks) and with a ragged d: the batches'
+    sums, counts and offsets add up to the in-core iteration and the oracle."""
+    fk = gpu_lib
+    rng = np.random.default_rng(d)
+    N, K = 50001, 300
+    X = rng.standard_normal((N, d)).astype(np.float32)
+    C = X[rng.choice(N, K, replace=False)].copy()
+    log(f"stream d={d} chunk={chunk} score={score}")
+    a_ic, C_ic, n_ic, _ = fk.fk_lloyd_iter(dev(X), dev(C), score=score)
+    ah = torch.empty(N, dtype=torch.int32, pin_memory=True)
+    C_s, n_s = fk.fk_lloyd_iter_stream(_pinned(X), dev(C), chunk, assign_host=ah, score=score)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ah.numpy(), host(a_ic))
+    np.testing.assert_array_equal(host(n_s), host(n_ic))
+    ref = oracle.lloyd_iter(X, C)
+    np.testing.assert_array_equal(ah.numpy(), ref["a"])
+    np.testing.assert_array_equal(host(n_s), ref["counts"])
+    assert centroid_rel_err(host(C_s), ref["C"], ref["counts"]) <= 1e-6
