@@ -44,7 +44,7 @@ struct Layout {
     size_t sums, cnt, pfirst, plast, csplit;
     size_t xchunk[2], achunk[2];      // out-of-core only
     size_t ctmp, cinit, labels, xcopy;  // fit / IVF build only
-    size_t knn_cand, knn_score, knn_win, knn_list;  // k nearest neighbours only
+    size_t knn_cand, knn_score, knn_win, knn_list, knn_tau;  // k nearest neighbours only
 };
 
 constexpr size_t kNone = ~(size_t)0;
@@ -100,7 +100,7 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc, int extras 
     L.cinit = ivf ? take((size_t)K * d * 4) : kNone;
     L.labels = ivf ? take((size_t)r * 4) : kNone;
     L.xcopy = (ivf && cos) ? take((size_t)r * d * 4) : kNone;
-    L.knn_cand = L.knn_score = L.knn_win = L.knn_list = kNone;
+    L.knn_cand = L.knn_score = L.knn_win = L.knn_list = L.knn_tau = kNone;
     L.total = off;
     return L;
 }
@@ -133,6 +133,7 @@ Layout make_knn_layout(int64_t M, int d, int64_t Ndb, int k, int metric) {
     L.knn_score = take(ncand * 4);
     L.knn_win = take((size_t)m * 4);
     L.knn_list = take((size_t)m * 4);
+    L.knn_tau = take((size_t)m * 4);
     L.flags = L.thr = L.pairs = L.cand = L.ccount = L.ovf = kNone;
     L.keys_sorted = L.perm = L.tmp_keys = L.tmp_vals = L.sort_scratch = L.offsets = kNone;
     L.sums = L.cnt = L.pfirst = L.plast = kNone;
@@ -776,7 +777,7 @@ fk_status fk_knn(const float *Q, int64_t M, int32_t d, const float *DB, int64_t 
     {
         PhaseScope ph(FK_PH_ASSIGN, s);
         FK_TRY(launch_knn_sweep(Q, M, d, DBu, at<float>(workspace, L.ncn), (int)Ndb, at<float>(workspace, L.scal), qn,
-                                c.split(), ip, k, cand, cscore, win, s),
+                                c.split(), ip, k, cand, cscore, win, at<float>(workspace, L.knn_tau), s),
                "knn sweep");
     }
     {

@@ -61,6 +61,11 @@ struct FlashArgs {
     int32_t *knn_cand;
     float *knn_score;
     float *knn_win;
+    // knn_tau: per point, a score at or below its L-th best over all rows
+    // (the lists start from it instead of -inf), or null; knn_tau_out: the
+    // sweep only writes each point's L-th best score of its rows there
+    const float *knn_tau;
+    float *knn_tau_out;
 };
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -315,6 +320,9 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     // their own, alongside its products (not beside candidate lists: the
     // registers are not there).
     constexpr bool PRE2 = PRE && SPLIT && TL == 0;
+    // top-L lists that may start from a threshold (the 16-long lists beside
+    // streamed d-chunks never do: that sweep runs without the threshold pass)
+    constexpr bool TAU = TL > 0 && (RES || TL > 16);
 
     __shared__ __attribute__((aligned(16))) float sC[2][SPLIT ? 4 : ROWS * LDR];
     __shared__ __attribute__((aligned(16))) __bf16 sCh[2][SPLIT ? ROWS * LDB : 8];
@@ -457,6 +465,19 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             b3[b] = -INFINITY;
             i1[b] = 0;
             i2[b] = 0;
+        }
+        if constexpr (TAU) {
+            // a lower bound of the point's L-th best score: a row scoring at
+            // or below it cannot be among the L best, so the lists start
+            // full of it (index 0x7fffffff: no row)
+            if (A.knn_tau != nullptr) {
+#pragma unroll
+                for (int b = 0; b < PB; ++b) {
+                    const float t0 = pv[b] ? A.knn_tau[pt[b]] : -INFINITY;
+#pragma unroll
+                    for (int j = 0; j < TL; ++j) bl[b][j] = t0;
+                }
+            }
         }
         // This wave's points in registers.  Slot q (of HALF per point block
         // and lane) holds, for fp32 scoring, dim ch*DP + h*HALF + q; for split
@@ -975,7 +996,9 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     }
                 }
                 const int64_t p = sbase + b * 32 + jl;
-                if (h == 0 && p < A.N) {
+                if (TAU && A.knn_tau_out != nullptr) {
+                    if (h == 0 && p < A.N) A.knn_tau_out[p] = mv[TL - 1];
+                } else if (h == 0 && p < A.N) {
                     const size_t o = ((size_t)p * A.knn_slices + blockIdx.y) * TL;
 #pragma unroll
                     for (int j = 0; j < TL; j += 4) {
@@ -1419,6 +1442,8 @@ static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, co
     A.sw = sc.w;
     A.ip = ip ? 1 : 0;
     A.cs_bytes = (unsigned)(cdiv(K, kCentroidPad) * kCentroidPad * 4 * (int64_t)sc.w);
+    A.knn_tau = nullptr;
+    A.knn_tau_out = nullptr;
     return A;
 }
 
@@ -1538,7 +1563,7 @@ KnnSlices knn_slices(int64_t M, int64_t Ndb) {
 
 hipError_t launch_knn_sweep(const float *Q, int64_t M, int d, const float *DB, const float *ncn, int Ndb,
                             const float *scal, const double *qnorm64, const SplitC &sc, bool ip, int k,
-                            int32_t *cand, float *score, float *win, hipStream_t s) {
+                            int32_t *cand, float *score, float *win, float *tau, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     NearTies nt{};
     FlashArgs A = flash_args(Q, M, d, DB, ncn, Ndb, scal, qnorm64, nullptr, nullptr, nt, sc, ip);
@@ -1549,9 +1574,28 @@ hipError_t launch_knn_sweep(const float *Q, int64_t M, int d, const float *DB, c
     A.knn_score = score;
     A.knn_win = win;
     const bool split = sc.cs != nullptr;
-    if (knn_list_len(k) == 16)
-        return split ? launch_knn_shape<true, 16>(A, s) : launch_knn_shape<false, 16>(A, s);
-    return split ? launch_knn_shape<true, 32>(A, s) : launch_knn_shape<false, 32>(A, s);
+    auto sweep = [&](const FlashArgs &a) {
+        if (knn_list_len(k) == 16)
+            return split ? launch_knn_shape<true, 16>(a, s) : launch_knn_shape<false, 16>(a, s);
+        return split ? launch_knn_shape<true, 32>(a, s) : launch_knn_shape<false, 32>(a, s);
+    };
+    // Every slice starts its lists from scratch, and while they fill, most
+    // values are inserted (a pass of list updates each).  With several
+    // slices, a first sweep over the first kKnnSampleRows rows gives each
+    // query its L-th best score there, which is at or below its L-th best
+    // over all rows; the slices' lists start full of it.  Only for d <= 128:
+    // with streamed d-chunks the products outweigh the list updates and the
+    // extra sweep does not pay (measured at d = 768).
+    if (tau != nullptr && d <= 128 && ks.slices >= 4 && Ndb >= 4 * kKnnSampleRows) {
+        FlashArgs P = A;
+        P.knn_slices = 1;
+        P.knn_rows = kKnnSampleRows;
+        P.knn_tau_out = tau;
+        hipError_t e = sweep(P);
+        if (e != hipSuccess) return e;
+        A.knn_tau = tau;
+    }
+    return sweep(A);
 }
 
 // One thread per query: merge the slices' candidate lists into the L best

@@ -142,6 +142,7 @@ hipError_t launch_finalize(const double *sums, const int32_t *cnt, const float *
 constexpr int kMaxKnn = 24;
 constexpr int kKnnShort = 12;   // k <= 12: 16 candidates per query and slice, else 32
 constexpr int kKnnMaxSlices = 64;
+constexpr int kKnnSampleRows = 4096;  // rows of the threshold sweep (a multiple of kCentroidPad)
 int knn_list_len(int k);
 struct KnnSlices {
     int slices, rows;  // rows per slice: a multiple of kCentroidPad
@@ -149,7 +150,7 @@ struct KnnSlices {
 KnnSlices knn_slices(int64_t M, int64_t Ndb);
 hipError_t launch_knn_sweep(const float *Q, int64_t M, int d, const float *DB, const float *ncn, int Ndb,
                             const float *scal, const double *qnorm64, const SplitC &sc, bool ip, int k,
-                            int32_t *cand, float *score, float *win, hipStream_t s);
+                            int32_t *cand, float *score, float *win, float *tau, hipStream_t s);
 hipError_t launch_knn_finish(const float *Q, int64_t M, int d, const float *DB32, const double *DB64,
                              const double *qnorm64, bool ip, const int32_t *cand, const float *score,
                              const float *win, int k, int Ndb, int32_t *list, int32_t *counters, int32_t *idx,

@@ -131,3 +131,28 @@ def test_knn_ties_across_slices(gpu_lib, score):
     log(f"knn ties across slices score={score}")
     _check(gpu_lib, Q, DB, 7, "l2", score)
     _check(gpu_lib, Q, DB, 16, "inner_product", score)
+
+
+@pytest.mark.parametrize("score", SCORES)
+@pytest.mark.parametrize("kind", ["near_first", "far_first", "repeated"])
+def test_knn_sample_threshold(gpu_lib, score, kind):
+    """With several database slices, a first sweep over the first 4096 rows
+    gives each query a score at or below its L-th best, and the slices' lists
+    start full of it.  The first rows either hold the true neighbours (a
+    tight threshold), lie far away (a loose one), or the database repeats a
+    few rows (the threshold ties with many rows, and with the L-th best)."""
+    rng = np.random.default_rng({"near_first": 1, "far_first": 2, "repeated": 3}[kind])
+    d, Ndb, M = 48, 24001, 900
+    Q = rng.standard_normal((M, d)).astype(np.float32)
+    if kind == "repeated":
+        base = rng.standard_normal((11, d)).astype(np.float32)
+        DB = base[rng.integers(0, 11, size=Ndb)]
+    else:
+        DB = rng.standard_normal((Ndb, d)).astype(np.float32) * np.float32(3.0)
+        if kind == "near_first":
+            DB[:M] = Q + np.float32(0.01) * rng.standard_normal((M, d)).astype(np.float32)
+        else:
+            DB[:4096] += np.float32(50.0)
+    log(f"knn sample threshold {kind} score={score}")
+    for k in (5, 20):
+        _check(gpu_lib, Q, DB, k, "l2", score)
