@@ -1251,8 +1251,8 @@ __global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, in
 #pragma unroll
             for (int pi = 0; pi < RP; ++pi) acc[pi] = 0.0;
             const CT *crow = C + (size_t)k * d;
-            for (int jj = 0; jj < d; ++jj) {
-                const double c = (double)crow[jj];
+            auto step = [&](int jj, double c) {
+#pragma clang fp contract(off)
 #pragma unroll
                 for (int pi = 0; pi < RP; ++pi) {
                     if (pi < np) {
@@ -1264,7 +1264,20 @@ __global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, in
                         }
                     }
                 }
+            };
+            int jj = 0;
+            if ((d & 3) == 0) {
+                // the row in 16-byte (fp32) or 32-byte (fp64) loads: each
+                // lane reads its own row, so wide loads cut the number of
+                // scattered load instructions by four
+                for (; jj < d; jj += 4) {
+                    double c4[4];
+                    load4_64(crow + jj, c4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) step(jj + e, c4[e]);
+                }
             }
+            for (; jj < d; ++jj) step(jj, (double)crow[jj]);
 #pragma unroll
             for (int pi = 0; pi < RP; ++pi) {
                 if (acc[pi] < best[pi]) {
