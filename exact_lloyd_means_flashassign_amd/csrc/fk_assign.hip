@@ -811,7 +811,10 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
                     // phase 1: lo.hi + hi.lo, from zero; each step's LDS
-                    // operands are read one step ahead
+                    // operands are read one step ahead.  The wave issuing
+                    // products takes priority over the other wave of its SIMD
+                    // (which may be in its epilogue) until its block is done.
+                    __builtin_amdgcn_s_setprio(1);
                     v8bf ah = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB);
                     v8bf al = *reinterpret_cast<const v8bf *>(sl + cb * 32 * LDB);
 #pragma unroll
@@ -857,6 +860,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                             acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah3, xh[b][st], acc[b][0], 0, 0, 0);
                         ah3 = ahn;
                     }
+                    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
                     for (int b = 0; b < PB; ++b) epilogue(acc[b][0], b, t * ROWS + cb * 32 + 4 * h);
                     // the next stage goes to the other LDS buffer (which no
@@ -897,6 +901,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 }
             } else {
                 const float *sc = &sC[buf][jl * LDR + h * HALF];
+                __builtin_amdgcn_s_setprio(1);  // as above: products first
 #pragma unroll
                 for (int s = 0; s < HALF; s += 4) {
                     float4 av[CB];
@@ -913,6 +918,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                         }
                     }
                 }
+                __builtin_amdgcn_s_setprio(0);
             }
 
             if constexpr (!PHASED) {
