@@ -1192,26 +1192,71 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
 }
 
 // fp64 check of a near-tie point whose winner is one of two known centroids:
-// the smaller direct-difference distance wins, the lower index on a tie.  One
-// thread per listed point.
+// the smaller direct-difference distance wins, the lower index on a tie.
+// A wave takes 64 listed points (one per lane) at a time and stages their
+// rows and both centroid rows through LDS, J dims at a time, with coalesced
+// loads (consecutive lanes read consecutive dims of a row; a lane reading
+// its own row from memory would touch 64 rows per load instruction); each
+// lane then runs the definition's sums over its own rows, in increasing j.
 template <typename CT>
 __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ X, int d, const CT *__restrict__ C,
                                                       const double *__restrict__ xnorm64,
                                                       const int32_t *__restrict__ pair_list,
                                                       const int32_t *__restrict__ counters,
                                                       int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+#pragma clang fp contract(off)
+    constexpr int J = sizeof(CT) == 4 ? 16 : 8;  // dims per stage
+    constexpr int JP = J + 1;                    // padded LDS row
+    __shared__ float sx[4][64 * JP];
+    __shared__ CT sc[4][2][64 * JP];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cnt = counters[1];
-    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
-        const int64_t p = pair_list[3 * (int64_t)q];
-        const int k1 = pair_list[3 * (int64_t)q + 1];
-        const int k2 = pair_list[3 * (int64_t)q + 2];
-        const CT *const rows[2] = {C + (size_t)k1 * d, C + (size_t)k2 * d};
-        double D[2];
-        sqdist64<CT, 2>(X + (size_t)p * d, rows, d, xnorm64 != nullptr ? xnorm64[p] : 1.0, xnorm64 != nullptr,
-                        ip != 0, D);
-        const bool second = (D[1] < D[0]) || (D[1] == D[0] && k2 < k1);
-        a_out[p] = second ? k2 : k1;
-        if (d1_out != nullptr) d1_out[p] = (float)(second ? D[1] : D[0]);
+    for (int64_t q0 = ((int64_t)blockIdx.x * 4 + w) * 64; q0 < cnt; q0 += (int64_t)gridDim.x * 4 * 64) {
+        const int64_t q = q0 + lane;
+        const bool ok = q < cnt;
+        const int64_t p = ok ? pair_list[3 * q] : 0;
+        const int k1 = ok ? pair_list[3 * q + 1] : 0;
+        const int k2 = ok ? pair_list[3 * q + 2] : 0;
+        const double nx = (xnorm64 != nullptr) ? xnorm64[p] : 1.0;
+        double D1 = 0.0, D2 = 0.0;
+        for (int j0 = 0; j0 < d; j0 += J) {
+            const int nj = min(J, d - j0);
+            // element e of the stage: row e / J, dim e % J (rows of lanes
+            // that hold no pair are those of row 0: read, never used)
+#pragma unroll
+            for (int i = 0; i < J; ++i) {
+                const int e = lane + 64 * i, r = e / J, c = e % J;
+                const int64_t pr = __shfl(p, r);
+                const int kr1 = __shfl(k1, r), kr2 = __shfl(k2, r);
+                if (c < nj) {
+                    sx[w][r * JP + c] = X[(size_t)pr * d + j0 + c];
+                    sc[w][0][r * JP + c] = C[(size_t)kr1 * d + j0 + c];
+                    sc[w][1][r * JP + c] = C[(size_t)kr2 * d + j0 + c];
+                }
+            }
+            __builtin_amdgcn_wave_barrier();
+            for (int c = 0; c < nj; ++c) {
+                double xv = (double)sx[w][lane * JP + c];
+                if (xnorm64 != nullptr) xv = xv / nx;
+                const double c1 = (double)sc[w][0][lane * JP + c];
+                const double c2 = (double)sc[w][1][lane * JP + c];
+                if (ip) {
+                    D1 = D1 - xv * c1;
+                    D2 = D2 - xv * c2;
+                } else {
+                    const double t1 = xv - c1, t2 = xv - c2;
+                    D1 = D1 + t1 * t1;
+                    D2 = D2 + t2 * t2;
+                }
+            }
+            // every lane has read this stage before the next one overwrites it
+            __builtin_amdgcn_wave_barrier();
+        }
+        if (ok) {
+            const bool second = (D2 < D1) || (D2 == D1 && k2 < k1);
+            a_out[p] = second ? k2 : k1;
+            if (d1_out != nullptr) d1_out[p] = (float)(second ? D2 : D1);
+        }
     }
 }
 
