@@ -1154,7 +1154,10 @@ __device__ __forceinline__ void sqdist64(const float *__restrict__ x, const CT *
 // collected: the lowest-index minimum of the direct-difference fp64 distance
 // over its candidates (both half-lane lists).  A point whose lists overflowed,
 // or that lies beyond the collected slots, goes to the overflow list for a
-// rescoring against all K.  One thread per listed point.
+// rescoring against all K.  A wave takes 64 listed points (one per lane) at a
+// time; for each candidate rank m it stages the points' rows and their m-th
+// candidate rows through LDS as k_recheck_pair does, and each lane sums its
+// own rows in increasing j.
 template <typename CT>
 __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ X, int d, const CT *__restrict__ C,
                                                       const double *__restrict__ xnorm64,
@@ -1164,30 +1167,68 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
                                                       int32_t *__restrict__ ovf_list, int32_t *__restrict__ counters,
                                                       int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
 #pragma clang fp contract(off)
+    constexpr int J = sizeof(CT) == 4 ? 16 : 8;  // dims per stage
+    constexpr int JP = J + 1;                    // padded LDS row
+    __shared__ float sx[4][64 * JP];
+    __shared__ CT sc[4][64 * JP];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cnt = counters[0];
-    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
-        const int64_t p = full_list[q];
-        const int c0 = q < cap_slots ? ccount[2 * (int64_t)q] : kMaxCand + 1;
-        const int c1 = q < cap_slots ? ccount[2 * (int64_t)q + 1] : kMaxCand + 1;
-        if (c0 > kMaxCand || c1 > kMaxCand) {
+    for (int64_t q0 = ((int64_t)blockIdx.x * 4 + w) * 64; q0 < cnt; q0 += (int64_t)gridDim.x * 4 * 64) {
+        const int64_t q = q0 + lane;
+        bool ok = q < cnt;
+        const int64_t p = ok ? full_list[q] : 0;
+        const int c0 = !ok ? 0 : q < cap_slots ? ccount[2 * q] : kMaxCand + 1;
+        const int c1 = !ok ? 0 : q < cap_slots ? ccount[2 * q + 1] : kMaxCand + 1;
+        if (ok && (c0 > kMaxCand || c1 > kMaxCand)) {
             ovf_list[atomicAdd(&counters[2], 1)] = (int32_t)p;
-            continue;
+            ok = false;
         }
-        const double nx = xnorm64 != nullptr ? xnorm64[p] : 1.0;
+        const int nc = ok ? c0 + c1 : 0;
+        int ncw = nc;  // the wave's largest candidate count
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) ncw = max(ncw, __shfl_xor(ncw, off));
+        const double nx = (xnorm64 != nullptr) ? xnorm64[p] : 1.0;
         double best = INFINITY;
         int bk = 0x7fffffff;
-        for (int m = 0; m < c0 + c1; ++m) {
-            const int k = m < c0 ? cand[2 * (int64_t)q * kMaxCand + m] : cand[(2 * (int64_t)q + 1) * kMaxCand + m - c0];
-            const CT *const row[1] = {C + (size_t)k * d};
-            double D[1];
-            sqdist64<CT, 1>(X + (size_t)p * d, row, d, nx, xnorm64 != nullptr, ip != 0, D);
-            if (D[0] < best || (D[0] == best && k < bk)) {
-                best = D[0];
+        for (int m = 0; m < ncw; ++m) {
+            const bool has = m < nc;
+            const int k = !has ? 0 : m < c0 ? cand[2 * q * kMaxCand + m] : cand[(2 * q + 1) * kMaxCand + m - c0];
+            double D = 0.0;
+            for (int j0 = 0; j0 < d; j0 += J) {
+                const int nj = min(J, d - j0);
+#pragma unroll
+                for (int i = 0; i < J; ++i) {
+                    const int e = lane + 64 * i, r = e / J, c = e % J;
+                    const int64_t pr = __shfl(p, r);
+                    const int kr = __shfl(k, r);
+                    if (c < nj) {
+                        sx[w][r * JP + c] = X[(size_t)pr * d + j0 + c];
+                        sc[w][r * JP + c] = C[(size_t)kr * d + j0 + c];
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+                for (int c = 0; c < nj; ++c) {
+                    double xv = (double)sx[w][lane * JP + c];
+                    if (xnorm64 != nullptr) xv = xv / nx;
+                    const double cv = (double)sc[w][lane * JP + c];
+                    if (ip) {
+                        D = D - xv * cv;
+                    } else {
+                        const double t = xv - cv;
+                        D = D + t * t;
+                    }
+                }
+                __builtin_amdgcn_wave_barrier();
+            }
+            if (has && (D < best || (D == best && k < bk))) {
+                best = D;
                 bk = k;
             }
         }
-        a_out[p] = bk;
-        if (d1_out != nullptr) d1_out[p] = (float)best;
+        if (ok) {
+            a_out[p] = bk;
+            if (d1_out != nullptr) d1_out[p] = (float)best;
+        }
     }
 }
 
