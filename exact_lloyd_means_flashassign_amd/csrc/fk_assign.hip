@@ -6,19 +6,25 @@
 // them to an argmin at once, so the N x K distance matrix is never written and
 // the IO is O(Nd + Kd).  This file does that on CDNA4:
 //   * the score s_ik = ||c_k||^2 - 2 x_i.c_k is a dense contraction, so it runs
-//     on v_mfma_f32_32x32x2_f32; the accumulator starts at -||c_k||^2 / 2, so
-//     the MFMA result is  x.c - ||c||^2/2 = (||x||^2 - D_ik) / 2  and the
-//     nearest centroid is the largest accumulator;
-//   * each wave keeps its points in VGPRs; centroid tiles are staged through
-//     LDS (double-buffered) and shared by the 4 waves of a workgroup;
+//     on the matrix cores: v_mfma_f32_32x32x2_f32 on the fp32 operands, or
+//     (split scoring) v_mfma_f32_32x32x16_bf16 on bf16 high and low parts of
+//     both operands, three products per fp32 product; the accumulator holds
+//     x.c - ||c||^2/2 = (||x||^2 - D_ik) / 2, so the nearest centroid is the
+//     largest accumulator;
+//   * each wave keeps its points in VGPRs (for d > 128 they are streamed in
+//     64-dim chunks, fetched a stage or two ahead); centroid tiles are staged
+//     through LDS (double-buffered) and shared by the waves of a workgroup;
 //   * the MFMA output puts one point per lane and 16 centroids per lane, so
 //     the running top-3 is kept per lane with no cross-lane traffic; lanes l
 //     and l^32 are merged once, after the last tile;
-//   * exactness: the fp32 accumulator has a proven error bound e_i.  A point
-//     whose top-2 gap is within 2 e_i is a near tie.  If its third score is
-//     more than 2 e_i below the best, only the top two can win and
-//     k_recheck_pair compares those two in fp64 by direct difference (the
-//     distance definition); otherwise k_recheck rescores it against all K.
+//   * exactness: the accumulator has a proven error bound e_i.  A point whose
+//     top-2 gap is within 2 e_i is a near tie.  If its third score is more
+//     than 2 e_i below the best, only the top two can win and k_recheck_pair
+//     compares those two in fp64 by direct difference (the distance
+//     definition); otherwise a second sweep (collect mode) gathers every
+//     centroid within the window and k_recheck_cand compares those in fp64,
+//     and a point with more than it can hold goes to k_recheck, which
+//     rescores it against all K.
 #include "fk_internal.h"
 
 namespace fk {
@@ -1492,9 +1498,10 @@ static hipError_t launch_fa_shape(const FlashArgs &A, hipStream_t s) {
     const AssignShape sh = assign_shape(A.d);
     if (sh.nch > 1) {
         // streamed points are re-read for every centroid tile: 128-row tiles
-        // halve that traffic (the d = 768 shape is bound by it at 64 rows).
-        // Split scoring at that height needs more than 256 registers: one
-        // wave per SIMD, accumulators in AGPRs, rather than spilling.
+        // halve that traffic and the stage overheads per product (at
+        // d = 768, K = 4096 they were 20 % faster than 64-row tiles).  Split
+        // scoring at that height needs more than 256 registers: one wave per
+        // SIMD, accumulators in AGPRs, rather than spilling.
         if constexpr (SPLIT)
             return launch_fa<64, 1, 4, 4, 1, false, COLLECT, SPLIT>(A, s);
         else
