@@ -134,8 +134,9 @@ def test_knn_ties_across_slices(gpu_lib, score):
 
 
 @pytest.mark.parametrize("score", SCORES)
+@pytest.mark.parametrize("metric", ["l2", "cosine", "inner_product"])
 @pytest.mark.parametrize("kind", ["near_first", "far_first", "repeated"])
-def test_knn_sample_threshold(gpu_lib, score, kind):
+def test_knn_sample_threshold(gpu_lib, score, kind, metric):
     """With several database slices, a first sweep over the first 4096 rows
     gives each query a score at or below its L-th best, and the slices' lists
     start full of it.  The first rows either hold the true neighbours (a
@@ -153,6 +154,6 @@ def test_knn_sample_threshold(gpu_lib, score, kind):
             DB[:M] = Q + np.float32(0.01) * rng.standard_normal((M, d)).astype(np.float32)
         else:
             DB[:4096] += np.float32(50.0)
-    log(f"knn sample threshold {kind} score={score}")
+    log(f"knn sample threshold {kind} {metric} score={score}")
     for k in (5, 20):
-        _check(gpu_lib, Q, DB, k, "l2", score)
+        _check(gpu_lib, Q, DB, k, metric, score)
