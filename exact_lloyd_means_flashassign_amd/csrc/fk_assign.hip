@@ -1156,6 +1156,72 @@ __device__ __forceinline__ void sqdist64(const float *__restrict__ x, const CT *
     }
 }
 
+// The near-tie checks below stage rows through LDS when there are many
+// listed points with short rows; with few listed points, or d > 128, a wave
+// would run through its d / J dependent stages (and, in the window check,
+// once per candidate) with too few waves in flight to hide them, and one
+// lane per point reading its own rows is faster (measured: 1M x 128, K =
+// 1024 with 3,000 listed pairs and 1M x 768 with 360).  These are those
+// per-lane versions.
+constexpr int kStagedMinList = 65536;  // listed points for the staged checks
+
+template <typename CT>
+__device__ __forceinline__ void recheck_cand_rows(const float *__restrict__ X, int d, const CT *__restrict__ C,
+                                                  const double *__restrict__ xnorm64,
+                                                  const int32_t *__restrict__ full_list,
+                                                  const int32_t *__restrict__ cand,
+                                                  const int32_t *__restrict__ ccount, int64_t cap_slots,
+                                                  int32_t *__restrict__ ovf_list, int32_t *__restrict__ counters,
+                                                  int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+#pragma clang fp contract(off)
+    const int cnt = counters[0];
+    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
+        const int64_t p = full_list[q];
+        const int c0 = q < cap_slots ? ccount[2 * (int64_t)q] : kMaxCand + 1;
+        const int c1 = q < cap_slots ? ccount[2 * (int64_t)q + 1] : kMaxCand + 1;
+        if (c0 > kMaxCand || c1 > kMaxCand) {
+            ovf_list[atomicAdd(&counters[2], 1)] = (int32_t)p;
+            continue;
+        }
+        const double nx = xnorm64 != nullptr ? xnorm64[p] : 1.0;
+        double best = INFINITY;
+        int bk = 0x7fffffff;
+        for (int m = 0; m < c0 + c1; ++m) {
+            const int k = m < c0 ? cand[2 * (int64_t)q * kMaxCand + m] : cand[(2 * (int64_t)q + 1) * kMaxCand + m - c0];
+            const CT *const row[1] = {C + (size_t)k * d};
+            double D[1];
+            sqdist64<CT, 1>(X + (size_t)p * d, row, d, nx, xnorm64 != nullptr, ip != 0, D);
+            if (D[0] < best || (D[0] == best && k < bk)) {
+                best = D[0];
+                bk = k;
+            }
+        }
+        a_out[p] = bk;
+        if (d1_out != nullptr) d1_out[p] = (float)best;
+    }
+}
+
+template <typename CT>
+__device__ __forceinline__ void recheck_pair_rows(const float *__restrict__ X, int d, const CT *__restrict__ C,
+                                                  const double *__restrict__ xnorm64,
+                                                  const int32_t *__restrict__ pair_list,
+                                                  const int32_t *__restrict__ counters,
+                                                  int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+    const int cnt = counters[1];
+    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
+        const int64_t p = pair_list[3 * (int64_t)q];
+        const int k1 = pair_list[3 * (int64_t)q + 1];
+        const int k2 = pair_list[3 * (int64_t)q + 2];
+        const CT *const rows[2] = {C + (size_t)k1 * d, C + (size_t)k2 * d};
+        double D[2];
+        sqdist64<CT, 2>(X + (size_t)p * d, rows, d, xnorm64 != nullptr ? xnorm64[p] : 1.0, xnorm64 != nullptr,
+                        ip != 0, D);
+        const bool second = (D[1] < D[0]) || (D[1] == D[0] && k2 < k1);
+        a_out[p] = second ? k2 : k1;
+        if (d1_out != nullptr) d1_out[p] = (float)(second ? D[1] : D[0]);
+    }
+}
+
 // fp64 check of a near-tie point from the full list whose candidates were
 // collected: the lowest-index minimum of the direct-difference fp64 distance
 // over its candidates (both half-lane lists).  A point whose lists overflowed,
@@ -1179,6 +1245,11 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
     __shared__ CT sc[4][64 * JP];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cnt = counters[0];
+    if (d > 128 || cnt < kStagedMinList) {
+        recheck_cand_rows<CT>(X, d, C, xnorm64, full_list, cand, ccount, cap_slots, ovf_list, counters, a_out, d1_out,
+                              ip);
+        return;
+    }
     for (int64_t q0 = ((int64_t)blockIdx.x * 4 + w) * 64; q0 < cnt; q0 += (int64_t)gridDim.x * 4 * 64) {
         const int64_t q = q0 + lane;
         bool ok = q < cnt;
@@ -1258,6 +1329,10 @@ __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ 
     __shared__ CT sc[4][2][64 * JP];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cnt = counters[1];
+    if (d > 128 || cnt < kStagedMinList) {
+        recheck_pair_rows<CT>(X, d, C, xnorm64, pair_list, counters, a_out, d1_out, ip);
+        return;
+    }
     for (int64_t q0 = ((int64_t)blockIdx.x * 4 + w) * 64; q0 < cnt; q0 += (int64_t)gridDim.x * 4 * 64) {
         const int64_t q = q0 + lane;
         const bool ok = q < cnt;
@@ -1304,69 +1379,6 @@ __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ 
             a_out[p] = second ? k2 : k1;
             if (d1_out != nullptr) d1_out[p] = (float)(second ? D2 : D1);
         }
-    }
-}
-
-// The same window check (and overflow listing) with one thread per listed
-// point reading its rows itself, for d > 128: there the staged version's
-// wave runs through d / J stages one after another, which costs more than
-// the scattered loads when few points are listed (measured at d = 768).
-template <typename CT>
-__global__ __launch_bounds__(256) void k_recheck_cand_rows(const float *__restrict__ X, int d, const CT *__restrict__ C,
-                                                      const double *__restrict__ xnorm64,
-                                                      const int32_t *__restrict__ full_list,
-                                                      const int32_t *__restrict__ cand,
-                                                      const int32_t *__restrict__ ccount, int64_t cap_slots,
-                                                      int32_t *__restrict__ ovf_list, int32_t *__restrict__ counters,
-                                                      int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
-#pragma clang fp contract(off)
-    const int cnt = counters[0];
-    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
-        const int64_t p = full_list[q];
-        const int c0 = q < cap_slots ? ccount[2 * (int64_t)q] : kMaxCand + 1;
-        const int c1 = q < cap_slots ? ccount[2 * (int64_t)q + 1] : kMaxCand + 1;
-        if (c0 > kMaxCand || c1 > kMaxCand) {
-            ovf_list[atomicAdd(&counters[2], 1)] = (int32_t)p;
-            continue;
-        }
-        const double nx = xnorm64 != nullptr ? xnorm64[p] : 1.0;
-        double best = INFINITY;
-        int bk = 0x7fffffff;
-        for (int m = 0; m < c0 + c1; ++m) {
-            const int k = m < c0 ? cand[2 * (int64_t)q * kMaxCand + m] : cand[(2 * (int64_t)q + 1) * kMaxCand + m - c0];
-            const CT *const row[1] = {C + (size_t)k * d};
-            double D[1];
-            sqdist64<CT, 1>(X + (size_t)p * d, row, d, nx, xnorm64 != nullptr, ip != 0, D);
-            if (D[0] < best || (D[0] == best && k < bk)) {
-                best = D[0];
-                bk = k;
-            }
-        }
-        a_out[p] = bk;
-        if (d1_out != nullptr) d1_out[p] = (float)best;
-    }
-}
-
-// The same pair check with one thread per listed point reading its rows
-// itself (wider rows; see k_recheck_cand_rows).
-template <typename CT>
-__global__ __launch_bounds__(256) void k_recheck_pair_rows(const float *__restrict__ X, int d, const CT *__restrict__ C,
-                                                      const double *__restrict__ xnorm64,
-                                                      const int32_t *__restrict__ pair_list,
-                                                      const int32_t *__restrict__ counters,
-                                                      int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
-    const int cnt = counters[1];
-    for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
-        const int64_t p = pair_list[3 * (int64_t)q];
-        const int k1 = pair_list[3 * (int64_t)q + 1];
-        const int k2 = pair_list[3 * (int64_t)q + 2];
-        const CT *const rows[2] = {C + (size_t)k1 * d, C + (size_t)k2 * d};
-        double D[2];
-        sqdist64<CT, 2>(X + (size_t)p * d, rows, d, xnorm64 != nullptr ? xnorm64[p] : 1.0, xnorm64 != nullptr,
-                        ip != 0, D);
-        const bool second = (D[1] < D[0]) || (D[1] == D[0] && k2 < k1);
-        a_out[p] = second ? k2 : k1;
-        if (d1_out != nullptr) d1_out[p] = (float)(second ? D[1] : D[0]);
     }
 }
 
@@ -1643,8 +1655,6 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
                           hipStream_t s) {
     if (N <= 0) return hipSuccess;
     hipError_t e;
-    // rows staged through LDS up to d = 128, read by each lane beyond
-    const bool staged = d <= 128;
     // 1. near ties between two known centroids
     {
         int64_t nb = cdiv(N, 256);
@@ -1652,13 +1662,10 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
 #define FK_PAIR(KERNEL, CT, CP)                                                                                    \
     hipLaunchKernelGGL(KERNEL<CT>, dim3((unsigned)nb), dim3(256), 0, s, X, d, CP, xnorm64, nt.pair_list, nt.counters, \
                        a_out, d1_out, ip ? 1 : 0)
-        if (C64 != nullptr) {
-            if (staged) FK_PAIR(k_recheck_pair, double, C64);
-            else FK_PAIR(k_recheck_pair_rows, double, C64);
-        } else {
-            if (staged) FK_PAIR(k_recheck_pair, float, C32);
-            else FK_PAIR(k_recheck_pair_rows, float, C32);
-        }
+        if (C64 != nullptr)
+            FK_PAIR(k_recheck_pair, double, C64);
+        else
+            FK_PAIR(k_recheck_pair, float, C32);
 #undef FK_PAIR
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1674,13 +1681,10 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
 #define FK_CAND(KERNEL, CT, CP)                                                                                   \
     hipLaunchKernelGGL(KERNEL<CT>, dim3((unsigned)nb), dim3(256), 0, s, X, d, CP, xnorm64, nt.full_list, nt.cand,  \
                        nt.ccount, cap, nt.ovf_list, nt.counters, a_out, d1_out, ip ? 1 : 0)
-        if (C64 != nullptr) {
-            if (staged) FK_CAND(k_recheck_cand, double, C64);
-            else FK_CAND(k_recheck_cand_rows, double, C64);
-        } else {
-            if (staged) FK_CAND(k_recheck_cand, float, C32);
-            else FK_CAND(k_recheck_cand_rows, float, C32);
-        }
+        if (C64 != nullptr)
+            FK_CAND(k_recheck_cand, double, C64);
+        else
+            FK_CAND(k_recheck_cand, float, C32);
 #undef FK_CAND
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
