@@ -221,7 +221,8 @@ def adversarial(seed: int, N: int, d: int, K: int, kind: str = "gauss"):
     """Small seeded inputs for edge cases: returns (X, C) float32.
 
     kinds: "gauss" (random), "dup" (C has duplicated rows, so exact ties),
-    "dup3" (every centroid has two copies, so three-way ties), "dup40" (40
+    "pairs" (C[1::2] copies C[0::2], so nearly every point has an exact
+    two-way tie), "dup3" (every centroid has two copies, so three-way ties), "dup40" (40
     copies of one row, so ties wider than any fixed candidate list),
     "grid" (small integers: many exact ties), "far" (large offset, so the
     expanded distance form cancels badly), "zero" (some zero rows in X and C).
@@ -237,6 +238,8 @@ def adversarial(seed: int, N: int, d: int, K: int, kind: str = "gauss"):
         src = rng.integers(0, K, size=K // 2)
         dst = rng.integers(0, K, size=K // 2)
         C[dst] = C[src]
+    if kind == "pairs" and K >= 2:
+        C[1::2] = C[0::2][: len(C[1::2])]
     if kind == "dup3" and K >= 3:
         C[1::3] = C[0::3][: len(C[1::3])]
         C[2::3] = C[0::3][: len(C[2::3])]

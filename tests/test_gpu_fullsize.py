@@ -1,14 +1,27 @@
 """Parity at the workloads' full sizes, in the launch configuration bench.py
 times (fk_lloyd_iter through the C ABI, X and C resident in HBM).
 
-The oracle cannot score every point against every centroid at these sizes, so
-the assignment is checked exactly on a seeded sample of points (the oracle
-scores each sampled point against all K); the update is checked in full by
-running the oracle's update on the GPU's own assignment (O(Nd)); counts are
-checked in full against bincount of the GPU assignment and against the
-oracle's update.  The out-of-core shape runs at a scaled N (its 10^9 rows need
-512 GB of pinned host memory, more than a GPU-box command may hold) with the
-configured 2^26-row chunks and a ragged last chunk."""
+Every label of every point is compared with the oracle's.  The oracle's own
+Lloyd trajectory on each workload, from the workload's initial centroids, is
+stored as digests in tests/golden/fullsize_<workload>.json (written by
+tests/golden/make_fullsize_digests.py, which calls only the oracle and the
+seeded generator): per iteration, a hash of the labels of every 65,536-row
+block, a hash of the counts, the objective per block and a hash of the next
+centroids.  The test walks the same trajectory: at iteration t the GPU
+iterates from the oracle's C_t; its labels must hash to the oracle's in every
+block and its counts to the oracle's counts; with the labels equal, the
+oracle's update of them (O(Nd), run here) is the oracle's C_{t+1}, whose hash
+must match the stored one, and the GPU's new centroids must be within 1e-6
+relative of it.  The objective sum of the GPU's min_dist must match the
+oracle's per block within the summed per-point bound.  A block that differs
+is rescored by the oracle in full to report the mismatches.
+
+The out-of-core shape runs at a scaled N (its 10^9 rows need 512 GB of pinned
+host memory, more than a GPU-box command may hold) with the configured
+2^26-row chunks and a ragged last chunk, sampled."""
+import hashlib
+import json
+import os
 import time
 
 import numpy as np
@@ -17,9 +30,11 @@ import torch
 
 import oracle
 import synth
-from gpu_helpers import centroid_rel_err, check_min_dist, dev, host, log
+from gpu_helpers import centroid_rel_err, dev, host, log, min_dist_tol
 
-pytestmark = [pytest.mark.gpu, pytest.mark.timeout(600)]
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def _sample(N, n, seed):
@@ -27,40 +42,72 @@ def _sample(N, n, seed):
     return np.sort(rng.choice(N, size=min(n, N), replace=False))
 
 
+def _digest(a):
+    return hashlib.blake2b(np.ascontiguousarray(a).tobytes(), digest_size=16).hexdigest()
+
+
+def _trajectory(name):
+    path = os.path.join(GOLDEN, f"fullsize_{name}.json")
+    with open(path) as f:
+        return json.load(f)
+
+
 @pytest.mark.parametrize("score", ["fp32", "split_bf16"])
-@pytest.mark.parametrize("name,nsample", [("gmm_1m_d128_k1024", 4096), ("ivf_1m_d768_k4096", 1024),
-                                          ("zipf_16m_d128_k32768", 2048)])
-def test_full_size_iteration(gpu_lib, name, nsample, score):
+@pytest.mark.parametrize("name", ["tiny_d16_k64", "gmm_1m_d128_k1024", "ivf_1m_d768_k4096", "zipf_16m_d128_k32768"])
+def test_full_size_oracle_trajectory(gpu_lib, name, score):
     fk = gpu_lib
+    doc = _trajectory(name)
     w = synth.WORKLOADS[name]
-    log(f"full size {name}: generating N={w.N}")
+    assert (doc["N"], doc["d"], doc["K"]) == (w.N, w.d, w.K)
+    B = doc["block_rows"]
+    log(f"full size {name} ({score}): generating N={w.N}, {len(doc['iterations'])} stored oracle iterations")
     X = synth.rows(w)
     C = synth.initial_centroids(w, X)
-    Xd, Cd = dev(X), dev(C)
-    # one warm-up iteration moves the centroids off the sampled points, as in
-    # the timed steps of the benchmark
-    _, C1d, _, _ = fk.fk_lloyd_iter(Xd, Cd, score=score)
-    C1 = host(C1d).copy()
-    log(f"full size {name}: second iteration")
-    a, C2d, counts, md = fk.fk_lloyd_iter(Xd, C1d, with_min_dist=True, score=score)
-    a = host(a)
-    counts = host(counts)
-    C2 = host(C2d)
-    md = host(md)
-    assert counts.sum() == w.N
-    np.testing.assert_array_equal(counts, np.bincount(a, minlength=w.K))
-    idx = _sample(w.N, nsample, w.seed)
-    log(f"full size {name}: oracle on {len(idx)} sampled points")
-    a_ref, D1, D2 = oracle.assign(X[idx], C1)
-    np.testing.assert_array_equal(a[idx], a_ref)
-    check_min_dist(md[idx], D1, X[idx], C1, score=score)
-    log(f"full size {name}: oracle update on the GPU assignment")
-    C_ref, n_ref = oracle.update(X, a, C1)
-    np.testing.assert_array_equal(counts, n_ref)
-    err = centroid_rel_err(C2, C_ref, n_ref)
-    assert err <= 1e-6, err
-    empty = n_ref == 0
-    assert np.array_equal(C2[empty].view(np.uint32), C1[empty].view(np.uint32))
+    assert _digest(C) == doc["initial_centroids_hash"], "the seeded inputs differ from those the oracle ran on"
+    Xd = dev(X)
+    worst_err = 0.0
+    for it in doc["iterations"]:
+        t = it["t"]
+        assert _digest(C) == it["centroids_hash"]
+        t0 = time.perf_counter()
+        a_d, C1d, counts_d, md_d = fk.fk_lloyd_iter(Xd, dev(C), with_min_dist=True, score=score)
+        a, C1, counts, md = host(a_d), host(C1d), host(counts_d), host(md_d)
+        gpu_s = time.perf_counter() - t0
+        blocks = [_digest(a[b:b + B].astype("<i4")) for b in range(0, w.N, B)]
+        bad = [i for i, (u, v) in enumerate(zip(blocks, it["label_blocks"])) if u != v]
+        if bad:
+            lines = []
+            for i in bad[:4]:
+                lo, hi = i * B, min(w.N, (i + 1) * B)
+                a_ref, D1, D2 = oracle.assign(X[lo:hi], C)
+                miss = np.nonzero(a[lo:hi] != a_ref)[0]
+                g = oracle.relative_gap(D1[miss], D2[miss])
+                lines.append(f"block {i}: {len(miss)} labels differ, rows {lo + miss[:5]}, gaps {g[:5]}")
+            pytest.fail(f"{name} iteration {t}: {len(bad)} of {len(blocks)} label blocks differ from the "
+                        f"oracle's; " + "; ".join(lines))
+        assert _digest(counts.astype("<i4")) == it["counts_hash"], f"iteration {t}: counts differ from the oracle's"
+        if it["counts"] is not None:
+            np.testing.assert_array_equal(counts, it["counts"])
+        # the labels equal the oracle's, so its update of them is the oracle's own C_{t+1}
+        C_ref, n_ref = oracle.update(X, a, C, w.metric)
+        np.testing.assert_array_equal(counts, n_ref)
+        C_next = C_ref.astype(np.float32)
+        assert _digest(C_next) == it["next_centroids_hash"]
+        err = centroid_rel_err(C1, C_ref, n_ref)
+        assert err <= 1e-6, f"iteration {t}: centroid rel err {err}"
+        empty = n_ref == 0
+        assert np.array_equal(C1[empty].view(np.uint32), C[empty].view(np.uint32))
+        worst_err = max(worst_err, err)
+        # objective: the GPU's fp32 min_dist summed per block against the oracle's D1 sums
+        J_gpu = 0.0
+        for i, Jb in enumerate(it["J_blocks"]):
+            lo, hi = i * B, min(w.N, (i + 1) * B)
+            s = float(md[lo:hi].astype(np.float64).sum())
+            tol = float(min_dist_tol(X[lo:hi], C, w.metric, score).sum())
+            assert abs(s - Jb) <= tol, f"iteration {t} block {i}: objective {s} vs oracle {Jb} (tol {tol})"
+            J_gpu += s
+        log(f"VALIDATION {json.dumps({'workload': name, 'score': score, 'iteration': t, 'N': w.N, 'label_mismatches': 0, 'blocks': len(blocks), 'counts_equal': True, 'exempt_g_le_1e-5': it['gap']['le_1e-05'], 'g_le_1e-7': it['gap']['le_1e-07'], 'exact_ties': it['gap']['eq_0'], 'empty': it['empty'], 'max_centroid_rel_err': err, 'J_oracle': it['J'], 'J_gpu_fp32_min_dist': J_gpu, 'gpu_iter_s_incl_copies': round(gpu_s, 3)})}")
+        C = C_next
 
 
 @pytest.mark.parametrize("score", ["fp32", "split_bf16"])

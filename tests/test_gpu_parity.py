@@ -83,6 +83,56 @@ def test_each_near_tie_path_is_taken(gpu_lib, kind, path, score):
     assert prof[path] > 0, prof
 
 
+NEAR_TIE_CAP_MIN = 65536  # the window pass collects candidates for max(N/8, 65,536) listed points
+
+
+@pytest.mark.parametrize("score", SCORES)
+@pytest.mark.parametrize("metric", ["l2", "cosine", "inner_product"])
+@pytest.mark.parametrize("d", [32, 128])
+@pytest.mark.parametrize("kind", ["pairs", "dup3"])
+def test_near_tie_paths_at_scale(gpu_lib, kind, d, metric, score):
+    """200,000 points against 24 centroids that come in exact copies: with
+    pairs nearly every point is an exact two-way tie, with three copies a
+    three-way tie, so the pair list or the window list holds far more than
+    65,536 points.  That takes the LDS-staged fp64 checks (d <= 128), and the
+    window points past the candidate slots (max(N/8, 65,536) of them) go to
+    the all-K rescoring.  Every label must equal the oracle's."""
+    fk = gpu_lib
+    N, K = 200000, 24
+    log(f"near ties at scale: {kind} N={N} d={d} K={K} {metric} {score}")
+    X, C = synth.adversarial(11, N, d, K, kind)
+    a_ref, D1, _ = oracle.assign(X, C, metric)
+    fk.fk_profile_enable(True)
+    a, md = fk.fk_assign(dev(X), dev(C), metric=metric, with_min_dist=True, score=score)
+    prof = fk.fk_profile_read()
+    fk.fk_profile_enable(False)
+    np.testing.assert_array_equal(host(a), a_ref)
+    check_min_dist(host(md), D1, X, C, metric, score=score)
+    cap = max(N // 8, NEAR_TIE_CAP_MIN)
+    if kind == "pairs":
+        assert prof["paired"] >= NEAR_TIE_CAP_MIN, prof
+    else:
+        assert prof["windowed"] >= N - 100, prof
+        assert prof["rechecked"] >= prof["windowed"] - cap, prof
+
+
+@pytest.mark.parametrize("score", SCORES)
+def test_window_list_beyond_cap(gpu_lib, score):
+    """600,000 points, d = 24, 300 centroids in groups of three copies: every
+    point is a three-way tie, the window list holds all of them, and the
+    points past the 75,000 candidate slots are rescored against all K."""
+    fk = gpu_lib
+    N, d, K = 600000, 24, 300
+    X, C = synth.adversarial(12, N, d, K, "dup3")
+    a_ref, _, _ = oracle.assign(X, C)
+    fk.fk_profile_enable(True)
+    a, _ = fk.fk_assign(dev(X), dev(C), score=score)
+    prof = fk.fk_profile_read()
+    fk.fk_profile_enable(False)
+    np.testing.assert_array_equal(host(a), a_ref)
+    assert prof["rechecked"] > max(N // 8, NEAR_TIE_CAP_MIN), prof
+
+
 def test_update_single_giant_cluster(gpu_lib):
     """Every point in one cluster: the cluster crosses every segment boundary."""
     fk = gpu_lib
