@@ -30,7 +30,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
 
-METRICS = {"l2": 0, "cosine": 1, "inner_product": 2}
+METRICS = {"l2": 0, "cosine": 1, "inner_product": 2, "spherical": 3}
 
 _CFLAGS = ["-O2", "-fno-fast-math", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared"]
 
@@ -160,13 +160,83 @@ def normalize_rows(X):
     return out
 
 
-def fit(X, C_init, n_iter: int, metric: str = "l2"):
-    """Lloyd k-means: the iteration above repeated n_iter times from C_init.
-    Between iterations the centroids are held in fp32, the precision of C in
-    the problem statement (Flash-KMeans article, "Why being fast took so
-    long": X and C are the inputs of every iteration).  Returns (C float32,
-    a of the last iteration, counts of the last iteration, [J per
-    iteration])."""
+_MASK64 = (1 << 64) - 1
+
+
+class _SplitMix64:
+    """SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+    generators", OOPSLA 2014): the state advances by the golden-ratio
+    increment 0x9E3779B97F4A7C15 and each output is the new state passed
+    through the variant-13 mix (xor-shifts by 30, 27 and 31 with multipliers
+    0xBF58476D1CE4E5B9 and 0x94D049BB133111EB), all modulo 2^64.  The output
+    is a function of the seed and the draw's position only."""
+
+    def __init__(self, seed: int):
+        self.st = seed & _MASK64
+
+    def next(self) -> int:
+        self.st = (self.st + 0x9E3779B97F4A7C15) & _MASK64
+        z = self.st
+        z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK64
+        z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK64
+        return z ^ (z >> 31)
+
+    def below(self, m: int) -> int:
+        """Uniform integer in [0, m): draws at or above the largest multiple
+        of m that fits in 2^64 are rejected, the rest taken modulo m."""
+        limit = (1 << 64) - ((1 << 64) % m)
+        while True:
+            r = self.next()
+            if r < limit:
+                return r % m
+
+
+def splitmix64(seed: int, n: int) -> list:
+    """The first n outputs of SplitMix64 seeded with `seed`."""
+    g = _SplitMix64(seed)
+    return [g.next() for _ in range(int(n))]
+
+
+def sample_rows(N: int, K: int, seed: int) -> np.ndarray:
+    """K distinct row indices of [0, N) drawn with `seed`: the first K
+    positions of a Fisher-Yates shuffle of 0..N-1 (Durstenfeld's form: step i
+    swaps position i with a uniform position in [i, N)), the shuffled array
+    held as a map of the positions moved, numbers from SplitMix64 above.  The
+    FlashLib guide's k-means takes a seed (paragraph "参数速查": seed 0) and
+    samples its initial centroids from the rows; the pages name no generator,
+    so this published one is the reading.  Requires 1 <= K <= N."""
+    N, K = int(N), int(K)
+    if not (1 <= K <= N):
+        raise ValueError("need 1 <= K <= N")
+    rng = _SplitMix64(seed)
+    moved = {}
+    out = np.empty(K, np.int64)
+    for i in range(K):
+        j = i + rng.below(N - i)
+        vi = moved.get(i, i)
+        vj = moved.get(j, j)
+        moved[j] = vi
+        moved[i] = vj
+        out[i] = vj
+    return out
+
+
+def centroid_shift(C_old, C_new) -> float:
+    """The largest squared L2 distance, in fp64, between a centroid's fp32
+    value before and after an iteration: the fit's stopping measure."""
+    D = np.asarray(C_new, np.float64) - np.asarray(C_old, np.float64)
+    return float((D * D).sum(1).max())
+
+
+def fit(X, C_init, n_iter: int, metric: str = "l2", tol=None):
+    """Lloyd k-means: the iteration above repeated from C_init, at most n_iter
+    times.  Between iterations the centroids are held in fp32, the precision
+    of C in the problem statement (Flash-KMeans article, "Why being fast took
+    so long": X and C are the inputs of every iteration).  With tol >= 0 the
+    fit stops after the first iteration whose centroid_shift is at or below
+    tol (tol = 0: once an iteration leaves every centroid unchanged, a fixed
+    point).  Returns (C float32, a of the last iteration, counts of the last
+    iteration, [J per iteration]); len(J) is the number of iterations run."""
     if n_iter < 1:
         raise ValueError("n_iter must be at least 1")
     C = _f32(C_init)
@@ -174,19 +244,36 @@ def fit(X, C_init, n_iter: int, metric: str = "l2"):
     for _ in range(int(n_iter)):
         r = lloyd_iter(X, C, metric)
         Js.append(r["J"])
-        C = r["C"].astype(np.float32)
+        C_new = r["C"].astype(np.float32)
+        stop = tol is not None and tol >= 0 and centroid_shift(C, C_new) <= tol
+        C = C_new
+        if stop:
+            break
     return C, r["a"], r["counts"], Js
 
 
-def ivf_build(X, init_idx, n_iter: int, metric: str = "l2"):
+def fit_seeded(X, K: int, n_iter: int, seed: int, metric: str = "l2", tol=None):
+    """The fit from K' = min(K, N) rows drawn by sample_rows(N, K', seed)
+    (the FlashLib guide clamps the cluster count to the row count, paragraph
+    "nlist 与 nprobe").  Returns fit()'s tuple plus the indices drawn."""
+    X = _f32(X)
+    idx = sample_rows(X.shape[0], min(int(K), X.shape[0]), seed)
+    return fit(X, X[idx], n_iter, metric, tol) + (idx,)
+
+
+def ivf_build(X, init_idx, n_iter: int, metric: str = "l2", nlist=None, seed=None):
     """IVF-Flat build as the LEANN FlashLib guide describes it (paragraphs
     "工作原理" and "参数速查"): for cosine the rows are normalised first; a
     coarse quantizer is trained by n_iter Lloyd iterations (L2) from the rows
-    init_idx; every row is then assigned to its nearest final centroid, and
+    init_idx (or, with init_idx None, from min(nlist, N) rows drawn by
+    sample_rows with `seed`: the guide clamps nlist to N, paragraph "nlist 与
+    nprobe"); every row is then assigned to its nearest final centroid, and
     the rows are grouped by cell (CSR offsets, the row ids of each cell in
     increasing order, and the rows themselves).  Returns a dict with
     centroids, labels, offsets, ids, data."""
     Xu = normalize_rows(X) if metric == "cosine" else _f32(X)
+    if init_idx is None:
+        init_idx = sample_rows(Xu.shape[0], min(int(nlist), Xu.shape[0]), seed)
     init_idx = np.asarray(init_idx, np.int64)
     C, _, _, _ = fit(Xu, Xu[init_idx], n_iter, "l2")
     a, _, _ = assign(Xu, C, "l2")
@@ -201,18 +288,24 @@ def knn(Q, DB, k: int, metric: str = "l2"):
     paragraph "何时使用": the exact GPU k-NN backend): for each query, the k
     database rows first in (fp64 distance, row index) order, the distance
     being the assignment step's (cosine: both rows normalised; inner
-    product: -q.x).  Returns (idx int32[M, k], dist float64[M, k])."""
+    product: -q.x).  The backend clamps k to the database size; here a k
+    above Ndb gives Ndb neighbours followed by index -1 at distance +inf.
+    Returns (idx int32[M, k], dist float64[M, k])."""
     Q = _f32(Q)
     DB = _f32(DB)
     M, d = Q.shape
     Ndb, dd = DB.shape
     if dd != d:
         raise ValueError("Q and DB differ in d")
-    idx = np.empty((M, k), np.int32)
-    dist = np.empty((M, k), np.float64)
-    rc = _load().fko_knn(_ptr(Q), M, d, _ptr(DB), Ndb, int(k), METRICS[metric], _ptr(idx), _ptr(dist))
+    kk = min(int(k), Ndb)
+    idx = np.empty((M, kk), np.int32)
+    dist = np.empty((M, kk), np.float64)
+    rc = _load().fko_knn(_ptr(Q), M, d, _ptr(DB), Ndb, kk, METRICS[metric], _ptr(idx), _ptr(dist))
     if rc != 0:
         raise ValueError("oracle knn rejected its arguments")
+    if kk < k:
+        idx = np.concatenate([idx, np.full((M, k - kk), -1, np.int32)], axis=1)
+        dist = np.concatenate([dist, np.full((M, k - kk), np.inf)], axis=1)
     return idx, dist
 
 

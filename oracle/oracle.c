@@ -43,6 +43,20 @@
 #define FKO_METRIC_L2 0
 #define FKO_METRIC_COSINE 1
 #define FKO_METRIC_INNER_PRODUCT 2
+#define FKO_METRIC_SPHERICAL 3
+
+/* Spherical k-means assigns as cosine does (rows normalised) and returns
+ * centroids normalised to unit length. */
+static int normalises(int metric)
+{
+    return metric == FKO_METRIC_COSINE || metric == FKO_METRIC_SPHERICAL;
+}
+
+static int known_metric(int metric)
+{
+    return metric == FKO_METRIC_L2 || metric == FKO_METRIC_COSINE || metric == FKO_METRIC_INNER_PRODUCT ||
+           metric == FKO_METRIC_SPHERICAL;
+}
 
 /* Promote one fp32 row to fp64; for cosine divide it by its L2 norm, the
  * norm being taken as 1 when it is 0 (FlashLib guide, "距离度量"). */
@@ -50,7 +64,7 @@ static void promote_row(const float *src, int64_t d, int metric, double *dst)
 {
     for (int64_t j = 0; j < d; ++j)
         dst[j] = (double)src[j];
-    if (metric == FKO_METRIC_COSINE) {
+    if (normalises(metric)) {
         double s = 0.0;
         for (int64_t j = 0; j < d; ++j)
             s = s + dst[j] * dst[j];
@@ -115,7 +129,7 @@ int fko_assign(const float *X, int64_t N, int64_t d, const float *C, int64_t K,
 {
     if (N < 0 || d <= 0 || K <= 0 || (N > 0 && !X) || !C)
         return -1;
-    if (metric != FKO_METRIC_L2 && metric != FKO_METRIC_COSINE && metric != FKO_METRIC_INNER_PRODUCT)
+    if (!known_metric(metric))
         return -1;
     double *Cd = promote_matrix(C, K, d, metric);
     if (!Cd)
@@ -161,17 +175,21 @@ int fko_assign(const float *X, int64_t N, int64_t d, const float *C, int64_t K,
 
 /*
  * Update step.  n_k = #{i : a_i = k}; s_k = sum of x_i over those i, in
- * increasing i, in fp64 (rows normalised for cosine; taken as they are for L2
- * and inner product); C_out[k] = s_k / n_k, or C_in[k] (as passed, not
- * normalised) when n_k == 0.  Returns 0, or -1 on bad arguments (including a
- * label outside [0, K)) or allocation failure.
+ * increasing i, in fp64 (rows normalised for cosine and spherical; taken as
+ * they are for L2 and inner product); C_out[k] = s_k / n_k, or C_in[k] (as
+ * passed, not normalised) when n_k == 0.  Spherical k-means (the explicit
+ * spherical-centroid option beside cosine, named in the Flash-KMeans article's
+ * section "Not a silver bullet" as where the metrics go next) then divides
+ * each C_out[k] by its L2 norm (summed in increasing j; a zero norm taken as
+ * 1, the guard of the FlashLib guide's "距离度量").  Returns 0, or -1 on bad
+ * arguments (including a label outside [0, K)) or allocation failure.
  */
 int fko_update(const float *X, int64_t N, int64_t d, const int32_t *a, int64_t K,
                int metric, const float *C_in, double *C_out, int64_t *counts)
 {
     if (N < 0 || d <= 0 || K <= 0 || (N > 0 && (!X || !a)) || !C_in || !C_out || !counts)
         return -1;
-    if (metric != FKO_METRIC_L2 && metric != FKO_METRIC_COSINE && metric != FKO_METRIC_INNER_PRODUCT)
+    if (!known_metric(metric))
         return -1;
     for (int64_t i = 0; i < N; ++i)
         if (a[i] < 0 || (int64_t)a[i] >= K)
@@ -198,6 +216,18 @@ int fko_update(const float *X, int64_t N, int64_t d, const int32_t *a, int64_t K
         } else {
             for (int64_t j = 0; j < d; ++j)
                 s[j] = (double)C_in[k * d + j];
+        }
+        /* spherical: the mean direction, a zero vector staying zero (the
+         * norm taken as 1), and an empty cluster's centroid normalised too */
+        if (metric == FKO_METRIC_SPHERICAL) {
+            double q = 0.0;
+            for (int64_t j = 0; j < d; ++j)
+                q = q + s[j] * s[j];
+            double n = sqrt(q);
+            if (n == 0.0)
+                n = 1.0;
+            for (int64_t j = 0; j < d; ++j)
+                s[j] = s[j] / n;
         }
     }
     free(xi);

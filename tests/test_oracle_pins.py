@@ -520,10 +520,149 @@ def test_knn_cosine_is_largest_cosine_similarity():
     np.testing.assert_allclose(dist, 2.0 - 2.0 * np.take_along_axis(cs, idx.astype(np.int64), 1), atol=1e-12)
 
 
-def test_knn_rejects_k_above_database_size():
-    Q = np.zeros((2, 3), np.float32)
-    DB = np.zeros((4, 3), np.float32)
-    with pytest.raises(ValueError):
-        oracle.knn(Q, DB, 5)
+def test_knn_clamps_k_to_database_size():
+    """k above the database size (the FlashLib backend clamps top_k to it):
+    every row, nearest first, then index -1 at distance +inf; k = 0 is
+    rejected."""
+    rng = np.random.default_rng(82)
+    Q = rng.integers(-3, 4, (5, 3)).astype(np.float32)
+    DB = rng.integers(-3, 4, (4, 3)).astype(np.float32)
+    idx, dist = oracle.knn(Q, DB, 7)
+    full, fd = oracle.knn(Q, DB, 4)
+    np.testing.assert_array_equal(idx[:, :4], full)
+    np.testing.assert_array_equal(dist[:, :4], fd)
+    assert (idx[:, 4:] == -1).all() and np.isinf(dist[:, 4:]).all()
+    exact = ((Q[:, None, :].astype(np.int64) - DB[None].astype(np.int64)) ** 2).sum(-1)
+    np.testing.assert_array_equal(np.sort(exact, axis=1), dist[:, :4])
     with pytest.raises(ValueError):
         oracle.knn(Q, DB, 0)
+
+
+# ---------------------------------------------------- seeded draw, fit, spherical
+
+def test_splitmix64_first_outputs():
+    """SplitMix64 from seed 0 starts 0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4,
+    0x06C45D188009454F (the values the generator's reference C code gives,
+    widely used to check implementations)."""
+    assert oracle.splitmix64(0, 3) == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+    # the output is a function of (seed, position): seeding one step later
+    # by the increment gives the same stream shifted by one
+    assert oracle.splitmix64(0x9E3779B97F4A7C15, 2) == oracle.splitmix64(0, 3)[1:]
+
+
+def test_sample_rows_distinct_in_range_and_uniform():
+    for N, K, seed in [(1, 1, 0), (10, 10, 3), (1000, 17, 5), (2 ** 31 - 1, 64, 9)]:
+        idx = oracle.sample_rows(N, K, seed)
+        assert len(idx) == K and len(set(idx.tolist())) == K
+        assert idx.min() >= 0 and idx.max() < N
+    assert sorted(oracle.sample_rows(10, 10, 3).tolist()) == list(range(10))
+    # every ordered pair of distinct rows of 5 is equally likely: 20 cells,
+    # 40,000 draws, chi-square with 19 degrees of freedom below its 0.999
+    # quantile (43.8); a shuffle that never picks the last row, or picks
+    # from [i, N - 1) only, fails this
+    cnt = np.zeros((5, 5))
+    for seed in range(40000):
+        i, j = oracle.sample_rows(5, 2, seed)
+        cnt[i, j] += 1
+    obs = cnt[~np.eye(5, dtype=bool)]
+    chi2 = ((obs - 2000.0) ** 2 / 2000.0).sum()
+    assert chi2 < 43.8, chi2
+    with pytest.raises(ValueError):
+        oracle.sample_rows(3, 4, 0)
+
+
+def test_fit_tolerance_zero_stops_at_a_fixed_point():
+    """tol = 0 stops once an iteration leaves every centroid unchanged; the
+    result equals running all the iterations (the iteration is then at a
+    fixed point), with fewer of them run."""
+    rng = np.random.default_rng(83)
+    X = np.concatenate([rng.normal(m, 0.05, (50, 2)) for m in ([0, 0], [3, 0], [0, 3])]).astype(np.float32)
+    C0 = X[[0, 50, 100]]
+    C_all, a_all, n_all, J_all = oracle.fit(X, C0, 30)
+    C_t, a_t, n_t, J_t = oracle.fit(X, C0, 30, tol=0.0)
+    assert len(J_t) < 30 and len(J_all) == 30
+    assert C_t.tobytes() == C_all.tobytes()
+    np.testing.assert_array_equal(a_t, a_all)
+    np.testing.assert_array_equal(n_t, n_all)
+    # an infinite tolerance stops after one iteration
+    C_1, _, _, J_1 = oracle.fit(X, C0, 30, tol=np.inf)
+    assert len(J_1) == 1
+    assert C_1.tobytes() == oracle.lloyd_iter(X, C0)["C"].astype(np.float32).tobytes()
+
+
+def test_centroid_shift_closed_form():
+    C0 = np.array([[0, 0], [1, 1]], np.float32)
+    C1 = np.array([[3, 4], [1, 2]], np.float32)
+    assert oracle.centroid_shift(C0, C1) == 25.0
+
+
+def test_fit_seeded_clamps_k_to_n():
+    """K above N: N clusters from every row; distinct rows are then each
+    their own centroid and the objective is zero."""
+    X = np.arange(14, dtype=np.float32).reshape(7, 2)
+    C, a, n, J, idx = oracle.fit_seeded(X, 10, 3, seed=4)
+    assert C.shape == (7, 2) and sorted(idx.tolist()) == list(range(7))
+    assert J[-1] == 0.0 and (n == 1).all()
+    np.testing.assert_array_equal(C[a], X)
+
+
+def test_spherical_update_closed_form():
+    """Spherical centroids are the normalised mean of the normalised rows:
+    rows (2, 0) and (0, 5) give (1/sqrt2, 1/sqrt2); a zero mean stays zero;
+    an empty cluster returns its given centroid normalised."""
+    X = np.array([[2, 0], [0, 5], [1, 0], [-3, 0]], np.float32)
+    a = np.array([0, 0, 1, 1], np.int32)
+    C_in = np.array([[9, 9], [9, 9], [0, -4]], np.float32)
+    C, n = oracle.update(X, a, C_in, "spherical")
+    np.testing.assert_array_equal(n, [2, 2, 0])
+    assert np.allclose(C[0], [2 ** -0.5, 2 ** -0.5], rtol=0, atol=4e-16)
+    assert (C[1] == 0).all()
+    np.testing.assert_array_equal(C[2], [0, -1])
+
+
+def test_spherical_centroid_maximises_cosine_sum():
+    """The spherical centroid of a cluster is the unit vector c maximising
+    sum_i xhat_i . c: no other unit vector (random ones, and small
+    perturbations of c) does better; the iteration's objective sum_i
+    (1 - xhat_i . c_{a_i}) does not increase."""
+    rng = np.random.default_rng(84)
+    X = (rng.standard_normal((300, 5)) + [2, 0, 0, 0, 0]).astype(np.float32)
+    a = np.zeros(300, np.int32)
+    C, _ = oracle.update(X, a, X[:1], "spherical")
+    c = C[0]
+    assert abs(np.linalg.norm(c) - 1) < 1e-12
+    xh = X.astype(np.float64) / np.linalg.norm(X.astype(np.float64), axis=1, keepdims=True)
+    best = (xh @ c).sum()
+    for _ in range(200):
+        v = c + 1e-3 * rng.standard_normal(5)
+        v /= np.linalg.norm(v)
+        assert (xh @ v).sum() <= best + 1e-9
+        w = rng.standard_normal(5)
+        w /= np.linalg.norm(w)
+        assert (xh @ w).sum() <= best + 1e-9
+    Xm = np.concatenate([rng.standard_normal((200, 6)) + m for m in np.eye(6) * 3]).astype(np.float32)
+    Cc = Xm[rng.choice(len(Xm), 6, replace=False)]
+    obj = []
+    for _ in range(8):
+        r = oracle.lloyd_iter(Xm, Cc, "spherical")
+        Cc = r["C"].astype(np.float32)
+        assert np.allclose(np.linalg.norm(r["C"], axis=1), 1.0, atol=1e-12)
+        obj.append(r["J"])
+    # under cosine assignment J = sum (2 - 2 xhat.c) with unit c (every
+    # centroid after the first iteration is unit length)
+    assert all(j1 <= j0 * (1 + 1e-12) for j0, j1 in zip(obj[1:], obj[2:]))
+
+
+def test_ivf_build_seeded_and_clamped():
+    """With no initial rows the quantizer starts from sample_rows(N,
+    min(nlist, N), seed); nlist above N gives N cells of one row each."""
+    rng = np.random.default_rng(85)
+    X = rng.standard_normal((300, 4)).astype(np.float32)
+    r1 = oracle.ivf_build(X, None, 3, nlist=16, seed=11)
+    r2 = oracle.ivf_build(X, oracle.sample_rows(300, 16, 11), 3)
+    for k in ("centroids", "offsets", "ids"):
+        np.testing.assert_array_equal(r1[k], r2[k])
+    small = X[:9]
+    r = oracle.ivf_build(small, None, 2, nlist=40, seed=1)
+    assert r["centroids"].shape == (9, 4)
+    np.testing.assert_array_equal(r["offsets"], np.arange(10))
