@@ -139,6 +139,11 @@ def test_out_of_core_scaled(gpu_lib, score):
     C_ref, n_ref = oracle.update(X, a, C)
     np.testing.assert_array_equal(counts, n_ref)
     assert centroid_rel_err(host(C1d), C_ref, n_ref) <= 1e-6
+    # give back the pinned rows and the chunked workspace at once
+    del Xh, ah, X
+    fk._ws_cache.clear()
+    torch.cuda.empty_cache()
+    torch._C._host_emptyCache()
 
 
 @pytest.mark.parametrize("score", ["fp32", "split_bf16"])
