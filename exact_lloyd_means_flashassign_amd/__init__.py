@@ -62,6 +62,7 @@ def load():
     lib.fk_sort_inverse.argtypes = [P, I64, I32, P, P, P, SZ, P]
     lib.fk_update.argtypes = [P, I64, I32, P, I32, I32, P, P, P, P, SZ, P]
     lib.fk_lloyd_iter.argtypes = [P, I64, I32, P, I32, I32, I32, P, P, P, P, P, SZ, P]
+    lib.fk_lloyd_iter_noalloc.argtypes = [P, I64, I32, P, I32, I32, I32, P, P, P, P, P]
     lib.fk_lloyd_iter_stream.argtypes = [P, I64, I32, P, I32, I32, I32, I64, P, P, P, P, SZ, P]
     lib.fk_fit_workspace_size.argtypes = [I64, I32, I32, I32]
     lib.fk_fit_workspace_size.restype = SZ
@@ -72,7 +73,7 @@ def load():
     lib.fk_knn_workspace_size.argtypes = [I64, I32, I64, I32, I32]
     lib.fk_knn_workspace_size.restype = SZ
     lib.fk_knn.argtypes = [P, I64, I32, P, I64, I32, I32, I32, P, P, P, SZ, P]
-    for f in ("fk_assign", "fk_sort_inverse", "fk_update", "fk_lloyd_iter", "fk_lloyd_iter_stream",
+    for f in ("fk_assign", "fk_sort_inverse", "fk_update", "fk_lloyd_iter", "fk_lloyd_iter_noalloc", "fk_lloyd_iter_stream",
               "fk_fit", "fk_ivf_build", "fk_knn", "fk_profile_enable", "fk_profile_read"):
         getattr(lib, f).restype = ctypes.c_int
     lib.fk_status_str.argtypes = [I32]
@@ -276,6 +277,31 @@ def fk_lloyd_iter(X, C_in, metric="l2", assign=None, C_out=None, counts=None, mi
     ws, wsn = _ws_args(N, d, K, metric, X.device, workspace)
     _check(load().fk_lloyd_iter(_ptr(X), N, d, _ptr(C_in), K, _metric(metric), _score(score), _ptr(assign),
                                 _ptr(min_dist), _ptr(C_out), _ptr(counts), ws, wsn, _stream(X.device)))
+    return assign, C_out, counts, min_dist
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # FK_NOALLOC_SCRATCH_BYTES of include/fk.h
+
+
+def fk_lloyd_iter_noalloc(X, C_in, assign, C_out, counts, metric="l2", min_dist=None, score="fp32"):
+    """One Lloyd iteration that allocates nothing: the library's static
+    per-device scratch replaces the workspace (sizes up to
+    NOALLOC_SCRATCH_BYTES of workspace; calls that overlap on one device
+    race).  Every output is the caller's.  Returns (assign, C_out, counts,
+    min_dist)."""
+    _dev(X, "X", torch.float32)
+    _dev(C_in, "C_in", torch.float32)
+    if X.dim() != 2 or C_in.dim() != 2 or X.shape[1] != C_in.shape[1]:
+        raise ValueError("X[N,d] and C[K,d] must be 2-D with the same d")
+    N, d = X.shape
+    K = C_in.shape[0]
+    _dev(assign, "assign", torch.int32, (N,))
+    _dev(C_out, "C_out", torch.float32, (K, d))
+    _dev(counts, "counts", torch.int32, (K,))
+    if min_dist is not None:
+        _dev(min_dist, "min_dist", torch.float32, (N,))
+    _check(load().fk_lloyd_iter_noalloc(_ptr(X), N, d, _ptr(C_in), K, _metric(metric), _score(score), _ptr(assign),
+                                        _ptr(min_dist), _ptr(C_out), _ptr(counts), _stream(X.device)))
     return assign, C_out, counts, min_dist
 
 

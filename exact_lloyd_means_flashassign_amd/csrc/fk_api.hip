@@ -209,6 +209,10 @@ struct Prof {
 };
 Prof g_prof;
 
+// Set for the duration of an fk_lloyd_iter_noalloc call on this thread: phase
+// timing is skipped there, since it creates events and pinned count slots.
+thread_local bool t_no_alloc = false;
+
 hipEvent_t prof_event() {
     if (!g_prof.pool.empty()) {
         hipEvent_t e = g_prof.pool.back();
@@ -225,6 +229,7 @@ struct PhaseScope {
     hipStream_t s;
     hipEvent_t a = nullptr, b = nullptr;
     PhaseScope(int ph, hipStream_t st) : phase(ph), s(st) {
+        if (t_no_alloc) return;
         std::lock_guard<std::mutex> g(g_prof.mu);
         if (!g_prof.on) return;
         a = prof_event();
@@ -240,6 +245,7 @@ struct PhaseScope {
 };
 
 void prof_count_rechecks(const int32_t *dev_counters, int64_t n_assigned, hipStream_t s) {
+    if (t_no_alloc) return;
     std::lock_guard<std::mutex> g(g_prof.mu);
     if (!g_prof.on) return;
     if (g_prof.slots_used == g_prof.count_slots.size()) {
@@ -518,10 +524,10 @@ fk_status fk_update(const float *X, int64_t N, int32_t d, const int32_t *assign,
     return step_finalize(c, C_prev, C_out, counts);
 }
 
-fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in, int32_t K, int32_t metric,
-                        int32_t score, int32_t *assign, float *min_dist, float *C_out, int32_t *counts,
-                        void *workspace, size_t workspace_bytes, void *stream) {
-    g_err[0] = 0;
+namespace {
+// Arguments of fk_lloyd_iter and fk_lloyd_iter_noalloc, workspace aside.
+fk_status check_lloyd_args(const float *X, int64_t N, int32_t d, const float *C_in, int32_t K, int32_t metric,
+                           int32_t score, const int32_t *assign, const float *C_out, const int32_t *counts) {
     fk_status st = check_common(X, N, d, C_in, K, metric);
     if (st != FK_OK) return st;
     if ((st = check_score(score)) != FK_OK) return st;
@@ -529,10 +535,48 @@ fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in,
     if (C_out == nullptr || counts == nullptr) return fail(FK_ERR_INVALID_ARG, "C_out and counts must not be NULL");
     const size_t cb = (size_t)K * d * 4;
     if (overlap(C_out, cb, C_in, cb)) return fail(FK_ERR_INVALID_ARG, "C_out overlaps C_in");
+    return FK_OK;
+}
+
+struct NoAllocScope {
+    NoAllocScope() { t_no_alloc = true; }
+    ~NoAllocScope() { t_no_alloc = false; }
+};
+}  // namespace
+
+fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in, int32_t K, int32_t metric,
+                        int32_t score, int32_t *assign, float *min_dist, float *C_out, int32_t *counts,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    g_err[0] = 0;
+    fk_status st = check_lloyd_args(X, N, d, C_in, K, metric, score, assign, C_out, counts);
+    if (st != FK_OK) return st;
     const Layout L = make_layout(N, d, K, metric, false);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
     const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
+    return lloyd_step(c, X, N, C_in, assign, min_dist, C_out, counts);
+}
+
+fk_status fk_lloyd_iter_noalloc(const float *X, int64_t N, int32_t d, const float *C_in, int32_t K, int32_t metric,
+                                int32_t score, int32_t *assign, float *min_dist, float *C_out, int32_t *counts,
+                                void *stream) {
+    g_err[0] = 0;
+    fk_status st = check_lloyd_args(X, N, d, C_in, K, metric, score, assign, C_out, counts);
+    if (st != FK_OK) return st;
+    const Layout L = make_layout(N, d, K, metric, false);
+    if (L.total > (size_t)FK_NOALLOC_SCRATCH_BYTES)
+        return fail(FK_ERR_WORKSPACE,
+                    "N=%lld, d=%d, K=%d needs %zu bytes of scratch; fk_lloyd_iter_noalloc holds %zu (use "
+                    "fk_lloyd_iter with a workspace)",
+                    (long long)N, (int)d, (int)K, L.total, (size_t)FK_NOALLOC_SCRATCH_BYTES);
+    if ((st = check_device()) != FK_OK) return st;
+    void *ws = nullptr;
+    int dev = 0;
+    FK_TRY(hipGetDevice(&dev), "hipGetDevice");
+    FK_TRY(noalloc_scratch(dev, &ws), "hipGetSymbolAddress of the static scratch");
+    if (ws == nullptr || !aligned(ws, 256)) return fail(FK_ERR_HIP, "the static scratch has no usable device address");
+    NoAllocScope no_alloc;
+    const Ctx c{L, ws, (hipStream_t)stream, d, K, metric, score};
     return lloyd_step(c, X, N, C_in, assign, min_dist, C_out, counts);
 }
 

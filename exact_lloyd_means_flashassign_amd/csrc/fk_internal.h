@@ -113,6 +113,10 @@ hipError_t launch_sort_by_key(const int32_t *keys, int64_t N, int K, int32_t *ke
 hipError_t launch_offsets(const int32_t *keys_sorted, int64_t N, int K, int32_t *offsets, hipStream_t s);
 
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s);
+// Device address of the static scratch of the allocation-free Lloyd
+// iteration (FK_NOALLOC_SCRATCH_BYTES) on device `device`, which must be the
+// current device: looked up once per device, then kept.
+hipError_t noalloc_scratch(int device, void **ptr);
 // The segmented reduction also writes the cluster offsets (first sorted row of
 // each key, offsets[K] = N).  acc: rows fed in several batches, cluster sums
 // added to sums (divided by launch_finalize at the end); otherwise the rows

@@ -21,6 +21,9 @@
 // (the wave of an inner cluster, k_seg_fixup for a crossing one), so the fp64
 // sums never go through memory; the cluster offsets are written by the
 // reduction as it meets each key change.
+#include <mutex>
+
+#include "fk.h"
 #include "fk_internal.h"
 
 namespace fk {
@@ -319,6 +322,34 @@ __global__ __launch_bounds__(256) void k_finalize(const double *__restrict__ sum
 }
 
 // ---------------------------------------------------------------------------
+// The scratch of the allocation-free Lloyd iteration (fk_lloyd_iter_noalloc):
+// every device holds its own copy of this array, from the library's load on
+// that device until the process ends, at its own address.  It sits in this
+// file beside kernels that every iteration launches.  Host code never uses
+// its name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, and is kept.
+static_assert(FK_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) unsigned char scratch[FK_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t noalloc_scratch(int device, void **ptr) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> g(g_scratch_mu);
+    if (g_scratch_ptr[device] == nullptr) {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = p;
+    }
+    *ptr = g_scratch_ptr[device];
+    return hipSuccess;
+}
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
     const int64_t n = (int64_t)(bytes / 4);
     if (n <= 0) return hipSuccess;

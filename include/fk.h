@@ -162,6 +162,23 @@ fk_status fk_lloyd_iter(const float *X, int64_t N, int32_t d, const float *C_in,
                         void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * fk_lloyd_iter for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, results and errors as fk_lloyd_iter, without the
+ * workspace: the call uses a scratch array of FK_NOALLOC_SCRATCH_BYTES that
+ * the library holds on every device it runs on until the process ends, and
+ * calls no allocating routine (phase timing is skipped).  Sizes whose
+ * fk_workspace_size(N, d, K, metric, 0) exceeds FK_NOALLOC_SCRATCH_BYTES are
+ * rejected with FK_ERR_WORKSPACE.  Every call on a device shares that
+ * device's scratch: calls that overlap on one device (other streams, other
+ * host threads) race and must be ordered by the caller.
+ */
+#define FK_NOALLOC_SCRATCH_BYTES (128u << 20)
+fk_status fk_lloyd_iter_noalloc(const float *X, int64_t N, int32_t d, const float *C_in, int32_t K, int32_t metric,
+                                int32_t score, int32_t *assign, float *min_dist, float *C_out, int32_t *counts,
+                                void *stream);
+
+/*
  * Out-of-core Lloyd iteration: X_host is PINNED host memory (hipHostMalloc
  * or a pinned torch tensor) holding N x d floats; it is copied to the device
  * in chunks of chunk_rows rows, double-buffered on a copy stream that
