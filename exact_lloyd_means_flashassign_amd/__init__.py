@@ -23,7 +23,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libfk.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "fk.h")
 
-METRICS = {"l2": 0, "cosine": 1, "inner_product": 2}
+METRICS = {"l2": 0, "cosine": 1, "inner_product": 2, "spherical": 3}
 SCORES = {"fp32": 0, "split_bf16": 1}
 PHASES = ("prep", "assign", "recheck", "sort", "reduce", "finalize", "h2d")
 MAX_K = 65536
@@ -42,6 +42,10 @@ class _Profile(ctypes.Structure):
     _fields_ = [("calls", ctypes.c_int64 * len(PHASES)), ("ms", ctypes.c_double * len(PHASES)),
                 ("rechecked", ctypes.c_int64), ("paired", ctypes.c_int64), ("windowed", ctypes.c_int64),
                 ("assigned", ctypes.c_int64)]
+
+
+class _FitInfo(ctypes.Structure):
+    _fields_ = [("k_used", ctypes.c_int32), ("iterations", ctypes.c_int32), ("last_shift", ctypes.c_double)]
 
 
 _lib = None
@@ -66,10 +70,12 @@ def load():
     lib.fk_lloyd_iter_stream.argtypes = [P, I64, I32, P, I32, I32, I32, I64, P, P, P, P, SZ, P]
     lib.fk_fit_workspace_size.argtypes = [I64, I32, I32, I32]
     lib.fk_fit_workspace_size.restype = SZ
-    lib.fk_fit.argtypes = [P, I64, I32, P, I32, I32, I32, I32, P, P, P, P, SZ, P]
+    lib.fk_fit.argtypes = [P, I64, I32, I32, I32, I32, P, ctypes.c_uint64, I32, ctypes.c_double, P, P, P,
+                           ctypes.POINTER(_FitInfo), P, SZ, P]
     lib.fk_ivf_workspace_size.argtypes = [I64, I32, I32, I32]
     lib.fk_ivf_workspace_size.restype = SZ
-    lib.fk_ivf_build.argtypes = [P, I64, I32, I32, I32, I32, I32, P, P, P, P, P, P, SZ, P]
+    lib.fk_ivf_build.argtypes = [P, I64, I32, I32, I32, I32, I32, P, ctypes.c_uint64, P, P, P, P,
+                                 ctypes.POINTER(ctypes.c_int32), P, SZ, P]
     lib.fk_knn_workspace_size.argtypes = [I64, I32, I64, I32, I32]
     lib.fk_knn_workspace_size.restype = SZ
     lib.fk_knn.argtypes = [P, I64, I32, P, I64, I32, I32, I32, P, P, P, SZ, P]
@@ -335,30 +341,48 @@ def fk_fit_workspace_size(N: int, d: int, K: int, metric="l2") -> int:
     return int(n)
 
 
-def fk_fit(X, C_init, n_iter: int, metric="l2", assign=None, C_out=None, counts=None, workspace=None,
-           score="fp32"):
-    """Lloyd k-means, n_iter iterations from C_init: returns (C_out, assign, counts)
-    (assign and counts are those of the last iteration)."""
+def fk_fit(X, C_init=None, n_iter: int = 20, metric="l2", K=None, seed: int = 0, tol: float = -1.0, assign=None,
+           C_out=None, counts=None, workspace=None, score="fp32", with_info=False):
+    """Lloyd k-means: up to n_iter iterations from C_init, or (C_init None)
+    from K' = min(K, N) rows of X drawn with `seed`; with tol >= 0 it stops
+    once no centroid moves by more than tol (squared L2).  Returns (C_out
+    [K', d], assign, counts [K']) and, with with_info, a dict with k_used,
+    iterations and last_shift as well."""
     _dev(X, "X", torch.float32)
-    _dev(C_init, "C_init", torch.float32)
-    if X.dim() != 2 or C_init.dim() != 2 or X.shape[1] != C_init.shape[1]:
-        raise ValueError("X[N,d] and C[K,d] must be 2-D with the same d")
+    if X.dim() != 2:
+        raise ValueError("X must be 2-D")
     N, d = X.shape
-    K = C_init.shape[0]
+    if C_init is not None:
+        _dev(C_init, "C_init", torch.float32)
+        if C_init.dim() != 2 or C_init.shape[1] != d:
+            raise ValueError("C_init must be [K, d] with the d of X")
+        K = C_init.shape[0]
+    elif K is None:
+        raise ValueError("give C_init or K")
+    K = int(K)
+    Ku = K if C_init is not None else min(K, int(N))
     if assign is None:
         assign = torch.empty(N, dtype=torch.int32, device=X.device)
     if C_out is None:
-        C_out = torch.empty_like(C_init)
+        C_out = torch.empty((max(Ku, 1), d), dtype=torch.float32, device=X.device)
     if counts is None:
-        counts = torch.empty(K, dtype=torch.int32, device=X.device)
+        counts = torch.empty(max(Ku, 1), dtype=torch.int32, device=X.device)
     _dev(assign, "assign", torch.int32, (N,))
-    _dev(C_out, "C_out", torch.float32, (K, d))
-    _dev(counts, "counts", torch.int32, (K,))
-    need = load().fk_fit_workspace_size(int(N), int(d), int(K), _metric(metric)) or 256
+    _dev(C_out, "C_out", torch.float32)
+    _dev(counts, "counts", torch.int32)
+    if C_out.numel() < Ku * d or counts.numel() < Ku:
+        raise ValueError("C_out and counts must hold K' rows")
+    need = load().fk_fit_workspace_size(int(N), int(d), K, _metric(metric)) or 256
     p, n = _workspace(need, X.device, workspace)
-    _check(load().fk_fit(_ptr(X), N, d, _ptr(C_init), K, _metric(metric), _score(score), int(n_iter), _ptr(C_out),
-                         _ptr(assign), _ptr(counts), ctypes.c_void_p(p), ctypes.c_size_t(n), _stream(X.device)))
-    return C_out, assign, counts
+    info = _FitInfo()
+    _check(load().fk_fit(_ptr(X), N, d, K, _metric(metric), _score(score), _ptr(C_init), int(seed) & (2 ** 64 - 1),
+                         int(n_iter), float(tol), _ptr(C_out), _ptr(assign), _ptr(counts), ctypes.byref(info),
+                         ctypes.c_void_p(p), ctypes.c_size_t(n), _stream(X.device)))
+    out = (C_out[:info.k_used], assign, counts[:info.k_used])
+    if with_info:
+        return out + ({"k_used": int(info.k_used), "iterations": int(info.iterations),
+                       "last_shift": float(info.last_shift)},)
+    return out
 
 
 def fk_ivf_workspace_size(N: int, d: int, nlist: int, metric="l2") -> int:
@@ -368,31 +392,38 @@ def fk_ivf_workspace_size(N: int, d: int, nlist: int, metric="l2") -> int:
     return int(n)
 
 
-def fk_ivf_build(X, nlist: int, init_idx, n_iter: int = 20, metric="l2", workspace=None, score="fp32"):
-    """IVF-Flat build: returns a dict with centroids [nlist', d], offsets
-    [nlist'+1], ids [N] and data [N, d] (rows grouped by cell), where nlist' =
-    min(nlist, N) as the FlashLib guide clamps it; init_idx holds the
-    quantizer's initial rows (at least nlist' of them, host ints)."""
+def fk_ivf_build(X, nlist: int, init_idx=None, n_iter: int = 20, metric="l2", seed: int = 0, workspace=None,
+                 score="fp32"):
+    """IVF-Flat build: returns a dict with centroids [nl, d], offsets [nl+1],
+    ids [N] and data [N, d] (rows grouped by cell), where nl = min(nlist, N)
+    (the library clamps it as the FlashLib guide does); init_idx holds the
+    quantizer's initial rows (host ints, at least nl of them), or None for
+    nl rows drawn with `seed`."""
     import numpy as np
     _dev(X, "X", torch.float32)
     if X.dim() != 2:
         raise ValueError("X must be 2-D")
     N, d = X.shape
-    nl = min(int(nlist), int(N))
-    idx = np.ascontiguousarray(np.asarray(init_idx, dtype=np.int32)[:nl])
-    if idx.shape[0] != nl:
-        raise ValueError(f"init_idx has {idx.shape[0]} entries, {nl} needed")
+    nlist = int(nlist)
+    idx = None
+    if init_idx is not None:
+        idx = np.ascontiguousarray(np.asarray(init_idx, dtype=np.int32))
+        if idx.ndim != 1 or idx.shape[0] < min(nlist, int(N)):
+            raise ValueError(f"init_idx has {idx.shape[0]} entries, {min(nlist, int(N))} needed")
     dev = X.device
-    out = {"centroids": torch.empty((nl, d), dtype=torch.float32, device=dev),
-           "offsets": torch.empty(nl + 1, dtype=torch.int32, device=dev),
+    rows = max(1, min(nlist, int(N)))
+    out = {"centroids": torch.empty((rows, d), dtype=torch.float32, device=dev),
+           "offsets": torch.empty(rows + 1, dtype=torch.int32, device=dev),
            "ids": torch.empty(N, dtype=torch.int32, device=dev),
-           "data": torch.empty((N, d), dtype=torch.float32, device=dev), "nlist": nl}
-    need = load().fk_ivf_workspace_size(int(N), int(d), nl, _metric(metric)) or 256
+           "data": torch.empty((N, d), dtype=torch.float32, device=dev)}
+    need = load().fk_ivf_workspace_size(int(N), int(d), nlist, _metric(metric)) or 256
     p, n = _workspace(need, dev, workspace)
-    _check(load().fk_ivf_build(_ptr(X), N, d, nl, _metric(metric), _score(score), int(n_iter),
-                               ctypes.c_void_p(idx.ctypes.data), _ptr(out["centroids"]), _ptr(out["offsets"]),
-                               _ptr(out["ids"]), _ptr(out["data"]), ctypes.c_void_p(p), ctypes.c_size_t(n),
-                               _stream(dev)))
+    nl = ctypes.c_int32(0)
+    _check(load().fk_ivf_build(_ptr(X), N, d, nlist, _metric(metric), _score(score), int(n_iter),
+                               None if idx is None else ctypes.c_void_p(idx.ctypes.data), int(seed) & (2 ** 64 - 1),
+                               _ptr(out["centroids"]), _ptr(out["offsets"]), _ptr(out["ids"]), _ptr(out["data"]),
+                               ctypes.byref(nl), ctypes.c_void_p(p), ctypes.c_size_t(n), _stream(dev)))
+    out["nlist"] = int(nl.value)
     return out
 
 
@@ -404,26 +435,26 @@ def fk_knn_workspace_size(M: int, d: int, Ndb: int, k: int, metric="l2") -> int:
 
 
 def fk_knn(Q, DB, k: int, metric="l2", idx=None, dist=None, workspace=None, score="fp32"):
-    """Exact k nearest database rows of every query: returns (idx [M, k'] int32,
-    dist [M, k'] fp32), nearest first (lower row index first on equal
-    distances), where k' = min(k, Ndb) as the FlashLib backend clamps top_k to
-    the corpus size."""
+    """Exact k nearest database rows of every query: returns (idx [M, k] int32,
+    dist [M, k] fp32), nearest first (lower row index first on equal
+    distances); with k above the database size the library clamps it as the
+    FlashLib backend does and the columns past Ndb hold -1 and +inf."""
     _dev(Q, "Q", torch.float32)
     _dev(DB, "DB", torch.float32)
     if Q.dim() != 2 or DB.dim() != 2 or Q.shape[1] != DB.shape[1]:
         raise ValueError("Q[M,d] and DB[Ndb,d] must be 2-D with the same d")
     M, d = Q.shape
     Ndb = DB.shape[0]
-    kk = min(int(k), int(Ndb))
+    k = int(k)
     if idx is None:
-        idx = torch.empty((M, kk), dtype=torch.int32, device=Q.device)
+        idx = torch.empty((M, k), dtype=torch.int32, device=Q.device)
     if dist is None:
-        dist = torch.empty((M, kk), dtype=torch.float32, device=Q.device)
-    _dev(idx, "idx", torch.int32, (M, kk))
-    _dev(dist, "dist", torch.float32, (M, kk))
-    need = load().fk_knn_workspace_size(int(M), int(d), int(Ndb), kk, _metric(metric)) or 256
+        dist = torch.empty((M, k), dtype=torch.float32, device=Q.device)
+    _dev(idx, "idx", torch.int32, (M, k))
+    _dev(dist, "dist", torch.float32, (M, k))
+    need = load().fk_knn_workspace_size(int(M), int(d), int(Ndb), k, _metric(metric)) or 256
     p, n = _workspace(need, Q.device, workspace)
-    _check(load().fk_knn(_ptr(Q), M, d, _ptr(DB), Ndb, kk, _metric(metric), _score(score), _ptr(idx), _ptr(dist),
+    _check(load().fk_knn(_ptr(Q), M, d, _ptr(DB), Ndb, k, _metric(metric), _score(score), _ptr(idx), _ptr(dist),
                          ctypes.c_void_p(p), ctypes.c_size_t(n), _stream(Q.device)))
     return idx, dist
 

@@ -1,8 +1,10 @@
 // Host side of libfk: argument validation, workspace carving, phase
 // sequencing on the caller's stream, the out-of-core chunk pipeline, and
 // phase timing.  Declared in include/fk.h.
+#include <cmath>
 #include <mutex>
 #include <stdarg.h>
+#include <unordered_map>
 #include <stdio.h>
 #include <string.h>
 #include <vector>
@@ -35,6 +37,10 @@ fk_status hip_fail(hipError_t e, const char *what) {
         if (e_ != hipSuccess) return hip_fail(e_, (what));  \
     } while (0)
 
+// Cosine and spherical normalise the rows they compare; spherical also
+// returns unit-length centroids.
+bool normalises(int metric) { return metric == FK_METRIC_COSINE || metric == FK_METRIC_SPHERICAL; }
+
 // ---- workspace layout -----------------------------------------------------
 struct Layout {
     size_t total = 0;
@@ -43,15 +49,17 @@ struct Layout {
     size_t keys_sorted, perm, tmp_keys, tmp_vals, sort_scratch, offsets;
     size_t sums, cnt, pfirst, plast, csplit;
     size_t xchunk[2], achunk[2];      // out-of-core only
-    size_t ctmp, cinit, labels, xcopy;  // fit / IVF build only
+    size_t ctmp, cinit, init_idx, labels, xcopy;  // fit / IVF build only
+    size_t shift_part, shift;                     // fit only (the stopping test)
     size_t knn_cand, knn_score, knn_win, knn_list, knn_tau;  // k nearest neighbours only
 };
 
 constexpr size_t kNone = ~(size_t)0;
 
-// extras: kFitExtras adds a second centroid buffer (the fit's ping-pong);
-// kIvfExtras adds the initial centroids, the list labels and, for cosine, a
-// normalised copy of X.
+// extras: kFitExtras adds a second centroid buffer (the fit's ping-pong),
+// the drawn initial rows and the stopping test's partial maxima; kIvfExtras
+// adds the initial centroids, the list labels and, for cosine, a normalised
+// copy of X.
 constexpr int kFitExtras = 1, kIvfExtras = 2;
 
 Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc, int extras = 0) {
@@ -65,7 +73,7 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc, int extras 
     const int64_t r = rows > 0 ? rows : 1;
     const int64_t Kpad = cdiv(K, kCentroidPad) * kCentroidPad;
     const int64_t nseg = seg_count_bound(r);
-    const bool cos = metric == FK_METRIC_COSINE;
+    const bool cos = normalises(metric);
     L.ncn = take((size_t)Kpad * 4);
     L.cmax_part = take((size_t)cdiv(Kpad, 4) * 3 * 4);
     L.scal = take(64);
@@ -97,7 +105,10 @@ Layout make_layout(int64_t rows, int d, int K, int metric, bool ooc, int extras 
     }
     const bool fit = (extras & (kFitExtras | kIvfExtras)) != 0, ivf = (extras & kIvfExtras) != 0;
     L.ctmp = fit ? take((size_t)K * d * 4) : kNone;
-    L.cinit = ivf ? take((size_t)K * d * 4) : kNone;
+    L.cinit = fit ? take((size_t)K * d * 4) : kNone;
+    L.init_idx = fit ? take((size_t)K * 4) : kNone;
+    L.shift_part = (extras & kFitExtras) ? take((size_t)cdiv(K, 4) * 8) : kNone;
+    L.shift = (extras & kFitExtras) ? take(64) : kNone;
     L.labels = ivf ? take((size_t)r * 4) : kNone;
     L.xcopy = (ivf && cos) ? take((size_t)r * d * 4) : kNone;
     L.knn_cand = L.knn_score = L.knn_win = L.knn_list = L.knn_tau = kNone;
@@ -118,7 +129,7 @@ Layout make_knn_layout(int64_t M, int d, int64_t Ndb, int k, int metric) {
     };
     const int64_t m = M > 0 ? M : 1;
     const int64_t Kpad = cdiv(Ndb, kCentroidPad) * kCentroidPad;
-    const bool cos = metric == FK_METRIC_COSINE;
+    const bool cos = normalises(metric);
     L.ncn = take((size_t)Kpad * 4);
     L.cmax_part = take((size_t)cdiv(Kpad, 4) * 3 * 4);
     L.scal = take(64);
@@ -138,7 +149,7 @@ Layout make_knn_layout(int64_t M, int d, int64_t Ndb, int k, int metric) {
     L.keys_sorted = L.perm = L.tmp_keys = L.tmp_vals = L.sort_scratch = L.offsets = kNone;
     L.sums = L.cnt = L.pfirst = L.plast = kNone;
     L.xchunk[0] = L.xchunk[1] = L.achunk[0] = L.achunk[1] = kNone;
-    L.ctmp = L.cinit = L.labels = L.xcopy = kNone;
+    L.ctmp = L.cinit = L.init_idx = L.labels = L.xcopy = L.shift_part = L.shift = kNone;
     L.total = off;
     return L;
 }
@@ -162,9 +173,13 @@ fk_status check_score(int32_t score) {
     return FK_OK;
 }
 
+bool known_metric(int32_t metric) {
+    return metric == FK_METRIC_L2 || metric == FK_METRIC_COSINE || metric == FK_METRIC_INNER_PRODUCT ||
+           metric == FK_METRIC_SPHERICAL;
+}
+
 fk_status check_metric(int32_t metric) {
-    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE && metric != FK_METRIC_INNER_PRODUCT)
-        return fail(FK_ERR_INVALID_ARG, "unknown metric %d", (int)metric);
+    if (!known_metric(metric)) return fail(FK_ERR_INVALID_ARG, "unknown metric %d", (int)metric);
     return FK_OK;
 }
 
@@ -277,7 +292,7 @@ struct Ctx {
 fk_status step_prep(const Ctx &c, const float *C, const float **C_use) {
     PhaseScope ph(FK_PH_PREP, c.s);
     const float *Cu = C;
-    if (c.metric == FK_METRIC_COSINE) {
+    if (normalises(c.metric)) {
         FK_TRY(launch_row_norm64(C, c.K, c.d, at<double>(c.ws, c.L.cnrm64), c.s), "centroid norms");
         FK_TRY(launch_normalize_rows(C, c.K, c.d, at<double>(c.ws, c.L.cnrm64), at<double>(c.ws, c.L.c64),
                                      at<float>(c.ws, c.L.c32), c.s),
@@ -296,7 +311,7 @@ fk_status step_prep(const Ctx &c, const float *C, const float **C_use) {
 }
 
 fk_status step_xnorm(const Ctx &c, const float *X, int64_t rows) {
-    if (c.metric != FK_METRIC_COSINE) return FK_OK;
+    if (!normalises(c.metric)) return FK_OK;
     PhaseScope ph(FK_PH_PREP, c.s);
     FK_TRY(launch_row_norm64(X, rows, c.d, at<double>(c.ws, c.L.xnorm64), c.s), "point norms");
     return FK_OK;
@@ -307,7 +322,7 @@ fk_status step_xnorm(const Ctx &c, const float *X, int64_t rows) {
 // step_prep zeroed the near-tie counter.
 fk_status step_assign(const Ctx &c, const float *X, int64_t rows, const float *C, const float *C_use,
                       int32_t *a_out, float *d1_out) {
-    const double *xn = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.xnorm64) : nullptr;
+    const double *xn = normalises(c.metric) ? at<double>(c.ws, c.L.xnorm64) : nullptr;
     NearTies nt;
     nt.full_list = at<int32_t>(c.ws, c.L.flags);
     nt.full_thr = at<float>(c.ws, c.L.thr);
@@ -324,7 +339,7 @@ fk_status step_assign(const Ctx &c, const float *X, int64_t rows, const float *C
     }
     {
         PhaseScope ph(FK_PH_RECHECK, c.s);
-        const double *c64 = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.c64) : nullptr;
+        const double *c64 = normalises(c.metric) ? at<double>(c.ws, c.L.c64) : nullptr;
         FK_TRY(launch_recheck(X, rows, c.d, C_use, C, c64, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal),
                               xn, nt, c.split(), c.metric == FK_METRIC_INNER_PRODUCT, a_out, d1_out, c.s),
                "near-tie recheck");
@@ -372,7 +387,7 @@ fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int3
     int32_t *offs = at<int32_t>(c.ws, c.L.offsets);
     {
         PhaseScope ph(FK_PH_REDUCE, c.s);
-        const double *xn = c.metric == FK_METRIC_COSINE ? at<double>(c.ws, c.L.xnorm64) : nullptr;
+        const double *xn = normalises(c.metric) ? at<double>(c.ws, c.L.xnorm64) : nullptr;
         FK_TRY(launch_seg_reduce(X, rows, c.d, c.K, at<int32_t>(c.ws, c.L.keys_sorted), at<int32_t>(c.ws, c.L.perm),
                                  xn, at<double>(c.ws, c.L.sums), at<double>(c.ws, c.L.pfirst),
                                  at<double>(c.ws, c.L.plast), batches, offs, C_out, c.s),
@@ -387,6 +402,7 @@ fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int3
     if (!batches) {
         PhaseScope ph(FK_PH_FINALIZE, c.s);
         FK_TRY(launch_counts_keep(offs, c.K, c.d, C_prev, C_out, counts, c.s), "counts");
+        if (c.metric == FK_METRIC_SPHERICAL) FK_TRY(launch_unit_rows(C_out, c.K, c.d, c.s), "unit centroids");
     }
     return FK_OK;
 }
@@ -397,6 +413,7 @@ fk_status step_finalize(const Ctx &c, const float *C_prev, float *C_out, int32_t
     FK_TRY(launch_finalize(at<double>(c.ws, c.L.sums), at<int32_t>(c.ws, c.L.cnt), C_prev, c.K, c.d, C_out, counts,
                            c.s),
            "finalize");
+    if (c.metric == FK_METRIC_SPHERICAL) FK_TRY(launch_unit_rows(C_out, c.K, c.d, c.s), "unit centroids");
     return FK_OK;
 }
 
@@ -443,11 +460,57 @@ fk_status fit_steps(const Ctx &c, const float *X, int64_t N, const float *C_init
 
 }  // namespace
 
+namespace {
+// SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number
+// generators", OOPSLA 2014): the state advances by 0x9E3779B97F4A7C15 and
+// every output is the new state through the variant-13 mix.
+struct SplitMix64 {
+    uint64_t st;
+    uint64_t next() {
+        st += 0x9E3779B97F4A7C15ull;
+        uint64_t z = st;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        return z ^ (z >> 31);
+    }
+    // uniform in [0, m): draws at or above the largest multiple of m below
+    // 2^64 are rejected, the rest reduced modulo m
+    uint64_t below(uint64_t m) {
+        const uint64_t rem = (UINT64_MAX % m + 1) % m;  // 2^64 mod m
+        for (;;) {
+            const uint64_t r = next();
+            if (rem == 0 || r < (uint64_t)0 - rem) return r % m;
+        }
+    }
+};
+
+// K distinct rows of [0, N): the first K positions of a Fisher-Yates shuffle
+// of 0..N-1 (step i swaps position i with i + below(N - i)), the shuffled
+// array kept as a map of the positions moved.
+std::vector<int32_t> sample_rows(int64_t N, int32_t K, uint64_t seed) {
+    SplitMix64 g{seed};
+    std::unordered_map<int64_t, int64_t> moved;
+    moved.reserve((size_t)K * 2);
+    std::vector<int32_t> out((size_t)K);
+    for (int64_t i = 0; i < K; ++i) {
+        const int64_t j = i + (int64_t)g.below((uint64_t)(N - i));
+        const auto fi = moved.find(i);
+        const int64_t vi = fi == moved.end() ? i : fi->second;
+        const auto fj = moved.find(j);
+        const int64_t vj = fj == moved.end() ? j : fj->second;
+        moved[j] = vi;
+        moved[i] = vj;
+        out[(size_t)i] = (int32_t)vj;
+    }
+    return out;
+}
+}  // namespace
+
 extern "C" {
 
 size_t fk_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric, int64_t chunk_rows) {
     if (N < 0 || N > INT32_MAX || d < 1 || d > FK_MAX_D || K < 1 || K > FK_MAX_K) return 0;
-    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE && metric != FK_METRIC_INNER_PRODUCT) return 0;
+    if (!known_metric(metric)) return 0;
     if (chunk_rows < 0 || chunk_rows > INT32_MAX) return 0;
     const bool ooc = chunk_rows > 0;
     return make_layout(ooc ? chunk_rows : N, d, K, metric, ooc).total;
@@ -689,66 +752,115 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
 
 size_t fk_fit_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric) {
     if (N < 0 || N > INT32_MAX || d < 1 || d > FK_MAX_D || K < 1 || K > FK_MAX_K) return 0;
-    if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE && metric != FK_METRIC_INNER_PRODUCT) return 0;
+    if (!known_metric(metric)) return 0;
     return make_layout(N, d, K, metric, false, kFitExtras).total;
 }
 
-fk_status fk_fit(const float *X, int64_t N, int32_t d, const float *C_init, int32_t K, int32_t metric, int32_t score,
-                 int32_t n_iter, float *C_out, int32_t *assign, int32_t *counts, void *workspace,
-                 size_t workspace_bytes, void *stream) {
+fk_status fk_fit(const float *X, int64_t N, int32_t d, int32_t K, int32_t metric, int32_t score, const float *C_init,
+                 uint64_t seed, int32_t n_iter, double tol, float *C_out, int32_t *assign, int32_t *counts,
+                 fk_fit_info *info, void *workspace, size_t workspace_bytes, void *stream) {
     g_err[0] = 0;
-    fk_status st = check_common(X, N, d, C_init, K, metric);
+    fk_status st = check_sizes(N, d, K);
     if (st != FK_OK) return st;
+    if ((st = check_metric(metric)) != FK_OK) return st;
     if ((st = check_score(score)) != FK_OK) return st;
     if (n_iter < 1) return fail(FK_ERR_INVALID_ARG, "n_iter=%d must be at least 1", (int)n_iter);
-    if (N > 0 && assign == nullptr) return fail(FK_ERR_INVALID_ARG, "assign is NULL");
+    if (C_init == nullptr && N < 1) return fail(FK_ERR_INVALID_ARG, "initial rows cannot be drawn from N=0 rows");
+    if (std::isnan(tol)) return fail(FK_ERR_INVALID_ARG, "tol is NaN");
+    if (N > 0 && (X == nullptr || assign == nullptr)) return fail(FK_ERR_INVALID_ARG, "X and assign are required");
     if (C_out == nullptr || counts == nullptr) return fail(FK_ERR_INVALID_ARG, "C_out and counts must not be NULL");
-    if (!aligned(C_out, 16)) return fail(FK_ERR_INVALID_ARG, "C_out must be 16-byte aligned");
-    const size_t cb = (size_t)K * d * 4;
-    if (overlap(C_out, cb, C_init, cb)) return fail(FK_ERR_INVALID_ARG, "C_out overlaps C_init");
-    const Layout L = make_layout(N, d, K, metric, false, kFitExtras);
+    if ((X != nullptr && !aligned(X, 16)) || (C_init != nullptr && !aligned(C_init, 16)) || !aligned(C_out, 16))
+        return fail(FK_ERR_INVALID_ARG, "X, C_init and C_out must be 16-byte aligned");
+    // the guide's clamp: no more clusters than rows when the rows are drawn
+    const int32_t Ku = C_init != nullptr ? K : (int32_t)(N < K ? N : K);
+    const size_t cb = (size_t)Ku * d * 4;
+    if (C_init != nullptr && overlap(C_out, cb, C_init, cb)) return fail(FK_ERR_INVALID_ARG, "C_out overlaps C_init");
+    const Layout L = make_layout(N, d, K, metric, false, kFitExtras);  // regions sized for K >= Ku
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
-    const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
-    return fit_steps(c, X, N, C_init, n_iter, C_out, assign, counts);
+    const hipStream_t s = (hipStream_t)stream;
+    const Ctx c{L, workspace, s, d, Ku, metric, score};
+    const float *cur = C_init;
+    if (cur == nullptr) {
+        const std::vector<int32_t> idx = sample_rows(N, Ku, seed);
+        int32_t *idx_dev = at<int32_t>(workspace, L.init_idx);
+        FK_TRY(hipMemcpyAsync(idx_dev, idx.data(), (size_t)Ku * 4, hipMemcpyHostToDevice, s), "initial row indices");
+        FK_TRY(hipStreamSynchronize(s), "stream sync");  // idx leaves scope
+        FK_TRY(launch_gather_rows(X, idx_dev, Ku, d, at<float>(workspace, L.cinit), s), "initial centroids");
+        cur = at<float>(workspace, L.cinit);
+    }
+    float *ctmp = at<float>(workspace, L.ctmp);
+    int32_t done = 0;
+    double last = -1.0;
+    for (int32_t i = 0; i < n_iter; ++i) {
+        // the buffers alternate so that a full run ends in C_out
+        float *next = ((n_iter - 1 - i) % 2 == 0) ? C_out : ctmp;
+        if ((st = lloyd_step(c, X, N, cur, assign, nullptr, next, counts)) != FK_OK) return st;
+        done = i + 1;
+        if (tol >= 0.0) {
+            FK_TRY(launch_max_shift(cur, next, Ku, d, at<double>(workspace, L.shift_part),
+                                    at<double>(workspace, L.shift), s),
+                   "centroid shift");
+            double h = 0.0;
+            FK_TRY(hipMemcpyAsync(&h, at<double>(workspace, L.shift), sizeof h, hipMemcpyDeviceToHost, s),
+                   "centroid shift copy");
+            FK_TRY(hipStreamSynchronize(s), "stream sync");
+            last = h;
+            cur = next;
+            if (h <= tol) break;
+        } else {
+            cur = next;
+        }
+    }
+    if (cur != C_out) FK_TRY(hipMemcpyAsync(C_out, cur, cb, hipMemcpyDeviceToDevice, s), "centroid copy");
+    if (info != nullptr) {
+        info->k_used = Ku;
+        info->iterations = done;
+        info->last_shift = last;
+    }
+    return FK_OK;
 }
 
 size_t fk_ivf_workspace_size(int64_t N, int32_t d, int32_t nlist, int32_t metric) {
-    if (N < 1 || N > INT32_MAX || d < 1 || d > FK_MAX_D || nlist < 1 || nlist > FK_MAX_K || nlist > N) return 0;
+    if (N < 1 || N > INT32_MAX || d < 1 || d > FK_MAX_D || nlist < 1 || nlist > FK_MAX_K) return 0;
     if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE) return 0;
-    return make_layout(N, d, nlist, metric, false, kIvfExtras).total;
+    const int32_t nl = (int32_t)(N < nlist ? N : nlist);
+    return make_layout(N, d, nl, metric, false, kIvfExtras).total;
 }
 
 fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int32_t metric, int32_t score,
-                       int32_t n_iter, const int32_t *init_idx_host, float *centroids, int32_t *list_offsets,
-                       int32_t *list_ids, float *list_data, void *workspace, size_t workspace_bytes, void *stream) {
+                       int32_t n_iter, const int32_t *init_idx_host, uint64_t seed, float *centroids,
+                       int32_t *list_offsets, int32_t *list_ids, float *list_data, int32_t *nlist_used,
+                       void *workspace, size_t workspace_bytes, void *stream) {
     g_err[0] = 0;
     fk_status st = check_sizes(N, d, nlist);
     if (st != FK_OK) return st;
     if ((st = check_metric(metric)) != FK_OK) return st;
-    if (metric == FK_METRIC_INNER_PRODUCT)
+    if (metric == FK_METRIC_INNER_PRODUCT || metric == FK_METRIC_SPHERICAL)
         return fail(FK_ERR_UNSUPPORTED, "the IVF build takes L2 or cosine (inner product: normalise, i.e. cosine)");
     if ((st = check_score(score)) != FK_OK) return st;
-    if (N < 1 || nlist > N) return fail(FK_ERR_INVALID_ARG, "need 1 <= nlist=%d <= N=%lld", (int)nlist, (long long)N);
+    if (N < 1) return fail(FK_ERR_INVALID_ARG, "the IVF build needs N >= 1 rows");
     if (n_iter < 1) return fail(FK_ERR_INVALID_ARG, "n_iter=%d must be at least 1", (int)n_iter);
-    if (X == nullptr || init_idx_host == nullptr || centroids == nullptr || list_offsets == nullptr ||
-        list_ids == nullptr || list_data == nullptr)
-        return fail(FK_ERR_INVALID_ARG, "X, init_idx, centroids, list_offsets, list_ids and list_data are required");
+    if (X == nullptr || centroids == nullptr || list_offsets == nullptr || list_ids == nullptr || list_data == nullptr)
+        return fail(FK_ERR_INVALID_ARG, "X, centroids, list_offsets, list_ids and list_data are required");
     if (!aligned(X, 16) || !aligned(centroids, 16) || !aligned(list_data, 16))
         return fail(FK_ERR_INVALID_ARG, "X, centroids and list_data must be 16-byte aligned");
-    for (int32_t k = 0; k < nlist; ++k)
-        if (init_idx_host[k] < 0 || init_idx_host[k] >= N)
-            return fail(FK_ERR_INVALID_ARG, "init_idx[%d]=%d outside [0, N)", (int)k, (int)init_idx_host[k]);
+    // the guide clamps the cell count to the row count
+    const int32_t nl = (int32_t)(N < nlist ? N : nlist);
+    if (init_idx_host != nullptr)
+        for (int32_t k = 0; k < nl; ++k)
+            if (init_idx_host[k] < 0 || init_idx_host[k] >= N)
+                return fail(FK_ERR_INVALID_ARG, "init_idx[%d]=%d outside [0, N)", (int)k, (int)init_idx_host[k]);
     const size_t xb = (size_t)N * d * 4;
     if (overlap(list_data, xb, X, xb)) return fail(FK_ERR_INVALID_ARG, "list_data overlaps X");
-    const Layout L = make_layout(N, d, nlist, metric, false, kIvfExtras);
+    const Layout L = make_layout(N, d, nl, metric, false, kIvfExtras);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
     const hipStream_t s = (hipStream_t)stream;
     // cosine: the lists hold the normalised rows and the quantizer is L2
     // k-means on them (normalising X and C on entry of every iteration would
     // train a different, spherical, quantizer)
-    const Ctx c{L, workspace, s, d, nlist, FK_METRIC_L2, score};
+    const Ctx c{L, workspace, s, d, nl, FK_METRIC_L2, score};
     const float *Xu = X;
     if (metric == FK_METRIC_COSINE) {
         PhaseScope ph(FK_PH_PREP, s);
@@ -758,9 +870,18 @@ fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int3
                "row normalisation");
         Xu = at<float>(workspace, L.xcopy);
     }
-    int32_t *idx_dev = at<int32_t>(workspace, L.labels);  // the labels buffer holds the indices first
-    FK_TRY(hipMemcpyAsync(idx_dev, init_idx_host, (size_t)nlist * 4, hipMemcpyHostToDevice, s), "init indices");
-    FK_TRY(launch_gather_rows(Xu, idx_dev, nlist, d, at<float>(workspace, L.cinit), s), "initial centroids");
+    int32_t *idx_dev = at<int32_t>(workspace, L.init_idx);
+    {
+        std::vector<int32_t> drawn;
+        const int32_t *idx_host = init_idx_host;
+        if (idx_host == nullptr) {
+            drawn = sample_rows(N, nl, seed);
+            idx_host = drawn.data();
+        }
+        FK_TRY(hipMemcpyAsync(idx_dev, idx_host, (size_t)nl * 4, hipMemcpyHostToDevice, s), "init indices");
+        FK_TRY(hipStreamSynchronize(s), "stream sync");  // the host indices may leave scope
+    }
+    FK_TRY(launch_gather_rows(Xu, idx_dev, nl, d, at<float>(workspace, L.cinit), s), "initial centroids");
     int32_t *labels = at<int32_t>(workspace, L.labels);
     int32_t *cnt = at<int32_t>(workspace, L.cnt);
     if ((st = fit_steps(c, Xu, N, at<float>(workspace, L.cinit), n_iter, centroids, labels, cnt)) != FK_OK) return st;
@@ -773,14 +894,16 @@ fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int3
         PhaseScope ph(FK_PH_REDUCE, s);
         FK_TRY(launch_gather_rows(Xu, list_ids, N, d, list_data, s), "list rows");
     }
+    if (nlist_used != nullptr) *nlist_used = nl;
     return FK_OK;
 }
 
 size_t fk_knn_workspace_size(int64_t M, int32_t d, int64_t Ndb, int32_t k, int32_t metric) {
-    if (M < 0 || M > INT32_MAX || d < 1 || d > FK_MAX_D || Ndb < 1 || Ndb > FK_MAX_KNN_DB) return 0;
-    if (k < 1 || k > FK_MAX_KNN_K || k > Ndb) return 0;
+    if (M < 0 || M > INT32_MAX || d < 1 || d > FK_MAX_D || Ndb < 1 || Ndb > FK_MAX_KNN_DB || k < 1) return 0;
+    const int32_t kk = (int32_t)(Ndb < k ? Ndb : k);
+    if (kk > FK_MAX_KNN_K) return 0;
     if (metric != FK_METRIC_L2 && metric != FK_METRIC_COSINE && metric != FK_METRIC_INNER_PRODUCT) return 0;
-    return make_knn_layout(M, d, Ndb, k, metric).total;
+    return make_knn_layout(M, d, Ndb, kk, metric).total;
 }
 
 fk_status fk_knn(const float *Q, int64_t M, int32_t d, const float *DB, int64_t Ndb, int32_t k, int32_t metric,
@@ -790,10 +913,15 @@ fk_status fk_knn(const float *Q, int64_t M, int32_t d, const float *DB, int64_t 
     if (d < 1 || d > FK_MAX_D) return fail(FK_ERR_INVALID_ARG, "d=%d outside [1, %d]", (int)d, FK_MAX_D);
     if (Ndb < 1 || Ndb > FK_MAX_KNN_DB)
         return fail(FK_ERR_INVALID_ARG, "Ndb=%lld outside [1, %d]", (long long)Ndb, FK_MAX_KNN_DB);
-    if (k < 1 || k > FK_MAX_KNN_K || k > Ndb)
-        return fail(FK_ERR_INVALID_ARG, "k=%d outside [1, min(%d, Ndb=%lld)]", (int)k, FK_MAX_KNN_K, (long long)Ndb);
+    // the backend clamps k to the database size; the columns past it are padding
+    const int32_t kk = (int32_t)(Ndb < k ? Ndb : k);
+    if (k < 1 || kk > FK_MAX_KNN_K)
+        return fail(FK_ERR_INVALID_ARG, "k=%d: need k >= 1 and min(k, Ndb=%lld) <= %d", (int)k, (long long)Ndb,
+                    FK_MAX_KNN_K);
     fk_status st = check_metric(metric);
     if (st != FK_OK) return st;
+    if (metric == FK_METRIC_SPHERICAL)
+        return fail(FK_ERR_UNSUPPORTED, "spherical is a centroid option; k-NN takes L2, cosine or inner product");
     if ((st = check_score(score)) != FK_OK) return st;
     if (DB == nullptr) return fail(FK_ERR_INVALID_ARG, "DB is NULL");
     if (M > 0 && (Q == nullptr || idx == nullptr || dist == nullptr))
@@ -804,7 +932,7 @@ fk_status fk_knn(const float *Q, int64_t M, int32_t d, const float *DB, int64_t 
         cdiv(Ndb, kCentroidPad) * kCentroidPad * 4 * (int64_t)split_width(d) > (int64_t)UINT32_MAX)
         return fail(FK_ERR_UNSUPPORTED, "split scoring: the database's bf16 copy (Ndb=%lld, d=%d) exceeds 4 GiB",
                     (long long)Ndb, (int)d);
-    const Layout L = make_knn_layout(M, d, Ndb, k, metric);
+    const Layout L = make_knn_layout(M, d, Ndb, kk, metric);
     if ((st = check_workspace(workspace, workspace_bytes, L.total)) != FK_OK) return st;
     if ((st = check_device()) != FK_OK) return st;
     if (M == 0) return FK_OK;
@@ -821,13 +949,13 @@ fk_status fk_knn(const float *Q, int64_t M, int32_t d, const float *DB, int64_t 
     {
         PhaseScope ph(FK_PH_ASSIGN, s);
         FK_TRY(launch_knn_sweep(Q, M, d, DBu, at<float>(workspace, L.ncn), (int)Ndb, at<float>(workspace, L.scal), qn,
-                                c.split(), ip, k, cand, cscore, win, at<float>(workspace, L.knn_tau), s),
+                                c.split(), ip, kk, cand, cscore, win, at<float>(workspace, L.knn_tau), s),
                "knn sweep");
     }
     {
         PhaseScope ph(FK_PH_RECHECK, s);
         FK_TRY(launch_knn_finish(Q, M, d, DB, cos ? at<double>(workspace, L.c64) : nullptr, qn, ip, cand, cscore, win,
-                                 k, (int)Ndb, list, counters, idx, dist, s),
+                                 kk, k, (int)Ndb, list, counters, idx, dist, s),
                "knn finish");
     }
     return FK_OK;

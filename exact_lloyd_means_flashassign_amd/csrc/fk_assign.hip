@@ -1799,12 +1799,17 @@ __global__ __launch_bounds__(256) void k_knn_finish(const float *__restrict__ Q,
                                                     const CT *__restrict__ DB, const double *__restrict__ qnorm64,
                                                     int ip, const int32_t *__restrict__ cand,
                                                     const float *__restrict__ score, const float *__restrict__ win,
-                                                    int S, int k, int Ndb, int32_t *__restrict__ list,
+                                                    int S, int k, int ld, int Ndb, int32_t *__restrict__ list,
                                                     int32_t *__restrict__ counter, int32_t *__restrict__ idx,
                                                     float *__restrict__ dist) {
 #pragma clang fp contract(off)
     const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     if (q >= M) return;
+    // columns past the database size (k clamped to Ndb): no row
+    for (int r = k; r < ld; ++r) {
+        idx[q * ld + r] = -1;
+        dist[q * ld + r] = INFINITY;
+    }
     float V[TL];
     int I[TL];
 #pragma unroll
@@ -1867,8 +1872,8 @@ __global__ __launch_bounds__(256) void k_knn_finish(const float *__restrict__ Q,
             bi = t ? I[j] : bi;
             bj = t ? j : bj;
         }
-        idx[q * k + r] = bi;
-        dist[q * k + r] = (float)b;
+        idx[q * ld + r] = bi;
+        dist[q * ld + r] = (float)b;
 #pragma unroll
         for (int j = 0; j < TL; ++j) D[j] = (j == bj) ? (double)INFINITY : D[j];
 #pragma unroll
@@ -1884,7 +1889,7 @@ template <typename CT>
 __global__ __launch_bounds__(256) void k_knn_full(const float *__restrict__ Q, int d, const CT *__restrict__ DB,
                                                   int Ndb, const double *__restrict__ qnorm64, int ip,
                                                   const int32_t *__restrict__ list,
-                                                  const int32_t *__restrict__ counters, int k,
+                                                  const int32_t *__restrict__ counters, int k, int ld,
                                                   int32_t *__restrict__ idx, float *__restrict__ dist) {
 #pragma clang fp contract(off)
     __shared__ double wd[4];
@@ -1950,8 +1955,8 @@ __global__ __launch_bounds__(256) void k_knn_full(const float *__restrict__ Q, i
                         bbi = wi[ww];
                         btt = wt[ww];
                     }
-                idx[q * k + r] = bbi;
-                dist[q * k + r] = (float)bb;
+                idx[q * ld + r] = bbi;
+                dist[q * ld + r] = (float)bb;
                 win_t = btt;
             }
             __syncthreads();
@@ -1972,15 +1977,16 @@ __global__ __launch_bounds__(256) void k_knn_full(const float *__restrict__ Q, i
 
 hipError_t launch_knn_finish(const float *Q, int64_t M, int d, const float *DB32, const double *DB64,
                              const double *qnorm64, bool ip, const int32_t *cand, const float *score,
-                             const float *win, int k, int Ndb, int32_t *list, int32_t *counters, int32_t *idx,
+                             const float *win, int k, int ld, int Ndb, int32_t *list, int32_t *counters, int32_t *idx,
                              float *dist, hipStream_t s) {
     if (M <= 0) return hipSuccess;
+    if (ld < k) return hipErrorInvalidValue;
     const unsigned nb = (unsigned)cdiv(M, 256);
     const int ipi = ip ? 1 : 0;
     const int S = knn_slices(M, Ndb).slices;
 #define FK_KNN_FINISH(CT, TLV, DBP)                                                                              \
     hipLaunchKernelGGL((k_knn_finish<CT, TLV>), dim3(nb), dim3(256), 0, s, Q, M, d, DBP, qnorm64, ipi, cand, score, \
-                       win, S, k, Ndb, list, counters, idx, dist)
+                       win, S, k, ld, Ndb, list, counters, idx, dist)
     if (knn_list_len(k) == 16) {
         if (DB64 != nullptr)
             FK_KNN_FINISH(double, 16, DB64);
@@ -1998,10 +2004,10 @@ hipError_t launch_knn_finish(const float *Q, int64_t M, int d, const float *DB32
     const int64_t nf = M < 4096 ? M : 4096;
     if (DB64 != nullptr)
         hipLaunchKernelGGL(k_knn_full<double>, dim3((unsigned)nf), dim3(256), 0, s, Q, d, DB64, Ndb, qnorm64, ipi,
-                           list, counters, k, idx, dist);
+                           list, counters, k, ld, idx, dist);
     else
         hipLaunchKernelGGL(k_knn_full<float>, dim3((unsigned)nf), dim3(256), 0, s, Q, d, DB32, Ndb, qnorm64, ipi,
-                           list, counters, k, idx, dist);
+                           list, counters, k, ld, idx, dist);
     return hipGetLastError();
 }
 

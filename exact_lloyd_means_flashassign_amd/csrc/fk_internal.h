@@ -132,6 +132,11 @@ hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, 
 // counts from the offsets, previous centroids for the empty clusters
 hipError_t launch_counts_keep(const int32_t *offsets, int K, int d, const float *C_prev, float *C_out,
                               int32_t *counts_out, hipStream_t s);
+// every row of C[K, d] divided by its L2 norm (fp64, a zero norm taken as 1):
+// the spherical centroids
+hipError_t launch_unit_rows(float *C, int K, int d, hipStream_t s);
+// *shift = max_k sum_j (b[k,j] - a[k,j])^2 in fp64 (part: cdiv(K, 4) doubles)
+hipError_t launch_max_shift(const float *a, const float *b, int K, int d, double *part, double *shift, hipStream_t s);
 // counts from cnt, C_out = sums / count (C_prev for an empty cluster)
 hipError_t launch_finalize(const double *sums, const int32_t *cnt, const float *C_prev, int K, int d, float *C_out,
                            int32_t *counts_out, hipStream_t s);
@@ -155,9 +160,10 @@ KnnSlices knn_slices(int64_t M, int64_t Ndb);
 hipError_t launch_knn_sweep(const float *Q, int64_t M, int d, const float *DB, const float *ncn, int Ndb,
                             const float *scal, const double *qnorm64, const SplitC &sc, bool ip, int k,
                             int32_t *cand, float *score, float *win, float *tau, hipStream_t s);
+// idx and dist rows are ld >= k entries long; entries k..ld-1 get -1 and +inf
 hipError_t launch_knn_finish(const float *Q, int64_t M, int d, const float *DB32, const double *DB64,
                              const double *qnorm64, bool ip, const int32_t *cand, const float *score,
-                             const float *win, int k, int Ndb, int32_t *list, int32_t *counters, int32_t *idx,
+                             const float *win, int k, int ld, int Ndb, int32_t *list, int32_t *counters, int32_t *idx,
                              float *dist, hipStream_t s);
 
 }  // namespace fk

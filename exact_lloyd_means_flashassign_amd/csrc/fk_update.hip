@@ -350,6 +350,71 @@ hipError_t noalloc_scratch(int device, void **ptr) {
     return hipSuccess;
 }
 
+// Spherical centroids: every row of C divided by its L2 norm, the norm taken
+// in fp64 (a zero norm is taken as 1, so a zero row stays zero).  One wave
+// per row.
+__global__ __launch_bounds__(256) void k_unit_rows(float *__restrict__ C, int K, int d) {
+    const int k = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (k >= K) return;
+    float *row = C + (size_t)k * d;
+    double q = 0.0;
+    for (int j = lane; j < d; j += 64) {
+        const double v = (double)row[j];
+        q += v * v;
+    }
+    for (int off = 32; off > 0; off >>= 1) q += __shfl_xor(q, off);
+    double n = sqrt(q);
+    if (n == 0.0) n = 1.0;
+    for (int j = lane; j < d; j += 64) row[j] = (float)((double)row[j] / n);
+}
+
+hipError_t launch_unit_rows(float *C, int K, int d, hipStream_t s) {
+    if (K <= 0) return hipSuccess;
+    hipLaunchKernelGGL(k_unit_rows, dim3((unsigned)cdiv(K, 4)), dim3(256), 0, s, C, K, d);
+    return hipGetLastError();
+}
+
+// The fit's stopping measure: part[block] = the largest sum_j (b - a)^2 (fp64)
+// over the block's four rows (one wave per row), then one workgroup takes the
+// maximum over the blocks (max is exact, so the order does not matter).
+__global__ __launch_bounds__(256) void k_row_shift(const float *__restrict__ a, const float *__restrict__ b, int K,
+                                                   int d, double *__restrict__ part) {
+    __shared__ double wm[4];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int k = blockIdx.x * 4 + w;
+    double q = 0.0;
+    if (k < K) {
+        for (int j = lane; j < d; j += 64) {
+            const double t = (double)b[(size_t)k * d + j] - (double)a[(size_t)k * d + j];
+            q += t * t;
+        }
+        for (int off = 32; off > 0; off >>= 1) q += __shfl_xor(q, off);
+    }
+    if (lane == 0) wm[w] = q;
+    __syncthreads();
+    if (threadIdx.x == 0) part[blockIdx.x] = fmax(fmax(wm[0], wm[1]), fmax(wm[2], wm[3]));
+}
+
+__global__ __launch_bounds__(256) void k_max_of(const double *__restrict__ part, int n, double *__restrict__ out) {
+    __shared__ double sm[256];
+    double m = 0.0;
+    for (int i = threadIdx.x; i < n; i += 256) m = fmax(m, part[i]);
+    sm[threadIdx.x] = m;
+    __syncthreads();
+    for (int o = 128; o > 0; o >>= 1) {
+        if ((int)threadIdx.x < o) sm[threadIdx.x] = fmax(sm[threadIdx.x], sm[threadIdx.x + o]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) *out = sm[0];
+}
+
+hipError_t launch_max_shift(const float *a, const float *b, int K, int d, double *part, double *shift, hipStream_t s) {
+    const int nb = (int)cdiv(K, 4);
+    hipLaunchKernelGGL(k_row_shift, dim3((unsigned)nb), dim3(256), 0, s, a, b, K, d, part);
+    hipLaunchKernelGGL(k_max_of, dim3(1), dim3(256), 0, s, part, nb, shift);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
     const int64_t n = (int64_t)(bytes / 4);
     if (n <= 0) return hipSuccess;

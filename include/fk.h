@@ -21,7 +21,11 @@
  * (LEANN FlashLib backend guide, mhpn.cn, paragraph "distance metric").
  * Inner product assigns each point to the centroid of largest x.c (lowest
  * index on ties, the dot product taken in fp64 in increasing j where it is
- * settled) and updates with plain means; its min_dist is -max_k x.c.  The
+ * settled) and updates with plain means; its min_dist is -max_k x.c.
+ * Spherical is the explicit spherical-centroid option beside cosine: points
+ * are assigned as for cosine, and every returned centroid (an empty
+ * cluster's kept one too) is divided by its L2 norm (fp64, a zero norm taken
+ * as 1), so chained iterations are spherical k-means.  The
  * out-of-core entry point follows the article's out-of-core mode, which keeps
  * the data in host memory and computes on the GPU (section "Real-time MoE
  * routing").
@@ -80,7 +84,8 @@ typedef enum {
 typedef enum {
     FK_METRIC_L2 = 0,            /* squared Euclidean distance                 */
     FK_METRIC_COSINE = 1,        /* L2 on rows normalised to unit length       */
-    FK_METRIC_INNER_PRODUCT = 2  /* largest x.c (no normalisation)             */
+    FK_METRIC_INNER_PRODUCT = 2, /* largest x.c (no normalisation)             */
+    FK_METRIC_SPHERICAL = 3      /* cosine assignment, unit-length centroids   */
 } fk_metric;
 
 /*
@@ -197,44 +202,73 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
                                void *stream);
 
 /*
- * Lloyd k-means: n_iter >= 1 iterations of fk_lloyd_iter starting from
- * C_init (the plain iteration of the Flash-KMeans article, repeated; the
- * LEANN FlashLib guide, paragraph "parameters", trains its IVF quantizer with
- * niter = 20 such iterations).  C_out receives the centroids after the last
- * iteration, assign the last iteration's assignment (under the centroids
- * before it) and counts its cluster sizes.  Workspace:
- * fk_fit_workspace_size() bytes (it also holds the intermediate centroids).
- * C_out must not overlap C_init.  Device pointers; errors as fk_lloyd_iter,
- * plus FK_ERR_INVALID_ARG for n_iter < 1.
+ * Lloyd k-means: up to n_iter >= 1 iterations of fk_lloyd_iter (the plain
+ * iteration of the Flash-KMeans article, repeated; the LEANN FlashLib guide,
+ * paragraph "parameters", trains its IVF quantizer with niter = 20 such
+ * iterations and a seed).
+ *   Start: from C_init[K, d] (device) when it is not NULL (K > N is then
+ *   accepted: some clusters stay empty).  With C_init NULL the guide's
+ *   clamp K' = min(K, N) applies (paragraph "nlist and nprobe"), N >= 1, and
+ *   the initial centroids are K' rows of X drawn with `seed`: the first K'
+ *   positions of a Fisher-Yates shuffle of 0..N-1 (step i swaps position i
+ *   with position i + r, r uniform in [0, N - i)), r taken from SplitMix64
+ *   (Steele, Lea and Flood 2014; state += 0x9E3779B97F4A7C15, output mixed
+ *   with shifts 30/27/31 and multipliers 0xBF58476D1CE4E5B9,
+ *   0x94D049BB133111EB) by rejecting draws at or above the largest multiple
+ *   of N - i below 2^64 and reducing the rest modulo N - i.
+ *   Stop: tol < 0 runs exactly n_iter iterations and the call only enqueues
+ *   work.  tol >= 0 also stops after the first iteration whose largest
+ *   squared centroid move, sum_j (c_new - c_old)^2 in fp64 over the fp32
+ *   centroids, is at most tol (tol = 0: a fixed point, after which further
+ *   iterations would change nothing); the call then waits for `stream` after
+ *   every iteration.
+ * C_out[0..K') receives the centroids after the last iteration, assign the
+ * last iteration's assignment (under the centroids before it) and
+ * counts[0..K') its cluster sizes.  info (host memory, may be NULL) receives
+ * K', the iterations run and the last measured move (-1 when tol < 0).
+ * Workspace: fk_fit_workspace_size() bytes.  C_out must not overlap C_init.
+ * Device pointers except info; errors as fk_lloyd_iter, plus
+ * FK_ERR_INVALID_ARG for n_iter < 1 or a draw from N = 0 rows.
  */
+typedef struct {
+    int32_t k_used;      /* clusters fitted: K, or min(K, N) when rows were drawn */
+    int32_t iterations;  /* iterations run                                      */
+    double last_shift;   /* largest squared centroid move of the last one (-1
+                            when tol < 0: not measured)                         */
+} fk_fit_info;
 size_t fk_fit_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric);
-fk_status fk_fit(const float *X, int64_t N, int32_t d, const float *C_init, int32_t K, int32_t metric, int32_t score,
-                 int32_t n_iter, float *C_out, int32_t *assign, int32_t *counts, void *workspace,
-                 size_t workspace_bytes, void *stream);
+fk_status fk_fit(const float *X, int64_t N, int32_t d, int32_t K, int32_t metric, int32_t score, const float *C_init,
+                 uint64_t seed, int32_t n_iter, double tol, float *C_out, int32_t *assign, int32_t *counts,
+                 fk_fit_info *info, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * IVF-Flat index build (LEANN FlashLib guide, paragraphs "how it works",
- * "parameters"): a coarse quantizer of nlist centroids trained by n_iter
- * Lloyd iterations from the rows init_idx_host[0..nlist) of X, then every row
- * assigned to its nearest final centroid and the rows grouped by cell:
- *   centroids[nlist, d]      the quantizer (fp32),
- *   list_offsets[nlist + 1]  CSR offsets: cell k holds list positions
+ * "parameters", "nlist and nprobe"): nl = min(nlist, N) cells (the guide's
+ * clamp); a coarse quantizer of nl centroids trained by n_iter Lloyd
+ * iterations from the rows init_idx_host[0..nl) of X, or, when
+ * init_idx_host is NULL, from nl rows drawn with `seed` as fk_fit draws
+ * them; then every row assigned to its nearest final centroid and the rows
+ * grouped by cell:
+ *   centroids[nl, d]         the quantizer (fp32),
+ *   list_offsets[nl + 1]     CSR offsets: cell k holds list positions
  *                            [list_offsets[k], list_offsets[k+1]),
  *   list_ids[N]              the row of X at each list position (increasing
  *                            within a cell),
  *   list_data[N, d]          those rows, cell-contiguous.
- * metric COSINE L2-normalises the rows first (zero norm taken as 1), trains
- * plain L2 k-means on them and stores the normalised rows; L2 uses X as is.
- * Requires 1 <= nlist <= N (the guide clamps nlist to N; the Python binding
- * does that).  init_idx_host is HOST memory (nlist int32 row indices, each
- * checked to lie in [0, N)); every other pointer is device memory.  Workspace:
- * fk_ivf_workspace_size() bytes.  list_data must not overlap X.  The
- * assignments are exact in the sense of fk_assign.
+ * Buffers sized for nlist rows are large enough.  metric COSINE
+ * L2-normalises the rows first (zero norm taken as 1), trains plain L2
+ * k-means on them and stores the normalised rows; L2 uses X as is; inner
+ * product and spherical give FK_ERR_UNSUPPORTED.  Requires N >= 1.
+ * init_idx_host (nl int32 row indices, each checked to lie in [0, N)) and
+ * nlist_used (receives nl; may be NULL) are HOST memory; every other pointer
+ * is device memory.  Workspace: fk_ivf_workspace_size() bytes.  list_data
+ * must not overlap X.  The assignments are exact in the sense of fk_assign.
  */
 size_t fk_ivf_workspace_size(int64_t N, int32_t d, int32_t nlist, int32_t metric);
 fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int32_t metric, int32_t score,
-                       int32_t n_iter, const int32_t *init_idx_host, float *centroids, int32_t *list_offsets,
-                       int32_t *list_ids, float *list_data, void *workspace, size_t workspace_bytes, void *stream);
+                       int32_t n_iter, const int32_t *init_idx_host, uint64_t seed, float *centroids,
+                       int32_t *list_offsets, int32_t *list_ids, float *list_data, int32_t *nlist_used,
+                       void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * Exact k nearest neighbours by brute force (flash-knn, the exact GPU k-NN
@@ -251,11 +285,14 @@ fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int3
  * among those L whenever the k-th score beats the L-th by more than twice the
  * score error bound (as for fk_assign); the L candidates are then ranked in
  * fp64.  The other queries are ranked against every database row in fp64.
- * Limits: 0 <= M <= 2^31-1, 1 <= Ndb <= FK_MAX_KNN_DB,
- * 1 <= k <= min(FK_MAX_KNN_K, Ndb); FK_SCORE_SPLIT_BF16 also needs the
- * database's bf16 copy (about 4 Ndb d bytes: Ndb rounded up to 128, d up to
- * 16, 32, 64, 128 or a multiple of 64) under 4 GiB, else FK_ERR_UNSUPPORTED.
- * Q, DB, idx[M,k] (int32) and dist[M,k] (fp32) are device pointers; workspace:
+ * The backend clamps k to the database size: with k > Ndb, idx[q, Ndb..k)
+ * = -1 and dist[q, Ndb..k) = +inf.  Limits: 0 <= M <= 2^31-1,
+ * 1 <= Ndb <= FK_MAX_KNN_DB, k >= 1 and min(k, Ndb) <= FK_MAX_KNN_K; metric
+ * L2, COSINE or INNER_PRODUCT (SPHERICAL, a centroid option, gives
+ * FK_ERR_UNSUPPORTED); FK_SCORE_SPLIT_BF16 also needs the database's bf16
+ * copy (about 4 Ndb d bytes: Ndb rounded up to 128, d up to 16, 32, 64, 128
+ * or a multiple of 64) under 4 GiB, else FK_ERR_UNSUPPORTED.  Q, DB,
+ * idx[M,k] (int32) and dist[M,k] (fp32) are device pointers; workspace:
  * fk_knn_workspace_size() bytes.
  */
 size_t fk_knn_workspace_size(int64_t M, int32_t d, int64_t Ndb, int32_t k, int32_t metric);

@@ -51,7 +51,8 @@ def test_workspace_sizes(lib):
     for bad in [(-1, 16, 4), (10, 0, 4), (10, 16, 0), (10, 16, 65537), (10, 4097, 4), (2 ** 31, 4, 4)]:
         assert lib.fk_workspace_size(*bad, 0, 0) == 0
     assert lib.fk_workspace_size(10, 4, 4, 2, 0) > 0             # inner product
-    assert lib.fk_workspace_size(10, 4, 4, 3, 0) == 0            # no such metric
+    assert lib.fk_workspace_size(10, 4, 4, 3, 0) > 0             # spherical
+    assert lib.fk_workspace_size(10, 4, 4, 4, 0) == 0            # no such metric
 
 
 P = ctypes.c_void_p
@@ -135,29 +136,33 @@ def test_profile_api_without_device(lib):
 
 def test_fit_and_ivf_validation(lib):
     ws = _fake(0x1000000)
-    # fk_fit: n_iter < 1, aliasing of C_out and C_init
-    st = lib.fk_fit(_fake(0x10000), 100, 8, _fake(0x20000), 4, 0, 0, 0, _fake(0x30000), _fake(0x40000),
-                    _fake(0x50000), ws, 1 << 30, None)
-    assert st == INVALID and b"n_iter" in lib.fk_last_error()
-    st = lib.fk_fit(_fake(0x10000), 100, 8, _fake(0x20000), 4, 0, 0, 3, _fake(0x20000 + 16), _fake(0x40000),
-                    _fake(0x50000), ws, 1 << 30, None)
-    assert st == INVALID and b"overlaps" in lib.fk_last_error()
+    info = fk._FitInfo()
+
+    def fit(N=100, K=4, C_init=_fake(0x20000), n_iter=3, tol=-1.0, C_out=_fake(0x30000), metric=0):
+        return lib.fk_fit(_fake(0x10000), N, 8, K, metric, 0, C_init, 0, n_iter, tol, C_out, _fake(0x40000),
+                          _fake(0x50000), ctypes.byref(info), ws, 1 << 30, None)
+    # n_iter < 1, aliasing of C_out and C_init, a draw from no rows, NaN tol, unknown metric
+    assert fit(n_iter=0) == INVALID and b"n_iter" in lib.fk_last_error()
+    assert fit(C_out=_fake(0x20000 + 16)) == INVALID and b"overlaps" in lib.fk_last_error()
+    assert fit(N=0, C_init=None) == INVALID and b"N=0" in lib.fk_last_error()
+    assert fit(tol=float("nan")) == INVALID and b"NaN" in lib.fk_last_error()
+    assert fit(metric=4) == INVALID
     assert fk.fk_fit_workspace_size(1000, 16, 10) > fk.fk_workspace_size(1000, 16, 10)
-    # fk_ivf_build: nlist > N, an initial index out of range, n_iter < 1
+    assert fk.fk_fit_workspace_size(1000, 16, 10, "spherical") > 0
+    # fk_ivf_build: an initial index out of range, n_iter < 1, no rows, unsupported metrics
     idx = (ctypes.c_int32 * 4)(0, 1, 2, 99)
     args = dict(X=_fake(0x10000), cent=_fake(0x20000), offs=_fake(0x30000), ids=_fake(0x40000), data=_fake(0x800000))
 
-    def ivf(N, nlist, n_iter, init):
-        return lib.fk_ivf_build(args["X"], N, 8, nlist, 0, 0, n_iter, init, args["cent"], args["offs"], args["ids"],
-                                args["data"], ws, 1 << 30, None)
-    assert ivf(3, 4, 2, idx) == INVALID
+    def ivf(N, nlist, n_iter, init, metric=0):
+        return lib.fk_ivf_build(args["X"], N, 8, nlist, metric, 0, n_iter, init, 0, args["cent"], args["offs"],
+                                args["ids"], args["data"], None, ws, 1 << 30, None)
     assert ivf(50, 4, 2, idx) == INVALID and b"init_idx[3]" in lib.fk_last_error()
     assert ivf(500, 4, 0, idx) == INVALID and b"n_iter" in lib.fk_last_error()
-    assert ivf(500, 4, 2, None) == INVALID
-    st = lib.fk_ivf_build(args["X"], 500, 8, 4, 2, 0, 2, idx, args["cent"], args["offs"], args["ids"], args["data"],
-                          ws, 1 << 30, None)
-    assert st == UNSUPPORTED and b"inner product" in lib.fk_last_error()
-    assert lib.fk_ivf_workspace_size(10, 8, 11, 0) == 0
+    assert ivf(0, 4, 2, None) == INVALID and b"N >= 1" in lib.fk_last_error()
+    assert ivf(500, 4, 2, idx, metric=2) == UNSUPPORTED and b"inner product" in lib.fk_last_error()
+    assert ivf(500, 4, 2, idx, metric=3) == UNSUPPORTED
+    assert lib.fk_ivf_workspace_size(10, 8, 11, 0) == lib.fk_ivf_workspace_size(10, 8, 10, 0) > 0
+    assert lib.fk_ivf_workspace_size(0, 8, 11, 0) == 0
     assert fk.fk_ivf_workspace_size(1000, 16, 10, "cosine") > fk.fk_ivf_workspace_size(1000, 16, 10)
 
 
@@ -169,18 +174,20 @@ def test_knn_validation(lib):
         return lib.fk_knn(q, M, d, db, Ndb, k, metric, score, idx, dist, ws, wsb, None)
     assert knn(k=0) == INVALID
     assert knn(k=25) == INVALID and b"k=25" in lib.fk_last_error()
-    assert knn(Ndb=4, k=5) == INVALID
     assert knn(Ndb=0) == INVALID
     assert knn(d=0) == INVALID
     assert knn(M=-1) == INVALID
-    assert knn(metric=3) == INVALID
+    assert knn(metric=4) == INVALID
+    assert knn(metric=3) == UNSUPPORTED and b"spherical" in lib.fk_last_error()
     assert knn(score=2) == INVALID
     assert knn(q=None) == INVALID
     assert knn(db=_fake(0x20004)) == INVALID and b"aligned" in lib.fk_last_error()
     assert knn(wsb=16) == WORKSPACE
     # the split copy of a 2^22 x 512 database is 8 GiB: beyond a buffer resource
     assert knn(d=512, Ndb=1 << 22, score=1) == UNSUPPORTED and b"4 GiB" in lib.fk_last_error()
-    assert lib.fk_knn_workspace_size(10, 8, 4, 5, 0) == 0
+    # k above the database size is clamped; k above the limit with a big database is not
+    assert lib.fk_knn_workspace_size(10, 8, 4, 5, 0) == lib.fk_knn_workspace_size(10, 8, 4, 4, 0) > 0
+    assert lib.fk_knn_workspace_size(10, 8, 4, 60, 0) > 0
     assert lib.fk_knn_workspace_size(10, 8, 100, 25, 0) == 0
     a = fk.fk_knn_workspace_size(10000, 128, 1 << 20, 10)
     assert a > (1 << 20) * 128 * 4                # the database's bf16 copy

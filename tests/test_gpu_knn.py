@@ -21,7 +21,7 @@ SCORES = ["fp32", "split_bf16"]
 
 def _check(fk, Q, DB, k, metric, score):
     idx, dist = fk.fk_knn(dev(Q), dev(DB), k, metric=metric, score=score)
-    i_ref, d_ref = oracle.knn(Q, DB, min(k, DB.shape[0]), metric)
+    i_ref, d_ref = oracle.knn(Q, DB, k, metric)
     gi, gd = host(idx), host(dist)
     np.testing.assert_array_equal(gi, i_ref)
     np.testing.assert_array_equal(gd, d_ref.astype(np.float32))
@@ -91,9 +91,14 @@ def test_knn_empty_queries_and_clamped_k(gpu_lib):
     idx, dist = gpu_lib.fk_knn(dev(np.zeros((0, 16), np.float32)), dev(DB), 5)
     assert tuple(idx.shape) == (0, 5) and tuple(dist.shape) == (0, 5)
     Q = np.random.default_rng(4).standard_normal((9, 16)).astype(np.float32)
-    idx, dist = gpu_lib.fk_knn(dev(Q), dev(DB), 10)   # k clamped to Ndb = 7
-    assert tuple(idx.shape) == (9, 7)
-    _check(gpu_lib, Q, DB, 7, "l2", "fp32")
+    idx, dist = gpu_lib.fk_knn(dev(Q), dev(DB), 10)   # k clamped to Ndb = 7 in the library
+    assert tuple(idx.shape) == (9, 10)
+    assert (host(idx)[:, 7:] == -1).all() and np.isinf(host(dist)[:, 7:]).all()
+    _check(gpu_lib, Q, DB, 10, "l2", "fp32")
+    _check(gpu_lib, Q, DB, 10, "cosine", "split_bf16")
+    DB1 = DB[:1]
+    _check(gpu_lib, Q, DB1, 24, "inner_product", "fp32")
+    _check(gpu_lib, Q, DB1, 60, "l2", "split_bf16")  # k beyond the limit, but Ndb = 1
 
 
 def test_knn_repeatable_and_workspace_reuse(gpu_lib):

@@ -267,7 +267,7 @@ def test_error_paths_on_device(gpu_lib):
     X = torch.zeros((100, 8), device="cuda:0")
     C = torch.zeros((4, 8), device="cuda:0")
     with pytest.raises(fk.FkError) as e:
-        fk.fk_assign(X, C, metric=3)
+        fk.fk_assign(X, C, metric=4)
     assert e.value.status == 1
     with pytest.raises(fk.FkError) as e:
         fk.fk_ivf_build(X, 4, np.arange(4, dtype=np.int32), metric="inner_product")
