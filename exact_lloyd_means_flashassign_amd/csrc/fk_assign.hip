@@ -317,6 +317,12 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     // the cross terms in a second accumulator instead (the phases would span
     // chunks).
     constexpr bool PHASED = SPLIT && RES;
+    // Split scoring on streamed chunks (no candidate lists) sums all three
+    // products in the one accumulator: every partial sum then holds up to
+    // 3d + 1 terms, so the error bound takes (3d + 4) u in place of (d + 4) u
+    // (the window is three times wider), and the 64 registers of a second
+    // accumulator go, which leaves room for two waves per SIMD.
+    constexpr bool ONEACC = SPLIT && !RES && TL == 0;
     // Streamed chunks fetch the next stage's points a stage ahead, except
     // beside 32-long candidate lists (no registers left for them there: the
     // points are loaded at the start of their own stage).
@@ -325,7 +331,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     // values are fetched two stages ahead and split during the stage before
     // their own, alongside its products (not beside candidate lists: the
     // registers are not there).
-    constexpr bool PRE2 = PRE && SPLIT && TL == 0;
+    constexpr bool PRE2 = PRE && SPLIT && TL == 0 && !ONEACC;
     // top-L lists that may start from a threshold (the 16-long lists beside
     // streamed d-chunks never do: that sweep runs without the threshold pass)
     constexpr bool TAU = TL > 0 && (RES || TL > 16);
@@ -622,7 +628,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         // the fp32 (or hi.hi) products; the split cross terms, below 2^-7 of
         // the products in size, pass through at most 2d + 1 and add less than
         // 0.016 (2d + 1) u ||x|| ||c||, which the 1.0625 factor covers
-        const float g = (float)(d + 4) * u + (A.xnorm64 != nullptr ? 8.f * u : 0.f);
+        const float g = (float)(ONEACC ? 3 * d + 4 : d + 4) * u + (A.xnorm64 != nullptr ? 8.f * u : 0.f);
         auto point_bounds = [&]() {
             const float M = A.scal[0] * (1.f + g);
             const float sqM = sqrtf(M) * (1.f + 2.f * u);
@@ -660,7 +666,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         // phased split scoring computes its centroid blocks one after another
         // (each with its epilogue), so one accumulator per point block serves
         v16f acc[PB][PHASED ? 1 : CB];
-        v16f acl[PB][SPLIT && !PHASED ? CB : 1];
+        v16f acl[PB][SPLIT && !PHASED && !ONEACC ? CB : 1];
 
         // Fold one 32-centroid block of scores (a) of point block b, centroid
         // indices kb + 8(r/4) + r%4, into this lane's state.
@@ -803,7 +809,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                             acc[b][cb][4 * q + 1] = nv.y;
                             acc[b][cb][4 * q + 2] = nv.z;
                             acc[b][cb][4 * q + 3] = nv.w;
-                            if constexpr (SPLIT)
+                            if constexpr (SPLIT && !ONEACC)
                                 for (int e = 0; e < 4; ++e) acl[b][cb][4 * q + e] = 0.f;
                         }
                     }
@@ -874,6 +880,25 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     // done, so the prefetch registers are free for the rest
                     if (CB > 1 && cb == 0 && more) store_stage(buf ^ 1, nc);
                 }
+            } else if constexpr (ONEACC) {
+                // x.c ~ hi.lo + lo.hi + hi.hi, one 32-centroid block after
+                // another (only one block's operands live at a time)
+                const __bf16 *sh = &sCh[buf][jl * LDB + 8 * h];
+                const __bf16 *sl = &sCl[buf][jl * LDB + 8 * h];
+#pragma unroll
+                for (int cb = 0; cb < CB; ++cb) {
+#pragma unroll
+                    for (int st = 0; st < NS; ++st) {
+                        const v8bf ah = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB + 16 * st);
+                        const v8bf al = *reinterpret_cast<const v8bf *>(sl + cb * 32 * LDB + 16 * st);
+#pragma unroll
+                        for (int b = 0; b < PB; ++b) {
+                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al, xh[b][st], acc[b][cb], 0, 0, 0);
+                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xl[b][st], acc[b][cb], 0, 0, 0);
+                            acc[b][cb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah, xh[b][st], acc[b][cb], 0, 0, 0);
+                        }
+                    }
+                }
             } else if constexpr (SPLIT) {
                 // x.c ~ hi.hi + (hi.lo + lo.hi)
                 const __bf16 *sh = &sCh[buf][jl * LDB + 8 * h];
@@ -933,7 +958,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     for (int b = 0; b < PB; ++b) {
 #pragma unroll
                         for (int cb = 0; cb < CB; ++cb) {
-                            if constexpr (SPLIT) acc[b][cb] += acl[b][cb];
+                            if constexpr (SPLIT && !ONEACC) acc[b][cb] += acl[b][cb];
                             epilogue(acc[b][cb], b, t * ROWS + cb * 32 + 4 * h);
                         }
                     }
@@ -1578,7 +1603,7 @@ static hipError_t launch_fa_shape(const FlashArgs &A, hipStream_t s) {
         // scoring at that height needs more than 256 registers: one wave per
         // SIMD, accumulators in AGPRs, rather than spilling.
         if constexpr (SPLIT)
-            return launch_fa<64, 1, 4, 4, 1, false, COLLECT, SPLIT>(A, s);
+            return launch_fa<32, 1, 4, 8, 2, false, COLLECT, SPLIT>(A, s);
         else
             return launch_fa<64, 1, 4, 4, 2, false, COLLECT, SPLIT>(A, s);
     }
