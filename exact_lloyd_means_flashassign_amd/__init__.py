@@ -7,9 +7,9 @@ of the computation runs in the HIP kernels of ``libfk.so``; torch is used only
 for device memory and streams.  If ``libfk.so`` has not been built, ``load()``
 raises -- there is no fallback path.
 
-The workspace is cached per device and reused by every call that does not pass
-its own ``workspace``; calls that may overlap on different streams must each
-pass their own.
+The workspace is cached per (device, stream) and reused by every call on that
+stream that does not pass its own ``workspace`` (calls on one stream run in
+order, so they may share it).
 """
 from __future__ import annotations
 
@@ -175,7 +175,8 @@ def _workspace(nbytes: int, device, workspace=None):
     if workspace is not None:
         _dev(workspace, "workspace", torch.uint8)
         return workspace.data_ptr(), workspace.numel()
-    key = device.index if device.index is not None else torch.cuda.current_device()
+    dev_index = device.index if device.index is not None else torch.cuda.current_device()
+    key = (dev_index, torch.cuda.current_stream(dev_index).cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes + 256:
         _ws_cache.pop(key, None)

@@ -392,16 +392,19 @@ fk_status step_accumulate(const Ctx &c, const float *X, int64_t rows, const int3
                                  xn, at<double>(c.ws, c.L.sums), at<double>(c.ws, c.L.pfirst),
                                  at<double>(c.ws, c.L.plast), batches, offs, C_out, c.s),
                "segmented reduction");
-        FK_TRY(launch_seg_fixup(at<int32_t>(c.ws, c.L.keys_sorted), offs, rows, c.d, c.K,
-                                at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast),
-                                at<double>(c.ws, c.L.sums), batches, C_out, c.s),
-               "segment fix-up");
-        if (batches)
+        if (batches) {
+            FK_TRY(launch_seg_fixup(at<int32_t>(c.ws, c.L.keys_sorted), offs, rows, c.d, c.K,
+                                    at<double>(c.ws, c.L.pfirst), at<double>(c.ws, c.L.plast),
+                                    at<double>(c.ws, c.L.sums), true, nullptr, c.s),
+                   "segment fix-up");
             FK_TRY(launch_count_accumulate(offs, c.K, at<int32_t>(c.ws, c.L.cnt), true, c.s), "count accumulate");
+        }
     }
     if (!batches) {
         PhaseScope ph(FK_PH_FINALIZE, c.s);
-        FK_TRY(launch_counts_keep(offs, c.K, c.d, C_prev, C_out, counts, c.s), "counts");
+        FK_TRY(launch_seg_finish(at<int32_t>(c.ws, c.L.keys_sorted), offs, rows, c.d, c.K, at<double>(c.ws, c.L.pfirst),
+                                 at<double>(c.ws, c.L.plast), C_prev, C_out, counts, c.s),
+               "segment fix-up and counts");
         if (c.metric == FK_METRIC_SPHERICAL) FK_TRY(launch_unit_rows(C_out, c.K, c.d, c.s), "unit centroids");
     }
     return FK_OK;
@@ -644,38 +647,41 @@ fk_status fk_lloyd_iter_noalloc(const float *X, int64_t N, int32_t d, const floa
 }
 
 // Library-owned copy stream and events for the out-of-core pipeline (one set
-// per device, created on first use, default priority).
+// per device, created on first use, default priority).  Calls on one device
+// share them, so a call holds the device's mutex while it enqueues: calls
+// from several host threads are then enqueued one after the other (a stream
+// wait takes the event's record at the time it is enqueued, so each call's
+// waits see its own records).
 namespace {
+constexpr int kMaxOocDevices = 64;
 struct OocRes {
-    int device = -1;
+    bool ready = false;
     hipStream_t copy = nullptr;
     hipEvent_t copied[2] = {nullptr, nullptr};
     hipEvent_t freed[2] = {nullptr, nullptr};
     hipEvent_t entry = nullptr;
+    std::mutex mu;
 };
 std::mutex g_ooc_mu;
-std::vector<OocRes> g_ooc;
+OocRes g_ooc[kMaxOocDevices];
 
 fk_status ooc_resources(OocRes **out) {
     int dev = 0;
     FK_TRY(hipGetDevice(&dev), "hipGetDevice");
+    if (dev < 0 || dev >= kMaxOocDevices)
+        return fail(FK_ERR_UNSUPPORTED, "device %d beyond the %d supported", dev, kMaxOocDevices);
     std::lock_guard<std::mutex> g(g_ooc_mu);
-    for (auto &r : g_ooc)
-        if (r.device == dev) {
-            *out = &r;
-            return FK_OK;
+    OocRes &r = g_ooc[dev];
+    if (!r.ready) {
+        FK_TRY(hipStreamCreateWithFlags(&r.copy, hipStreamNonBlocking), "copy stream");
+        for (int i = 0; i < 2; ++i) {
+            FK_TRY(hipEventCreateWithFlags(&r.copied[i], hipEventDisableTiming), "event");
+            FK_TRY(hipEventCreateWithFlags(&r.freed[i], hipEventDisableTiming), "event");
         }
-    OocRes r;
-    r.device = dev;
-    FK_TRY(hipStreamCreateWithFlags(&r.copy, hipStreamNonBlocking), "copy stream");
-    for (int i = 0; i < 2; ++i) {
-        FK_TRY(hipEventCreateWithFlags(&r.copied[i], hipEventDisableTiming), "event");
-        FK_TRY(hipEventCreateWithFlags(&r.freed[i], hipEventDisableTiming), "event");
+        FK_TRY(hipEventCreateWithFlags(&r.entry, hipEventDisableTiming), "event");
+        r.ready = true;
     }
-    FK_TRY(hipEventCreateWithFlags(&r.entry, hipEventDisableTiming), "event");
-    g_ooc.reserve(16);
-    g_ooc.push_back(r);
-    *out = &g_ooc.back();
+    *out = &r;
     return FK_OK;
 }
 
@@ -712,6 +718,7 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
         return fail(FK_ERR_INVALID_ARG, "assign_host is not pinned host memory");
     OocRes *R = nullptr;
     if ((st = ooc_resources(&R)) != FK_OK) return st;
+    std::lock_guard<std::mutex> serial(R->mu);
 
     const Ctx c{L, workspace, (hipStream_t)stream, d, K, metric, score};
     if ((st = step_zero_accumulators(c, true, N)) != FK_OK) return st;

@@ -20,21 +20,25 @@ constexpr int kCentroidPad = 128;
 // ---- radix sort geometry --------------------------------------------------
 constexpr int kSortWaves = 8;
 constexpr int kSortThreads = kSortWaves * kWave;
-constexpr int kSortRows = 16;                                  // 64-key rows per wave
-constexpr int kSortTile = kSortWaves * kSortRows * kWave;       // 8192 keys per tile
+// (a tile is kSortWaves waves of 4 to 16 rows of 64 keys, chosen from N)
 
 // ---- segmented reduction geometry -----------------------------------------
 constexpr int kSegWaves = 4;
-// Sorted rows per wave segment: enough segments to fill the chip (about 8192
-// waves) while keeping each segment long enough to stream, 64..2048 rows.
-inline int seg_rows(int64_t N) {
+// Sorted rows per wave segment, 64..2048: enough segments to keep about
+// 32 MB of rows in flight (eight rows per wave: 8192 waves up to d = 128,
+// fewer for longer rows, at least 1024) while keeping each segment long, since
+// every cluster that crosses a segment boundary leaves partial sums.
+inline int seg_rows(int64_t N, int d) {
+    int64_t target = ((int64_t)1 << 20) / (d > 128 ? d : 128);
+    if (target < 1024) target = 1024;
     int r = 2048;
-    while (r > 64 && N / r < 8192) r >>= 1;
+    while (r > 64 && N / r < target) r >>= 1;
     return r;
 }
-// An upper bound of cdiv(n, seg_rows(n)) over all n <= rows (the count is not
-// monotone in n): either the rows were shortened, and then n / (2r) < 8192,
-// or they were not (2048-row segments), or they stopped at 64.
+// An upper bound of cdiv(n, seg_rows(n, d)) over all n <= rows and all d (the
+// count is not monotone in n, and longer rows only lengthen the segments):
+// either the rows were shortened, and then n / (2r) < 8192, or they were not
+// (2048-row segments), or they stopped at 64.
 inline int64_t seg_count_bound(int64_t rows) {
     const int64_t a = (rows + 63) / 64;
     int64_t b = (rows + 2047) / 2048;
@@ -121,7 +125,7 @@ hipError_t noalloc_scratch(int device, void **ptr);
 // each key, offsets[K] = N).  acc: rows fed in several batches, cluster sums
 // added to sums (divided by launch_finalize at the end); otherwise the rows
 // came in one batch and the reduction and its fix-up write the new centroids
-// of the non-empty clusters to C_out, launch_counts_keep the rest.
+// of the non-empty clusters to C_out, launch_seg_finish the rest.
 hipError_t launch_seg_reduce(const float *X, int64_t N, int d, int K, const int32_t *keys_sorted, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
                              int32_t *offsets, float *C_out, hipStream_t s);
@@ -129,9 +133,12 @@ hipError_t launch_seg_fixup(const int32_t *keys_sorted, const int32_t *offsets, 
                             const double *pfirst, const double *plast, double *sums, bool acc, float *C_out,
                             hipStream_t s);
 hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, bool acc, hipStream_t s);
-// counts from the offsets, previous centroids for the empty clusters
-hipError_t launch_counts_keep(const int32_t *offsets, int K, int d, const float *C_prev, float *C_out,
-                              int32_t *counts_out, hipStream_t s);
+// Rows in one batch, after launch_seg_reduce: the crossing clusters' partials
+// added and divided into C_out, counts from the offsets, and the previous
+// centroid kept for an empty cluster (one launch)
+hipError_t launch_seg_finish(const int32_t *keys_sorted, const int32_t *offsets, int64_t N, int d, int K,
+                             const double *pfirst, const double *plast, const float *C_prev, float *C_out,
+                             int32_t *counts_out, hipStream_t s);
 // every row of C[K, d] divided by its L2 norm (fp64, a zero norm taken as 1):
 // the spherical centroids
 hipError_t launch_unit_rows(float *C, int K, int d, hipStream_t s);

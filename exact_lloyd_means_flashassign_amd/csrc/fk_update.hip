@@ -7,13 +7,14 @@
 // clusters.  Under a skewed (Zipf) size distribution one cluster can hold a
 // fifth of all points, so a block per cluster would leave one block reading
 // millions of rows.  Here the sorted rows are cut into equal segments of
-// seg_rows(N) rows, one wave each:
+// seg_rows(N, d) rows, one wave each:
 //   * a cluster that lies inside one segment is summed and written by that
 //     wave alone;
 //   * a cluster that crosses segment boundaries leaves one partial row per
 //     segment it touches (pfirst: the segment's first cluster when it started
 //     earlier; plast: the segment's last cluster when it continues later), and
-//     k_seg_fixup adds those partials in a fixed order.
+//     k_seg_finish (rows in one batch) or k_seg_fixup (several batches) adds
+//     those partials in a fixed order.
 // Every output element has exactly one writer and a fixed summation order, so
 // the result is bitwise reproducible.  Sums are fp64.  The gathered rows
 // X[perm[r]] are read as whole coalesced rows.  When all rows come in one
@@ -43,7 +44,7 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t *__restrict__ p, int
 // fed in several batches; the finalize step divides).  Otherwise the rows
 // come in one batch and a cluster inside the segment is written to C_out as
 // its sum divided by its row count (clusters that no row reaches are left to
-// k_counts_keep).  The column block blockIdx.y == 0 also writes offsets[k] =
+// k_seg_finish).  The column block blockIdx.y == 0 also writes offsets[k] =
 // the first sorted row whose key is >= k (offsets[K] = N): the entries between
 // two consecutive keys are written by the wave that sees the change.
 template <int NV, int E, int U, bool COS, bool ACC>
@@ -236,24 +237,37 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
 // 8 wave sums are added in wave order.  Most workgroups find no cluster to
 // finish and exit at once, so they stay small.
 constexpr int kFixWaves = 8;
-__global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__restrict__ ks,
-                                                             const int32_t *__restrict__ offsets, int64_t N, int d,
-                                                             int K, int srows,
-                                                             const double *__restrict__ pfirst,
-                                                             const double *__restrict__ plast,
-                                                             double *__restrict__ sums, bool acc,
-                                                             float *__restrict__ C_out) {
+
+// Whether cluster k crosses boundary b (between segments b and b+1) and b is
+// the first boundary it crosses; then *sa, *sb are its first and last
+// segments and *n its row count.
+__device__ __forceinline__ bool first_crossing(int64_t b, const int32_t *__restrict__ ks,
+                                               const int32_t *__restrict__ offsets, int64_t N, int K, int srows,
+                                               int *k_out, int64_t *sa, int64_t *sb, int64_t *n) {
+    const int64_t rb = (b + 1) * srows;
+    if (rb >= N) return false;
+    const int k = ks[rb];
+    if (ks[rb - 1] != k || (unsigned)k >= (unsigned)K) return false;
+    const int64_t o0 = offsets[k], o1 = offsets[k + 1];
+    if (o0 / srows != b) return false;
+    *k_out = k;
+    *sa = b;
+    *sb = (o1 - 1) / srows;
+    *n = o1 - o0;
+    return true;
+}
+
+// The whole workgroup adds cluster k's partials: plast of its first segment
+// sa, then pfirst of every later segment up to sb; wave w takes the segments
+// sa+1+w, sa+1+w+8, ... in order (eight loads in flight: the largest cluster
+// of a skewed mixture crosses thousands of boundaries) and the eight wave
+// sums are added in wave order.  The total goes into sums[k] (acc) or,
+// divided by the row count n, into C_out[k].
+__device__ __forceinline__ void sum_partials(int k, int64_t sa, int64_t sb, int64_t n, int d,
+                                             const double *__restrict__ pfirst, const double *__restrict__ plast,
+                                             double *__restrict__ sums, bool acc, float *__restrict__ C_out) {
     __shared__ double red[kFixWaves][64];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t b = blockIdx.x;
-    const int64_t rb = (b + 1) * srows;
-    if (rb >= N) return;
-    const int k = ks[rb];
-    if (ks[rb - 1] != k || (unsigned)k >= (unsigned)K) return;
-    const int64_t o0 = offsets[k], o1 = offsets[k + 1];
-    const int64_t sa = o0 / srows;
-    if (sa != b) return;
-    const int64_t sb = (o1 - 1) / srows;
     for (int c0 = 0; c0 < d; c0 += 64) {
         const int c = c0 + lane;
         double s = 0.0;
@@ -279,9 +293,66 @@ __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__r
                 double *dst = sums + (int64_t)k * d + c;
                 *dst += t;
             } else {
-                C_out[(int64_t)k * d + c] = (float)(t / (double)(o1 - o0));
+                C_out[(int64_t)k * d + c] = (float)(t / (double)n);
             }
         }
+        __syncthreads();
+    }
+}
+
+// Rows in several batches: one workgroup per segment boundary b; if b is the
+// first boundary a cluster crosses, the workgroup adds its partials into the
+// fp64 sums.  Most workgroups find nothing to do and exit at once.
+__global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__restrict__ ks,
+                                                             const int32_t *__restrict__ offsets, int64_t N, int d,
+                                                             int K, int srows,
+                                                             const double *__restrict__ pfirst,
+                                                             const double *__restrict__ plast,
+                                                             double *__restrict__ sums, bool acc,
+                                                             float *__restrict__ C_out) {
+    int k;
+    int64_t sa, sb, n;
+    if (first_crossing(blockIdx.x, ks, offsets, N, K, srows, &k, &sa, &sb, &n))
+        sum_partials(k, sa, sb, n, d, pfirst, plast, sums, acc, C_out);
+}
+
+// Rows in one batch: workgroup g takes clusters 8g .. 8g+7 (then 8(g + G) ..,
+// G workgroups), one per wave (counts_out[k] from the offsets; an empty
+// cluster's previous centroid copied by the whole wave, coalesced); then the
+// segment boundaries 8g .. 8g+7 (then 8(g + G) ..): each wave checks one of
+// them, and the whole workgroup sums the partials of every cluster found
+// crossing its first boundary there, divided into C_out.  Checking eight
+// boundaries at once keeps their dependent loads in parallel.
+__global__ __launch_bounds__(kFixWaves * 64) void k_seg_finish(const int32_t *__restrict__ ks,
+                                                              const int32_t *__restrict__ offsets, int64_t N, int d,
+                                                              int K, int srows, int64_t nbound,
+                                                              const double *__restrict__ pfirst,
+                                                              const double *__restrict__ plast,
+                                                              const float *__restrict__ C_prev,
+                                                              float *__restrict__ C_out,
+                                                              int32_t *__restrict__ counts_out) {
+    __shared__ int jk[kFixWaves];
+    __shared__ int64_t jsa[kFixWaves], jsb[kFixWaves], jn[kFixWaves];
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    for (int64_t k = (int64_t)blockIdx.x * kFixWaves + w; k < K; k += (int64_t)gridDim.x * kFixWaves) {
+        const int c = offsets[k + 1] - offsets[k];
+        if (lane == 0) counts_out[k] = c;
+        if (c == 0)
+            for (int j = lane; j < d; j += 64) C_out[k * d + j] = C_prev[k * d + j];
+    }
+    for (int64_t b0 = (int64_t)blockIdx.x * kFixWaves; b0 < nbound; b0 += (int64_t)gridDim.x * kFixWaves) {
+        int k = -1;
+        int64_t sa = 0, sb = 0, n = 0;
+        if (b0 + w < nbound && !first_crossing(b0 + w, ks, offsets, N, K, srows, &k, &sa, &sb, &n)) k = -1;
+        if (lane == 0) {
+            jk[w] = k;
+            jsa[w] = sa;
+            jsb[w] = sb;
+            jn[w] = n;
+        }
+        __syncthreads();
+        for (int j = 0; j < kFixWaves; ++j)
+            if (jk[j] >= 0) sum_partials(jk[j], jsa[j], jsb[j], jn[j], d, pfirst, plast, nullptr, false, C_out);
         __syncthreads();
     }
 }
@@ -291,21 +362,6 @@ __global__ __launch_bounds__(256) void k_count_acc(const int32_t *__restrict__ o
                                                    int32_t *__restrict__ cnt, bool acc) {
     const int k = blockIdx.x * blockDim.x + threadIdx.x;
     if (k < K) cnt[k] = (acc ? cnt[k] : 0) + offsets[k + 1] - offsets[k];
-}
-
-// Rows in one batch: counts_out[k] = offsets[k+1] - offsets[k], and a cluster
-// with no row keeps its previous centroid (the others were written by the
-// reduction).  One wave per cluster: an empty cluster's row is copied by the
-// whole wave, coalesced.
-__global__ __launch_bounds__(256) void k_counts_keep(const int32_t *__restrict__ offsets, int K, int d,
-                                                     const float *__restrict__ C_prev, float *__restrict__ C_out,
-                                                     int32_t *__restrict__ counts_out) {
-    const int k = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (k >= K) return;
-    const int c = offsets[k + 1] - offsets[k];
-    if (lane == 0) counts_out[k] = c;
-    if (c == 0)
-        for (int j = lane; j < d; j += 64) C_out[(int64_t)k * d + j] = C_prev[(int64_t)k * d + j];
 }
 
 // Rows in several batches: C_out = sums / n_k, or C_prev for an empty
@@ -429,7 +485,7 @@ static hipError_t seg_launch(const float *X, int64_t N, int d, int K, const int3
                              const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
                              int32_t *offsets, float *C_out, hipStream_t s) {
     constexpr int U = NV * E <= 2 ? 8 : (NV * E <= 8 ? 8 : 4);
-    const int srows = seg_rows(N);
+    const int srows = seg_rows(N, d);
     const int64_t nseg = cdiv(N, srows);
     const dim3 grid((unsigned)cdiv(nseg, kSegWaves), (unsigned)cdiv(d, 64 * E * NV));
     const dim3 block(kSegWaves * 64);
@@ -480,7 +536,7 @@ hipError_t launch_seg_reduce(const float *X, int64_t N, int d, int K, const int3
 
 hipError_t launch_seg_fixup(const int32_t *ks, const int32_t *offsets, int64_t N, int d, int K, const double *pfirst,
                             const double *plast, double *sums, bool acc, float *C_out, hipStream_t s) {
-    const int srows = seg_rows(N);
+    const int srows = seg_rows(N, d);
     const int64_t nseg = cdiv(N, srows);
     if (nseg <= 1) return hipSuccess;
     hipLaunchKernelGGL(k_seg_fixup, dim3((unsigned)(nseg - 1)), dim3(kFixWaves * 64), 0, s, ks, offsets, N, d, K,
@@ -493,10 +549,17 @@ hipError_t launch_count_accumulate(const int32_t *offsets, int K, int32_t *cnt, 
     return hipGetLastError();
 }
 
-hipError_t launch_counts_keep(const int32_t *offsets, int K, int d, const float *C_prev, float *C_out,
-                              int32_t *counts_out, hipStream_t s) {
-    hipLaunchKernelGGL(k_counts_keep, dim3((unsigned)cdiv(K, 4)), dim3(256), 0, s, offsets, K, d, C_prev, C_out,
-                       counts_out);
+hipError_t launch_seg_finish(const int32_t *ks, const int32_t *offsets, int64_t N, int d, int K,
+                             const double *pfirst, const double *plast, const float *C_prev, float *C_out,
+                             int32_t *counts_out, hipStream_t s) {
+    const int srows = seg_rows(N > 0 ? N : 1, d);
+    const int64_t nbound = N > 0 ? cdiv(N, srows) - 1 : 0;
+    int64_t g = cdiv(K, kFixWaves);
+    if (g < cdiv(nbound, kFixWaves)) g = cdiv(nbound, kFixWaves);
+    if (g > 2048) g = 2048;
+    if (g < 1) g = 1;
+    hipLaunchKernelGGL(k_seg_finish, dim3((unsigned)g), dim3(kFixWaves * 64), 0, s, ks, offsets, N, d, K, srows,
+                       nbound, pfirst, plast, C_prev, C_out, counts_out);
     return hipGetLastError();
 }
 

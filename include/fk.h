@@ -193,7 +193,9 @@ fk_status fk_lloyd_iter_noalloc(const float *X, int64_t N, int32_t d, const floa
  * device pointers; assign_host, when not NULL, is pinned host memory of N
  * int32 that receives the assignment.  The call returns once every chunk is
  * enqueued; the caller synchronises `stream`.  X_host must not be modified
- * until then.  Returns FK_ERR_INVALID_ARG when X_host or assign_host is not
+ * until then.  Calls on one device share the library's copy stream: calls
+ * from several host threads are enqueued one at a time (each with its own
+ * workspace).  Returns FK_ERR_INVALID_ARG when X_host or assign_host is not
  * pinned.
  */
 fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const float *C_in, int32_t K,
@@ -317,11 +319,12 @@ enum {
     FK_PH_ASSIGN = 1,    /* the FlashAssign kernel                          */
     FK_PH_RECHECK = 2,   /* fp64 rescoring of near-tie points               */
     FK_PH_SORT = 3,      /* radix sort (the inverse index)                  */
-    FK_PH_REDUCE = 4,    /* segmented reduction + carry fix-up (with the
-                            cluster offsets; rows in one batch: also the
-                            divide by count)                                */
-    FK_PH_FINALIZE = 5,  /* counts, empty centroids kept (and the divide
-                            when rows came in several batches)              */
+    FK_PH_REDUCE = 4,    /* segmented reduction (with the cluster offsets;
+                            rows in one batch: also the divide by count of
+                            the clusters inside a segment; rows in several
+                            batches: also the carry fix-up)                 */
+    FK_PH_FINALIZE = 5,  /* rows in one batch: carry fix-up, counts, empty
+                            centroids kept; in several batches: the divide  */
     FK_PH_H2D = 6,       /* host-to-device chunk copies (out-of-core)       */
     FK_NPHASE = 7
 };

@@ -177,7 +177,9 @@ def test_update_empty_input(gpu_lib):
 
 
 @pytest.mark.parametrize("N,K", [(0, 5), (1, 1), (100, 1), (4096, 256), (4097, 257), (10000, 2), (70000, 1024),
-                                 (300000, 32768), (50000, 65536), (8191, 255), (20000001, 40000)])
+                                 (300000, 32768), (50000, 65536), (8191, 255), (20000001, 40000),
+                                 (2048, 2048), (2049, 2049), (1048576, 1024), (2097151, 2048), (2097152, 70),
+                                 (4194303, 2047), (4194304, 4096), (3000000, 65536)])
 def test_sort_inverse_matches_stable_argsort(gpu_lib, N, K):
     fk = gpu_lib
     log(f"sort N={N} K={K}")

@@ -75,3 +75,41 @@ def test_stream_other_widths(gpu_lib, d, chunk, score):
     np.testing.assert_array_equal(ah.numpy(), ref["a"])
     np.testing.assert_array_equal(host(n_s), ref["counts"])
     assert centroid_rel_err(host(C_s), ref["C"], ref["counts"]) <= 1e-6
+
+
+def test_stream_calls_from_two_threads(gpu_lib):
+    """Two host threads stream at once, each on its own stream with its own
+    workspace: both results equal the in-core iteration (the library
+    enqueues the calls one at a time on the shared copy stream)."""
+    import threading
+    fk = gpu_lib
+    w = synth.WORKLOADS["ooc_1b_d128_k32768"].scaled(120000)
+    X = synth.rows(w)
+    C = X[synth.init_indices(w)[:500]].copy()
+    Xh = _pinned(X)
+    Cd = dev(C)
+    a_ic, C_ic, n_ic, _ = fk.fk_lloyd_iter(dev(X), Cd)
+    torch.cuda.synchronize()
+    chunk = 30001
+    nbytes = fk.fk_workspace_size(w.N, w.d, 500, "l2", chunk) + 256
+    res = [None, None]
+
+    def run(i):
+        s = torch.cuda.Stream()
+        ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+        ah = torch.empty(w.N, dtype=torch.int32, pin_memory=True)
+        with torch.cuda.stream(s):
+            for _ in range(3):
+                C_s, n_s = fk.fk_lloyd_iter_stream(Xh, Cd, chunk, assign_host=ah, workspace=ws)
+        s.synchronize()
+        res[i] = (ah.numpy().copy(), host(C_s), host(n_s))
+
+    ts = [threading.Thread(target=run, args=(i,)) for i in range(2)]
+    for t in ts:
+        t.start()
+    for t in ts:
+        t.join()
+    for a, Cs, n in res:
+        np.testing.assert_array_equal(a, host(a_ic))
+        np.testing.assert_array_equal(n, host(n_ic))
+        assert centroid_rel_err(Cs, host(C_ic).astype(np.float64), host(n_ic)) <= 1e-6
