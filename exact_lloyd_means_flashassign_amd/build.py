@@ -14,6 +14,10 @@ LIB = os.path.join(HERE, "libfk.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["fk_api.hip", "fk_assign.hip", "fk_sort.hip", "fk_update.hip"]
+# on-box microbenchmarks (HBM stream, row gather, matrix-product loops): a
+# library of their own, loaded only by the benchmark
+MICRO_SOURCE = "fk_micro.hip"
+MICRO_LIB = os.path.join(HERE, "libfk_micro.so")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -41,14 +45,21 @@ def build(verbose: bool = False) -> str:
             sys.stderr.write(r.stderr)
         return obj
 
-    with ThreadPoolExecutor(len(SOURCES)) as ex:
-        objs = list(ex.map(compile_one, SOURCES))
+    with ThreadPoolExecutor(len(SOURCES) + 1) as ex:
+        objs = list(ex.map(compile_one, SOURCES + [MICRO_SOURCE]))
+    micro_obj = objs.pop()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
     os.replace(tmp, LIB)
+    tmp = MICRO_LIB + ".tmp%d" % os.getpid()
+    r = subprocess.run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, micro_obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link of the microbenchmarks failed:\n{r.stderr}")
+    os.replace(tmp, MICRO_LIB)
     return LIB
 
 

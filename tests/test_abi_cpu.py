@@ -193,3 +193,12 @@ def test_knn_validation(lib):
     assert a > (1 << 20) * 128 * 4                # the database's bf16 copy
     assert fk.fk_knn_workspace_size(10000, 128, 1 << 20, 10, "cosine") > a + (1 << 20) * 128 * 12
     assert fk.fk_knn_workspace_size(10000, 128, 1 << 20, 20) > a  # 32 candidates per query
+
+
+def test_microbenchmark_library_exports():
+    """The on-box microbenchmarks the benchmark loads are built beside libfk."""
+    path = os.path.join(os.path.dirname(fk.LIB_PATH), "libfk_micro.so")
+    assert os.path.exists(path), "run __graft_entry__.build() first"
+    m = ctypes.CDLL(path)
+    for name in ("fkm_stream_copy", "fkm_stream_read", "fkm_gather_rows", "fkm_mfma"):
+        assert hasattr(m, name), name
