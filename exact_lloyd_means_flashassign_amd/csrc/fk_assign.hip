@@ -25,6 +25,8 @@
 //     centroid within the window and k_recheck_cand compares those in fp64,
 //     and a point with more than it can hold goes to k_recheck, which
 //     rescores it against all K.
+#include <type_traits>
+
 #include "fk_internal.h"
 
 namespace fk {
@@ -513,16 +515,20 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             }
         };
         // put_x: slot q's value into the MFMA operand registers (scaled for
-        // cosine) and, with add_norm, into the point's squared norms
-        auto put_x = [&](int b, int q, float v, bool add_norm, float &nacc, float &lacc, float &racc) {
-            const float xv = (A.xnorm64 != nullptr) ? v * xsc[b] : v;
+        // cosine; streamed chunks multiply by xsc, which is 1 otherwise, to
+        // save the select on every stage) and,
+        // with add_norm (a compile-time flag: std::true_type or
+        // std::false_type), into the point's squared norms
+        auto put_x = [&](int b, int q, float v, auto add_norm_c, float &nacc, float &lacc, float &racc) {
+            constexpr bool add_norm = decltype(add_norm_c)::value;
+            const float xv = (RES && A.xnorm64 == nullptr) ? v : v * xsc[b];
             if constexpr (SPLIT) {
                 const __bf16 hi = (__bf16)xv;
                 const float dl = xv - (float)hi;  // exact
                 const __bf16 lo = (__bf16)dl;
                 xh[b][q / 8][q % 8] = hi;
                 xl[b][q / 8][q % 8] = lo;
-                if (add_norm) {
+                if constexpr (add_norm) {
                     const float lf = (float)lo, r = dl - lf;  // exact
                     nacc = fmaf(xv, xv, nacc);
                     lacc = fmaf(lf, lf, lacc);
@@ -530,10 +536,10 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 }
             } else {
                 xr[b][q] = xv;
-                if (add_norm) nacc = fmaf(xv, xv, nacc);
+                if constexpr (add_norm) nacc = fmaf(xv, xv, nacc);
             }
         };
-        auto load_x = [&](int ch, bool add_norm) {
+        auto load_x = [&](int ch, auto add_norm) {
 #pragma unroll
             for (int b = 0; b < PB; ++b) {
                 float nacc = xn[b], lacc = xl2[b], racc = xr2[b];
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
 #pragma unroll
                 for (int q = 0; q < HALF; ++q) {
                     const float v = xraw[b][q];
-                    const float xv = (A.xnorm64 != nullptr) ? v * xsc[b] : v;
+                    const float xv = (RES && A.xnorm64 == nullptr) ? v : v * xsc[b];
                     const __bf16 hi = (__bf16)xv;
                     const __bf16 lo = (__bf16)(xv - (float)hi);
                     xhn[b][q / 8][q % 8] = hi;
@@ -596,7 +602,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
 #pragma unroll
                 for (int q = 0; q < HALF; ++q) {
                     const float v = xraw[b][q];
-                    const float xv = (A.xnorm64 != nullptr) ? v * xsc[b] : v;
+                    const float xv = (RES && A.xnorm64 == nullptr) ? v : v * xsc[b];
                     const float dl = xv - (float)(__bf16)xv;  // exact
                     const float lf = (float)(__bf16)dl, r = dl - lf;  // exact
                     nacc = fmaf(xv, xv, nacc);
@@ -608,7 +614,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 xr2[b] = racc;
             }
         };
-        auto put_next = [&](bool add_norm) {
+        auto put_next = [&](auto add_norm) {
 #pragma unroll
             for (int b = 0; b < PB; ++b) {
                 float nacc = xn[b], lacc = xl2[b], racc = xr2[b];
@@ -751,7 +757,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         const int tb = TL > 0 ? (int)blockIdx.y * A.knn_tps : 0;
         const int te = TL > 0 ? min(A.ntiles, tb + A.knn_tps) : A.ntiles;
         const int nst = (te - tb) * cnch;
-        if (RES || PRE) load_x(0, true);
+        if (RES || PRE) load_x(0, std::true_type{});
         if constexpr (PRE2) {
 #pragma unroll
             for (int b = 0; b < PB; ++b)
@@ -792,7 +798,10 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             } else if constexpr (PRE) {
                 if (more) fetch_next(nc);
             } else if constexpr (!RES) {
-                load_x(ch, t == tb);
+                if (t == tb)
+                    load_x(ch, std::true_type{});
+                else
+                    load_x(ch, std::false_type{});
             }
             if (more) load_stage(nt, nc);
 
@@ -984,7 +993,10 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     // after this stage's products: the wait for the fetched
                     // values must not move ahead of them
                     __builtin_amdgcn_sched_barrier(0);
-                    put_next(nt == tb);
+                    if (nt == tb)
+                        put_next(std::true_type{});
+                    else
+                        put_next(std::false_type{});
                 }
             }
             __syncthreads();
