@@ -1609,13 +1609,15 @@ template <bool COLLECT, bool SPLIT>
 static hipError_t launch_fa_shape(const FlashArgs &A, hipStream_t s) {
     const AssignShape sh = assign_shape(A.d);
     if (sh.nch > 1) {
-        // streamed points are re-read for every centroid tile: 128-row tiles
-        // halve that traffic and the stage overheads per product (at
-        // d = 768, K = 4096 they were 20 % faster than 64-row tiles).  Split
-        // scoring at that height needs more than 256 registers: one wave per
-        // SIMD, accumulators in AGPRs, rather than spilling.
+        // streamed points are re-read for every centroid tile, and that
+        // traffic (not the products) bounds the kernel: 128-row tiles were
+        // 20 % faster than 64-row ones for fp32 scoring at d = 768,
+        // K = 4096, and 256-row tiles 20 % faster again than 128-row ones
+        // for split scoring (one accumulator, 216 registers, two waves per
+        // SIMD).  More waves per CU are slower there (38 ms against 27 ms
+        // at four per SIMD): the points in flight then outgrow the caches.
         if constexpr (SPLIT)
-            return launch_fa<32, 1, 4, 8, 2, false, COLLECT, SPLIT>(A, s);
+            return launch_fa<32, 1, 8, 8, 2, false, COLLECT, SPLIT>(A, s);
         else
             return launch_fa<64, 1, 4, 4, 2, false, COLLECT, SPLIT>(A, s);
     }

@@ -15,7 +15,7 @@ constexpr int kWave = 64;
 // their coordinates for one d-chunk of DP dims in VGPRs; all waves share
 // centroid tiles of CB*32 rows x DP dims staged through LDS.
 // Centroid counts are padded to a multiple of this (largest tile height).
-constexpr int kCentroidPad = 128;
+constexpr int kCentroidPad = 256;
 
 // ---- radix sort geometry --------------------------------------------------
 constexpr int kSortWaves = 8;

@@ -292,7 +292,7 @@ fk_status fk_ivf_build(const float *X, int64_t N, int32_t d, int32_t nlist, int3
  * 1 <= Ndb <= FK_MAX_KNN_DB, k >= 1 and min(k, Ndb) <= FK_MAX_KNN_K; metric
  * L2, COSINE or INNER_PRODUCT (SPHERICAL, a centroid option, gives
  * FK_ERR_UNSUPPORTED); FK_SCORE_SPLIT_BF16 also needs the database's bf16
- * copy (about 4 Ndb d bytes: Ndb rounded up to 128, d up to 16, 32, 64, 128
+ * copy (about 4 Ndb d bytes: Ndb rounded up to 256, d up to 16, 32, 64, 128
  * or a multiple of 64) under 4 GiB, else FK_ERR_UNSUPPORTED.  Q, DB,
  * idx[M,k] (int32) and dist[M,k] (fp32) are device pointers; workspace:
  * fk_knn_workspace_size() bytes.
