@@ -337,6 +337,13 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     // top-L lists that may start from a threshold (the 16-long lists beside
     // streamed d-chunks never do: that sweep runs without the threshold pass)
     constexpr bool TAU = TL > 0 && (RES || TL > 16);
+    // The phased kernel at DP = 128 moves each centroid stage into LDS with
+    // buffer loads that write LDS themselves (no staging registers, which
+    // the resident points need).  One such load of a wave fills 64
+    // consecutive 16-byte LDS chunks (lane i the i-th); the padded rows
+    // (DP + 8 bf16 = 17 chunks) are filled chunk by chunk, a row's pad chunk
+    // with a copy of its first chunk (never read).
+    constexpr bool DMA = PHASED && DP == 128;
 
     __shared__ __attribute__((aligned(16))) float sC[2][SPLIT ? 4 : ROWS * LDR];
     __shared__ __attribute__((aligned(16))) __bf16 sCh[2][SPLIT ? ROWS * LDB : 8];
@@ -356,6 +363,9 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     // loads past its end read zero)
     const __amdgpu_buffer_rsrc_t cs_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)A.Cs, (short)0, SPLIT ? (int)A.cs_bytes : 0, 0x00020000);
+    // and of -||c||^2/2 (ntiles * ROWS values)
+    const __amdgpu_buffer_rsrc_t ncn_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc((void *)A.ncn, (short)0, DMA ? A.ntiles * ROWS * 4 : 0, 0x00020000);
 
     // Assign mode: workgroup g takes points [g*BM, (g+1)*BM).  Collect mode:
     // the workgroups stride over slots of the full near-tie list.
@@ -413,6 +423,34 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 }
             }
             if (ch == 0 && tid < ROWS) pn = A.ncn[t * ROWS + tid];
+        };
+        // global -> LDS buffer directly (DMA): stage t of the split copy and
+        // of -||c||^2/2
+        auto dma_stage = [&](int buf, int t) {
+            constexpr int RCH = LDB / 8;    // 16-byte chunks per padded row
+            constexpr int NINS = ROWS * RCH / 64;
+            static_assert(!DMA || (ROWS * RCH) % 64 == 0, "whole wave loads per buffer");
+            static_assert(!DMA || ROWS % 64 == 0, "whole wave loads of the norms");
+            typedef __attribute__((address_space(3))) void *lds_ptr;
+            const unsigned tile_b = (unsigned)t * ROWS * (4u * A.sw);
+#pragma unroll
+            for (int i = 0; i < (NINS + WAVES - 1) / WAVES; ++i) {
+                const int j = wv + i * WAVES;  // wave-uniform
+                if (j < NINS) {
+                    const int q = j * 64 + lane;
+                    const int row = q / RCH, c = q % RCH;
+                    const unsigned o = (unsigned)row * (4u * A.sw) + (c < DP / 8 ? c : 0) * 16u;
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(cs_rsrc, (lds_ptr)&sCh[buf][j * 512], 16, o, tile_b, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(cs_rsrc, (lds_ptr)&sCl[buf][j * 512], 16, o,
+                                                             tile_b + 2u * A.sw, 0, 0);
+                }
+            }
+            if (wv == WAVES - 1) {
+#pragma unroll
+                for (int j = 0; j < ROWS / 64; ++j)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ncn_rsrc, (lds_ptr)&sN[buf][j * 64], 4, 4u * lane,
+                                                             (unsigned)(t * ROWS + j * 64) * 4u, 0, 0);
+            }
         };
         // registers -> LDS buffer
         auto store_stage = [&](int buf, int ch) {
@@ -777,8 +815,13 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     for (int st = 0; st < NS; ++st) asm volatile("" : "+v"(xh[b][st]), "+v"(xl[b][st]));
             }
         }
-        load_stage(tb, 0);
-        store_stage(0, 0);
+        if constexpr (DMA) {
+            dma_stage(0, tb);
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        } else {
+            load_stage(tb, 0);
+            store_stage(0, 0);
+        }
         __syncthreads();
 
         int t = tb, ch = 0;
@@ -803,7 +846,12 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 else
                     load_x(ch, std::false_type{});
             }
-            if (more) load_stage(nt, nc);
+            if constexpr (DMA) {
+                // into the other buffer, which no wave reads in this stage
+                if (more) dma_stage(buf ^ 1, nt);
+            } else {
+                if (more) load_stage(nt, nc);
+            }
 
             if constexpr (!PHASED) {
               if (ch == 0) {
@@ -887,7 +935,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     // the next stage goes to the other LDS buffer (which no
                     // wave reads during this tile) once the first block is
                     // done, so the prefetch registers are free for the rest
-                    if (CB > 1 && cb == 0 && more) store_stage(buf ^ 1, nc);
+                    if (!DMA && CB > 1 && cb == 0 && more) store_stage(buf ^ 1, nc);
                 }
             } else if constexpr (ONEACC) {
                 // x.c ~ hi.lo + lo.hi + hi.hi, one 32-centroid block after
@@ -973,7 +1021,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     }
                 }
             }
-            if (!(PHASED && CB > 1) && more) store_stage(buf ^ 1, nc);
+            if (!DMA && !(PHASED && CB > 1) && more) store_stage(buf ^ 1, nc);
             if constexpr (PRE2) {
                 if (more) {
                     if (nt == tb) norm_next();
@@ -999,6 +1047,8 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                         put_next(std::false_type{});
                 }
             }
+            // (the next stage's LDS loads have landed once vmcnt is zero)
+            if constexpr (DMA) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             __syncthreads();
             t = nt;
             ch = nc;

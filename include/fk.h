@@ -14,7 +14,8 @@
  *   - Sort-Inverse Update (section "Sort-Inverse Update: another answer to
  *     atomics"): the assignments are sorted by cluster id into an inverse
  *     index, and the per-cluster sums are reduced by reading that index
- *     contiguously, with no atomic operations.
+ *     contiguously, with no global atomic operations (the sort's per-tile
+ *     digit counts are LDS atomic adds, where the order does not matter).
  * The article lists squared L2 and cosine as the supported metrics and inner
  * product as the next one (section "Not a silver bullet").  Cosine is L2 on
  * L2-normalised vectors, a zero norm being taken as 1 before the divide
@@ -136,8 +137,9 @@ fk_status fk_assign(const float *X, int64_t N, int32_t d, const float *C, int32_
  * ids ordered by cluster id (stable: increasing point id within a cluster),
  * and offsets[0..K] gives the start of each cluster's run in perm, with
  * offsets[K] = N, so cluster k has offsets[k+1] - offsets[k] points.  Built
- * with an atomic-free LSD radix sort (Sort-Inverse Update section of the
- * Flash-KMeans article).  Every assign[i] must lie in [0, K); other values
+ * with an LSD radix sort (Sort-Inverse Update section of the Flash-KMeans
+ * article) whose ranking is ballot-based and stable; its per-tile digit
+ * counts are LDS atomic adds, and no global memory is updated atomically.  Every assign[i] must lie in [0, K); other values
  * give undefined results.  All pointers are device pointers.
  */
 fk_status fk_sort_inverse(const int32_t *assign, int64_t N, int32_t K, int32_t *perm, int32_t *offsets,
@@ -149,7 +151,7 @@ fk_status fk_sort_inverse(const int32_t *assign, int64_t N, int32_t K, int32_t *
  * cosine), accumulated in fp64; a cluster with no point keeps C_prev[k] as
  * passed.  The per-cluster reduction walks the inverse index over
  * equal-length row segments with a deterministic carry fix-up, so it uses no
- * atomics.  C_out must not overlap C_prev.  All pointers are device
+ * atomics (the sort under it counts digits with LDS atomic adds).  C_out must not overlap C_prev.  All pointers are device
  * pointers; assign[i] must lie in [0, K).
  */
 fk_status fk_update(const float *X, int64_t N, int32_t d, const int32_t *assign, int32_t K, int32_t metric,
