@@ -292,6 +292,25 @@ __global__ __launch_bounds__(1024) void k_prep_finish(const float *__restrict__ 
 // the full list.  For cosine, the fp32 normalised rows differ from the fp64
 // normalised ones by at most 3.1u relative, which moves a by at most
 // 3.1u (||x|| ||c|| + ||c||^2); 8u is added to g for it.
+// Tile slices of the collect sweep for a full list of nslots points: as
+// many as the persistent grid (grid workgroups) has room for beside the
+// list's slot groups, at most 64 and at most the tile count, such that the
+// candidate storage (cap_slots slots) holds nslots * slices lists, and
+// rounded so that every slice has tiles.  A long list (kStagedMinList points
+// or more) takes one slice: its fp64 check stages rows for one list per
+// point.  The fp64 check reads the count back from counters[3].
+constexpr int kStagedMinList = 65536;  // listed points for the staged checks
+__device__ __forceinline__ int collect_slices(int64_t nslots, int64_t cap_slots, int ntiles, int bm, int grid) {
+    if (nslots >= kStagedMinList || nslots <= 0) return 1;
+    const int64_t ng = (nslots + bm - 1) / bm;
+    int64_t s = grid / ng;
+    s = min(s, (int64_t)min(ntiles, 64));
+    s = min(s, cap_slots / (ng * bm));
+    if (s < 1) return 1;
+    const int64_t tps = (ntiles + s - 1) / s;
+    return (int)((ntiles + tps - 1) / tps);
+}
+
 template <int DP, int PB, int CB, int WAVES, int MINB, bool RES, bool VEC, bool COLLECT, bool SPLIT, int TL = 0>
 __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashArgs A) {
     // TL > 0: k-nearest-neighbour mode; every lane keeps its TL best scores
@@ -368,10 +387,18 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         __builtin_amdgcn_make_buffer_rsrc((void *)A.ncn, (short)0, DMA ? A.ntiles * ROWS * 4 : 0, 0x00020000);
 
     // Assign mode: workgroup g takes points [g*BM, (g+1)*BM).  Collect mode:
-    // the workgroups stride over slots of the full near-tie list.
+    // the workgroups stride over (slot group, tile slice) units of the full
+    // near-tie list: a short list is swept by several workgroups at once,
+    // each over a slice of the centroid tiles with its own candidate lists
+    // (collect_slices), instead of one workgroup walking all K.
     const int64_t nslots = COLLECT ? (int64_t)min((int64_t)A.counters[0], A.cap_slots) : A.N;
     const int64_t ngroups = COLLECT ? (nslots + BM - 1) / BM : 1;
-    for (int64_t grp = COLLECT ? (int64_t)blockIdx.x : 0; grp < ngroups; grp += COLLECT ? gridDim.x : 1) {
+    const int nsl = COLLECT ? collect_slices(nslots, A.cap_slots, A.ntiles, BM, gridDim.x) : 1;
+    const int tps = COLLECT ? (A.ntiles + nsl - 1) / nsl : 0;
+    if (COLLECT && blockIdx.x == 0 && tid == 0) A.counters[3] = nsl;  // for the fp64 check
+    for (int64_t unit = COLLECT ? (int64_t)blockIdx.x : 0; unit < ngroups * nsl; unit += COLLECT ? gridDim.x : 1) {
+        const int64_t grp = COLLECT ? unit / nsl : 0;
+        const int slice = COLLECT ? (int)(unit % nsl) : 0;
         const int64_t sbase = ((COLLECT ? grp : (int64_t)blockIdx.x) * WAVES + wv) * (PB * 32);
 
         // global -> registers for one centroid stage (tile t, d-chunk ch)
@@ -771,7 +798,8 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 if (COLLECT) {
                     // every centroid within the window may win
                     if (v >= b1[b]) {
-                        if (i1[b] < kMaxCand) A.cand[((sbase + b * 32 + jl) * 2 + h) * kMaxCand + i1[b]] = k;
+                        if (i1[b] < kMaxCand)
+                            A.cand[(((sbase + b * 32 + jl) * nsl + slice) * 2 + h) * kMaxCand + i1[b]] = k;
                         ++i1[b];
                     }
                 } else if (v > b3[b]) {
@@ -791,9 +819,10 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             }
         };
         const int cnch = RES ? 1 : A.nch;
-        // the tiles this workgroup sweeps: all, or its slice in top-L mode
-        const int tb = TL > 0 ? (int)blockIdx.y * A.knn_tps : 0;
-        const int te = TL > 0 ? min(A.ntiles, tb + A.knn_tps) : A.ntiles;
+        // the tiles this workgroup sweeps: all, or its slice (top-L mode,
+        // collect mode)
+        const int tb = TL > 0 ? (int)blockIdx.y * A.knn_tps : COLLECT ? slice * tps : 0;
+        const int te = TL > 0 ? min(A.ntiles, tb + A.knn_tps) : COLLECT ? min(A.ntiles, tb + tps) : A.ntiles;
         const int nst = (te - tb) * cnch;
         if (RES || PRE) load_x(0, std::true_type{});
         if constexpr (PRE2) {
@@ -1057,7 +1086,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         if (COLLECT) {
 #pragma unroll
             for (int b = 0; b < PB; ++b)
-                if (pv[b]) A.ccount[(sbase + b * 32 + jl) * 2 + h] = i1[b];
+                if (pv[b]) A.ccount[((sbase + b * 32 + jl) * nsl + slice) * 2 + h] = i1[b];
             continue;
         }
 
@@ -1250,8 +1279,6 @@ __device__ __forceinline__ void sqdist64(const float *__restrict__ x, const CT *
 // lane per point reading its own rows is faster (measured: 1M x 128, K =
 // 1024 with 3,000 listed pairs and 1M x 768 with 360).  These are those
 // per-lane versions.
-constexpr int kStagedMinList = 65536;  // listed points for the staged checks
-
 template <typename CT>
 __device__ __forceinline__ void recheck_cand_rows(const float *__restrict__ X, int d, const CT *__restrict__ C,
                                                   const double *__restrict__ xnorm64,
@@ -1262,29 +1289,203 @@ __device__ __forceinline__ void recheck_cand_rows(const float *__restrict__ X, i
                                                   int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
 #pragma clang fp contract(off)
     const int cnt = counters[0];
+    const int nl = 2 * max(counters[3], 1);  // candidate lists per slot
     for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
         const int64_t p = full_list[q];
-        const int c0 = q < cap_slots ? ccount[2 * (int64_t)q] : kMaxCand + 1;
-        const int c1 = q < cap_slots ? ccount[2 * (int64_t)q + 1] : kMaxCand + 1;
-        if (c0 > kMaxCand || c1 > kMaxCand) {
+        bool ovf = q >= cap_slots;
+        for (int l = 0; l < nl && !ovf; ++l) ovf = ccount[(int64_t)q * nl + l] > kMaxCand;
+        if (ovf) {
             ovf_list[atomicAdd(&counters[2], 1)] = (int32_t)p;
             continue;
         }
         const double nx = xnorm64 != nullptr ? xnorm64[p] : 1.0;
         double best = INFINITY;
         int bk = 0x7fffffff;
-        for (int m = 0; m < c0 + c1; ++m) {
-            const int k = m < c0 ? cand[2 * (int64_t)q * kMaxCand + m] : cand[(2 * (int64_t)q + 1) * kMaxCand + m - c0];
+        for (int l = 0; l < nl; ++l) {
+            for (int m = 0; m < ccount[(int64_t)q * nl + l]; ++m) {
+                const int k = cand[((int64_t)q * nl + l) * kMaxCand + m];
+                const CT *const row[1] = {C + (size_t)k * d};
+                double D[1];
+                sqdist64<CT, 1>(X + (size_t)p * d, row, d, nx, xnorm64 != nullptr, ip != 0, D);
+                if (D[0] < best || (D[0] == best && k < bk)) {
+                    best = D[0];
+                    bk = k;
+                }
+            }
+        }
+        a_out[p] = bk;
+        if (d1_out != nullptr) d1_out[p] = (float)best;
+    }
+}
+
+// The same fp64 distances by a group of 32 lanes (one point, NC centroid
+// rows): lane g of the group loads dims [gS, gS + S) of every row at once (S
+// = ceil(d / 32) rounded up to 4, at most kGroupSpan), and the running sums
+// then pass from lane to lane, each lane adding its own dims in increasing j
+// -- the same terms in the same order as sqdist64, so the same bits -- while
+// the loads of all lanes were in flight together.  `base` is the group's
+// first lane in the wave; every lane of the group returns the sums.
+constexpr int kGroupSpan = 24;                  // dims per lane: d <= 768
+constexpr int kGroupMaxD = 32 * kGroupSpan;
+template <typename CT, int NC>
+__device__ __forceinline__ void group_sqdist64(const float *__restrict__ x, const CT *const (&c)[NC], int d,
+                                               double nx, bool cosine, bool ip, int gl, int base, double (&D)[NC]) {
+#pragma clang fp contract(off)
+    const int S = ((d + 31) / 32 + 3) & ~3;
+    const int j0 = gl * S;
+    const int ns = max(0, min(S, d - j0));
+    float xr[kGroupSpan];
+    CT cr[NC][kGroupSpan];
+#pragma unroll
+    for (int s = 0; s < kGroupSpan; ++s) {
+        xr[s] = 0.f;
+#pragma unroll
+        for (int m = 0; m < NC; ++m) cr[m][s] = (CT)0;
+    }
+    if ((d & 3) == 0) {
+#pragma unroll
+        for (int s = 0; s < kGroupSpan; s += 4) {
+            if (s < ns) {
+                const float4 v = *reinterpret_cast<const float4 *>(x + j0 + s);
+                xr[s] = v.x;
+                xr[s + 1] = v.y;
+                xr[s + 2] = v.z;
+                xr[s + 3] = v.w;
+#pragma unroll
+                for (int m = 0; m < NC; ++m) {
+                    double cv[4];
+                    load4_64(c[m] + j0 + s, cv);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) cr[m][s + e] = (CT)cv[e];
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < kGroupSpan; ++s) {
+            if (s < ns) {
+                xr[s] = x[j0 + s];
+#pragma unroll
+                for (int m = 0; m < NC; ++m) cr[m][s] = c[m][j0 + s];
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < NC; ++m) D[m] = 0.0;
+    for (int g = 0; g < 32; ++g) {
+        if (gl == g) {
+#pragma unroll
+            for (int s = 0; s < kGroupSpan; ++s) {
+                if (s < ns) {
+                    double xv = (double)xr[s];
+                    if (cosine) xv = xv / nx;
+#pragma unroll
+                    for (int m = 0; m < NC; ++m) {
+                        if (ip) {
+                            D[m] = D[m] - xv * (double)cr[m][s];
+                        } else {
+                            const double t = xv - (double)cr[m][s];
+                            D[m] = D[m] + t * t;
+                        }
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < NC; ++m) D[m] = __shfl(D[m], base + g);
+    }
+}
+
+// Pair check, one 32-lane group per listed point (d <= kGroupMaxD).
+template <typename CT>
+__device__ __forceinline__ void recheck_pair_group(const float *__restrict__ X, int d, const CT *__restrict__ C,
+                                                   const double *__restrict__ xnorm64,
+                                                   const int32_t *__restrict__ pair_list,
+                                                   const int32_t *__restrict__ counters,
+                                                   int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+    const int cnt = counters[1];
+    const int lane = threadIdx.x & 63, gl = lane & 31, base = lane & 32;
+    const int64_t ng = (int64_t)gridDim.x * (blockDim.x / 32);
+    for (int64_t q = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 32; q < cnt; q += ng) {
+        const int64_t p = pair_list[3 * q];
+        const int k1 = pair_list[3 * q + 1];
+        const int k2 = pair_list[3 * q + 2];
+        const CT *const rows[2] = {C + (size_t)k1 * d, C + (size_t)k2 * d};
+        double D[2];
+        group_sqdist64<CT, 2>(X + (size_t)p * d, rows, d, xnorm64 != nullptr ? xnorm64[p] : 1.0,
+                              xnorm64 != nullptr, ip != 0, gl, base, D);
+        if (gl == 0) {
+            const bool second = (D[1] < D[0]) || (D[1] == D[0] && k2 < k1);
+            a_out[p] = second ? k2 : k1;
+            if (d1_out != nullptr) d1_out[p] = (float)(second ? D[1] : D[0]);
+        }
+    }
+}
+
+// Window check, one workgroup per listed point (d <= kGroupMaxD): its
+// 32-lane groups take the candidates round-robin, and the lowest (distance,
+// index) of the groups is taken in LDS.
+template <typename CT>
+__device__ __forceinline__ void recheck_cand_group(const float *__restrict__ X, int d, const CT *__restrict__ C,
+                                                   const double *__restrict__ xnorm64,
+                                                   const int32_t *__restrict__ full_list,
+                                                   const int32_t *__restrict__ cand,
+                                                   const int32_t *__restrict__ ccount, int64_t cap_slots,
+                                                   int32_t *__restrict__ ovf_list, int32_t *__restrict__ counters,
+                                                   int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+    __shared__ double sD[16];
+    __shared__ int sK[16];
+    const int cnt = counters[0];
+    const int nl = 2 * max(counters[3], 1);  // candidate lists per slot
+    const int lane = threadIdx.x & 63, gl = lane & 31, base = lane & 32;
+    const int grp = threadIdx.x / 32, ngrp = blockDim.x / 32;  // at most 16
+    for (int64_t q = blockIdx.x; q < cnt; q += gridDim.x) {
+        const int64_t p = full_list[q];
+        bool ovf = q >= cap_slots;
+        int ntot = 0;
+        for (int l = 0; l < nl && !ovf; ++l) {
+            const int c = ccount[q * nl + l];
+            ovf = c > kMaxCand;
+            ntot += c;
+        }
+        if (ovf) {
+            if (threadIdx.x == 0) ovf_list[atomicAdd(&counters[2], 1)] = (int32_t)p;
+            continue;
+        }
+        const double nx = xnorm64 != nullptr ? xnorm64[p] : 1.0;
+        double best = INFINITY;
+        int bk = 0x7fffffff;
+        for (int m = grp; m < ntot; m += ngrp) {
+            int l = 0, r = m;  // the m-th candidate: list l, rank r
+            for (int c = ccount[q * nl]; r >= c; c = ccount[q * nl + l]) {
+                r -= c;
+                ++l;
+            }
+            const int k = cand[(q * nl + l) * kMaxCand + r];
             const CT *const row[1] = {C + (size_t)k * d};
             double D[1];
-            sqdist64<CT, 1>(X + (size_t)p * d, row, d, nx, xnorm64 != nullptr, ip != 0, D);
+            group_sqdist64<CT, 1>(X + (size_t)p * d, row, d, nx, xnorm64 != nullptr, ip != 0, gl, base, D);
             if (D[0] < best || (D[0] == best && k < bk)) {
                 best = D[0];
                 bk = k;
             }
         }
-        a_out[p] = bk;
-        if (d1_out != nullptr) d1_out[p] = (float)best;
+        if (gl == 0) {
+            sD[grp] = best;
+            sK[grp] = bk;
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            for (int g = 1; g < ngrp; ++g) {
+                if (sD[g] < best || (sD[g] == best && sK[g] < bk)) {
+                    best = sD[g];
+                    bk = sK[g];
+                }
+            }
+            a_out[p] = bk;
+            if (d1_out != nullptr) d1_out[p] = (float)best;
+        }
+        __syncthreads();
     }
 }
 
@@ -1333,8 +1534,12 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cnt = counters[0];
     if (d > 128 || cnt < kStagedMinList) {
-        recheck_cand_rows<CT>(X, d, C, xnorm64, full_list, cand, ccount, cap_slots, ovf_list, counters, a_out, d1_out,
-                              ip);
+        if (d <= kGroupMaxD)
+            recheck_cand_group<CT>(X, d, C, xnorm64, full_list, cand, ccount, cap_slots, ovf_list, counters, a_out,
+                                   d1_out, ip);
+        else
+            recheck_cand_rows<CT>(X, d, C, xnorm64, full_list, cand, ccount, cap_slots, ovf_list, counters, a_out,
+                                  d1_out, ip);
         return;
     }
     for (int64_t q0 = ((int64_t)blockIdx.x * 4 + w) * 64; q0 < cnt; q0 += (int64_t)gridDim.x * 4 * 64) {
@@ -1417,7 +1622,10 @@ __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ 
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cnt = counters[1];
     if (d > 128 || cnt < kStagedMinList) {
-        recheck_pair_rows<CT>(X, d, C, xnorm64, pair_list, counters, a_out, d1_out, ip);
+        if (d <= kGroupMaxD)
+            recheck_pair_group<CT>(X, d, C, xnorm64, pair_list, counters, a_out, d1_out, ip);
+        else
+            recheck_pair_rows<CT>(X, d, C, xnorm64, pair_list, counters, a_out, d1_out, ip);
         return;
     }
     for (int64_t q0 = ((int64_t)blockIdx.x * 4 + w) * 64; q0 < cnt; q0 += (int64_t)gridDim.x * 4 * 64) {

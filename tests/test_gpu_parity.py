@@ -83,6 +83,28 @@ def test_each_near_tie_path_is_taken(gpu_lib, kind, path, score):
     assert prof[path] > 0, prof
 
 
+@pytest.mark.parametrize("score", SCORES)
+@pytest.mark.parametrize("metric", ["l2", "cosine"])
+@pytest.mark.parametrize("d", [64, 201, 768, 1000])
+@pytest.mark.parametrize("kind,path", [("dup", "paired"), ("dup3", "windowed"), ("dup40", "rechecked")])
+def test_short_list_paths(gpu_lib, kind, path, d, metric, score):
+    """Short near-tie lists (3,000 points) take the checks built for them:
+    the window pass split over several tile slices of K = 600 centroids,
+    each with its own candidate lists, and the fp64 distances summed by
+    32-lane groups that pass the running sum from lane to lane (d <= 768;
+    d = 1000 takes one lane per point), including a d that is not a multiple
+    of four.  Every label must equal the oracle's."""
+    fk = gpu_lib
+    X, C = synth.adversarial(7, 3000, d, 600, kind)
+    a_ref, _, _ = oracle.assign(X, C, metric)
+    fk.fk_profile_enable(True)
+    a, _ = fk.fk_assign(dev(X), dev(C), metric=metric, score=score)
+    prof = fk.fk_profile_read()
+    fk.fk_profile_enable(False)
+    np.testing.assert_array_equal(host(a), a_ref)
+    assert prof[path] > 0, prof
+
+
 NEAR_TIE_CAP_MIN = 65536  # the window pass collects candidates for max(N/8, 65,536) listed points
 
 
