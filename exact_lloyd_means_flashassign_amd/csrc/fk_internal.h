@@ -109,7 +109,7 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
                           const NearTies &nt, const SplitC &sc, bool ip, int32_t *a_out, float *d1_out,
                           hipStream_t s);
 
-// Radix sort of (key = assign[i], value = i), stable, atomic-free.  Writes the
+// Radix sort of (key = assign[i], value = i), stable, no global atomics.  Writes the
 // sorted keys and the permutation.  tmp* are N-sized scratch arrays.
 size_t sort_scratch_bytes(int64_t N);
 hipError_t launch_sort_by_key(const int32_t *keys, int64_t N, int K, int32_t *keys_sorted, int32_t *perm,
