@@ -300,6 +300,35 @@ __device__ __forceinline__ void sum_partials(int k, int64_t sa, int64_t sb, int6
     }
 }
 
+// A cluster that crosses at most kShortCross boundaries is finished by the
+// one wave that finds it: each lane takes columns lane, lane + 64, ... and
+// issues the loads of all its partials of a column at once, then adds them
+// in segment order: plast of the first segment, then pfirst of each later
+// one.  That is the order sum_partials gives with at most eight later
+// segments (wave w's sum is then just segment sa+1+w, added in wave order),
+// so both give the same bits.  Without it a workgroup would run through
+// d / 64 dependent load rounds, two barriers each, per cluster (1M x 768,
+// K = 4096: about 1,900 such clusters, 62 us).
+constexpr int kShortCross = kFixWaves;
+__device__ __forceinline__ void wave_sum_partials(int k, int64_t sa, int64_t sb, int64_t n, int d,
+                                                  const double *__restrict__ pfirst,
+                                                  const double *__restrict__ plast, float *__restrict__ C_out) {
+    const int lane = threadIdx.x & 63;
+    const int np = (int)(sb - sa);  // later segments, 1 .. kShortCross
+    for (int c = lane; c < d; c += 64) {
+        double v[kShortCross + 1];
+        v[0] = plast[sa * d + c];
+#pragma unroll
+        for (int i = 1; i <= kShortCross; ++i)
+            if (i <= np) v[i] = pfirst[(sa + i) * d + c];
+        double t = v[0];
+#pragma unroll
+        for (int i = 1; i <= kShortCross; ++i)
+            if (i <= np) t += v[i];
+        C_out[(int64_t)k * d + c] = (float)(t / (double)n);
+    }
+}
+
 // Rows in several batches: one workgroup per segment boundary b; if b is the
 // first boundary a cluster crosses, the workgroup adds its partials into the
 // fp64 sums.  Most workgroups find nothing to do and exit at once.
@@ -320,9 +349,10 @@ __global__ __launch_bounds__(kFixWaves * 64) void k_seg_fixup(const int32_t *__r
 // G workgroups), one per wave (counts_out[k] from the offsets; an empty
 // cluster's previous centroid copied by the whole wave, coalesced); then the
 // segment boundaries 8g .. 8g+7 (then 8(g + G) ..): each wave checks one of
-// them, and the whole workgroup sums the partials of every cluster found
-// crossing its first boundary there, divided into C_out.  Checking eight
-// boundaries at once keeps their dependent loads in parallel.
+// them; a cluster found crossing its first boundary there is summed and
+// divided into C_out by that wave when it crosses at most kShortCross
+// boundaries, else by the whole workgroup.  Checking eight boundaries at
+// once keeps their dependent loads in parallel.
 __global__ __launch_bounds__(kFixWaves * 64) void k_seg_finish(const int32_t *__restrict__ ks,
                                                               const int32_t *__restrict__ offsets, int64_t N, int d,
                                                               int K, int srows, int64_t nbound,
@@ -343,7 +373,14 @@ __global__ __launch_bounds__(kFixWaves * 64) void k_seg_finish(const int32_t *__
     for (int64_t b0 = (int64_t)blockIdx.x * kFixWaves; b0 < nbound; b0 += (int64_t)gridDim.x * kFixWaves) {
         int k = -1;
         int64_t sa = 0, sb = 0, n = 0;
-        if (b0 + w < nbound && !first_crossing(b0 + w, ks, offsets, N, K, srows, &k, &sa, &sb, &n)) k = -1;
+        if (b0 + w < nbound && first_crossing(b0 + w, ks, offsets, N, K, srows, &k, &sa, &sb, &n)) {
+            if (sb - sa <= kShortCross) {
+                wave_sum_partials(k, sa, sb, n, d, pfirst, plast, C_out);
+                k = -1;
+            }
+        } else {
+            k = -1;
+        }
         if (lane == 0) {
             jk[w] = k;
             jsa[w] = sa;
