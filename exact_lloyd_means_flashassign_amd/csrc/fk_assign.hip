@@ -453,7 +453,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         };
         // global -> LDS buffer directly (DMA): stage t of the split copy and
         // of -||c||^2/2
-        auto dma_stage = [&](int buf, int t) {
+        auto dma_to = [&](const __bf16 *cs, const float *ncn, __bf16 *dh, __bf16 *dl, float *dn, int t) {
+            const __amdgpu_buffer_rsrc_t cs_rsrc =
+                __builtin_amdgcn_make_buffer_rsrc((void *)cs, (short)0, (int)A.cs_bytes, 0x00020000);
+            const __amdgpu_buffer_rsrc_t ncn_rsrc =
+                __builtin_amdgcn_make_buffer_rsrc((void *)ncn, (short)0, A.ntiles * ROWS * 4, 0x00020000);
             constexpr int RCH = LDB / 8;    // 16-byte chunks per padded row
             constexpr int NINS = ROWS * RCH / 64;
             static_assert(!DMA || (ROWS * RCH) % 64 == 0, "whole wave loads per buffer");
@@ -467,15 +471,15 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     const int q = j * 64 + lane;
                     const int row = q / RCH, c = q % RCH;
                     const unsigned o = (unsigned)row * (4u * A.sw) + (c < DP / 8 ? c : 0) * 16u;
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(cs_rsrc, (lds_ptr)&sCh[buf][j * 512], 16, o, tile_b, 0, 0);
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(cs_rsrc, (lds_ptr)&sCl[buf][j * 512], 16, o,
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(cs_rsrc, (lds_ptr)(dh + j * 512), 16, o, tile_b, 0, 0);
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(cs_rsrc, (lds_ptr)(dl + j * 512), 16, o,
                                                              tile_b + 2u * A.sw, 0, 0);
                 }
             }
             if (wv == WAVES - 1) {
 #pragma unroll
                 for (int j = 0; j < ROWS / 64; ++j)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ncn_rsrc, (lds_ptr)&sN[buf][j * 64], 4, 4u * lane,
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(ncn_rsrc, (lds_ptr)(dn + j * 64), 4, 4u * lane,
                                                              (unsigned)(t * ROWS + j * 64) * 4u, 0, 0);
             }
         };
@@ -845,7 +849,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             }
         }
         if constexpr (DMA) {
-            dma_stage(0, tb);
+            dma_to(A.Cs, A.ncn, sCh[0], sCl[0], sN[0], tb);
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         } else {
             load_stage(tb, 0);
@@ -875,10 +879,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 else
                     load_x(ch, std::false_type{});
             }
-            if constexpr (DMA) {
-                // into the other buffer, which no wave reads in this stage
-                if (more) dma_stage(buf ^ 1, nt);
-            } else {
+            if constexpr (!DMA) {
                 if (more) load_stage(nt, nc);
             }
 
@@ -904,8 +905,20 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             }
 
             if constexpr (PHASED) {
-                const __bf16 *sh = &sCh[buf][jl * LDB + 8 * h];
-                const __bf16 *sl = &sCl[buf][jl * LDB + 8 * h];
+            // The phased stage reads its LDS buffer (rh, rl, rn) and, with
+            // DMA, first sends the next stage into the other one (wh, wl,
+            // wn).  Both come in as restrict pointers, one inlined copy per
+            // buffer: the compiler then knows that this stage's LDS reads do
+            // not touch what the in-flight loads write, and does not make
+            // them wait for those loads.
+            auto phased = [&](const __bf16 *__restrict__ rh, const __bf16 *__restrict__ rl,
+                              const float *__restrict__ rn, __bf16 *__restrict__ wh, __bf16 *__restrict__ wl,
+                              float *__restrict__ wn, const __bf16 *__restrict__ cs,
+                              const float *__restrict__ ncn) {
+                // into the other buffer, which no wave reads in this stage
+                if (DMA && more) dma_to(cs, ncn, wh, wl, wn, nt);
+                const __bf16 *sh = rh + jl * LDB + 8 * h;
+                const __bf16 *sl = rl + jl * LDB + 8 * h;
 #pragma unroll
                 for (int cb = 0; cb < CB; ++cb) {
                     // phase 1: lo.hi + hi.lo, from zero; each step's LDS
@@ -935,7 +948,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     // phase 2: + -||c||^2/2 (fp32) of this lane's 16 centroid rows
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const float4 nv = *reinterpret_cast<const float4 *>(&sN[buf][cb * 32 + 8 * q + 4 * h]);
+                        const float4 nv = *reinterpret_cast<const float4 *>(rn + cb * 32 + 8 * q + 4 * h);
 #pragma unroll
                         for (int b = 0; b < PB; ++b) {
                             acc[b][0][4 * q + 0] += nv.x;
@@ -966,6 +979,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     // done, so the prefetch registers are free for the rest
                     if (!DMA && CB > 1 && cb == 0 && more) store_stage(buf ^ 1, nc);
                 }
+            };
+                if (buf == 0)
+                    phased(sCh[0], sCl[0], sN[0], sCh[1], sCl[1], sN[1], A.Cs, A.ncn);
+                else
+                    phased(sCh[1], sCl[1], sN[1], sCh[0], sCl[0], sN[0], A.Cs, A.ncn);
             } else if constexpr (ONEACC) {
                 // x.c ~ hi.lo + lo.hi + hi.hi, one 32-centroid block after
                 // another (only one block's operands live at a time)
