@@ -382,9 +382,6 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     // loads past its end read zero)
     const __amdgpu_buffer_rsrc_t cs_rsrc =
         __builtin_amdgcn_make_buffer_rsrc((void *)A.Cs, (short)0, SPLIT ? (int)A.cs_bytes : 0, 0x00020000);
-    // and of -||c||^2/2 (ntiles * ROWS values)
-    const __amdgpu_buffer_rsrc_t ncn_rsrc =
-        __builtin_amdgcn_make_buffer_rsrc((void *)A.ncn, (short)0, DMA ? A.ntiles * ROWS * 4 : 0, 0x00020000);
 
     // Assign mode: workgroup g takes points [g*BM, (g+1)*BM).  Collect mode:
     // the workgroups stride over (slot group, tile slice) units of the full

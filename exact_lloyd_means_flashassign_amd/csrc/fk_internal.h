@@ -24,12 +24,14 @@ constexpr int kSortThreads = kSortWaves * kWave;
 
 // ---- segmented reduction geometry -----------------------------------------
 constexpr int kSegWaves = 4;
-// Sorted rows per wave segment, 64..2048: enough segments to keep about
-// 32 MB of rows in flight (eight rows per wave: 8192 waves up to d = 128,
-// fewer for longer rows, at least 1024) while keeping each segment long, since
-// every cluster that crosses a segment boundary leaves partial sums.
+// Sorted rows per wave segment, 64..2048: the longest segments (up to 2048
+// rows) that still give at least 2048 waves up to d = 128 (fewer for longer
+// rows, at least 1024), since every cluster that crosses a segment boundary
+// leaves partial sums that the fix-up reads back.  At 16M rows that is 8192
+// segments of 2048 rows; at 2^20 rows x 128, 512-row segments took the
+// update 139 -> 130 us against the 128-row ones of a target of 8192 waves.
 inline int seg_rows(int64_t N, int d) {
-    int64_t target = ((int64_t)1 << 20) / (d > 128 ? d : 128);
+    int64_t target = ((int64_t)1 << 18) / (d > 128 ? d : 128);
     if (target < 1024) target = 1024;
     int r = 2048;
     while (r > 64 && N / r < target) r >>= 1;

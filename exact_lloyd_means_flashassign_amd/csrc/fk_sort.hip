@@ -292,10 +292,11 @@ static int key_bits(int K) {
 
 // 64-key rows per wave: tiles of 8 waves x 16 rows (8192 keys) when that
 // still leaves at least 512 tiles (two per CU), else shorter tiles, so that a
-// small sort still spreads over the chip (at 2^20 keys: 512 tiles of 2048).
+// small sort still spreads over the chip: 4096 keys while that leaves 256
+// tiles (at 2^20 keys: 4 us faster than 512 tiles of 2048), then 2048.
 static int sort_rows(int64_t N) {
     if (N >= (int64_t)512 * kSortWaves * 16 * kWave) return 16;
-    if (N >= (int64_t)512 * kSortWaves * 8 * kWave) return 8;
+    if (N >= (int64_t)256 * kSortWaves * 8 * kWave) return 8;
     return 4;
 }
 constexpr int kMinSortTile = kSortWaves * 4 * kWave;
