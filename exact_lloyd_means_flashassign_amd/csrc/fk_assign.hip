@@ -1961,6 +1961,58 @@ hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C,
                                   sc.cs != nullptr, s);
 }
 
+// The objective terms: d1[p] = the fp64 distance of point p to its assigned
+// centroid a[p] by the definition (direct differences in increasing j, no
+// fused multiply-add; cosine on the fp64-normalised rows; inner product
+// -x.c), rounded once to fp32 -- the oracle's D1 rounded, bit for bit.  One
+// 32-lane group per point with coalesced row loads (d <= kGroupMaxD), else
+// one lane per point.
+// Inner product: the sums subtract each product from +0, which gives the
+// negated dot product -(x.c) in value, rounding included (rounding to nearest
+// is symmetric in sign); only a zero differs, +0 where -(x.c) is -0.
+__device__ __forceinline__ float exact_d1_value(double D, int ip) {
+    return (float)((ip && D == 0.0) ? -0.0 : D);
+}
+template <typename CT>
+__global__ __launch_bounds__(256) void k_exact_d1(const float *__restrict__ X, int64_t N, int d,
+                                                  const CT *__restrict__ C, const double *__restrict__ xnorm64,
+                                                  const int32_t *__restrict__ a, float *__restrict__ d1, int ip) {
+    if (d <= kGroupMaxD) {
+        const int lane = threadIdx.x & 63, gl = lane & 31, base = lane & 32;
+        const int64_t ng = (int64_t)gridDim.x * (blockDim.x / 32);
+        for (int64_t p = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / 32; p < N; p += ng) {
+            const CT *const row[1] = {C + (size_t)a[p] * d};
+            double D[1];
+            group_sqdist64<CT, 1>(X + (size_t)p * d, row, d, xnorm64 != nullptr ? xnorm64[p] : 1.0,
+                                  xnorm64 != nullptr, ip != 0, gl, base, D);
+            if (gl == 0) d1[p] = exact_d1_value(D[0], ip);
+        }
+    } else {
+        for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < N; p += (int64_t)gridDim.x * blockDim.x) {
+            const CT *const row[1] = {C + (size_t)a[p] * d};
+            double D[1];
+            sqdist64<CT, 1>(X + (size_t)p * d, row, d, xnorm64 != nullptr ? xnorm64[p] : 1.0, xnorm64 != nullptr,
+                            ip != 0, D);
+            d1[p] = exact_d1_value(D[0], ip);
+        }
+    }
+}
+
+hipError_t launch_exact_d1(const float *X, int64_t N, int d, const float *C32, const double *C64,
+                           const double *xnorm64, const int32_t *a, float *d1, bool ip, hipStream_t s) {
+    if (N <= 0) return hipSuccess;
+    const int64_t per_block = d <= kGroupMaxD ? 8 : 256;  // points per workgroup pass
+    int64_t nb = cdiv(N, per_block);
+    if (nb > 8192) nb = 8192;
+    if (C64 != nullptr)
+        hipLaunchKernelGGL(k_exact_d1<double>, dim3((unsigned)nb), dim3(256), 0, s, X, N, d, C64, xnorm64, a, d1,
+                           ip ? 1 : 0);
+    else
+        hipLaunchKernelGGL(k_exact_d1<float>, dim3((unsigned)nb), dim3(256), 0, s, X, N, d, C32, xnorm64, a, d1,
+                           ip ? 1 : 0);
+    return hipGetLastError();
+}
+
 hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma, const float *C32,
                           const double *C64, const float *ncn, int K, const float *scal, const double *xnorm64,
                           const NearTies &nt, const SplitC &sc, bool ip, int32_t *a_out, float *d1_out,

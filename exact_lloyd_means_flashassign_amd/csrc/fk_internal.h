@@ -111,6 +111,11 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
                           const NearTies &nt, const SplitC &sc, bool ip, int32_t *a_out, float *d1_out,
                           hipStream_t s);
 
+// d1[p] = fp32 rounding of the fp64 direct-difference distance of point p to
+// centroid a[p] (C32 for L2 and inner product, C64 normalised for cosine).
+hipError_t launch_exact_d1(const float *X, int64_t N, int d, const float *C32, const double *C64,
+                           const double *xnorm64, const int32_t *a, float *d1, bool ip, hipStream_t s);
+
 // Radix sort of (key = assign[i], value = i), stable, no global atomics.  Writes the
 // sorted keys and the permutation.  tmp* are N-sized scratch arrays.
 size_t sort_scratch_bytes(int64_t N);

@@ -119,8 +119,12 @@ size_t fk_workspace_size(int64_t N, int32_t d, int32_t K, int32_t metric, int64_
 
 /*
  * FlashAssign: assign[i] = the nearest centroid of point i (lowest index on
- * ties), and, when min_dist is not NULL, min_dist[i] = its squared distance
- * (fp32; the fp64 value rounded for rescored points).  score is an
+ * ties), and, when min_dist is not NULL, min_dist[i] = its distance by the
+ * definition -- sum_j (x_j - c_j)^2 in fp64 by direct differences in
+ * increasing j (cosine: of the fp64-normalised rows; inner product: -x.c),
+ * rounded once to fp32, so sum_i min_dist[i] is the objective of the
+ * iteration's centroids (an extra pass over X that reads each point's row
+ * and its centroid's).  score is an
  * fk_score.  X, C, assign and min_dist are device pointers.  The N x K
  * distance matrix is never stored: each workgroup keeps a block of points in
  * registers, streams centroid tiles through LDS into MFMA (fp32, or
@@ -319,7 +323,8 @@ const char *fk_last_error(void);
 enum {
     FK_PH_PREP = 0,      /* centroid norms (and cosine normalisation)       */
     FK_PH_ASSIGN = 1,    /* the FlashAssign kernel                          */
-    FK_PH_RECHECK = 2,   /* fp64 rescoring of near-tie points               */
+    FK_PH_RECHECK = 2,   /* fp64 rescoring of near-tie points (and the
+                            exact min_dist pass when it is asked for)       */
     FK_PH_SORT = 3,      /* radix sort (the inverse index)                  */
     FK_PH_REDUCE = 4,    /* segmented reduction (with the cluster offsets;
                             rows in one batch: also the divide by count of

@@ -32,7 +32,7 @@ def test_assign_matches_oracle(gpu_lib, N, d, K, kind, score):
     a, md = fk.fk_assign(dev(X), dev(C), with_min_dist=True, score=score)
     a = host(a)
     np.testing.assert_array_equal(a, a_ref)
-    check_min_dist(host(md), D1, X, C, score=score)
+    check_min_dist(host(md), D1)
 
 
 @pytest.mark.parametrize("score", SCORES)
@@ -46,7 +46,7 @@ def test_assign_cosine_matches_oracle(gpu_lib, N, d, K, kind, score):
     a_ref, D1, _ = oracle.assign(X, C, "cosine")
     a, md = fk.fk_assign(dev(X), dev(C), metric="cosine", with_min_dist=True, score=score)
     np.testing.assert_array_equal(host(a), a_ref)
-    check_min_dist(host(md), D1, X, C, "cosine", score=score)
+    check_min_dist(host(md), D1)
 
 
 @pytest.mark.parametrize("N,d,K", [(1, 4, 1), (1000, 16, 64), (5000, 128, 1024), (4096 * 3 + 5, 8, 300),
@@ -129,7 +129,7 @@ def test_near_tie_paths_at_scale(gpu_lib, kind, d, metric, score):
     prof = fk.fk_profile_read()
     fk.fk_profile_enable(False)
     np.testing.assert_array_equal(host(a), a_ref)
-    check_min_dist(host(md), D1, X, C, metric, score=score)
+    check_min_dist(host(md), D1)
     cap = max(N // 8, NEAR_TIE_CAP_MIN)
     if kind == "pairs":
         assert prof["paired"] >= NEAR_TIE_CAP_MIN, prof
@@ -329,7 +329,7 @@ def test_inner_product_assign_matches_oracle(gpu_lib, N, d, K, kind, score):
     a_ref, D1, _ = oracle.assign(X, C, "inner_product")
     a, md = fk.fk_assign(dev(X), dev(C), metric="inner_product", with_min_dist=True, score=score)
     np.testing.assert_array_equal(host(a), a_ref)
-    check_min_dist(host(md), D1, X, C, metric="inner_product", score=score)
+    check_min_dist(host(md), D1)
 
 
 @pytest.mark.parametrize("score", SCORES)
