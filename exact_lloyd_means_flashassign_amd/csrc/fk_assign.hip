@@ -2237,7 +2237,7 @@ __global__ __launch_bounds__(256) void k_knn_finish(const float *__restrict__ Q,
             bj = t ? j : bj;
         }
         idx[q * ld + r] = bi;
-        dist[q * ld + r] = (float)b;
+        dist[q * ld + r] = exact_d1_value(b, ip);
 #pragma unroll
         for (int j = 0; j < TL; ++j) D[j] = (j == bj) ? (double)INFINITY : D[j];
 #pragma unroll
@@ -2320,7 +2320,7 @@ __global__ __launch_bounds__(256) void k_knn_full(const float *__restrict__ Q, i
                         btt = wt[ww];
                     }
                 idx[q * ld + r] = bbi;
-                dist[q * ld + r] = (float)bb;
+                dist[q * ld + r] = exact_d1_value(bb, ip);
                 win_t = btt;
             }
             __syncthreads();

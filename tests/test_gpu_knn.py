@@ -24,7 +24,8 @@ def _check(fk, Q, DB, k, metric, score):
     i_ref, d_ref = oracle.knn(Q, DB, k, metric)
     gi, gd = host(idx), host(dist)
     np.testing.assert_array_equal(gi, i_ref)
-    np.testing.assert_array_equal(gd, d_ref.astype(np.float32))
+    # distances bit for bit (inner product: -0 for a zero dot product)
+    np.testing.assert_array_equal(gd.view(np.uint32), d_ref.astype(np.float32).view(np.uint32))
 
 
 @pytest.mark.parametrize("score", SCORES)
