@@ -336,14 +336,14 @@ fk_status step_assign(const Ctx &c, const float *X, int64_t rows, const float *C
     {
         PhaseScope ph(FK_PH_ASSIGN, c.s);
         FK_TRY(launch_flash_assign(X, rows, c.d, C_use, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal), xn,
-                                   a_out, nullptr, nt, c.split(), c.metric == FK_METRIC_INNER_PRODUCT, c.s),
+                                   a_out, nt, c.split(), c.metric == FK_METRIC_INNER_PRODUCT, c.s),
                "flash assign");
     }
     {
         PhaseScope ph(FK_PH_RECHECK, c.s);
         const double *c64 = normalises(c.metric) ? at<double>(c.ws, c.L.c64) : nullptr;
         FK_TRY(launch_recheck(X, rows, c.d, C_use, C, c64, at<float>(c.ws, c.L.ncn), c.K, at<float>(c.ws, c.L.scal),
-                              xn, nt, c.split(), c.metric == FK_METRIC_INNER_PRODUCT, a_out, nullptr, c.s),
+                              xn, nt, c.split(), c.metric == FK_METRIC_INNER_PRODUCT, a_out, c.s),
                "near-tie recheck");
         if (d1_out != nullptr)
             FK_TRY(launch_exact_d1(X, rows, c.d, C, c64, xn, a_out, d1_out, c.metric == FK_METRIC_INNER_PRODUCT, c.s),

@@ -47,7 +47,6 @@ struct FlashArgs {
     const float *scal;
     const double *xnorm64;  // cosine: fp64 row norms of X, else null
     int32_t *a_out;
-    float *d1_out;
     int32_t *full_list;  // near ties with a third score within the window
     float *full_thr;     // their score threshold
     int32_t *pair_list;  // near ties settled by the top two: (point, k1, k2)
@@ -697,9 +696,11 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         // xl2[b] holds 2 e_i, the near-tie window.
         const float u = 5.9604645e-8f;
         // roundings per accumulator path: at most d + 3 for -||c||^2/2 and
-        // the fp32 (or hi.hi) products; the split cross terms, below 2^-7 of
-        // the products in size, pass through at most 2d + 1 and add less than
-        // 0.016 (2d + 1) u ||x|| ||c||, which the 1.0625 factor covers
+        // the fp32 (or hi.hi) products; the split cross terms come first,
+        // their absolute values sum to at most 2 (1 + 2^-8) 2^-9 ||x|| ||c||
+        // < 0.004 ||x|| ||c||, and passing through at most 3d + 1 roundings
+        // they add less than 0.004 (3d + 1) u ||x|| ||c||, which the 1.0625
+        // factor covers
         const float g = (float)(ONEACC ? 3 * d + 4 : d + 4) * u + (A.xnorm64 != nullptr ? 8.f * u : 0.f);
         auto point_bounds = [&]() {
             const float M = A.scal[0] * (1.f + g);
@@ -1174,7 +1175,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             const int si2 = wsec ? wi2 : li1;
             const float s3 = wsec ? fmaxf(w3, l1) : fmaxf(w2, l2);
 
-            const float xnt = xn[b], e2 = xl2[b];
+            const float e2 = xl2[b];
             const int64_t p = sbase + b * 32 + jl;
             const bool valid = (h == 0) && p < A.N;
             // near tie: the exact winner is not certain
@@ -1182,10 +1183,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             // only the top two can win: every other score is more than 2e below
             const bool pair = flagged && ((w1 - s3) > e2);
             const bool full = flagged && !pair;
-            if (valid) {
-                A.a_out[p] = wi1;
-                if (A.d1_out != nullptr) A.d1_out[p] = A.ip ? -w1 : fmaxf(xnt - 2.f * w1, 0.f);
-            }
+            if (valid) A.a_out[p] = wi1;
             const uint64_t lt = lanemask_lt();
             const uint64_t mp = __ballot(valid && pair);
             if (mp != 0ull) {
@@ -1301,7 +1299,7 @@ __device__ __forceinline__ void recheck_cand_rows(const float *__restrict__ X, i
                                                   const int32_t *__restrict__ cand,
                                                   const int32_t *__restrict__ ccount, int64_t cap_slots,
                                                   int32_t *__restrict__ ovf_list, int32_t *__restrict__ counters,
-                                                  int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+                                                  int32_t *__restrict__ a_out, int ip) {
 #pragma clang fp contract(off)
     const int cnt = counters[0];
     const int nl = 2 * max(counters[3], 1);  // candidate lists per slot
@@ -1329,7 +1327,6 @@ __device__ __forceinline__ void recheck_cand_rows(const float *__restrict__ X, i
             }
         }
         a_out[p] = bk;
-        if (d1_out != nullptr) d1_out[p] = (float)best;
     }
 }
 
@@ -1417,7 +1414,7 @@ __device__ __forceinline__ void recheck_pair_group(const float *__restrict__ X, 
                                                    const double *__restrict__ xnorm64,
                                                    const int32_t *__restrict__ pair_list,
                                                    const int32_t *__restrict__ counters,
-                                                   int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+                                                   int32_t *__restrict__ a_out, int ip) {
     const int cnt = counters[1];
     const int lane = threadIdx.x & 63, gl = lane & 31, base = lane & 32;
     const int64_t ng = (int64_t)gridDim.x * (blockDim.x / 32);
@@ -1432,7 +1429,6 @@ __device__ __forceinline__ void recheck_pair_group(const float *__restrict__ X, 
         if (gl == 0) {
             const bool second = (D[1] < D[0]) || (D[1] == D[0] && k2 < k1);
             a_out[p] = second ? k2 : k1;
-            if (d1_out != nullptr) d1_out[p] = (float)(second ? D[1] : D[0]);
         }
     }
 }
@@ -1447,7 +1443,7 @@ __device__ __forceinline__ void recheck_cand_group(const float *__restrict__ X, 
                                                    const int32_t *__restrict__ cand,
                                                    const int32_t *__restrict__ ccount, int64_t cap_slots,
                                                    int32_t *__restrict__ ovf_list, int32_t *__restrict__ counters,
-                                                   int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+                                                   int32_t *__restrict__ a_out, int ip) {
     __shared__ double sD[16];
     __shared__ int sK[16];
     const int cnt = counters[0];
@@ -1498,7 +1494,6 @@ __device__ __forceinline__ void recheck_cand_group(const float *__restrict__ X, 
                 }
             }
             a_out[p] = bk;
-            if (d1_out != nullptr) d1_out[p] = (float)best;
         }
         __syncthreads();
     }
@@ -1509,7 +1504,7 @@ __device__ __forceinline__ void recheck_pair_rows(const float *__restrict__ X, i
                                                   const double *__restrict__ xnorm64,
                                                   const int32_t *__restrict__ pair_list,
                                                   const int32_t *__restrict__ counters,
-                                                  int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+                                                  int32_t *__restrict__ a_out, int ip) {
     const int cnt = counters[1];
     for (int q = blockIdx.x * blockDim.x + threadIdx.x; q < cnt; q += gridDim.x * blockDim.x) {
         const int64_t p = pair_list[3 * (int64_t)q];
@@ -1521,7 +1516,6 @@ __device__ __forceinline__ void recheck_pair_rows(const float *__restrict__ X, i
                         ip != 0, D);
         const bool second = (D[1] < D[0]) || (D[1] == D[0] && k2 < k1);
         a_out[p] = second ? k2 : k1;
-        if (d1_out != nullptr) d1_out[p] = (float)(second ? D[1] : D[0]);
     }
 }
 
@@ -1540,7 +1534,7 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
                                                       const int32_t *__restrict__ cand,
                                                       const int32_t *__restrict__ ccount, int64_t cap_slots,
                                                       int32_t *__restrict__ ovf_list, int32_t *__restrict__ counters,
-                                                      int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+                                                      int32_t *__restrict__ a_out, int ip) {
 #pragma clang fp contract(off)
     constexpr int J = sizeof(CT) == 4 ? 16 : 8;  // dims per stage
     constexpr int JP = J + 1;                    // padded LDS row
@@ -1551,10 +1545,10 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
     if (d > 128 || cnt < kStagedMinList) {
         if (d <= kGroupMaxD)
             recheck_cand_group<CT>(X, d, C, xnorm64, full_list, cand, ccount, cap_slots, ovf_list, counters, a_out,
-                                   d1_out, ip);
+                                   ip);
         else
             recheck_cand_rows<CT>(X, d, C, xnorm64, full_list, cand, ccount, cap_slots, ovf_list, counters, a_out,
-                                  d1_out, ip);
+                                  ip);
         return;
     }
     for (int64_t q0 = ((int64_t)blockIdx.x * 4 + w) * 64; q0 < cnt; q0 += (int64_t)gridDim.x * 4 * 64) {
@@ -1611,7 +1605,6 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
         }
         if (ok) {
             a_out[p] = bk;
-            if (d1_out != nullptr) d1_out[p] = (float)best;
         }
     }
 }
@@ -1628,7 +1621,7 @@ __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ 
                                                       const double *__restrict__ xnorm64,
                                                       const int32_t *__restrict__ pair_list,
                                                       const int32_t *__restrict__ counters,
-                                                      int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+                                                      int32_t *__restrict__ a_out, int ip) {
 #pragma clang fp contract(off)
     constexpr int J = sizeof(CT) == 4 ? 16 : 8;  // dims per stage
     constexpr int JP = J + 1;                    // padded LDS row
@@ -1638,9 +1631,9 @@ __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ 
     const int cnt = counters[1];
     if (d > 128 || cnt < kStagedMinList) {
         if (d <= kGroupMaxD)
-            recheck_pair_group<CT>(X, d, C, xnorm64, pair_list, counters, a_out, d1_out, ip);
+            recheck_pair_group<CT>(X, d, C, xnorm64, pair_list, counters, a_out, ip);
         else
-            recheck_pair_rows<CT>(X, d, C, xnorm64, pair_list, counters, a_out, d1_out, ip);
+            recheck_pair_rows<CT>(X, d, C, xnorm64, pair_list, counters, a_out, ip);
         return;
     }
     for (int64_t q0 = ((int64_t)blockIdx.x * 4 + w) * 64; q0 < cnt; q0 += (int64_t)gridDim.x * 4 * 64) {
@@ -1687,7 +1680,6 @@ __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ 
         if (ok) {
             const bool second = (D2 < D1) || (D2 == D1 && k2 < k1);
             a_out[p] = second ? k2 : k1;
-            if (d1_out != nullptr) d1_out[p] = (float)(second ? D2 : D1);
         }
     }
 }
@@ -1705,7 +1697,7 @@ __global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, in
                                                  int K, const double *__restrict__ xnorm64,
                                                  const int32_t *__restrict__ flag_list,
                                                  const int32_t *__restrict__ counters, int P,
-                                                 int32_t *__restrict__ a_out, float *__restrict__ d1_out, int ip) {
+                                                 int32_t *__restrict__ a_out, int ip) {
 #pragma clang fp contract(off)
     extern __shared__ double sx[];  // P * d
     __shared__ double rb[4][RP];
@@ -1800,7 +1792,6 @@ __global__ __launch_bounds__(256) void k_recheck(const float *__restrict__ X, in
             }
             const int64_t p = flag_list[base + tid];
             a_out[p] = i;
-            if (d1_out != nullptr) d1_out[p] = (float)b;
         }
         __syncthreads();
     }
@@ -1899,10 +1890,15 @@ static hipError_t launch_fa_shape(const FlashArgs &A, hipStream_t s) {
     case 32: return launch_fa<32, 1, 1, 8, 4, true, COLLECT, SPLIT>(A, s);
     case 64: return launch_fa<64, 1, 1, 8, 4, true, COLLECT, SPLIT>(A, s);
     default:
-        // split scoring: 8 waves of 2 point blocks (a few values of the
-        // prologue spill; the tile loop does not)
+        // split scoring: 4 waves of 2 point blocks (two waves per SIMD), so
+        // two workgroups share a CU and one's prologue and epilogue overlap
+        // the other's products: 3 % faster than 8-wave workgroups at
+        // 16M x 128, K = 32768 and 5 % at 1M x 128, K = 1024, measured side
+        // by side, although the prologue then spills about 60 bytes per lane
+        // (once per workgroup; the sweep itself spills nothing), which the
+        // 8-wave form does not; one point block per wave: 10-14 % slower
         if constexpr (SPLIT)
-            return launch_fa<128, 2, 2, 8, 2, true, COLLECT, SPLIT>(A, s);
+            return launch_fa<128, 2, 2, 4, 2, true, COLLECT, SPLIT>(A, s);
         else
             return launch_fa<128, 2, 1, 4, 2, true, COLLECT, SPLIT>(A, s);
     }
@@ -1914,7 +1910,7 @@ static hipError_t launch_fa_score(const FlashArgs &A, bool split, hipStream_t s)
 }
 
 static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
-                            const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
+                            const float *scal, const double *xnorm64, int32_t *a_out,
                             const NearTies &nt, const SplitC &sc, bool ip) {
     const AssignShape sh = assign_shape(d);
     FlashArgs A;
@@ -1929,7 +1925,6 @@ static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, co
     A.scal = scal;
     A.xnorm64 = xnorm64;
     A.a_out = a_out;
-    A.d1_out = d1_out;
     A.full_list = nt.full_list;
     A.full_thr = nt.full_thr;
     A.pair_list = nt.pair_list;
@@ -1954,10 +1949,10 @@ int64_t near_tie_cap(int64_t N) {
 }
 
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
-                               const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
+                               const float *scal, const double *xnorm64, int32_t *a_out,
                                const NearTies &nt, const SplitC &sc, bool ip, hipStream_t s) {
     if (N <= 0) return hipSuccess;
-    return launch_fa_score<false>(flash_args(X, N, d, C, ncn, K, scal, xnorm64, a_out, d1_out, nt, sc, ip),
+    return launch_fa_score<false>(flash_args(X, N, d, C, ncn, K, scal, xnorm64, a_out, nt, sc, ip),
                                   sc.cs != nullptr, s);
 }
 
@@ -2015,8 +2010,7 @@ hipError_t launch_exact_d1(const float *X, int64_t N, int d, const float *C32, c
 
 hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma, const float *C32,
                           const double *C64, const float *ncn, int K, const float *scal, const double *xnorm64,
-                          const NearTies &nt, const SplitC &sc, bool ip, int32_t *a_out, float *d1_out,
-                          hipStream_t s) {
+                          const NearTies &nt, const SplitC &sc, bool ip, int32_t *a_out, hipStream_t s) {
     if (N <= 0) return hipSuccess;
     hipError_t e;
     // 1. near ties between two known centroids
@@ -2025,7 +2019,7 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
         if (nb > 4096) nb = 4096;
 #define FK_PAIR(KERNEL, CT, CP)                                                                                    \
     hipLaunchKernelGGL(KERNEL<CT>, dim3((unsigned)nb), dim3(256), 0, s, X, d, CP, xnorm64, nt.pair_list, nt.counters, \
-                       a_out, d1_out, ip ? 1 : 0)
+                       a_out, ip ? 1 : 0)
         if (C64 != nullptr)
             FK_PAIR(k_recheck_pair, double, C64);
         else
@@ -2034,7 +2028,7 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // 2. the full list: collect every centroid within each point's window
-    if ((e = launch_fa_score<true>(flash_args(X, N, d, C_mfma, ncn, K, scal, xnorm64, a_out, d1_out, nt, sc, ip),
+    if ((e = launch_fa_score<true>(flash_args(X, N, d, C_mfma, ncn, K, scal, xnorm64, a_out, nt, sc, ip),
                                    sc.cs != nullptr, s)) != hipSuccess)
         return e;
     // 3. fp64 over the collected candidates; overflows go to the last list
@@ -2044,7 +2038,7 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
         if (nb > 4096) nb = 4096;
 #define FK_CAND(KERNEL, CT, CP)                                                                                   \
     hipLaunchKernelGGL(KERNEL<CT>, dim3((unsigned)nb), dim3(256), 0, s, X, d, CP, xnorm64, nt.full_list, nt.cand,  \
-                       nt.ccount, cap, nt.ovf_list, nt.counters, a_out, d1_out, ip ? 1 : 0)
+                       nt.ccount, cap, nt.ovf_list, nt.counters, a_out, ip ? 1 : 0)
         if (C64 != nullptr)
             FK_CAND(k_recheck_cand, double, C64);
         else
@@ -2062,10 +2056,10 @@ hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma,
     if (nb > 2048) nb = 2048;
     if (C64 != nullptr)
         hipLaunchKernelGGL((k_recheck<double, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C64, K, xnorm64,
-                           nt.ovf_list, nt.counters + 2, P, a_out, d1_out, ip ? 1 : 0);
+                           nt.ovf_list, nt.counters + 2, P, a_out, ip ? 1 : 0);
     else
         hipLaunchKernelGGL((k_recheck<float, RP>), dim3((unsigned)nb), dim3(256), lds, s, X, d, C32, K, xnorm64,
-                           nt.ovf_list, nt.counters + 2, P, a_out, d1_out, ip ? 1 : 0);
+                           nt.ovf_list, nt.counters + 2, P, a_out, ip ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -2119,7 +2113,7 @@ hipError_t launch_knn_sweep(const float *Q, int64_t M, int d, const float *DB, c
                             int32_t *cand, float *score, float *win, float *tau, hipStream_t s) {
     if (M <= 0) return hipSuccess;
     NearTies nt{};
-    FlashArgs A = flash_args(Q, M, d, DB, ncn, Ndb, scal, qnorm64, nullptr, nullptr, nt, sc, ip);
+    FlashArgs A = flash_args(Q, M, d, DB, ncn, Ndb, scal, qnorm64, nullptr, nt, sc, ip);
     const KnnSlices ks = knn_slices(M, Ndb);
     A.knn_slices = ks.slices;
     A.knn_rows = ks.rows;

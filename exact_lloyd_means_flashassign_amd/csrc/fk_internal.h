@@ -101,15 +101,14 @@ struct NearTies {
 constexpr int kCandPerSlot = 16;
 int64_t near_tie_cap(int64_t N);
 hipError_t launch_flash_assign(const float *X, int64_t N, int d, const float *C, const float *ncn, int K,
-                               const float *scal, const double *xnorm64, int32_t *a_out, float *d1_out,
+                               const float *scal, const double *xnorm64, int32_t *a_out,
                                const NearTies &nt, const SplitC &sc, bool ip, hipStream_t s);
 // Settles every listed near tie exactly (fp64 direct-difference distances).
 // C_mfma is the centroid array the MFMA pass used (normalised for cosine); C32
 // (L2) or C64 (cosine, normalised in fp64) is the one the distances use.
 hipError_t launch_recheck(const float *X, int64_t N, int d, const float *C_mfma, const float *C32,
                           const double *C64, const float *ncn, int K, const float *scal, const double *xnorm64,
-                          const NearTies &nt, const SplitC &sc, bool ip, int32_t *a_out, float *d1_out,
-                          hipStream_t s);
+                          const NearTies &nt, const SplitC &sc, bool ip, int32_t *a_out, hipStream_t s);
 
 // d1[p] = fp32 rounding of the fp64 direct-difference distance of point p to
 // centroid a[p] (C32 for L2 and inner product, C64 normalised for cosine).
