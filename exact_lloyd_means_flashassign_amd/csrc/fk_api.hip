@@ -734,11 +734,16 @@ fk_status fk_lloyd_iter_stream(const float *X_host, int64_t N, int32_t d, const 
     FK_TRY(hipEventRecord(R->entry, c.s), "event record");
     FK_TRY(hipStreamWaitEvent(R->copy, R->entry, 0), "stream wait");
 
-    const int64_t nchunks = cdiv(N, chunk_rows);
-    for (int64_t ci = 0; ci < nchunks; ++ci) {
+    // Chunk lengths: a ramp that doubles from chunk_rows / 16 (when that is
+    // over 2^20 rows) up to chunk_rows.  Only the first copy is not hidden
+    // behind compute, and assigning a chunk takes about twice as long as
+    // copying one twice its length, so each copy still lands before it is
+    // needed while the first one is short.
+    int64_t len = chunk_rows / 16 > ((int64_t)1 << 20) ? chunk_rows / 16 : chunk_rows;
+    int64_t r0 = 0;
+    for (int64_t ci = 0; r0 < N; ++ci, r0 += len, len = (2 * len < chunk_rows ? 2 * len : chunk_rows)) {
         const int b = (int)(ci & 1);
-        const int64_t r0 = ci * chunk_rows;
-        const int64_t rows = (N - r0) < chunk_rows ? (N - r0) : chunk_rows;
+        const int64_t rows = (N - r0) < len ? (N - r0) : len;
         float *Xd = at<float>(workspace, L.xchunk[b]);
         int32_t *ad = at<int32_t>(workspace, L.achunk[b]);
         if (ci >= 2) FK_TRY(hipStreamWaitEvent(R->copy, R->freed[b], 0), "stream wait");

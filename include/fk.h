@@ -192,8 +192,10 @@ fk_status fk_lloyd_iter_noalloc(const float *X, int64_t N, int32_t d, const floa
 /*
  * Out-of-core Lloyd iteration: X_host is PINNED host memory (hipHostMalloc
  * or a pinned torch tensor) holding N x d floats; it is copied to the device
- * in chunks of chunk_rows rows, double-buffered on a copy stream that
- * overlaps the compute of the previous chunk.  Each chunk is assigned and
+ * in chunks of at most chunk_rows rows, double-buffered on a copy stream that
+ * overlaps the compute of the previous chunk (the first chunks ramp up, from
+ * chunk_rows / 16 doubling to chunk_rows when chunk_rows / 16 exceeds 2^20
+ * rows, so that the one copy not hidden behind compute is short).  Each chunk is assigned and
  * reduced into fp64 cluster sums; the means are taken once at the end.  The
  * result equals fk_lloyd_iter on the same data.  C_in, C_out and counts are
  * device pointers; assign_host, when not NULL, is pinned host memory of N
