@@ -69,10 +69,8 @@ struct FlashArgs {
     float *knn_score;
     float *knn_win;
     // knn_tau: per point, a score at or below its L-th best over all rows
-    // (the lists start from it instead of -inf), or null; knn_tau_out: the
-    // sweep only writes each point's L-th best score of its rows there
+    // (the lists start from it instead of -inf), or null
     const float *knn_tau;
-    float *knn_tau_out;
 };
 
 __device__ __forceinline__ uint64_t lanemask_lt() {
@@ -1140,9 +1138,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     }
                 }
                 const int64_t p = sbase + b * 32 + jl;
-                if (TAU && A.knn_tau_out != nullptr) {
-                    if (h == 0 && p < A.N) A.knn_tau_out[p] = mv[TL - 1];
-                } else if (h == 0 && p < A.N) {
+                if (h == 0 && p < A.N) {
                     const size_t o = ((size_t)p * A.knn_slices + blockIdx.y) * TL;
 #pragma unroll
                     for (int j = 0; j < TL; j += 4) {
@@ -1937,7 +1933,6 @@ static FlashArgs flash_args(const float *X, int64_t N, int d, const float *C, co
     A.ip = ip ? 1 : 0;
     A.cs_bytes = (unsigned)(cdiv(K, kCentroidPad) * kCentroidPad * 4 * (int64_t)sc.w);
     A.knn_tau = nullptr;
-    A.knn_tau_out = nullptr;
     return A;
 }
 
@@ -2108,6 +2103,36 @@ KnnSlices knn_slices(int64_t M, int64_t Ndb) {
     return KnnSlices{(int)cdiv(Ndb, R), (int)R};
 }
 
+// tau[q] = the TL-th best score of query q over the S1 lists of the sample
+// sweep (each list sorted best first, TL long, -inf where a slice had fewer
+// rows): TL steps of taking the best remaining list head.  Any value at or
+// below the query's TL-th best over all rows would do; this one is the
+// largest the sample gives.  One thread per query.
+template <int TL>
+__global__ __launch_bounds__(256) void k_knn_tau(const float *__restrict__ score, int64_t M, int S1,
+                                                 float *__restrict__ tau) {
+    const int64_t q = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (q >= M) return;
+    const float *base = score + (size_t)q * S1 * TL;
+    int pos[kKnnSampleSlices];
+    for (int i = 0; i < S1; ++i) pos[i] = 0;
+    float v = -INFINITY;
+    for (int r = 0; r < TL; ++r) {
+        int bi = 0;
+        float bv = -INFINITY;
+        for (int i = 0; i < S1; ++i) {
+            const float h = pos[i] < TL ? base[i * TL + pos[i]] : -INFINITY;
+            if (h > bv) {
+                bv = h;
+                bi = i;
+            }
+        }
+        v = bv;
+        ++pos[bi];
+    }
+    tau[q] = v;
+}
+
 hipError_t launch_knn_sweep(const float *Q, int64_t M, int d, const float *DB, const float *ncn, int Ndb,
                             const float *scal, const double *qnorm64, const SplitC &sc, bool ip, int k,
                             int32_t *cand, float *score, float *win, float *tau, hipStream_t s) {
@@ -2128,18 +2153,32 @@ hipError_t launch_knn_sweep(const float *Q, int64_t M, int d, const float *DB, c
     };
     // Every slice starts its lists from scratch, and while they fill, most
     // values are inserted (a pass of list updates each).  With several
-    // slices, a first sweep over the first kKnnSampleRows rows gives each
-    // query its L-th best score there, which is at or below its L-th best
-    // over all rows; the slices' lists start full of it.  Only for d <= 128:
-    // with streamed d-chunks the products outweigh the list updates and the
-    // extra sweep does not pay (measured at d = 768).
+    // slices, a first sweep over a sample of the first rows gives each query
+    // its L-th best score there, which is at or below its L-th best over all
+    // rows; the slices' lists start full of it, so only values above it are
+    // ever inserted.  The sample is S1 slices of kKnnSampleRows rows (up to
+    // 65,536 rows, at most a sixteenth of the database), each writing its
+    // own lists, which k_knn_tau merges into the L-th best of the sample:
+    // the larger the sample, the closer that comes to the final L-th best and
+    // the fewer values pass it.  Only for d <= 128: with streamed d-chunks
+    // the products outweigh the list updates and the extra sweep does not
+    // pay (measured at d = 768).
     if (tau != nullptr && d <= 128 && ks.slices >= 4 && Ndb >= 4 * kKnnSampleRows) {
+        int s1 = (int)(Ndb / (16 * (int64_t)kKnnSampleRows));
+        s1 = s1 < 1 ? 1 : s1 > kKnnSampleSlices ? kKnnSampleSlices : s1;
+        if (s1 > ks.slices) s1 = ks.slices;
         FlashArgs P = A;
-        P.knn_slices = 1;
+        P.knn_slices = s1;
         P.knn_rows = kKnnSampleRows;
-        P.knn_tau_out = tau;
         hipError_t e = sweep(P);
         if (e != hipSuccess) return e;
+        const int TL = knn_list_len(k);
+        const int64_t nb = cdiv(M, 256);
+        if (TL == 16)
+            hipLaunchKernelGGL((k_knn_tau<16>), dim3((unsigned)nb), dim3(256), 0, s, score, M, s1, tau);
+        else
+            hipLaunchKernelGGL((k_knn_tau<32>), dim3((unsigned)nb), dim3(256), 0, s, score, M, s1, tau);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
         A.knn_tau = tau;
     }
     return sweep(A);

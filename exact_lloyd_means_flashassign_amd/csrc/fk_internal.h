@@ -164,7 +164,8 @@ hipError_t launch_finalize(const double *sums, const int32_t *cnt, const float *
 constexpr int kMaxKnn = 24;
 constexpr int kKnnShort = 12;   // k <= 12: 16 candidates per query and slice, else 32
 constexpr int kKnnMaxSlices = 64;
-constexpr int kKnnSampleRows = 4096;  // rows of the threshold sweep (a multiple of kCentroidPad)
+constexpr int kKnnSampleRows = 4096;  // rows per slice of the threshold sweep (a multiple of kCentroidPad)
+constexpr int kKnnSampleSlices = 16;  // slices of the threshold sweep (at most)
 int knn_list_len(int k);
 struct KnnSlices {
     int slices, rows;  // rows per slice: a multiple of kCentroidPad
