@@ -39,7 +39,11 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t *__restrict__ p, int
 
 // NV loads of E consecutive floats per lane cover 64*E*NV columns starting at
 // blockIdx.y * 64*E*NV.  U rows are loaded before they are accumulated so that
-// U row reads per lane are in flight at once.  COS: rows are scaled by
+// U row reads per lane are in flight at once.  RP = 2 (rows of 128 floats or
+// fewer, E = 4, NV = 1): each half-wave loads one row, so one 16-byte load per
+// lane brings two rows (half the load instructions of 8-byte loads); the
+// lower half sums the pair's first rows and the upper half the second ones,
+// and a cluster's total is the lower half's sum plus the upper half's.  COS: rows are scaled by
 // 1/xnorm64 (cosine).  ACC: cluster sums are added to what sums holds (rows
 // fed in several batches; the finalize step divides).  Otherwise the rows
 // come in one batch and a cluster inside the segment is written to C_out as
@@ -47,7 +51,9 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t *__restrict__ p, int
 // k_seg_finish).  The column block blockIdx.y == 0 also writes offsets[k] =
 // the first sorted row whose key is >= k (offsets[K] = N): the entries between
 // two consecutive keys are written by the wave that sees the change.
-template <int NV, int E, int U, bool COS, bool ACC>
+// (paired rows: registers capped so that eight waves share a SIMD, which
+// keeps every segment of 2^24 rows resident at once)
+template <int NV, int E, int U, bool COS, bool ACC, int RP>
 __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X, int64_t N, int d, int K, int srows,
                                                     const int32_t *__restrict__ ks, const int32_t *__restrict__ perm,
                                                     const double *__restrict__ xnorm64, double *__restrict__ sums,
@@ -55,12 +61,16 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
                                                     int32_t *__restrict__ offsets, float *__restrict__ C_out) {
     // the wave index is uniform across the wave: taking it as a scalar makes
     // the segment bounds, the keys and every branch on them scalar
+    static_assert(RP == 1 || (RP == 2 && NV == 1 && E == 4), "paired rows take one 16-byte load per lane");
     const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    // RP = 2: the half-wave (which row of a pair) and the lane within it
+    const int half = RP == 2 ? lane >> 5 : 0;
+    const int cl = RP == 2 ? lane & 31 : lane;
     const int64_t seg = (int64_t)blockIdx.x * kSegWaves + w;
     const int64_t r0 = seg * srows;
     if (r0 >= N) return;
     const int64_t r1 = (r0 + srows < N) ? r0 + srows : N;
-    const int cbase = blockIdx.y * (64 * E * NV);
+    const int cbase = blockIdx.y * (64 / RP * E * NV);
 
     const int first_k = ks[r0];
     const int prev_k = r0 > 0 ? ks[r0 - 1] : -1;
@@ -77,11 +87,12 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
     if (offs != nullptr) mark(prev_k, first_k, r0);
 
     int col[NV];
-    bool cok[NV];
+    bool cok[NV], wok[NV];
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
-        col[v] = cbase + (v * 64 + lane) * E;
+        col[v] = cbase + (v * (64 / RP) + cl) * E;
         cok[v] = col[v] < d;  // d is a multiple of E, so the whole E-group is in or out
+        wok[v] = cok[v] && half == 0;  // paired rows: the lower half writes the totals
     }
 
     double acc[NV][E];
@@ -94,6 +105,11 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
 
     // the sum of cluster k, whose rows in this segment end before row rend
     auto flush = [&](int k, int64_t rend) {
+        if constexpr (RP == 2) {
+            // both halves get the same total (a0 + a1 == a1 + a0)
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc[0][e] += __shfl_xor(acc[0][e], 32);
+        }
         // keys are documented to lie in [0, K); a bad key is dropped rather
         // than written outside the sums
         if ((unsigned)k >= (unsigned)K) {
@@ -111,7 +127,11 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
             float *o = C_out + (int64_t)k * d;
 #pragma unroll
             for (int v = 0; v < NV; ++v) {
-                if (!cok[v]) continue;
+                if (!wok[v]) {
+#pragma unroll
+                    for (int e = 0; e < E; ++e) acc[v][e] = 0.0;
+                    continue;
+                }
 #pragma unroll
                 for (int e = 0; e < E; ++e) {
                     o[col[v] + e] = (float)(acc[v][e] / n);
@@ -126,7 +146,11 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
         const bool add = !part_first && !part_last;  // ACC here
 #pragma unroll
         for (int v = 0; v < NV; ++v) {
-            if (!cok[v]) continue;
+            if (!wok[v]) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) acc[v][e] = 0.0;
+                continue;
+            }
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const double val = add ? dst[col[v] + e] + acc[v][e] : acc[v][e];
@@ -142,8 +166,9 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
     // the segment repeat its last row, columns past d repeat the last valid
     // group), so that the wait for a batch never waits on later loads or on
     // the stores of a flush.
-    static_assert(64 % (2 * U) == 0, "batches must pair up inside a window");
-    constexpr int NBW = 64 / U;  // batches per window
+    constexpr int RB = U * RP;   // rows per batch
+    static_assert(64 % (2 * RB) == 0, "batches must pair up inside a window");
+    constexpr int NBW = 64 / RB;  // batches per window
     auto load_window = [&](int64_t r, int &kk, int &pp) {
         const int64_t q = (r + lane < r1) ? r + lane : r1 - 1;
         kk = ks[q];
@@ -155,7 +180,11 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
     auto load_batch = [&](float (&vb)[U][NV][E], double (&sb)[U], int pp, int off) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int p = __builtin_amdgcn_readlane(pp, off + u);
+            int p = __builtin_amdgcn_readlane(pp, off + RP * u);
+            if constexpr (RP == 2) {
+                const int p2 = __builtin_amdgcn_readlane(pp, off + 2 * u + 1);
+                p = half ? p2 : p;
+            }
             const float *row = X + (size_t)p * d;
             if (COS) sb[u] = 1.0 / xnorm64[p];
 #pragma unroll
@@ -178,7 +207,46 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
             }
         }
     };
+    auto add_row = [&](const float (&vb)[U][NV][E], const double (&sb)[U], int u) {
+#pragma unroll
+        for (int v = 0; v < NV; ++v)
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const double x = (double)vb[u][v][e];
+                acc[v][e] += COS ? x * sb[u] : x;
+            }
+    };
     auto consume = [&](const float (&vb)[U][NV][E], const double (&sb)[U], int kk, int64_t r, int off) {
+        if constexpr (RP == 2) {
+            // pair u: rows ra (lower half) and ra + 1 (upper half)
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t ra = r + off + 2 * u;
+                if (ra >= r1) break;
+                const int ka = __builtin_amdgcn_readlane(kk, off + 2 * u);
+                const int kb = __builtin_amdgcn_readlane(kk, off + 2 * u + 1);
+                const bool bv = ra + 1 < r1;
+                if (ka != cur) {
+                    if (offs != nullptr) mark(cur, ka, ra);
+                    flush(cur, ra);
+                    cur = ka;
+                    cstart = ra;
+                }
+                if (bv && kb == ka) {
+                    add_row(vb, sb, u);
+                } else {
+                    if (half == 0) add_row(vb, sb, u);
+                    if (bv) {
+                        if (offs != nullptr) mark(cur, kb, ra + 1);
+                        flush(cur, ra + 1);
+                        cur = kb;
+                        cstart = ra + 1;
+                        if (half == 1) add_row(vb, sb, u);
+                    }
+                }
+            }
+            return;
+        }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             if (r + off + u >= r1) break;
@@ -191,13 +259,7 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
                 cstart = rr;
             }
             // columns past d add into accumulators that are never written
-#pragma unroll
-            for (int v = 0; v < NV; ++v)
-#pragma unroll
-                for (int e = 0; e < E; ++e) {
-                    const double x = (double)vb[u][v][e];
-                    acc[v][e] += COS ? x * sb[u] : x;
-                }
+            add_row(vb, sb, u);
         }
     };
 
@@ -211,13 +273,13 @@ __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X,
 #pragma unroll
         for (int j = 0; j < NBW; j += 2) {
             // even batches sit in va, odd ones in vb
-            load_batch(vb, sb, ppc, (j + 1) * U);
-            consume(va, sa, kkc, r, j * U);
+            load_batch(vb, sb, ppc, (j + 1) * RB);
+            consume(va, sa, kkc, r, j * RB);
             if (j + 2 < NBW)
-                load_batch(va, sa, ppc, (j + 2) * U);
+                load_batch(va, sa, ppc, (j + 2) * RB);
             else
                 load_batch(va, sa, ppn, 0);
-            consume(vb, sb, kkc, r, (j + 1) * U);
+            consume(vb, sb, kkc, r, (j + 1) * RB);
         }
         kkc = kkn;
         ppc = ppn;
@@ -517,29 +579,32 @@ hipError_t launch_fill_zero(void *p, size_t bytes, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int NV, int E>
+template <int NV, int E, int RP = 1>
 static hipError_t seg_launch(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
                              int32_t *offsets, float *C_out, hipStream_t s) {
-    constexpr int U = NV * E <= 2 ? 8 : (NV * E <= 8 ? 8 : 4);
+    // rows in flight per wave: two batches of U (of row pairs with RP = 2:
+    // 2 x 2 pairs keeps the paired kernel at 58 registers, eight waves per
+    // SIMD, and measured as fast as 2 x 4 pairs at 2^20 and 2^24 rows)
+    constexpr int U = RP == 2 ? 2 : (NV * E <= 8 ? 8 : 4);
     const int srows = seg_rows(N, d);
     const int64_t nseg = cdiv(N, srows);
-    const dim3 grid((unsigned)cdiv(nseg, kSegWaves), (unsigned)cdiv(d, 64 * E * NV));
+    const dim3 grid((unsigned)cdiv(nseg, kSegWaves), (unsigned)cdiv(d, 64 / RP * E * NV));
     const dim3 block(kSegWaves * 64);
     if (xnorm64 != nullptr) {
         if (acc)
-            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, true, true>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
-                               xnorm64, sums, pfirst, plast, offsets, C_out);
+            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, true, true, RP>), grid, block, 0, s, X, N, d, K, srows, ks,
+                               perm, xnorm64, sums, pfirst, plast, offsets, C_out);
         else
-            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, true, false>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
-                               xnorm64, sums, pfirst, plast, offsets, C_out);
+            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, true, false, RP>), grid, block, 0, s, X, N, d, K, srows, ks,
+                               perm, xnorm64, sums, pfirst, plast, offsets, C_out);
     } else {
         if (acc)
-            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, false, true>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
-                               xnorm64, sums, pfirst, plast, offsets, C_out);
+            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, false, true, RP>), grid, block, 0, s, X, N, d, K, srows, ks,
+                               perm, xnorm64, sums, pfirst, plast, offsets, C_out);
         else
-            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, false, false>), grid, block, 0, s, X, N, d, K, srows, ks, perm,
-                               xnorm64, sums, pfirst, plast, offsets, C_out);
+            hipLaunchKernelGGL((k_seg_reduce<NV, E, U, false, false, RP>), grid, block, 0, s, X, N, d, K, srows, ks,
+                               perm, xnorm64, sums, pfirst, plast, offsets, C_out);
     }
     return hipGetLastError();
 }
@@ -558,12 +623,16 @@ static hipError_t seg_launch_e(const float *X, int64_t N, int d, int K, const in
 }
 
 // Row loads of E floats per lane: float4 when a row spans at least 256
-// floats, float2 from 128, scalar otherwise (or when d is not a multiple);
-// column blocks of up to 4 loads per lane, more blocks on blockIdx.y.
+// floats, or (two rows per load, one per half-wave) between 65 and 128
+// floats; float2 from 128 otherwise, scalar below (or when d is not a
+// multiple); column blocks of up to 4 loads per lane, more blocks on
+// blockIdx.y.
 hipError_t launch_seg_reduce(const float *X, int64_t N, int d, int K, const int32_t *ks, const int32_t *perm,
                              const double *xnorm64, double *sums, double *pfirst, double *plast, bool acc,
                              int32_t *offsets, float *C_out, hipStream_t s) {
     if (N <= 0) return hipSuccess;
+    if (d % 4 == 0 && d > 64 && d <= 128)
+        return seg_launch<1, 4, 2>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, offsets, C_out, s);
     if (d % 4 == 0 && d >= 256)
         return seg_launch_e<4>(X, N, d, K, ks, perm, xnorm64, sums, pfirst, plast, acc, offsets, C_out, s);
     if (d % 2 == 0 && d >= 128)
