@@ -602,7 +602,60 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 if constexpr (add_norm) nacc = fmaf(xv, xv, nacc);
             }
         };
+        // resident split points: the same values with unconditional loads
+        // (the row index and column clamped into X, out-of-range values
+        // zeroed by a select), so that no load sits in a branch of its own
+        auto fetch_x4_nb = [&](int b, int q, float *v) {
+            const int col0 = 16 * (q / 8) + 8 * h + (q % 8);
+            const float *row = X + (size_t)(pv[b] ? pt[b] : 0) * d;
+            if constexpr (VEC) {
+                const bool ok = pv[b] && col0 < d;
+                const float4 u = *reinterpret_cast<const float4 *>(row + (col0 < d ? col0 : d - 4));
+                v[0] = ok ? u.x : 0.f;
+                v[1] = ok ? u.y : 0.f;
+                v[2] = ok ? u.z : 0.f;
+                v[3] = ok ? u.w : 0.f;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float t = row[col0 + e < d ? col0 + e : d - 1];
+                    v[e] = (pv[b] && col0 + e < d) ? t : 0.f;
+                }
+            }
+        };
         auto load_x = [&](int ch, auto add_norm) {
+            if constexpr (SPLIT && RES && !COLLECT && TL == 0) {
+                // (the assignment sweep; the window and top-L passes keep the
+                // form below, which spills less there)
+                // Groups of 8 slots go through a ring of LDEP register
+                // groups: group g + LDEP - 1 is loaded while group g is split,
+                // and the scheduling barriers keep the compiler from hoisting
+                // every load of the rows ahead of the splits (it would hold
+                // all the fp32 values and the bf16 halves live at once, and
+                // spill).
+                constexpr int NG = HALF / 8, TOT = PB * NG, LDEP = 4;
+                float rq[LDEP][8];
+#pragma unroll
+                for (int g = 0; g < LDEP - 1; ++g)
+                    if (g < TOT) {
+                        fetch_x4_nb(g / NG, (g % NG) * 8, rq[g]);
+                        fetch_x4_nb(g / NG, (g % NG) * 8 + 4, rq[g] + 4);
+                    }
+#pragma unroll
+                for (int g = 0; g < TOT; ++g) {
+                    const int gn = g + LDEP - 1;
+                    if (gn < TOT) {
+                        fetch_x4_nb(gn / NG, (gn % NG) * 8, rq[gn % LDEP]);
+                        fetch_x4_nb(gn / NG, (gn % NG) * 8 + 4, rq[gn % LDEP] + 4);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    const int b = g / NG, q = (g % NG) * 8;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) put_x(b, q + e, rq[g % LDEP][e], add_norm, xn[b], xl2[b], xr2[b]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                return;
+            }
 #pragma unroll
             for (int b = 0; b < PB; ++b) {
                 float nacc = xn[b], lacc = xl2[b], racc = xr2[b];
@@ -921,11 +974,14 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                     // operands are read one step ahead.  The wave issuing
                     // products takes priority over the other wave of its SIMD
                     // (which may be in its epilogue) until its block is done.
+                    // The high parts read here are kept for phase 3 (ahs).
                     __builtin_amdgcn_s_setprio(1);
+                    v8bf ahs[NS];
                     v8bf ah = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB);
                     v8bf al = *reinterpret_cast<const v8bf *>(sl + cb * 32 * LDB);
 #pragma unroll
                     for (int st = 0; st < NS; ++st) {
+                        ahs[st] = ah;
                         v8bf ahn = ah, aln = al;
                         if (st + 1 < NS) {
                             ahn = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB + 16 * (st + 1));
@@ -953,20 +1009,14 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                             acc[b][0][4 * q + 3] += nv.w;
                         }
                     }
-                    // phase 3: hi.hi (the high parts are read from LDS again:
-                    // the empty asm keeps the compiler from holding the phase-1
-                    // reads in registers)
-                    asm volatile("" ::: "memory");
-                    v8bf ah3 = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB);
+                    // phase 3: hi.hi, on the high parts phase 1 read (held in
+                    // registers: reading them from LDS again measured 1 %
+                    // slower at 16M x 128, K = 32768)
 #pragma unroll
-                    for (int st = 0; st < NS; ++st) {
-                        v8bf ahn = ah3;
-                        if (st + 1 < NS) ahn = *reinterpret_cast<const v8bf *>(sh + cb * 32 * LDB + 16 * (st + 1));
+                    for (int st = 0; st < NS; ++st)
 #pragma unroll
                         for (int b = 0; b < PB; ++b)
-                            acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ah3, xh[b][st], acc[b][0], 0, 0, 0);
-                        ah3 = ahn;
-                    }
+                            acc[b][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ahs[st], xh[b][st], acc[b][0], 0, 0, 0);
                     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
                     for (int b = 0; b < PB; ++b) epilogue(acc[b][0], b, t * ROWS + cb * 32 + 4 * h);
