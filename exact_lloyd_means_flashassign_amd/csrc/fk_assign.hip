@@ -1940,9 +1940,8 @@ static hipError_t launch_fa_shape(const FlashArgs &A, hipStream_t s) {
         // two workgroups share a CU and one's prologue and epilogue overlap
         // the other's products: 3 % faster than 8-wave workgroups at
         // 16M x 128, K = 32768 and 5 % at 1M x 128, K = 1024, measured side
-        // by side, although the prologue then spills about 60 bytes per lane
-        // (once per workgroup; the sweep itself spills nothing), which the
-        // 8-wave form does not; one point block per wave: 10-14 % slower
+        // by side (252 registers, no scratch); one point block per wave:
+        // 10-14 % slower
         if constexpr (SPLIT)
             return launch_fa<128, 2, 2, 4, 2, true, COLLECT, SPLIT>(A, s);
         else
