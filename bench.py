@@ -51,6 +51,26 @@ def source_sha(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
+def run_env(torch, np):
+    """Versions and hardware the numbers were taken with (the seeded streams
+    and the timings both depend on them)."""
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None), "numpy": np.__version__,
+            "gpu": torch.cuda.get_device_name(0), "cpu": cpu, "host_cores_available": cores}
+
+
 def traffic_file(workload, score):
     return os.path.join(ROOT, "profiles", f"flash_assign_{score}_{workload}_traffic.json")
 
@@ -570,6 +590,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, X, C0)
     else:
         out["cpu_baseline"] = None
+    out["env"] = run_env(torch, np)
     print(json.dumps(out), flush=True)
 
 
