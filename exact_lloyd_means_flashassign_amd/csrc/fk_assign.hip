@@ -345,11 +345,6 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
     // beside 32-long candidate lists (no registers left for them there: the
     // points are loaded at the start of their own stage).
     constexpr bool PRE = !RES && TL <= 16;
-    // Split scoring turns each fetched value into its bf16 parts: there the
-    // values are fetched two stages ahead and split during the stage before
-    // their own, alongside its products (not beside candidate lists: the
-    // registers are not there).
-    constexpr bool PRE2 = PRE && SPLIT && TL == 0 && !ONEACC;
     // top-L lists that may start from a threshold (the 16-long lists beside
     // streamed d-chunks never do: that sweep runs without the threshold pass)
     constexpr bool TAU = TL > 0 && (RES || TL > 16);
@@ -685,51 +680,6 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
 #pragma unroll
                 for (int q = 0; q < HALF; q += 4) fetch_x4(ch, b, q, &xraw[b][q]);
         };
-        // two stages ahead (split scoring): xraw holds the next stage's
-        // values, xraw2 receives the one after, xhn and xln the next stage's
-        // bf16 parts
-        float xraw2[PB][PRE2 ? HALF : 4];
-        v8bf xhn[PB][PRE2 ? NS : 1], xln[PB][PRE2 ? NS : 1];
-        auto fetch_next2 = [&](int ch) {
-#pragma unroll
-            for (int b = 0; b < PB; ++b)
-#pragma unroll
-                for (int q = 0; q < HALF; q += 4) fetch_x4(ch, b, q, &xraw2[b][q]);
-        };
-        // xraw -> xhn, xln (no branch: it runs among the stage's products)
-        auto split_next = [&]() {
-#pragma unroll
-            for (int b = 0; b < PB; ++b)
-#pragma unroll
-                for (int q = 0; q < HALF; ++q) {
-                    const float v = xraw[b][q];
-                    const float xv = (RES && A.xnorm64 == nullptr) ? v : v * xsc[b];
-                    const __bf16 hi = (__bf16)xv;
-                    const __bf16 lo = (__bf16)(xv - (float)hi);
-                    xhn[b][q / 8][q % 8] = hi;
-                    xln[b][q / 8][q % 8] = lo;
-                }
-        };
-        // the squared norms of the next stage's values (first tile only)
-        auto norm_next = [&]() {
-#pragma unroll
-            for (int b = 0; b < PB; ++b) {
-                float nacc = xn[b], lacc = xl2[b], racc = xr2[b];
-#pragma unroll
-                for (int q = 0; q < HALF; ++q) {
-                    const float v = xraw[b][q];
-                    const float xv = (RES && A.xnorm64 == nullptr) ? v : v * xsc[b];
-                    const float dl = xv - (float)(__bf16)xv;  // exact
-                    const float lf = (float)(__bf16)dl, r = dl - lf;  // exact
-                    nacc = fmaf(xv, xv, nacc);
-                    lacc = fmaf(lf, lf, lacc);
-                    racc = fmaf(r, r, racc);
-                }
-                xn[b] = nacc;
-                xl2[b] = lacc;
-                xr2[b] = racc;
-            }
-        };
         auto put_next = [&](auto add_norm) {
 #pragma unroll
             for (int b = 0; b < PB; ++b) {
@@ -878,13 +828,6 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
         const int te = TL > 0 ? min(A.ntiles, tb + A.knn_tps) : COLLECT ? min(A.ntiles, tb + tps) : A.ntiles;
         const int nst = (te - tb) * cnch;
         if (RES || PRE) load_x(0, std::true_type{});
-        if constexpr (PRE2) {
-#pragma unroll
-            for (int b = 0; b < PB; ++b)
-#pragma unroll
-                for (int q = 0; q < HALF; ++q) xraw[b][q] = 0.f;
-            if (nst > 1) fetch_next(cnch > 1 ? 1 : 0);
-        }
         if (RES) {
             if (!COLLECT) point_bounds();
             if constexpr (PHASED) {
@@ -918,9 +861,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
             // streamed chunks: the next stage's points are fetched with the
             // next centroid stage, a whole stage before they are used (beside
             // 32-long lists: this stage's points, loaded now)
-            if constexpr (PRE2) {
-                if (st + 2 < nst) fetch_next2(nc + 1 < cnch ? nc + 1 : 0);
-            } else if constexpr (PRE) {
+            if constexpr (PRE) {
                 if (more) fetch_next(nc);
             } else if constexpr (!RES) {
                 if (t == tb)
@@ -1071,15 +1012,6 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                         }
                     }
                 }
-                if constexpr (PRE2) {
-                    split_next();
-                    // keep the split here, among this stage's products (left
-                    // alone the compiler sinks it to the end of the stage)
-#pragma unroll
-                    for (int b = 0; b < PB; ++b)
-#pragma unroll
-                        for (int q = 0; q < NS; ++q) asm volatile("" : "+v"(xhn[b][q]), "+v"(xln[b][q]));
-                }
             } else {
                 const float *sc = &sC[buf][jl * LDR + h * HALF];
                 __builtin_amdgcn_s_setprio(1);  // as above: products first
@@ -1115,21 +1047,7 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                 }
             }
             if (!DMA && !(PHASED && CB > 1) && more) store_stage(buf ^ 1, nc);
-            if constexpr (PRE2) {
-                if (more) {
-                    if (nt == tb) norm_next();
-#pragma unroll
-                    for (int b = 0; b < PB; ++b) {
-#pragma unroll
-                        for (int q = 0; q < NS; ++q) {
-                            xh[b][q] = xhn[b][q];
-                            xl[b][q] = xln[b][q];
-                        }
-#pragma unroll
-                        for (int q = 0; q < HALF; ++q) xraw[b][q] = xraw2[b][q];
-                    }
-                }
-            } else if constexpr (PRE) {
+            if constexpr (PRE) {
                 if (more) {
                     // after this stage's products: the wait for the fetched
                     // values must not move ahead of them
