@@ -764,17 +764,25 @@ __global__ __launch_bounds__(WAVES * 64, MINB) void k_flash_assign(const FlashAr
                         int rs = 15;
 #pragma unroll
                         for (int r = 15; r >= 0; --r) rs = (v[r] == m) ? r : rs;
-                        float sv = m;
-                        int sk = kb + 8 * (rs >> 2) + (rs & 3);
+                        const int sk = kb + 8 * (rs >> 2) + (rs & 3);
+                        // m goes to the first place j with m > bl[j] (a
+                        // suffix of the sorted list): a place past it takes
+                        // the entry before it, the places before it keep
+                        // theirs -- for the scores, the median of the entry
+                        // before, the entry and m (v_med3_f32)
+                        float pv = 0.f;
+                        int pk = 0;
+                        bool pc = false;
 #pragma unroll
                         for (int j = 0; j < TL; ++j) {
-                            const bool c = sv > bl[b][j];
-                            const float tv = bl[b][j];
-                            const int tk = il[b][j];
-                            bl[b][j] = c ? sv : tv;
-                            il[b][j] = c ? sk : tk;
-                            sv = c ? tv : sv;
-                            sk = c ? tk : sk;
+                            const float ov = bl[b][j];
+                            const int ok = il[b][j];
+                            const bool c = m > ov;
+                            bl[b][j] = j == 0 ? (c ? m : ov) : __builtin_amdgcn_fmed3f(pv, ov, m);
+                            il[b][j] = pc ? pk : (c ? sk : ok);
+                            pv = ov;
+                            pk = ok;
+                            pc = c;
                         }
 #pragma unroll
                         for (int r = 0; r < 16; ++r) v[r] = (r == rs) ? -INFINITY : v[r];
