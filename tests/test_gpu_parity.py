@@ -50,7 +50,8 @@ def test_assign_cosine_matches_oracle(gpu_lib, N, d, K, kind, score):
 
 
 @pytest.mark.parametrize("N,d,K", [(1, 4, 1), (1000, 16, 64), (5000, 128, 1024), (4096 * 3 + 5, 8, 300),
-                                   (2048 * 5 + 7, 65, 40), (300, 768, 4096), (20000, 3, 2), (9000, 1030, 7)])
+                                   (2048 * 5 + 7, 65, 40), (300, 768, 4096), (20000, 3, 2), (9000, 1030, 7),
+                                   (2048 * 3 + 3, 100, 77), (4097, 68, 5)])
 @pytest.mark.parametrize("metric", ["l2", "cosine"])
 def test_update_matches_oracle(gpu_lib, N, d, K, metric):
     fk = gpu_lib
@@ -155,10 +156,13 @@ def test_window_list_beyond_cap(gpu_lib, score):
     assert prof["rechecked"] > max(N // 8, NEAR_TIE_CAP_MIN), prof
 
 
-def test_update_single_giant_cluster(gpu_lib):
-    """Every point in one cluster: the cluster crosses every segment boundary."""
+@pytest.mark.parametrize("d", [64, 100])
+def test_update_single_giant_cluster(gpu_lib, d):
+    """Every point in one cluster: the cluster crosses every segment boundary
+    (d = 100: rows read two per 16-byte load, one per half-wave, with an odd
+    row count, so the last pair of the last segment has one row)."""
     fk = gpu_lib
-    N, d, K = 200000, 64, 5
+    N, K = 200001, 5
     rng = np.random.default_rng(9)
     X = rng.standard_normal((N, d)).astype(np.float32)
     a = np.full(N, 3, np.int32)

@@ -54,11 +54,13 @@ def test_stream_without_assignment_output(gpu_lib):
 
 
 @pytest.mark.parametrize("score", ["fp32", "split_bf16"])
-@pytest.mark.parametrize("d,chunk", [(200, 20000), (37, 7777)])
+@pytest.mark.parametrize("d,chunk", [(200, 20000), (37, 7777), (100, 9999)])
 def test_stream_other_widths(gpu_lib, d, chunk, score):
     """Streamed chunks of rows with d > 128 (points streamed through the
-    assignment kernel in 64-dim chunks) and with a ragged d: the batches'
-    sums, counts and offsets add up to the in-core iteration and the oracle."""
+    assignment kernel in 64-dim chunks), with a ragged d, and with d = 100
+    (the reduction reads those rows two per 16-byte load and adds each
+    batch's sums to the running ones): the batches' sums, counts and offsets
+    add up to the in-core iteration and the oracle."""
     fk = gpu_lib
     rng = np.random.default_rng(d)
     N, K = 50001, 300
