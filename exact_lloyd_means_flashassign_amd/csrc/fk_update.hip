@@ -43,16 +43,14 @@ __global__ __launch_bounds__(256) void k_fill_zero(uint32_t *__restrict__ p, int
 // fewer, E = 4, NV = 1): each half-wave loads one row, so one 16-byte load per
 // lane brings two rows (half the load instructions of 8-byte loads); the
 // lower half sums the pair's first rows and the upper half the second ones,
-// and a cluster's total is the lower half's sum plus the upper half's.  COS: rows are scaled by
-// 1/xnorm64 (cosine).  ACC: cluster sums are added to what sums holds (rows
+// and a cluster's total is the lower half's sum plus the upper half's.
+// COS: rows are scaled by 1/xnorm64 (cosine).  ACC: cluster sums are added to what sums holds (rows
 // fed in several batches; the finalize step divides).  Otherwise the rows
 // come in one batch and a cluster inside the segment is written to C_out as
 // its sum divided by its row count (clusters that no row reaches are left to
 // k_seg_finish).  The column block blockIdx.y == 0 also writes offsets[k] =
 // the first sorted row whose key is >= k (offsets[K] = N): the entries between
 // two consecutive keys are written by the wave that sees the change.
-// (paired rows: registers capped so that eight waves share a SIMD, which
-// keeps every segment of 2^24 rows resident at once)
 template <int NV, int E, int U, bool COS, bool ACC, int RP>
 __global__ __launch_bounds__(256) void k_seg_reduce(const float *__restrict__ X, int64_t N, int d, int K, int srows,
                                                     const int32_t *__restrict__ ks, const int32_t *__restrict__ perm,
