@@ -357,7 +357,11 @@ def ooc_bench(args, fk, synth, np, torch):
     t0 = time.perf_counter()
     Xh = torch.empty((N, w.d), dtype=torch.float32, pin_memory=True)
     X = Xh.numpy()
-    synth.rows(w, out=X)
+    piece = 1 << 25
+    for lo in range(0, N, piece):
+        hi = min(N, lo + piece)
+        synth.rows(w, lo, hi, out=X[lo:hi])
+        log(f"generated rows [{lo}, {hi}) of {N}")
     C = X[synth.init_indices(w)].copy()
     ah = torch.empty(N, dtype=torch.int32, pin_memory=True)
     Cd = torch.from_numpy(C).to("cuda:0")
