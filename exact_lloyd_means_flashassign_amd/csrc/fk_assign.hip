@@ -1499,6 +1499,15 @@ __device__ __forceinline__ void recheck_pair_rows(const float *__restrict__ X, i
 // time; for each candidate rank m it stages the points' rows and their m-th
 // candidate rows through LDS as k_recheck_pair does, and each lane sums its
 // own rows in increasing j.
+// four consecutive floats into a padded LDS row (the rows are J + 1 floats
+// long, so no 16-byte LDS store fits them)
+__device__ __forceinline__ void stage4(float *dst, const float4 v) {
+    dst[0] = v.x;
+    dst[1] = v.y;
+    dst[2] = v.z;
+    dst[3] = v.w;
+}
+
 template <typename CT>
 __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ X, int d, const CT *__restrict__ C,
                                                       const double *__restrict__ xnorm64,
@@ -1514,6 +1523,7 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
     __shared__ CT sc[4][64 * JP];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cnt = counters[0];
+    const bool vec4 = sizeof(CT) == 4 && d % J == 0;
     if (d > 128 || cnt < kStagedMinList) {
         if (d <= kGroupMaxD)
             recheck_cand_group<CT>(X, d, C, xnorm64, full_list, cand, ccount, cap_slots, ovf_list, counters, a_out,
@@ -1546,14 +1556,30 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
             double D = 0.0;
             for (int j0 = 0; j0 < d; j0 += J) {
                 const int nj = min(J, d - j0);
+                if (vec4) {
+                    // fp32 rows and d a multiple of J: 16-byte loads, four
+                    // dims of a row per lane (X and C are 16-byte aligned)
 #pragma unroll
-                for (int i = 0; i < J; ++i) {
-                    const int e = lane + 64 * i, r = e / J, c = e % J;
-                    const int64_t pr = __shfl(p, r);
-                    const int kr = __shfl(k, r);
-                    if (c < nj) {
-                        sx[w][r * JP + c] = X[(size_t)pr * d + j0 + c];
-                        sc[w][r * JP + c] = C[(size_t)kr * d + j0 + c];
+                    for (int i = 0; i < J / 4; ++i) {
+                        const int e = lane + 64 * i, r = e / (J / 4), c = (e % (J / 4)) * 4;
+                        const int64_t pr = __shfl(p, r);
+                        const int kr = __shfl(k, r);
+                        const float4 xv = *reinterpret_cast<const float4 *>(X + (size_t)pr * d + j0 + c);
+                        const float4 cv = *reinterpret_cast<const float4 *>(
+                            reinterpret_cast<const float *>(C) + (size_t)kr * d + j0 + c);
+                        stage4(&sx[w][r * JP + c], xv);
+                        stage4(reinterpret_cast<float *>(&sc[w][r * JP + c]), cv);
+                    }
+                } else {
+#pragma unroll
+                    for (int i = 0; i < J; ++i) {
+                        const int e = lane + 64 * i, r = e / J, c = e % J;
+                        const int64_t pr = __shfl(p, r);
+                        const int kr = __shfl(k, r);
+                        if (c < nj) {
+                            sx[w][r * JP + c] = X[(size_t)pr * d + j0 + c];
+                            sc[w][r * JP + c] = C[(size_t)kr * d + j0 + c];
+                        }
                     }
                 }
                 __builtin_amdgcn_wave_barrier();
@@ -1601,6 +1627,7 @@ __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ 
     __shared__ CT sc[4][2][64 * JP];
     const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int cnt = counters[1];
+    const bool vec4 = sizeof(CT) == 4 && d % J == 0;
     if (d > 128 || cnt < kStagedMinList) {
         if (d <= kGroupMaxD)
             recheck_pair_group<CT>(X, d, C, xnorm64, pair_list, counters, a_out, ip);
@@ -1620,15 +1647,33 @@ __global__ __launch_bounds__(256) void k_recheck_pair(const float *__restrict__ 
             const int nj = min(J, d - j0);
             // element e of the stage: row e / J, dim e % J (rows of lanes
             // that hold no pair are those of row 0: read, never used)
+            if (vec4) {
+                // fp32 rows and d a multiple of J: 16-byte loads, four dims
+                // of a row per lane (X and C are 16-byte aligned)
 #pragma unroll
-            for (int i = 0; i < J; ++i) {
-                const int e = lane + 64 * i, r = e / J, c = e % J;
-                const int64_t pr = __shfl(p, r);
-                const int kr1 = __shfl(k1, r), kr2 = __shfl(k2, r);
-                if (c < nj) {
-                    sx[w][r * JP + c] = X[(size_t)pr * d + j0 + c];
-                    sc[w][0][r * JP + c] = C[(size_t)kr1 * d + j0 + c];
-                    sc[w][1][r * JP + c] = C[(size_t)kr2 * d + j0 + c];
+                for (int i = 0; i < J / 4; ++i) {
+                    const int e = lane + 64 * i, r = e / (J / 4), c = (e % (J / 4)) * 4;
+                    const int64_t pr = __shfl(p, r);
+                    const int kr1 = __shfl(k1, r), kr2 = __shfl(k2, r);
+                    const float *Cf = reinterpret_cast<const float *>(C);
+                    const float4 xv = *reinterpret_cast<const float4 *>(X + (size_t)pr * d + j0 + c);
+                    const float4 c1 = *reinterpret_cast<const float4 *>(Cf + (size_t)kr1 * d + j0 + c);
+                    const float4 c2 = *reinterpret_cast<const float4 *>(Cf + (size_t)kr2 * d + j0 + c);
+                    stage4(&sx[w][r * JP + c], xv);
+                    stage4(reinterpret_cast<float *>(&sc[w][0][r * JP + c]), c1);
+                    stage4(reinterpret_cast<float *>(&sc[w][1][r * JP + c]), c2);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < J; ++i) {
+                    const int e = lane + 64 * i, r = e / J, c = e % J;
+                    const int64_t pr = __shfl(p, r);
+                    const int kr1 = __shfl(k1, r), kr2 = __shfl(k2, r);
+                    if (c < nj) {
+                        sx[w][r * JP + c] = X[(size_t)pr * d + j0 + c];
+                        sc[w][0][r * JP + c] = C[(size_t)kr1 * d + j0 + c];
+                        sc[w][1][r * JP + c] = C[(size_t)kr2 * d + j0 + c];
+                    }
                 }
             }
             __builtin_amdgcn_wave_barrier();
