@@ -289,21 +289,33 @@ __global__ __launch_bounds__(1024) void k_prep_finish(const float *__restrict__ 
 // the full list.  For cosine, the fp32 normalised rows differ from the fp64
 // normalised ones by at most 3.1u relative, which moves a by at most
 // 3.1u (||x|| ||c|| + ||c||^2); 8u is added to g for it.
-// Tile slices of the collect sweep for a full list of nslots points: as
-// many as the persistent grid (grid workgroups) has room for beside the
-// list's slot groups, at most 64 and at most the tile count, such that the
-// candidate storage (cap_slots slots) holds nslots * slices lists, and
-// rounded so that every slice has tiles.  A long list (kStagedMinList points
-// or more) takes one slice: its fp64 check stages rows for one list per
-// point.  The fp64 check reads the count back from counters[3].
+// Tile slices of the collect sweep for a full list of nslots points.  The
+// list's ng slot groups times s slices are the units that the persistent
+// grid (grid workgroups) strides over.  A list that fills less than one
+// round takes as many slices as the grid has room for.  A longer one would
+// leave its last round mostly idle with one slice (1.3 rounds take two), so
+// it is cut into the fewest slices whose estimated time -- rounds times the
+// tiles a unit sweeps, plus one for its prologue -- is within 3 % of the
+// least.  At most 64 slices and at most the tile count, and the candidate
+// storage (cap_slots slots) must hold nslots * s lists; the count is
+// rounded so that every slice has tiles.  The fp64 checks read it back from
+// counters[3].
 constexpr int kStagedMinList = 65536;  // listed points for the staged checks
 __device__ __forceinline__ int collect_slices(int64_t nslots, int64_t cap_slots, int ntiles, int bm, int grid) {
-    if (nslots >= kStagedMinList || nslots <= 0) return 1;
+    if (nslots <= 0) return 1;
     const int64_t ng = (nslots + bm - 1) / bm;
-    int64_t s = grid / ng;
-    s = min(s, (int64_t)min(ntiles, 64));
-    s = min(s, cap_slots / (ng * bm));
-    if (s < 1) return 1;
+    const int64_t smax = min((int64_t)min(ntiles, 64), cap_slots / (ng * bm));
+    if (smax < 1) return 1;
+    int64_t s;
+    if (ng <= grid) {
+        s = min((int64_t)grid / ng, smax);
+    } else {
+        auto cost = [&](int64_t sl) { return ((ng * sl + grid - 1) / grid) * ((ntiles + sl - 1) / sl + 1); };
+        int64_t cmin = cost(1);
+        for (int64_t sl = 2; sl <= smax; ++sl) cmin = min(cmin, cost(sl));
+        s = 1;
+        while (s < smax && cost(s) * 100 > cmin * 103) ++s;
+    }
     const int64_t tps = (ntiles + s - 1) / s;
     return (int)((ntiles + tps - 1) / tps);
 }
@@ -1533,17 +1545,24 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
                                   ip);
         return;
     }
+    const int nl = 2 * max(counters[3], 1);  // candidate lists per slot (two per tile slice)
     for (int64_t q0 = ((int64_t)blockIdx.x * 4 + w) * 64; q0 < cnt; q0 += (int64_t)gridDim.x * 4 * 64) {
         const int64_t q = q0 + lane;
         bool ok = q < cnt;
         const int64_t p = ok ? full_list[q] : 0;
-        const int c0 = !ok ? 0 : q < cap_slots ? ccount[2 * q] : kMaxCand + 1;
-        const int c1 = !ok ? 0 : q < cap_slots ? ccount[2 * q + 1] : kMaxCand + 1;
-        if (ok && (c0 > kMaxCand || c1 > kMaxCand)) {
+        bool ovf = ok && q >= cap_slots;
+        int nc = 0;
+        if (ok && !ovf)
+            for (int l = 0; l < nl; ++l) {
+                const int c = ccount[q * nl + l];
+                ovf = ovf || c > kMaxCand;
+                nc += c;
+            }
+        if (ovf) {
             ovf_list[atomicAdd(&counters[2], 1)] = (int32_t)p;
             ok = false;
         }
-        const int nc = ok ? c0 + c1 : 0;
+        if (!ok) nc = 0;
         int ncw = nc;  // the wave's largest candidate count
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1) ncw = max(ncw, __shfl_xor(ncw, off));
@@ -1552,7 +1571,15 @@ __global__ __launch_bounds__(256) void k_recheck_cand(const float *__restrict__ 
         int bk = 0x7fffffff;
         for (int m = 0; m < ncw; ++m) {
             const bool has = m < nc;
-            const int k = !has ? 0 : m < c0 ? cand[2 * q * kMaxCand + m] : cand[(2 * q + 1) * kMaxCand + m - c0];
+            int k = 0;
+            if (has) {
+                int l = 0, r = m;  // the m-th candidate: list l, rank r
+                for (int c = ccount[q * nl]; r >= c; c = ccount[q * nl + l]) {
+                    r -= c;
+                    ++l;
+                }
+                k = cand[(q * nl + l) * kMaxCand + r];
+            }
             double D = 0.0;
             for (int j0 = 0; j0 < d; j0 += J) {
                 const int nj = min(J, d - j0);
