@@ -156,6 +156,34 @@ def test_window_list_beyond_cap(gpu_lib, score):
     assert prof["rechecked"] > max(N // 8, NEAR_TIE_CAP_MIN), prof
 
 
+@pytest.mark.parametrize("score", SCORES)
+def test_window_list_over_several_grid_rounds(gpu_lib, score):
+    """About 160,000 window points, more than one round of the window pass's
+    persistent grid (625 slot groups of 256 on 512 workgroups) and under half
+    the candidate slots: the pass cuts the centroid tiles into slices and the
+    LDS-staged fp64 check merges several candidate lists per point.  Points
+    around 8 of 200 well-separated centres, each centre present three times
+    over, are exact three-way ties; every label must equal the oracle's
+    (lowest index among the copies)."""
+    fk = gpu_lib
+    rng = np.random.default_rng(13)
+    N, d, G = 4_000_000, 16, 200
+    centres = (4.0 * rng.standard_normal((G, d))).astype(np.float32)
+    C = np.concatenate([centres, centres[:8], centres[:8]])
+    C = C[rng.permutation(len(C))]
+    X = (centres[rng.integers(0, G, N)] + 0.3 * rng.standard_normal((N, d))).astype(np.float32)
+    log(f"window list over several grid rounds: N={N} d={d} K={len(C)} {score}")
+    a_ref, _, _ = oracle.assign(X, C)
+    fk.fk_profile_enable(True)
+    a, _ = fk.fk_assign(dev(X), dev(C), score=score)
+    prof = fk.fk_profile_read()
+    fk.fk_profile_enable(False)
+    np.testing.assert_array_equal(host(a), a_ref)
+    cap = max(N // 8, NEAR_TIE_CAP_MIN)
+    assert 512 * 256 < prof["windowed"] <= cap // 2, prof
+    assert prof["rechecked"] == 0, prof
+
+
 @pytest.mark.parametrize("d", [64, 100])
 def test_update_single_giant_cluster(gpu_lib, d):
     """Every point in one cluster: the cluster crosses every segment boundary
